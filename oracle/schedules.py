@@ -1,0 +1,473 @@
+"""Step-by-step replays of every Allreduce schedule on the pages (oracle).
+
+Each replay drives the rank simulator of ``net`` (or, for the generalized
+algorithm, the paper's own vector-and-placement formalism) through the
+schedule's steps in the pages' order, then returns every rank's final buffer.
+The per-element combination order therefore is exactly the schedule's.
+
+Where a page leaves a step open, the reading taken is stated at the function.
+
+Public entry point: ``allreduce(x, algo, dtype, op, ...)``.
+"""
+from __future__ import annotations
+
+import math
+from functools import reduce as _fold
+
+import numpy as np
+
+from .net import COPY, REDUCE, Net, partition
+from .numerics import Algebra, Symbolic, ceil_log2
+
+ALGOS = ("direct", "ring", "rh_rd", "rd", "binomial", "generalized", "generalized_xor", "ahc")
+
+
+def _pow2_floor(P: int) -> int:
+    return 1 << (P.bit_length() - 1)
+
+
+# --------------------------------------------------------------------------
+# direct: gather to one root, combine, broadcast
+# --------------------------------------------------------------------------
+def _direct(net: Net):
+    """The naive one-root schedule of the all-reduce blog page ("A cost model for
+    collectives": gather at GPU 0, sum, broadcast back).
+
+    Reading: the page fixes no order for the root's combinations; the root
+    folds the other ranks in rank order, x0 + x1, then + x2, ..., one incoming
+    buffer per step (a rank receives one message per step), then sends the
+    result to each rank in rank order.
+    """
+    P, n = net.P, net.n
+    for s in range(1, P):
+        net.step([(s, 0, 0, n, REDUCE)])
+    for s in range(1, P):
+        net.step([(0, s, 0, n, COPY)])
+
+
+# --------------------------------------------------------------------------
+# ring reduce-scatter + all-gather
+# --------------------------------------------------------------------------
+def _ring(net: Net):
+    """Ring Allreduce ("The ring algorithm", all-reduce blog page; also the cyclic
+    case of the straightforward algorithm, generalized-Allreduce paper,
+    eqs. (14)-(16) and Fig. 5).
+
+    P parts by the ceil split. Reduce-scatter: in step t = 0..P-2 every rank
+    r passes part (r - t) mod P to its right neighbour r + 1, which adds it
+    into its own copy. Afterwards rank r owns the full sum of part (r + 1)
+    mod P. All-gather: in step t rank r passes part (r + 1 - t) mod P to
+    r + 1, which overwrites its copy.
+    """
+    P, n = net.P, net.n
+    parts = partition(n, P)
+    for t in range(P - 1):
+        net.step([(r, (r + 1) % P, *parts[(r - t) % P], REDUCE) for r in range(P)])
+    for t in range(P - 1):
+        net.step([(r, (r + 1) % P, *parts[(r + 1 - t) % P], COPY) for r in range(P)])
+
+
+# --------------------------------------------------------------------------
+# fold-in for non-power-of-two P
+# --------------------------------------------------------------------------
+def _fold_in(net: Net) -> int:
+    """Preparation step for P that is not a power of two (generalized-Allreduce
+    paper, related-work paragraph on non-power-of-two process counts): the
+    excess ranks hand their whole buffer to ranks that take part in the
+    power-of-two algorithm.
+
+    Reading: excess rank P' + j sends to rank j (j < P - P'), which adds it in.
+    Returns P' (the largest power of two <= P).
+    """
+    P, n = net.P, net.n
+    Pp = _pow2_floor(P)
+    if P > Pp:
+        net.step([(Pp + j, j, 0, n, REDUCE) for j in range(P - Pp)])
+    return Pp
+
+
+def _fold_out(net: Net, Pp: int):
+    """Finalization step: rank j returns the result to excess rank P' + j."""
+    P, n = net.P, net.n
+    if P > Pp:
+        net.step([(j, Pp + j, 0, n, COPY) for j in range(P - Pp)])
+
+
+# --------------------------------------------------------------------------
+# recursive halving reduce-scatter + recursive doubling all-gather
+# --------------------------------------------------------------------------
+def _rh_rd(net: Net):
+    """Recursive Halving (bandwidth-optimal, 2 log P steps; generalized-Allreduce
+    paper, introduction; it is the bandwidth-optimal generalized algorithm over
+    the self-inverse group of Table 1.b).
+
+    P' parts. Reduction step s = 0..L-1 with distance d = P' / 2^(s+1): rank p
+    works on a window of 2d parts (those whose index agrees with p on all bits
+    of value >= 2d); it sends the half whose bit d differs from p's to partner
+    p XOR d and adds the partner's copy of the half it keeps. After L steps
+    rank p holds the sum of part p. All-gather: the same distances in reverse
+    order (d = 1, 2, ...), each rank copying its whole current window to
+    p XOR d.
+
+    Reading: the distance order (P'/2 first) is the one the generalized
+    algorithm produces over the XOR group; the pages do not fix it otherwise.
+    """
+    n = net.n
+    Pp = _fold_in(net)
+    L = Pp.bit_length() - 1
+    parts = partition(n, Pp)
+
+    def rng(first_part: int, count: int):
+        return parts[first_part][0], parts[first_part + count - 1][1]
+
+    for s in range(L):
+        d = Pp >> (s + 1)
+        msgs = []
+        for p in range(Pp):
+            base = p & ~(2 * d - 1)
+            give = base + (d if (p & d) == 0 else 0)  # half the partner keeps
+            msgs.append((p, p ^ d, *rng(give, d), REDUCE))
+        net.step(msgs)
+    for s in reversed(range(L)):
+        d = Pp >> (s + 1)
+        msgs = []
+        for p in range(Pp):
+            base = p & ~(d - 1)
+            msgs.append((p, p ^ d, *rng(base, d), COPY))
+        net.step(msgs)
+    _fold_out(net, Pp)
+
+
+# --------------------------------------------------------------------------
+# recursive doubling
+# --------------------------------------------------------------------------
+def _rd(net: Net):
+    """Recursive Doubling (latency-optimal, log P steps; generalized-Allreduce
+    paper, introduction and the latency-optimal section, which identifies it
+    with the latency-optimal generalized algorithm over Table 1.b's group).
+
+    In step s (distance d = P' / 2^(s+1)) ranks p and p XOR d exchange their
+    whole buffers and both combine. Non-power-of-two P uses the fold-in.
+    Reading: distance order P'/2 first, as for recursive halving.
+    """
+    n = net.n
+    Pp = _fold_in(net)
+    L = Pp.bit_length() - 1
+    for s in range(L):
+        d = Pp >> (s + 1)
+        net.step([(p ^ d, p, 0, n, REDUCE) for p in range(Pp)])
+    _fold_out(net, Pp)
+
+
+# --------------------------------------------------------------------------
+# binomial tree reduce + broadcast
+# --------------------------------------------------------------------------
+def _binomial(net: Net):
+    """Binomial-tree reduce ("Reduction Operator" page, the PRAM algorithm and its
+    distributed-memory form) followed by a broadcast from rank 0.
+
+    For k = 0..ceil(log2 P)-1, every still-active rank i whose bit k is set
+    sends its value to i - 2^k and becomes inactive; an active rank with bit k
+    clear and i + 2^k < P combines x_i <- x_i (+) x_{i+2^k}.
+
+    Reading: the broadcast is the reverse of the reduce (the page says the
+    reverse procedure is commonly used to broadcast): for k from the top down,
+    every rank i that is a multiple of 2^(k+1) with i + 2^k < P copies its
+    buffer to i + 2^k.
+    """
+    P, n = net.P, net.n
+    K = ceil_log2(P)
+    active = [True] * P
+    for k in range(K):
+        b = 1 << k
+        msgs = []
+        for i in range(P):
+            if not active[i]:
+                continue
+            if i & b:
+                active[i] = False
+            elif i + b < P:
+                msgs.append((i + b, i, 0, n, REDUCE))
+        net.step(msgs)
+    for k in reversed(range(K)):
+        b = 1 << k
+        net.step([(i, i + b, 0, n, COPY) for i in range(0, P, 2 * b) if i + b < P])
+
+
+# --------------------------------------------------------------------------
+# AHC: asymmetric hierarchical Allreduce
+# --------------------------------------------------------------------------
+def _ahc(net: Net, groups):
+    """AHC (HCCL "AHC" page, Description, steps 1-3).
+
+    Groups are contiguous rank ranges ("adjacent NPUs"). With G groups and Lc
+    the least common multiple of the group sizes, the buffer is cut into
+    Lc * G chunks (ceil split). Group a of size g sees the buffer as g
+    segments of C / g chunks each.
+
+    1. Ring reduce-scatter inside every group in parallel, segments as parts
+       (the ring's rule: local rank l passes segment (l - t) mod g to l + 1).
+       Segment k's partial sum ends at local rank (k - 1) mod g.
+    2. The union of all groups' segment boundaries cuts the buffer into pieces;
+       each piece lies in one segment of every group, and that segment's owner
+       in each group are the "logical devices with identical IDs". They run an
+       Allreduce per piece.
+       Reading: the sub-algorithm is the ring (one of the three the page names;
+       the other two are not described), over the owners in group order, with
+       the piece split into G equal sub-pieces (every piece is a whole multiple
+       of G chunks).
+    3. Ring all-gather inside every group.
+    Groups smaller than the largest finish their ring phases early and idle.
+    """
+    P, n = net.P, net.n
+    G = len(groups)
+    if sum(groups) != P or min(groups) < 1:
+        raise ValueError("group sizes must be positive and sum to P")
+    Lc = _fold(lambda a, b: a * b // math.gcd(a, b), groups)
+    C = Lc * G
+    chunks = partition(n, C)
+    offs = [sum(groups[:a]) for a in range(G)]
+    span = [C // g for g in groups]  # chunks per segment
+
+    def erange(c0: int, c1: int):
+        return chunks[c0][0], chunks[c1 - 1][1]
+
+    def seg(a: int, k: int):
+        return erange(k * span[a], (k + 1) * span[a])
+
+    gmax = max(groups)
+    for t in range(gmax - 1):
+        msgs = []
+        for a, g in enumerate(groups):
+            if t < g - 1:
+                for l in range(g):
+                    msgs.append((offs[a] + l, offs[a] + (l + 1) % g, *seg(a, (l - t) % g), REDUCE))
+        net.step(msgs)
+
+    pieces = []
+    for b0, b1, owners in ahc_pieces(groups):
+        w = (b1 - b0) // G
+        subs = [erange(b0 + s * w, b0 + (s + 1) * w) for s in range(G)]
+        pieces.append(([offs[a] + owners[a] for a in range(G)], subs))
+    for t in range(G - 1):
+        net.step([(ow[s], ow[(s + 1) % G], *sub[(s - t) % G], REDUCE)
+                  for ow, sub in pieces for s in range(G)])
+    for t in range(G - 1):
+        net.step([(ow[s], ow[(s + 1) % G], *sub[(s + 1 - t) % G], COPY)
+                  for ow, sub in pieces for s in range(G)])
+
+    for t in range(gmax - 1):
+        msgs = []
+        for a, g in enumerate(groups):
+            if t < g - 1:
+                for l in range(g):
+                    msgs.append((offs[a] + l, offs[a] + (l + 1) % g, *seg(a, (l + 1 - t) % g), COPY))
+        net.step(msgs)
+
+
+def ahc_pieces(groups):
+    """AHC phase-2 pieces as (first chunk, end chunk, owner local rank per group).
+
+    The cut points are the union of every group's segment boundaries (the
+    page's "segment ... along the data boundaries of individual NPUs"); in
+    group a the piece lies in segment k_a, whose ring reduce-scatter partial
+    ends at local rank (k_a - 1) mod g_a.
+    """
+    G = len(groups)
+    Lc = _fold(lambda a, b: a * b // math.gcd(a, b), groups)
+    C = Lc * G
+    span = [C // g for g in groups]
+    bounds = sorted({k * span[a] for a, g in enumerate(groups) for k in range(g + 1)})
+    return [(b0, b1, [(b0 // span[a] - 1) % g for a, g in enumerate(groups)])
+            for b0, b1 in zip(bounds[:-1], bounds[1:])]
+
+
+def ahc_chunks(groups) -> int:
+    """Number of chunks AHC cuts the buffer into: LCM of group sizes times G."""
+    Lc = _fold(lambda a, b: a * b // math.gcd(a, b), groups)
+    return Lc * len(groups)
+
+
+# --------------------------------------------------------------------------
+# generalized Allreduce over a transitive abelian group of order P
+# --------------------------------------------------------------------------
+def _levels(P: int):
+    """N_0 = P, N_{i+1} = ceil(N_i / 2) (N_L = 1); h_i = floor(N_i / 2)."""
+    L = ceil_log2(P)
+    N = [P]
+    for _ in range(L):
+        N.append((N[-1] + 1) // 2)
+    h = [N[i] // 2 for i in range(L)]
+    return L, N, h
+
+
+def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: str):
+    """Generalized Allreduce (generalized-Allreduce paper: bandwidth-optimal
+    section eqs. (17)-(25), intermediate steps eqs. (26)-(36) and Fig. 6,
+    latency-optimal section eqs. (38)-(44)). The equations are missing from the
+    extracted text; this is the reading reconstructed from its prose.
+
+    Placements. The group element t_j sends rank q to q + j (cyclic group,
+    generator q -> q + 1 as in Fig. 2) or to q XOR j (the self-inverse group
+    of Table 1.b, P a power of two). A distributed vector at placement j holds
+    part i at rank t_j(i). The initial data matrix splits into P such vectors
+    d_j (part i of rank t_j(i)'s buffer).
+
+    Base reduction S_0 over vectors v_0..v_{N-1} (v_k = d_k initially): in step
+    i, for k in [N_i - h_i, N_i), v_k is moved onto v_{k - h_i}'s placement
+    (every rank sends its part of v_k to one rank, q - h_i) and combined into
+    it. When N_i is odd, v_0 sits the step out ("the first data vector").
+    After L = ceil(log2 P) steps v_0 is the sum at placement 0: rank i holds
+    part i (a reduce-scatter).
+
+    Knob r (removed distribution steps): the schedules S_j for j in
+    J_r = {0 .. N_{L-r} - 1} run together; S_j is S_0 with every vector's
+    placement shifted by j and the same communication operators. Reading: J_r
+    is the smallest result set that lets the distribution skip r steps; it
+    has 2^r members when N_{L-r} = 2^r. Identical vectors (same placement, same
+    combination tree) are sent and combined once; distinct vectors on one
+    placement are kept apart (the paper's q* and q').
+
+    Distribution: the reduction steps L-r-1 .. 0 reversed, copying instead of
+    combining: v_k <- v_{k - h_i} moved back (rank q sends to q + h_i).
+    Steps: 2L - r. r = L is the latency-optimal version (no distribution).
+
+    Returns (per-rank outputs (P, B, m), stats dict with step counts and the
+    per-step number of distinct parts sent / combined per rank).
+    """
+    P = xacc.shape[0]
+    L, N, h = _levels(P)
+    if not 0 <= r <= L:
+        raise ValueError(f"knob r must be in [0, {L}]")
+    if group == "cyclic":
+        place = lambda k, j: (k + j) % P  # noqa: E731
+        owner = lambda p, i: (p - i) % P  # placement held by rank p at part i  # noqa: E731
+    elif group == "xor":
+        if P & (P - 1):
+            raise ValueError("the XOR group needs P to be a power of two")
+        place = lambda k, j: k ^ j  # noqa: E731
+        owner = lambda p, i: p ^ i  # noqa: E731
+    else:
+        raise ValueError(group)
+
+    c = -(-n // P) if n else 1
+    part_of = (np.asarray(idx, dtype=np.int64) // c) if n else np.zeros(0, dtype=np.int64)
+    cols = np.arange(len(idx))
+    xt = np.transpose(xacc, (0, 2, 1))  # (P, m, B)
+
+    def diag(j: int):
+        # element at offset e (in part i) comes from rank t_j(i)
+        return xt[place(part_of, j), cols].T if len(idx) else xacc[0, :, :0].copy()
+
+    J = list(range(N[L - r]))
+    sym = Symbolic(P)  # diagonal-level shadow, for dedupe and traffic counts
+    sent_steps, red_steps = [], []
+    vals = {j: [diag(place(k, j)) for k in range(P)] for j in J}
+    syms = {j: [place(k, j) for k in range(P)] for j in J}
+    for i in range(L):
+        sends, reds = set(), set()
+        new_vals, new_syms = {}, {}
+        for j in J:
+            v, s = list(vals[j]), list(syms[j])
+            for k in range(N[i] - h[i], N[i]):
+                sends.add((place(k, j), syms[j][k]))
+                s[k - h[i]] = sym.node(syms[j][k - h[i]], syms[j][k])
+                v[k - h[i]] = alg.op(vals[j][k - h[i]], vals[j][k])
+                reds.add((place(k - h[i], j), s[k - h[i]]))
+            new_vals[j], new_syms[j] = v, s
+        vals, syms = new_vals, new_syms
+        sent_steps.append(len(sends))
+        red_steps.append(len(reds))
+    results = {j: vals[j][0] for j in J}  # result j sits at placement j
+
+    src = {j: j for j in J}
+    copy_steps = []
+    for i in reversed(range(L - r)):
+        for k in range(N[i] - h[i], N[i]):
+            src[k] = src[k - h[i]]
+        copy_steps.append(h[i])
+    out = np.empty_like(xacc)
+    src_of = np.array([src[k] for k in range(P)])
+    for p in range(P):
+        if len(idx):
+            sel = src_of[owner(p, part_of)]
+            for j in J:
+                m = sel == j
+                if m.any():
+                    out[p][:, m] = results[j][:, m]
+    stats = dict(
+        steps=L + (L - r),
+        reduction_sent_parts=sent_steps,
+        reduction_reduced_parts=red_steps,
+        distribution_sent_parts=copy_steps,
+        J=J,
+        src=[src[k] for k in range(P)],
+    )
+    return out, stats
+
+
+# --------------------------------------------------------------------------
+# entry point
+# --------------------------------------------------------------------------
+def allreduce(x: np.ndarray, algo: str, dtype: str, op: str = "sum", knob: int = 0,
+              groups=None, n: int | None = None, idx=None, symbolic: bool = False,
+              return_stats: bool = False):
+    """Replay one Allreduce schedule on the CPU.
+
+    x       (P, m) or (P, B, m): each rank's buffer (B independent instances of
+            length n), restricted to the element offsets ``idx`` (default: all
+            n offsets). int32 / fp32 arrays, bf16 as uint16 bit patterns.
+    algo    one of ALGOS; ``knob`` is r for the generalized algorithm;
+            ``groups`` the AHC group sizes (contiguous ranks).
+    symbolic  ignore the values and return, per rank and offset, the id of the
+            combination tree (leaves = ranks) in ``stats['algebra']``.
+    Returns the per-rank outputs in x's shape (and a stats dict if asked).
+    """
+    x = np.asarray(x)
+    squeeze = x.ndim == 2
+    if squeeze:
+        x = x[:, None, :]
+    P, B, m = x.shape
+    if n is None:
+        n = m
+    idx = np.arange(n, dtype=np.int64) if idx is None else np.asarray(idx, dtype=np.int64)
+    if len(idx) != m:
+        raise ValueError("idx must list one offset per sampled element")
+    if symbolic:
+        alg = Symbolic(P)
+        xacc = np.empty((P, B, m), dtype=object)
+        for p in range(P):
+            xacc[p] = p
+    else:
+        alg = Algebra(dtype, op)
+        xacc = np.stack([alg.load(x[p]) for p in range(P)])
+
+    if P == 1 or n == 0:
+        out, stats = xacc.copy(), dict(steps=0)
+    elif algo in ("generalized", "generalized_xor"):
+        out, stats = _generalized(alg, xacc, n, idx, knob, "cyclic" if algo == "generalized" else "xor")
+    else:
+        net = Net(alg, xacc.copy(), n, idx)
+        if algo == "direct":
+            _direct(net)
+        elif algo == "ring":
+            _ring(net)
+        elif algo == "rh_rd":
+            _rh_rd(net)
+        elif algo == "rd":
+            _rd(net)
+        elif algo == "binomial":
+            _binomial(net)
+        elif algo == "ahc":
+            _ahc(net, list(groups) if groups else [P])
+        else:
+            raise ValueError(f"unknown algorithm {algo!r}")
+        out, stats = net.buf, net.stats()
+    if symbolic:
+        stats["algebra"] = alg
+        res = out
+    else:
+        res = np.stack([alg.store(out[p]) for p in range(P)])
+    if squeeze:
+        res = res[:, 0, :]
+    return (res, stats) if return_stats else res
