@@ -1,0 +1,45 @@
+"""MI355X-native Allreduce schedules: Python side of libar_mi355x.so.
+
+``_ar`` is the ctypes binding of include/ar.h (same function names). The
+helpers below only marshal torch tensors into those calls; the product path
+has no CPU fallback and fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+from . import _ar
+from ._ar import (  # noqa: F401
+    ALGOS, DTYPES, EXECS, OPS, Algo, ArError, Dtype, Exec, Op, Schedule, Status, ar_allreduce,
+    ar_allreduce_ex, ar_last_error_message, ar_last_hip_error, ar_schedule_build, ar_status_string,
+    ar_table_check, ar_version, ar_workspace_bytes, make_call,
+)
+
+_TORCH_DTYPE = {"int32": "int32", "fp32": "float32", "bf16": "bfloat16"}
+
+
+def allreduce(tensors, algo="ring", op="sum", knob=0, exec="fused", batch=1, groups=None,
+              stream=None, workspace=None):
+    """In-place Allreduce over a list of P equally sized CUDA tensors (one per rank).
+
+    dtype comes from the tensors (int32, float32 or bfloat16); each tensor holds
+    ``batch`` contiguous instances. ``stream`` defaults to torch's current stream.
+    """
+    import torch
+
+    P = len(tensors)
+    t0 = tensors[0]
+    rev = {v: k for k, v in _TORCH_DTYPE.items()}
+    dname = str(t0.dtype).replace("torch.", "")
+    if dname not in rev:
+        raise ArError(Status.AR_INVALID_ARGUMENT, f"unsupported tensor dtype {t0.dtype}")
+    for t in tensors:
+        if t.dtype != t0.dtype or t.numel() != t0.numel() or not t.is_cuda or not t.is_contiguous():
+            raise ArError(Status.AR_INVALID_ARGUMENT, "tensors must be contiguous CUDA tensors of one dtype and size")
+    total = t0.numel()
+    if total % batch:
+        raise ArError(Status.AR_INVALID_ARGUMENT, "tensor size is not a multiple of batch")
+    if stream is None:
+        stream = torch.cuda.current_stream(t0.device)
+    call = make_call(P, total // batch, rev[dname], op, algo, knob, exec, batch, groups,
+                     workspace=workspace, workspace_bytes=(workspace.numel() * workspace.element_size()
+                                                           if workspace is not None else 0))
+    ar_allreduce_ex(tensors, call, stream)

@@ -1,0 +1,210 @@
+// extern "C" entry points declared in include/ar.h.
+#include "../../include/ar.h"
+
+#include <algorithm>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "exec.h"
+#include "sched.h"
+
+static_assert(sizeof(ar_oprec) == sizeof(ar::OpRec), "ar_oprec layout");
+
+namespace {
+
+thread_local std::string t_msg;
+thread_local int32_t t_hip = 0;
+
+ar_status fail(ar_status st, const std::string& m) {
+  t_msg = m;
+  return st;
+}
+
+bool to_spec(const ar_call* c, ar::Spec* s, std::string* err) {
+  if (!c) { *err = "call is NULL"; return false; }
+  s->P = c->P;
+  s->n = c->n;
+  s->batch = c->batch == 0 ? 1 : c->batch;
+  s->dtype = c->dtype;
+  s->op = c->op;
+  s->algo = c->algo;
+  s->knob = (c->algo == AR_GENERALIZED || c->algo == AR_GENERALIZED_XOR) ? c->knob : 0;
+  s->groups.clear();
+  if (c->algo == AR_AHC) {
+    if (c->ngroups < 1 || !c->groups) { *err = "AHC needs ngroups >= 1 and a groups array"; return false; }
+    if (c->ngroups > AR_MAX_RANKS) { *err = "too many AHC groups"; return false; }
+    s->groups.assign(c->groups, c->groups + c->ngroups);
+  }
+  if (c->exec < AR_EXEC_FUSED || c->exec > AR_EXEC_REPLAY) { *err = "unknown exec mode"; return false; }
+  return ar::validate_spec(*s, err);
+}
+
+ar_status check_bufs(void* const* bufs, int P) {
+  if (!bufs) return fail(AR_INVALID_ARGUMENT, "bufs is NULL");
+  std::vector<uintptr_t> v(P);
+  for (int p = 0; p < P; ++p) {
+    if (!bufs[p]) return fail(AR_INVALID_ARGUMENT, "bufs[" + std::to_string(p) + "] is NULL");
+    v[p] = reinterpret_cast<uintptr_t>(bufs[p]);
+  }
+  std::sort(v.begin(), v.end());
+  for (int p = 1; p < P; ++p)
+    if (v[p] == v[p - 1]) return fail(AR_INVALID_ARGUMENT, "two ranks share one buffer");
+  return AR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ar_status_string(ar_status st) {
+  switch (st) {
+    case AR_OK: return "AR_OK";
+    case AR_INVALID_ARGUMENT: return "AR_INVALID_ARGUMENT";
+    case AR_UNSUPPORTED: return "AR_UNSUPPORTED";
+    case AR_WORKSPACE_TOO_SMALL: return "AR_WORKSPACE_TOO_SMALL";
+    case AR_HIP_ERROR: return "AR_HIP_ERROR";
+    case AR_INTERNAL: return "AR_INTERNAL";
+  }
+  return "unknown status";
+}
+
+int32_t ar_last_hip_error(void) { return t_hip; }
+const char* ar_last_error_message(void) { return t_msg.c_str(); }
+const char* ar_version(void) { return "allreduce-schedules-mi355x 0.1 (gfx950)"; }
+
+ar_status ar_allreduce_ex(void* const* bufs, const ar_call* call, void* stream) {
+  std::string err;
+  ar::Spec spec;
+  if (!to_spec(call, &spec, &err)) return fail(AR_INVALID_ARGUMENT, err);
+  ar_status st = check_bufs(bufs, spec.P);
+  if (st != AR_OK) return st;
+  ar::RunResult r = ar::run_allreduce(bufs, spec, call->exec, call->workspace, call->workspace_bytes, stream);
+  t_hip = r.hip_error;
+  if (r.status) return fail(ar_status(r.status), r.message);
+  t_msg.clear();
+  return AR_OK;
+}
+
+ar_status ar_allreduce(void* const* bufs, int32_t P, int64_t n, int32_t dtype, int32_t op, int32_t algo,
+                       int32_t knob, void* stream) {
+  if (algo == AR_AHC) return fail(AR_INVALID_ARGUMENT, "AR_AHC needs group sizes: use ar_allreduce_ex");
+  ar_call c;
+  std::memset(&c, 0, sizeof(c));
+  c.P = P;
+  c.n = n;
+  c.batch = 1;
+  c.dtype = dtype;
+  c.op = op;
+  c.algo = algo;
+  c.knob = knob;
+  c.exec = AR_EXEC_FUSED;
+  return ar_allreduce_ex(bufs, &c, stream);
+}
+
+ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes) {
+  std::string err;
+  ar::Spec spec;
+  if (!bytes) return fail(AR_INVALID_ARGUMENT, "bytes is NULL");
+  if (!to_spec(call, &spec, &err)) return fail(AR_INVALID_ARGUMENT, err);
+  *bytes = 0;
+  if (call->exec != AR_EXEC_LITERAL || spec.P <= 1 || spec.n == 0) return AR_OK;
+  ar::RunResult r = ar::literal_workspace_bytes(spec, bytes);
+  if (r.status) return fail(ar_status(r.status), r.message);
+  return AR_OK;
+}
+
+ar_status ar_schedule_build(const ar_call* call, ar_schedule** out) {
+  std::string err;
+  ar::Spec spec;
+  if (!out) return fail(AR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  if (!to_spec(call, &spec, &err)) return fail(AR_INVALID_ARGUMENT, err);
+  ar::Schedule* s = ar::build_schedule(spec, &err);
+  if (!s) return fail(AR_INTERNAL, err);
+  *out = reinterpret_cast<ar_schedule*>(s);
+  return AR_OK;
+}
+
+void ar_schedule_free(ar_schedule* s) { delete reinterpret_cast<ar::Schedule*>(s); }
+
+ar_status ar_schedule_info_get(const ar_schedule* sh, ar_schedule_info* info) {
+  if (!sh || !info) return fail(AR_INVALID_ARGUMENT, "NULL argument");
+  const ar::Schedule& s = *reinterpret_cast<const ar::Schedule*>(sh);
+  info->steps = s.nsteps;
+  info->slots = s.nslots;
+  info->atoms = s.C;
+  info->single_port = s.single_port ? 1 : 0;
+  info->ops = int64_t(s.ops.size());
+  info->finalize_ops = s.finalize_ops;
+  info->fused_ok = s.fused_ok ? 1 : 0;
+  info->ranges = int32_t(s.ranges.size());
+  info->max_trees = s.max_trees;
+  info->max_need = s.max_need;
+  info->max_leaves = s.max_leaves;
+  info->program_words = int32_t(s.prog.size());
+  return AR_OK;
+}
+
+ar_status ar_schedule_export(const ar_schedule* sh, ar_oprec* ops, size_t cap, size_t* count) {
+  if (!sh) return fail(AR_INVALID_ARGUMENT, "NULL schedule");
+  const ar::Schedule& s = *reinterpret_cast<const ar::Schedule*>(sh);
+  if (count) *count = s.ops.size();
+  if (ops) std::memcpy(ops, s.ops.data(), std::min(cap, s.ops.size()) * sizeof(ar_oprec));
+  return AR_OK;
+}
+
+ar_status ar_schedule_fused_export(const ar_schedule* sh, int64_t* starts, int64_t* lens, int32_t* offsets,
+                                   size_t range_cap, int32_t* words, size_t word_cap, size_t* nranges,
+                                   size_t* nwords) {
+  if (!sh) return fail(AR_INVALID_ARGUMENT, "NULL schedule");
+  const ar::Schedule& s = *reinterpret_cast<const ar::Schedule*>(sh);
+  if (!s.fused_ok) return fail(AR_UNSUPPORTED, "no fused program: " + s.fused_error);
+  if (nranges) *nranges = s.ranges.size();
+  if (nwords) *nwords = s.prog.size();
+  for (size_t r = 0; r < std::min(range_cap, s.ranges.size()); ++r) {
+    if (starts) starts[r] = s.ranges[r].start;
+    if (lens) lens[r] = s.ranges[r].len;
+    if (offsets) offsets[r] = s.ranges[r].prog;
+  }
+  if (words) std::memcpy(words, s.prog.data(), std::min(word_cap, s.prog.size()) * sizeof(int32_t));
+  return AR_OK;
+}
+
+ar_status ar_table_check(int32_t P, int64_t n, int32_t dtype, const ar_oprec* ops, size_t count,
+                         int32_t* single_port) {
+  if (!ops && count) return fail(AR_INVALID_ARGUMENT, "ops is NULL");
+  if (dtype < AR_INT32 || dtype > AR_BF16) return fail(AR_INVALID_ARGUMENT, "unknown dtype");
+  ar::TableCheck tc = ar::check_table(P, n, dtype, reinterpret_cast<const ar::OpRec*>(ops), count);
+  if (single_port) *single_port = tc.single_port ? 1 : 0;
+  if (!tc.ok) return fail(AR_INVALID_ARGUMENT, tc.message);
+  return AR_OK;
+}
+
+ar_status ar_cost_report(const ar_schedule* sh, double alpha, double beta, double gamma, ar_cost* out) {
+  if (!sh || !out) return fail(AR_INVALID_ARGUMENT, "NULL argument");
+  const ar::Schedule& s = *reinterpret_cast<const ar::Schedule*>(sh);
+  ar::CostOut c = ar::cost_walk(s, alpha, beta, gamma);
+  out->steps = c.steps;
+  out->sent_busiest = c.sent_busiest;
+  out->recv_busiest = c.recv_busiest;
+  out->reduced_busiest = c.reduced_busiest;
+  out->sent_total = c.sent_total;
+  out->reduced_total = c.reduced_total;
+  out->max_rank_sent = c.max_rank_sent;
+  out->max_rank_reduced = c.max_rank_reduced;
+  out->predicted_seconds = c.predicted_seconds;
+  out->closed_form_seconds = c.closed_form_seconds;
+  out->literal_hbm_bytes = c.literal_hbm_bytes;
+  out->fused_hbm_bytes = c.fused_hbm_bytes;
+  out->essential_bytes = c.essential_bytes;
+  return AR_OK;
+}
+
+ar_status ar_cost_steps(const ar_schedule* sh, int64_t* sent, int64_t* recv, int64_t* reduced) {
+  if (!sh || !sent || !recv || !reduced) return fail(AR_INVALID_ARGUMENT, "NULL argument");
+  ar::cost_steps(*reinterpret_cast<const ar::Schedule*>(sh), sent, recv, reduced);
+  return AR_OK;
+}
+
+}  // extern "C"

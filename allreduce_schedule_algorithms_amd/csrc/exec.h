@@ -1,0 +1,30 @@
+// Device executor interface (implemented in exec.hip).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "sched.h"
+
+namespace ar {
+
+enum Exec : int32_t { E_FUSED = 0, E_LITERAL = 1, E_REPLAY = 2 };
+
+struct RunResult {
+  int status = 0;     // ar_status value
+  int hip_error = 0;  // hipError_t when status == AR_HIP_ERROR
+  std::string message;
+};
+
+// Enqueue one Allreduce on `stream`. Arguments have been validated.
+RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+// Workspace an AR_EXEC_LITERAL call needs for this spec (builds the schedule).
+RunResult literal_workspace_bytes(const Spec& spec, size_t* bytes);
+
+// Cached host schedule for a spec (shared with the executor's plan cache).
+const Schedule* cached_schedule(const Spec& spec, std::string* err);
+
+}  // namespace ar

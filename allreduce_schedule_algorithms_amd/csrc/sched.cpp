@@ -1,0 +1,981 @@
+// Schedule generators, slot realizer, table checker, fused planner, cost walk.
+#include "sched.h"
+
+#include <algorithm>
+#include <cmath>
+#include <functional>
+#include <memory>
+#include <tuple>
+#include <limits>
+#include <map>
+#include <numeric>
+#include <set>
+#include <sstream>
+#include <unordered_set>
+
+namespace ar {
+
+int ceil_log2(int P) {
+  int L = 0;
+  while ((1 << L) < P) ++L;
+  return L;
+}
+int elt_bytes(int dtype) { return dtype == D_BF16 ? 2 : 4; }
+int acc_bytes(int) { return 4; }
+
+static int pow2_floor(int P) {
+  int p = 1;
+  while (p * 2 <= P) p *= 2;
+  return p;
+}
+
+// Ceil split of [0, n) into C parts (the all-reduce blog page's split():
+// chunk length ceil(n / C), the last parts short or empty).
+static std::vector<std::pair<int64_t, int64_t>> partition(int64_t n, int C) {
+  std::vector<std::pair<int64_t, int64_t>> out(C);
+  int64_t c = C > 0 ? (n + C - 1) / C : 0;
+  for (int k = 0; k < C; ++k) out[k] = {std::min<int64_t>(k * c, n), std::min<int64_t>((k + 1) * c, n)};
+  return out;
+}
+
+static int64_t lcm_of(const std::vector<int>& g) {
+  int64_t l = 1;
+  for (int v : g) {
+    l = l / std::gcd<int64_t>(l, v) * v;
+    if (l > (1 << 20)) return l;
+  }
+  return l;
+}
+
+// ----------------------------------------------------------------------------
+// expression DAG
+// ----------------------------------------------------------------------------
+Exprs::Exprs(int P) : P_(P) {
+  leafmask_.resize(P);
+  for (int p = 0; p < P; ++p) {
+    leafmask_[p].fill(0);
+    leafmask_[p][p / 64] |= uint64_t(1) << (p % 64);
+    full_[p / 64] |= uint64_t(1) << (p % 64);
+  }
+}
+
+int Exprs::combine(int a, int b) {
+  if (a > b) std::swap(a, b);
+  uint64_t key = (uint64_t(uint32_t(a)) << 32) | uint32_t(b);
+  auto it = ids_.find(key);
+  if (it != ids_.end()) return it->second;
+  int id = P_ + int(a_.size());
+  a_.push_back(a);
+  b_.push_back(b);
+  cnt_.push_back(leaves(a) + leaves(b));
+  Mask m;
+  const Mask& ma = mask(a);
+  const Mask& mb = mask(b);
+  for (size_t w = 0; w < m.size(); ++w) m[w] = ma[w] | mb[w];
+  mask_.push_back(m);
+  ids_.emplace(key, id);
+  return id;
+}
+
+bool Exprs::complete(int id) const { return leaves(id) == P_ && mask(id) == full_; }
+
+// ----------------------------------------------------------------------------
+// generators: logical step lists over atoms
+// ----------------------------------------------------------------------------
+struct Logical {
+  int C = 1;
+  std::vector<std::vector<LOp>> steps;
+};
+
+// Helper for schedules in which every rank holds one current value per atom.
+struct BufGen {
+  int P, C;
+  Exprs& ex;
+  Logical& lg;
+  std::vector<int> cur;
+  std::vector<std::pair<int, int>> staged;
+  BufGen(int P_, int C_, Exprs& e, Logical& l) : P(P_), C(C_), ex(e), lg(l), cur(size_t(P_) * C_) {
+    lg.C = C_;
+    for (int p = 0; p < P; ++p)
+      for (int a = 0; a < C; ++a) cur[size_t(p) * C + a] = p;
+  }
+  void begin() { lg.steps.emplace_back(); }
+  void msg(int kind, int src, int dst, int a0, int a1) {
+    for (int a = a0; a < a1; ++a) {
+      int sv = cur[size_t(src) * C + a];
+      int ov = cur[size_t(dst) * C + a];
+      int out = kind == K_REDUCE ? ex.combine(ov, sv) : sv;
+      lg.steps.back().push_back({kind, src, dst, a, sv, kind == K_REDUCE ? ov : -1, out});
+      staged.push_back({dst * C + a, out});
+    }
+  }
+  void end() {
+    for (auto& s : staged) cur[s.first] = s.second;
+    staged.clear();
+  }
+};
+
+// Naive one-root schedule (all-reduce blog page, cost-model section): the root
+// folds ranks 1..P-1 in rank order, one per step, then sends the result back.
+static void gen_direct(int P, Exprs& ex, Logical& lg) {
+  BufGen g(P, 1, ex, lg);
+  for (int s = 1; s < P; ++s) { g.begin(); g.msg(K_REDUCE, s, 0, 0, 1); g.end(); }
+  for (int s = 1; s < P; ++s) { g.begin(); g.msg(K_COPY, 0, s, 0, 1); g.end(); }
+}
+
+// Ring reduce-scatter + all-gather (all-reduce blog page, "The ring
+// algorithm"; generalized-Allreduce paper eqs. (14)-(16)).
+static void gen_ring(int P, Exprs& ex, Logical& lg) {
+  BufGen g(P, P, ex, lg);
+  for (int t = 0; t < P - 1; ++t) {
+    g.begin();
+    for (int r = 0; r < P; ++r) {
+      int k = ((r - t) % P + P) % P;
+      g.msg(K_REDUCE, r, (r + 1) % P, k, k + 1);
+    }
+    g.end();
+  }
+  for (int t = 0; t < P - 1; ++t) {
+    g.begin();
+    for (int r = 0; r < P; ++r) {
+      int k = ((r + 1 - t) % P + P) % P;
+      g.msg(K_COPY, r, (r + 1) % P, k, k + 1);
+    }
+    g.end();
+  }
+}
+
+// Non-power-of-two preparation / finalization (generalized-Allreduce paper,
+// related work): excess rank P'+j hands its buffer to rank j and gets the
+// result back.
+static void fold_in(BufGen& g, int P, int Pp) {
+  if (P == Pp) return;
+  g.begin();
+  for (int j = 0; j < P - Pp; ++j) g.msg(K_REDUCE, Pp + j, j, 0, g.C);
+  g.end();
+}
+static void fold_out(BufGen& g, int P, int Pp) {
+  if (P == Pp) return;
+  g.begin();
+  for (int j = 0; j < P - Pp; ++j) g.msg(K_COPY, j, Pp + j, 0, g.C);
+  g.end();
+}
+
+// Recursive halving reduce-scatter + recursive doubling all-gather over P'
+// parts, partner distance P'/2 first.
+static void gen_rh_rd(int P, Exprs& ex, Logical& lg) {
+  int Pp = pow2_floor(P);
+  int L = ceil_log2(Pp);
+  BufGen g(P, Pp, ex, lg);
+  fold_in(g, P, Pp);
+  for (int s = 0; s < L; ++s) {
+    int d = Pp >> (s + 1);
+    g.begin();
+    for (int p = 0; p < Pp; ++p) {
+      int base = p & ~(2 * d - 1);
+      int give = base + ((p & d) ? 0 : d);
+      g.msg(K_REDUCE, p, p ^ d, give, give + d);
+    }
+    g.end();
+  }
+  for (int s = L - 1; s >= 0; --s) {
+    int d = Pp >> (s + 1);
+    g.begin();
+    for (int p = 0; p < Pp; ++p) {
+      int base = p & ~(d - 1);
+      g.msg(K_COPY, p, p ^ d, base, base + d);
+    }
+    g.end();
+  }
+  fold_out(g, P, Pp);
+}
+
+// Recursive doubling: full-buffer exchange with partner p XOR d, d = P'/2 first.
+static void gen_rd(int P, Exprs& ex, Logical& lg) {
+  int Pp = pow2_floor(P);
+  int L = ceil_log2(Pp);
+  BufGen g(P, 1, ex, lg);
+  fold_in(g, P, Pp);
+  for (int s = 0; s < L; ++s) {
+    int d = Pp >> (s + 1);
+    g.begin();
+    for (int p = 0; p < Pp; ++p) g.msg(K_REDUCE, p ^ d, p, 0, 1);
+    g.end();
+  }
+  fold_out(g, P, Pp);
+}
+
+// Binomial-tree reduce ("Reduction Operator" page) + broadcast as its reverse.
+static void gen_binomial(int P, Exprs& ex, Logical& lg) {
+  int K = ceil_log2(P);
+  BufGen g(P, 1, ex, lg);
+  std::vector<char> active(P, 1);
+  for (int k = 0; k < K; ++k) {
+    int b = 1 << k;
+    g.begin();
+    for (int i = 0; i < P; ++i) {
+      if (!active[i]) continue;
+      if (i & b) active[i] = 0;
+      else if (i + b < P) g.msg(K_REDUCE, i + b, i, 0, 1);
+    }
+    g.end();
+  }
+  for (int k = K - 1; k >= 0; --k) {
+    int b = 1 << k;
+    g.begin();
+    for (int i = 0; i + b < P; i += 2 * b) g.msg(K_COPY, i, i + b, 0, 1);
+    g.end();
+  }
+}
+
+// AHC (HCCL "AHC" page): Lc x G chunks; ring reduce-scatter inside each group,
+// ring Allreduce per piece between the owners ("logical devices with
+// identical IDs") over G equal sub-pieces, ring all-gather inside each group.
+static void gen_ahc(int P, const std::vector<int>& groups, Exprs& ex, Logical& lg) {
+  int G = int(groups.size());
+  int C = int(lcm_of(groups)) * G;
+  BufGen g(P, C, ex, lg);
+  std::vector<int> offs(G, 0), span(G);
+  for (int a = 1; a < G; ++a) offs[a] = offs[a - 1] + groups[a - 1];
+  for (int a = 0; a < G; ++a) span[a] = C / groups[a];
+  int gmax = *std::max_element(groups.begin(), groups.end());
+  for (int t = 0; t < gmax - 1; ++t) {
+    g.begin();
+    for (int a = 0; a < G; ++a) {
+      int ga = groups[a];
+      if (t >= ga - 1) continue;
+      for (int l = 0; l < ga; ++l) {
+        int k = ((l - t) % ga + ga) % ga;
+        g.msg(K_REDUCE, offs[a] + l, offs[a] + (l + 1) % ga, k * span[a], (k + 1) * span[a]);
+      }
+    }
+    g.end();
+  }
+  std::set<int> cuts;
+  for (int a = 0; a < G; ++a)
+    for (int k = 0; k <= groups[a]; ++k) cuts.insert(k * span[a]);
+  std::vector<int> b(cuts.begin(), cuts.end());
+  struct Piece { std::vector<int> owner; std::vector<int> sub; };
+  std::vector<Piece> pieces;
+  for (size_t q = 0; q + 1 < b.size(); ++q) {
+    Piece pc;
+    for (int a = 0; a < G; ++a) {
+      int ka = b[q] / span[a];
+      pc.owner.push_back(offs[a] + ((ka - 1) % groups[a] + groups[a]) % groups[a]);
+    }
+    int w = (b[q + 1] - b[q]) / G;
+    for (int s = 0; s <= G; ++s) pc.sub.push_back(b[q] + s * w);
+    pieces.push_back(pc);
+  }
+  for (int t = 0; t < G - 1; ++t) {
+    g.begin();
+    for (auto& pc : pieces)
+      for (int s = 0; s < G; ++s) {
+        int sp = ((s - t) % G + G) % G;
+        g.msg(K_REDUCE, pc.owner[s], pc.owner[(s + 1) % G], pc.sub[sp], pc.sub[sp + 1]);
+      }
+    g.end();
+  }
+  for (int t = 0; t < G - 1; ++t) {
+    g.begin();
+    for (auto& pc : pieces)
+      for (int s = 0; s < G; ++s) {
+        int sp = ((s + 1 - t) % G + G) % G;
+        g.msg(K_COPY, pc.owner[s], pc.owner[(s + 1) % G], pc.sub[sp], pc.sub[sp + 1]);
+      }
+    g.end();
+  }
+  for (int t = 0; t < gmax - 1; ++t) {
+    g.begin();
+    for (int a = 0; a < G; ++a) {
+      int ga = groups[a];
+      if (t >= ga - 1) continue;
+      for (int l = 0; l < ga; ++l) {
+        int k = ((l + 1 - t) % ga + ga) % ga;
+        g.msg(K_COPY, offs[a] + l, offs[a] + (l + 1) % ga, k * span[a], (k + 1) * span[a]);
+      }
+    }
+    g.end();
+  }
+}
+
+// Generalized Allreduce (generalized-Allreduce paper, bandwidth-optimal,
+// intermediate and latency-optimal sections). Placement j puts part i at rank
+// t_j(i) = i + j mod P (cyclic group) or i XOR j (self-inverse group). The
+// shifted schedules S_j, j < N_{L-r}, run together; an identical vector (same
+// placement, same tree) is sent and combined once.
+static void gen_generalized(int P, int r, bool use_xor, Exprs& ex, Logical& lg) {
+  int L = ceil_log2(P);
+  std::vector<int> N(1, P), h;
+  for (int i = 0; i < L; ++i) N.push_back((N.back() + 1) / 2);
+  for (int i = 0; i < L; ++i) h.push_back(N[i] / 2);
+  auto place = [&](int k, int j) { return use_xor ? (k ^ j) : (k + j) % P; };
+  auto holder = [&](int i, int pl) { return use_xor ? (i ^ pl) : (i + pl) % P; };
+  lg.C = P;
+  int J = N[L - r];
+  // vals[j][k][atom]
+  std::vector<std::vector<std::vector<int>>> vals(J, std::vector<std::vector<int>>(P, std::vector<int>(P)));
+  for (int j = 0; j < J; ++j)
+    for (int k = 0; k < P; ++k)
+      for (int a = 0; a < P; ++a) vals[j][k][a] = holder(a, place(k, j));
+  for (int i = 0; i < L; ++i) {
+    lg.steps.emplace_back();
+    auto& st = lg.steps.back();
+    std::set<std::tuple<int, int, int>> seen;
+    auto nv = vals;
+    for (int j = 0; j < J; ++j)
+      for (int k = N[i] - h[i]; k < N[i]; ++k) {
+        int tgt = k - h[i];
+        int pls = place(k, j), pld = place(tgt, j);
+        for (int a = 0; a < P; ++a) {
+          int sv = vals[j][k][a], ov = vals[j][tgt][a];
+          int out = ex.combine(ov, sv);
+          int src = holder(a, pls), dst = holder(a, pld);
+          if (seen.insert({dst, a, out}).second) st.push_back({K_REDUCE, src, dst, a, sv, ov, out});
+          nv[j][tgt][a] = out;
+        }
+      }
+    vals.swap(nv);
+  }
+  std::vector<std::vector<int>> dist(P);
+  for (int j = 0; j < J; ++j) dist[j] = vals[j][0];  // result j sits at placement j
+  for (int i = L - r - 1; i >= 0; --i) {
+    lg.steps.emplace_back();
+    auto& st = lg.steps.back();
+    for (int k = N[i] - h[i]; k < N[i]; ++k) {
+      int from = k - h[i];
+      dist[k] = dist[from];
+      for (int a = 0; a < P; ++a) {
+        int v = dist[from][a];
+        st.push_back({K_COPY, holder(a, from), holder(a, k), a, v, -1, v});
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// spec validation
+// ----------------------------------------------------------------------------
+bool validate_spec(const Spec& s, std::string* err) {
+  auto fail = [&](const std::string& m) { if (err) *err = m; return false; };
+  if (s.P < 1 || s.P > kMaxRanks) return fail("P must be in [1, 256]");
+  if (s.n < 0) return fail("n must be >= 0");
+  if (s.batch < 1) return fail("batch must be >= 1");
+  if (s.n > 0 && s.batch > (int64_t(1) << 40) / s.n) return fail("batch * n is too large");
+  if (s.dtype < D_INT32 || s.dtype > D_BF16) return fail("unknown dtype");
+  if (s.op < O_SUM || s.op > O_MAX) return fail("unknown op");
+  if (s.algo < 0 || s.algo >= A_NUM_ALGOS) return fail("unknown algorithm");
+  int L = ceil_log2(s.P);
+  if (s.algo == A_GENERALIZED || s.algo == A_GENERALIZED_XOR) {
+    if (s.knob < 0 || s.knob > L) return fail("knob r must be in [0, ceil(log2 P)]");
+    if (s.algo == A_GENERALIZED_XOR && (s.P & (s.P - 1))) return fail("the XOR group needs P to be a power of two");
+  }
+  if (s.algo == A_AHC) {
+    if (s.groups.empty()) return fail("AHC needs group sizes");
+    int sum = 0;
+    for (int g : s.groups) {
+      if (g < 1) return fail("AHC group sizes must be >= 1");
+      sum += g;
+    }
+    if (sum != s.P) return fail("AHC group sizes must sum to P");
+    int64_t C = lcm_of(s.groups) * int64_t(s.groups.size());
+    if (C > 65536) return fail("AHC needs lcm(groups) * G <= 65536 chunks");
+  }
+  return true;
+}
+
+// ----------------------------------------------------------------------------
+// realizer: logical ops -> slot table with snapshot semantics
+// ----------------------------------------------------------------------------
+static inline uint64_t ckey(int cell, int val) { return (uint64_t(uint32_t(cell)) << 32) | uint32_t(val); }
+
+struct Realizer {
+  const Spec& sp;
+  Exprs& ex;
+  const Logical& lg;
+  int P, C;
+  std::vector<std::vector<std::pair<int, int>>> cell;  // (slot, value)
+  std::unordered_map<uint64_t, int> last_read;
+  std::vector<int> final_val;
+  int nslots = 1;
+  std::string err;
+
+  Realizer(const Spec& s, Exprs& e, const Logical& l) : sp(s), ex(e), lg(l), P(s.P), C(l.C) {}
+
+  int slot_of(int c, int v) const {
+    for (auto& sv : cell[c]) if (sv.second == v) return sv.first;
+    return -1;
+  }
+  int value_at(int c, int slot) const {
+    for (auto& sv : cell[c]) if (sv.first == slot) return sv.second;
+    return -1;
+  }
+  void put(int c, int slot, int v) {
+    for (auto& sv : cell[c]) if (sv.first == slot) { sv.second = v; return; }
+    cell[c].push_back({slot, v});
+  }
+
+  bool run(std::vector<LOp>& flat, std::vector<int>& step_of, std::vector<int>& ssl,
+           std::vector<int>& osl, std::vector<int>& dsl, std::vector<int>& pair) {
+    cell.assign(size_t(P) * C, {});
+    for (int p = 0; p < P; ++p)
+      for (int a = 0; a < C; ++a) cell[size_t(p) * C + a].push_back({0, p});
+    // liveness and finals
+    std::vector<std::vector<int>> present(size_t(P) * C);
+    for (int p = 0; p < P; ++p)
+      for (int a = 0; a < C; ++a) present[size_t(p) * C + a].push_back(p);
+    for (size_t s = 0; s < lg.steps.size(); ++s)
+      for (auto& o : lg.steps[s]) {
+        last_read[ckey(o.src * C + o.atom, o.src_val)] = int(s);
+        if (o.kind == K_REDUCE) last_read[ckey(o.dst * C + o.atom, o.own_val)] = int(s);
+        present[size_t(o.dst) * C + o.atom].push_back(o.out_val);
+      }
+    final_val.assign(size_t(P) * C, -1);
+    for (size_t c = 0; c < present.size(); ++c) {
+      int fv = -1;
+      for (int v : present[c]) {
+        if (!ex.complete(v)) continue;
+        if (fv >= 0 && fv != v) { err = "two different complete results at one cell"; return false; }
+        fv = v;
+      }
+      if (fv < 0 && P > 1) { err = "a rank ends without the complete result"; return false; }
+      final_val[c] = fv < 0 ? int(c / C) : fv;
+    }
+    const bool bf16 = sp.dtype == D_BF16;
+    for (size_t s = 0; s < lg.steps.size(); ++s) {
+      const auto& st = lg.steps[s];
+      size_t base = flat.size();
+      std::unordered_map<uint64_t, std::vector<int>> readers;
+      std::map<std::tuple<int, int, int>, int> by_link;  // (src, dst, atom) -> op
+      for (size_t i = 0; i < st.size(); ++i) {
+        const LOp& o = st[i];
+        readers[ckey(o.src * C + o.atom, o.src_val)].push_back(int(i));
+        if (o.kind == K_REDUCE) readers[ckey(o.dst * C + o.atom, o.own_val)].push_back(int(i));
+        if (o.kind == K_REDUCE) by_link[{o.src, o.dst, o.atom}] = int(i);
+      }
+      std::vector<int> partner(st.size(), -1);
+      for (size_t i = 0; i < st.size(); ++i) {
+        const LOp& o = st[i];
+        if (o.kind != K_REDUCE) continue;
+        auto it = by_link.find({o.dst, o.src, o.atom});
+        if (it == by_link.end()) continue;
+        const LOp& q = st[it->second];
+        if (q.own_val == o.src_val && q.src_val == o.own_val) partner[i] = it->second;
+      }
+      std::unordered_set<uint64_t> written;
+      std::vector<int> jointly(st.size(), 0);
+      for (size_t i = 0; i < st.size(); ++i) {
+        const LOp& o = st[i];
+        int sc = o.src * C + o.atom, dc = o.dst * C + o.atom;
+        int s_sl = slot_of(sc, o.src_val);
+        int o_sl = o.kind == K_REDUCE ? slot_of(dc, o.own_val) : -1;
+        if (s_sl < 0 || (o.kind == K_REDUCE && o_sl < 0)) { err = "operand not present (generator bug)"; return false; }
+        if (slot_of(dc, o.out_val) >= 0) { err = "destination already holds the value"; return false; }
+        bool used_pair = false;
+        auto ok = [&](int sl) {
+          used_pair = false;
+          if (bf16 && sl == 0 && !ex.complete(o.out_val)) return false;
+          if (written.count(ckey(dc, sl))) return false;
+          int v = value_at(dc, sl);
+          if (v < 0) return true;
+          if (v == final_val[dc]) return false;
+          auto it = last_read.find(ckey(dc, v));
+          int lr = it == last_read.end() ? -1 : it->second;
+          if (lr > int(s)) return false;
+          if (lr == int(s)) {
+            for (int rd : readers[ckey(dc, v)]) {
+              if (rd == int(i)) continue;
+              if (rd == partner[i]) { used_pair = true; continue; }
+              return false;
+            }
+          }
+          return true;
+        };
+        int chosen = -1;
+        std::vector<int> cand;
+        if (o.out_val == final_val[dc]) cand.push_back(0);
+        if (o_sl >= 0) cand.push_back(o_sl);
+        for (int sl = 0; sl < 64; ++sl) cand.push_back(sl);
+        bool pairx = false;
+        for (int sl : cand) if (ok(sl)) { chosen = sl; pairx = used_pair; break; }
+        if (chosen < 0) { err = "no free slot"; return false; }
+        written.insert(ckey(dc, chosen));
+        nslots = std::max(nslots, chosen + 1);
+        if (pairx) { jointly[i] = 1; jointly[partner[i]] = 1; }
+        flat.push_back(o);
+        step_of.push_back(int(s));
+        ssl.push_back(s_sl);
+        osl.push_back(o_sl);
+        dsl.push_back(chosen);
+        pair.push_back(-1);
+      }
+      for (size_t i = 0; i < st.size(); ++i)
+        if (jointly[i]) pair[base + i] = int(base) + partner[i];
+      for (size_t i = 0; i < st.size(); ++i) put(st[i].dst * C + st[i].atom, dsl[base + i], st[i].out_val);
+    }
+    return true;
+  }
+};
+
+// ----------------------------------------------------------------------------
+// table checker (any table, including corrupted ones)
+// ----------------------------------------------------------------------------
+TableCheck check_table(int P, int64_t n, int dtype, const OpRec* ops, size_t count) {
+  TableCheck tc;
+  auto fail = [&](const std::string& m) { tc.ok = false; tc.message = m; return tc; };
+  if (P < 1 || P > kMaxRanks) return fail("bad P");
+  int nslots = 1;
+  for (size_t i = 0; i < count; ++i) {
+    const OpRec& o = ops[i];
+    if (o.kind < K_REDUCE || o.kind > K_MOVE) return fail("bad kind at op " + std::to_string(i));
+    if (o.src_rank < 0 || o.src_rank >= P || o.dst_rank < 0 || o.dst_rank >= P) return fail("bad rank at op " + std::to_string(i));
+    if (o.src_slot < 0 || o.dst_slot < 0 || o.src_slot > 63 || o.dst_slot > 63) return fail("bad slot at op " + std::to_string(i));
+    if (o.kind == K_REDUCE && (o.own_slot < 0 || o.own_slot > 63)) return fail("bad own slot at op " + std::to_string(i));
+    if (o.offset < 0 || o.length < 0 || o.offset + o.length > n) return fail("range outside the buffer at op " + std::to_string(i));
+    if ((o.kind == K_MOVE) != (o.src_rank == o.dst_rank)) return fail("only a MOVE stays on one rank (op " + std::to_string(i) + ")");
+    if (i && o.step < ops[i - 1].step) return fail("ops not sorted by step");
+    if (o.pair >= 0 && (size_t(o.pair) >= count || ops[o.pair].pair != int32_t(i) || ops[o.pair].step != o.step))
+      return fail("inconsistent pair at op " + std::to_string(i));
+    nslots = std::max({nslots, o.src_slot + 1, o.dst_slot + 1, o.own_slot + 1});
+  }
+  tc.nslots = nslots;
+  // hazards per step
+  size_t i0 = 0;
+  while (i0 < count) {
+    size_t i1 = i0;
+    while (i1 < count && ops[i1].step == ops[i0].step) ++i1;
+    struct Iv { int64_t lo, hi; int grp; bool w; };
+    std::map<std::pair<int, int>, std::vector<Iv>> acc;
+    std::map<int, std::set<int>> dests, srcs;
+    for (size_t i = i0; i < i1; ++i) {
+      const OpRec& o = ops[i];
+      if (o.length == 0) continue;
+      int grp = o.pair >= 0 ? std::min<int>(int(i), o.pair) : int(i);
+      acc[{o.src_rank, o.src_slot}].push_back({o.offset, o.offset + o.length, grp, false});
+      if (o.kind == K_REDUCE) acc[{o.dst_rank, o.own_slot}].push_back({o.offset, o.offset + o.length, grp, false});
+      acc[{o.dst_rank, o.dst_slot}].push_back({o.offset, o.offset + o.length, grp, true});
+      if (o.kind != K_MOVE) { dests[o.src_rank].insert(o.dst_rank); srcs[o.dst_rank].insert(o.src_rank); }
+    }
+    for (auto& kv : acc) {
+      auto& v = kv.second;
+      std::sort(v.begin(), v.end(), [](const Iv& a, const Iv& b) { return a.lo < b.lo; });
+      for (size_t a = 0; a < v.size(); ++a)
+        for (size_t b = a + 1; b < v.size() && v[b].lo < v[a].hi; ++b) {
+          if (v[a].grp == v[b].grp) continue;
+          if (v[a].w || v[b].w) {
+            std::ostringstream m;
+            m << "step " << ops[i0].step << ": " << (v[a].w && v[b].w ? "two writes" : "a write and a read")
+              << " of rank " << kv.first.first << " slot " << kv.first.second << " overlap";
+            return fail(m.str());
+          }
+        }
+    }
+    for (auto& kv : dests) if (kv.second.size() > 1) tc.single_port = false;
+    for (auto& kv : srcs) if (kv.second.size() > 1) tc.single_port = false;
+    i0 = i1;
+  }
+  // symbolic replay over elementary intervals
+  std::vector<int64_t> cuts = {0, n};
+  for (size_t i = 0; i < count; ++i) { cuts.push_back(ops[i].offset); cuts.push_back(ops[i].offset + ops[i].length); }
+  std::sort(cuts.begin(), cuts.end());
+  cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+  Exprs ex(P);
+  for (size_t q = 0; q + 1 < cuts.size(); ++q) {
+    int64_t lo = cuts[q], hi = cuts[q + 1];
+    if (hi <= lo) continue;
+    std::vector<int> val(size_t(P) * nslots, -1);
+    std::vector<char> rnd(size_t(P) * nslots, 0);
+    for (int p = 0; p < P; ++p) val[size_t(p) * nslots] = p;
+    size_t j0 = 0;
+    while (j0 < count) {
+      size_t j1 = j0;
+      while (j1 < count && ops[j1].step == ops[j0].step) ++j1;
+      std::vector<std::tuple<size_t, int, char>> upd;
+      for (size_t j = j0; j < j1; ++j) {
+        const OpRec& o = ops[j];
+        if (o.offset > lo || o.offset + o.length < hi) {
+          if (o.offset < hi && o.offset + o.length > lo) return fail("op boundary inside an interval");
+          continue;
+        }
+        size_t si = size_t(o.src_rank) * nslots + o.src_slot, di = size_t(o.dst_rank) * nslots + o.dst_slot;
+        int sv = val[si];
+        if (sv < 0) return fail("op " + std::to_string(j) + " reads an empty slot");
+        int out;
+        char r = rnd[si];
+        if (o.kind == K_REDUCE) {
+          size_t oi = size_t(o.dst_rank) * nslots + o.own_slot;
+          int ov = val[oi];
+          if (ov < 0) return fail("op " + std::to_string(j) + " reads an empty own slot");
+          if (dtype == D_BF16 && (rnd[si] || rnd[oi])) return fail("a rounded bf16 value is combined again");
+          out = ex.combine(ov, sv);
+          r = 0;
+        } else {
+          out = sv;
+        }
+        if (dtype == D_BF16 && o.dst_slot == 0) {
+          if (!ex.complete(out)) return fail("an incomplete bf16 partial is stored in the caller's buffer");
+          r = 1;
+        }
+        upd.push_back({di, out, r});
+      }
+      for (auto& u : upd) { val[std::get<0>(u)] = std::get<1>(u); rnd[std::get<0>(u)] = std::get<2>(u); }
+      j0 = j1;
+    }
+    for (int p = 0; p < P; ++p) {
+      int v = val[size_t(p) * nslots];
+      if (P > 1 && !ex.complete(v)) {
+        std::ostringstream m;
+        m << "rank " << p << " does not hold the complete result for elements [" << lo << ", " << hi << ")";
+        return fail(m.str());
+      }
+    }
+  }
+  tc.ok = true;
+  return tc;
+}
+
+// ----------------------------------------------------------------------------
+// fused replay planner
+// ----------------------------------------------------------------------------
+static bool plan_fused(Schedule& s, std::string* err) {
+  const int P = s.spec.P;
+  const int S = s.nslots;
+  s.prog.clear();
+  s.ranges.clear();
+  if (P == 1 || s.spec.n == 0) { s.fused_ok = true; return true; }
+  std::vector<std::vector<int>> by_atom(s.C);
+  // map element offsets back to atoms
+  std::vector<int64_t> starts(s.C);
+  for (int a = 0; a < s.C; ++a) starts[a] = s.atoms[a].first;
+  for (size_t i = 0; i < s.ops.size(); ++i) {
+    const OpRec& o = s.ops[i];
+    if (o.length == 0) continue;
+    // atoms tile [0, n) in order; find the first atom starting at the op's offset
+    int a = int(std::lower_bound(starts.begin(), starts.end(), o.offset) - starts.begin());
+    for (; a < s.C && s.atoms[a].first < o.offset + o.length; ++a) {
+      if (s.atoms[a].second <= s.atoms[a].first) continue;
+      if (s.atoms[a].first >= o.offset && s.atoms[a].second <= o.offset + o.length) by_atom[a].push_back(int(i));
+    }
+  }
+  Exprs ex(P);
+  std::unordered_map<int, int> need_memo;
+  std::function<int(int)> need = [&](int id) -> int {
+    if (ex.is_leaf(id)) return 1;
+    auto it = need_memo.find(id);
+    if (it != need_memo.end()) return it->second;
+    int a = need(ex.left(id)), b = need(ex.right(id));
+    int r = a == b ? a + 1 : std::max(a, b);
+    need_memo[id] = r;
+    return r;
+  };
+  std::vector<int32_t> last_words;
+  for (int a = 0; a < s.C; ++a) {
+    int64_t lo = s.atoms[a].first, hi = s.atoms[a].second;
+    if (hi <= lo) continue;
+    std::vector<int> val(size_t(P) * S, -1);
+    std::vector<char> rnd(size_t(P) * S, 0);
+    for (int p = 0; p < P; ++p) val[size_t(p) * S] = p;
+    const auto& lst = by_atom[a];
+    size_t j0 = 0;
+    while (j0 < lst.size()) {
+      size_t j1 = j0;
+      while (j1 < lst.size() && s.ops[lst[j1]].step == s.ops[lst[j0]].step) ++j1;
+      std::vector<std::tuple<size_t, int, char>> upd;
+      for (size_t j = j0; j < j1; ++j) {
+        const OpRec& o = s.ops[lst[j]];
+        size_t si = size_t(o.src_rank) * S + o.src_slot, di = size_t(o.dst_rank) * S + o.dst_slot;
+        int out = val[si];
+        char r = rnd[si];
+        if (o.kind == K_REDUCE) {
+          size_t oi = size_t(o.dst_rank) * S + o.own_slot;
+          if (rnd[si] || rnd[oi]) { *err = "a rounded value is combined again"; return false; }
+          out = ex.combine(val[oi], val[si]);
+          r = 0;
+        }
+        if (s.spec.dtype == D_BF16 && o.dst_slot == 0 && !ex.is_leaf(out)) r = 1;
+        upd.push_back({di, out, r});
+      }
+      for (auto& u : upd) { val[std::get<0>(u)] = std::get<1>(u); rnd[std::get<0>(u)] = std::get<2>(u); }
+      j0 = j1;
+    }
+    // distinct final trees and their output ranks
+    std::vector<int> roots;
+    std::vector<std::vector<int>> outs;
+    for (int p = 0; p < P; ++p) {
+      int v = val[size_t(p) * S];
+      if (!ex.complete(v)) { *err = "fused planner: incomplete result"; return false; }
+      auto it = std::find(roots.begin(), roots.end(), v);
+      if (it == roots.end()) { roots.push_back(v); outs.push_back({p}); }
+      else outs[it - roots.begin()].push_back(p);
+    }
+    std::vector<int32_t> words;
+    words.push_back(int32_t(roots.size()));
+    int range_need = 0;
+    for (size_t t = 0; t < roots.size(); ++t) {
+      // postfix, deeper-need child first (Sethi-Ullman order keeps the stack at need(root))
+      std::vector<int> leaves, ncomb;
+      std::vector<std::pair<int, int>> stack = {{roots[t], 0}};
+      while (!stack.empty()) {
+        auto [id, state] = stack.back();
+        stack.pop_back();
+        if (ex.is_leaf(id)) { leaves.push_back(id); ncomb.push_back(0); continue; }
+        if (state == 0) {
+          int l = ex.left(id), r = ex.right(id);
+          int first = need(l) >= need(r) ? l : r, second = first == l ? r : l;
+          stack.push_back({id, 1});
+          stack.push_back({second, 0});
+          stack.push_back({first, 0});
+        } else {
+          ncomb.back() += 1;
+        }
+      }
+      int nd = need(roots[t]);
+      range_need = std::max(range_need, nd);
+      words.push_back(int32_t(leaves.size()));
+      words.push_back(int32_t(outs[t].size()));
+      for (int v : leaves) words.push_back(v);
+      for (int v : ncomb) words.push_back(v);
+      for (int v : outs[t]) words.push_back(v);
+      s.max_leaves = std::max<int>(s.max_leaves, int(leaves.size()));
+    }
+    s.max_trees = std::max<int>(s.max_trees, int(roots.size()));
+    s.max_need = std::max(s.max_need, range_need);
+    if (!s.ranges.empty() && s.ranges.back().start + s.ranges.back().len == lo && words == last_words) {
+      s.ranges.back().len += hi - lo;
+    } else {
+      FusedRange fr;
+      fr.start = lo;
+      fr.len = hi - lo;
+      fr.prog = int32_t(s.prog.size());
+      fr.ntrees = int32_t(roots.size());
+      fr.need = range_need;
+      s.prog.insert(s.prog.end(), words.begin(), words.end());
+      s.ranges.push_back(fr);
+      last_words = words;
+    }
+  }
+  s.fused_ok = true;
+  return true;
+}
+
+// ----------------------------------------------------------------------------
+// build
+// ----------------------------------------------------------------------------
+Schedule* build_schedule(const Spec& spec, std::string* err) {
+  if (!validate_spec(spec, err)) return nullptr;
+  const int P = spec.P;
+  Exprs ex(P);
+  Logical lg;
+  if (P > 1) {
+    switch (spec.algo) {
+      case A_DIRECT: gen_direct(P, ex, lg); break;
+      case A_RING: gen_ring(P, ex, lg); break;
+      case A_RH_RD: gen_rh_rd(P, ex, lg); break;
+      case A_RD: gen_rd(P, ex, lg); break;
+      case A_BINOMIAL: gen_binomial(P, ex, lg); break;
+      case A_GENERALIZED: gen_generalized(P, spec.knob, false, ex, lg); break;
+      case A_GENERALIZED_XOR: gen_generalized(P, spec.knob, true, ex, lg); break;
+      case A_AHC: gen_ahc(P, spec.groups, ex, lg); break;
+      default: if (err) *err = "unknown algorithm"; return nullptr;
+    }
+  }
+  auto s = std::make_unique<Schedule>();
+  s->spec = spec;
+  s->nsteps = int(lg.steps.size());
+  s->C = lg.C;
+  s->atoms = partition(spec.n, lg.C);
+  std::vector<LOp> flat;
+  std::vector<int> step_of, ssl, osl, dsl, pair;
+  Realizer rz(spec, ex, lg);
+  if (P > 1 && !rz.run(flat, step_of, ssl, osl, dsl, pair)) {
+    if (err) *err = "schedule realization failed: " + rz.err;
+    return nullptr;
+  }
+  s->nslots = rz.nslots;
+  // export: merge consecutive atoms of identical unpaired ops, drop empty ranges
+  std::vector<int> rec_of(flat.size(), -1);
+  for (size_t i = 0; i < flat.size(); ++i) {
+    const LOp& o = flat[i];
+    int64_t lo = s->atoms[o.atom].first, hi = s->atoms[o.atom].second;
+    if (hi <= lo) continue;
+    if (pair[i] < 0 && !s->ops.empty() && i > 0 && rec_of[i - 1] == int(s->ops.size()) - 1) {
+      OpRec& last = s->ops.back();
+      const LOp& q = flat[i - 1];
+      if (last.pair < 0 && pair[i - 1] < 0 && last.step == step_of[i] && q.kind == o.kind && q.src == o.src &&
+          q.dst == o.dst && q.atom + 1 == o.atom && last.src_slot == ssl[i] && last.dst_slot == dsl[i] &&
+          last.own_slot == osl[i] && last.offset + last.length == lo) {
+        last.length += hi - lo;
+        rec_of[i] = int(s->ops.size()) - 1;
+        continue;
+      }
+    }
+    OpRec r{step_of[i], o.kind, o.src, ssl[i], o.dst, dsl[i], osl[i], -1, lo, hi - lo};
+    rec_of[i] = int(s->ops.size());
+    s->ops.push_back(r);
+  }
+  for (size_t i = 0; i < flat.size(); ++i)
+    if (pair[i] >= 0 && rec_of[i] >= 0) s->ops[rec_of[i]].pair = rec_of[pair[i]];
+  // finalize moves: bring each final value into slot 0
+  if (P > 1) {
+    for (int p = 0; p < P; ++p) {
+      for (int a = 0; a < s->C; ++a) {
+        int c = p * s->C + a;
+        int sl = rz.slot_of(c, rz.final_val[c]);
+        int64_t lo = s->atoms[a].first, hi = s->atoms[a].second;
+        if (sl <= 0 || hi <= lo) continue;
+        if (!s->ops.empty()) {
+          OpRec& last = s->ops.back();
+          if (last.kind == K_MOVE && last.src_rank == p && last.src_slot == sl && last.offset + last.length == lo) {
+            last.length += hi - lo;
+            continue;
+          }
+        }
+        s->ops.push_back({s->nsteps, K_MOVE, p, sl, p, 0, -1, -1, lo, hi - lo});
+        s->finalize_ops++;
+      }
+    }
+  }
+  s->steps_begin.assign(s->nsteps + 2, int32_t(s->ops.size()));
+  for (int st = s->nsteps + 1; st >= 0; --st) {
+    // first op with step >= st
+    auto it = std::lower_bound(s->ops.begin(), s->ops.end(), st,
+                               [](const OpRec& o, int v) { return o.step < v; });
+    s->steps_begin[st] = int32_t(it - s->ops.begin());
+  }
+  TableCheck tc = check_table(P, spec.n, spec.dtype, s->ops.data(), s->ops.size());
+  if (!tc.ok) {
+    if (err) *err = "internal: generated table fails its check: " + tc.message;
+    return nullptr;
+  }
+  s->single_port = tc.single_port;
+  std::string ferr;
+  if (!plan_fused(*s, &ferr)) {
+    s->fused_ok = false;
+    s->fused_error = ferr;
+  }
+  return s.release();
+}
+
+// ----------------------------------------------------------------------------
+// cost walk
+// ----------------------------------------------------------------------------
+void cost_steps(const Schedule& s, int64_t* sent, int64_t* recv, int64_t* reduced) {
+  // A message is what crosses a link: ops of one step that read the same source
+  // range of one rank for the same destination rank carry the same data (one
+  // received vector combined into two different partials), so it is counted once.
+  const int P = s.spec.P;
+  std::fill(sent, sent + size_t(s.nsteps) * P, 0);
+  std::fill(recv, recv + size_t(s.nsteps) * P, 0);
+  std::fill(reduced, reduced + size_t(s.nsteps) * P, 0);
+  std::set<std::tuple<int, int, int, int, int64_t, int64_t>> msgs;
+  for (const OpRec& o : s.ops) {
+    if (o.kind == K_MOVE || o.step >= s.nsteps) continue;
+    if (msgs.insert({o.step, o.src_rank, o.src_slot, o.dst_rank, o.offset, o.length}).second) {
+      sent[size_t(o.step) * P + o.src_rank] += o.length;
+      recv[size_t(o.step) * P + o.dst_rank] += o.length;
+    }
+    if (o.kind == K_REDUCE) reduced[size_t(o.step) * P + o.dst_rank] += o.length;
+  }
+}
+
+static double closed_form(const Schedule& s, double m, double alpha, double beta, double gamma) {
+  const int P = s.spec.P;
+  if (P <= 1) return 0.0;
+  const int L = ceil_log2(P);
+  const double u = m / P;
+  const int Pp = pow2_floor(P);
+  const int Lp = ceil_log2(Pp);
+  const double fold = P == Pp ? 0.0 : 2 * alpha + 2 * m * beta + m * gamma;
+  switch (s.spec.algo) {
+    case A_DIRECT:  // root receives and sends (P-1) m one message per step
+      return 2 * (P - 1) * (alpha + m * beta) + (P - 1) * m * gamma;
+    case A_RING:  // eqs. (15)-(16)
+      return 2 * (P - 1) * alpha + 2 * (P - 1) * u * beta + (P - 1) * u * gamma;
+    case A_RH_RD: {
+      double up = m / Pp;
+      return fold + 2 * Lp * alpha + 2 * (Pp - 1) * up * beta + (Pp - 1) * up * gamma;
+    }
+    case A_RD:
+      return fold + Lp * (alpha + m * beta + m * gamma);
+    case A_BINOMIAL:
+      return 2 * L * (alpha + m * beta) + L * m * gamma;
+    case A_GENERALIZED:
+    case A_GENERALIZED_XOR: {
+      int r = s.spec.knob;
+      if (r >= L)  // latency-optimal: all vectors each step; worst-case combinations (2L-2) m
+        return L * alpha + L * m * beta + (2 * L - 2) * m * gamma;
+      double extra = double((1 << r) - 1);
+      return (2 * L - r) * alpha + (2 * (P - 1) + extra * L) * u * beta + ((P - 1) + extra * (2 * L - 2)) * u * gamma;
+    }
+    default:
+      return std::numeric_limits<double>::quiet_NaN();  // AHC: the page's formula is truncated
+  }
+}
+
+CostOut cost_walk(const Schedule& s, double alpha, double beta, double gamma) {
+  CostOut c{};
+  const int P = s.spec.P;
+  const double elt = elt_bytes(s.spec.dtype);
+  const double batch = double(s.spec.batch);
+  c.steps = s.nsteps;
+  std::vector<int64_t> sent(size_t(s.nsteps) * P), recv(size_t(s.nsteps) * P), red(size_t(s.nsteps) * P);
+  if (s.nsteps) cost_steps(s, sent.data(), recv.data(), red.data());
+  std::vector<int64_t> rank_sent(P, 0), rank_red(P, 0);
+  double t = 0;
+  for (int st = 0; st < s.nsteps; ++st) {
+    int64_t ms = 0, mr = 0, md = 0;
+    for (int p = 0; p < P; ++p) {
+      int64_t a = sent[size_t(st) * P + p], b = recv[size_t(st) * P + p], d = red[size_t(st) * P + p];
+      ms = std::max(ms, a);
+      mr = std::max(mr, b);
+      md = std::max(md, d);
+      c.sent_total += a;
+      c.reduced_total += d;
+      rank_sent[p] += a;
+      rank_red[p] += d;
+    }
+    c.sent_busiest += ms;
+    c.recv_busiest += mr;
+    c.reduced_busiest += md;
+    t += alpha + double(std::max(ms, mr)) * batch * elt * beta + double(md) * batch * elt * gamma;
+  }
+  c.max_rank_sent = P ? *std::max_element(rank_sent.begin(), rank_sent.end()) : 0;
+  c.max_rank_reduced = P ? *std::max_element(rank_red.begin(), rank_red.end()) : 0;
+  c.predicted_seconds = t;
+  double m = double(s.spec.n) * batch * elt;
+  c.closed_form_seconds = closed_form(s, m, alpha, beta, gamma);
+  // bytes through HBM
+  auto sz = [&](int slot) { return slot == 0 ? elt : double(acc_bytes(s.spec.dtype)); };
+  double lit = 0;
+  for (size_t i = 0; i < s.ops.size(); ++i) {
+    const OpRec& o = s.ops[i];
+    double len = double(o.length) * batch;
+    if (o.kind == K_REDUCE) {
+      if (o.pair >= 0) {
+        if (size_t(o.pair) < i) continue;  // the partner's bytes are counted with it
+        const OpRec& q = s.ops[o.pair];
+        lit += len * (sz(o.src_slot) + sz(o.own_slot) + sz(o.dst_slot) + sz(q.dst_slot));
+      } else {
+        lit += len * (sz(o.src_slot) + sz(o.own_slot) + sz(o.dst_slot));
+      }
+    } else {
+      lit += len * (sz(o.src_slot) + sz(o.dst_slot));
+    }
+  }
+  c.literal_hbm_bytes = lit;
+  double fz = 0;
+  for (const FusedRange& r : s.ranges) {
+    const int32_t* w = s.prog.data() + r.prog;
+    int nt = *w++;
+    for (int t2 = 0; t2 < nt; ++t2) {
+      int nl = w[0], no = w[1];
+      fz += double(r.len) * batch * elt * (nl + no);
+      w += 2 + 2 * nl + no;
+    }
+  }
+  c.fused_hbm_bytes = fz;
+  c.essential_bytes = 2.0 * P * double(s.spec.n) * batch * elt;
+  return c;
+}
+
+}  // namespace ar

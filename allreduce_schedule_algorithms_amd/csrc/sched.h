@@ -1,0 +1,145 @@
+// Host schedule layer: step-table generators for every Allreduce schedule,
+// slot realization with snapshot semantics, a hazard / port checker, the
+// fused per-element replay planner and the alpha-beta-gamma cost walk.
+//
+// A schedule is a list of steps; a step is a set of operations that all read
+// the state from before the step. An operation moves a range of elements
+// from (src rank, src slot) to (dst rank, dst slot), either combining it with
+// the destination rank's own operand (REDUCE) or overwriting (COPY). Every
+// operation touches the same element offsets in both ranks: the rows of the
+// generalized-Allreduce paper's data matrix are "data elements with the same
+// index number", and ring and AHC chunks are cut at the same offsets on every
+// device. Slot 0 of a rank is the caller's buffer; slots >= 1 are workspace
+// buffers of the accumulation type.
+#pragma once
+
+#include <array>
+#include <cstdint>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+namespace ar {
+
+enum Kind : int32_t { K_REDUCE = 0, K_COPY = 1, K_MOVE = 2 };
+enum Algo : int32_t {
+  A_DIRECT = 0, A_RING = 1, A_RH_RD = 2, A_RD = 3, A_BINOMIAL = 4,
+  A_GENERALIZED = 5, A_GENERALIZED_XOR = 6, A_AHC = 7, A_NUM_ALGOS = 8
+};
+enum Dtype : int32_t { D_INT32 = 0, D_FP32 = 1, D_BF16 = 2 };
+enum Op : int32_t { O_SUM = 0, O_MAX = 1 };
+
+constexpr int kMaxRanks = 256;
+
+struct Spec {
+  int P = 0;
+  int64_t n = 0;       // elements per instance
+  int64_t batch = 1;   // instances per rank buffer, contiguous (instance b at b * n)
+  int dtype = D_FP32;
+  int op = O_SUM;
+  int algo = A_RING;
+  int knob = 0;
+  std::vector<int> groups;  // AHC group sizes (contiguous ranks)
+};
+
+// Hash-consed commutative expression DAG over rank leaves 0..P-1.
+class Exprs {
+ public:
+  explicit Exprs(int P);
+  int combine(int a, int b);
+  bool is_leaf(int id) const { return id < P_; }
+  int left(int id) const { return a_[id - P_]; }
+  int right(int id) const { return b_[id - P_]; }
+  bool complete(int id) const;   // every rank exactly once
+  int leaves(int id) const { return id < P_ ? 1 : cnt_[id - P_]; }
+  int P() const { return P_; }
+
+ private:
+  using Mask = std::array<uint64_t, kMaxRanks / 64>;
+  const Mask& mask(int id) const { return id < P_ ? leafmask_[id] : mask_[id - P_]; }
+  int P_;
+  std::vector<int> a_, b_, cnt_;
+  std::vector<Mask> mask_;
+  std::vector<Mask> leafmask_;
+  Mask full_{};
+  std::unordered_map<uint64_t, int> ids_;
+};
+
+// One logical operation on one atom (chunk) of the algorithm's partition.
+struct LOp {
+  int kind, src, dst, atom;
+  int src_val, own_val, out_val;
+};
+
+// Realized table record (also the exported C record layout).
+struct OpRec {
+  int32_t step, kind;
+  int32_t src_rank, src_slot;
+  int32_t dst_rank, dst_slot;
+  int32_t own_slot;  // REDUCE: slot of the destination rank's own operand
+  int32_t pair;      // index of the op executed jointly with this one, or -1
+  int64_t offset, length;  // element range within one instance
+};
+
+struct FusedRange {
+  int64_t start, len;   // element range within one instance
+  int32_t prog;         // offset of its program in the word stream
+  int32_t ntrees;
+  int32_t need;         // evaluation stack depth
+};
+
+struct Schedule {
+  Spec spec;
+  int nsteps = 0;
+  int nslots = 1;
+  int C = 1;  // atoms
+  std::vector<std::pair<int64_t, int64_t>> atoms;  // element range per atom
+  std::vector<OpRec> ops;  // sorted by step; MOVE ops (step == nsteps) restore slot 0
+  std::vector<int32_t> steps_begin;  // ops index where each step starts (nsteps + 2 entries)
+  int64_t finalize_ops = 0;
+  bool single_port = true;
+  // fused replay program (per instance)
+  bool fused_ok = false;
+  std::string fused_error;
+  std::vector<int32_t> prog;
+  std::vector<FusedRange> ranges;
+  int max_need = 0, max_trees = 0, max_leaves = 0;
+};
+
+// Generate + realize + plan. Returns nullptr and sets *err on invalid input.
+Schedule* build_schedule(const Spec& spec, std::string* err);
+
+// Validate a spec without building (cheap argument checks).
+bool validate_spec(const Spec& spec, std::string* err);
+
+// Check an arbitrary exported table: snapshot hazards inside each step, that
+// every final value in slot 0 is a complete reduction (symbolic replay), and
+// the single-port property. Returns true when the table is a correct Allreduce.
+struct TableCheck {
+  bool ok = false;
+  bool single_port = true;
+  int nslots = 0;
+  std::string message;
+};
+TableCheck check_table(int P, int64_t n, int dtype, const OpRec* ops, size_t count);
+
+struct CostOut {
+  int32_t steps;
+  int64_t sent_busiest, recv_busiest, reduced_busiest;  // elements, summed over steps of the per-step max
+  int64_t sent_total, reduced_total;                      // elements, all ranks, all steps
+  int64_t max_rank_sent, max_rank_reduced;                // elements, the busiest rank over the whole run
+  double predicted_seconds;
+  double closed_form_seconds;  // NaN when the pages give none
+  double literal_hbm_bytes;    // bytes the literal executor moves through HBM per call
+  double fused_hbm_bytes;      // bytes the fused replay requests per call
+  double essential_bytes;      // 2 P n elt per call
+};
+CostOut cost_walk(const Schedule& s, double alpha, double beta, double gamma);
+// per-step, per-rank element counters (steps x P, row-major)
+void cost_steps(const Schedule& s, int64_t* sent, int64_t* recv, int64_t* reduced);
+
+int elt_bytes(int dtype);
+int acc_bytes(int dtype);
+int ceil_log2(int P);
+
+}  // namespace ar

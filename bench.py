@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Allreduce throughput on one MI355X: essential GB/s and % of HBM peak.
+
+A step is one in-place Allreduce of P rank buffers resident in HBM (one call of
+ar_allreduce_ex), timed with HIP events on the stream it is launched on. Before
+every step, outside the timed region, the inputs are restored from a pristine
+copy (in-place sums grow the values) and the 256 MB Infinity Cache is flushed
+by writing a 1 GiB buffer, so each step starts cold from HBM.
+
+Essential bytes = P * n * elt read + P * n * elt written (every input read
+once, every output written once). value = essential bytes / mean step time.
+
+Default workload: 8 ranks x 2^20 fp32 N(0,1), recursive halving + doubling,
+fused replay (the schedule the workload names), with ring, direct and
+recursive doubling (fused and literal) reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+
+WORKLOADS = {
+    "rh_fp32": dict(
+        desc="8 ranks x 2^20 fp32 N(0,1), seed 0",
+        P=8, n=1 << 20, dtype="fp32", batch=1, groups=None,
+        headline=("rh_rd", 0, "fused"),
+        others=[("ring", 0, "fused"), ("direct", 0, "fused"), ("rd", 0, "fused"), ("generalized_xor", 0, "fused"),
+                ("rh_rd", 0, "literal"), ("ring", 0, "literal")]),
+    "prime_fp32": dict(
+        desc="7 ranks x 2^24 fp32 N(0,1e-3), seed 0",
+        P=7, n=1 << 24, dtype="fp32", batch=1, groups=None,
+        headline=("generalized", 0, "fused"),
+        others=[("generalized", 1, "fused"), ("generalized", 2, "fused"), ("generalized", 3, "fused"),
+                ("ring", 0, "fused"), ("direct", 0, "fused"), ("ring", 0, "literal"), ("generalized", 0, "literal")]),
+    "ahc_bf16": dict(
+        desc="192 ranks in groups (64, 128) x 2^20 bf16 N(0,1), fp32 accumulation, seed 0",
+        P=192, n=1 << 20, dtype="bf16", batch=1, groups=[64, 128],
+        headline=("ahc", 0, "fused"),
+        others=[("direct", 0, "fused"), ("ahc", 0, "literal")]),
+    "small_batch": dict(
+        desc="24 ranks x 10^4 instances x 106 fp32 U(-1,1), seed 0",
+        P=24, n=106, dtype="fp32", batch=10_000, groups=None,
+        headline=("rd", 0, "fused"),
+        others=[("binomial", 0, "fused"), ("direct", 0, "fused"), ("rd", 0, "literal"), ("binomial", 0, "literal")]),
+    "ring_int32": dict(
+        desc="5 ranks x 4096 int32 U[-2^20, 2^20], seed 0",
+        P=5, n=4096, dtype="int32", batch=1, groups=None,
+        headline=("ring", 0, "fused"),
+        others=[("direct", 0, "fused"), ("ring", 0, "literal")]),
+}
+
+DT_NAME = {"fp32": "f32", "bf16": "bf16", "int32": "i32"}
+ELT = {"fp32": 4, "bf16": 2, "int32": 4}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "allreduce_schedule_algorithms_amd", "csrc", "exec.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def make_inputs(wl):
+    from synth import inputs
+    if wl["name"] == "small_batch":
+        return inputs.workload("small_batch", P=wl["P"])
+    return inputs.workload(wl["name"])
+
+
+def host_to_device(x, dtype):
+    import numpy as np
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.cuda()
+
+
+class Runner:
+    def __init__(self, wl, x):
+        import torch
+
+        import allreduce_schedule_algorithms_amd as A
+        self.A = A
+        self.wl = wl
+        self.stream = torch.cuda.Stream()
+        self.pristine = host_to_device(x, wl["dtype"])           # (P, batch*n)
+        self.work = torch.empty_like(self.pristine)
+        self.flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        self.ptrs = [self.work[p].data_ptr() for p in range(wl["P"])]
+        self.essential = 2.0 * wl["P"] * wl["n"] * wl["batch"] * ELT[wl["dtype"]]
+
+    def call_for(self, algo, knob, ex):
+        wl = self.wl
+        return self.A.make_call(wl["P"], wl["n"], wl["dtype"], "sum", algo, knob, ex, wl["batch"], wl["groups"])
+
+    def time(self, algo, knob, ex, steps, warmup, cold=True):
+        import torch
+        call = self.call_for(algo, knob, ex)
+        st = self.stream
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
+        def prep():
+            with torch.cuda.stream(st):
+                self.work.copy_(self.pristine)
+                if cold:
+                    self.flush.zero_()
+
+        for _ in range(warmup):
+            prep()
+            self.A.ar_allreduce_ex(self.ptrs, call, st)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            prep()
+            evs[k][0].record(st)
+            self.A.ar_allreduce_ex(self.ptrs, call, st)
+            evs[k][1].record(st)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = [a.elapsed_time(b) for a, b in evs]
+        mean = statistics.fmean(ms)
+        return dict(ms=mean, ms_median=statistics.median(ms), ms_min=min(ms), wall_ms_per_step=1e3 * wall / steps,
+                    GBps=self.essential / (mean * 1e-3) / 1e9)
+
+    def copy_ceiling(self, gib=2):
+        import torch
+        a = torch.empty(gib << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        for _ in range(2):
+            b.copy_(a)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        reps = 5
+        for _ in range(reps):
+            b.copy_(a)
+        e.record()
+        torch.cuda.synchronize()
+        t = s.elapsed_time(e) / reps * 1e-3
+        del a, b
+        return 2.0 * (gib << 30) / t / 1e9
+
+
+def cpu_baseline(wl, x, budget_s=12.0):
+    """The oracle, as it stands, on this host: repeated replays of the headline schedule."""
+    import numpy as np
+
+    import oracle
+    algo, knob, _ = wl["headline"]
+    P, n, B = wl["P"], wl["n"], wl["batch"]
+    if B > 1:
+        xs = x.reshape(P, B, n)
+        sample = f"full workload ({B} instances of {n})"
+        ess = 2.0 * P * n * B * ELT[wl["dtype"]]
+        idx = None
+    elif P * n > (1 << 24):
+        # bounded sample: every rank's first 2^20 offsets' worth, spread over the buffer
+        from synth import inputs
+        idx = np.unique(np.linspace(0, n - 1, num=min(n, (1 << 24) // P), dtype=np.int64))
+        xs = np.ascontiguousarray(x[:, idx])
+        sample = f"{len(idx)} of {n} offsets per rank (evenly spaced, all parts covered)"
+        ess = 2.0 * P * len(idx) * ELT[wl["dtype"]]
+        del inputs
+    else:
+        xs = x
+        idx = None
+        sample = f"full workload ({P} x {n})"
+        ess = 2.0 * P * n * ELT[wl["dtype"]]
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        if idx is None:
+            oracle.allreduce(xs, algo, wl["dtype"], "sum", knob=knob, groups=wl["groups"],
+                             n=n if B > 1 else None)
+        else:
+            oracle.allreduce(xs, algo, wl["dtype"], "sum", knob=knob, groups=wl["groups"], n=n, idx=idx)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 50:
+            break
+    mean = statistics.fmean(times)
+    return {"value": round(ess / mean / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{sample}; {algo} replay, {len(times)} runs, mean {mean:.3f} s (NumPy, one thread)"}
+
+
+def load_traffic(wl_name, algo, knob, ex):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    key = f"{wl_name}/{algo}/{knob}/{ex}"
+    rec = t.get(key)
+    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="rh_fp32", choices=sorted(WORKLOADS))
+    ap.add_argument("--headline-only", action="store_true", help="time only the headline schedule")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--warm", action="store_true", help="also report warm-cache (no flush) figures")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="run one plain device copy of MIB MiB (for counter scaling) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs every rank of an Allreduce as a buffer "
+              f"in one GPU's HBM and has no multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    torch.cuda.set_device(0)
+
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy << 20
+        a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": nbytes}))
+        return
+
+    wl = dict(WORKLOADS[args.workload])
+    wl["name"] = args.workload
+    x = make_inputs(wl)
+    r = Runner(wl, x)
+    algo, knob, ex = wl["headline"]
+
+    head = r.time(algo, knob, ex, args.steps, args.warmup)
+    schedules = {f"{algo}/r{knob}/{ex}": head}
+    if not args.headline_only:
+        for a2, k2, e2 in wl["others"]:
+            schedules[f"{a2}/r{k2}/{e2}"] = r.time(a2, k2, e2, max(10, args.steps // 2), 2)
+    if args.warm:
+        for key in list(schedules):
+            a2, k2, e2 = key.split("/")
+            schedules[key]["warm_GBps"] = r.time(a2, int(k2[1:]), e2, max(10, args.steps // 2), 2, cold=False)["GBps"]
+    for v in schedules.values():
+        v["pct_hbm_peak"] = round(100.0 * v["GBps"] / HBM_PEAK_GBPS, 2)
+        for k in ("ms", "ms_median", "ms_min", "wall_ms_per_step", "GBps"):
+            v[k] = round(v[k], 5 if k.startswith("ms") else 2)
+    ceiling = r.copy_ceiling()
+
+    # model bytes from the library's cost walk (fused / literal HBM bytes per call)
+    import allreduce_schedule_algorithms_amd as A
+    s = A.ar_schedule_build(r.call_for(algo, knob, ex))
+    cst = s.cost()
+    achieved = head["GBps"]
+    traffic = load_traffic(args.workload, algo, knob, ex)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": "k_fused" if not (algo == "direct" and ex == "fused") else "k_direct",
+                "algorithmic_bytes_per_launch": r.essential,
+                "model_bytes_per_launch": cst.fused_hbm_bytes if ex != "literal" else cst.literal_hbm_bytes}
+
+    cpu = None if args.no_cpu else cpu_baseline(wl, x)
+    line = {
+        "metric": "allreduce essential GB/s (P·n in + P·n out) and % of HBM peak, per schedule",
+        "value": round(achieved, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DT_NAME[wl["dtype"]],
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {wl['desc']}", "P": wl["P"], "n": wl["n"], "batch": wl["batch"],
+                   "schedule": algo, "knob": knob, "exec": ex, "cache": "cold (1 GiB flush before each step)"},
+        "pct_hbm_peak": round(100.0 * achieved / HBM_PEAK_GBPS, 2),
+        "copy_ceiling_GBps": round(ceiling, 1),
+        "wall_ms_per_step": head["wall_ms_per_step"],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "schedules": schedules,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+/*
+ * ar.h -- C ABI of the MI355X Allreduce schedule library (libar_mi355x.so).
+ *
+ * One call combines P rank buffers that live in the HBM of one GPU into their
+ * elementwise reduction and writes that result back into every buffer, the
+ * Allreduce operation defined in the introduction of "A Generalization of the
+ * Allreduce Operation" (vectors owned by the processes are combined into a
+ * result that is distributed back to all of them; the elementwise combine is
+ * the vector operator of the "Reduction Operator" page). Each schedule named
+ * below is executed as its own step list; a call never falls back to a
+ * different schedule or to the CPU.
+ *
+ * Conventions shared by every entry point
+ *  - Buffers: bufs[p] is rank p's buffer, caller-owned device memory holding
+ *    batch * n elements of the call's dtype (instance b at element b * n).
+ *    The call is in place: bufs[p] is input and output, as an in-place
+ *    ncclAllReduce (all-reduce blog page, "The APIs"). The library never frees
+ *    or keeps the pointers; the host array bufs is read before the call returns.
+ *    16-byte aligned buffers use 128-bit accesses; other alignments are
+ *    accepted and take a per-element path.
+ *  - Stream: `stream` is a hipStream_t (NULL = the default stream). Work is
+ *    enqueued and the call returns without waiting, like ncclAllReduce
+ *    (all-reduce blog page, "The APIs"). Kernel faults surface at the caller's
+ *    next synchronization.
+ *  - Errors: arguments are validated on the host before any device work; on
+ *    a non-AR_OK return no buffer has been touched. AR_HIP_ERROR carries the
+ *    HIP code in ar_last_hip_error(); ar_last_error_message() gives text.
+ *  - Precision: int32 sums wrap modulo 2^32; fp32 sums round to nearest even
+ *    at every combination, in the schedule's order; bf16 inputs are widened
+ *    exactly to fp32, every partial that crosses a step stays fp32, and each
+ *    complete result is rounded to bf16 once (all-reduce blog page, "Numerics
+ *    and reproducibility"). max uses the total order with -0 < +0; inputs must
+ *    be NaN-free.
+ *  - Threading: calls are thread-safe; calls on one stream run in order.
+ *    Calls that overlap on different streams must not share buffers.
+ *  - Limits: 1 <= P <= 256 (AR_MAX_RANKS).
+ */
+#ifndef AR_MI355X_H
+#define AR_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AR_MAX_RANKS 256
+
+typedef enum {
+  AR_OK = 0,
+  AR_INVALID_ARGUMENT = 1,
+  AR_UNSUPPORTED = 2,
+  AR_WORKSPACE_TOO_SMALL = 3,
+  AR_HIP_ERROR = 4,
+  AR_INTERNAL = 5
+} ar_status;
+
+typedef enum { AR_INT32 = 0, AR_FP32 = 1, AR_BF16 = 2 } ar_dtype;
+typedef enum { AR_SUM = 0, AR_MAX = 1 } ar_op;
+
+/* Schedules (the pages that define each one):
+ *  AR_DIRECT          one root gathers, combines in rank order, broadcasts (all-reduce blog
+ *                     page, cost-model section, the naive approach); 2(P-1) steps.
+ *  AR_RING            ring reduce-scatter + all-gather, 2(P-1) steps (blog page, "The ring
+ *                     algorithm"; generalized-Allreduce paper, eqs. (14)-(16), Fig. 5).
+ *  AR_RH_RD           recursive halving reduce-scatter + recursive doubling all-gather,
+ *                     2 log2 P' steps, plus fold-in/out steps when P is not a power of two
+ *                     (generalized-Allreduce paper, introduction and related work).
+ *  AR_RD              recursive doubling, log2 P' steps (+2 with fold-in) (same paper).
+ *  AR_BINOMIAL        binomial-tree reduce + broadcast, 2 ceil(log2 P) steps ("Reduction
+ *                     Operator" page).
+ *  AR_GENERALIZED     group-theoretic generalized Allreduce over the cyclic group Z_P, any P,
+ *                     2 ceil(log2 P) - knob steps (generalized-Allreduce paper, eqs. (17)-(44),
+ *                     Figs. 5-6).
+ *  AR_GENERALIZED_XOR the same over the self-inverse group of Table 1.b (P a power of two).
+ *  AR_AHC             asymmetric hierarchical Allreduce over contiguous groups (HCCL "AHC"
+ *                     page, Description), 2(max g - 1) + 2(G - 1) steps. */
+typedef enum {
+  AR_DIRECT = 0,
+  AR_RING = 1,
+  AR_RH_RD = 2,
+  AR_RD = 3,
+  AR_BINOMIAL = 4,
+  AR_GENERALIZED = 5,
+  AR_GENERALIZED_XOR = 6,
+  AR_AHC = 7
+} ar_algo;
+
+/* Execution of a schedule on the GPU.
+ *  AR_EXEC_FUSED    default. AR_DIRECT runs the one-pass direct kernel (read all P, combine
+ *                   left to right, write all P); every other schedule runs its fused
+ *                   per-element replay: one launch evaluates, per element, exactly the
+ *                   combination trees the step list builds, in registers.
+ *  AR_EXEC_LITERAL  one launch per schedule step (chunk REDUCE / COPY kernels), partials
+ *                   through HBM workspace slots; a last launch moves results that ended in
+ *                   a workspace slot into the caller's buffer.
+ *  AR_EXEC_REPLAY   the fused replay kernel for every schedule, AR_DIRECT included.
+ * All three give bit-identical results for the same schedule. */
+typedef enum { AR_EXEC_FUSED = 0, AR_EXEC_LITERAL = 1, AR_EXEC_REPLAY = 2 } ar_exec;
+
+/* Full description of one call. */
+typedef struct ar_call {
+  int32_t P;               /* ranks, 1..AR_MAX_RANKS */
+  int32_t dtype;           /* ar_dtype */
+  int32_t op;              /* ar_op */
+  int32_t algo;            /* ar_algo */
+  int32_t knob;            /* AR_GENERALIZED*: r = distribution steps removed, 0..ceil(log2 P);
+                              ignored otherwise */
+  int32_t exec;            /* ar_exec */
+  int64_t n;               /* elements per instance (>= 0) */
+  int64_t batch;           /* independent instances per buffer (>= 1); 0 is read as 1 */
+  int32_t ngroups;         /* AR_AHC: number of groups G (>= 1) */
+  const int32_t* groups;   /* AR_AHC: G group sizes summing to P, ranks assigned in order */
+  void* workspace;         /* AR_EXEC_LITERAL: device scratch of ar_workspace_bytes() bytes, or
+                              NULL to let the library allocate and cache one per device */
+  size_t workspace_bytes;
+} ar_call;
+
+/* Plain Allreduce: fused execution, batch 1, no groups (AR_AHC needs ar_allreduce_ex).
+ * bufs: host array of P device pointers, each to n elements. */
+ar_status ar_allreduce(void* const* bufs, int32_t P, int64_t n, int32_t dtype, int32_t op,
+                       int32_t algo, int32_t knob, void* stream);
+
+/* Allreduce with every option of ar_call. */
+ar_status ar_allreduce_ex(void* const* bufs, const ar_call* call, void* stream);
+
+/* Workspace bytes an AR_EXEC_LITERAL call needs (0 for fused execution). */
+ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes);
+
+/* ---- schedules on the host (no GPU needed) ---- */
+typedef struct ar_schedule ar_schedule;
+
+typedef struct ar_oprec {
+  int32_t step;      /* method step; finalize moves carry step == steps */
+  int32_t kind;      /* 0 REDUCE: dst = own (+) src; 1 COPY: dst = src; 2 MOVE: same-rank slot
+                        move after the last step */
+  int32_t src_rank, src_slot;
+  int32_t dst_rank, dst_slot;
+  int32_t own_slot;  /* REDUCE: slot of dst_rank's own operand; -1 otherwise */
+  int32_t pair;      /* index of the REDUCE executed jointly with this one (both read before
+                        either writes), or -1 */
+  int64_t offset;    /* first element, within one instance */
+  int64_t length;    /* elements */
+} ar_oprec;
+/* Slot 0 is the caller's buffer; slot s >= 1 is a workspace buffer of the accumulation
+ * type (int32 / fp32 / fp32 for int32 / fp32 / bf16). */
+
+typedef struct ar_schedule_info {
+  int32_t steps;         /* method steps */
+  int32_t slots;         /* slots per rank including the caller's buffer */
+  int32_t atoms;         /* chunks of the schedule's partition */
+  int32_t single_port;   /* 1 if in every step each rank sends to <= 1 rank and receives from
+                            <= 1 rank (the generalized paper's cost-model assumption) */
+  int64_t ops;           /* exported records, finalize moves included */
+  int64_t finalize_ops;
+  int32_t fused_ok;      /* 1 if the fused replay program exists */
+  int32_t ranges;        /* ranges of the fused program (per instance) */
+  int32_t max_trees;     /* most distinct result trees in one range */
+  int32_t max_need;      /* deepest evaluation stack of the fused program */
+  int32_t max_leaves;
+  int32_t program_words;
+} ar_schedule_info;
+
+/* Build (and validate) the step table of a call; host only. *out must be freed
+ * with ar_schedule_free. */
+ar_status ar_schedule_build(const ar_call* call, ar_schedule** out);
+ar_status ar_schedule_info_get(const ar_schedule* s, ar_schedule_info* info);
+/* Copy up to cap records into ops; *count receives the total number. */
+ar_status ar_schedule_export(const ar_schedule* s, ar_oprec* ops, size_t cap, size_t* count);
+/* Fused replay program. Per range r: starts[r], lens[r] (elements within an instance) and
+ * offsets[r] into the int32 word stream. Words of a range: ntrees, then per tree
+ * nleaves, nouts, nleaves leaf ranks (postfix order), nleaves counts of combinations that
+ * follow each leaf, nouts destination ranks. Any pointer may be NULL to query sizes. */
+ar_status ar_schedule_fused_export(const ar_schedule* s, int64_t* starts, int64_t* lens,
+                                   int32_t* offsets, size_t range_cap, int32_t* words,
+                                   size_t word_cap, size_t* nranges, size_t* nwords);
+void ar_schedule_free(ar_schedule* s);
+
+/* Validate any table (for example a modified export): snapshot hazards inside a step,
+ * complete results in every rank's slot 0 (symbolic replay), single-port property.
+ * Returns AR_OK when the table is a correct Allreduce, AR_INVALID_ARGUMENT otherwise;
+ * ar_last_error_message() says why. */
+ar_status ar_table_check(int32_t P, int64_t n, int32_t dtype, const ar_oprec* ops,
+                         size_t count, int32_t* single_port);
+
+/* ---- alpha-beta-gamma cost report ----
+ * A step costs alpha + (bytes sent or received by the busiest rank) * beta + (bytes
+ * combined by the busiest rank) * gamma (generalized-Allreduce paper,
+ * cost-model paragraph; all-reduce blog page, "A cost model for collectives").
+ * closed_form_seconds evaluates the pages' printed closed form for the schedule (eqs.
+ * (15), (25), (36), (44) of the generalized paper; NaN for AHC, whose formula the page
+ * truncates). Elements are per call (all instances). */
+typedef struct ar_cost {
+  int32_t steps;
+  int64_t sent_busiest, recv_busiest, reduced_busiest; /* per instance, sum over steps of the
+                                                          per-step maximum over ranks */
+  int64_t sent_total, reduced_total;                   /* per instance, all ranks */
+  int64_t max_rank_sent, max_rank_reduced;             /* per instance, busiest rank overall */
+  double predicted_seconds;
+  double closed_form_seconds;
+  double literal_hbm_bytes;  /* bytes AR_EXEC_LITERAL moves through HBM per call */
+  double fused_hbm_bytes;    /* bytes the fused replay requests per call */
+  double essential_bytes;    /* 2 P n batch elt: every input read once, every output written once */
+} ar_cost;
+ar_status ar_cost_report(const ar_schedule* s, double alpha, double beta, double gamma,
+                         ar_cost* out);
+/* Per-step, per-rank element counts (steps x P, row-major, per instance). */
+ar_status ar_cost_steps(const ar_schedule* s, int64_t* sent, int64_t* recv, int64_t* reduced);
+
+const char* ar_status_string(ar_status st);
+int32_t ar_last_hip_error(void);
+const char* ar_last_error_message(void);
+/* Library version string. */
+const char* ar_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AR_MI355X_H */

@@ -1,0 +1,183 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Bit-exact for every schedule, dtype and op (int32 and max reach the plain
+result; fp32 / bf16 sums must reproduce the oracle's replay of the same
+schedule), plus the normwise tolerance against an fp64 reference
+(1e-5 fp32, 8e-3 bf16) at the full workload sizes, where the oracle is
+evaluated on sampled offsets (every part boundary included).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import numerics as nu
+from synth import inputs
+from gpu_util import bits, gpu_allreduce
+
+pytestmark = pytest.mark.gpu
+
+ALGOS = ("direct", "ring", "rh_rd", "rd", "binomial", "generalized", "generalized_xor", "ahc")
+FP_TOL = {"fp32": 1e-5, "bf16": 8e-3}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    torch.cuda.set_device(0)
+
+
+def knobs(algo, P):
+    return range(nu.ceil_log2(P) + 1) if algo.startswith("generalized") else [0]
+
+
+def groups_for(algo, P):
+    if algo != "ahc":
+        return None
+    return [P] if P < 3 else [P // 3 + 1, P - (P // 3 + 1)]
+
+
+def check_tol(y, x, dtype):
+    ref = nu.fp64_reference(x, dtype)
+    for p in range(y.shape[0]):
+        yp = nu.bf16_to_f32(y[p]) if dtype == "bf16" else y[p]
+        assert nu.normwise_rel_error(yp, ref) <= FP_TOL[dtype], p
+
+
+# --------------------------------------------------------------------------
+# every schedule x dtype x op x execution mode, small ragged sizes
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["int32", "fp32", "bf16"])
+@pytest.mark.parametrize("algo", ALGOS)
+def test_small_all_schedules(algo, dtype):
+    for P in (3, 5, 7, 8, 12):
+        if algo == "generalized_xor" and P & (P - 1):
+            continue
+        for n in (37, 4099):
+            for r in knobs(algo, P):
+                x = inputs.make(dtype, P, n, seed=P * 7 + n)
+                for op in ("sum", "max"):
+                    want = oracle.allreduce(x, algo, dtype, op, knob=r, groups=groups_for(algo, P))
+                    for ex in ("fused", "literal", "replay"):
+                        got = gpu_allreduce(x, algo, dtype, op, r, ex, groups_for(algo, P))
+                        assert np.array_equal(bits(got), bits(want)), (algo, dtype, P, n, r, op, ex)
+
+
+@pytest.mark.parametrize("algo", ["direct", "ring", "rd", "generalized", "ahc"])
+def test_misaligned_buffers_take_element_path(algo):
+    P, n = 6, 1000
+    for dtype in ("fp32", "bf16"):
+        x = inputs.make(dtype, P, n, seed=3)
+        for r in knobs(algo, P):
+            want = oracle.allreduce(x, algo, dtype, "sum", knob=r, groups=groups_for(algo, P))
+            for ex in ("fused", "literal"):
+                got = gpu_allreduce(x, algo, dtype, "sum", r, ex, groups_for(algo, P), misalign=True)
+                assert np.array_equal(bits(got), bits(want)), (algo, dtype, r, ex)
+
+
+@pytest.mark.parametrize("algo", ["ring", "rh_rd", "binomial", "generalized", "ahc"])
+def test_batched_instances(algo):
+    P, n, B = 6, 53, 7
+    x = inputs.make("fp32", P, B * n, seed=11, dist="uniform_pm1")
+    for r in knobs(algo, P):
+        want = oracle.allreduce(x.reshape(P, B, n), algo, "fp32", "sum", knob=r, groups=groups_for(algo, P),
+                                n=n).reshape(P, B * n)
+        for ex in ("fused", "literal"):
+            got = gpu_allreduce(x, algo, "fp32", "sum", r, ex, groups_for(algo, P), batch=B)
+            assert np.array_equal(bits(got), bits(want)), (algo, r, ex)
+
+
+def test_most_ranks_and_tiny_buffers():
+    for P in (2, 256):
+        for n in (1, 3, 64):
+            x = inputs.make("fp32", P, n, seed=P + n)
+            for algo in ("direct", "ring", "rd", "binomial"):
+                want = oracle.allreduce(x, algo, "fp32", "sum")
+                for ex in ("fused", "literal"):
+                    got = gpu_allreduce(x, algo, "fp32", "sum", 0, ex)
+                    assert np.array_equal(bits(got), bits(want)), (P, n, algo, ex)
+
+
+def test_side_stream_and_signed_zero():
+    import torch
+    s = torch.cuda.Stream()
+    x = np.zeros((5, 300), dtype=np.float32)
+    x[1] = -0.0
+    x[4, ::2] = -0.0
+    got = gpu_allreduce(x, "ring", "fp32", "max", stream=s)
+    assert not np.signbit(got).any()
+    x = inputs.make("fp32", 5, 300, seed=2)
+    want = oracle.allreduce(x, "rh_rd", "fp32", "sum")
+    assert np.array_equal(gpu_allreduce(x, "rh_rd", "fp32", "sum", stream=s), want)
+
+
+# --------------------------------------------------------------------------
+# the workloads at full size
+# --------------------------------------------------------------------------
+def test_ring_int32_5_ranks():
+    x = inputs.workload("ring_int32")
+    bf = nu.brute_force(x, "int32", "sum")
+    for algo in ("ring", "direct"):
+        for ex in ("fused", "literal"):
+            got = gpu_allreduce(x, algo, "int32", "sum", 0, ex)
+            assert np.array_equal(got, np.broadcast_to(bf, got.shape)), (algo, ex)
+
+
+def test_rh_fp32_8_ranks():
+    x = inputs.workload("rh_fp32")
+    for algo in ("rh_rd", "ring", "direct", "rd"):
+        want = oracle.allreduce(x, algo, "fp32", "sum")
+        for ex in ("fused", "literal"):
+            got = gpu_allreduce(x, algo, "fp32", "sum", 0, ex)
+            assert np.array_equal(bits(got), bits(want)), (algo, ex)
+            check_tol(got, x, "fp32")
+
+
+def test_prime_fp32_7_ranks_sampled():
+    x = inputs.workload("prime_fp32")
+    P, n = x.shape
+    idx = inputs.sample_indices(n, P, count=4096)
+    xs = np.ascontiguousarray(x[:, idx])
+    cases = [("generalized", r, "fused") for r in range(4)] + [("generalized", 0, "literal"),
+                                                               ("generalized", 3, "literal"),
+                                                               ("ring", 0, "fused"), ("direct", 0, "fused")]
+    for algo, r, ex in cases:
+        got = gpu_allreduce(x, algo, "fp32", "sum", r, ex)
+        want = oracle.allreduce(xs, algo, "fp32", "sum", knob=r, n=n, idx=idx)
+        assert np.array_equal(bits(got[:, idx]), bits(want)), (algo, r, ex)
+        check_tol(got, x, "fp32")
+        if r == 0 or algo != "generalized":
+            assert (got == got[:1]).all()  # one tree per part: every rank holds the same bits
+
+
+@pytest.mark.parametrize("P", [3, 6, 12, 24])
+def test_small_batch_latency_path(P):
+    x = inputs.workload("small_batch", P=P)
+    B, ln = 10_000, 106
+    for algo in ("rd", "binomial"):
+        want = oracle.allreduce(x.reshape(P, B, ln), algo, "fp32", "sum", n=ln).reshape(P, B * ln)
+        for ex in ("fused", "literal"):
+            got = gpu_allreduce(x, algo, "fp32", "sum", 0, ex, batch=B)
+            assert np.array_equal(bits(got), bits(want)), (algo, ex)
+        check_tol(got, x, "fp32")
+
+
+def test_ahc_bf16_192_ranks_sampled():
+    x = inputs.workload("ahc_bf16")
+    P, n = x.shape
+    groups = [64, 128]
+    idx = inputs.sample_indices(n, 256, count=2048)
+    xs = np.ascontiguousarray(x[:, idx])
+    for op in ("sum", "max"):
+        want = oracle.allreduce(xs, "ahc", "bf16", op, groups=groups, n=n, idx=idx)
+        for ex in ("fused", "literal"):
+            got = gpu_allreduce(x, "ahc", "bf16", op, 0, ex, groups)
+            assert np.array_equal(bits(got[:, idx]), bits(want)), (op, ex)
+            assert (got == got[:1]).all()
+            if op == "sum":
+                check_tol(got, x, "bf16")
+            else:
+                assert np.array_equal(bits(got[0]), bits(nu.brute_force(x, "bf16", "max")))
+    got = gpu_allreduce(x, "direct", "bf16", "sum")
+    want = oracle.allreduce(xs, "direct", "bf16", "sum", n=n, idx=idx)
+    assert np.array_equal(bits(got[:, idx]), bits(want))
