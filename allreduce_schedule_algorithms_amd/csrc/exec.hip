@@ -53,6 +53,7 @@ struct LitOp {
 
 constexpr int kThreads = 256;
 constexpr int kLeafBatch = 8;
+constexpr int kMaxFusedTrees = 8;  // distinct result trees per range the fused replay keeps in registers
 
 // ----------------------------------------------------------------------------
 // element types
@@ -170,65 +171,90 @@ __device__ __forceinline__ void store_acc(void* base, int64_t e, const typename 
 // ----------------------------------------------------------------------------
 // Program words of one range: ntrees, then per tree: nleaves, nouts,
 // leaf rank[nleaves] (postfix order), ncomb[nleaves] (combinations that follow
-// each leaf), out rank[nouts].
+// each leaf), out rank[nouts]. Every tree reads the values from before the
+// call, so all trees of a range are evaluated before any result is stored
+// (results stay in registers; TM bounds the trees per range).
 template <int DT, int OPK, int D, int W>
+__device__ __forceinline__ void eval_one(const RankPtrs& ptrs, const int32_t* __restrict__ w, int64_t e,
+                                         typename TT<DT>::A (&res)[W]) {
+  using A = typename TT<DT>::A;
+  const int nl = w[0];
+  const int32_t* __restrict__ leaf = w + 2;
+  const int32_t* __restrict__ nc = leaf + nl;
+  A st[D][W];
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+#pragma unroll
+    for (int i = 0; i < W; ++i) st[d][i] = A(0);
+  for (int base = 0; base < nl; base += kLeafBatch) {
+    A l[kLeafBatch][W];
+#pragma unroll
+    for (int k = 0; k < kLeafBatch; ++k) {
+      const int idx = base + k < nl ? base + k : base;
+      load_user<DT, W>(ptrs.p[leaf[idx]], e, l[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < kLeafBatch; ++k) {
+      if (base + k < nl) {
+#pragma unroll
+        for (int d = D - 1; d > 0; --d)
+#pragma unroll
+          for (int i = 0; i < W; ++i) st[d][i] = st[d - 1][i];
+#pragma unroll
+        for (int i = 0; i < W; ++i) st[0][i] = l[k][i];
+        for (int c = nc[base + k]; c > 0; --c) {
+#pragma unroll
+          for (int i = 0; i < W; ++i) st[0][i] = cmb<OPK>(st[1][i], st[0][i]);
+#pragma unroll
+          for (int d = 1; d < D - 1; ++d)
+#pragma unroll
+            for (int i = 0; i < W; ++i) st[d][i] = st[d + 1][i];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < W; ++i) res[i] = st[0][i];
+}
+
+template <int DT, int OPK, int D, int TM, int W>
 __device__ __forceinline__ void replay(const RankPtrs& ptrs, const int32_t* __restrict__ w, int64_t e) {
   using A = typename TT<DT>::A;
   const int ntrees = w[0];
   w += 1;
-  for (int t = 0; t < ntrees; ++t) {
-    const int nl = w[0], no = w[1];
-    const int32_t* __restrict__ leaf = w + 2;
-    const int32_t* __restrict__ nc = leaf + nl;
-    const int32_t* __restrict__ outs = nc + nl;
-    A st[D][W];
+  A res[TM][W];
+  const int32_t* outs[TM];
+  int nouts[TM];
 #pragma unroll
-    for (int d = 0; d < D; ++d)
-#pragma unroll
-      for (int i = 0; i < W; ++i) st[d][i] = A(0);
-    for (int base = 0; base < nl; base += kLeafBatch) {
-      A l[kLeafBatch][W];
-#pragma unroll
-      for (int k = 0; k < kLeafBatch; ++k) {
-        const int idx = base + k < nl ? base + k : base;
-        load_user<DT, W>(ptrs.p[leaf[idx]], e, l[k]);
-      }
-#pragma unroll
-      for (int k = 0; k < kLeafBatch; ++k) {
-        if (base + k < nl) {
-#pragma unroll
-          for (int d = D - 1; d > 0; --d)
-#pragma unroll
-            for (int i = 0; i < W; ++i) st[d][i] = st[d - 1][i];
-#pragma unroll
-          for (int i = 0; i < W; ++i) st[0][i] = l[k][i];
-          for (int c = nc[base + k]; c > 0; --c) {
-#pragma unroll
-            for (int i = 0; i < W; ++i) st[0][i] = cmb<OPK>(st[1][i], st[0][i]);
-#pragma unroll
-            for (int d = 1; d < D - 1; ++d)
-#pragma unroll
-              for (int i = 0; i < W; ++i) st[d][i] = st[d + 1][i];
-          }
-        }
-      }
+  for (int t = 0; t < TM; ++t) {
+    if (t < ntrees) {
+      const int nl = w[0];
+      nouts[t] = w[1];
+      outs[t] = w + 2 + 2 * nl;
+      eval_one<DT, OPK, D, W>(ptrs, w, e, res[t]);
+      w = outs[t] + nouts[t];
     }
-    for (int o = 0; o < no; ++o) store_user<DT, W>(ptrs.p[outs[o]], e, st[0]);
-    w = outs + no;
+  }
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    if (t < ntrees) {
+      for (int o = 0; o < nouts[t]; ++o) store_user<DT, W>(ptrs.p[outs[t][o]], e, res[t]);
+    }
   }
 }
 
-template <int DT, int OPK, int D>
+template <int DT, int OPK, int D, int TM>
 __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* __restrict__ items,
                                                     const int32_t* __restrict__ prog) {
   constexpr int V = TT<DT>::V;
   const Item it = items[blockIdx.x];
   const int32_t* w = prog + it.tag;
   if (it.count > 0) {
-    for (int v = threadIdx.x; v < it.count; v += kThreads) replay<DT, OPK, D, V>(ptrs, w, it.start + int64_t(v) * V);
+    for (int v = threadIdx.x; v < it.count; v += kThreads)
+      replay<DT, OPK, D, TM, V>(ptrs, w, it.start + int64_t(v) * V);
   } else {
     const int cnt = -it.count;
-    for (int v = threadIdx.x; v < cnt; v += kThreads) replay<DT, OPK, D, 1>(ptrs, w, it.start + v);
+    for (int v = threadIdx.x; v < cnt; v += kThreads) replay<DT, OPK, D, TM, 1>(ptrs, w, it.start + v);
   }
 }
 
@@ -523,15 +549,23 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
 
 // ---- kernel dispatch ----
 template <int DT, int OPK>
-hipError_t launch_fused_t(int D, int64_t nitems, const RankPtrs& ptrs, const Item* items, const int32_t* prog,
+hipError_t launch_fused_t(int D, int TM, int64_t nitems, const RankPtrs& ptrs, const Item* items, const int32_t* prog,
                           hipStream_t st) {
   const dim3 g{unsigned(nitems), 1, 1};
   const dim3 b{unsigned(kThreads), 1, 1};
-  switch (D) {
-    case 2: hipLaunchKernelGGL((k_fused<DT, OPK, 2>), g, b, 0, st, ptrs, items, prog); break;
-    case 4: hipLaunchKernelGGL((k_fused<DT, OPK, 4>), g, b, 0, st, ptrs, items, prog); break;
-    case 8: hipLaunchKernelGGL((k_fused<DT, OPK, 8>), g, b, 0, st, ptrs, items, prog); break;
-    default: hipLaunchKernelGGL((k_fused<DT, OPK, 16>), g, b, 0, st, ptrs, items, prog); break;
+  if (TM == 1) {
+    switch (D) {
+      case 2: hipLaunchKernelGGL((k_fused<DT, OPK, 2, 1>), g, b, 0, st, ptrs, items, prog); break;
+      case 4: hipLaunchKernelGGL((k_fused<DT, OPK, 4, 1>), g, b, 0, st, ptrs, items, prog); break;
+      case 8: hipLaunchKernelGGL((k_fused<DT, OPK, 8, 1>), g, b, 0, st, ptrs, items, prog); break;
+      default: hipLaunchKernelGGL((k_fused<DT, OPK, 16, 1>), g, b, 0, st, ptrs, items, prog); break;
+    }
+  } else {
+    switch (D) {
+      case 2: hipLaunchKernelGGL((k_fused<DT, OPK, 2, kMaxFusedTrees>), g, b, 0, st, ptrs, items, prog); break;
+      case 4: hipLaunchKernelGGL((k_fused<DT, OPK, 4, kMaxFusedTrees>), g, b, 0, st, ptrs, items, prog); break;
+      default: hipLaunchKernelGGL((k_fused<DT, OPK, 8, kMaxFusedTrees>), g, b, 0, st, ptrs, items, prog); break;
+    }
   }
   return hipGetLastError();
 }
@@ -619,6 +653,13 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
         res.message = "fused replay program unavailable: " + pl->s->fused_error;
         return res;
       }
+      if (pl->exec != E_LITERAL && (pl->s->max_trees > kMaxFusedTrees || (pl->s->max_trees > 1 && pl->D > 8))) {
+        res.status = 2;
+        res.message = "fused replay keeps at most " + std::to_string(kMaxFusedTrees) +
+                      " distinct result trees of stack depth <= 8 per range in registers; this schedule has " +
+                      std::to_string(pl->s->max_trees) + " (use AR_EXEC_LITERAL)";
+        return res;
+      }
       res = build_items(*pl, vec);
       if (res.status) return res;
     }
@@ -661,7 +702,9 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
     if (pl->nitems[mode] == 0) return res;
     const Item* items = reinterpret_cast<const Item*>(pl->items[mode].p);
     const int32_t* prog = reinterpret_cast<const int32_t*>(pl->prog.p);
-    AR_DISPATCH(spec.dtype, spec.op, (e = launch_fused_t<DT, OPK>(pl->D, pl->nitems[mode], ptrs, items, prog, st)));
+    AR_DISPATCH(spec.dtype, spec.op,
+                (e = launch_fused_t<DT, OPK>(pl->D, pl->s->max_trees > 1 ? kMaxFusedTrees : 1, pl->nitems[mode], ptrs,
+                                             items, prog, st)));
     if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
   }
   (void)V;

@@ -60,7 +60,7 @@ def test_small_all_schedules(algo, dtype):
                     want = oracle.allreduce(x, algo, dtype, op, knob=r, groups=groups_for(algo, P))
                     for ex in ("fused", "literal", "replay"):
                         got = gpu_allreduce(x, algo, dtype, op, r, ex, groups_for(algo, P))
-                        assert np.array_equal(bits(got), bits(want)), (algo, dtype, P, n, r, op, ex)
+                        assert np.array_equal(bits(got), bits(want)), (ex, algo, dtype, P, n, r, op)
 
 
 @pytest.mark.parametrize("algo", ["direct", "ring", "rd", "generalized", "ahc"])
