@@ -90,78 +90,148 @@ template <int OPK> __device__ __forceinline__ uint32_t cmb(uint32_t a, uint32_t 
   else return int32_t(b) > int32_t(a) ? b : a;
 }
 
-// Load W elements of the caller's dtype at element `e`, widened to the accumulation type.
-// W == V: one 128-bit load (16-byte aligned); W == 1: one element.
-template <int DT, int W>
-__device__ __forceinline__ void load_user(const void* base, int64_t e, typename TT<DT>::A (&out)[W]) {
+// ----------------------------------------------------------------------------
+// fragments: what one thread moves per rank
+// ----------------------------------------------------------------------------
+// A fragment is M 16-byte vectors (M >= 1) at element offsets e, e + kThreads*V,
+// ... (the vectors of a block interleave so that every load instruction of a
+// wave covers 1 KB of contiguous memory), or a single element (M == 0, used at
+// ragged range edges and for buffers that are not 16-byte aligned). Loads and
+// stores carry the non-temporal hint: every byte is touched once per call.
+template <int M> constexpr int mm() { return M ? M : 1; }
+template <int DT, int M> constexpr int nvals() { return M ? M * TT<DT>::V : 1; }
+
+// Raw bits of one fragment of the caller's dtype. NT = non-temporal hint; it is
+// dropped where a program loads the same leaf again (several result trees).
+template <typename T, bool NT>
+__device__ __forceinline__ T ld(const T* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <int DT, int M, bool NT = true>
+__device__ __forceinline__ void ld_user(const void* base, int64_t e, const bool (&ok)[mm<M>()],
+                                        u32x4 (&r)[mm<M>()]) {
   using S = typename TT<DT>::S;
-  if constexpr (W == 1) {
-    S v = reinterpret_cast<const S*>(base)[e];
-    if constexpr (DT == D_BF16) out[0] = as_f(uint32_t(v) << 16);
-    else from_u(*reinterpret_cast<const uint32_t*>(&v), out[0]);
-  } else {
-    static_assert(W == TT<DT>::V, "vector width");
-    u32x4 r = *reinterpret_cast<const u32x4*>(reinterpret_cast<const S*>(base) + e);
-    if constexpr (DT == D_BF16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        out[2 * i] = as_f(r[i] << 16);
-        out[2 * i + 1] = as_f(r[i] & 0xffff0000u);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) from_u(r[i], out[i]);
+  if constexpr (M == 0) {
+    if (ok[0]) {
+      if constexpr (DT == D_BF16) r[0][0] = uint32_t(ld<uint16_t, NT>(reinterpret_cast<const uint16_t*>(base) + e));
+      else r[0][0] = ld<uint32_t, NT>(reinterpret_cast<const uint32_t*>(base) + e);
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < M; ++j)
+      if (ok[j])
+        r[j] = ld<u32x4, NT>(
+            reinterpret_cast<const u32x4*>(reinterpret_cast<const S*>(base) + e + int64_t(j) * kThreads * TT<DT>::V));
   }
 }
 
-template <int DT, int W>
-__device__ __forceinline__ void store_user(void* base, int64_t e, const typename TT<DT>::A (&v)[W]) {
-  using S = typename TT<DT>::S;
-  if constexpr (W == 1) {
-    if constexpr (DT == D_BF16) reinterpret_cast<S*>(base)[e] = S(to_bf16(v[0]));
-    else reinterpret_cast<uint32_t*>(base)[e] = as_u(v[0]);
+// Widen raw bits to the accumulation type (bf16 -> fp32 is exact).
+template <int DT, int M>
+__device__ __forceinline__ void widen(const u32x4 (&r)[mm<M>()], typename TT<DT>::A (&out)[nvals<DT, M>()]) {
+  if constexpr (M == 0) {
+    if constexpr (DT == D_BF16) out[0] = as_f(r[0][0] << 16);
+    else from_u(r[0][0], out[0]);
   } else {
-    u32x4 r;
-    if constexpr (DT == D_BF16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = to_bf16(v[2 * i]) | (to_bf16(v[2 * i + 1]) << 16);
-    } else {
+    for (int j = 0; j < M; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = as_u(v[i]);
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (DT == D_BF16) {
+          out[8 * j + 2 * i] = as_f(r[j][i] << 16);
+          out[8 * j + 2 * i + 1] = as_f(r[j][i] & 0xffff0000u);
+        } else {
+          from_u(r[j][i], out[4 * j + i]);
+        }
+      }
+  }
+}
+
+// Store a fragment in the caller's dtype (bf16: one round to nearest even).
+template <int DT, int M>
+__device__ __forceinline__ void st_user(void* base, int64_t e, const bool (&ok)[mm<M>()],
+                                        const typename TT<DT>::A (&v)[nvals<DT, M>()]) {
+  using S = typename TT<DT>::S;
+  if constexpr (M == 0) {
+    if (ok[0]) {
+      if constexpr (DT == D_BF16) __builtin_nontemporal_store(uint16_t(to_bf16(v[0])), reinterpret_cast<uint16_t*>(base) + e);
+      else __builtin_nontemporal_store(as_u(v[0]), reinterpret_cast<uint32_t*>(base) + e);
     }
-    *reinterpret_cast<u32x4*>(reinterpret_cast<S*>(base) + e) = r;
+  } else {
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      u32x4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (DT == D_BF16) r[i] = to_bf16(v[8 * j + 2 * i]) | (to_bf16(v[8 * j + 2 * i + 1]) << 16);
+        else r[i] = as_u(v[4 * j + i]);
+      }
+      if (ok[j])
+        __builtin_nontemporal_store(
+            r, reinterpret_cast<u32x4*>(reinterpret_cast<S*>(base) + e + int64_t(j) * kThreads * TT<DT>::V));
+    }
   }
 }
 
 // Workspace slots hold the accumulation type (4 bytes per element).
-template <int DT, int W>
-__device__ __forceinline__ void load_acc(const void* base, int64_t e, typename TT<DT>::A (&out)[W]) {
+template <int DT, int M>
+__device__ __forceinline__ void ld_acc(const void* base, int64_t e, const bool (&ok)[mm<M>()],
+                                       typename TT<DT>::A (&out)[nvals<DT, M>()]) {
   const uint32_t* p = reinterpret_cast<const uint32_t*>(base) + e;
-  if constexpr (W == 1) {
-    from_u(p[0], out[0]);
+  if constexpr (M == 0) {
+    if (ok[0]) from_u(__builtin_nontemporal_load(p), out[0]);
   } else {
+    constexpr int V = TT<DT>::V;
 #pragma unroll
-    for (int q = 0; q < W / 4; ++q) {
-      u32x4 r = reinterpret_cast<const u32x4*>(p)[q];
+    for (int j = 0; j < M; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) from_u(r[i], out[4 * q + i]);
-    }
+      for (int q = 0; q < V / 4; ++q) {
+        u32x4 r = {0, 0, 0, 0};
+        if (ok[j]) r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + int64_t(j) * kThreads * V) + q);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) from_u(r[i], out[V * j + 4 * q + i]);
+      }
   }
 }
 
-template <int DT, int W>
-__device__ __forceinline__ void store_acc(void* base, int64_t e, const typename TT<DT>::A (&v)[W]) {
+template <int DT, int M>
+__device__ __forceinline__ void st_acc(void* base, int64_t e, const bool (&ok)[mm<M>()],
+                                       const typename TT<DT>::A (&v)[nvals<DT, M>()]) {
   uint32_t* p = reinterpret_cast<uint32_t*>(base) + e;
-  if constexpr (W == 1) {
-    p[0] = as_u(v[0]);
+  if constexpr (M == 0) {
+    if (ok[0]) __builtin_nontemporal_store(as_u(v[0]), p);
   } else {
+    constexpr int V = TT<DT>::V;
 #pragma unroll
-    for (int q = 0; q < W / 4; ++q) {
-      u32x4 r;
+    for (int j = 0; j < M; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = as_u(v[4 * q + i]);
-      reinterpret_cast<u32x4*>(p)[q] = r;
+      for (int q = 0; q < V / 4; ++q) {
+        u32x4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = as_u(v[V * j + 4 * q + i]);
+        if (ok[j]) __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(p + int64_t(j) * kThreads * V) + q);
+      }
+  }
+}
+
+// Iterate over the fragments of one work item: f(e, ok) for every fragment of
+// this thread. Vector items hold `count` vectors; element items -count elements.
+template <int M, typename F>
+__device__ __forceinline__ void for_fragments(const Item& it, int V, F&& f) {
+  if constexpr (M == 0) {
+    const int cnt = -it.count;
+    for (int v = threadIdx.x; v < cnt; v += kThreads) {
+      const bool ok[1] = {true};
+      f(it.start + v, ok);
+    }
+  } else {
+    for (int v0 = 0; v0 < it.count; v0 += kThreads * M) {
+      const int vb = v0 + int(threadIdx.x);
+      bool ok[M];
+#pragma unroll
+      for (int j = 0; j < M; ++j) ok[j] = vb + j * kThreads < it.count;
+      if (ok[0]) f(it.start + int64_t(vb) * V, ok);
     }
   }
 }
@@ -174,24 +244,25 @@ __device__ __forceinline__ void store_acc(void* base, int64_t e, const typename 
 // each leaf), out rank[nouts]. Every tree reads the values from before the
 // call, so all trees of a range are evaluated before any result is stored
 // (results stay in registers; TM bounds the trees per range).
-template <int DT, int OPK, int D, int W>
+template <int DT, int OPK, int D, int M, bool NT>
 __device__ __forceinline__ void eval_one(const RankPtrs& ptrs, const int32_t* __restrict__ w, int64_t e,
-                                         typename TT<DT>::A (&res)[W]) {
+                                         const bool (&ok)[mm<M>()], typename TT<DT>::A (&res)[nvals<DT, M>()]) {
   using A = typename TT<DT>::A;
+  constexpr int N = nvals<DT, M>();
   const int nl = w[0];
   const int32_t* __restrict__ leaf = w + 2;
   const int32_t* __restrict__ nc = leaf + nl;
-  A st[D][W];
+  A st[D][N];
 #pragma unroll
   for (int d = 0; d < D; ++d)
 #pragma unroll
-    for (int i = 0; i < W; ++i) st[d][i] = A(0);
+    for (int i = 0; i < N; ++i) st[d][i] = A(0);
   for (int base = 0; base < nl; base += kLeafBatch) {
-    A l[kLeafBatch][W];
+    u32x4 raw[kLeafBatch][mm<M>()];
 #pragma unroll
     for (int k = 0; k < kLeafBatch; ++k) {
       const int idx = base + k < nl ? base + k : base;
-      load_user<DT, W>(ptrs.p[leaf[idx]], e, l[k]);
+      ld_user<DT, M, NT>(ptrs.p[leaf[idx]], e, ok, raw[k]);
     }
 #pragma unroll
     for (int k = 0; k < kLeafBatch; ++k) {
@@ -199,30 +270,30 @@ __device__ __forceinline__ void eval_one(const RankPtrs& ptrs, const int32_t* __
 #pragma unroll
         for (int d = D - 1; d > 0; --d)
 #pragma unroll
-          for (int i = 0; i < W; ++i) st[d][i] = st[d - 1][i];
-#pragma unroll
-        for (int i = 0; i < W; ++i) st[0][i] = l[k][i];
+          for (int i = 0; i < N; ++i) st[d][i] = st[d - 1][i];
+        widen<DT, M>(raw[k], st[0]);
         for (int c = nc[base + k]; c > 0; --c) {
 #pragma unroll
-          for (int i = 0; i < W; ++i) st[0][i] = cmb<OPK>(st[1][i], st[0][i]);
+          for (int i = 0; i < N; ++i) st[0][i] = cmb<OPK>(st[1][i], st[0][i]);
 #pragma unroll
           for (int d = 1; d < D - 1; ++d)
 #pragma unroll
-            for (int i = 0; i < W; ++i) st[d][i] = st[d + 1][i];
+            for (int i = 0; i < N; ++i) st[d][i] = st[d + 1][i];
         }
       }
     }
   }
 #pragma unroll
-  for (int i = 0; i < W; ++i) res[i] = st[0][i];
+  for (int i = 0; i < N; ++i) res[i] = st[0][i];
 }
 
-template <int DT, int OPK, int D, int TM, int W>
-__device__ __forceinline__ void replay(const RankPtrs& ptrs, const int32_t* __restrict__ w, int64_t e) {
+template <int DT, int OPK, int D, int TM, int M>
+__device__ __forceinline__ void replay(const RankPtrs& ptrs, const int32_t* __restrict__ w, int64_t e,
+                                       const bool (&ok)[mm<M>()]) {
   using A = typename TT<DT>::A;
   const int ntrees = w[0];
   w += 1;
-  A res[TM][W];
+  A res[TM][nvals<DT, M>()];
   const int32_t* outs[TM];
   int nouts[TM];
 #pragma unroll
@@ -231,30 +302,33 @@ __device__ __forceinline__ void replay(const RankPtrs& ptrs, const int32_t* __re
       const int nl = w[0];
       nouts[t] = w[1];
       outs[t] = w + 2 + 2 * nl;
-      eval_one<DT, OPK, D, W>(ptrs, w, e, res[t]);
+      eval_one<DT, OPK, D, M, TM == 1>(ptrs, w, e, ok, res[t]);
       w = outs[t] + nouts[t];
     }
   }
 #pragma unroll
   for (int t = 0; t < TM; ++t) {
     if (t < ntrees) {
-      for (int o = 0; o < nouts[t]; ++o) store_user<DT, W>(ptrs.p[outs[t][o]], e, res[t]);
+      for (int o = 0; o < nouts[t]; ++o) st_user<DT, M>(ptrs.p[outs[t][o]], e, ok, res[t]);
     }
   }
 }
+
+// Vectors per thread of the fused replay: two for shallow single-tree
+// programs, one where the register stack or several results need the room.
+template <int DT, int D, int TM> constexpr int fused_m() { return (TM == 1 && D <= 4) ? 2 : 1; }
 
 template <int DT, int OPK, int D, int TM>
 __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* __restrict__ items,
                                                     const int32_t* __restrict__ prog) {
   constexpr int V = TT<DT>::V;
+  constexpr int M = fused_m<DT, D, TM>();
   const Item it = items[blockIdx.x];
   const int32_t* w = prog + it.tag;
   if (it.count > 0) {
-    for (int v = threadIdx.x; v < it.count; v += kThreads)
-      replay<DT, OPK, D, TM, V>(ptrs, w, it.start + int64_t(v) * V);
+    for_fragments<M>(it, V, [&](int64_t e, const bool (&ok)[M]) { replay<DT, OPK, D, TM, M>(ptrs, w, e, ok); });
   } else {
-    const int cnt = -it.count;
-    for (int v = threadIdx.x; v < cnt; v += kThreads) replay<DT, OPK, D, TM, 1>(ptrs, w, it.start + v);
+    for_fragments<0>(it, V, [&](int64_t e, const bool (&ok)[1]) { replay<DT, OPK, D, TM, 0>(ptrs, w, e, ok); });
   }
 }
 
@@ -271,90 +345,110 @@ __device__ __forceinline__ void* slot_ptr(const RankPtrs& ptrs, const WsDesc& ws
   return slot == 0 ? ptrs.p[rank] : ws.base + (int64_t(slot - 1) * ws.P + rank) * ws.slot_bytes;
 }
 
-template <int DT, int W>
-__device__ __forceinline__ void load_slot(const RankPtrs& ptrs, const WsDesc& ws, int rank, int slot, int64_t e,
-                                          typename TT<DT>::A (&out)[W]) {
-  if (slot == 0) load_user<DT, W>(ptrs.p[rank], e, out);
-  else load_acc<DT, W>(slot_ptr(ptrs, ws, rank, slot), e, out);
-}
-
-template <int DT, int W>
-__device__ __forceinline__ void store_slot(const RankPtrs& ptrs, const WsDesc& ws, int rank, int slot, int64_t e,
-                                           const typename TT<DT>::A (&v)[W]) {
-  if (slot == 0) store_user<DT, W>(ptrs.p[rank], e, v);
-  else store_acc<DT, W>(slot_ptr(ptrs, ws, rank, slot), e, v);
-}
-
-template <int DT, int OPK, int W>
-__device__ __forceinline__ void literal_one(const RankPtrs& ptrs, const WsDesc& ws, const LitOp& op, int64_t e) {
-  using A = typename TT<DT>::A;
-  A s[W], r[W];
-  load_slot<DT, W>(ptrs, ws, op.src_rank, op.src_slot, e, s);
-  if (op.kind == K_REDUCE) {
-    A o[W];
-    load_slot<DT, W>(ptrs, ws, op.dst_rank, op.own_slot, e, o);
+template <int DT, int M>
+__device__ __forceinline__ void ld_slot(const RankPtrs& ptrs, const WsDesc& ws, int rank, int slot, int64_t e,
+                                        const bool (&ok)[mm<M>()], typename TT<DT>::A (&out)[nvals<DT, M>()]) {
+  if (slot == 0) {
+    u32x4 r[mm<M>()];
 #pragma unroll
-    for (int i = 0; i < W; ++i) r[i] = cmb<OPK>(o[i], s[i]);
+    for (int j = 0; j < mm<M>(); ++j) r[j] = u32x4{0, 0, 0, 0};
+    ld_user<DT, M>(ptrs.p[rank], e, ok, r);
+    widen<DT, M>(r, out);
+  } else {
+    ld_acc<DT, M>(slot_ptr(ptrs, ws, rank, slot), e, ok, out);
+  }
+}
+
+template <int DT, int M>
+__device__ __forceinline__ void st_slot(const RankPtrs& ptrs, const WsDesc& ws, int rank, int slot, int64_t e,
+                                        const bool (&ok)[mm<M>()], const typename TT<DT>::A (&v)[nvals<DT, M>()]) {
+  if (slot == 0) st_user<DT, M>(ptrs.p[rank], e, ok, v);
+  else st_acc<DT, M>(slot_ptr(ptrs, ws, rank, slot), e, ok, v);
+}
+
+template <int DT, int OPK, int M>
+__device__ __forceinline__ void literal_one(const RankPtrs& ptrs, const WsDesc& ws, const LitOp& op, int64_t e,
+                                            const bool (&ok)[mm<M>()]) {
+  using A = typename TT<DT>::A;
+  constexpr int N = nvals<DT, M>();
+  A s[N], r[N];
+  ld_slot<DT, M>(ptrs, ws, op.src_rank, op.src_slot, e, ok, s);
+  if (op.kind == K_REDUCE) {
+    A o[N];
+    ld_slot<DT, M>(ptrs, ws, op.dst_rank, op.own_slot, e, ok, o);
+#pragma unroll
+    for (int i = 0; i < N; ++i) r[i] = cmb<OPK>(o[i], s[i]);
   } else {
 #pragma unroll
-    for (int i = 0; i < W; ++i) r[i] = s[i];
+    for (int i = 0; i < N; ++i) r[i] = s[i];
   }
-  store_slot<DT, W>(ptrs, ws, op.dst_rank, op.dst_slot, e, r);
-  if (op.dst2_rank >= 0) store_slot<DT, W>(ptrs, ws, op.dst2_rank, op.dst2_slot, e, r);
+  st_slot<DT, M>(ptrs, ws, op.dst_rank, op.dst_slot, e, ok, r);
+  if (op.dst2_rank >= 0) st_slot<DT, M>(ptrs, ws, op.dst2_rank, op.dst2_slot, e, ok, r);
 }
 
 template <int DT, int OPK>
 __global__ __launch_bounds__(kThreads) void k_literal(RankPtrs ptrs, WsDesc ws, const Item* __restrict__ items,
                                                       const LitOp* __restrict__ ops) {
   constexpr int V = TT<DT>::V;
+  constexpr int M = 2;
   const Item it = items[blockIdx.x];
   const LitOp op = ops[it.tag];
   if (it.count > 0) {
-    for (int v = threadIdx.x; v < it.count; v += kThreads) literal_one<DT, OPK, V>(ptrs, ws, op, it.start + int64_t(v) * V);
+    for_fragments<M>(it, V, [&](int64_t e, const bool (&ok)[M]) { literal_one<DT, OPK, M>(ptrs, ws, op, e, ok); });
   } else {
-    const int cnt = -it.count;
-    for (int v = threadIdx.x; v < cnt; v += kThreads) literal_one<DT, OPK, 1>(ptrs, ws, op, it.start + v);
+    for_fragments<0>(it, V, [&](int64_t e, const bool (&ok)[1]) { literal_one<DT, OPK, 0>(ptrs, ws, op, e, ok); });
   }
 }
 
 // ----------------------------------------------------------------------------
 // direct: read all P, fold left to right, write all P
 // ----------------------------------------------------------------------------
-template <int DT, int OPK, int W>
-__device__ __forceinline__ void direct_one(const RankPtrs& ptrs, int P, int64_t e) {
+template <int DT, int OPK, int M>
+__device__ __forceinline__ void direct_one(const RankPtrs& ptrs, int P, int64_t e, const bool (&ok)[mm<M>()]) {
   using A = typename TT<DT>::A;
-  A acc[W];
+  constexpr int N = nvals<DT, M>();
+  A acc[N];
   for (int base = 0; base < P; base += kLeafBatch) {
-    A l[kLeafBatch][W];
+    u32x4 raw[kLeafBatch][mm<M>()];
 #pragma unroll
     for (int k = 0; k < kLeafBatch; ++k) {
       const int r = base + k < P ? base + k : base;
-      load_user<DT, W>(ptrs.p[r], e, l[k]);
+      ld_user<DT, M>(ptrs.p[r], e, ok, raw[k]);
     }
 #pragma unroll
     for (int k = 0; k < kLeafBatch; ++k) {
       if (base + k == 0) {
-#pragma unroll
-        for (int i = 0; i < W; ++i) acc[i] = l[0][i];
+        widen<DT, M>(raw[0], acc);
       } else if (base + k < P) {
+        A l[N];
+        widen<DT, M>(raw[k], l);
 #pragma unroll
-        for (int i = 0; i < W; ++i) acc[i] = cmb<OPK>(acc[i], l[k][i]);
+        for (int i = 0; i < N; ++i) acc[i] = cmb<OPK>(acc[i], l[i]);
       }
     }
   }
-  for (int p = 0; p < P; ++p) store_user<DT, W>(ptrs.p[p], e, acc);
+  for (int p = 0; p < P; ++p) st_user<DT, M>(ptrs.p[p], e, ok, acc);
 }
+
+constexpr int kDirectM = 2;
 
 template <int DT, int OPK, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_direct(RankPtrs ptrs, int P, int64_t nvec, int64_t total) {
   constexpr int V = TT<DT>::V;
-  const int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if constexpr (VEC) {
-    if (g < nvec) direct_one<DT, OPK, V>(ptrs, P, g * V);
-    if (blockIdx.x == 0)
-      for (int64_t e = nvec * V + threadIdx.x; e < total; e += kThreads) direct_one<DT, OPK, 1>(ptrs, P, e);
+    const int64_t vb = int64_t(blockIdx.x) * kThreads * kDirectM + threadIdx.x;
+    bool ok[kDirectM];
+#pragma unroll
+    for (int j = 0; j < kDirectM; ++j) ok[j] = vb + j * kThreads < nvec;
+    if (ok[0]) direct_one<DT, OPK, kDirectM>(ptrs, P, vb * V, ok);
+    if (blockIdx.x == 0) {
+      const bool one[1] = {true};
+      for (int64_t e = nvec * V + threadIdx.x; e < total; e += kThreads) direct_one<DT, OPK, 0>(ptrs, P, e, one);
+    }
   } else {
-    if (g < total) direct_one<DT, OPK, 1>(ptrs, P, g);
+    const int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    const bool one[1] = {true};
+    if (g < total) direct_one<DT, OPK, 0>(ptrs, P, g, one);
   }
 }
 
@@ -398,7 +492,7 @@ int64_t env_int(const char* name, int64_t dflt) {
 }
 
 void add_segment(std::vector<Item>& out, int64_t s0, int64_t len, int32_t tag, int V, bool vec) {
-  static const int64_t item_vec = env_int("AR_ITEM_VECTORS", kThreads);
+  static const int64_t item_vec = env_int("AR_ITEM_VECTORS", 2 * kThreads);
   const int64_t item_sc = kThreads;
   if (len <= 0) return;
   if (!vec) {
@@ -582,7 +676,7 @@ hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total,
   constexpr int V = TT<DT>::V;
   if (vec) {
     int64_t nvec = total / V;
-    int64_t blocks = std::max<int64_t>(1, (nvec + kThreads - 1) / kThreads);
+    int64_t blocks = std::max<int64_t>(1, (nvec + kThreads * kDirectM - 1) / (kThreads * kDirectM));
     hipLaunchKernelGGL((k_direct<DT, OPK, true>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, ptrs, P, nvec, total);
   } else {
     int64_t blocks = std::max<int64_t>(1, (total + kThreads - 1) / kThreads);
