@@ -65,7 +65,8 @@ class ar_call(C.Structure):
     _fields_ = [("P", C.c_int32), ("dtype", C.c_int32), ("op", C.c_int32), ("algo", C.c_int32),
                 ("knob", C.c_int32), ("exec", C.c_int32), ("n", C.c_int64), ("batch", C.c_int64),
                 ("ngroups", C.c_int32), ("groups", C.POINTER(C.c_int32)),
-                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
+                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+                ("start_event", C.c_void_p), ("stop_event", C.c_void_p)]
 
 
 class ar_oprec(C.Structure):
@@ -166,8 +167,14 @@ def _enum(table, v):
     return int(table[v]) if isinstance(v, str) else int(v)
 
 
+def _event(ev):
+    if ev is None or isinstance(ev, int):
+        return ev
+    return ev.cuda_event  # a torch.cuda.Event that has been recorded once (so it exists)
+
+
 def make_call(P, n, dtype, op="sum", algo="ring", knob=0, exec="fused", batch=1, groups=None,
-              workspace=None, workspace_bytes=0):
+              workspace=None, workspace_bytes=0, start_event=None, stop_event=None):
     call = ar_call()
     call.P, call.n, call.batch = int(P), int(n), int(batch)
     call.dtype, call.op = _enum(DTYPES, dtype), _enum(OPS, op)
@@ -180,6 +187,7 @@ def make_call(P, n, dtype, op="sum", algo="ring", knob=0, exec="fused", batch=1,
         call.ngroups, call.groups = 0, None
     call.workspace = workspace if isinstance(workspace, (int, type(None))) else workspace.data_ptr()
     call.workspace_bytes = int(workspace_bytes)
+    call.start_event, call.stop_event = _event(start_event), _event(stop_event)
     return call
 
 

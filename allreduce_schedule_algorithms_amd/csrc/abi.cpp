@@ -79,7 +79,8 @@ ar_status ar_allreduce_ex(void* const* bufs, const ar_call* call, void* stream) 
   if (!to_spec(call, &spec, &err)) return fail(AR_INVALID_ARGUMENT, err);
   ar_status st = check_bufs(bufs, spec.P);
   if (st != AR_OK) return st;
-  ar::RunResult r = ar::run_allreduce(bufs, spec, call->exec, call->workspace, call->workspace_bytes, stream);
+  ar::RunResult r = ar::run_allreduce(bufs, spec, call->exec, call->workspace, call->workspace_bytes, stream,
+                                      call->start_event, call->stop_event);
   t_hip = r.hip_error;
   if (r.status) return fail(ar_status(r.status), r.message);
   t_msg.clear();

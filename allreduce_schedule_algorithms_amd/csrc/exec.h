@@ -19,7 +19,8 @@ struct RunResult {
 
 // Enqueue one Allreduce on `stream`. Arguments have been validated.
 RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                        size_t workspace_bytes, void* stream, void* start_event = nullptr,
+                        void* stop_event = nullptr);
 
 // Workspace an AR_EXEC_LITERAL call needs for this spec (builds the schedule).
 RunResult literal_workspace_bytes(const Spec& spec, size_t* bytes);

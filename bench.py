@@ -8,7 +8,10 @@ copy (in-place sums grow the values) and the 256 MB Infinity Cache is flushed
 by writing a 1 GiB buffer, so each step starts cold from HBM.
 
 Essential bytes = P * n * elt read + P * n * elt written (every input read
-once, every output written once). value = essential bytes / mean step time.
+once, every output written once). value = essential bytes / mean time of the
+call between two events (launch latency included); roofline.achieved =
+essential bytes / mean device time of the call's kernel, from events the
+library records around its own launch.
 
 Default workload: 8 ranks x 2^20 fp32 N(0,1), recursive halving + doubling,
 fused replay (the schedule the workload names), with ring, direct and
@@ -65,7 +68,7 @@ ELT = {"fp32": 4, "bf16": 2, "int32": 4}
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "allreduce_schedule_algorithms_amd", "csrc", "exec.hip"), "rb") as f:
+    with open(os.path.join(ROOT, "allreduce_schedule_algorithms_amd", "csrc", "kernels.h"), "rb") as f:
         h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -101,15 +104,29 @@ class Runner:
         self.ptrs = [self.work[p].data_ptr() for p in range(wl["P"])]
         self.essential = 2.0 * wl["P"] * wl["n"] * wl["batch"] * ELT[wl["dtype"]]
 
-    def call_for(self, algo, knob, ex):
+    def call_for(self, algo, knob, ex, start_event=None, stop_event=None):
         wl = self.wl
-        return self.A.make_call(wl["P"], wl["n"], wl["dtype"], "sum", algo, knob, ex, wl["batch"], wl["groups"])
+        return self.A.make_call(wl["P"], wl["n"], wl["dtype"], "sum", algo, knob, ex, wl["batch"], wl["groups"],
+                                start_event=start_event, stop_event=stop_event)
 
-    def time(self, algo, knob, ex, steps, warmup, cold=True):
+    def time(self, algo, knob, ex, steps, warmup, cold=True, kernel_pass=True):
+        """Per step: (untimed) restore + flush, then the timed call.
+
+        Pass 1 brackets each plain call with two events on the library's stream
+        (what a caller waits for, launch latency included): value, ms_per_step.
+        Pass 2 repeats the steps with ar_call.start_event / stop_event, which the
+        library records at the start and end of its own kernels: the kernels'
+        device time, the figure rocprofv3's kernel trace reports.
+        """
         import torch
-        call = self.call_for(algo, knob, ex)
         st = self.stream
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
+        def ev():
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(st)  # creates the underlying hipEvent_t
+            return e
+
+        plain = self.call_for(algo, knob, ex)
 
         def prep():
             with torch.cuda.stream(st):
@@ -119,20 +136,32 @@ class Runner:
 
         for _ in range(warmup):
             prep()
-            self.A.ar_allreduce_ex(self.ptrs, call, st)
+            self.A.ar_allreduce_ex(self.ptrs, plain, st)
+        call_evs = [(ev(), ev()) for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(steps):
             prep()
-            evs[k][0].record(st)
-            self.A.ar_allreduce_ex(self.ptrs, call, st)
-            evs[k][1].record(st)
+            call_evs[k][0].record(st)
+            self.A.ar_allreduce_ex(self.ptrs, plain, st)
+            call_evs[k][1].record(st)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        ms = [a.elapsed_time(b) for a, b in evs]
+        ms = [a.elapsed_time(b) for a, b in call_evs]
         mean = statistics.fmean(ms)
-        return dict(ms=mean, ms_median=statistics.median(ms), ms_min=min(ms), wall_ms_per_step=1e3 * wall / steps,
-                    GBps=self.essential / (mean * 1e-3) / 1e9)
+        out = dict(ms=mean, ms_median=statistics.median(ms), ms_min=min(ms), wall_ms_per_step=1e3 * wall / steps,
+                   GBps=self.essential / (mean * 1e-3) / 1e9)
+        if kernel_pass:
+            kern_evs = [(ev(), ev()) for _ in range(steps)]
+            calls = [self.call_for(algo, knob, ex, a, b) for a, b in kern_evs]
+            torch.cuda.synchronize()
+            for k in range(steps):
+                prep()
+                self.A.ar_allreduce_ex(self.ptrs, calls[k], st)
+            torch.cuda.synchronize()
+            kmean = statistics.fmean([a.elapsed_time(b) for a, b in kern_evs])
+            out.update(kernel_ms=kmean, kernel_GBps=self.essential / (kmean * 1e-3) / 1e9)
+        return out
 
     def copy_ceiling(self, gib=2):
         import torch
@@ -197,6 +226,9 @@ def cpu_baseline(wl, x, budget_s=12.0):
 
 
 def load_traffic(wl_name, algo, knob, ex):
+    """HBM bytes per launch from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by what it reads for a plain copy of known size), or
+    None when the summary was taken from a different kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -205,11 +237,10 @@ def load_traffic(wl_name, algo, knob, ex):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    key = f"{wl_name}/{algo}/{knob}/{ex}"
-    rec = t.get(key)
-    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+    if t.get("kernel_hash") != kernel_source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    rec = t.get("entries", {}).get(f"{wl_name}/{algo}/{knob}/{ex}")
+    return rec.get("bytes_per_launch") if rec else None
 
 
 def main():
@@ -258,29 +289,33 @@ def main():
     if args.warm:
         for key in list(schedules):
             a2, k2, e2 = key.split("/")
-            schedules[key]["warm_GBps"] = r.time(a2, int(k2[1:]), e2, max(10, args.steps // 2), 2, cold=False)["GBps"]
+            schedules[key]["warm_GBps"] = r.time(a2, int(k2[1:]), e2, max(10, args.steps // 2), 2, cold=False,
+                                                 kernel_pass=False)["GBps"]
     for v in schedules.values():
         v["pct_hbm_peak"] = round(100.0 * v["GBps"] / HBM_PEAK_GBPS, 2)
-        for k in ("ms", "ms_median", "ms_min", "wall_ms_per_step", "GBps"):
-            v[k] = round(v[k], 5 if k.startswith("ms") else 2)
+        for k in ("ms", "ms_median", "ms_min", "kernel_ms", "wall_ms_per_step", "GBps", "kernel_GBps"):
+            if k in v:
+                v[k] = round(v[k], 5 if "ms" in k else 2)
     ceiling = r.copy_ceiling()
 
     # model bytes from the library's cost walk (fused / literal HBM bytes per call)
     import allreduce_schedule_algorithms_amd as A
     s = A.ar_schedule_build(r.call_for(algo, knob, ex))
     cst = s.cost()
-    achieved = head["GBps"]
+    value = head["GBps"]
+    achieved = head["kernel_GBps"]
     traffic = load_traffic(args.workload, algo, knob, ex)
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": "k_fused" if not (algo == "direct" and ex == "fused") else "k_direct",
+                "avg_launch_ms": head["kernel_ms"],
                 "algorithmic_bytes_per_launch": r.essential,
                 "model_bytes_per_launch": cst.fused_hbm_bytes if ex != "literal" else cst.literal_hbm_bytes}
 
     cpu = None if args.no_cpu else cpu_baseline(wl, x)
     line = {
         "metric": "allreduce essential GB/s (P·n in + P·n out) and % of HBM peak, per schedule",
-        "value": round(achieved, 2),
+        "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -293,8 +328,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {wl['desc']}", "P": wl["P"], "n": wl["n"], "batch": wl["batch"],
                    "schedule": algo, "knob": knob, "exec": ex, "cache": "cold (1 GiB flush before each step)"},
-        "pct_hbm_peak": round(100.0 * achieved / HBM_PEAK_GBPS, 2),
-        "copy_ceiling_GBps": round(ceiling, 1),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "runtime_copy_GBps": round(ceiling, 1),  # torch D2D copy of 2 GiB (HIP runtime blit), context only
         "wall_ms_per_step": head["wall_ms_per_step"],
         "roofline": roofline,
         "cpu_baseline": cpu,

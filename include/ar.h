@@ -115,6 +115,11 @@ typedef struct ar_call {
   void* workspace;         /* AR_EXEC_LITERAL: device scratch of ar_workspace_bytes() bytes, or
                               NULL to let the library allocate and cache one per device */
   size_t workspace_bytes;
+  void* start_event;       /* optional hipEvent_t (created by the caller): recorded when the
+                              call's first kernel starts */
+  void* stop_event;        /* optional hipEvent_t: recorded when the call's last kernel ends.
+                              With both set, hipEventElapsedTime gives the device time of the
+                              call's kernels without the launch latency in front of them */
 } ar_call;
 
 /* Plain Allreduce: fused execution, batch 1, no groups (AR_AHC needs ar_allreduce_ex).
