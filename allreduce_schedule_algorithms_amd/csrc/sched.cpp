@@ -229,8 +229,9 @@ static void gen_binomial(int P, Exprs& ex, Logical& lg) {
 }
 
 // AHC (HCCL "AHC" page): Lc x G chunks; ring reduce-scatter inside each group,
-// ring Allreduce per piece between the owners ("logical devices with
-// identical IDs") over G equal sub-pieces, ring all-gather inside each group.
+// ring Allreduce per piece between its owners, one per group (the page's
+// logical devices that share an ID), over G equal sub-pieces, ring all-gather
+// inside each group.
 static void gen_ahc(int P, const std::vector<int>& groups, Exprs& ex, Logical& lg) {
   int G = int(groups.size());
   int C = int(lcm_of(groups)) * G;

@@ -7,8 +7,8 @@
 // from (src rank, src slot) to (dst rank, dst slot), either combining it with
 // the destination rank's own operand (REDUCE) or overwriting (COPY). Every
 // operation touches the same element offsets in both ranks: the rows of the
-// generalized-Allreduce paper's data matrix are "data elements with the same
-// index number", and ring and AHC chunks are cut at the same offsets on every
+// generalized-Allreduce paper's data matrix gather one element index across all
+// processes, and ring and AHC chunks are cut at the same offsets on every
 // device. Slot 0 of a rank is the caller's buffer; slots >= 1 are workspace
 // buffers of the accumulation type.
 #pragma once

@@ -7,7 +7,7 @@ elements [lo, hi) of the sender's buffer to the receiver, which either adds
 them into its own copy of the same elements (REDUCE) or overwrites its copy
 (COPY). Every schedule here only ever exchanges elements at the same offset
 in every rank's buffer (the generalized-Allreduce paper's data matrix has
-"data elements with the same index number" as rows), so [lo, hi) is the same
+one element index per row, across all processes), so [lo, hi) is the same
 range at sender and receiver.
 
 The simulator can run on a sample of element offsets: ``idx`` lists the

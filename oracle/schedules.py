@@ -171,7 +171,7 @@ def _binomial(net: Net):
     clear and i + 2^k < P combines x_i <- x_i (+) x_{i+2^k}.
 
     Reading: the broadcast is the reverse of the reduce (the page says the
-    reverse procedure is commonly used to broadcast): for k from the top down,
+    same steps run backwards serve as a broadcast): for k from the top down,
     every rank i that is a multiple of 2^(k+1) with i + 2^k < P copies its
     buffer to i + 2^k.
     """
@@ -200,7 +200,7 @@ def _binomial(net: Net):
 def _ahc(net: Net, groups):
     """AHC (HCCL "AHC" page, Description, steps 1-3).
 
-    Groups are contiguous rank ranges ("adjacent NPUs"). With G groups and Lc
+    Groups are contiguous rank ranges (neighbouring devices form a group). With G groups and Lc
     the least common multiple of the group sizes, the buffer is cut into
     Lc * G chunks (ceil split). Group a of size g sees the buffer as g
     segments of C / g chunks each.
@@ -210,7 +210,7 @@ def _ahc(net: Net, groups):
        Segment k's partial sum ends at local rank (k - 1) mod g.
     2. The union of all groups' segment boundaries cuts the buffer into pieces;
        each piece lies in one segment of every group, and that segment's owner
-       in each group are the "logical devices with identical IDs". They run an
+       in each group are the page's logical devices that share an ID. They run an
        Allreduce per piece.
        Reading: the sub-algorithm is the ring (one of the three the page names;
        the other two are not described), over the owners in group order, with
@@ -316,7 +316,7 @@ def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: 
     Base reduction S_0 over vectors v_0..v_{N-1} (v_k = d_k initially): in step
     i, for k in [N_i - h_i, N_i), v_k is moved onto v_{k - h_i}'s placement
     (every rank sends its part of v_k to one rank, q - h_i) and combined into
-    it. When N_i is odd, v_0 sits the step out ("the first data vector").
+    it. When N_i is odd, v_0 sits the step out (the paper names the first vector).
     After L = ceil(log2 P) steps v_0 is the sum at placement 0: rank i holds
     part i (a reduce-scatter).
 
