@@ -232,8 +232,8 @@ struct Evs {
 };
 
 template <int DT, int OPK>
-hipError_t launch_fused_t(int D, int TM, int64_t nitems, const RankPtrs& ptrs, const Item* items, const int32_t* prog,
-                          hipStream_t st, Evs ev) {
+hipError_t launch_fused_t(int D, int TM, int P, int64_t nitems, const RankPtrs& ptrs, const Item* items,
+                          const int32_t* prog, hipStream_t st, Evs ev) {
   const dim3 g{unsigned(nitems), 1, 1};
   const dim3 b{unsigned(kThreads), 1, 1};
   if (TM == 1) {
@@ -242,6 +242,13 @@ hipError_t launch_fused_t(int D, int TM, int64_t nitems, const RankPtrs& ptrs, c
       case 4: hipExtLaunchKernelGGL((k_fused<DT, OPK, 4, 1>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog); break;
       case 8: hipExtLaunchKernelGGL((k_fused<DT, OPK, 8, 1>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog); break;
       default: hipExtLaunchKernelGGL((k_fused<DT, OPK, 16, 1>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog); break;
+    }
+  } else if (P <= kMaxStagedRanks) {
+    const uint32_t lds = uint32_t(P) * kThreads * sizeof(u32x4);
+    switch (D) {
+      case 2: hipExtLaunchKernelGGL((k_fused_staged<DT, OPK, 2>), g, b, lds, st, ev.start, ev.stop, 0, ptrs, items, prog, P); break;
+      case 4: hipExtLaunchKernelGGL((k_fused_staged<DT, OPK, 4>), g, b, lds, st, ev.start, ev.stop, 0, ptrs, items, prog, P); break;
+      default: hipExtLaunchKernelGGL((k_fused_staged<DT, OPK, 8>), g, b, lds, st, ev.start, ev.stop, 0, ptrs, items, prog, P); break;
     }
   } else {
     switch (D) {
@@ -401,8 +408,8 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
     const Item* items = reinterpret_cast<const Item*>(pl->items[mode].p);
     const int32_t* prog = reinterpret_cast<const int32_t*>(pl->prog.p);
     AR_DISPATCH(spec.dtype, spec.op,
-                (e = launch_fused_t<DT, OPK>(pl->D, pl->s->max_trees > 1 ? kMaxFusedTrees : 1, pl->nitems[mode], ptrs,
-                                             items, prog, st, ev)));
+                (e = launch_fused_t<DT, OPK>(pl->D, pl->s->max_trees > 1 ? kMaxFusedTrees : 1, spec.P, pl->nitems[mode],
+                                             ptrs, items, prog, st, ev)));
     if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
   }
   (void)V;

@@ -32,6 +32,7 @@ struct LitOp {
 constexpr int kThreads = 256;
 constexpr int kLeafBatch = 8;
 constexpr int kMaxFusedTrees = 8;  // distinct result trees per range the fused replay keeps in registers
+constexpr int kMaxStagedRanks = 16;  // ranks whose fragments fit the LDS staging of multi-tree ranges
 
 // ----------------------------------------------------------------------------
 // element types
@@ -152,6 +153,22 @@ __device__ __forceinline__ void st_user(void* base, int64_t e, const bool (&ok)[
   }
 }
 
+// Store one fragment to `cnt` ranks: rank_of(i) gives the i-th destination.
+// Destinations go 8 at a time so their pointer lookups (scalar loads) overlap.
+template <int DT, int M, typename RankOf>
+__device__ __forceinline__ void st_user_all(const RankPtrs& ptrs, int cnt, RankOf&& rank_of, int64_t e,
+                                            const bool (&ok)[mm<M>()],
+                                            const typename TT<DT>::A (&v)[nvals<DT, M>()]) {
+  for (int b = 0; b < cnt; b += kLeafBatch) {
+    void* pp[kLeafBatch];
+#pragma unroll
+    for (int k = 0; k < kLeafBatch; ++k) pp[k] = ptrs.p[rank_of(b + k < cnt ? b + k : b)];
+#pragma unroll
+    for (int k = 0; k < kLeafBatch; ++k)
+      if (b + k < cnt) st_user<DT, M>(pp[k], e, ok, v);
+  }
+}
+
 // Workspace slots hold the accumulation type (4 bytes per element).
 template <int DT, int M>
 __device__ __forceinline__ void ld_acc(const void* base, int64_t e, const bool (&ok)[mm<M>()],
@@ -222,9 +239,12 @@ __device__ __forceinline__ void for_fragments(const Item& it, int V, F&& f) {
 // each leaf), out rank[nouts]. Every tree reads the values from before the
 // call, so all trees of a range are evaluated before any result is stored
 // (results stay in registers; TM bounds the trees per range).
-template <int DT, int OPK, int D, int M, bool NT>
-__device__ __forceinline__ void eval_one(const RankPtrs& ptrs, const int32_t* __restrict__ w, int64_t e,
-                                         const bool (&ok)[mm<M>()], typename TT<DT>::A (&res)[nvals<DT, M>()]) {
+// Evaluate one tree's postfix program on a register stack of depth D. `leaf_at`
+// fetches the raw bits of a leaf rank's fragment (from HBM, or from LDS where
+// a range's leaves were staged once for several trees).
+template <int DT, int OPK, int D, int M, typename LeafAt>
+__device__ __forceinline__ void eval_one(const int32_t* __restrict__ w, LeafAt&& leaf_at,
+                                         typename TT<DT>::A (&res)[nvals<DT, M>()]) {
   using A = typename TT<DT>::A;
   constexpr int N = nvals<DT, M>();
   const int nl = w[0];
@@ -240,16 +260,18 @@ __device__ __forceinline__ void eval_one(const RankPtrs& ptrs, const int32_t* __
 #pragma unroll
     for (int k = 0; k < kLeafBatch; ++k) {
       const int idx = base + k < nl ? base + k : base;
-      ld_user<DT, M, NT>(ptrs.p[leaf[idx]], e, ok, raw[k]);
+      leaf_at(leaf[idx], raw[k]);
     }
 #pragma unroll
     for (int k = 0; k < kLeafBatch; ++k) {
       if (base + k < nl) {
+        // push: shift the stack down by one (static register moves), widen the leaf on top
 #pragma unroll
         for (int d = D - 1; d > 0; --d)
 #pragma unroll
           for (int i = 0; i < N; ++i) st[d][i] = st[d - 1][i];
         widen<DT, M>(raw[k], st[0]);
+        // each combination folds the top two entries and shifts the rest up
         for (int c = nc[base + k]; c > 0; --c) {
 #pragma unroll
           for (int i = 0; i < N; ++i) st[0][i] = cmb<OPK>(st[1][i], st[0][i]);
@@ -265,9 +287,9 @@ __device__ __forceinline__ void eval_one(const RankPtrs& ptrs, const int32_t* __
   for (int i = 0; i < N; ++i) res[i] = st[0][i];
 }
 
-template <int DT, int OPK, int D, int TM, int M>
+template <int DT, int OPK, int D, int TM, int M, typename LeafAt>
 __device__ __forceinline__ void replay(const RankPtrs& ptrs, const int32_t* __restrict__ w, int64_t e,
-                                       const bool (&ok)[mm<M>()]) {
+                                       const bool (&ok)[mm<M>()], LeafAt&& leaf_at) {
   using A = typename TT<DT>::A;
   const int ntrees = w[0];
   w += 1;
@@ -280,33 +302,87 @@ __device__ __forceinline__ void replay(const RankPtrs& ptrs, const int32_t* __re
       const int nl = w[0];
       nouts[t] = w[1];
       outs[t] = w + 2 + 2 * nl;
-      eval_one<DT, OPK, D, M, TM == 1>(ptrs, w, e, ok, res[t]);
+      eval_one<DT, OPK, D, M>(w, leaf_at, res[t]);
       w = outs[t] + nouts[t];
     }
   }
 #pragma unroll
   for (int t = 0; t < TM; ++t) {
     if (t < ntrees) {
-      for (int o = 0; o < nouts[t]; ++o) st_user<DT, M>(ptrs.p[outs[t][o]], e, ok, res[t]);
+      const int32_t* ot = outs[t];
+      st_user_all<DT, M>(ptrs, nouts[t], [&](int i) { return ot[i]; }, e, ok, res[t]);
     }
   }
 }
 
-// Vectors per thread of the fused replay: two for shallow single-tree
-// programs, one where the register stack or several results need the room.
-template <int DT, int D, int TM> constexpr int fused_m() { return (TM == 1 && D <= 4) ? 2 : 1; }
+// Vectors per thread of the fused replay: two for single-tree programs whose
+// register stack fits (depth <= 8 for 4-byte types, <= 4 for bf16, which widens
+// to twice the values per vector), one where the stack or several results
+// need the room.
+template <int DT, int D, int TM> constexpr int fused_m() {
+  return (TM == 1 && D <= (DT == D_BF16 ? 4 : 8)) ? 2 : 1;
+}
 
 template <int DT, int OPK, int D, int TM>
 __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* __restrict__ items,
                                                     const int32_t* __restrict__ prog) {
   constexpr int V = TT<DT>::V;
   constexpr int M = fused_m<DT, D, TM>();
+  constexpr bool NT = TM == 1;  // several trees re-read their leaves: keep them cacheable
   const Item it = items[blockIdx.x];
   const int32_t* w = prog + it.tag;
   if (it.count > 0) {
-    for_fragments<M>(it, V, [&](int64_t e, const bool (&ok)[M]) { replay<DT, OPK, D, TM, M>(ptrs, w, e, ok); });
+    for_fragments<M>(it, V, [&](int64_t e, const bool (&ok)[M]) {
+      replay<DT, OPK, D, TM, M>(ptrs, w, e, ok,
+                                [&](int rank, u32x4(&r)[M]) { ld_user<DT, M, NT>(ptrs.p[rank], e, ok, r); });
+    });
   } else {
-    for_fragments<0>(it, V, [&](int64_t e, const bool (&ok)[1]) { replay<DT, OPK, D, TM, 0>(ptrs, w, e, ok); });
+    for_fragments<0>(it, V, [&](int64_t e, const bool (&ok)[1]) {
+      replay<DT, OPK, D, TM, 0>(ptrs, w, e, ok,
+                                [&](int rank, u32x4(&r)[1]) { ld_user<DT, 0, NT>(ptrs.p[rank], e, ok, r); });
+    });
+  }
+}
+
+// Several result trees per range and few ranks: each thread loads its fragment of
+// every rank once (non-temporal) into its own LDS slots, then evaluates every tree
+// from LDS. Dynamic LDS holds P x kThreads 16-byte entries; each thread touches
+// only its own entries, so no barrier is needed.
+template <int DT, int OPK, int D>
+__global__ __launch_bounds__(kThreads) void k_fused_staged(RankPtrs ptrs, const Item* __restrict__ items,
+                                                           const int32_t* __restrict__ prog, int P) {
+  constexpr int V = TT<DT>::V;
+  extern __shared__ u32x4 stage[];
+  const Item it = items[blockIdx.x];
+  const int32_t* w = prog + it.tag;
+  if (it.count > 0) {
+    for_fragments<1>(it, V, [&](int64_t e, const bool (&ok)[1]) {
+      for (int base = 0; base < P; base += kLeafBatch) {
+        u32x4 raw[kLeafBatch][1];
+#pragma unroll
+        for (int k = 0; k < kLeafBatch; ++k) {
+          const int r = base + k < P ? base + k : base;
+          ld_user<DT, 1, true>(ptrs.p[r], e, ok, raw[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < kLeafBatch; ++k)
+          if (base + k < P) stage[(base + k) * kThreads + threadIdx.x] = raw[k][0];
+      }
+      replay<DT, OPK, D, kMaxFusedTrees, 1>(ptrs, w, e, ok, [&](int rank, u32x4(&r)[1]) {
+        r[0] = stage[rank * kThreads + threadIdx.x];
+      });
+    });
+  } else {
+    for_fragments<0>(it, V, [&](int64_t e, const bool (&ok)[1]) {
+      for (int rank = 0; rank < P; ++rank) {
+        u32x4 raw[1] = {u32x4{0, 0, 0, 0}};
+        ld_user<DT, 0, true>(ptrs.p[rank], e, ok, raw);
+        stage[rank * kThreads + threadIdx.x] = raw[0];
+      }
+      replay<DT, OPK, D, kMaxFusedTrees, 0>(ptrs, w, e, ok, [&](int rank, u32x4(&r)[1]) {
+        r[0] = stage[rank * kThreads + threadIdx.x];
+      });
+    });
   }
 }
 
@@ -405,7 +481,7 @@ __device__ __forceinline__ void direct_one(const RankPtrs& ptrs, int P, int64_t 
       }
     }
   }
-  for (int p = 0; p < P; ++p) st_user<DT, M>(ptrs.p[p], e, ok, acc);
+  st_user_all<DT, M>(ptrs, P, [](int i) { return i; }, e, ok, acc);
 }
 
 constexpr int kDirectM = 2;
