@@ -2,7 +2,7 @@
 
 This module only marshals arguments; every step of an Allreduce runs in the
 library's HIP kernels. Importing it loads the library and fails loudly when it
-is missing (build it with ``python -m allreduce_schedule_algorithms_amd.build_lib``).
+is missing (build it with ``python allreduce_schedule_algorithms_amd/build_lib.py``).
 """
 from __future__ import annotations
 
@@ -11,7 +11,9 @@ import enum
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libar_mi355x.so")
+# AR_LIBRARY may name another build of the same library (for example one built
+# with different compiler options); the default is the in-tree build.
+LIB_PATH = os.environ.get("AR_LIBRARY") or os.path.join(_HERE, "libar_mi355x.so")
 
 AR_MAX_RANKS = 256
 
@@ -126,7 +128,7 @@ def _load():
         pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m allreduce_schedule_algorithms_amd.build_lib` "
+            f"{LIB_PATH} is missing: build it with `python allreduce_schedule_algorithms_amd/build_lib.py` "
             "(there is no fallback path)")
     lib = C.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():

@@ -1,6 +1,7 @@
 """Build libar_mi355x.so in-tree with hipcc for gfx950.
 
-Usage: python -m allreduce_schedule_algorithms_amd.build_lib
+Usage: python allreduce_schedule_algorithms_amd/build_lib.py   (or __graft_entry__.build())
+Run it as a file, not as a package module: importing the package loads the library.
 """
 from __future__ import annotations
 
@@ -28,7 +29,7 @@ SOURCES = [
     ("sched.cpp", False),
     ("abi.cpp", False),
     ("exec.hip", True),
-]
+] + [(f"launch_{d}_{o}.hip", True) for d in ("i32", "f32", "bf16") for o in ("sum", "max")]
 
 
 def _compile(src: str, device: bool) -> str:
@@ -43,7 +44,7 @@ def _compile(src: str, device: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4, 16)) as ex:
         objs = list(ex.map(lambda s: _compile(*s), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs

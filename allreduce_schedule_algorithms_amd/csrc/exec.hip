@@ -31,7 +31,7 @@
 #include <vector>
 
 #include "exec.h"
-#include "kernels.h"
+#include "launch.h"
 
 namespace ar {
 
@@ -82,7 +82,11 @@ void add_segment(std::vector<Item>& out, int64_t s0, int64_t len, int32_t tag, i
     for (int64_t off = 0; off < len; off += item_sc) out.push_back({s0 + off, -int32_t(std::min(item_sc, len - off)), tag});
     return;
   }
-  int64_t head = (V - s0 % V) % V;
+  // Vector runs start on a 256-byte boundary (16 vectors of V elements): a wave's
+  // 1 KB access then covers whole 128-byte lines instead of splitting one line
+  // with the neighbouring wave. The peeled head goes through the element path.
+  const int64_t A = int64_t(V) * 16;
+  int64_t head = (A - s0 % A) % A;
   head = std::min(head, len);
   if (head) out.push_back({s0, -int32_t(head), tag});
   const int64_t b0 = s0 + head;
@@ -225,65 +229,6 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
 }
 
 // ---- kernel dispatch ----
-// Launches go through hipExtLaunchKernelGGL so that optional caller events can
-// be recorded at the kernel's own start and end.
-struct Evs {
-  hipEvent_t start = nullptr, stop = nullptr;
-};
-
-template <int DT, int OPK>
-hipError_t launch_fused_t(int D, int TM, int P, int64_t nitems, const RankPtrs& ptrs, const Item* items,
-                          const int32_t* prog, hipStream_t st, Evs ev) {
-  const dim3 g{unsigned(nitems), 1, 1};
-  const dim3 b{unsigned(kThreads), 1, 1};
-  if (TM == 1) {
-    switch (D) {
-      case 2: hipExtLaunchKernelGGL((k_fused<DT, OPK, 2, 1>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog); break;
-      case 4: hipExtLaunchKernelGGL((k_fused<DT, OPK, 4, 1>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog); break;
-      case 8: hipExtLaunchKernelGGL((k_fused<DT, OPK, 8, 1>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog); break;
-      default: hipExtLaunchKernelGGL((k_fused<DT, OPK, 16, 1>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog); break;
-    }
-  } else if (P <= kMaxStagedRanks) {
-    const uint32_t lds = uint32_t(P) * kThreads * sizeof(u32x4);
-    switch (D) {
-      case 2: hipExtLaunchKernelGGL((k_fused_staged<DT, OPK, 2>), g, b, lds, st, ev.start, ev.stop, 0, ptrs, items, prog, P); break;
-      case 4: hipExtLaunchKernelGGL((k_fused_staged<DT, OPK, 4>), g, b, lds, st, ev.start, ev.stop, 0, ptrs, items, prog, P); break;
-      default: hipExtLaunchKernelGGL((k_fused_staged<DT, OPK, 8>), g, b, lds, st, ev.start, ev.stop, 0, ptrs, items, prog, P); break;
-    }
-  } else {
-    switch (D) {
-      case 2: hipExtLaunchKernelGGL((k_fused<DT, OPK, 2, kMaxFusedTrees>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog); break;
-      case 4: hipExtLaunchKernelGGL((k_fused<DT, OPK, 4, kMaxFusedTrees>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog); break;
-      default: hipExtLaunchKernelGGL((k_fused<DT, OPK, 8, kMaxFusedTrees>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog); break;
-    }
-  }
-  return hipGetLastError();
-}
-
-template <int DT, int OPK>
-hipError_t launch_literal_t(int64_t nitems, const RankPtrs& ptrs, const WsDesc& ws, const Item* items,
-                            const LitOp* ops, hipStream_t st, Evs ev) {
-  hipExtLaunchKernelGGL((k_literal<DT, OPK>), dim3(unsigned(nitems)), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
-                        ptrs, ws, items, ops);
-  return hipGetLastError();
-}
-
-template <int DT, int OPK>
-hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total, hipStream_t st, Evs ev) {
-  constexpr int V = TT<DT>::V;
-  if (vec) {
-    int64_t nvec = total / V;
-    int64_t blocks = std::max<int64_t>(1, (nvec + kThreads * kDirectM - 1) / (kThreads * kDirectM));
-    hipExtLaunchKernelGGL((k_direct<DT, OPK, true>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
-                          ptrs, P, nvec, total);
-  } else {
-    int64_t blocks = std::max<int64_t>(1, (total + kThreads - 1) / kThreads);
-    hipExtLaunchKernelGGL((k_direct<DT, OPK, false>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
-                          ptrs, P, int64_t(0), total);
-  }
-  return hipGetLastError();
-}
-
 #define AR_DISPATCH(DTV, OPV, CALL)                                      \
   do {                                                                    \
     if ((DTV) == D_INT32 && (OPV) == O_SUM) { constexpr int DT = D_INT32, OPK = O_SUM; CALL; } \

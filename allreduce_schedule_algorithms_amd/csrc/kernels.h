@@ -242,7 +242,11 @@ __device__ __forceinline__ void for_fragments(const Item& it, int V, F&& f) {
 // Evaluate one tree's postfix program on a register stack of depth D. `leaf_at`
 // fetches the raw bits of a leaf rank's fragment (from HBM, or from LDS where
 // a range's leaves were staged once for several trees).
-template <int DT, int OPK, int D, int M, typename LeafAt>
+// Leaves are fetched B at a time with unconditional loads, so a batch is one
+// clause of loads in flight. The host picks B from the leaf count so that the
+// last batch is full where it can (B = 7 for seven leaves); otherwise the
+// missing slots repeat the batch's first leaf.
+template <int DT, int OPK, int D, int M, int B, typename LeafAt>
 __device__ __forceinline__ void eval_one(const int32_t* __restrict__ w, LeafAt&& leaf_at,
                                          typename TT<DT>::A (&res)[nvals<DT, M>()]) {
   using A = typename TT<DT>::A;
@@ -255,15 +259,12 @@ __device__ __forceinline__ void eval_one(const int32_t* __restrict__ w, LeafAt&&
   for (int d = 0; d < D; ++d)
 #pragma unroll
     for (int i = 0; i < N; ++i) st[d][i] = A(0);
-  for (int base = 0; base < nl; base += kLeafBatch) {
-    u32x4 raw[kLeafBatch][mm<M>()];
+  for (int base = 0; base < nl; base += B) {
+    u32x4 raw[B][mm<M>()];
 #pragma unroll
-    for (int k = 0; k < kLeafBatch; ++k) {
-      const int idx = base + k < nl ? base + k : base;
-      leaf_at(leaf[idx], raw[k]);
-    }
+    for (int k = 0; k < B; ++k) leaf_at(leaf[base + k < nl ? base + k : base], raw[k]);
 #pragma unroll
-    for (int k = 0; k < kLeafBatch; ++k) {
+    for (int k = 0; k < B; ++k) {
       if (base + k < nl) {
         // push: shift the stack down by one (static register moves), widen the leaf on top
 #pragma unroll
@@ -287,7 +288,7 @@ __device__ __forceinline__ void eval_one(const int32_t* __restrict__ w, LeafAt&&
   for (int i = 0; i < N; ++i) res[i] = st[0][i];
 }
 
-template <int DT, int OPK, int D, int TM, int M, typename LeafAt>
+template <int DT, int OPK, int D, int TM, int M, int B, typename LeafAt>
 __device__ __forceinline__ void replay(const RankPtrs& ptrs, const int32_t* __restrict__ w, int64_t e,
                                        const bool (&ok)[mm<M>()], LeafAt&& leaf_at) {
   using A = typename TT<DT>::A;
@@ -302,7 +303,7 @@ __device__ __forceinline__ void replay(const RankPtrs& ptrs, const int32_t* __re
       const int nl = w[0];
       nouts[t] = w[1];
       outs[t] = w + 2 + 2 * nl;
-      eval_one<DT, OPK, D, M>(w, leaf_at, res[t]);
+      eval_one<DT, OPK, D, M, B>(w, leaf_at, res[t]);
       w = outs[t] + nouts[t];
     }
   }
@@ -323,7 +324,7 @@ template <int DT, int D, int TM> constexpr int fused_m() {
   return (TM == 1 && D <= (DT == D_BF16 ? 4 : 8)) ? 2 : 1;
 }
 
-template <int DT, int OPK, int D, int TM>
+template <int DT, int OPK, int D, int TM, int B>
 __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* __restrict__ items,
                                                     const int32_t* __restrict__ prog) {
   constexpr int V = TT<DT>::V;
@@ -333,13 +334,13 @@ __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* _
   const int32_t* w = prog + it.tag;
   if (it.count > 0) {
     for_fragments<M>(it, V, [&](int64_t e, const bool (&ok)[M]) {
-      replay<DT, OPK, D, TM, M>(ptrs, w, e, ok,
-                                [&](int rank, u32x4(&r)[M]) { ld_user<DT, M, NT>(ptrs.p[rank], e, ok, r); });
+      replay<DT, OPK, D, TM, M, B>(ptrs, w, e, ok,
+                                   [&](int rank, u32x4(&r)[M]) { ld_user<DT, M, NT>(ptrs.p[rank], e, ok, r); });
     });
   } else {
     for_fragments<0>(it, V, [&](int64_t e, const bool (&ok)[1]) {
-      replay<DT, OPK, D, TM, 0>(ptrs, w, e, ok,
-                                [&](int rank, u32x4(&r)[1]) { ld_user<DT, 0, NT>(ptrs.p[rank], e, ok, r); });
+      replay<DT, OPK, D, TM, 0, B>(ptrs, w, e, ok,
+                                   [&](int rank, u32x4(&r)[1]) { ld_user<DT, 0, NT>(ptrs.p[rank], e, ok, r); });
     });
   }
 }
@@ -360,15 +361,13 @@ __global__ __launch_bounds__(kThreads) void k_fused_staged(RankPtrs ptrs, const 
       for (int base = 0; base < P; base += kLeafBatch) {
         u32x4 raw[kLeafBatch][1];
 #pragma unroll
-        for (int k = 0; k < kLeafBatch; ++k) {
-          const int r = base + k < P ? base + k : base;
-          ld_user<DT, 1, true>(ptrs.p[r], e, ok, raw[k]);
-        }
+        for (int k = 0; k < kLeafBatch; ++k)
+          if (base + k < P) ld_user<DT, 1, true>(ptrs.p[base + k], e, ok, raw[k]);
 #pragma unroll
         for (int k = 0; k < kLeafBatch; ++k)
           if (base + k < P) stage[(base + k) * kThreads + threadIdx.x] = raw[k][0];
       }
-      replay<DT, OPK, D, kMaxFusedTrees, 1>(ptrs, w, e, ok, [&](int rank, u32x4(&r)[1]) {
+      replay<DT, OPK, D, kMaxFusedTrees, 1, kLeafBatch>(ptrs, w, e, ok, [&](int rank, u32x4(&r)[1]) {
         r[0] = stage[rank * kThreads + threadIdx.x];
       });
     });
@@ -379,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_staged(RankPtrs ptrs, const 
         ld_user<DT, 0, true>(ptrs.p[rank], e, ok, raw);
         stage[rank * kThreads + threadIdx.x] = raw[0];
       }
-      replay<DT, OPK, D, kMaxFusedTrees, 0>(ptrs, w, e, ok, [&](int rank, u32x4(&r)[1]) {
+      replay<DT, OPK, D, kMaxFusedTrees, 0, kLeafBatch>(ptrs, w, e, ok, [&](int rank, u32x4(&r)[1]) {
         r[0] = stage[rank * kThreads + threadIdx.x];
       });
     });
@@ -457,20 +456,17 @@ __global__ __launch_bounds__(kThreads) void k_literal(RankPtrs ptrs, WsDesc ws, 
 // ----------------------------------------------------------------------------
 // direct: read all P, fold left to right, write all P
 // ----------------------------------------------------------------------------
-template <int DT, int OPK, int M>
+template <int DT, int OPK, int M, int B>
 __device__ __forceinline__ void direct_one(const RankPtrs& ptrs, int P, int64_t e, const bool (&ok)[mm<M>()]) {
   using A = typename TT<DT>::A;
   constexpr int N = nvals<DT, M>();
   A acc[N];
-  for (int base = 0; base < P; base += kLeafBatch) {
-    u32x4 raw[kLeafBatch][mm<M>()];
+  for (int base = 0; base < P; base += B) {
+    u32x4 raw[B][mm<M>()];
 #pragma unroll
-    for (int k = 0; k < kLeafBatch; ++k) {
-      const int r = base + k < P ? base + k : base;
-      ld_user<DT, M>(ptrs.p[r], e, ok, raw[k]);
-    }
+    for (int k = 0; k < B; ++k) ld_user<DT, M>(ptrs.p[base + k < P ? base + k : base], e, ok, raw[k]);
 #pragma unroll
-    for (int k = 0; k < kLeafBatch; ++k) {
+    for (int k = 0; k < B; ++k) {
       if (base + k == 0) {
         widen<DT, M>(raw[0], acc);
       } else if (base + k < P) {
@@ -486,7 +482,7 @@ __device__ __forceinline__ void direct_one(const RankPtrs& ptrs, int P, int64_t 
 
 constexpr int kDirectM = 2;
 
-template <int DT, int OPK, bool VEC>
+template <int DT, int OPK, bool VEC, int B>
 __global__ __launch_bounds__(kThreads) void k_direct(RankPtrs ptrs, int P, int64_t nvec, int64_t total) {
   constexpr int V = TT<DT>::V;
   if constexpr (VEC) {
@@ -494,15 +490,15 @@ __global__ __launch_bounds__(kThreads) void k_direct(RankPtrs ptrs, int P, int64
     bool ok[kDirectM];
 #pragma unroll
     for (int j = 0; j < kDirectM; ++j) ok[j] = vb + j * kThreads < nvec;
-    if (ok[0]) direct_one<DT, OPK, kDirectM>(ptrs, P, vb * V, ok);
+    if (ok[0]) direct_one<DT, OPK, kDirectM, B>(ptrs, P, vb * V, ok);
     if (blockIdx.x == 0) {
       const bool one[1] = {true};
-      for (int64_t e = nvec * V + threadIdx.x; e < total; e += kThreads) direct_one<DT, OPK, 0>(ptrs, P, e, one);
+      for (int64_t e = nvec * V + threadIdx.x; e < total; e += kThreads) direct_one<DT, OPK, 0, B>(ptrs, P, e, one);
     }
   } else {
     const int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x;
     const bool one[1] = {true};
-    if (g < total) direct_one<DT, OPK, 0>(ptrs, P, g, one);
+    if (g < total) direct_one<DT, OPK, 0, B>(ptrs, P, g, one);
   }
 }
 

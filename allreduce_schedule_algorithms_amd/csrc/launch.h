@@ -1,0 +1,150 @@
+// Kernel launch helpers, one explicit instantiation per (dtype, op) in the
+// launch_<dtype>_<op>.hip translation units (compiled in parallel).
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace ar {
+
+// Optional caller events recorded at a launch's own start and end.
+struct Evs {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+// Leaf batch for P leaves per tree: the size in [2, 8] that leaves the fewest
+// empty slots in the last batch (larger on ties).
+inline int leaf_batch(int P) {
+  int best = 8, waste = 1 << 30;
+  for (int b = 8; b >= 2; --b) {
+    int w = (P + b - 1) / b * b - P;
+    if (w < waste) { waste = w; best = b; }
+  }
+  return best;
+}
+
+template <int DT, int OPK>
+hipError_t launch_fused_t(int D, int TM, int P, int64_t nitems, const RankPtrs& ptrs, const Item* items,
+                          const int32_t* prog, hipStream_t st, Evs ev);
+template <int DT, int OPK>
+hipError_t launch_literal_t(int64_t nitems, const RankPtrs& ptrs, const WsDesc& ws, const Item* items,
+                            const LitOp* ops, hipStream_t st, Evs ev);
+template <int DT, int OPK>
+hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total, hipStream_t st, Evs ev);
+
+#ifdef AR_LAUNCH_DEFINITIONS
+// Launches go through hipExtLaunchKernelGGL so that optional caller events can
+// be recorded at the kernel's own start and end.
+
+// Leaf batch for P leaves per tree: the size in [2, 8] that leaves the fewest
+// empty slots in the last batch (larger on ties). Single-tree programs are
+// compiled for the (stack depth, batch) pairs that occur; others use 8.
+
+template <int DT, int OPK, int D, int B>
+void fused1(const dim3& g, const dim3& b, hipStream_t st, Evs ev, const RankPtrs& ptrs, const Item* items,
+            const int32_t* prog) {
+  hipExtLaunchKernelGGL((k_fused<DT, OPK, D, 1, B>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog);
+}
+
+template <int DT, int OPK>
+hipError_t launch_fused_t(int D, int TM, int P, int64_t nitems, const RankPtrs& ptrs, const Item* items,
+                          const int32_t* prog, hipStream_t st, Evs ev) {
+  const dim3 g{unsigned(nitems), 1, 1};
+  const dim3 b{unsigned(kThreads), 1, 1};
+  if (TM == 1) {
+    const int B = leaf_batch(P);
+    if (D == 2) {
+      switch (B) {
+        case 2: fused1<DT, OPK, 2, 2>(g, b, st, ev, ptrs, items, prog); break;
+        case 3: fused1<DT, OPK, 2, 3>(g, b, st, ev, ptrs, items, prog); break;
+        case 4: fused1<DT, OPK, 2, 4>(g, b, st, ev, ptrs, items, prog); break;
+        case 5: fused1<DT, OPK, 2, 5>(g, b, st, ev, ptrs, items, prog); break;
+        case 6: fused1<DT, OPK, 2, 6>(g, b, st, ev, ptrs, items, prog); break;
+        case 7: fused1<DT, OPK, 2, 7>(g, b, st, ev, ptrs, items, prog); break;
+        default: fused1<DT, OPK, 2, 8>(g, b, st, ev, ptrs, items, prog); break;
+      }
+    } else if (D == 4) {
+      switch (B) {
+        case 3: fused1<DT, OPK, 4, 3>(g, b, st, ev, ptrs, items, prog); break;
+        case 4: fused1<DT, OPK, 4, 4>(g, b, st, ev, ptrs, items, prog); break;
+        case 5: fused1<DT, OPK, 4, 5>(g, b, st, ev, ptrs, items, prog); break;
+        case 6: fused1<DT, OPK, 4, 6>(g, b, st, ev, ptrs, items, prog); break;
+        case 7: fused1<DT, OPK, 4, 7>(g, b, st, ev, ptrs, items, prog); break;
+        default: fused1<DT, OPK, 4, 8>(g, b, st, ev, ptrs, items, prog); break;
+      }
+    } else if (D == 8) {
+      switch (B) {
+        case 5: fused1<DT, OPK, 8, 5>(g, b, st, ev, ptrs, items, prog); break;
+        case 6: fused1<DT, OPK, 8, 6>(g, b, st, ev, ptrs, items, prog); break;
+        case 7: fused1<DT, OPK, 8, 7>(g, b, st, ev, ptrs, items, prog); break;
+        default: fused1<DT, OPK, 8, 8>(g, b, st, ev, ptrs, items, prog); break;
+      }
+    } else {
+      fused1<DT, OPK, 16, 8>(g, b, st, ev, ptrs, items, prog);
+    }
+  } else if (P <= kMaxStagedRanks) {
+    const uint32_t lds = uint32_t(P) * kThreads * sizeof(u32x4);
+    switch (D) {
+      case 2: hipExtLaunchKernelGGL((k_fused_staged<DT, OPK, 2>), g, b, lds, st, ev.start, ev.stop, 0, ptrs, items, prog, P); break;
+      case 4: hipExtLaunchKernelGGL((k_fused_staged<DT, OPK, 4>), g, b, lds, st, ev.start, ev.stop, 0, ptrs, items, prog, P); break;
+      default: hipExtLaunchKernelGGL((k_fused_staged<DT, OPK, 8>), g, b, lds, st, ev.start, ev.stop, 0, ptrs, items, prog, P); break;
+    }
+  } else {
+    switch (D) {
+      case 2: hipExtLaunchKernelGGL((k_fused<DT, OPK, 2, kMaxFusedTrees, 8>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog); break;
+      case 4: hipExtLaunchKernelGGL((k_fused<DT, OPK, 4, kMaxFusedTrees, 8>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog); break;
+      default: hipExtLaunchKernelGGL((k_fused<DT, OPK, 8, kMaxFusedTrees, 8>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+template <int DT, int OPK>
+hipError_t launch_literal_t(int64_t nitems, const RankPtrs& ptrs, const WsDesc& ws, const Item* items,
+                            const LitOp* ops, hipStream_t st, Evs ev) {
+  hipExtLaunchKernelGGL((k_literal<DT, OPK>), dim3(unsigned(nitems)), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
+                        ptrs, ws, items, ops);
+  return hipGetLastError();
+}
+
+template <int DT, int OPK, int B>
+void direct_b(bool vec, const RankPtrs& ptrs, int P, int64_t total, hipStream_t st, Evs ev) {
+  constexpr int V = TT<DT>::V;
+  if (vec) {
+    int64_t nvec = total / V;
+    int64_t blocks = std::max<int64_t>(1, (nvec + kThreads * kDirectM - 1) / (kThreads * kDirectM));
+    hipExtLaunchKernelGGL((k_direct<DT, OPK, true, B>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, ev.start,
+                          ev.stop, 0, ptrs, P, nvec, total);
+  } else {
+    int64_t blocks = std::max<int64_t>(1, (total + kThreads - 1) / kThreads);
+    hipExtLaunchKernelGGL((k_direct<DT, OPK, false, B>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, ev.start,
+                          ev.stop, 0, ptrs, P, int64_t(0), total);
+  }
+}
+
+template <int DT, int OPK>
+hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total, hipStream_t st, Evs ev) {
+  switch (leaf_batch(P)) {
+    case 2: direct_b<DT, OPK, 2>(vec, ptrs, P, total, st, ev); break;
+    case 3: direct_b<DT, OPK, 3>(vec, ptrs, P, total, st, ev); break;
+    case 4: direct_b<DT, OPK, 4>(vec, ptrs, P, total, st, ev); break;
+    case 5: direct_b<DT, OPK, 5>(vec, ptrs, P, total, st, ev); break;
+    case 6: direct_b<DT, OPK, 6>(vec, ptrs, P, total, st, ev); break;
+    case 7: direct_b<DT, OPK, 7>(vec, ptrs, P, total, st, ev); break;
+    default: direct_b<DT, OPK, 8>(vec, ptrs, P, total, st, ev); break;
+  }
+  return hipGetLastError();
+}
+
+
+#define AR_INSTANTIATE_LAUNCHES(DT, OPK)                                                                    \
+  template hipError_t launch_fused_t<DT, OPK>(int, int, int, int64_t, const RankPtrs&, const Item*,         \
+                                              const int32_t*, hipStream_t, Evs);                            \
+  template hipError_t launch_literal_t<DT, OPK>(int64_t, const RankPtrs&, const WsDesc&, const Item*,       \
+                                                const LitOp*, hipStream_t, Evs);                            \
+  template hipError_t launch_direct_t<DT, OPK>(bool, const RankPtrs&, int, int64_t, hipStream_t, Evs);
+#endif  // AR_LAUNCH_DEFINITIONS
+
+}  // namespace ar

@@ -1,0 +1,7 @@
+// Kernel instantiations for dtype i32, op sum.
+#define AR_LAUNCH_DEFINITIONS
+#include "launch.h"
+
+namespace ar {
+AR_INSTANTIATE_LAUNCHES(0, 0)
+}  // namespace ar

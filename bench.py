@@ -67,9 +67,11 @@ ELT = {"fp32": 4, "bf16": 2, "int32": 4}
 
 
 def kernel_source_hash() -> str:
+    """Hash of the device code and of the executor that lays out its work items."""
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "allreduce_schedule_algorithms_amd", "csrc", "kernels.h"), "rb") as f:
-        h.update(f.read())
+    for name in ("kernels.h", "launch.h", "exec.hip"):
+        with open(os.path.join(ROOT, "allreduce_schedule_algorithms_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
