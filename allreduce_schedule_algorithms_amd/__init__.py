@@ -8,9 +8,10 @@ from __future__ import annotations
 
 from . import _ar
 from ._ar import (  # noqa: F401
-    ALGOS, DTYPES, EXECS, OPS, Algo, ArError, Dtype, Exec, Op, Schedule, Status, ar_allreduce,
-    ar_allreduce_ex, ar_last_error_message, ar_last_hip_error, ar_schedule_build, ar_status_string,
-    ar_table_check, ar_version, ar_workspace_bytes, make_call,
+    ALGO_NAMES, ALGOS, AR_KNOB_AUTO, COST_FORMS, DTYPES, EXECS, OPS, Algo, ArError, CostForm, Dtype, Exec,
+    Op, Schedule, Status, ar_allreduce, ar_allreduce_ex, ar_get_cost_model, ar_last_error_message,
+    ar_last_hip_error, ar_schedule_build, ar_select, ar_set_cost_model, ar_status_string, ar_table_check,
+    ar_version, ar_workspace_bytes, make_call,
 )
 
 _TORCH_DTYPE = {"int32": "int32", "fp32": "float32", "bf16": "bfloat16"}

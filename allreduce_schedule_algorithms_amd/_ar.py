@@ -47,6 +47,15 @@ class Algo(enum.IntEnum):
     AR_GENERALIZED = 5
     AR_GENERALIZED_XOR = 6
     AR_AHC = 7
+    AR_AUTO = -1
+
+
+AR_KNOB_AUTO = -1
+
+
+class CostForm(enum.IntEnum):
+    AR_COST_BUSIEST_RANK = 0
+    AR_COST_ALL_RANKS = 1
 
 
 class Exec(enum.IntEnum):
@@ -59,7 +68,9 @@ DTYPES = {"int32": Dtype.AR_INT32, "fp32": Dtype.AR_FP32, "bf16": Dtype.AR_BF16}
 OPS = {"sum": Op.AR_SUM, "max": Op.AR_MAX}
 ALGOS = {"direct": Algo.AR_DIRECT, "ring": Algo.AR_RING, "rh_rd": Algo.AR_RH_RD, "rd": Algo.AR_RD,
          "binomial": Algo.AR_BINOMIAL, "generalized": Algo.AR_GENERALIZED,
-         "generalized_xor": Algo.AR_GENERALIZED_XOR, "ahc": Algo.AR_AHC}
+         "generalized_xor": Algo.AR_GENERALIZED_XOR, "ahc": Algo.AR_AHC, "auto": Algo.AR_AUTO}
+ALGO_NAMES = {int(v): k for k, v in ALGOS.items()}
+COST_FORMS = {"busiest": CostForm.AR_COST_BUSIEST_RANK, "all_ranks": CostForm.AR_COST_ALL_RANKS}
 EXECS = {"fused": Exec.AR_EXEC_FUSED, "literal": Exec.AR_EXEC_LITERAL, "replay": Exec.AR_EXEC_REPLAY}
 
 
@@ -93,6 +104,11 @@ class ar_cost(C.Structure):
                 ("essential_bytes", C.c_double)]
 
 
+class ar_cost_model(C.Structure):
+    _fields_ = [("alpha", C.c_double), ("beta", C.c_double), ("gamma", C.c_double), ("form", C.c_int32),
+                ("reserved", C.c_int32)]
+
+
 # exported symbol -> (restype, argtypes)
 SIGNATURES = {
     "ar_allreduce": (C.c_int, [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_int32,
@@ -110,6 +126,10 @@ SIGNATURES = {
                                  C.POINTER(C.c_int32)]),
     "ar_cost_report": (C.c_int, [C.c_void_p, C.c_double, C.c_double, C.c_double, C.POINTER(ar_cost)]),
     "ar_cost_steps": (C.c_int, [C.c_void_p, C.POINTER(C.c_int64), C.POINTER(C.c_int64), C.POINTER(C.c_int64)]),
+    "ar_set_cost_model": (C.c_int, [C.POINTER(ar_cost_model)]),
+    "ar_get_cost_model": (C.c_int, [C.POINTER(ar_cost_model)]),
+    "ar_select": (C.c_int, [C.POINTER(ar_call), C.POINTER(C.c_int32), C.POINTER(C.c_int32),
+                            C.POINTER(C.c_double)]),
     "ar_status_string": (C.c_char_p, [C.c_int]),
     "ar_last_hip_error": (C.c_int32, []),
     "ar_last_error_message": (C.c_char_p, []),
@@ -221,6 +241,29 @@ def ar_table_check(P, n, dtype, ops) -> bool:
     sp = C.c_int32(0)
     _check(lib.ar_table_check(int(P), int(n), _enum(DTYPES, dtype), arr, len(ops), C.byref(sp)))
     return bool(sp.value)
+
+
+def ar_set_cost_model(alpha=None, beta=None, gamma=None, form="all_ranks"):
+    """Set the process-wide model; with no arguments restore the default."""
+    if alpha is None and beta is None and gamma is None:
+        _check(lib.ar_set_cost_model(None))
+        return
+    m = ar_cost_model(float(alpha), float(beta), float(gamma), _enum(COST_FORMS, form), 0)
+    _check(lib.ar_set_cost_model(C.byref(m)))
+
+
+def ar_get_cost_model() -> dict:
+    m = ar_cost_model()
+    _check(lib.ar_get_cost_model(C.byref(m)))
+    names = {int(v): k for k, v in COST_FORMS.items()}
+    return dict(alpha=m.alpha, beta=m.beta, gamma=m.gamma, form=names[m.form])
+
+
+def ar_select(call: ar_call):
+    """(algorithm name, knob, model seconds) of the schedule the call runs."""
+    a, k, t = C.c_int32(0), C.c_int32(0), C.c_double(0)
+    _check(lib.ar_select(C.byref(call), C.byref(a), C.byref(k), C.byref(t)))
+    return ALGO_NAMES[a.value], k.value, t.value
 
 
 def ar_status_string(st) -> str:

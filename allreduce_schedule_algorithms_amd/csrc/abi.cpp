@@ -2,7 +2,10 @@
 #include "../../include/ar.h"
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -21,6 +24,40 @@ ar_status fail(ar_status st, const std::string& m) {
   return st;
 }
 
+// Process-wide cost model for AR_AUTO / AR_KNOB_AUTO and the choices made under it.
+// Default: least-squares fit of AR_EXEC_LITERAL fp32 calls on MI355X (P = 7 and 8,
+// 2^10..2^22 elements, every schedule and r), one launch per step, all ranks'
+// bytes through one HBM.
+constexpr ar::CostModel kDefaultModel{3.66e-6, 2.04e-13, 2.19e-13, ar::F_ALL_RANKS};
+std::mutex g_model_mu;
+ar::CostModel g_model = kDefaultModel;
+std::map<std::string, std::pair<ar::Spec, double>> g_choices;
+
+std::string choice_key(const ar::Spec& s) {
+  std::string k = std::to_string(s.P) + "/" + std::to_string(s.n) + "/" + std::to_string(s.batch) + "/" +
+                  std::to_string(s.dtype) + "/" + std::to_string(s.op) + "/" + std::to_string(s.algo) + "/" +
+                  std::to_string(s.knob) + "/";
+  for (int g : s.groups) k += std::to_string(g) + ",";
+  return k;
+}
+
+// Replace an AR_AUTO / AR_KNOB_AUTO spec by the model's choice (cached per spec).
+bool resolve(ar::Spec* s, double* seconds, std::string* err) {
+  std::lock_guard<std::mutex> lk(g_model_mu);
+  const std::string key = choice_key(*s);
+  auto it = g_choices.find(key);
+  if (it == g_choices.end()) {
+    ar::Spec out;
+    double t = 0;
+    if (!ar::select_spec(*s, g_model, &out, &t, err)) return false;
+    if (g_choices.size() > 4096) g_choices.clear();
+    it = g_choices.emplace(key, std::make_pair(out, t)).first;
+  }
+  *s = it->second.first;
+  if (seconds) *seconds = it->second.second;
+  return true;
+}
+
 bool to_spec(const ar_call* c, ar::Spec* s, std::string* err) {
   if (!c) { *err = "call is NULL"; return false; }
   s->P = c->P;
@@ -35,8 +72,16 @@ bool to_spec(const ar_call* c, ar::Spec* s, std::string* err) {
     if (c->ngroups < 1 || !c->groups) { *err = "AHC needs ngroups >= 1 and a groups array"; return false; }
     if (c->ngroups > AR_MAX_RANKS) { *err = "too many AHC groups"; return false; }
     s->groups.assign(c->groups, c->groups + c->ngroups);
+  } else if (c->algo == AR_AUTO && c->ngroups != 0) {
+    if (c->ngroups < 0 || !c->groups) { *err = "ngroups > 0 needs a groups array"; return false; }
+    if (c->ngroups > AR_MAX_RANKS) { *err = "too many AHC groups"; return false; }
+    s->groups.assign(c->groups, c->groups + c->ngroups);
+    ar::Spec probe = *s;
+    probe.algo = ar::A_AHC;
+    if (!ar::validate_spec(probe, err)) return false;
   }
   if (c->exec < AR_EXEC_FUSED || c->exec > AR_EXEC_REPLAY) { *err = "unknown exec mode"; return false; }
+  if (ar::is_auto(*s)) return resolve(s, nullptr, err);
   return ar::validate_spec(*s, err);
 }
 
@@ -56,6 +101,52 @@ ar_status check_bufs(void* const* bufs, int P) {
 }  // namespace
 
 extern "C" {
+
+ar_status ar_set_cost_model(const ar_cost_model* m) {
+  ar::CostModel cm = kDefaultModel;
+  if (m) {
+    if (!(std::isfinite(m->alpha) && std::isfinite(m->beta) && std::isfinite(m->gamma)) || m->alpha < 0 ||
+        m->beta < 0 || m->gamma < 0)
+      return fail(AR_INVALID_ARGUMENT, "alpha, beta, gamma must be finite and >= 0");
+    if (m->form != AR_COST_BUSIEST_RANK && m->form != AR_COST_ALL_RANKS)
+      return fail(AR_INVALID_ARGUMENT, "unknown cost form");
+    cm = ar::CostModel{m->alpha, m->beta, m->gamma, m->form};
+  }
+  std::lock_guard<std::mutex> lk(g_model_mu);
+  g_model = cm;
+  g_choices.clear();
+  return AR_OK;
+}
+
+ar_status ar_get_cost_model(ar_cost_model* m) {
+  if (!m) return fail(AR_INVALID_ARGUMENT, "model is NULL");
+  std::lock_guard<std::mutex> lk(g_model_mu);
+  m->alpha = g_model.alpha;
+  m->beta = g_model.beta;
+  m->gamma = g_model.gamma;
+  m->form = g_model.form;
+  m->reserved = 0;
+  return AR_OK;
+}
+
+ar_status ar_select(const ar_call* call, int32_t* algo, int32_t* knob, double* predicted_seconds) {
+  std::string err;
+  ar::Spec spec;
+  if (!to_spec(call, &spec, &err)) return fail(AR_INVALID_ARGUMENT, err);
+  double t = 0;
+  if (predicted_seconds) {
+    ar::CostModel cm;
+    {
+      std::lock_guard<std::mutex> lk(g_model_mu);
+      cm = g_model;
+    }
+    if (!ar::select_spec(spec, cm, &spec, &t, &err)) return fail(AR_INVALID_ARGUMENT, err);
+    *predicted_seconds = t;
+  }
+  if (algo) *algo = spec.algo;
+  if (knob) *knob = spec.knob;
+  return AR_OK;
+}
 
 const char* ar_status_string(ar_status st) {
   switch (st) {

@@ -322,7 +322,7 @@ static void gen_generalized(int P, int r, bool use_xor, Exprs& ex, Logical& lg) 
   for (int i = 0; i < L; ++i) {
     lg.steps.emplace_back();
     auto& st = lg.steps.back();
-    std::set<std::tuple<int, int, int>> seen;
+    std::unordered_set<uint64_t> seen;  // (dst, atom, result) already combined this step
     auto nv = vals;
     for (int j = 0; j < J; ++j)
       for (int k = N[i] - h[i]; k < N[i]; ++k) {
@@ -332,7 +332,8 @@ static void gen_generalized(int P, int r, bool use_xor, Exprs& ex, Logical& lg) 
           int sv = vals[j][k][a], ov = vals[j][tgt][a];
           int out = ex.combine(ov, sv);
           int src = holder(a, pls), dst = holder(a, pld);
-          if (seen.insert({dst, a, out}).second) st.push_back({K_REDUCE, src, dst, a, sv, ov, out});
+          if (seen.insert((uint64_t(uint32_t(out)) << 16) | (uint64_t(dst) << 8) | uint64_t(a)).second)
+            st.push_back({K_REDUCE, src, dst, a, sv, ov, out});
           nv[j][tgt][a] = out;
         }
       }
@@ -762,24 +763,33 @@ static bool plan_fused(Schedule& s, std::string* err) {
 // ----------------------------------------------------------------------------
 // build
 // ----------------------------------------------------------------------------
+static bool generate(const Spec& spec, Exprs& ex, Logical& lg, std::string* err) {
+  const int P = spec.P;
+  if (P <= 1) return true;
+  switch (spec.algo) {
+    case A_DIRECT: gen_direct(P, ex, lg); break;
+    case A_RING: gen_ring(P, ex, lg); break;
+    case A_RH_RD: gen_rh_rd(P, ex, lg); break;
+    case A_RD: gen_rd(P, ex, lg); break;
+    case A_BINOMIAL: gen_binomial(P, ex, lg); break;
+    case A_GENERALIZED: gen_generalized(P, spec.knob, false, ex, lg); break;
+    case A_GENERALIZED_XOR: gen_generalized(P, spec.knob, true, ex, lg); break;
+    case A_AHC: gen_ahc(P, spec.groups, ex, lg); break;
+    default: if (err) *err = "unknown algorithm"; return false;
+  }
+  return true;
+}
+
 Schedule* build_schedule(const Spec& spec, std::string* err) {
+  if (is_auto(spec)) {
+    if (err) *err = "resolve AR_AUTO / AR_KNOB_AUTO before building";
+    return nullptr;
+  }
   if (!validate_spec(spec, err)) return nullptr;
   const int P = spec.P;
   Exprs ex(P);
   Logical lg;
-  if (P > 1) {
-    switch (spec.algo) {
-      case A_DIRECT: gen_direct(P, ex, lg); break;
-      case A_RING: gen_ring(P, ex, lg); break;
-      case A_RH_RD: gen_rh_rd(P, ex, lg); break;
-      case A_RD: gen_rd(P, ex, lg); break;
-      case A_BINOMIAL: gen_binomial(P, ex, lg); break;
-      case A_GENERALIZED: gen_generalized(P, spec.knob, false, ex, lg); break;
-      case A_GENERALIZED_XOR: gen_generalized(P, spec.knob, true, ex, lg); break;
-      case A_AHC: gen_ahc(P, spec.groups, ex, lg); break;
-      default: if (err) *err = "unknown algorithm"; return nullptr;
-    }
-  }
+  if (!generate(spec, ex, lg, err)) return nullptr;
   auto s = std::make_unique<Schedule>();
   s->spec = spec;
   s->nsteps = int(lg.steps.size());
@@ -923,6 +933,7 @@ CostOut cost_walk(const Schedule& s, double alpha, double beta, double gamma) {
   if (s.nsteps) cost_steps(s, sent.data(), recv.data(), red.data());
   std::vector<int64_t> rank_sent(P, 0), rank_red(P, 0);
   double t = 0;
+  int64_t xb = 0, xg = 0;
   for (int st = 0; st < s.nsteps; ++st) {
     int64_t ms = 0, mr = 0, md = 0;
     for (int p = 0; p < P; ++p) {
@@ -938,8 +949,10 @@ CostOut cost_walk(const Schedule& s, double alpha, double beta, double gamma) {
     c.sent_busiest += ms;
     c.recv_busiest += mr;
     c.reduced_busiest += md;
-    t += alpha + double(std::max(ms, mr)) * batch * elt * beta + double(md) * batch * elt * gamma;
+    xb += std::max(ms, mr);
+    xg += md;
   }
+  t = alpha * double(s.nsteps) + beta * (double(xb) * elt * batch) + gamma * (double(xg) * elt * batch);
   c.max_rank_sent = P ? *std::max_element(rank_sent.begin(), rank_sent.end()) : 0;
   c.max_rank_reduced = P ? *std::max_element(rank_red.begin(), rank_red.end()) : 0;
   c.predicted_seconds = t;
@@ -977,6 +990,128 @@ CostOut cost_walk(const Schedule& s, double alpha, double beta, double gamma) {
   c.fused_hbm_bytes = fz;
   c.essential_bytes = 2.0 * P * double(s.spec.n) * batch * elt;
   return c;
+}
+
+// ----------------------------------------------------------------------------
+// cost-only step counts and model-driven selection
+// ----------------------------------------------------------------------------
+bool is_auto(const Spec& s) {
+  return s.algo == kAutoAlgo ||
+         ((s.algo == A_GENERALIZED || s.algo == A_GENERALIZED_XOR) && s.knob == kAutoKnob);
+}
+
+bool step_counts(const Spec& spec, StepCounts* out, std::string* err) {
+  if (!validate_spec(spec, err)) return false;
+  const int P = spec.P;
+  *out = StepCounts{};
+  if (spec.n == 0 || P <= 1) return true;  // nothing moves: no steps
+  Exprs ex(P);
+  Logical lg;
+  if (!generate(spec, ex, lg, err)) return false;
+  const auto atoms = partition(spec.n, lg.C);
+  const int S = int(lg.steps.size());
+  out->nsteps = S;
+  out->sent.assign(size_t(S) * P, 0);
+  out->recv.assign(size_t(S) * P, 0);
+  out->reduced.assign(size_t(S) * P, 0);
+  std::unordered_set<uint64_t> msgs;
+  for (int st = 0; st < S; ++st) {
+    msgs.clear();
+    int64_t* sent = out->sent.data() + size_t(st) * P;
+    int64_t* recv = out->recv.data() + size_t(st) * P;
+    int64_t* red = out->reduced.data() + size_t(st) * P;
+    for (const LOp& o : lg.steps[st]) {
+      int64_t len = atoms[o.atom].second - atoms[o.atom].first;
+      if (len <= 0) continue;
+      // value ids fit 31 bits, ranks 8, atoms 17 (AHC: lcm * G <= 65536)
+      uint64_t key = (uint64_t(uint32_t(o.src_val)) << 33) | (uint64_t(o.src) << 25) |
+                     (uint64_t(o.dst) << 17) | uint64_t(o.atom);
+      if (msgs.insert(key).second) {
+        sent[o.src] += len;
+        recv[o.dst] += len;
+      }
+      if (o.kind == K_REDUCE) red[o.dst] += len;
+    }
+  }
+  return true;
+}
+
+double model_seconds(const StepCounts& c, const Spec& spec, const CostModel& m) {
+  const int P = spec.P;
+  int64_t xb = 0, xg = 0;
+  for (int st = 0; st < c.nsteps; ++st) {
+    const int64_t* sent = c.sent.data() + size_t(st) * P;
+    const int64_t* recv = c.recv.data() + size_t(st) * P;
+    const int64_t* red = c.reduced.data() + size_t(st) * P;
+    if (m.form == F_BUSIEST) {
+      int64_t mb = 0, mg = 0;
+      for (int p = 0; p < P; ++p) {
+        mb = std::max(mb, std::max(sent[p], recv[p]));
+        mg = std::max(mg, red[p]);
+      }
+      xb += mb;
+      xg += mg;
+    } else {
+      for (int p = 0; p < P; ++p) {
+        xb += sent[p];
+        xg += red[p];
+      }
+    }
+  }
+  const double elt = elt_bytes(spec.dtype);
+  const double batch = double(spec.batch);
+  return m.alpha * double(c.nsteps) + m.beta * (double(xb) * elt * batch) + m.gamma * (double(xg) * elt * batch);
+}
+
+bool select_spec(const Spec& in, const CostModel& m, Spec* out, double* seconds, std::string* err) {
+  auto fail = [&](const std::string& msg) { if (err) *err = msg; return false; };
+  if (!is_auto(in)) {
+    *out = in;
+    if (seconds) {
+      StepCounts c;
+      if (!step_counts(in, &c, err)) return false;
+      *seconds = model_seconds(c, in, m);
+    }
+    return true;
+  }
+  if (!(std::isfinite(m.alpha) && std::isfinite(m.beta) && std::isfinite(m.gamma)) || m.alpha < 0 ||
+      m.beta < 0 || m.gamma < 0)
+    return fail("the cost model needs finite, non-negative alpha, beta, gamma");
+  if (in.P < 1 || in.P > kMaxRanks) return fail("P must be in [1, 256]");
+  const int L = ceil_log2(in.P);
+  const bool pow2 = (in.P & (in.P - 1)) == 0;
+  std::vector<std::pair<int, int>> cand;  // (algo, knob), in the order ties are broken
+  if (in.algo == kAutoAlgo) {
+    for (int a : {A_DIRECT, A_RING, A_RH_RD, A_RD, A_BINOMIAL}) cand.push_back({a, 0});
+    for (int r = 0; r <= L; ++r) cand.push_back({A_GENERALIZED, r});
+    if (pow2)
+      for (int r = 0; r <= L; ++r) cand.push_back({A_GENERALIZED_XOR, r});
+    if (!in.groups.empty()) cand.push_back({A_AHC, 0});
+  } else {
+    for (int r = 0; r <= L; ++r) cand.push_back({in.algo, r});
+  }
+  bool have = false;
+  double best_t = 0;
+  int best_steps = 0;
+  Spec best;
+  for (auto [a, r] : cand) {
+    Spec c = in;
+    c.algo = a;
+    c.knob = r;
+    if (a != A_AHC) c.groups.clear();
+    StepCounts sc;
+    if (!step_counts(c, &sc, err)) return false;
+    double t = model_seconds(sc, c, m);
+    if (!have || t < best_t || (t == best_t && sc.nsteps < best_steps)) {
+      have = true;
+      best_t = t;
+      best_steps = sc.nsteps;
+      best = c;
+    }
+  }
+  *out = best;
+  if (seconds) *seconds = best_t;
+  return true;
 }
 
 }  // namespace ar

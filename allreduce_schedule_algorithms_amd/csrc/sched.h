@@ -138,6 +138,36 @@ CostOut cost_walk(const Schedule& s, double alpha, double beta, double gamma);
 // per-step, per-rank element counters (steps x P, row-major)
 void cost_steps(const Schedule& s, int64_t* sent, int64_t* recv, int64_t* reduced);
 
+// Per-step, per-rank element counts straight from the generator's logical
+// operations (no realization, no fused planning): the same counts as
+// cost_steps on the realized table, at a fraction of the build cost. A
+// message is one (src rank, src value, dst rank, atom) per step. With n == 0
+// or P == 1 nothing moves and there are no steps.
+struct StepCounts {
+  int nsteps = 0;
+  std::vector<int64_t> sent, recv, reduced;  // nsteps x P, row-major, per instance
+};
+bool step_counts(const Spec& spec, StepCounts* out, std::string* err);
+
+// Model-driven choice of schedule (generalized-Allreduce paper: the optimal
+// step count follows from the measured alpha, beta, gamma; all-reduce blog
+// page: the library picks an algorithm per call from a cost model).
+enum CostForm : int32_t { F_BUSIEST = 0, F_ALL_RANKS = 1 };
+struct CostModel {
+  double alpha = 0, beta = 0, gamma = 0;
+  int form = F_BUSIEST;
+};
+constexpr int kAutoAlgo = -1;
+constexpr int kAutoKnob = -1;
+// Model time of a schedule from its step counts: alpha per step plus beta per
+// byte moved and gamma per byte combined, where the bytes are the per-step
+// maxima over ranks (F_BUSIEST) or the sums over ranks (F_ALL_RANKS).
+double model_seconds(const StepCounts& c, const Spec& spec, const CostModel& m);
+// Resolve kAutoAlgo / kAutoKnob in `in` to the candidate of least model time
+// (ties: fewer steps, then the earlier candidate). Other specs pass through.
+bool select_spec(const Spec& in, const CostModel& m, Spec* out, double* seconds, std::string* err);
+bool is_auto(const Spec& s);
+
 int elt_bytes(int dtype);
 int acc_bytes(int dtype);
 int ceil_log2(int P);

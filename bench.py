@@ -227,6 +227,84 @@ def cpu_baseline(wl, x, budget_s=12.0):
             "sample": f"{sample}; {algo} replay, {len(times)} runs, mean {mean:.3f} s (NumPy, one thread)"}
 
 
+def model_fit(args):
+    """Literal execution runs one launch per step, so each step pays a fixed cost
+    (alpha) plus a per-byte cost of what it moves (beta) and of what it combines
+    (gamma): the generalized paper's cost model, measured the way the paper
+    estimated its network parameters. On one GPU every rank shares one HBM, so the
+    bytes are the step's totals over all ranks. Fits T_call = steps*alpha +
+    sent_bytes*beta + reduced_bytes*gamma by least squares over several schedules
+    and sizes, then checks the model's ranking of the generalized algorithm's knob r
+    against the measured ranking."""
+    import numpy as np
+    import torch
+
+    import allreduce_schedule_algorithms_amd as A
+    from synth import inputs
+
+    rows = []
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    st = torch.cuda.Stream()
+
+    def timed(P, n, algo, knob, reps=12):
+        x = inputs.make("fp32", P, n, seed=1)
+        pristine = torch.from_numpy(x).cuda()
+        work = torch.empty_like(pristine)
+        ptrs = [work[p].data_ptr() for p in range(P)]
+        call = A.make_call(P, n, "fp32", "sum", algo, knob, "literal")
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for k in range(reps + 2):
+            with torch.cuda.stream(st):
+                work.copy_(pristine)
+                flush.zero_()
+            if k >= 2:
+                evs[k - 2][0].record(st)
+            A.ar_allreduce_ex(ptrs, call, st)
+            if k >= 2:
+                evs[k - 2][1].record(st)
+        torch.cuda.synchronize()
+        return statistics.median([a.elapsed_time(b) for a, b in evs]) * 1e-3
+
+    cases = []
+    for P in (7, 8):
+        L = (P - 1).bit_length()
+        for n in (1 << 10, 1 << 14, 1 << 17, 1 << 20, 1 << 22):
+            for algo, knob in [("ring", 0), ("rh_rd", 0), ("rd", 0), ("binomial", 0), ("direct", 0)] + \
+                    [("generalized", r) for r in range(L + 1)]:
+                cases.append((P, n, algo, knob))
+    for P, n, algo, knob in cases:
+        s = A.ar_schedule_build(A.make_call(P, n, "fp32", "sum", algo, knob, "literal"))
+        c = s.cost()
+        t = timed(P, n, algo, knob)
+        rows.append(dict(P=P, n=n, algo=algo, knob=knob, steps=c.steps, sent=c.sent_total * 4.0,
+                         reduced=c.reduced_total * 4.0, seconds=t))
+    X = np.array([[r["steps"], r["sent"], r["reduced"]] for r in rows])
+    y = np.array([r["seconds"] for r in rows])
+    w = 1.0 / y  # relative least squares: every case counts alike
+    coef, *_ = np.linalg.lstsq(X * w[:, None], y * w, rcond=None)
+    alpha, beta, gamma = (float(v) for v in coef)
+    pred = X @ coef
+    rel = np.abs(pred - y) / y
+    # knob choice per (P, n): model argmin vs measured argmin over r
+    knob_rows = []
+    for P in (7, 8):
+        L = (P - 1).bit_length()
+        for n in (1 << 10, 1 << 14, 1 << 17, 1 << 20, 1 << 22):
+            sel = [(r, row) for r in range(L + 1) for row in rows
+                   if row["P"] == P and row["n"] == n and row["algo"] == "generalized" and row["knob"] == r]
+            meas = min(sel, key=lambda t: t[1]["seconds"])[0]
+            mod = min(sel, key=lambda t: alpha * t[1]["steps"] + beta * t[1]["sent"] + gamma * t[1]["reduced"])[0]
+            knob_rows.append(dict(P=P, n=n, measured_best_r=meas, model_best_r=mod,
+                                  times_us=[round(t[1]["seconds"] * 1e6, 2) for t in sel]))
+    out = {"alpha_s": alpha, "beta_s_per_byte": beta, "gamma_s_per_byte": gamma,
+           "beta_GBps": (1.0 / beta / 1e9) if beta > 0 else None,
+           "gamma_GBps": (1.0 / gamma / 1e9) if gamma > 0 else None,
+           "median_rel_error": float(np.median(rel)), "max_rel_error": float(np.max(rel)),
+           "knob_choice": knob_rows, "cases": len(rows),
+           "rows": [dict(r, predicted=float(p)) for r, p in zip(rows, pred)]}
+    print(json.dumps(out))
+
+
 def load_traffic(wl_name, algo, knob, ex):
     """HBM bytes per launch from the committed counter summary (FETCH_SIZE and
     WRITE_SIZE, each scaled by what it reads for a plain copy of known size), or
@@ -256,6 +334,9 @@ def main():
     ap.add_argument("--warm", action="store_true", help="also report warm-cache (no flush) figures")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of MIB MiB (for counter scaling) and exit")
+    ap.add_argument("--model", action="store_true",
+                    help="fit alpha/beta/gamma to literal-mode (one launch per step) timings and check "
+                         "the model's choice of schedule and knob against measurement")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -275,6 +356,10 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": nbytes}))
+        return
+
+    if args.model:
+        model_fit(args)
         return
 
     wl = dict(WORKLOADS[args.workload])

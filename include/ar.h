@@ -84,8 +84,12 @@ typedef enum {
   AR_BINOMIAL = 4,
   AR_GENERALIZED = 5,
   AR_GENERALIZED_XOR = 6,
-  AR_AHC = 7
+  AR_AHC = 7,
+  AR_AUTO = -1             /* let the cost model pick (see ar_select) */
 } ar_algo;
+
+/* ar_call.knob with AR_GENERALIZED / AR_GENERALIZED_XOR: let the cost model pick r. */
+#define AR_KNOB_AUTO (-1)
 
 /* Execution of a schedule on the GPU.
  *  AR_EXEC_FUSED    default. AR_DIRECT runs the one-pass direct kernel (read all P, combine
@@ -104,13 +108,14 @@ typedef struct ar_call {
   int32_t P;               /* ranks, 1..AR_MAX_RANKS */
   int32_t dtype;           /* ar_dtype */
   int32_t op;              /* ar_op */
-  int32_t algo;            /* ar_algo */
-  int32_t knob;            /* AR_GENERALIZED*: r = distribution steps removed, 0..ceil(log2 P);
-                              ignored otherwise */
+  int32_t algo;            /* ar_algo; AR_AUTO lets the cost model choose */
+  int32_t knob;            /* AR_GENERALIZED*: r = distribution steps removed, 0..ceil(log2 P),
+                              or AR_KNOB_AUTO; ignored otherwise */
   int32_t exec;            /* ar_exec */
   int64_t n;               /* elements per instance (>= 0) */
   int64_t batch;           /* independent instances per buffer (>= 1); 0 is read as 1 */
-  int32_t ngroups;         /* AR_AHC: number of groups G (>= 1) */
+  int32_t ngroups;         /* AR_AHC: number of groups G (>= 1); with AR_AUTO, optional (0 leaves
+                              AHC out of the candidates) */
   const int32_t* groups;   /* AR_AHC: G group sizes summing to P, ranks assigned in order */
   void* workspace;         /* AR_EXEC_LITERAL: device scratch of ar_workspace_bytes() bytes, or
                               NULL to let the library allocate and cache one per device */
@@ -212,6 +217,45 @@ ar_status ar_cost_report(const ar_schedule* s, double alpha, double beta, double
                          ar_cost* out);
 /* Per-step, per-rank element counts (steps x P, row-major, per instance). */
 ar_status ar_cost_steps(const ar_schedule* s, int64_t* sent, int64_t* recv, int64_t* reduced);
+
+/* ---- model-driven choice of schedule ----
+ * The generalized-Allreduce paper picks its step count r from measured alpha (latency),
+ * beta (transfer time per byte) and gamma (combination time per byte) by minimising the
+ * cost of eq. (36) (section "Intermediate version" and eq. (37)); the all-reduce blog page
+ * describes a library that picks algorithm and protocol per call from a tuning model
+ * ("Protocols: Simple, LL and LL128"). Here the model time of a schedule is
+ *   alpha * steps + beta * B_sent + gamma * B_combined
+ * with the bytes taken from the schedule's exact per-step, per-rank counts (the counts
+ * ar_cost_steps returns, times the element size and batch):
+ *   AR_COST_BUSIEST_RANK  per step the busiest rank (max of sent and received bytes, and of
+ *                         combined bytes), summed over steps: ranks on separate links, the
+ *                         paper's model.
+ *   AR_COST_ALL_RANKS     every rank's bytes summed: all ranks share one memory, as in this
+ *                         library's step-by-step executor (AR_EXEC_LITERAL) on one device.
+ * AR_AUTO enumerates AR_DIRECT, AR_RING, AR_RH_RD, AR_RD, AR_BINOMIAL, AR_GENERALIZED r = 0..
+ * ceil(log2 P), AR_GENERALIZED_XOR r = 0..ceil(log2 P) when P is a power of two, and AR_AHC when
+ * groups are given; AR_KNOB_AUTO enumerates r for the given algorithm. The least model time
+ * wins; ties go to fewer steps, then to the earlier candidate in that order. The choice
+ * depends only on (P, n, batch, dtype, groups) and the model, never on timing. The default
+ * model is a least-squares fit of AR_EXEC_LITERAL fp32 calls measured on MI355X, form
+ * AR_COST_ALL_RANKS (values via ar_get_cost_model). */
+typedef enum { AR_COST_BUSIEST_RANK = 0, AR_COST_ALL_RANKS = 1 } ar_cost_form;
+typedef struct ar_cost_model {
+  double alpha;  /* seconds per step */
+  double beta;   /* seconds per byte sent */
+  double gamma;  /* seconds per byte combined */
+  int32_t form;  /* ar_cost_form */
+  int32_t reserved;
+} ar_cost_model;
+/* Replace the process-wide model (NULL restores the default). Parameters must be finite and
+ * >= 0. Calls already resolved keep no stale choice: the selection cache is cleared. Not
+ * meant to race with calls on other threads that use AR_AUTO / AR_KNOB_AUTO. */
+ar_status ar_set_cost_model(const ar_cost_model* model);
+ar_status ar_get_cost_model(ar_cost_model* model);
+/* Resolve a call's schedule as ar_allreduce_ex would: *algo and *knob receive the schedule
+ * that runs (unchanged for explicit calls), *predicted_seconds its model time under the
+ * current model. Any output pointer may be NULL. Host only. */
+ar_status ar_select(const ar_call* call, int32_t* algo, int32_t* knob, double* predicted_seconds);
 
 const char* ar_status_string(ar_status st);
 int32_t ar_last_hip_error(void);

@@ -14,12 +14,25 @@
   ("Reading benchmarks: algbw and busbw", "Worked example").
 * The pipelined chain reduce of the "Reduction Operator" page (p + m - 2
   steps of n / m bytes; optimal segment count).
+* Model-driven choice of schedule: the generalized-Allreduce paper picks its
+  step count r by minimising eq. (36) under measured alpha, beta, gamma
+  ("Intermediate version", eq. (37), experiments section); the all-reduce blog
+  page's library picks an algorithm per call from a tuning model ("Protocols:
+  Simple, LL and LL128"). ``select`` enumerates every schedule the oracle
+  replays and evaluates the model on the exact per-step, per-rank element
+  counts of the replay (not on the prose closed forms, which hold for P | n
+  and state the combine count only as a worst case).
 """
 from __future__ import annotations
 
 import math
 
+import numpy as np
+
+from . import schedules
 from .numerics import ceil_log2
+
+ELT_BYTES = {"int32": 4, "fp32": 4, "bf16": 2}
 
 
 def message_time(nbytes: float, alpha: float, bandwidth: float) -> float:
@@ -80,3 +93,72 @@ def pipelined_chain_time(n: float, p: int, m: int, t_start: float, t_byte: float
 
 def pipelined_chain_best_m(n: float, p: int, t_start: float, t_byte: float) -> float:
     return math.sqrt(n * (p - 2) * t_byte / t_start)
+
+
+# --------------------------------------------------------------------------
+# model-driven choice of schedule
+# --------------------------------------------------------------------------
+def step_counts(P: int, n: int, algo: str, knob: int = 0, groups=None):
+    """Per-step, per-rank elements sent, received and combined by one instance.
+
+    Counts come from the oracle's own replay of the schedule on a one-offset
+    sample (the simulator counts whole-buffer elements whatever the sample).
+    Nothing moves when n == 0 or P == 1: zero steps.
+    """
+    z = np.zeros((0, P), dtype=np.int64)
+    if P == 1 or n == 0:
+        return z, z, z
+    x = np.zeros((P, 1), dtype=np.int32)
+    _, st = schedules.allreduce(x, algo, "int32", "sum", knob=knob, groups=groups, n=n, idx=[0],
+                                return_stats=True)
+    return (np.asarray(st["sent"], dtype=np.int64).reshape(-1, P),
+            np.asarray(st["recv"], dtype=np.int64).reshape(-1, P),
+            np.asarray(st["reduced"], dtype=np.int64).reshape(-1, P))
+
+
+def model_seconds(counts, elt: int, batch: int, alpha: float, beta: float, gamma: float,
+                  form: str = "busiest") -> float:
+    """alpha per step + beta per byte moved + gamma per byte combined.
+
+    form "busiest": in each step the busiest rank's bytes (the larger of what
+    it sends and receives; what it combines), summed over steps -- every rank
+    on its own links, the paper's model. form "all_ranks": every rank's bytes
+    summed -- all ranks share one memory.
+    """
+    sent, recv, red = counts
+    S = int(sent.shape[0])
+    if form == "busiest":
+        xb = int(np.maximum(sent, recv).max(axis=1).sum()) if S else 0
+        xg = int(red.max(axis=1).sum()) if S else 0
+    elif form == "all_ranks":
+        xb, xg = int(sent.sum()), int(red.sum())
+    else:
+        raise ValueError(form)
+    return alpha * S + beta * (float(xb) * elt * batch) + gamma * (float(xg) * elt * batch)
+
+
+def candidates(P: int, algo: str = "auto", groups=None):
+    """(algo, knob) pairs in tie-breaking order."""
+    L = ceil_log2(P)
+    if algo != "auto":
+        return [(algo, r) for r in range(L + 1)]
+    out = [(a, 0) for a in ("direct", "ring", "rh_rd", "rd", "binomial")]
+    out += [("generalized", r) for r in range(L + 1)]
+    if P & (P - 1) == 0:
+        out += [("generalized_xor", r) for r in range(L + 1)]
+    if groups:
+        out.append(("ahc", 0))
+    return out
+
+
+def select(P: int, n: int, dtype: str, alpha: float, beta: float, gamma: float, form: str = "busiest",
+           algo: str = "auto", batch: int = 1, groups=None):
+    """(algo, knob, seconds) of least model time; ties: fewer steps, then earlier candidate."""
+    best = None
+    for a, r in candidates(P, algo, groups):
+        c = step_counts(P, n, a, r, groups if a == "ahc" else None)
+        t = model_seconds(c, ELT_BYTES[dtype], batch, alpha, beta, gamma, form)
+        key = (t, c[0].shape[0])
+        if best is None or key < best[0]:
+            best = (key, a, r)
+    return best[1], best[2], best[0][0]

@@ -342,11 +342,13 @@ def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: 
     if group == "cyclic":
         place = lambda k, j: (k + j) % P  # noqa: E731
         owner = lambda p, i: (p - i) % P  # placement held by rank p at part i  # noqa: E731
+        ranks_of = lambda t: (t + np.arange(P)) % P  # rank holding part a of placement t  # noqa: E731
     elif group == "xor":
         if P & (P - 1):
             raise ValueError("the XOR group needs P to be a power of two")
         place = lambda k, j: k ^ j  # noqa: E731
         owner = lambda p, i: p ^ i  # noqa: E731
+        ranks_of = lambda t: t ^ np.arange(P)  # noqa: E731
     else:
         raise ValueError(group)
 
@@ -362,15 +364,20 @@ def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: 
     J = list(range(N[L - r]))
     sym = Symbolic(P)  # diagonal-level shadow, for dedupe and traffic counts
     sent_steps, red_steps = [], []
+    # per-rank element counters: a vector at placement t is spread over all
+    # ranks, part a on rank ranks_of(t)[a], so moving it moves every part once
+    plen = np.array([hi - lo for lo, hi in partition(n, P)], dtype=np.int64)
+    el_sent, el_recv, el_red = [], [], []
     vals = {j: [diag(place(k, j)) for k in range(P)] for j in J}
     syms = {j: [place(k, j) for k in range(P)] for j in J}
     for i in range(L):
-        sends, reds = set(), set()
+        sends, reds, msgs = set(), set(), set()
         new_vals, new_syms = {}, {}
         for j in J:
             v, s = list(vals[j]), list(syms[j])
             for k in range(N[i] - h[i], N[i]):
                 sends.add((place(k, j), syms[j][k]))
+                msgs.add((place(k, j), syms[j][k], place(k - h[i], j)))
                 s[k - h[i]] = sym.node(syms[j][k - h[i]], syms[j][k])
                 v[k - h[i]] = alg.op(vals[j][k - h[i]], vals[j][k])
                 reds.add((place(k - h[i], j), s[k - h[i]]))
@@ -378,14 +385,29 @@ def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: 
         vals, syms = new_vals, new_syms
         sent_steps.append(len(sends))
         red_steps.append(len(reds))
+        es, er, ed = (np.zeros(P, dtype=np.int64) for _ in range(3))
+        for t_from, _, t_to in msgs:
+            es[ranks_of(t_from)] += plen
+            er[ranks_of(t_to)] += plen
+        for t_to, _ in reds:
+            ed[ranks_of(t_to)] += plen
+        el_sent.append(es)
+        el_recv.append(er)
+        el_red.append(ed)
     results = {j: vals[j][0] for j in J}  # result j sits at placement j
 
     src = {j: j for j in J}
     copy_steps = []
     for i in reversed(range(L - r)):
+        es, er = np.zeros(P, dtype=np.int64), np.zeros(P, dtype=np.int64)
         for k in range(N[i] - h[i], N[i]):
             src[k] = src[k - h[i]]
+            es[ranks_of(k - h[i])] += plen
+            er[ranks_of(k)] += plen
         copy_steps.append(h[i])
+        el_sent.append(es)
+        el_recv.append(er)
+        el_red.append(np.zeros(P, dtype=np.int64))
     out = np.empty_like(xacc)
     src_of = np.array([src[k] for k in range(P)])
     for p in range(P):
@@ -397,6 +419,9 @@ def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: 
                     out[p][:, m] = results[j][:, m]
     stats = dict(
         steps=L + (L - r),
+        sent=np.array(el_sent).reshape(-1, P),
+        recv=np.array(el_recv).reshape(-1, P),
+        reduced=np.array(el_red).reshape(-1, P),
         reduction_sent_parts=sent_steps,
         reduction_reduced_parts=red_steps,
         distribution_sent_parts=copy_steps,

@@ -294,7 +294,7 @@ FAKE = [0x1000 * (i + 1) for i in range(256)]
 @pytest.mark.parametrize("kw,match", [
     (dict(P=0), "P must"), (dict(P=257), "P must"), (dict(n=-1), "n must"), (dict(dtype=7), "dtype"),
     (dict(op=5), "op"), (dict(algo=11), "algorithm"), (dict(algo="generalized", knob=4), "knob"),
-    (dict(algo="generalized", knob=-1), "knob"), (dict(algo="generalized_xor", P=6), "power of two"),
+    (dict(algo="generalized", knob=-2), "knob"), (dict(algo="generalized_xor", P=6), "power of two"),
     (dict(algo="ahc", groups=[2, 2]), "sum to P"), (dict(algo="ahc", groups=None), "group"),
     (dict(algo="ahc", groups=[5, 0]), "group sizes"), (dict(exec=9), "exec"),
 ])
