@@ -28,7 +28,7 @@ ar_status fail(ar_status st, const std::string& m) {
 // Default: least-squares fit of AR_EXEC_LITERAL fp32 calls on MI355X (P = 7 and 8,
 // 2^10..2^22 elements, every schedule and r), one launch per step, all ranks'
 // bytes through one HBM.
-constexpr ar::CostModel kDefaultModel{3.66e-6, 2.04e-13, 2.19e-13, ar::F_ALL_RANKS};
+constexpr ar::CostModel kDefaultModel{3.52e-6, 2.10e-13, 2.07e-13, ar::F_ALL_RANKS};
 std::mutex g_model_mu;
 ar::CostModel g_model = kDefaultModel;
 std::map<std::string, std::pair<ar::Spec, double>> g_choices;

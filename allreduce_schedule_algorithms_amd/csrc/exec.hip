@@ -24,6 +24,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <limits>
 #include <map>
 #include <memory>
 #include <mutex>
@@ -105,12 +106,14 @@ struct Plan {
   const Schedule* s = nullptr;
   int exec = E_FUSED;
   int D = 2;
-  DevBuf prog, lops;
+  DevBuf prog;
   DevBuf items[2];  // [vector mode, scalar mode]
   int64_t nitems[2] = {0, 0};
   bool built[2] = {false, false};
-  // literal: per launch (step or finalize), range of items
+  // literal: per launch (step or finalize), range of work records; packed
+  // small chunks
   std::vector<std::pair<int64_t, int64_t>> launches[2];
+  DevBuf packed[2];
   int64_t slot_bytes = 0;
   size_t ws_bytes = 0;
 };
@@ -155,34 +158,74 @@ RunResult build_items(Plan& pl, bool vec) {
   const int mode = vec ? 0 : 1;
   std::vector<Item> items;
   if (pl.exec == E_LITERAL) {
-    // joint ops per launch
-    std::vector<LitOp> lops;
+    // per launch (schedule step, then the finalize moves): the step's chunks,
+    // each joint op with its op code inline
+    if (s.nslots > 255) return RunResult{2, 0, "literal execution supports at most 255 slots"};
+    std::vector<LitWork> work, packed;
     std::vector<std::pair<int64_t, int64_t>> launches;
+    std::vector<Item> chunks;
+    std::vector<LitCode> codes;
     for (int st = 0; st <= s.nsteps; ++st) {
-      int64_t first = int64_t(items.size());
+      chunks.clear();
+      codes.clear();
       for (int32_t i = s.steps_begin[st]; i < s.steps_begin[st + 1]; ++i) {
         const OpRec& o = s.ops[i];
         if (o.pair >= 0 && o.pair < i) continue;  // executed with its partner
-        LitOp lo{o.kind, o.src_rank, o.src_slot, o.own_slot, o.dst_rank, o.dst_slot, -1, -1};
+        LitCode c{uint8_t(o.kind == K_REDUCE ? 0 : kLitCopy), uint8_t(o.src_rank), uint8_t(o.src_slot),
+                  uint8_t(o.own_slot < 0 ? 0 : o.own_slot), uint8_t(o.dst_rank), uint8_t(o.dst_slot), 0, 0};
         if (o.pair >= 0) {
-          lo.dst2_rank = s.ops[o.pair].dst_rank;
-          lo.dst2_slot = s.ops[o.pair].dst_slot;
+          c.kind |= kLitDst2;
+          c.dst2_rank = uint8_t(s.ops[o.pair].dst_rank);
+          c.dst2_slot = uint8_t(s.ops[o.pair].dst_slot);
         }
-        int32_t tag = int32_t(lops.size());
-        lops.push_back(lo);
+        const int32_t tag = int32_t(codes.size());
+        codes.push_back(c);
         if (sp.batch > 1 && o.offset == 0 && o.length == sp.n) {
-          add_segment(items, 0, sp.n * sp.batch, tag, V, vec);
+          add_segment(chunks, 0, sp.n * sp.batch, tag, V, vec);
         } else {
-          for (int64_t b = 0; b < sp.batch; ++b) add_segment(items, b * sp.n + o.offset, o.length, tag, V, vec);
+          for (int64_t b = 0; b < sp.batch; ++b) add_segment(chunks, b * sp.n + o.offset, o.length, tag, V, vec);
         }
       }
-      if (int64_t(items.size()) > first) launches.push_back({first, int64_t(items.size()) - first});
+      if (chunks.empty()) continue;
+      // chunks of kPackSmall units or more get a workgroup each; smaller ones
+      // are packed, S threads per chunk, kThreads / S chunks per workgroup
+      const int64_t w0 = int64_t(work.size());
+      size_t i = 0;
+      while (i < chunks.size()) {
+        const int32_t u0 = chunks[i].count > 0 ? chunks[i].count : -chunks[i].count;
+        if (u0 >= kPackSmall) {
+          work.push_back({chunks[i].start, chunks[i].count, 0, codes[chunks[i].tag]});
+          ++i;
+          continue;
+        }
+        size_t j = i;
+        int lg = 0;
+        while (j < chunks.size()) {
+          const int32_t u = chunks[j].count > 0 ? chunks[j].count : -chunks[j].count;
+          if (u >= kPackSmall) break;
+          int l2 = lg;
+          while ((1 << l2) < u) ++l2;
+          if (int64_t(j - i + 1) << l2 > kThreads) break;
+          lg = l2;
+          ++j;
+        }
+        if (j - i == 1) {
+          work.push_back({chunks[i].start, chunks[i].count, 0, codes[chunks[i].tag]});
+        } else {
+          work.push_back({int64_t(packed.size()), 0, int32_t((j - i) << 8) | lg, LitCode{}});
+          for (size_t q = i; q < j; ++q) packed.push_back({chunks[q].start, chunks[q].count, 0, codes[chunks[q].tag]});
+        }
+        i = j;
+      }
+      launches.push_back({w0, int64_t(work.size()) - w0});
     }
-    if (!pl.lops.p) {
-      hipError_t e = upload(pl.lops, lops);
-      if (e != hipSuccess) return hip_fail(e, "uploading literal ops");
-    }
+    hipError_t e = upload(pl.items[mode], work);
+    if (e == hipSuccess) e = upload(pl.packed[mode], packed);
+    if (e != hipSuccess) return hip_fail(e, "uploading literal work");
     pl.launches[mode] = launches;
+    pl.nitems[mode] = int64_t(work.size());
+    pl.built[mode] = true;
+    return RunResult{};
   } else {
     const bool flat = s.ranges.size() == 1 && s.ranges[0].start == 0 && s.ranges[0].len == sp.n;
     if (sp.batch == 1 || flat) {
@@ -338,14 +381,14 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
   const int mode = vec ? 0 : 1;
   if (pl->exec == E_LITERAL) {
     WsDesc wd{reinterpret_cast<char*>(ws), pl->slot_bytes, spec.P};
-    const Item* items = reinterpret_cast<const Item*>(pl->items[mode].p);
-    const LitOp* lops = reinterpret_cast<const LitOp*>(pl->lops.p);
+    const LitWork* work = reinterpret_cast<const LitWork*>(pl->items[mode].p);
+    const LitWork* packed = reinterpret_cast<const LitWork*>(pl->packed[mode].p);
     const auto& lns = pl->launches[mode];
     if (lns.empty()) return mark_empty();
     for (size_t i = 0; i < lns.size(); ++i) {
       Evs ei{i == 0 ? ev.start : nullptr, i + 1 == lns.size() ? ev.stop : nullptr};
       AR_DISPATCH(spec.dtype, spec.op,
-                  (e = launch_literal_t<DT, OPK>(lns[i].second, ptrs, wd, items + lns[i].first, lops, st, ei)));
+                  (e = launch_literal_t<DT, OPK>(lns[i].second, ptrs, wd, work + lns[i].first, packed, st, ei)));
       if (e != hipSuccess) return hip_fail(e, "launching a literal step");
     }
   } else {

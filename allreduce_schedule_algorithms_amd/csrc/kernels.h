@@ -25,10 +25,6 @@ struct Item {
   int32_t tag;  // program word offset (fused) or op index (literal)
 };
 
-struct LitOp {
-  int32_t kind, src_rank, src_slot, own_slot, dst_rank, dst_slot, dst2_rank, dst2_slot;
-};
-
 constexpr int kThreads = 256;
 constexpr int kLeafBatch = 8;
 constexpr int kMaxFusedTrees = 8;  // distinct result trees per range the fused replay keeps in registers
@@ -419,37 +415,73 @@ __device__ __forceinline__ void st_slot(const RankPtrs& ptrs, const WsDesc& ws, 
   else st_acc<DT, M>(slot_ptr(ptrs, ws, rank, slot), e, ok, v);
 }
 
+
+// Literal work records. A workgroup either runs one chunk (count != 0) or a
+// packed group of up to kThreads / S small chunks, S threads each (S a power of
+// two >= the chunk's units; a unit is one vector of a vector chunk or one
+// element of an element chunk). The op travels inside the record, so a
+// workgroup reaches its data after one metadata load (two when packed): a step
+// made of thousands of tiny chunks then neither pays one workgroup per chunk
+// nor a chain of dependent table lookups.
+struct LitCode {
+  uint8_t kind;  // bit 0: copy (else combine into dst); bit 1: second destination
+  uint8_t src_rank, src_slot, own_slot, dst_rank, dst_slot, dst2_rank, dst2_slot;
+};
+enum : uint8_t { kLitCopy = 1, kLitDst2 = 2 };
+struct LitWork {
+  int64_t start;  // first element of the chunk, or first packed chunk (count == 0)
+  int32_t count;  // > 0 vectors, < 0 elements, 0 packed group
+  int32_t pack;   // packed group: (chunks << 8) | log2 S
+  LitCode code;
+};
+constexpr int kPackSmall = 64;  // chunks of fewer units are packed
+
 template <int DT, int OPK, int M>
-__device__ __forceinline__ void literal_one(const RankPtrs& ptrs, const WsDesc& ws, const LitOp& op, int64_t e,
+__device__ __forceinline__ void literal_one(const RankPtrs& ptrs, const WsDesc& ws, const LitCode& c, int64_t e,
                                             const bool (&ok)[mm<M>()]) {
   using A = typename TT<DT>::A;
   constexpr int N = nvals<DT, M>();
   A s[N], r[N];
-  ld_slot<DT, M>(ptrs, ws, op.src_rank, op.src_slot, e, ok, s);
-  if (op.kind == K_REDUCE) {
+  ld_slot<DT, M>(ptrs, ws, c.src_rank, c.src_slot, e, ok, s);
+  if (!(c.kind & kLitCopy)) {
     A o[N];
-    ld_slot<DT, M>(ptrs, ws, op.dst_rank, op.own_slot, e, ok, o);
+    ld_slot<DT, M>(ptrs, ws, c.dst_rank, c.own_slot, e, ok, o);
 #pragma unroll
     for (int i = 0; i < N; ++i) r[i] = cmb<OPK>(o[i], s[i]);
   } else {
 #pragma unroll
     for (int i = 0; i < N; ++i) r[i] = s[i];
   }
-  st_slot<DT, M>(ptrs, ws, op.dst_rank, op.dst_slot, e, ok, r);
-  if (op.dst2_rank >= 0) st_slot<DT, M>(ptrs, ws, op.dst2_rank, op.dst2_slot, e, ok, r);
+  st_slot<DT, M>(ptrs, ws, c.dst_rank, c.dst_slot, e, ok, r);
+  if (c.kind & kLitDst2) st_slot<DT, M>(ptrs, ws, c.dst2_rank, c.dst2_slot, e, ok, r);
 }
 
 template <int DT, int OPK>
-__global__ __launch_bounds__(kThreads) void k_literal(RankPtrs ptrs, WsDesc ws, const Item* __restrict__ items,
-                                                      const LitOp* __restrict__ ops) {
+__global__ __launch_bounds__(kThreads) void k_literal(RankPtrs ptrs, WsDesc ws, const LitWork* __restrict__ work,
+                                                      const LitWork* __restrict__ packed) {
   constexpr int V = TT<DT>::V;
   constexpr int M = 2;
-  const Item it = items[blockIdx.x];
-  const LitOp op = ops[it.tag];
-  if (it.count > 0) {
-    for_fragments<M>(it, V, [&](int64_t e, const bool (&ok)[M]) { literal_one<DT, OPK, M>(ptrs, ws, op, e, ok); });
-  } else {
-    for_fragments<0>(it, V, [&](int64_t e, const bool (&ok)[1]) { literal_one<DT, OPK, 0>(ptrs, ws, op, e, ok); });
+  const LitWork w = work[blockIdx.x];
+  if (w.count != 0) {
+    const Item it{w.start, w.count, 0};
+    if (it.count > 0) {
+      for_fragments<M>(it, V, [&](int64_t e, const bool (&ok)[M]) { literal_one<DT, OPK, M>(ptrs, ws, w.code, e, ok); });
+    } else {
+      for_fragments<0>(it, V, [&](int64_t e, const bool (&ok)[1]) { literal_one<DT, OPK, 0>(ptrs, ws, w.code, e, ok); });
+    }
+    return;
+  }
+  const int lg = w.pack & 0xff;
+  const int chunks = w.pack >> 8;
+  const int c = int(threadIdx.x) >> lg;
+  const int k = int(threadIdx.x) & ((1 << lg) - 1);
+  if (c >= chunks) return;
+  const LitWork x = packed[w.start + c];
+  const bool ok[1] = {true};
+  if (x.count > 0) {
+    if (k < x.count) literal_one<DT, OPK, 1>(ptrs, ws, x.code, x.start + int64_t(k) * V, ok);
+  } else if (k < -x.count) {
+    literal_one<DT, OPK, 0>(ptrs, ws, x.code, x.start + k, ok);
   }
 }
 

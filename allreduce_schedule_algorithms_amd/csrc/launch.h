@@ -29,8 +29,8 @@ template <int DT, int OPK>
 hipError_t launch_fused_t(int D, int TM, int P, int64_t nitems, const RankPtrs& ptrs, const Item* items,
                           const int32_t* prog, hipStream_t st, Evs ev);
 template <int DT, int OPK>
-hipError_t launch_literal_t(int64_t nitems, const RankPtrs& ptrs, const WsDesc& ws, const Item* items,
-                            const LitOp* ops, hipStream_t st, Evs ev);
+hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& ws, const LitWork* work,
+                            const LitWork* packed, hipStream_t st, Evs ev);
 template <int DT, int OPK>
 hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total, hipStream_t st, Evs ev);
 
@@ -102,10 +102,10 @@ hipError_t launch_fused_t(int D, int TM, int P, int64_t nitems, const RankPtrs& 
 }
 
 template <int DT, int OPK>
-hipError_t launch_literal_t(int64_t nitems, const RankPtrs& ptrs, const WsDesc& ws, const Item* items,
-                            const LitOp* ops, hipStream_t st, Evs ev) {
-  hipExtLaunchKernelGGL((k_literal<DT, OPK>), dim3(unsigned(nitems)), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
-                        ptrs, ws, items, ops);
+hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& ws, const LitWork* work,
+                            const LitWork* packed, hipStream_t st, Evs ev) {
+  hipExtLaunchKernelGGL((k_literal<DT, OPK>), dim3(unsigned(nwork)), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
+                        ptrs, ws, work, packed);
   return hipGetLastError();
 }
 
@@ -142,8 +142,8 @@ hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total,
 #define AR_INSTANTIATE_LAUNCHES(DT, OPK)                                                                    \
   template hipError_t launch_fused_t<DT, OPK>(int, int, int, int64_t, const RankPtrs&, const Item*,         \
                                               const int32_t*, hipStream_t, Evs);                            \
-  template hipError_t launch_literal_t<DT, OPK>(int64_t, const RankPtrs&, const WsDesc&, const Item*,       \
-                                                const LitOp*, hipStream_t, Evs);                            \
+  template hipError_t launch_literal_t<DT, OPK>(int64_t, const RankPtrs&, const WsDesc&, const LitWork*,    \
+                                                const LitWork*, hipStream_t, Evs);                          \
   template hipError_t launch_direct_t<DT, OPK>(bool, const RankPtrs&, int, int64_t, hipStream_t, Evs);
 #endif  // AR_LAUNCH_DEFINITIONS
 

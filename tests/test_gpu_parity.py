@@ -98,6 +98,21 @@ def test_most_ranks_and_tiny_buffers():
                     assert np.array_equal(bits(got), bits(want)), (P, n, algo, ex)
 
 
+def test_many_tiny_chunks_pack_into_shared_workgroups():
+    # P = 127 with a few hundred elements: thousands of 2-3 element chunks per
+    # literal step, packed several to a workgroup; mixed with vector runs at
+    # larger n
+    P = 127
+    for n in (256, 3000, 40_000):
+        x = inputs.make("fp32", P, n, seed=n)
+        cases = (("generalized", 0), ("ring", 0)) if n > 10_000 else \
+            (("generalized", 0), ("generalized", 3), ("generalized", 7), ("ring", 0))
+        for algo, r in cases:
+            want = oracle.allreduce(x, algo, "fp32", "sum", knob=r)
+            got = gpu_allreduce(x, algo, "fp32", "sum", r, "literal")
+            assert np.array_equal(bits(got), bits(want)), (n, algo, r)
+
+
 def test_side_stream_and_signed_zero():
     import torch
     s = torch.cuda.Stream()
@@ -181,3 +196,28 @@ def test_ahc_bf16_192_ranks_sampled():
     got = gpu_allreduce(x, "direct", "bf16", "sum")
     want = oracle.allreduce(xs, "direct", "bf16", "sum", n=n, idx=idx)
     assert np.array_equal(bits(got[:, idx]), bits(want))
+
+
+# --------------------------------------------------------------------------
+# model-driven choice: the call runs the schedule the oracle's model picks
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("form", ["all_ranks", "busiest"])
+def test_auto_choice_runs_the_oracle_choice(form):
+    import allreduce_schedule_algorithms_amd as A
+    from oracle import cost
+    try:
+        if form == "busiest":
+            A.ar_set_cost_model(2e-6, 1e-11, 2e-12, "busiest")
+        m = A.ar_get_cost_model()
+        for P in (5, 7, 8):
+            for n in (64, 4099, 1 << 17):
+                x = inputs.make("fp32", P, n, seed=P + n)
+                for algo, knob in (("auto", 0), ("generalized", -1)):
+                    a, r, _ = cost.select(P, n, "fp32", m["alpha"], m["beta"], m["gamma"], m["form"],
+                                          algo=algo)
+                    want = oracle.allreduce(x, a, "fp32", "sum", knob=r)
+                    for ex in ("fused", "literal"):
+                        got = gpu_allreduce(x, algo, "fp32", "sum", knob, ex)
+                        assert np.array_equal(bits(got), bits(want)), (P, n, algo, a, r, ex)
+    finally:
+        A.ar_set_cost_model()
