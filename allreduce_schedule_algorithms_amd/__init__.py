@@ -8,21 +8,22 @@ from __future__ import annotations
 
 from . import _ar
 from ._ar import (  # noqa: F401
-    ALGO_NAMES, ALGOS, AR_KNOB_AUTO, COST_FORMS, DTYPES, EXECS, OPS, Algo, ArError, CostForm, Dtype, Exec,
-    Op, Schedule, Status, ar_allreduce, ar_allreduce_ex, ar_get_cost_model, ar_last_error_message,
-    ar_last_hip_error, ar_schedule_build, ar_select, ar_set_cost_model, ar_status_string, ar_table_check,
-    ar_version, ar_workspace_bytes, make_call,
+    ALGO_NAMES, ALGOS, AR_KNOB_AUTO, COLLECTIVES, COST_FORMS, DTYPES, EXECS, OPS, Algo, ArError, Collective,
+    CostForm, Dtype, Exec, Op, Schedule, Status, ar_all_gather, ar_allreduce, ar_allreduce_ex, ar_get_cost_model,
+    ar_last_error_message, ar_last_hip_error, ar_reduce_scatter, ar_schedule_build, ar_select, ar_set_cost_model,
+    ar_status_string, ar_table_check, ar_table_check_ex, ar_version, ar_workspace_bytes, make_call,
 )
 
 _TORCH_DTYPE = {"int32": "int32", "fp32": "float32", "bf16": "bfloat16"}
 
 
 def allreduce(tensors, algo="ring", op="sum", knob=0, exec="fused", batch=1, groups=None,
-              stream=None, workspace=None):
+              stream=None, workspace=None, collective="allreduce"):
     """In-place Allreduce over a list of P equally sized CUDA tensors (one per rank).
 
     dtype comes from the tensors (int32, float32 or bfloat16); each tensor holds
     ``batch`` contiguous instances. ``stream`` defaults to torch's current stream.
+    ``collective`` selects the reduce-scatter or all-gather half instead.
     """
     import torch
 
@@ -42,5 +43,16 @@ def allreduce(tensors, algo="ring", op="sum", knob=0, exec="fused", batch=1, gro
         stream = torch.cuda.current_stream(t0.device)
     call = make_call(P, total // batch, rev[dname], op, algo, knob, exec, batch, groups,
                      workspace=workspace, workspace_bytes=(workspace.numel() * workspace.element_size()
-                                                           if workspace is not None else 0))
+                                                           if workspace is not None else 0),
+                     collective=collective)
     ar_allreduce_ex(tensors, call, stream)
+
+
+def reduce_scatter(tensors, algo="ring", op="sum", exec="fused", batch=1, stream=None, workspace=None):
+    """In place: tensor q ends with the reduced part q (the ceil split into P parts)."""
+    allreduce(tensors, algo, op, 0, exec, batch, None, stream, workspace, "reduce_scatter")
+
+
+def all_gather(tensors, algo="ring", exec="fused", batch=1, stream=None, workspace=None):
+    """In place: tensor q contributes part q; every tensor ends with all parts."""
+    allreduce(tensors, algo, "sum", 0, exec, batch, None, stream, workspace, "all_gather")

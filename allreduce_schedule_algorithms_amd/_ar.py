@@ -36,6 +36,13 @@ class Dtype(enum.IntEnum):
 class Op(enum.IntEnum):
     AR_SUM = 0
     AR_MAX = 1
+    AR_AVG = 2
+
+
+class Collective(enum.IntEnum):
+    AR_ALLREDUCE = 0
+    AR_REDUCE_SCATTER = 1
+    AR_ALL_GATHER = 2
 
 
 class Algo(enum.IntEnum):
@@ -65,7 +72,9 @@ class Exec(enum.IntEnum):
 
 
 DTYPES = {"int32": Dtype.AR_INT32, "fp32": Dtype.AR_FP32, "bf16": Dtype.AR_BF16}
-OPS = {"sum": Op.AR_SUM, "max": Op.AR_MAX}
+OPS = {"sum": Op.AR_SUM, "max": Op.AR_MAX, "avg": Op.AR_AVG}
+COLLECTIVES = {"allreduce": Collective.AR_ALLREDUCE, "reduce_scatter": Collective.AR_REDUCE_SCATTER,
+               "all_gather": Collective.AR_ALL_GATHER}
 ALGOS = {"direct": Algo.AR_DIRECT, "ring": Algo.AR_RING, "rh_rd": Algo.AR_RH_RD, "rd": Algo.AR_RD,
          "binomial": Algo.AR_BINOMIAL, "generalized": Algo.AR_GENERALIZED,
          "generalized_xor": Algo.AR_GENERALIZED_XOR, "ahc": Algo.AR_AHC, "auto": Algo.AR_AUTO}
@@ -79,7 +88,8 @@ class ar_call(C.Structure):
                 ("knob", C.c_int32), ("exec", C.c_int32), ("n", C.c_int64), ("batch", C.c_int64),
                 ("ngroups", C.c_int32), ("groups", C.POINTER(C.c_int32)),
                 ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
-                ("start_event", C.c_void_p), ("stop_event", C.c_void_p)]
+                ("start_event", C.c_void_p), ("stop_event", C.c_void_p), ("collective", C.c_int32),
+                ("reserved", C.c_int32)]
 
 
 class ar_oprec(C.Structure):
@@ -114,6 +124,9 @@ SIGNATURES = {
     "ar_allreduce": (C.c_int, [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_int32,
                                C.c_int32, C.c_void_p]),
     "ar_allreduce_ex": (C.c_int, [C.POINTER(C.c_void_p), C.POINTER(ar_call), C.c_void_p]),
+    "ar_reduce_scatter": (C.c_int, [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int32, C.c_int32,
+                                    C.c_int32, C.c_void_p]),
+    "ar_all_gather": (C.c_int, [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_void_p]),
     "ar_workspace_bytes": (C.c_int, [C.POINTER(ar_call), C.POINTER(C.c_size_t)]),
     "ar_schedule_build": (C.c_int, [C.POINTER(ar_call), C.POINTER(C.c_void_p)]),
     "ar_schedule_info_get": (C.c_int, [C.c_void_p, C.POINTER(ar_schedule_info)]),
@@ -124,6 +137,7 @@ SIGNATURES = {
     "ar_schedule_free": (None, [C.c_void_p]),
     "ar_table_check": (C.c_int, [C.c_int32, C.c_int64, C.c_int32, C.POINTER(ar_oprec), C.c_size_t,
                                  C.POINTER(C.c_int32)]),
+    "ar_table_check_ex": (C.c_int, [C.POINTER(ar_call), C.POINTER(ar_oprec), C.c_size_t, C.POINTER(C.c_int32)]),
     "ar_cost_report": (C.c_int, [C.c_void_p, C.c_double, C.c_double, C.c_double, C.POINTER(ar_cost)]),
     "ar_cost_steps": (C.c_int, [C.c_void_p, C.POINTER(C.c_int64), C.POINTER(C.c_int64), C.POINTER(C.c_int64)]),
     "ar_set_cost_model": (C.c_int, [C.POINTER(ar_cost_model)]),
@@ -196,8 +210,9 @@ def _event(ev):
 
 
 def make_call(P, n, dtype, op="sum", algo="ring", knob=0, exec="fused", batch=1, groups=None,
-              workspace=None, workspace_bytes=0, start_event=None, stop_event=None):
+              workspace=None, workspace_bytes=0, start_event=None, stop_event=None, collective="allreduce"):
     call = ar_call()
+    call.collective = _enum(COLLECTIVES, collective)
     call.P, call.n, call.batch = int(P), int(n), int(batch)
     call.dtype, call.op = _enum(DTYPES, dtype), _enum(OPS, op)
     call.algo, call.knob, call.exec = _enum(ALGOS, algo), int(knob), _enum(EXECS, exec)
@@ -217,6 +232,16 @@ def make_call(P, n, dtype, op="sum", algo="ring", knob=0, exec="fused", batch=1,
 def ar_allreduce(bufs, P, n, dtype, op, algo, knob=0, stream=None):
     _check(lib.ar_allreduce(_ptrs(bufs), int(P), int(n), _enum(DTYPES, dtype), _enum(OPS, op),
                             _enum(ALGOS, algo), int(knob), _stream(stream)))
+
+
+def ar_reduce_scatter(bufs, P, n, dtype, op, algo, stream=None):
+    _check(lib.ar_reduce_scatter(_ptrs(bufs), int(P), int(n), _enum(DTYPES, dtype), _enum(OPS, op),
+                                 _enum(ALGOS, algo), _stream(stream)))
+
+
+def ar_all_gather(bufs, P, n, dtype, algo, stream=None):
+    _check(lib.ar_all_gather(_ptrs(bufs), int(P), int(n), _enum(DTYPES, dtype), _enum(ALGOS, algo),
+                             _stream(stream)))
 
 
 def ar_allreduce_ex(bufs, call: ar_call, stream=None):
@@ -264,6 +289,14 @@ def ar_select(call: ar_call):
     a, k, t = C.c_int32(0), C.c_int32(0), C.c_double(0)
     _check(lib.ar_select(C.byref(call), C.byref(a), C.byref(k), C.byref(t)))
     return ALGO_NAMES[a.value], k.value, t.value
+
+
+def ar_table_check_ex(call: ar_call, ops) -> bool:
+    """ar_table_check for the call's collective; returns the single-port flag."""
+    arr = (ar_oprec * max(len(ops), 1))(*ops)
+    sp = C.c_int32(0)
+    _check(lib.ar_table_check_ex(C.byref(call), arr, len(ops), C.byref(sp)))
+    return bool(sp.value)
 
 
 def ar_status_string(st) -> str:

@@ -29,7 +29,8 @@ SOURCES = [
     ("sched.cpp", False),
     ("abi.cpp", False),
     ("exec.hip", True),
-] + [(f"launch_{d}_{o}.hip", True) for d in ("i32", "f32", "bf16") for o in ("sum", "max")]
+] + [(f"launch_{d}_{o}.hip", True) for d in ("i32", "f32", "bf16") for o in ("sum", "max")] + \
+    [(f"launch_{d}_avg.hip", True) for d in ("f32", "bf16")]
 
 
 def _compile(src: str, device: bool) -> str:

@@ -36,7 +36,7 @@ std::map<std::string, std::pair<ar::Spec, double>> g_choices;
 std::string choice_key(const ar::Spec& s) {
   std::string k = std::to_string(s.P) + "/" + std::to_string(s.n) + "/" + std::to_string(s.batch) + "/" +
                   std::to_string(s.dtype) + "/" + std::to_string(s.op) + "/" + std::to_string(s.algo) + "/" +
-                  std::to_string(s.knob) + "/";
+                  std::to_string(s.knob) + "/" + std::to_string(s.coll) + "/";
   for (int g : s.groups) k += std::to_string(g) + ",";
   return k;
 }
@@ -81,6 +81,9 @@ bool to_spec(const ar_call* c, ar::Spec* s, std::string* err) {
     if (!ar::validate_spec(probe, err)) return false;
   }
   if (c->exec < AR_EXEC_FUSED || c->exec > AR_EXEC_REPLAY) { *err = "unknown exec mode"; return false; }
+  if (c->collective < AR_ALLREDUCE || c->collective > AR_ALL_GATHER) { *err = "unknown collective"; return false; }
+  s->coll = c->collective;
+  if (s->coll == AR_ALL_GATHER) s->op = ar::O_SUM;  // copies only: the op plays no part
   if (ar::is_auto(*s)) return resolve(s, nullptr, err);
   return ar::validate_spec(*s, err);
 }
@@ -194,6 +197,37 @@ ar_status ar_allreduce(void* const* bufs, int32_t P, int64_t n, int32_t dtype, i
   return ar_allreduce_ex(bufs, &c, stream);
 }
 
+ar_status ar_reduce_scatter(void* const* bufs, int32_t P, int64_t n, int32_t dtype, int32_t op, int32_t algo,
+                            void* stream) {
+  if (algo == AR_AHC) return fail(AR_INVALID_ARGUMENT, "AR_AHC has no reduce-scatter half here");
+  ar_call c;
+  std::memset(&c, 0, sizeof(c));
+  c.P = P;
+  c.n = n;
+  c.batch = 1;
+  c.dtype = dtype;
+  c.op = op;
+  c.algo = algo;
+  c.exec = AR_EXEC_FUSED;
+  c.collective = AR_REDUCE_SCATTER;
+  return ar_allreduce_ex(bufs, &c, stream);
+}
+
+ar_status ar_all_gather(void* const* bufs, int32_t P, int64_t n, int32_t dtype, int32_t algo, void* stream) {
+  if (algo == AR_AHC) return fail(AR_INVALID_ARGUMENT, "AR_AHC has no all-gather half here");
+  ar_call c;
+  std::memset(&c, 0, sizeof(c));
+  c.P = P;
+  c.n = n;
+  c.batch = 1;
+  c.dtype = dtype;
+  c.op = AR_SUM;
+  c.algo = algo;
+  c.exec = AR_EXEC_FUSED;
+  c.collective = AR_ALL_GATHER;
+  return ar_allreduce_ex(bufs, &c, stream);
+}
+
 ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes) {
   std::string err;
   ar::Spec spec;
@@ -268,6 +302,20 @@ ar_status ar_table_check(int32_t P, int64_t n, int32_t dtype, const ar_oprec* op
   if (!ops && count) return fail(AR_INVALID_ARGUMENT, "ops is NULL");
   if (dtype < AR_INT32 || dtype > AR_BF16) return fail(AR_INVALID_ARGUMENT, "unknown dtype");
   ar::TableCheck tc = ar::check_table(P, n, dtype, reinterpret_cast<const ar::OpRec*>(ops), count);
+  if (single_port) *single_port = tc.single_port ? 1 : 0;
+  if (!tc.ok) return fail(AR_INVALID_ARGUMENT, tc.message);
+  return AR_OK;
+}
+
+ar_status ar_table_check_ex(const ar_call* call, const ar_oprec* ops, size_t count, int32_t* single_port) {
+  if (!call) return fail(AR_INVALID_ARGUMENT, "call is NULL");
+  if (!ops && count) return fail(AR_INVALID_ARGUMENT, "ops is NULL");
+  if (call->dtype < AR_INT32 || call->dtype > AR_BF16) return fail(AR_INVALID_ARGUMENT, "unknown dtype");
+  if (call->collective < AR_ALLREDUCE || call->collective > AR_ALL_GATHER)
+    return fail(AR_INVALID_ARGUMENT, "unknown collective");
+  if (call->n < 0) return fail(AR_INVALID_ARGUMENT, "n must be >= 0");
+  ar::TableCheck tc = ar::check_table(call->P, call->n, call->dtype, reinterpret_cast<const ar::OpRec*>(ops),
+                                      count, call->collective);
   if (single_port) *single_port = tc.single_port ? 1 : 0;
   if (!tc.ok) return fail(AR_INVALID_ARGUMENT, tc.message);
   return AR_OK;

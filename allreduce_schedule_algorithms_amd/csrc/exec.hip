@@ -45,7 +45,8 @@ std::mutex g_mu;
 
 std::string spec_key(const Spec& s) {
   std::ostringstream k;
-  k << s.P << ',' << s.n << ',' << s.batch << ',' << s.dtype << ',' << s.op << ',' << s.algo << ',' << s.knob << ':';
+  k << s.P << ',' << s.n << ',' << s.batch << ',' << s.dtype << ',' << s.op << ',' << s.algo << ',' << s.knob << ','
+    << s.coll << ':';
   for (int g : s.groups) k << g << '.';
   return k.str();
 }
@@ -178,6 +179,7 @@ RunResult build_items(Plan& pl, bool vec) {
           c.dst2_rank = uint8_t(s.ops[o.pair].dst_rank);
           c.dst2_slot = uint8_t(s.ops[o.pair].dst_slot);
         }
+        if (sp.op == O_AVG && s.completes[i]) c.kind |= kLitAvg;
         const int32_t tag = int32_t(codes.size());
         codes.push_back(c);
         if (sp.batch > 1 && o.offset == 0 && o.length == sp.n) {
@@ -277,8 +279,10 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
     if ((DTV) == D_INT32 && (OPV) == O_SUM) { constexpr int DT = D_INT32, OPK = O_SUM; CALL; } \
     else if ((DTV) == D_INT32) { constexpr int DT = D_INT32, OPK = O_MAX; CALL; }              \
     else if ((DTV) == D_FP32 && (OPV) == O_SUM) { constexpr int DT = D_FP32, OPK = O_SUM; CALL; } \
+    else if ((DTV) == D_FP32 && (OPV) == O_AVG) { constexpr int DT = D_FP32, OPK = O_AVG; CALL; } \
     else if ((DTV) == D_FP32) { constexpr int DT = D_FP32, OPK = O_MAX; CALL; }                \
     else if ((OPV) == O_SUM) { constexpr int DT = D_BF16, OPK = O_SUM; CALL; }                 \
+    else if ((OPV) == O_AVG) { constexpr int DT = D_BF16, OPK = O_AVG; CALL; }                 \
     else { constexpr int DT = D_BF16, OPK = O_MAX; CALL; }                                     \
   } while (0)
 
@@ -319,8 +323,9 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
     ptrs.p[p] = bufs[p];
     if (reinterpret_cast<uintptr_t>(bufs[p]) % 16) vec = false;
   }
+  ptrs.div = float(spec.P);
   const int64_t total = spec.n * spec.batch;
-  if (exec == E_FUSED && spec.algo == A_DIRECT) {
+  if (exec == E_FUSED && spec.algo == A_DIRECT && spec.coll == C_ALLREDUCE) {
     hipError_t e = hipSuccess;
     AR_DISPATCH(spec.dtype, spec.op, (e = launch_direct_t<DT, OPK>(vec, ptrs, spec.P, total, st, ev)));
     if (e != hipSuccess) return hip_fail(e, "launching the direct kernel");

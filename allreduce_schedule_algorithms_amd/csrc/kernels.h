@@ -15,6 +15,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct RankPtrs {
   void* p[kMaxRanks];
+  float div;  // O_AVG: the complete sum is divided by this (P), once, before the store
 };
 
 // Work item: `count` > 0 is a run of vectors, < 0 a run of -count single elements;
@@ -51,7 +52,7 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
 }
 
 template <int OPK> __device__ __forceinline__ float cmb(float a, float b) {
-  if constexpr (OPK == O_SUM) {
+  if constexpr (OPK == O_SUM || OPK == O_AVG) {
     return a + b;
   } else {
     // total order on non-NaN floats with -0 < +0: flip the magnitude bits of negatives
@@ -307,6 +308,10 @@ __device__ __forceinline__ void replay(const RankPtrs& ptrs, const int32_t* __re
   for (int t = 0; t < TM; ++t) {
     if (t < ntrees) {
       const int32_t* ot = outs[t];
+      if constexpr (OPK == O_AVG) {
+#pragma unroll
+        for (int i = 0; i < nvals<DT, M>(); ++i) res[t][i] = res[t][i] / ptrs.div;
+      }
       st_user_all<DT, M>(ptrs, nouts[t], [&](int i) { return ot[i]; }, e, ok, res[t]);
     }
   }
@@ -427,7 +432,7 @@ struct LitCode {
   uint8_t kind;  // bit 0: copy (else combine into dst); bit 1: second destination
   uint8_t src_rank, src_slot, own_slot, dst_rank, dst_slot, dst2_rank, dst2_slot;
 };
-enum : uint8_t { kLitCopy = 1, kLitDst2 = 2 };
+enum : uint8_t { kLitCopy = 1, kLitDst2 = 2, kLitAvg = 4 };  // kLitAvg: the combination completes an average
 struct LitWork {
   int64_t start;  // first element of the chunk, or first packed chunk (count == 0)
   int32_t count;  // > 0 vectors, < 0 elements, 0 packed group
@@ -448,6 +453,12 @@ __device__ __forceinline__ void literal_one(const RankPtrs& ptrs, const WsDesc& 
     ld_slot<DT, M>(ptrs, ws, c.dst_rank, c.own_slot, e, ok, o);
 #pragma unroll
     for (int i = 0; i < N; ++i) r[i] = cmb<OPK>(o[i], s[i]);
+    if constexpr (OPK == O_AVG) {
+      if (c.kind & kLitAvg) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) r[i] = r[i] / ptrs.div;
+      }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < N; ++i) r[i] = s[i];
@@ -508,6 +519,10 @@ __device__ __forceinline__ void direct_one(const RankPtrs& ptrs, int P, int64_t 
         for (int i = 0; i < N; ++i) acc[i] = cmb<OPK>(acc[i], l[i]);
       }
     }
+  }
+  if constexpr (OPK == O_AVG) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = acc[i] / ptrs.div;
   }
   st_user_all<DT, M>(ptrs, P, [](int i) { return i; }, e, ok, acc);
 }

@@ -161,13 +161,10 @@ static void fold_out(BufGen& g, int P, int Pp) {
   g.end();
 }
 
-// Recursive halving reduce-scatter + recursive doubling all-gather over P'
-// parts, partner distance P'/2 first.
-static void gen_rh_rd(int P, Exprs& ex, Logical& lg) {
-  int Pp = pow2_floor(P);
-  int L = ceil_log2(Pp);
-  BufGen g(P, Pp, ex, lg);
-  fold_in(g, P, Pp);
+// Recursive halving over ranks 0..P'-1 (P' parts, partner distance P'/2
+// first): afterwards rank p holds the complete part p.
+static void halving(BufGen& g, int Pp) {
+  const int L = ceil_log2(Pp);
   for (int s = 0; s < L; ++s) {
     int d = Pp >> (s + 1);
     g.begin();
@@ -178,6 +175,12 @@ static void gen_rh_rd(int P, Exprs& ex, Logical& lg) {
     }
     g.end();
   }
+}
+
+// Recursive doubling all-gather: distances 1, 2, ..., each rank copying its
+// current window of parts to p XOR d.
+static void doubling(BufGen& g, int Pp) {
+  const int L = ceil_log2(Pp);
   for (int s = L - 1; s >= 0; --s) {
     int d = Pp >> (s + 1);
     g.begin();
@@ -187,7 +190,68 @@ static void gen_rh_rd(int P, Exprs& ex, Logical& lg) {
     }
     g.end();
   }
+}
+
+// Recursive halving reduce-scatter + recursive doubling all-gather over P'
+// parts, with fold-in / fold-out for the excess ranks.
+static void gen_rh_rd(int P, Exprs& ex, Logical& lg) {
+  int Pp = pow2_floor(P);
+  BufGen g(P, Pp, ex, lg);
+  fold_in(g, P, Pp);
+  halving(g, Pp);
+  doubling(g, Pp);
   fold_out(g, P, Pp);
+}
+
+// Reduce-scatter and all-gather halves (part q belongs to rank q; P parts).
+// Ring: the ring's phases with part labels rotated by one, so that part q
+// travels q+1, q+2, ..., q and completes on arrival at rank q.
+static void gen_ring_rs(int P, Exprs& ex, Logical& lg) {
+  BufGen g(P, P, ex, lg);
+  for (int t = 0; t < P - 1; ++t) {
+    g.begin();
+    for (int r = 0; r < P; ++r) {
+      int k = ((r - t - 1) % P + P) % P;
+      g.msg(K_REDUCE, r, (r + 1) % P, k, k + 1);
+    }
+    g.end();
+  }
+}
+static void gen_ring_ag(int P, Exprs& ex, Logical& lg) {
+  BufGen g(P, P, ex, lg);
+  for (int t = 0; t < P - 1; ++t) {
+    g.begin();
+    for (int r = 0; r < P; ++r) {
+      int k = ((r - t) % P + P) % P;
+      g.msg(K_COPY, r, (r + 1) % P, k, k + 1);
+    }
+    g.end();
+  }
+}
+// Direct: the one-root fold (rank order), then rank 0 hands part q to rank q;
+// all-gather: every rank sends its part to every other rank in one step.
+static void gen_direct_rs(int P, Exprs& ex, Logical& lg) {
+  BufGen g(P, P, ex, lg);
+  for (int s = 1; s < P; ++s) { g.begin(); g.msg(K_REDUCE, s, 0, 0, P); g.end(); }
+  g.begin();
+  for (int q = 1; q < P; ++q) g.msg(K_COPY, 0, q, q, q + 1);
+  g.end();
+}
+static void gen_direct_ag(int P, Exprs& ex, Logical& lg) {
+  BufGen g(P, P, ex, lg);
+  g.begin();
+  for (int q = 0; q < P; ++q)
+    for (int d = 0; d < P; ++d)
+      if (d != q) g.msg(K_COPY, q, d, q, q + 1);
+  g.end();
+}
+static void gen_halving_rs(int P, Exprs& ex, Logical& lg) {
+  BufGen g(P, P, ex, lg);
+  halving(g, P);
+}
+static void gen_doubling_ag(int P, Exprs& ex, Logical& lg) {
+  BufGen g(P, P, ex, lg);
+  doubling(g, P);
 }
 
 // Recursive doubling: full-buffer exchange with partner p XOR d, d = P'/2 first.
@@ -305,7 +369,7 @@ static void gen_ahc(int P, const std::vector<int>& groups, Exprs& ex, Logical& l
 // t_j(i) = i + j mod P (cyclic group) or i XOR j (self-inverse group). The
 // shifted schedules S_j, j < N_{L-r}, run together; an identical vector (same
 // placement, same tree) is sent and combined once.
-static void gen_generalized(int P, int r, bool use_xor, Exprs& ex, Logical& lg) {
+static void gen_generalized(int P, int r, bool use_xor, Exprs& ex, Logical& lg, int coll = C_ALLREDUCE) {
   int L = ceil_log2(P);
   std::vector<int> N(1, P), h;
   for (int i = 0; i < L; ++i) N.push_back((N.back() + 1) / 2);
@@ -319,7 +383,7 @@ static void gen_generalized(int P, int r, bool use_xor, Exprs& ex, Logical& lg) 
   for (int j = 0; j < J; ++j)
     for (int k = 0; k < P; ++k)
       for (int a = 0; a < P; ++a) vals[j][k][a] = holder(a, place(k, j));
-  for (int i = 0; i < L; ++i) {
+  for (int i = 0; i < (coll == C_ALL_GATHER ? 0 : L); ++i) {
     lg.steps.emplace_back();
     auto& st = lg.steps.back();
     std::unordered_set<uint64_t> seen;  // (dst, atom, result) already combined this step
@@ -339,6 +403,7 @@ static void gen_generalized(int P, int r, bool use_xor, Exprs& ex, Logical& lg) 
       }
     vals.swap(nv);
   }
+  if (coll == C_REDUCE_SCATTER) return;  // placement 0 holds part a at rank a
   std::vector<std::vector<int>> dist(P);
   for (int j = 0; j < J; ++j) dist[j] = vals[j][0];  // result j sits at placement j
   for (int i = L - r - 1; i >= 0; --i) {
@@ -365,12 +430,21 @@ bool validate_spec(const Spec& s, std::string* err) {
   if (s.batch < 1) return fail("batch must be >= 1");
   if (s.n > 0 && s.batch > (int64_t(1) << 40) / s.n) return fail("batch * n is too large");
   if (s.dtype < D_INT32 || s.dtype > D_BF16) return fail("unknown dtype");
-  if (s.op < O_SUM || s.op > O_MAX) return fail("unknown op");
+  if (s.op < O_SUM || s.op > O_AVG) return fail("unknown op");
+  if (s.op == O_AVG && s.dtype == D_INT32) return fail("avg is defined for fp32 and bf16 only");
+  if (s.coll < C_ALLREDUCE || s.coll > C_ALL_GATHER) return fail("unknown collective");
   if (s.algo < 0 || s.algo >= A_NUM_ALGOS) return fail("unknown algorithm");
   int L = ceil_log2(s.P);
   if (s.algo == A_GENERALIZED || s.algo == A_GENERALIZED_XOR) {
     if (s.knob < 0 || s.knob > L) return fail("knob r must be in [0, ceil(log2 P)]");
     if (s.algo == A_GENERALIZED_XOR && (s.P & (s.P - 1))) return fail("the XOR group needs P to be a power of two");
+  }
+  if (s.coll != C_ALLREDUCE) {
+    if (!half_supported(s.algo))
+      return fail("reduce-scatter / all-gather support direct, ring, rh_rd, generalized and generalized_xor");
+    if (s.algo == A_RH_RD && (s.P & (s.P - 1))) return fail("the halving / doubling half needs P to be a power of two");
+    if ((s.algo == A_GENERALIZED || s.algo == A_GENERALIZED_XOR) && s.knob != 0)
+      return fail("the generalized halves use knob r = 0");
   }
   if (s.algo == A_AHC) {
     if (s.groups.empty()) return fail("AHC needs group sizes");
@@ -390,6 +464,16 @@ bool validate_spec(const Spec& s, std::string* err) {
 // realizer: logical ops -> slot table with snapshot semantics
 // ----------------------------------------------------------------------------
 static inline uint64_t ckey(int cell, int val) { return (uint64_t(uint32_t(cell)) << 32) | uint32_t(val); }
+
+// What a rank's buffer must hold at the end, per part: a complete reduction
+// (Allreduce everywhere; reduce-scatter at the part's owner), anything
+// (reduce-scatter elsewhere), or the owner's own value (all-gather: the leaf).
+constexpr int kNeedComplete = -2, kDontCare = -1;
+static int target_of(int coll, int rank, int part) {
+  if (coll == C_ALLREDUCE) return kNeedComplete;
+  if (coll == C_REDUCE_SCATTER) return rank == part ? kNeedComplete : kDontCare;
+  return part;
+}
 
 struct Realizer {
   const Spec& sp;
@@ -432,8 +516,19 @@ struct Realizer {
         if (o.kind == K_REDUCE) last_read[ckey(o.dst * C + o.atom, o.own_val)] = int(s);
         present[size_t(o.dst) * C + o.atom].push_back(o.out_val);
       }
+    if (sp.coll != C_ALLREDUCE && C != P) { err = "a half needs one atom per part"; return false; }
     final_val.assign(size_t(P) * C, -1);
     for (size_t c = 0; c < present.size(); ++c) {
+      const int tgt = target_of(sp.coll, int(c / C), int(c % C));
+      if (tgt == kDontCare) continue;
+      if (tgt >= 0) {  // an owner's own value, copied
+        if (std::find(present[c].begin(), present[c].end(), tgt) == present[c].end()) {
+          err = "a rank ends without an owner's part";
+          return false;
+        }
+        final_val[c] = tgt;
+        continue;
+      }
       int fv = -1;
       for (int v : present[c]) {
         if (!ex.complete(v)) continue;
@@ -476,7 +571,7 @@ struct Realizer {
         bool used_pair = false;
         auto ok = [&](int sl) {
           used_pair = false;
-          if (bf16 && sl == 0 && !ex.complete(o.out_val)) return false;
+          if (bf16 && sl == 0 && !ex.complete(o.out_val) && !ex.is_leaf(o.out_val)) return false;
           if (written.count(ckey(dc, sl))) return false;
           int v = value_at(dc, sl);
           if (v < 0) return true;
@@ -522,7 +617,7 @@ struct Realizer {
 // ----------------------------------------------------------------------------
 // table checker (any table, including corrupted ones)
 // ----------------------------------------------------------------------------
-TableCheck check_table(int P, int64_t n, int dtype, const OpRec* ops, size_t count) {
+TableCheck check_table(int P, int64_t n, int dtype, const OpRec* ops, size_t count, int coll) {
   TableCheck tc;
   auto fail = [&](const std::string& m) { tc.ok = false; tc.message = m; return tc; };
   if (P < 1 || P > kMaxRanks) return fail("bad P");
@@ -576,9 +671,14 @@ TableCheck check_table(int P, int64_t n, int dtype, const OpRec* ops, size_t cou
     for (auto& kv : srcs) if (kv.second.size() > 1) tc.single_port = false;
     i0 = i1;
   }
-  // symbolic replay over elementary intervals
+  // symbolic replay over elementary intervals (cut at part boundaries too:
+  // a half's targets change from part to part)
+  if (coll < C_ALLREDUCE || coll > C_ALL_GATHER) return fail("unknown collective");
+  const int64_t part = (n + P - 1) / P;
   std::vector<int64_t> cuts = {0, n};
   for (size_t i = 0; i < count; ++i) { cuts.push_back(ops[i].offset); cuts.push_back(ops[i].offset + ops[i].length); }
+  if (coll != C_ALLREDUCE)
+    for (int q = 1; q < P; ++q) cuts.push_back(std::min<int64_t>(q * part, n));
   std::sort(cuts.begin(), cuts.end());
   cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
   Exprs ex(P);
@@ -614,7 +714,7 @@ TableCheck check_table(int P, int64_t n, int dtype, const OpRec* ops, size_t cou
         } else {
           out = sv;
         }
-        if (dtype == D_BF16 && o.dst_slot == 0) {
+        if (dtype == D_BF16 && o.dst_slot == 0 && !ex.is_leaf(out)) {
           if (!ex.complete(out)) return fail("an incomplete bf16 partial is stored in the caller's buffer");
           r = 1;
         }
@@ -623,11 +723,15 @@ TableCheck check_table(int P, int64_t n, int dtype, const OpRec* ops, size_t cou
       for (auto& u : upd) { val[std::get<0>(u)] = std::get<1>(u); rnd[std::get<0>(u)] = std::get<2>(u); }
       j0 = j1;
     }
+    const int owner = part > 0 ? int(lo / part) : 0;
     for (int p = 0; p < P; ++p) {
       int v = val[size_t(p) * nslots];
-      if (P > 1 && !ex.complete(v)) {
+      const int tgt = target_of(coll, p, owner);
+      if (P == 1 || tgt == kDontCare) continue;
+      if (tgt >= 0 ? v != tgt : !ex.complete(v)) {
         std::ostringstream m;
-        m << "rank " << p << " does not hold the complete result for elements [" << lo << ", " << hi << ")";
+        m << "rank " << p << (tgt >= 0 ? " does not hold the owner's part" : " does not hold the complete result")
+          << " for elements [" << lo << ", " << hi << ")";
         return fail(m.str());
       }
     }
@@ -705,11 +809,15 @@ static bool plan_fused(Schedule& s, std::string* err) {
     std::vector<std::vector<int>> outs;
     for (int p = 0; p < P; ++p) {
       int v = val[size_t(p) * S];
-      if (!ex.complete(v)) { *err = "fused planner: incomplete result"; return false; }
+      const int tgt = target_of(s.spec.coll, p, a);
+      if (tgt == kDontCare) continue;
+      if (tgt >= 0 ? v != tgt : !ex.complete(v)) { *err = "fused planner: incomplete result"; return false; }
+      if (v == p) continue;  // the rank keeps its own value
       auto it = std::find(roots.begin(), roots.end(), v);
       if (it == roots.end()) { roots.push_back(v); outs.push_back({p}); }
       else outs[it - roots.begin()].push_back(p);
     }
+    if (roots.empty()) continue;  // nothing to write in this atom
     std::vector<int32_t> words;
     words.push_back(int32_t(roots.size()));
     int range_need = 0;
@@ -763,9 +871,25 @@ static bool plan_fused(Schedule& s, std::string* err) {
 // ----------------------------------------------------------------------------
 // build
 // ----------------------------------------------------------------------------
+bool half_supported(int algo) {
+  return algo == A_DIRECT || algo == A_RING || algo == A_RH_RD || algo == A_GENERALIZED || algo == A_GENERALIZED_XOR;
+}
+
 static bool generate(const Spec& spec, Exprs& ex, Logical& lg, std::string* err) {
   const int P = spec.P;
   if (P <= 1) return true;
+  if (spec.coll != C_ALLREDUCE) {
+    const bool rs = spec.coll == C_REDUCE_SCATTER;
+    switch (spec.algo) {
+      case A_DIRECT: rs ? gen_direct_rs(P, ex, lg) : gen_direct_ag(P, ex, lg); break;
+      case A_RING: rs ? gen_ring_rs(P, ex, lg) : gen_ring_ag(P, ex, lg); break;
+      case A_RH_RD: rs ? gen_halving_rs(P, ex, lg) : gen_doubling_ag(P, ex, lg); break;
+      case A_GENERALIZED: gen_generalized(P, 0, false, ex, lg, spec.coll); break;
+      case A_GENERALIZED_XOR: gen_generalized(P, 0, true, ex, lg, spec.coll); break;
+      default: if (err) *err = "no reduce-scatter / all-gather half for this algorithm"; return false;
+    }
+    return true;
+  }
   switch (spec.algo) {
     case A_DIRECT: gen_direct(P, ex, lg); break;
     case A_RING: gen_ring(P, ex, lg); break;
@@ -812,9 +936,10 @@ Schedule* build_schedule(const Spec& spec, std::string* err) {
     if (pair[i] < 0 && !s->ops.empty() && i > 0 && rec_of[i - 1] == int(s->ops.size()) - 1) {
       OpRec& last = s->ops.back();
       const LOp& q = flat[i - 1];
+      const bool same_completion = s->completes.back() == uint8_t(o.kind == K_REDUCE && ex.complete(o.out_val));
       if (last.pair < 0 && pair[i - 1] < 0 && last.step == step_of[i] && q.kind == o.kind && q.src == o.src &&
           q.dst == o.dst && q.atom + 1 == o.atom && last.src_slot == ssl[i] && last.dst_slot == dsl[i] &&
-          last.own_slot == osl[i] && last.offset + last.length == lo) {
+          last.own_slot == osl[i] && last.offset + last.length == lo && same_completion) {
         last.length += hi - lo;
         rec_of[i] = int(s->ops.size()) - 1;
         continue;
@@ -823,6 +948,7 @@ Schedule* build_schedule(const Spec& spec, std::string* err) {
     OpRec r{step_of[i], o.kind, o.src, ssl[i], o.dst, dsl[i], osl[i], -1, lo, hi - lo};
     rec_of[i] = int(s->ops.size());
     s->ops.push_back(r);
+    s->completes.push_back(uint8_t(o.kind == K_REDUCE && ex.complete(o.out_val)));
   }
   for (size_t i = 0; i < flat.size(); ++i)
     if (pair[i] >= 0 && rec_of[i] >= 0) s->ops[rec_of[i]].pair = rec_of[pair[i]];
@@ -842,6 +968,7 @@ Schedule* build_schedule(const Spec& spec, std::string* err) {
           }
         }
         s->ops.push_back({s->nsteps, K_MOVE, p, sl, p, 0, -1, -1, lo, hi - lo});
+        s->completes.push_back(0);
         s->finalize_ops++;
       }
     }
@@ -853,7 +980,7 @@ Schedule* build_schedule(const Spec& spec, std::string* err) {
                                [](const OpRec& o, int v) { return o.step < v; });
     s->steps_begin[st] = int32_t(it - s->ops.begin());
   }
-  TableCheck tc = check_table(P, spec.n, spec.dtype, s->ops.data(), s->ops.size());
+  TableCheck tc = check_table(P, spec.n, spec.dtype, s->ops.data(), s->ops.size(), spec.coll);
   if (!tc.ok) {
     if (err) *err = "internal: generated table fails its check: " + tc.message;
     return nullptr;
@@ -892,6 +1019,7 @@ void cost_steps(const Schedule& s, int64_t* sent, int64_t* recv, int64_t* reduce
 static double closed_form(const Schedule& s, double m, double alpha, double beta, double gamma) {
   const int P = s.spec.P;
   if (P <= 1) return 0.0;
+  if (s.spec.coll != C_ALLREDUCE) return std::numeric_limits<double>::quiet_NaN();  // pages: Allreduce only
   const int L = ceil_log2(P);
   const double u = m / P;
   const int Pp = pow2_floor(P);
@@ -988,7 +1116,11 @@ CostOut cost_walk(const Schedule& s, double alpha, double beta, double gamma) {
     }
   }
   c.fused_hbm_bytes = fz;
-  c.essential_bytes = 2.0 * P * double(s.spec.n) * batch * elt;
+  // every input read once and every output written once: P n in and P n out
+  // (Allreduce); P n in and n out (reduce-scatter); n in and (P - 1) n out
+  // (all-gather: each part read at its owner, written to the others)
+  const double pn = double(P) * double(s.spec.n) * batch * elt, n1 = double(s.spec.n) * batch * elt;
+  c.essential_bytes = s.spec.coll == C_ALLREDUCE ? 2.0 * pn : s.spec.coll == C_REDUCE_SCATTER ? pn + n1 : pn;
   return c;
 }
 
@@ -1081,14 +1213,20 @@ bool select_spec(const Spec& in, const CostModel& m, Spec* out, double* seconds,
   const int L = ceil_log2(in.P);
   const bool pow2 = (in.P & (in.P - 1)) == 0;
   std::vector<std::pair<int, int>> cand;  // (algo, knob), in the order ties are broken
-  if (in.algo == kAutoAlgo) {
+  if (in.algo == kAutoAlgo && in.coll != C_ALLREDUCE) {
+    cand.push_back({A_DIRECT, 0});
+    cand.push_back({A_RING, 0});
+    if (pow2) cand.push_back({A_RH_RD, 0});
+    cand.push_back({A_GENERALIZED, 0});
+    if (pow2) cand.push_back({A_GENERALIZED_XOR, 0});
+  } else if (in.algo == kAutoAlgo) {
     for (int a : {A_DIRECT, A_RING, A_RH_RD, A_RD, A_BINOMIAL}) cand.push_back({a, 0});
     for (int r = 0; r <= L; ++r) cand.push_back({A_GENERALIZED, r});
     if (pow2)
       for (int r = 0; r <= L; ++r) cand.push_back({A_GENERALIZED_XOR, r});
     if (!in.groups.empty()) cand.push_back({A_AHC, 0});
   } else {
-    for (int r = 0; r <= L; ++r) cand.push_back({in.algo, r});
+    for (int r = 0; r <= (in.coll == C_ALLREDUCE ? L : 0); ++r) cand.push_back({in.algo, r});
   }
   bool have = false;
   double best_t = 0;

@@ -27,7 +27,12 @@ enum Algo : int32_t {
   A_GENERALIZED = 5, A_GENERALIZED_XOR = 6, A_AHC = 7, A_NUM_ALGOS = 8
 };
 enum Dtype : int32_t { D_INT32 = 0, D_FP32 = 1, D_BF16 = 2 };
-enum Op : int32_t { O_SUM = 0, O_MAX = 1 };
+// O_AVG combines as a sum; the complete result is divided by P once.
+enum Op : int32_t { O_SUM = 0, O_MAX = 1, O_AVG = 2 };
+// Collective: the Allreduce, or one of its halves over the ceil split into P
+// parts (reduce-scatter: rank q ends with the reduced part q; all-gather: rank
+// q contributes its part q and every rank ends with all parts).
+enum Coll : int32_t { C_ALLREDUCE = 0, C_REDUCE_SCATTER = 1, C_ALL_GATHER = 2 };
 
 constexpr int kMaxRanks = 256;
 
@@ -40,6 +45,7 @@ struct Spec {
   int algo = A_RING;
   int knob = 0;
   std::vector<int> groups;  // AHC group sizes (contiguous ranks)
+  int coll = C_ALLREDUCE;
 };
 
 // Hash-consed commutative expression DAG over rank leaves 0..P-1.
@@ -95,6 +101,7 @@ struct Schedule {
   int C = 1;  // atoms
   std::vector<std::pair<int64_t, int64_t>> atoms;  // element range per atom
   std::vector<OpRec> ops;  // sorted by step; MOVE ops (step == nsteps) restore slot 0
+  std::vector<uint8_t> completes;  // per op: a REDUCE whose result is a complete reduction
   std::vector<int32_t> steps_begin;  // ops index where each step starts (nsteps + 2 entries)
   int64_t finalize_ops = 0;
   bool single_port = true;
@@ -121,7 +128,10 @@ struct TableCheck {
   int nslots = 0;
   std::string message;
 };
-TableCheck check_table(int P, int64_t n, int dtype, const OpRec* ops, size_t count);
+TableCheck check_table(int P, int64_t n, int dtype, const OpRec* ops, size_t count, int coll = C_ALLREDUCE);
+
+// Whether a schedule has a reduce-scatter / all-gather half here.
+bool half_supported(int algo);
 
 struct CostOut {
   int32_t steps;

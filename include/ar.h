@@ -57,7 +57,24 @@ typedef enum {
 } ar_status;
 
 typedef enum { AR_INT32 = 0, AR_FP32 = 1, AR_BF16 = 2 } ar_dtype;
-typedef enum { AR_SUM = 0, AR_MAX = 1 } ar_op;
+/* AR_AVG (fp32, bf16): the sum, in the accumulation type (fp32), divided by P once when it is
+ * complete, then rounded once to the caller's type (all-reduce blog page, "The APIs": the
+ * average is taken inside the collective). The division is IEEE (correctly rounded). */
+typedef enum { AR_SUM = 0, AR_MAX = 1, AR_AVG = 2 } ar_op;
+
+/* The collective a call runs. Parts are the ceil split of the n elements of an instance into
+ * P parts (part q = [q c, (q + 1) c) cut to n, c = ceil(n / P)); the blog page's FSDP/ZeRO
+ * paragraph ("The APIs") splits the Allreduce into these two halves.
+ *  AR_ALLREDUCE       every rank ends with the reduction of all P buffers.
+ *  AR_REDUCE_SCATTER  rank q ends with the reduction of part q, in place at part q's offsets.
+ *                     Other elements: untouched by AR_EXEC_FUSED; the step-by-step executor may
+ *                     leave partial results there. op as for the Allreduce.
+ *  AR_ALL_GATHER      rank q contributes its part q (its other elements are ignored); every
+ *                     rank ends with every part. op is ignored (copies only).
+ * Halves exist for AR_DIRECT, AR_RING, AR_RH_RD (P a power of two), AR_GENERALIZED and
+ * AR_GENERALIZED_XOR (knob 0: the reduction phase, or the distribution phase, of the
+ * bandwidth-optimal version), and AR_AUTO among those. */
+typedef enum { AR_ALLREDUCE = 0, AR_REDUCE_SCATTER = 1, AR_ALL_GATHER = 2 } ar_collective;
 
 /* Schedules (the pages that define each one):
  *  AR_DIRECT          one root gathers, combines in rank order, broadcasts (all-reduce blog
@@ -125,6 +142,8 @@ typedef struct ar_call {
   void* stop_event;        /* optional hipEvent_t: recorded when the call's last kernel ends.
                               With both set, hipEventElapsedTime gives the device time of the
                               call's kernels without the launch latency in front of them */
+  int32_t collective;      /* ar_collective; 0 (AR_ALLREDUCE) for a zeroed call */
+  int32_t reserved;        /* 0 */
 } ar_call;
 
 /* Plain Allreduce: fused execution, batch 1, no groups (AR_AHC needs ar_allreduce_ex).
@@ -132,7 +151,14 @@ typedef struct ar_call {
 ar_status ar_allreduce(void* const* bufs, int32_t P, int64_t n, int32_t dtype, int32_t op,
                        int32_t algo, int32_t knob, void* stream);
 
-/* Allreduce with every option of ar_call. */
+/* Reduce-scatter and all-gather halves: fused execution, batch 1, no groups (see
+ * ar_collective). bufs: host array of P device pointers, each to n elements. */
+ar_status ar_reduce_scatter(void* const* bufs, int32_t P, int64_t n, int32_t dtype, int32_t op,
+                            int32_t algo, void* stream);
+ar_status ar_all_gather(void* const* bufs, int32_t P, int64_t n, int32_t dtype, int32_t algo,
+                        void* stream);
+
+/* The collective of call->collective (an Allreduce by default) with every option of ar_call. */
 ar_status ar_allreduce_ex(void* const* bufs, const ar_call* call, void* stream);
 
 /* Workspace bytes an AR_EXEC_LITERAL call needs (0 for fused execution). */
@@ -193,6 +219,11 @@ void ar_schedule_free(ar_schedule* s);
  * ar_last_error_message() says why. */
 ar_status ar_table_check(int32_t P, int64_t n, int32_t dtype, const ar_oprec* ops,
                          size_t count, int32_t* single_port);
+/* The same for any collective: P, n, dtype and collective are taken from call (its other
+ * fields are ignored). A reduce-scatter table must leave the complete part q in rank q's slot
+ * 0; an all-gather table must leave the owner's part in every rank's slot 0. */
+ar_status ar_table_check_ex(const ar_call* call, const ar_oprec* ops, size_t count,
+                            int32_t* single_port);
 
 /* ---- alpha-beta-gamma cost report ----
  * A step costs alpha + (bytes sent or received by the busiest rank) * beta + (bytes

@@ -98,19 +98,25 @@ def pipelined_chain_best_m(n: float, p: int, t_start: float, t_byte: float) -> f
 # --------------------------------------------------------------------------
 # model-driven choice of schedule
 # --------------------------------------------------------------------------
-def step_counts(P: int, n: int, algo: str, knob: int = 0, groups=None):
+def step_counts(P: int, n: int, algo: str, knob: int = 0, groups=None, coll: str = "allreduce"):
     """Per-step, per-rank elements sent, received and combined by one instance.
 
     Counts come from the oracle's own replay of the schedule on a one-offset
     sample (the simulator counts whole-buffer elements whatever the sample).
-    Nothing moves when n == 0 or P == 1: zero steps.
+    Nothing moves when n == 0 or P == 1: zero steps. coll selects the
+    Allreduce or its reduce-scatter / all-gather half.
     """
     z = np.zeros((0, P), dtype=np.int64)
     if P == 1 or n == 0:
         return z, z, z
     x = np.zeros((P, 1), dtype=np.int32)
-    _, st = schedules.allreduce(x, algo, "int32", "sum", knob=knob, groups=groups, n=n, idx=[0],
-                                return_stats=True)
+    if coll == "reduce_scatter":
+        _, st = schedules.reduce_scatter(x, algo, "int32", "sum", n=n, idx=[0], return_stats=True)
+    elif coll == "all_gather":
+        _, st = schedules.all_gather(x, algo, "int32", n=n, idx=[0], return_stats=True)
+    else:
+        _, st = schedules.allreduce(x, algo, "int32", "sum", knob=knob, groups=groups, n=n, idx=[0],
+                                    return_stats=True)
     return (np.asarray(st["sent"], dtype=np.int64).reshape(-1, P),
             np.asarray(st["recv"], dtype=np.int64).reshape(-1, P),
             np.asarray(st["reduced"], dtype=np.int64).reshape(-1, P))
@@ -137,9 +143,15 @@ def model_seconds(counts, elt: int, batch: int, alpha: float, beta: float, gamma
     return alpha * S + beta * (float(xb) * elt * batch) + gamma * (float(xg) * elt * batch)
 
 
-def candidates(P: int, algo: str = "auto", groups=None):
+def candidates(P: int, algo: str = "auto", groups=None, coll: str = "allreduce"):
     """(algo, knob) pairs in tie-breaking order."""
     L = ceil_log2(P)
+    pow2 = P & (P - 1) == 0
+    if coll != "allreduce":
+        if algo != "auto":
+            return [(algo, 0)]
+        out = [("direct", 0), ("ring", 0)] + ([("rh_rd", 0)] if pow2 else []) + [("generalized", 0)]
+        return out + ([("generalized_xor", 0)] if pow2 else [])
     if algo != "auto":
         return [(algo, r) for r in range(L + 1)]
     out = [(a, 0) for a in ("direct", "ring", "rh_rd", "rd", "binomial")]
@@ -152,11 +164,11 @@ def candidates(P: int, algo: str = "auto", groups=None):
 
 
 def select(P: int, n: int, dtype: str, alpha: float, beta: float, gamma: float, form: str = "busiest",
-           algo: str = "auto", batch: int = 1, groups=None):
+           algo: str = "auto", batch: int = 1, groups=None, coll: str = "allreduce"):
     """(algo, knob, seconds) of least model time; ties: fewer steps, then earlier candidate."""
     best = None
-    for a, r in candidates(P, algo, groups):
-        c = step_counts(P, n, a, r, groups if a == "ahc" else None)
+    for a, r in candidates(P, algo, groups, coll):
+        c = step_counts(P, n, a, r, groups if a == "ahc" else None, coll)
         t = model_seconds(c, ELT_BYTES[dtype], batch, alpha, beta, gamma, form)
         key = (t, c[0].shape[0])
         if best is None or key < best[0]:

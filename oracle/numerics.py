@@ -56,8 +56,10 @@ class Algebra:
     def __init__(self, dtype: str, op: str):
         if dtype not in ("int32", "fp32", "bf16"):
             raise ValueError(dtype)
-        if op not in ("sum", "max"):
+        if op not in ("sum", "max", "avg"):
             raise ValueError(op)
+        if op == "avg" and dtype == "int32":
+            raise ValueError("avg is defined for floating-point data only")
         self.dtype, self.opname = dtype, op
 
     def load(self, x: np.ndarray) -> np.ndarray:
@@ -69,11 +71,20 @@ class Algebra:
         return bf16_to_f32(x)
 
     def op(self, a: np.ndarray, b: np.ndarray) -> np.ndarray:
-        if self.opname == "sum":
+        if self.opname in ("sum", "avg"):
             return a + b  # uint32 wraps, float32 rounds to nearest even
         if self.dtype == "int32":
             return np.maximum(a, b)
         return max_total(a, b)
+
+    def finish(self, acc: np.ndarray, P: int) -> np.ndarray:
+        """avg: the complete sum divided by P once, in the accumulation type
+        (all-reduce blog page, "The APIs": the average is taken inside the
+        collective). Reading: one IEEE division of the finished sum, no
+        pre-scaling; other ops pass through."""
+        if self.opname != "avg":
+            return acc
+        return (np.asarray(acc, dtype=np.float32) / np.float32(P)).astype(np.float32)
 
     def store(self, acc: np.ndarray) -> np.ndarray:
         if self.dtype == "int32":
@@ -111,6 +122,9 @@ class Symbolic:
 
     def load(self, x: np.ndarray) -> np.ndarray:
         return np.asarray(x, dtype=object).copy()
+
+    def finish(self, acc: np.ndarray, P: int) -> np.ndarray:
+        return acc  # trees: the division does not change the combination order
 
     def store(self, acc: np.ndarray) -> np.ndarray:
         return acc

@@ -112,10 +112,17 @@ def _rh_rd(net: Net):
     Reading: the distance order (P'/2 first) is the one the generalized
     algorithm produces over the XOR group; the pages do not fix it otherwise.
     """
-    n = net.n
     Pp = _fold_in(net)
+    _halving(net, Pp)
+    _doubling(net, Pp)
+    _fold_out(net, Pp)
+
+
+def _halving(net: Net, Pp: int):
+    """The reduction half of recursive halving over ranks 0..P'-1: afterwards
+    rank p holds the complete part p of P' parts."""
+    parts = partition(net.n, Pp)
     L = Pp.bit_length() - 1
-    parts = partition(n, Pp)
 
     def rng(first_part: int, count: int):
         return parts[first_part][0], parts[first_part + count - 1][1]
@@ -128,14 +135,20 @@ def _rh_rd(net: Net):
             give = base + (d if (p & d) == 0 else 0)  # half the partner keeps
             msgs.append((p, p ^ d, *rng(give, d), REDUCE))
         net.step(msgs)
+
+
+def _doubling(net: Net, Pp: int):
+    """The all-gather half: distances 1, 2, ..., each rank copying its whole
+    current window of parts to p XOR d."""
+    parts = partition(net.n, Pp)
+    L = Pp.bit_length() - 1
     for s in reversed(range(L)):
         d = Pp >> (s + 1)
         msgs = []
         for p in range(Pp):
             base = p & ~(d - 1)
-            msgs.append((p, p ^ d, *rng(base, d), COPY))
+            msgs.append((p, p ^ d, parts[base][0], parts[base + d - 1][1], COPY))
         net.step(msgs)
-    _fold_out(net, Pp)
 
 
 # --------------------------------------------------------------------------
@@ -301,7 +314,7 @@ def _levels(P: int):
     return L, N, h
 
 
-def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: str):
+def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: str, phase: str = "all"):
     """Generalized Allreduce (generalized-Allreduce paper: bandwidth-optimal
     section eqs. (17)-(25), intermediate steps eqs. (26)-(36) and Fig. 6,
     latency-optimal section eqs. (38)-(44)). The equations are missing from the
@@ -332,6 +345,10 @@ def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: 
     combining: v_k <- v_{k - h_i} moved back (rank q sends to q + h_i).
     Steps: 2L - r. r = L is the latency-optimal version (no distribution).
 
+    phase "reduce" runs only the reduction with r = 0 (the reduce-scatter the
+    paper notes at its end); phase "gather" runs only the distribution with
+    r = 0, starting from placement 0 = every rank's own part (an all-gather).
+
     Returns (per-rank outputs (P, B, m), stats dict with step counts and the
     per-step number of distinct parts sent / combined per rank).
     """
@@ -361,6 +378,10 @@ def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: 
         # element at offset e (in part i) comes from rank t_j(i)
         return xt[place(part_of, j), cols].T if len(idx) else xacc[0, :, :0].copy()
 
+    if phase not in ("all", "reduce", "gather"):
+        raise ValueError(phase)
+    if phase != "all" and r != 0:
+        raise ValueError("the reduce-scatter and all-gather halves use r = 0")
     J = list(range(N[L - r]))
     sym = Symbolic(P)  # diagonal-level shadow, for dedupe and traffic counts
     sent_steps, red_steps = [], []
@@ -370,7 +391,7 @@ def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: 
     el_sent, el_recv, el_red = [], [], []
     vals = {j: [diag(place(k, j)) for k in range(P)] for j in J}
     syms = {j: [place(k, j) for k in range(P)] for j in J}
-    for i in range(L):
+    for i in range(L if phase != "gather" else 0):
         sends, reds, msgs = set(), set(), set()
         new_vals, new_syms = {}, {}
         for j in J:
@@ -398,6 +419,10 @@ def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: 
 
     src = {j: j for j in J}
     copy_steps = []
+    if phase == "reduce":
+        stats = dict(steps=L, sent=np.array(el_sent).reshape(-1, P), recv=np.array(el_recv).reshape(-1, P),
+                     reduced=np.array(el_red).reshape(-1, P))
+        return results[0], stats
     for i in reversed(range(L - r)):
         es, er = np.zeros(P, dtype=np.int64), np.zeros(P, dtype=np.int64)
         for k in range(N[i] - h[i], N[i]):
@@ -418,7 +443,7 @@ def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: 
                 if m.any():
                     out[p][:, m] = results[j][:, m]
     stats = dict(
-        steps=L + (L - r),
+        steps=(L if phase != "gather" else 0) + (L - r),
         sent=np.array(el_sent).reshape(-1, P),
         recv=np.array(el_recv).reshape(-1, P),
         reduced=np.array(el_red).reshape(-1, P),
@@ -492,7 +517,143 @@ def allreduce(x: np.ndarray, algo: str, dtype: str, op: str = "sum", knob: int =
         stats["algebra"] = alg
         res = out
     else:
-        res = np.stack([alg.store(out[p]) for p in range(P)])
+        res = np.stack([alg.store(alg.finish(out[p], P)) for p in range(P)])
+    if squeeze:
+        res = res[:, 0, :]
+    return (res, stats) if return_stats else res
+
+
+# --------------------------------------------------------------------------
+# the two halves: reduce-scatter and all-gather
+# --------------------------------------------------------------------------
+HALF_ALGOS = ("direct", "ring", "rh_rd", "generalized", "generalized_xor")
+
+
+def _ring_rs(net: Net):
+    """Ring reduce-scatter with rank q ending on part q (the convention of a
+    reduce-scatter that hands rank q block q; all-reduce blog page, "The APIs",
+    FSDP/ZeRO paragraph). It is the ring's first phase ("The ring algorithm")
+    with the part labels rotated by one: in step t rank r passes part
+    (r - t - 1) mod P to r + 1, so part q travels q+1, q+2, ..., q and is
+    complete on arrival at q."""
+    P = net.P
+    parts = partition(net.n, P)
+    for t in range(P - 1):
+        net.step([(r, (r + 1) % P, *parts[(r - t - 1) % P], REDUCE) for r in range(P)])
+
+
+def _ring_ag(net: Net):
+    """Ring all-gather from rank q holding part q: in step t rank r passes part
+    (r - t) mod P (its own part first, then the one it just received)."""
+    P = net.P
+    parts = partition(net.n, P)
+    for t in range(P - 1):
+        net.step([(r, (r + 1) % P, *parts[(r - t) % P], COPY) for r in range(P)])
+
+
+def _direct_rs(net: Net):
+    """The one-root schedule's reduce half (rank 0 folds ranks 1..P-1 in rank
+    order), then one step in which rank 0 hands part q to rank q."""
+    P, n = net.P, net.n
+    parts = partition(n, P)
+    for s in range(1, P):
+        net.step([(s, 0, 0, n, REDUCE)])
+    net.step([(0, q, *parts[q], COPY) for q in range(1, P)])
+
+
+def _direct_ag(net: Net):
+    """One step in which every rank q sends part q to every other rank."""
+    P = net.P
+    parts = partition(net.n, P)
+    net.step([(q, d, *parts[q], COPY) for q in range(P) for d in range(P) if d != q])
+
+
+def _half_input(x, alg, symbolic, P):
+    x = np.asarray(x)
+    squeeze = x.ndim == 2
+    if squeeze:
+        x = x[:, None, :]
+    if symbolic:
+        xacc = np.empty(x.shape, dtype=object)
+        for p in range(P):
+            xacc[p] = p
+    else:
+        xacc = np.stack([alg.load(x[p]) for p in range(P)])
+    return xacc, squeeze
+
+
+def reduce_scatter(x: np.ndarray, algo: str, dtype: str, op: str = "sum", n: int | None = None, idx=None,
+                   symbolic: bool = False, return_stats: bool = False):
+    """Replay a reduce-scatter: rank q ends with the reduced part q of the ceil
+    split into P parts. x as for ``allreduce``. Returns the result vector
+    (element e as rank e // ceil(n / P) holds it), shape (m,) or (B, m).
+
+    Schedules: ring (above), rh_rd = the halving half (P a power of two),
+    generalized / generalized_xor = the reduction phase with r = 0, direct =
+    one-root fold then hand-out."""
+    P = np.asarray(x).shape[0]
+    alg = Symbolic(P) if symbolic else Algebra(dtype, op)
+    xacc, squeeze = _half_input(x, alg, symbolic, P)
+    m = xacc.shape[2]
+    n = m if n is None else n
+    idx = np.arange(n, dtype=np.int64) if idx is None else np.asarray(idx, dtype=np.int64)
+    c = -(-n // P) if n else 1
+    owner = idx // c
+    if P == 1 or n == 0:
+        res, stats = xacc[0].copy(), dict(steps=0)
+    elif algo in ("generalized", "generalized_xor"):
+        res, stats = _generalized(alg, xacc, n, idx, 0, "cyclic" if algo == "generalized" else "xor", "reduce")
+    else:
+        net = Net(alg, xacc.copy(), n, idx)
+        if algo == "ring":
+            _ring_rs(net)
+        elif algo == "rh_rd":
+            if P & (P - 1):
+                raise ValueError("the halving reduce-scatter needs P to be a power of two")
+            _halving(net, P)
+        elif algo == "direct":
+            _direct_rs(net)
+        else:
+            raise ValueError(f"no reduce-scatter for {algo!r}")
+        res = net.buf[owner, :, np.arange(m)].T if m else net.buf[0, :, :0]
+        stats = net.stats()
+    if symbolic:
+        stats["algebra"] = alg
+    else:
+        res = alg.store(alg.finish(res, P))
+    if squeeze:
+        res = res[0]
+    return (res, stats) if return_stats else res
+
+
+def all_gather(x: np.ndarray, algo: str, dtype: str, n: int | None = None, idx=None, return_stats: bool = False):
+    """Replay an all-gather: rank q contributes part q of its buffer (the rest
+    of its input is ignored); every rank ends with every part. Returns the
+    per-rank buffers in x's shape. Pure copies: the bits are the owners'."""
+    P = np.asarray(x).shape[0]
+    alg = Algebra(dtype, "sum")
+    xacc, squeeze = _half_input(x, alg, False, P)
+    m = xacc.shape[2]
+    n = m if n is None else n
+    idx = np.arange(n, dtype=np.int64) if idx is None else np.asarray(idx, dtype=np.int64)
+    if P == 1 or n == 0:
+        out, stats = xacc.copy(), dict(steps=0)
+    elif algo in ("generalized", "generalized_xor"):
+        out, stats = _generalized(alg, xacc, n, idx, 0, "cyclic" if algo == "generalized" else "xor", "gather")
+    else:
+        net = Net(alg, xacc.copy(), n, idx)
+        if algo == "ring":
+            _ring_ag(net)
+        elif algo == "rh_rd":
+            if P & (P - 1):
+                raise ValueError("the doubling all-gather needs P to be a power of two")
+            _doubling(net, P)
+        elif algo == "direct":
+            _direct_ag(net)
+        else:
+            raise ValueError(f"no all-gather for {algo!r}")
+        out, stats = net.buf, net.stats()
+    res = np.stack([alg.store(out[p]) for p in range(P)])
     if squeeze:
         res = res[:, 0, :]
     return (res, stats) if return_stats else res

@@ -24,7 +24,7 @@ def _narrow(f):
 
 
 def _combine(a, b, dtype, op):
-    if op == "sum":
+    if op in ("sum", "avg"):
         return a + b
     if dtype == "int32":
         return np.where(b.view(np.int32) > a.view(np.int32), b, a)
@@ -50,7 +50,10 @@ def _from_acc(a, dtype):
 
 
 def run_table(x, ops, dtype, op, n, batch=1, nslots=None):
-    """x: (P, batch * n) caller buffers. Returns the final caller buffers."""
+    """x: (P, batch * n) caller buffers. Returns the final caller buffers.
+
+    op "avg": a combination whose result covers all P ranks (counted per
+    element alongside the values) is divided by P before it is stored."""
     P = x.shape[0]
     if nslots is None:
         nslots = 1 + max([0] + [max(o.src_slot, o.dst_slot, o.own_slot) for o in ops])
@@ -58,6 +61,8 @@ def run_table(x, ops, dtype, op, n, batch=1, nslots=None):
     user = [np.array(x[p]) for p in range(P)]
     acc_t = np.uint32 if dtype == "int32" else np.float32
     ws = [[np.zeros(batch * n, dtype=acc_t) for _ in range(nslots)] for _ in range(P)]
+    cnt = [[np.ones(batch * n, dtype=np.int64) if s == 0 else np.zeros(batch * n, dtype=np.int64)
+            for s in range(nslots)] for _ in range(P)]
 
     def rd(rank, slot, sl):
         if slot == 0:
@@ -84,10 +89,18 @@ def run_table(x, ops, dtype, op, n, batch=1, nslots=None):
         for o in ops[i:j]:
             for sl in spans(o):
                 s = rd(o.src_rank, o.src_slot, sl)
-                v = _combine(rd(o.dst_rank, o.own_slot, sl), s, dtype, op) if o.kind == 0 else s
-                pending.append((o.dst_rank, o.dst_slot, sl, v))
-        for rank, slot, sl, v in pending:
+                c = cnt[o.src_rank][o.src_slot][sl].copy()
+                if o.kind == 0:
+                    v = _combine(rd(o.dst_rank, o.own_slot, sl), s, dtype, op)
+                    c = c + cnt[o.dst_rank][o.own_slot][sl]
+                    if op == "avg":
+                        v = np.where(c == P, v / np.float32(P), v).astype(np.float32)
+                else:
+                    v = s
+                pending.append((o.dst_rank, o.dst_slot, sl, v, c))
+        for rank, slot, sl, v, c in pending:
             wr(rank, slot, sl, v)
+            cnt[rank][slot][sl] = c
         i = j
     return np.stack(user)
 
@@ -116,7 +129,8 @@ def run_fused(x, starts, lens, offs, words, dtype, op, n, batch=1):
                         below = stack.pop()
                         stack.append(_combine(below, top, dtype, op))
                 assert len(stack) == 1
+                res = stack[0] / np.float32(P) if op == "avg" else stack[0]
                 for r in outs:
-                    out[r][sl] = _from_acc(stack[0], dtype)
+                    out[r][sl] = _from_acc(res, dtype)
                 w += 2 + 2 * nl + no
     return out
