@@ -221,3 +221,70 @@ def test_auto_choice_runs_the_oracle_choice(form):
                         assert np.array_equal(bits(got), bits(want)), (P, n, algo, a, r, ex)
     finally:
         A.ar_set_cost_model()
+
+
+# --------------------------------------------------------------------------
+# reduce-scatter / all-gather halves and avg
+# --------------------------------------------------------------------------
+HALVES = ("direct", "ring", "rh_rd", "generalized", "generalized_xor")
+
+
+def half_owner(n, P):
+    c = -(-n // P) if n else 1
+    return np.arange(n) // c
+
+
+@pytest.mark.parametrize("dtype", ["int32", "fp32", "bf16"])
+@pytest.mark.parametrize("algo", HALVES)
+def test_small_halves(algo, dtype):
+    from oracle import schedules as sch
+    for P in (2, 3, 5, 8, 12):
+        if algo in ("rh_rd", "generalized_xor") and P & (P - 1):
+            continue
+        for n in (37, 4099):
+            x = inputs.make(dtype, P, n, seed=P * 11 + n)
+            own = half_owner(n, P)
+            for op in ("sum", "max") + (("avg",) if dtype != "int32" else ()):
+                want = sch.reduce_scatter(x, algo, dtype, op)
+                for ex in ("fused", "literal", "replay"):
+                    got = gpu_allreduce(x, algo, dtype, op, 0, ex, collective="reduce_scatter")
+                    assert np.array_equal(bits(got[own, np.arange(n)]), bits(want)), (P, n, op, ex)
+                    if ex == "fused":  # the rest of every buffer is untouched
+                        keep = np.ones(x.shape, bool)
+                        keep[own, np.arange(n)] = False
+                        assert np.array_equal(bits(got)[keep], bits(x)[keep])
+            want = sch.all_gather(x, algo, dtype)
+            for ex in ("fused", "literal"):
+                got = gpu_allreduce(x, algo, dtype, "sum", 0, ex, collective="all_gather")
+                assert np.array_equal(bits(got), bits(want)), (P, n, ex)
+
+
+@pytest.mark.parametrize("algo", ["direct", "ring", "rh_rd", "rd", "binomial", "generalized", "ahc"])
+def test_small_allreduce_avg(algo):
+    for P in (3, 5, 8):
+        g = [P // 3 + 1, P - (P // 3 + 1)] if algo == "ahc" else None
+        for dtype in ("fp32", "bf16"):
+            for n in (37, 4099):
+                x = inputs.make(dtype, P, n, seed=P + n)
+                for r in knobs(algo, P):
+                    want = oracle.allreduce(x, algo, dtype, "avg", knob=r, groups=g)
+                    for ex in ("fused", "literal", "replay"):
+                        got = gpu_allreduce(x, algo, dtype, "avg", r, ex, g)
+                        assert np.array_equal(bits(got), bits(want)), (P, n, dtype, r, ex)
+
+
+def test_halves_full_size_prime_ranks():
+    # the 7-rank 2^24 fp32 workload through both halves, sampled oracle
+    from oracle import schedules as sch
+    x = inputs.workload("prime_fp32")
+    P, n = x.shape
+    idx = inputs.sample_indices(n, P, count=4096)
+    xs = np.ascontiguousarray(x[:, idx])
+    own = half_owner(n, P)[idx]
+    for algo in ("ring", "generalized", "direct"):
+        want = sch.reduce_scatter(xs, algo, "fp32", "sum", n=n, idx=idx)
+        for ex in ("fused", "literal"):
+            got = gpu_allreduce(x, algo, "fp32", "sum", 0, ex, collective="reduce_scatter")
+            assert np.array_equal(bits(got[own, idx]), bits(want)), (algo, ex)
+        got = gpu_allreduce(x, algo, "fp32", "sum", 0, "fused", collective="all_gather")
+        assert np.array_equal(bits(got[:, idx]), bits(np.broadcast_to(x[own, idx], (P, len(idx))))), algo
