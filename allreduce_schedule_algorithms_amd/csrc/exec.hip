@@ -401,8 +401,8 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
     const Item* items = reinterpret_cast<const Item*>(pl->items[mode].p);
     const int32_t* prog = reinterpret_cast<const int32_t*>(pl->prog.p);
     AR_DISPATCH(spec.dtype, spec.op,
-                (e = launch_fused_t<DT, OPK>(pl->D, pl->s->max_trees > 1 ? kMaxFusedTrees : 1, spec.P, pl->nitems[mode],
-                                             ptrs, items, prog, st, ev)));
+                (e = launch_fused_t<DT, OPK>(pl->D, pl->s->max_trees > 1 ? kMaxFusedTrees : 1, spec.P,
+                                             pl->s->max_leaves, pl->nitems[mode], ptrs, items, prog, st, ev)));
     if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
   }
   (void)V;

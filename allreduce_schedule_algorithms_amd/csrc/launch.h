@@ -5,6 +5,8 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace ar {
@@ -15,8 +17,9 @@ struct Evs {
 };
 
 // Leaf batch for P leaves per tree: the size in [2, 8] that leaves the fewest
-// empty slots in the last batch (larger on ties).
+// empty slots in the last batch (larger on ties); 1 for single-leaf trees.
 inline int leaf_batch(int P) {
+  if (P <= 1) return 1;  // single-leaf trees (all-gather copies): one load, no clamped repeats
   int best = 8, waste = 1 << 30;
   for (int b = 8; b >= 2; --b) {
     int w = (P + b - 1) / b * b - P;
@@ -25,8 +28,9 @@ inline int leaf_batch(int P) {
   return best;
 }
 
+// P: ranks (LDS staging); leaves: the most leaves of one tree (leaf batch).
 template <int DT, int OPK>
-hipError_t launch_fused_t(int D, int TM, int P, int64_t nitems, const RankPtrs& ptrs, const Item* items,
+hipError_t launch_fused_t(int D, int TM, int P, int leaves, int64_t nitems, const RankPtrs& ptrs, const Item* items,
                           const int32_t* prog, hipStream_t st, Evs ev);
 template <int DT, int OPK>
 hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& ws, const LitWork* work,
@@ -39,7 +43,7 @@ hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total,
 // be recorded at the kernel's own start and end.
 
 // Leaf batch for P leaves per tree: the size in [2, 8] that leaves the fewest
-// empty slots in the last batch (larger on ties). Single-tree programs are
+// empty slots in the last batch (larger on ties); 1 for single-leaf trees. Single-tree programs are
 // compiled for the (stack depth, batch) pairs that occur; others use 8.
 
 template <int DT, int OPK, int D, int B>
@@ -49,14 +53,15 @@ void fused1(const dim3& g, const dim3& b, hipStream_t st, Evs ev, const RankPtrs
 }
 
 template <int DT, int OPK>
-hipError_t launch_fused_t(int D, int TM, int P, int64_t nitems, const RankPtrs& ptrs, const Item* items,
+hipError_t launch_fused_t(int D, int TM, int P, int leaves, int64_t nitems, const RankPtrs& ptrs, const Item* items,
                           const int32_t* prog, hipStream_t st, Evs ev) {
   const dim3 g{unsigned(nitems), 1, 1};
   const dim3 b{unsigned(kThreads), 1, 1};
   if (TM == 1) {
-    const int B = leaf_batch(P);
+    const int B = leaf_batch(std::min(P, leaves));
     if (D == 2) {
       switch (B) {
+        case 1: fused1<DT, OPK, 2, 1>(g, b, st, ev, ptrs, items, prog); break;
         case 2: fused1<DT, OPK, 2, 2>(g, b, st, ev, ptrs, items, prog); break;
         case 3: fused1<DT, OPK, 2, 3>(g, b, st, ev, ptrs, items, prog); break;
         case 4: fused1<DT, OPK, 2, 4>(g, b, st, ev, ptrs, items, prog); break;
@@ -140,7 +145,7 @@ hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total,
 
 
 #define AR_INSTANTIATE_LAUNCHES(DT, OPK)                                                                    \
-  template hipError_t launch_fused_t<DT, OPK>(int, int, int, int64_t, const RankPtrs&, const Item*,         \
+  template hipError_t launch_fused_t<DT, OPK>(int, int, int, int, int64_t, const RankPtrs&, const Item*,    \
                                               const int32_t*, hipStream_t, Evs);                            \
   template hipError_t launch_literal_t<DT, OPK>(int64_t, const RankPtrs&, const WsDesc&, const LitWork*,    \
                                                 const LitWork*, hipStream_t, Evs);                          \

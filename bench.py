@@ -38,18 +38,24 @@ WORKLOADS = {
         P=8, n=1 << 20, dtype="fp32", batch=1, groups=None,
         headline=("rh_rd", 0, "fused"),
         others=[("ring", 0, "fused"), ("direct", 0, "fused"), ("rd", 0, "fused"), ("generalized_xor", 0, "fused"),
-                ("rh_rd", 0, "literal"), ("ring", 0, "literal")]),
+                ("rh_rd", 0, "literal"), ("ring", 0, "literal"),
+                ("rh_rd", 0, "fused", "reduce_scatter"), ("rh_rd", 0, "fused", "all_gather")]),
     "prime_fp32": dict(
         desc="7 ranks x 2^24 fp32 N(0,1e-3), seed 0",
         P=7, n=1 << 24, dtype="fp32", batch=1, groups=None,
         headline=("generalized", 0, "fused"),
         others=[("generalized", 1, "fused"), ("generalized", 2, "fused"), ("generalized", 3, "fused"),
-                ("ring", 0, "fused"), ("direct", 0, "fused"), ("ring", 0, "literal"), ("generalized", 0, "literal")]),
+                ("ring", 0, "fused"), ("direct", 0, "fused"), ("ring", 0, "literal"), ("generalized", 0, "literal"),
+                ("generalized", 0, "fused", "allreduce", "avg"),
+                ("generalized", 0, "fused", "reduce_scatter"), ("ring", 0, "fused", "reduce_scatter"),
+                ("direct", 0, "fused", "reduce_scatter"), ("generalized", 0, "literal", "reduce_scatter"),
+                ("generalized", 0, "fused", "all_gather"), ("ring", 0, "fused", "all_gather"),
+                ("direct", 0, "fused", "all_gather"), ("generalized", 0, "literal", "all_gather")]),
     "ahc_bf16": dict(
         desc="192 ranks in groups (64, 128) x 2^20 bf16 N(0,1), fp32 accumulation, seed 0",
         P=192, n=1 << 20, dtype="bf16", batch=1, groups=[64, 128],
         headline=("ahc", 0, "fused"),
-        others=[("direct", 0, "fused"), ("ahc", 0, "literal")]),
+        others=[("direct", 0, "fused"), ("ahc", 0, "literal"), ("ahc", 0, "fused", "allreduce", "avg")]),
     "small_batch": dict(
         desc="24 ranks x 10^4 instances x 106 fp32 U(-1,1), seed 0",
         P=24, n=106, dtype="fp32", batch=10_000, groups=None,
@@ -92,6 +98,15 @@ def host_to_device(x, dtype):
     return t.cuda()
 
 
+def essential_bytes(wl, coll="allreduce"):
+    """Every input read once, every output written once: 2 P n (Allreduce),
+    P n + n (reduce-scatter: one part out per rank), P n (all-gather: each part
+    read at its owner and written to the P - 1 others)."""
+    pn = float(wl["P"]) * wl["n"] * wl["batch"] * ELT[wl["dtype"]]
+    n1 = float(wl["n"]) * wl["batch"] * ELT[wl["dtype"]]
+    return {"allreduce": 2.0 * pn, "reduce_scatter": pn + n1, "all_gather": pn}[coll]
+
+
 class Runner:
     def __init__(self, wl, x):
         import torch
@@ -104,14 +119,15 @@ class Runner:
         self.work = torch.empty_like(self.pristine)
         self.flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
         self.ptrs = [self.work[p].data_ptr() for p in range(wl["P"])]
-        self.essential = 2.0 * wl["P"] * wl["n"] * wl["batch"] * ELT[wl["dtype"]]
+        self.essential = essential_bytes(wl)
 
-    def call_for(self, algo, knob, ex, start_event=None, stop_event=None):
+    def call_for(self, algo, knob, ex, start_event=None, stop_event=None, coll="allreduce", op="sum"):
         wl = self.wl
-        return self.A.make_call(wl["P"], wl["n"], wl["dtype"], "sum", algo, knob, ex, wl["batch"], wl["groups"],
-                                start_event=start_event, stop_event=stop_event)
+        return self.A.make_call(wl["P"], wl["n"], wl["dtype"], op, algo, knob, ex, wl["batch"],
+                                wl["groups"] if algo == "ahc" else None,
+                                start_event=start_event, stop_event=stop_event, collective=coll)
 
-    def time(self, algo, knob, ex, steps, warmup, cold=True, kernel_pass=True):
+    def time(self, algo, knob, ex, steps, warmup, cold=True, kernel_pass=True, coll="allreduce", op="sum"):
         """Per step: (untimed) restore + flush, then the timed call.
 
         Pass 1 brackets each plain call with two events on the library's stream
@@ -128,7 +144,8 @@ class Runner:
             e.record(st)  # creates the underlying hipEvent_t
             return e
 
-        plain = self.call_for(algo, knob, ex)
+        plain = self.call_for(algo, knob, ex, coll=coll, op=op)
+        essential = essential_bytes(self.wl, coll)
 
         def prep():
             with torch.cuda.stream(st):
@@ -152,17 +169,17 @@ class Runner:
         ms = [a.elapsed_time(b) for a, b in call_evs]
         mean = statistics.fmean(ms)
         out = dict(ms=mean, ms_median=statistics.median(ms), ms_min=min(ms), wall_ms_per_step=1e3 * wall / steps,
-                   GBps=self.essential / (mean * 1e-3) / 1e9)
+                   GBps=essential / (mean * 1e-3) / 1e9)
         if kernel_pass:
             kern_evs = [(ev(), ev()) for _ in range(steps)]
-            calls = [self.call_for(algo, knob, ex, a, b) for a, b in kern_evs]
+            calls = [self.call_for(algo, knob, ex, a, b, coll, op) for a, b in kern_evs]
             torch.cuda.synchronize()
             for k in range(steps):
                 prep()
                 self.A.ar_allreduce_ex(self.ptrs, calls[k], st)
             torch.cuda.synchronize()
             kmean = statistics.fmean([a.elapsed_time(b) for a, b in kern_evs])
-            out.update(kernel_ms=kmean, kernel_GBps=self.essential / (kmean * 1e-3) / 1e9)
+            out.update(kernel_ms=kmean, kernel_GBps=essential / (kmean * 1e-3) / 1e9)
         return out
 
     def copy_ceiling(self, gib=2):
@@ -417,13 +434,19 @@ def main():
     head = r.time(algo, knob, ex, args.steps, args.warmup)
     schedules = {f"{algo}/r{knob}/{ex}": head}
     if not args.headline_only:
-        for a2, k2, e2 in wl["others"]:
-            schedules[f"{a2}/r{k2}/{e2}"] = r.time(a2, k2, e2, max(10, args.steps // 2), 2)
+        for entry in wl["others"]:
+            a2, k2, e2 = entry[:3]
+            coll = entry[3] if len(entry) > 3 else "allreduce"
+            op = entry[4] if len(entry) > 4 else "sum"
+            key = f"{a2}/r{k2}/{e2}" + ("" if coll == "allreduce" else f"/{coll}") + ("" if op == "sum" else f"/{op}")
+            schedules[key] = r.time(a2, k2, e2, max(10, args.steps // 2), 2, coll=coll, op=op)
     if args.warm:
         for key in list(schedules):
-            a2, k2, e2 = key.split("/")
+            a2, k2, e2, *rest = key.split("/")
+            coll = rest[0] if rest and rest[0] in ("reduce_scatter", "all_gather") else "allreduce"
+            op = rest[-1] if rest and rest[-1] in ("max", "avg") else "sum"
             schedules[key]["warm_GBps"] = r.time(a2, int(k2[1:]), e2, max(10, args.steps // 2), 2, cold=False,
-                                                 kernel_pass=False)["GBps"]
+                                                 kernel_pass=False, coll=coll, op=op)["GBps"]
     for v in schedules.values():
         v["pct_hbm_peak"] = round(100.0 * v["GBps"] / HBM_PEAK_GBPS, 2)
         for k in ("ms", "ms_median", "ms_min", "kernel_ms", "wall_ms_per_step", "GBps", "kernel_GBps"):
