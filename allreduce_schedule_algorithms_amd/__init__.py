@@ -18,12 +18,13 @@ _TORCH_DTYPE = {"int32": "int32", "fp32": "float32", "bf16": "bfloat16"}
 
 
 def allreduce(tensors, algo="ring", op="sum", knob=0, exec="fused", batch=1, groups=None,
-              stream=None, workspace=None, collective="allreduce"):
+              stream=None, workspace=None, collective="allreduce", steps=0):
     """In-place Allreduce over a list of P equally sized CUDA tensors (one per rank).
 
     dtype comes from the tensors (int32, float32 or bfloat16); each tensor holds
     ``batch`` contiguous instances. ``stream`` defaults to torch's current stream.
-    ``collective`` selects the reduce-scatter or all-gather half instead.
+    ``collective`` selects the reduce-scatter or all-gather half instead; ``steps``
+    sets the generalized algorithm's reduction steps (0: ceil(log2 P)).
     """
     import torch
 
@@ -44,7 +45,7 @@ def allreduce(tensors, algo="ring", op="sum", knob=0, exec="fused", batch=1, gro
     call = make_call(P, total // batch, rev[dname], op, algo, knob, exec, batch, groups,
                      workspace=workspace, workspace_bytes=(workspace.numel() * workspace.element_size()
                                                            if workspace is not None else 0),
-                     collective=collective)
+                     collective=collective, steps=steps)
     ar_allreduce_ex(tensors, call, stream)
 
 

@@ -89,7 +89,7 @@ class ar_call(C.Structure):
                 ("ngroups", C.c_int32), ("groups", C.POINTER(C.c_int32)),
                 ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
                 ("start_event", C.c_void_p), ("stop_event", C.c_void_p), ("collective", C.c_int32),
-                ("reserved", C.c_int32)]
+                ("steps", C.c_int32)]
 
 
 class ar_oprec(C.Structure):
@@ -210,9 +210,11 @@ def _event(ev):
 
 
 def make_call(P, n, dtype, op="sum", algo="ring", knob=0, exec="fused", batch=1, groups=None,
-              workspace=None, workspace_bytes=0, start_event=None, stop_event=None, collective="allreduce"):
+              workspace=None, workspace_bytes=0, start_event=None, stop_event=None, collective="allreduce",
+              steps=0):
     call = ar_call()
     call.collective = _enum(COLLECTIVES, collective)
+    call.steps = int(steps)
     call.P, call.n, call.batch = int(P), int(n), int(batch)
     call.dtype, call.op = _enum(DTYPES, dtype), _enum(OPS, op)
     call.algo, call.knob, call.exec = _enum(ALGOS, algo), int(knob), _enum(EXECS, exec)

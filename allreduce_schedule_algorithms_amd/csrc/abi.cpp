@@ -36,7 +36,7 @@ std::map<std::string, std::pair<ar::Spec, double>> g_choices;
 std::string choice_key(const ar::Spec& s) {
   std::string k = std::to_string(s.P) + "/" + std::to_string(s.n) + "/" + std::to_string(s.batch) + "/" +
                   std::to_string(s.dtype) + "/" + std::to_string(s.op) + "/" + std::to_string(s.algo) + "/" +
-                  std::to_string(s.knob) + "/" + std::to_string(s.coll) + "/";
+                  std::to_string(s.knob) + "/" + std::to_string(s.coll) + "/" + std::to_string(s.steps) + "/";
   for (int g : s.groups) k += std::to_string(g) + ",";
   return k;
 }
@@ -67,6 +67,7 @@ bool to_spec(const ar_call* c, ar::Spec* s, std::string* err) {
   s->op = c->op;
   s->algo = c->algo;
   s->knob = (c->algo == AR_GENERALIZED || c->algo == AR_GENERALIZED_XOR) ? c->knob : 0;
+  s->steps = c->steps;
   s->groups.clear();
   if (c->algo == AR_AHC) {
     if (c->ngroups < 1 || !c->groups) { *err = "AHC needs ngroups >= 1 and a groups array"; return false; }

@@ -46,7 +46,7 @@ std::mutex g_mu;
 std::string spec_key(const Spec& s) {
   std::ostringstream k;
   k << s.P << ',' << s.n << ',' << s.batch << ',' << s.dtype << ',' << s.op << ',' << s.algo << ',' << s.knob << ','
-    << s.coll << ':';
+    << s.coll << ',' << s.steps << ':';
   for (int g : s.groups) k << g << '.';
   return k.str();
 }

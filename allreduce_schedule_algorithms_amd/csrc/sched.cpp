@@ -369,11 +369,37 @@ static void gen_ahc(int P, const std::vector<int>& groups, Exprs& ex, Logical& l
 // t_j(i) = i + j mod P (cyclic group) or i XOR j (self-inverse group). The
 // shifted schedules S_j, j < N_{L-r}, run together; an identical vector (same
 // placement, same tree) is sent and combined once.
-static void gen_generalized(int P, int r, bool use_xor, Exprs& ex, Logical& lg, int coll = C_ALLREDUCE) {
-  int L = ceil_log2(P);
-  std::vector<int> N(1, P), h;
-  for (int i = 0; i < L; ++i) N.push_back((N.back() + 1) / 2);
-  for (int i = 0; i < L; ++i) h.push_back(N[i] / 2);
+//
+// steps S > ceil(log2 P) (the paper's conclusion: more steps, smaller pieces,
+// up to the ring's 2(P - 1); not defined there): the same base step with a
+// smaller h_i, the even share of the parts still to move, ceil((N_i - 1) /
+// (S - i)), raised where needed so that N_{i+1} can still halve down to one
+// vector in the remaining steps (N_i - 2^(S-i-1)). S = P - 1 moves one part
+// per step. Cyclic group only.
+static void levels(int P, int S, std::vector<int>& N, std::vector<int>& h) {
+  const int L = ceil_log2(P);
+  N.assign(1, P);
+  h.clear();
+  for (int i = 0; i < S; ++i) {
+    int hi;
+    if (S == L) {
+      hi = N[i] / 2;
+    } else {
+      const int left = S - i;
+      const int share = (N[i] - 1 + left - 1) / left;
+      const int64_t reach = left - 1 >= 30 ? 0 : int64_t(N[i]) - (int64_t(1) << (left - 1));
+      hi = int(std::max<int64_t>(share, reach));
+    }
+    h.push_back(hi);
+    N.push_back(N[i] - hi);
+  }
+}
+
+static void gen_generalized(int P, int r, bool use_xor, Exprs& ex, Logical& lg, int coll = C_ALLREDUCE,
+                            int steps = 0) {
+  const int L = steps > 0 ? steps : ceil_log2(P);  // reduction steps
+  std::vector<int> N, h;
+  levels(P, L, N, h);
   auto place = [&](int k, int j) { return use_xor ? (k ^ j) : (k + j) % P; };
   auto holder = [&](int i, int pl) { return use_xor ? (i ^ pl) : (i + pl) % P; };
   lg.C = P;
@@ -383,10 +409,13 @@ static void gen_generalized(int P, int r, bool use_xor, Exprs& ex, Logical& lg, 
   for (int j = 0; j < J; ++j)
     for (int k = 0; k < P; ++k)
       for (int a = 0; a < P; ++a) vals[j][k][a] = holder(a, place(k, j));
+  // (dst, atom, result) combined so far: an identical vector is combined once,
+  // in this step or an earlier one (more steps can bring a shifted schedule
+  // to a tree another one built before)
+  std::unordered_set<uint64_t> seen;
   for (int i = 0; i < (coll == C_ALL_GATHER ? 0 : L); ++i) {
     lg.steps.emplace_back();
     auto& st = lg.steps.back();
-    std::unordered_set<uint64_t> seen;  // (dst, atom, result) already combined this step
     auto nv = vals;
     for (int j = 0; j < J; ++j)
       for (int k = N[i] - h[i]; k < N[i]; ++k) {
@@ -435,8 +464,14 @@ bool validate_spec(const Spec& s, std::string* err) {
   if (s.coll < C_ALLREDUCE || s.coll > C_ALL_GATHER) return fail("unknown collective");
   if (s.algo < 0 || s.algo >= A_NUM_ALGOS) return fail("unknown algorithm");
   int L = ceil_log2(s.P);
+  if (s.steps != 0) {
+    if (s.algo != A_GENERALIZED) return fail("steps applies to the generalized algorithm over the cyclic group");
+    if (s.steps < L || s.steps > std::max(L, s.P - 1))
+      return fail("steps must be in [ceil(log2 P), P - 1] (0: ceil(log2 P))");
+    L = s.steps;
+  }
   if (s.algo == A_GENERALIZED || s.algo == A_GENERALIZED_XOR) {
-    if (s.knob < 0 || s.knob > L) return fail("knob r must be in [0, ceil(log2 P)]");
+    if (s.knob < 0 || s.knob > L) return fail("knob r must be in [0, reduction steps]");
     if (s.algo == A_GENERALIZED_XOR && (s.P & (s.P - 1))) return fail("the XOR group needs P to be a power of two");
   }
   if (s.coll != C_ALLREDUCE) {
@@ -884,7 +919,7 @@ static bool generate(const Spec& spec, Exprs& ex, Logical& lg, std::string* err)
       case A_DIRECT: rs ? gen_direct_rs(P, ex, lg) : gen_direct_ag(P, ex, lg); break;
       case A_RING: rs ? gen_ring_rs(P, ex, lg) : gen_ring_ag(P, ex, lg); break;
       case A_RH_RD: rs ? gen_halving_rs(P, ex, lg) : gen_doubling_ag(P, ex, lg); break;
-      case A_GENERALIZED: gen_generalized(P, 0, false, ex, lg, spec.coll); break;
+      case A_GENERALIZED: gen_generalized(P, 0, false, ex, lg, spec.coll, spec.steps); break;
       case A_GENERALIZED_XOR: gen_generalized(P, 0, true, ex, lg, spec.coll); break;
       default: if (err) *err = "no reduce-scatter / all-gather half for this algorithm"; return false;
     }
@@ -896,7 +931,7 @@ static bool generate(const Spec& spec, Exprs& ex, Logical& lg, std::string* err)
     case A_RH_RD: gen_rh_rd(P, ex, lg); break;
     case A_RD: gen_rd(P, ex, lg); break;
     case A_BINOMIAL: gen_binomial(P, ex, lg); break;
-    case A_GENERALIZED: gen_generalized(P, spec.knob, false, ex, lg); break;
+    case A_GENERALIZED: gen_generalized(P, spec.knob, false, ex, lg, C_ALLREDUCE, spec.steps); break;
     case A_GENERALIZED_XOR: gen_generalized(P, spec.knob, true, ex, lg); break;
     case A_AHC: gen_ahc(P, spec.groups, ex, lg); break;
     default: if (err) *err = "unknown algorithm"; return false;
@@ -1041,6 +1076,10 @@ static double closed_form(const Schedule& s, double m, double alpha, double beta
     case A_GENERALIZED:
     case A_GENERALIZED_XOR: {
       int r = s.spec.knob;
+      if (s.spec.steps > L) {  // more steps: every part still moves once each way (r = 0 only)
+        if (r != 0) return std::numeric_limits<double>::quiet_NaN();
+        return 2 * s.spec.steps * alpha + 2 * (P - 1) * u * beta + (P - 1) * u * gamma;
+      }
       if (r >= L)  // latency-optimal: all vectors each step; worst-case combinations (2L-2) m
         return L * alpha + L * m * beta + (2 * L - 2) * m * gamma;
       double extra = double((1 << r) - 1);
@@ -1226,7 +1265,8 @@ bool select_spec(const Spec& in, const CostModel& m, Spec* out, double* seconds,
       for (int r = 0; r <= L; ++r) cand.push_back({A_GENERALIZED_XOR, r});
     if (!in.groups.empty()) cand.push_back({A_AHC, 0});
   } else {
-    for (int r = 0; r <= (in.coll == C_ALLREDUCE ? L : 0); ++r) cand.push_back({in.algo, r});
+    const int S = in.steps > 0 ? in.steps : L;
+    for (int r = 0; r <= (in.coll == C_ALLREDUCE ? S : 0); ++r) cand.push_back({in.algo, r});
   }
   bool have = false;
   double best_t = 0;

@@ -46,6 +46,7 @@ struct Spec {
   int knob = 0;
   std::vector<int> groups;  // AHC group sizes (contiguous ranks)
   int coll = C_ALLREDUCE;
+  int steps = 0;  // generalized (cyclic): reduction steps, 0 = ceil(log2 P)
 };
 
 // Hash-consed commutative expression DAG over rank leaves 0..P-1.

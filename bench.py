@@ -50,7 +50,11 @@ WORKLOADS = {
                 ("generalized", 0, "fused", "reduce_scatter"), ("ring", 0, "fused", "reduce_scatter"),
                 ("direct", 0, "fused", "reduce_scatter"), ("generalized", 0, "literal", "reduce_scatter"),
                 ("generalized", 0, "fused", "all_gather"), ("ring", 0, "fused", "all_gather"),
-                ("direct", 0, "fused", "all_gather"), ("generalized", 0, "literal", "all_gather")]),
+                ("direct", 0, "fused", "all_gather"), ("generalized", 0, "literal", "all_gather"),
+                ("generalized", 0, "fused", "allreduce", "sum", 4), ("generalized", 0, "fused", "allreduce", "sum", 6),
+                ("generalized", 0, "literal", "allreduce", "sum", 4),
+                ("generalized", 0, "literal", "allreduce", "sum", 5),
+                ("generalized", 0, "literal", "allreduce", "sum", 6)]),
     "ahc_bf16": dict(
         desc="192 ranks in groups (64, 128) x 2^20 bf16 N(0,1), fp32 accumulation, seed 0",
         P=192, n=1 << 20, dtype="bf16", batch=1, groups=[64, 128],
@@ -121,13 +125,14 @@ class Runner:
         self.ptrs = [self.work[p].data_ptr() for p in range(wl["P"])]
         self.essential = essential_bytes(wl)
 
-    def call_for(self, algo, knob, ex, start_event=None, stop_event=None, coll="allreduce", op="sum"):
+    def call_for(self, algo, knob, ex, start_event=None, stop_event=None, coll="allreduce", op="sum", rsteps=0):
         wl = self.wl
         return self.A.make_call(wl["P"], wl["n"], wl["dtype"], op, algo, knob, ex, wl["batch"],
                                 wl["groups"] if algo == "ahc" else None,
-                                start_event=start_event, stop_event=stop_event, collective=coll)
+                                start_event=start_event, stop_event=stop_event, collective=coll, steps=rsteps)
 
-    def time(self, algo, knob, ex, steps, warmup, cold=True, kernel_pass=True, coll="allreduce", op="sum"):
+    def time(self, algo, knob, ex, steps, warmup, cold=True, kernel_pass=True, coll="allreduce", op="sum",
+             rsteps=0):
         """Per step: (untimed) restore + flush, then the timed call.
 
         Pass 1 brackets each plain call with two events on the library's stream
@@ -144,7 +149,7 @@ class Runner:
             e.record(st)  # creates the underlying hipEvent_t
             return e
 
-        plain = self.call_for(algo, knob, ex, coll=coll, op=op)
+        plain = self.call_for(algo, knob, ex, coll=coll, op=op, rsteps=rsteps)
         essential = essential_bytes(self.wl, coll)
 
         def prep():
@@ -172,7 +177,7 @@ class Runner:
                    GBps=essential / (mean * 1e-3) / 1e9)
         if kernel_pass:
             kern_evs = [(ev(), ev()) for _ in range(steps)]
-            calls = [self.call_for(algo, knob, ex, a, b, coll, op) for a, b in kern_evs]
+            calls = [self.call_for(algo, knob, ex, a, b, coll, op, rsteps) for a, b in kern_evs]
             torch.cuda.synchronize()
             for k in range(steps):
                 prep()
@@ -438,15 +443,18 @@ def main():
             a2, k2, e2 = entry[:3]
             coll = entry[3] if len(entry) > 3 else "allreduce"
             op = entry[4] if len(entry) > 4 else "sum"
+            rsteps = entry[5] if len(entry) > 5 else 0
             key = f"{a2}/r{k2}/{e2}" + ("" if coll == "allreduce" else f"/{coll}") + ("" if op == "sum" else f"/{op}")
-            schedules[key] = r.time(a2, k2, e2, max(10, args.steps // 2), 2, coll=coll, op=op)
+            key += f"/S{rsteps}" if rsteps else ""
+            schedules[key] = r.time(a2, k2, e2, max(10, args.steps // 2), 2, coll=coll, op=op, rsteps=rsteps)
     if args.warm:
         for key in list(schedules):
             a2, k2, e2, *rest = key.split("/")
-            coll = rest[0] if rest and rest[0] in ("reduce_scatter", "all_gather") else "allreduce"
-            op = rest[-1] if rest and rest[-1] in ("max", "avg") else "sum"
+            coll = next((t for t in rest if t in ("reduce_scatter", "all_gather")), "allreduce")
+            op = next((t for t in rest if t in ("max", "avg")), "sum")
+            rsteps = next((int(t[1:]) for t in rest if t.startswith("S")), 0)
             schedules[key]["warm_GBps"] = r.time(a2, int(k2[1:]), e2, max(10, args.steps // 2), 2, cold=False,
-                                                 kernel_pass=False, coll=coll, op=op)["GBps"]
+                                                 kernel_pass=False, coll=coll, op=op, rsteps=rsteps)["GBps"]
     for v in schedules.values():
         v["pct_hbm_peak"] = round(100.0 * v["GBps"] / HBM_PEAK_GBPS, 2)
         for k in ("ms", "ms_median", "ms_min", "kernel_ms", "wall_ms_per_step", "GBps", "kernel_GBps"):

@@ -90,6 +90,10 @@ typedef enum { AR_ALLREDUCE = 0, AR_REDUCE_SCATTER = 1, AR_ALL_GATHER = 2 } ar_c
  *  AR_GENERALIZED     group-theoretic generalized Allreduce over the cyclic group Z_P, any P,
  *                     2 ceil(log2 P) - knob steps (generalized-Allreduce paper, eqs. (17)-(44),
  *                     Figs. 5-6).
+ *                     With ar_call.steps = S > ceil(log2 P) (the paper's conclusion names such a
+ *                     version, up to 2(P-1) steps, without defining it): the same base step
+ *                     moving fewer vectors, h_i = max(ceil((N_i - 1) / (S - i)),
+ *                     N_i - 2^(S-i-1)), N_{i+1} = N_i - h_i.
  *  AR_GENERALIZED_XOR the same over the self-inverse group of Table 1.b (P a power of two).
  *  AR_AHC             asymmetric hierarchical Allreduce over contiguous groups (HCCL "AHC"
  *                     page, Description), 2(max g - 1) + 2(G - 1) steps. */
@@ -143,7 +147,11 @@ typedef struct ar_call {
                               With both set, hipEventElapsedTime gives the device time of the
                               call's kernels without the launch latency in front of them */
   int32_t collective;      /* ar_collective; 0 (AR_ALLREDUCE) for a zeroed call */
-  int32_t reserved;        /* 0 */
+  int32_t steps;           /* AR_GENERALIZED: reduction steps S, ceil(log2 P) <= S <= P - 1, or 0
+                              for ceil(log2 P). More steps move smaller pieces (S = P - 1: one part
+                              per step, a ring-shaped chain); the call takes 2S - knob steps and
+                              knob ranges over 0..S. Must be 0 for other algorithms. See the
+                              schedule notes above. */
 } ar_call;
 
 /* Plain Allreduce: fused execution, batch 1, no groups (AR_AHC needs ar_allreduce_ex).

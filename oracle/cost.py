@@ -98,7 +98,8 @@ def pipelined_chain_best_m(n: float, p: int, t_start: float, t_byte: float) -> f
 # --------------------------------------------------------------------------
 # model-driven choice of schedule
 # --------------------------------------------------------------------------
-def step_counts(P: int, n: int, algo: str, knob: int = 0, groups=None, coll: str = "allreduce"):
+def step_counts(P: int, n: int, algo: str, knob: int = 0, groups=None, coll: str = "allreduce",
+                steps: int | None = None):
     """Per-step, per-rank elements sent, received and combined by one instance.
 
     Counts come from the oracle's own replay of the schedule on a one-offset
@@ -111,12 +112,12 @@ def step_counts(P: int, n: int, algo: str, knob: int = 0, groups=None, coll: str
         return z, z, z
     x = np.zeros((P, 1), dtype=np.int32)
     if coll == "reduce_scatter":
-        _, st = schedules.reduce_scatter(x, algo, "int32", "sum", n=n, idx=[0], return_stats=True)
+        _, st = schedules.reduce_scatter(x, algo, "int32", "sum", n=n, idx=[0], return_stats=True, steps=steps)
     elif coll == "all_gather":
-        _, st = schedules.all_gather(x, algo, "int32", n=n, idx=[0], return_stats=True)
+        _, st = schedules.all_gather(x, algo, "int32", n=n, idx=[0], return_stats=True, steps=steps)
     else:
         _, st = schedules.allreduce(x, algo, "int32", "sum", knob=knob, groups=groups, n=n, idx=[0],
-                                    return_stats=True)
+                                    return_stats=True, steps=steps)
     return (np.asarray(st["sent"], dtype=np.int64).reshape(-1, P),
             np.asarray(st["recv"], dtype=np.int64).reshape(-1, P),
             np.asarray(st["reduced"], dtype=np.int64).reshape(-1, P))
@@ -143,9 +144,9 @@ def model_seconds(counts, elt: int, batch: int, alpha: float, beta: float, gamma
     return alpha * S + beta * (float(xb) * elt * batch) + gamma * (float(xg) * elt * batch)
 
 
-def candidates(P: int, algo: str = "auto", groups=None, coll: str = "allreduce"):
-    """(algo, knob) pairs in tie-breaking order."""
-    L = ceil_log2(P)
+def candidates(P: int, algo: str = "auto", groups=None, coll: str = "allreduce", steps: int | None = None):
+    """(algo, knob) pairs in tie-breaking order (knob up to the reduction steps)."""
+    L = ceil_log2(P) if not steps else steps
     pow2 = P & (P - 1) == 0
     if coll != "allreduce":
         if algo != "auto":
@@ -164,11 +165,13 @@ def candidates(P: int, algo: str = "auto", groups=None, coll: str = "allreduce")
 
 
 def select(P: int, n: int, dtype: str, alpha: float, beta: float, gamma: float, form: str = "busiest",
-           algo: str = "auto", batch: int = 1, groups=None, coll: str = "allreduce"):
-    """(algo, knob, seconds) of least model time; ties: fewer steps, then earlier candidate."""
+           algo: str = "auto", batch: int = 1, groups=None, coll: str = "allreduce", steps: int | None = None):
+    """(algo, knob, seconds) of least model time; ties: fewer steps, then earlier candidate.
+    ``steps`` (the generalized algorithm's reduction steps) applies to an explicit algorithm only."""
     best = None
-    for a, r in candidates(P, algo, groups, coll):
-        c = step_counts(P, n, a, r, groups if a == "ahc" else None, coll)
+    steps = steps if algo != "auto" else None
+    for a, r in candidates(P, algo, groups, coll, steps):
+        c = step_counts(P, n, a, r, groups if a == "ahc" else None, coll, steps)
         t = model_seconds(c, ELT_BYTES[dtype], batch, alpha, beta, gamma, form)
         key = (t, c[0].shape[0])
         if best is None or key < best[0]:

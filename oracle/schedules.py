@@ -304,17 +304,42 @@ def ahc_chunks(groups) -> int:
 # --------------------------------------------------------------------------
 # generalized Allreduce over a transitive abelian group of order P
 # --------------------------------------------------------------------------
-def _levels(P: int):
-    """N_0 = P, N_{i+1} = ceil(N_i / 2) (N_L = 1); h_i = floor(N_i / 2)."""
+def _levels(P: int, steps: int | None = None):
+    """Vector counts of the base reduction: step i moves v_k, k in [N_i - h_i, N_i),
+    onto v_{k - h_i}, and N_{i+1} = N_i - h_i. Returns (S, N, h) for S steps.
+
+    S = ceil(log2 P) (default): the paper's halving, N_{i+1} = ceil(N_i / 2),
+    h_i = floor(N_i / 2).
+
+    S > ceil(log2 P): the paper's conclusion names a version with more than
+    2 ceil(log P) steps and smaller pieces per step, up to the ring's 2(P - 1),
+    without defining it. Reading: the same base step with smaller h_i. Any
+    1 <= h_i <= floor(N_i / 2) keeps every target v_{k - h_i} below N_i - h_i
+    and distinct. h_i spreads the P - 1 parts as evenly as the remaining steps
+    allow: h_i = max(ceil((N_i - 1) / (S - i)), N_i - 2^(S - i - 1)). The
+    second term is the least h that still lets the rest halve down to one
+    vector. S = P - 1 gives h_i = 1: a ring-shaped chain.
+    """
     L = ceil_log2(P)
-    N = [P]
-    for _ in range(L):
-        N.append((N[-1] + 1) // 2)
-    h = [N[i] // 2 for i in range(L)]
-    return L, N, h
+    S = L if steps is None else steps
+    if not L <= S <= max(P - 1, L):
+        raise ValueError(f"steps must be in [{L}, {max(P - 1, L)}]")
+    N, h = [P], []
+    for i in range(S):
+        if S == L:
+            hi = N[i] // 2
+        else:
+            left = S - i
+            hi = max(-(-(N[i] - 1) // left), N[i] - (1 << (left - 1)))
+        if not 1 <= hi <= N[i] // 2:
+            raise AssertionError("level sequence out of range")
+        h.append(hi)
+        N.append(N[i] - hi)
+    return S, N, h
 
 
-def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: str, phase: str = "all"):
+def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: str, phase: str = "all",
+                 steps: int | None = None):
     """Generalized Allreduce (generalized-Allreduce paper: bandwidth-optimal
     section eqs. (17)-(25), intermediate steps eqs. (26)-(36) and Fig. 6,
     latency-optimal section eqs. (38)-(44)). The equations are missing from the
@@ -353,7 +378,7 @@ def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: 
     per-step number of distinct parts sent / combined per rank).
     """
     P = xacc.shape[0]
-    L, N, h = _levels(P)
+    L, N, h = _levels(P, steps)  # L: reduction steps
     if not 0 <= r <= L:
         raise ValueError(f"knob r must be in [0, {L}]")
     if group == "cyclic":
@@ -391,19 +416,23 @@ def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: 
     el_sent, el_recv, el_red = [], [], []
     vals = {j: [diag(place(k, j)) for k in range(P)] for j in J}
     syms = {j: [place(k, j) for k in range(P)] for j in J}
+    built = set()  # (placement, tree) combined in an earlier step: not sent or combined again
     for i in range(L if phase != "gather" else 0):
         sends, reds, msgs = set(), set(), set()
         new_vals, new_syms = {}, {}
         for j in J:
             v, s = list(vals[j]), list(syms[j])
             for k in range(N[i] - h[i], N[i]):
-                sends.add((place(k, j), syms[j][k]))
-                msgs.add((place(k, j), syms[j][k], place(k - h[i], j)))
                 s[k - h[i]] = sym.node(syms[j][k - h[i]], syms[j][k])
                 v[k - h[i]] = alg.op(vals[j][k - h[i]], vals[j][k])
+                if (place(k - h[i], j), s[k - h[i]]) in built:
+                    continue
+                sends.add((place(k, j), syms[j][k]))
+                msgs.add((place(k, j), syms[j][k], place(k - h[i], j)))
                 reds.add((place(k - h[i], j), s[k - h[i]]))
             new_vals[j], new_syms[j] = v, s
         vals, syms = new_vals, new_syms
+        built |= reds
         sent_steps.append(len(sends))
         red_steps.append(len(reds))
         es, er, ed = (np.zeros(P, dtype=np.int64) for _ in range(3))
@@ -461,14 +490,15 @@ def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: 
 # --------------------------------------------------------------------------
 def allreduce(x: np.ndarray, algo: str, dtype: str, op: str = "sum", knob: int = 0,
               groups=None, n: int | None = None, idx=None, symbolic: bool = False,
-              return_stats: bool = False):
+              return_stats: bool = False, steps: int | None = None):
     """Replay one Allreduce schedule on the CPU.
 
     x       (P, m) or (P, B, m): each rank's buffer (B independent instances of
             length n), restricted to the element offsets ``idx`` (default: all
             n offsets). int32 / fp32 arrays, bf16 as uint16 bit patterns.
     algo    one of ALGOS; ``knob`` is r for the generalized algorithm;
-            ``groups`` the AHC group sizes (contiguous ranks).
+            ``groups`` the AHC group sizes (contiguous ranks); ``steps`` the
+            generalized algorithm's reduction steps (default ceil(log2 P)).
     symbolic  ignore the values and return, per rank and offset, the id of the
             combination tree (leaves = ranks) in ``stats['algebra']``.
     Returns the per-rank outputs in x's shape (and a stats dict if asked).
@@ -495,7 +525,10 @@ def allreduce(x: np.ndarray, algo: str, dtype: str, op: str = "sum", knob: int =
     if P == 1 or n == 0:
         out, stats = xacc.copy(), dict(steps=0)
     elif algo in ("generalized", "generalized_xor"):
-        out, stats = _generalized(alg, xacc, n, idx, knob, "cyclic" if algo == "generalized" else "xor")
+        if steps is not None and algo == "generalized_xor" and steps != ceil_log2(P):
+            raise ValueError("more steps are defined for the cyclic group only")
+        out, stats = _generalized(alg, xacc, n, idx, knob, "cyclic" if algo == "generalized" else "xor",
+                                  steps=steps)
     else:
         net = Net(alg, xacc.copy(), n, idx)
         if algo == "direct":
@@ -583,7 +616,7 @@ def _half_input(x, alg, symbolic, P):
 
 
 def reduce_scatter(x: np.ndarray, algo: str, dtype: str, op: str = "sum", n: int | None = None, idx=None,
-                   symbolic: bool = False, return_stats: bool = False):
+                   symbolic: bool = False, return_stats: bool = False, steps: int | None = None):
     """Replay a reduce-scatter: rank q ends with the reduced part q of the ceil
     split into P parts. x as for ``allreduce``. Returns the result vector
     (element e as rank e // ceil(n / P) holds it), shape (m,) or (B, m).
@@ -602,7 +635,8 @@ def reduce_scatter(x: np.ndarray, algo: str, dtype: str, op: str = "sum", n: int
     if P == 1 or n == 0:
         res, stats = xacc[0].copy(), dict(steps=0)
     elif algo in ("generalized", "generalized_xor"):
-        res, stats = _generalized(alg, xacc, n, idx, 0, "cyclic" if algo == "generalized" else "xor", "reduce")
+        res, stats = _generalized(alg, xacc, n, idx, 0, "cyclic" if algo == "generalized" else "xor", "reduce",
+                                  steps if algo == "generalized" else None)
     else:
         net = Net(alg, xacc.copy(), n, idx)
         if algo == "ring":
@@ -626,7 +660,8 @@ def reduce_scatter(x: np.ndarray, algo: str, dtype: str, op: str = "sum", n: int
     return (res, stats) if return_stats else res
 
 
-def all_gather(x: np.ndarray, algo: str, dtype: str, n: int | None = None, idx=None, return_stats: bool = False):
+def all_gather(x: np.ndarray, algo: str, dtype: str, n: int | None = None, idx=None, return_stats: bool = False,
+               steps: int | None = None):
     """Replay an all-gather: rank q contributes part q of its buffer (the rest
     of its input is ignored); every rank ends with every part. Returns the
     per-rank buffers in x's shape. Pure copies: the bits are the owners'."""
@@ -639,7 +674,8 @@ def all_gather(x: np.ndarray, algo: str, dtype: str, n: int | None = None, idx=N
     if P == 1 or n == 0:
         out, stats = xacc.copy(), dict(steps=0)
     elif algo in ("generalized", "generalized_xor"):
-        out, stats = _generalized(alg, xacc, n, idx, 0, "cyclic" if algo == "generalized" else "xor", "gather")
+        out, stats = _generalized(alg, xacc, n, idx, 0, "cyclic" if algo == "generalized" else "xor", "gather",
+                                  steps if algo == "generalized" else None)
     else:
         net = Net(alg, xacc.copy(), n, idx)
         if algo == "ring":

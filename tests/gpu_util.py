@@ -51,13 +51,13 @@ def from_device(bufs, dtype: str) -> np.ndarray:
 
 def gpu_allreduce(x: np.ndarray, algo: str, dtype: str, op: str = "sum", knob: int = 0, exec: str = "fused",
                   groups=None, batch: int = 1, misalign: bool = False, stream=None,
-                  collective: str = "allreduce") -> np.ndarray:
+                  collective: str = "allreduce", steps: int = 0) -> np.ndarray:
     """Run one collective on cuda:0 through ar_allreduce_ex and return every rank's buffer."""
     torch = torch_mod()
     P, total = x.shape
     n = total // batch
     bufs, keep = to_device(x, dtype, misalign)
-    call = A.make_call(P, n, dtype, op, algo, knob, exec, batch, groups, collective=collective)
+    call = A.make_call(P, n, dtype, op, algo, knob, exec, batch, groups, collective=collective, steps=steps)
     s = stream if stream is not None else torch.cuda.current_stream()
     A.ar_allreduce_ex([b.data_ptr() for b in bufs], call, s)
     torch.cuda.synchronize()

@@ -288,3 +288,33 @@ def test_halves_full_size_prime_ranks():
             assert np.array_equal(bits(got[own, idx]), bits(want)), (algo, ex)
         got = gpu_allreduce(x, algo, "fp32", "sum", 0, "fused", collective="all_gather")
         assert np.array_equal(bits(got[:, idx]), bits(np.broadcast_to(x[own, idx], (P, len(idx))))), algo
+
+
+# --------------------------------------------------------------------------
+# the generalized algorithm with more than 2 ceil(log2 P) steps
+# --------------------------------------------------------------------------
+def test_generalized_more_steps_small():
+    for P in (5, 7, 12):
+        L = nu.ceil_log2(P)
+        for S in range(L, P):
+            for r in sorted({0, 1, S}):
+                for dtype in ("fp32", "bf16"):
+                    for n in (37, 4099):
+                        x = inputs.make(dtype, P, n, seed=S * 13 + r + n)
+                        want = oracle.allreduce(x, "generalized", dtype, "sum", knob=r, steps=S)
+                        for ex in ("fused", "literal"):
+                            got = gpu_allreduce(x, "generalized", dtype, "sum", r, ex, steps=S)
+                            assert np.array_equal(bits(got), bits(want)), (P, S, r, dtype, n, ex)
+
+
+def test_generalized_more_steps_full_size_prime_ranks():
+    x = inputs.workload("prime_fp32")
+    P, n = x.shape
+    idx = inputs.sample_indices(n, P, count=4096)
+    xs = np.ascontiguousarray(x[:, idx])
+    for S in (4, 5, 6):
+        want = oracle.allreduce(xs, "generalized", "fp32", "sum", n=n, idx=idx, steps=S)
+        for ex in ("fused", "literal"):
+            got = gpu_allreduce(x, "generalized", "fp32", "sum", 0, ex, steps=S)
+            assert np.array_equal(bits(got[:, idx]), bits(want)), (S, ex)
+        check_tol(got, x, "fp32")

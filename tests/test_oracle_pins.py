@@ -452,7 +452,7 @@ def test_bus_bandwidth_and_ring_bytes():
 # planted mistakes: the pins above must catch them
 # --------------------------------------------------------------------------
 def test_planted_floor_levels_is_caught(monkeypatch):
-    def bad_levels(P):
+    def bad_levels(P, steps=None):
         L = nu.ceil_log2(P)
         N = [P]
         for _ in range(L):

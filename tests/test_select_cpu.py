@@ -147,8 +147,8 @@ def test_planted_dropped_alpha_is_caught(monkeypatch):
 def test_planted_swapped_counters_are_caught(monkeypatch):
     orig = cost.step_counts
 
-    def bad(P, n, algo, knob=0, groups=None, coll="allreduce"):
-        s, r, d = orig(P, n, algo, knob, groups, coll)
+    def bad(P, n, algo, knob=0, groups=None, coll="allreduce", steps=None):
+        s, r, d = orig(P, n, algo, knob, groups, coll, steps)
         return d, d, s
     monkeypatch.setattr(cost, "step_counts", bad)
     with pytest.raises(AssertionError):
