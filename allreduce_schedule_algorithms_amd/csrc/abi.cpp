@@ -73,6 +73,10 @@ bool to_spec(const ar_call* c, ar::Spec* s, std::string* err) {
     if (c->ngroups < 1 || !c->groups) { *err = "AHC needs ngroups >= 1 and a groups array"; return false; }
     if (c->ngroups > AR_MAX_RANKS) { *err = "too many AHC groups"; return false; }
     s->groups.assign(c->groups, c->groups + c->ngroups);
+  } else if (c->algo == AR_GENERALIZED && c->ngroups != 0) {
+    if (c->ngroups < 0 || !c->groups) { *err = "ngroups > 0 needs a groups array"; return false; }
+    if (c->ngroups > 8) { *err = "at most 8 group factors"; return false; }
+    s->groups.assign(c->groups, c->groups + c->ngroups);
   } else if (c->algo == AR_AUTO && c->ngroups != 0) {
     if (c->ngroups < 0 || !c->groups) { *err = "ngroups > 0 needs a groups array"; return false; }
     if (c->ngroups > AR_MAX_RANKS) { *err = "too many AHC groups"; return false; }

@@ -395,13 +395,34 @@ static void levels(int P, int S, std::vector<int>& N, std::vector<int>& h) {
   }
 }
 
-static void gen_generalized(int P, int r, bool use_xor, Exprs& ex, Logical& lg, int coll = C_ALLREDUCE,
-                            int steps = 0) {
+// The group T_P = Z_m1 x ... x Z_mt (generalized paper: any suitable group,
+// Table 1): element k is the mixed-radix number with digits k mod m1,
+// (k / m1) mod m2, ...; the operation adds digits modulo their radix. {P} is
+// the cyclic group, {2, 2, ...} the self-inverse group of Table 1.b.
+static std::vector<int> group_table(int P, const std::vector<int>& radices) {
+  std::vector<int> t(size_t(P) * P);
+  for (int a = 0; a < P; ++a)
+    for (int b = 0; b < P; ++b) {
+      int x = a, y = b, out = 0, w = 1;
+      for (int m : radices) {
+        out += ((x % m + y % m) % m) * w;
+        x /= m;
+        y /= m;
+        w *= m;
+      }
+      t[size_t(a) * P + b] = out;
+    }
+  return t;
+}
+
+static void gen_generalized(int P, int r, const std::vector<int>& radices, Exprs& ex, Logical& lg,
+                            int coll = C_ALLREDUCE, int steps = 0) {
   const int L = steps > 0 ? steps : ceil_log2(P);  // reduction steps
   std::vector<int> N, h;
   levels(P, L, N, h);
-  auto place = [&](int k, int j) { return use_xor ? (k ^ j) : (k + j) % P; };
-  auto holder = [&](int i, int pl) { return use_xor ? (i ^ pl) : (i + pl) % P; };
+  const std::vector<int> op = group_table(P, radices);
+  auto place = [&](int k, int j) { return op[size_t(k) * P + j]; };
+  auto holder = [&](int i, int pl) { return op[size_t(i) * P + pl]; };
   lg.C = P;
   int J = N[L - r];
   // vals[j][k][atom]
@@ -481,6 +502,17 @@ bool validate_spec(const Spec& s, std::string* err) {
     if ((s.algo == A_GENERALIZED || s.algo == A_GENERALIZED_XOR) && s.knob != 0)
       return fail("the generalized halves use knob r = 0");
   }
+  if (s.algo == A_GENERALIZED && !s.groups.empty()) {
+    int64_t prod = 1;
+    for (int m : s.groups) {
+      if (m < 2) return fail("group factors must be >= 2");
+      prod *= m;
+      if (prod > kMaxRanks) break;
+    }
+    if (prod != s.P) return fail("the group factors' product must be P");
+  }
+  if (s.algo != A_AHC && s.algo != A_GENERALIZED && !s.groups.empty())
+    return fail("groups apply to AR_AHC (group sizes) and AR_GENERALIZED (group factors) only");
   if (s.algo == A_AHC) {
     if (s.groups.empty()) return fail("AHC needs group sizes");
     int sum = 0;
@@ -906,6 +938,14 @@ static bool plan_fused(Schedule& s, std::string* err) {
 // ----------------------------------------------------------------------------
 // build
 // ----------------------------------------------------------------------------
+// Radices of the generalized algorithm's group: the caller's factors, else
+// Z_P (cyclic) or Z_2^L (self-inverse).
+static std::vector<int> radices_of(const Spec& s) {
+  if (s.algo == A_GENERALIZED_XOR) return std::vector<int>(size_t(ceil_log2(s.P)), 2);
+  if (!s.groups.empty()) return s.groups;
+  return {s.P};
+}
+
 bool half_supported(int algo) {
   return algo == A_DIRECT || algo == A_RING || algo == A_RH_RD || algo == A_GENERALIZED || algo == A_GENERALIZED_XOR;
 }
@@ -919,8 +959,8 @@ static bool generate(const Spec& spec, Exprs& ex, Logical& lg, std::string* err)
       case A_DIRECT: rs ? gen_direct_rs(P, ex, lg) : gen_direct_ag(P, ex, lg); break;
       case A_RING: rs ? gen_ring_rs(P, ex, lg) : gen_ring_ag(P, ex, lg); break;
       case A_RH_RD: rs ? gen_halving_rs(P, ex, lg) : gen_doubling_ag(P, ex, lg); break;
-      case A_GENERALIZED: gen_generalized(P, 0, false, ex, lg, spec.coll, spec.steps); break;
-      case A_GENERALIZED_XOR: gen_generalized(P, 0, true, ex, lg, spec.coll); break;
+      case A_GENERALIZED: gen_generalized(P, 0, radices_of(spec), ex, lg, spec.coll, spec.steps); break;
+      case A_GENERALIZED_XOR: gen_generalized(P, 0, radices_of(spec), ex, lg, spec.coll); break;
       default: if (err) *err = "no reduce-scatter / all-gather half for this algorithm"; return false;
     }
     return true;
@@ -931,8 +971,8 @@ static bool generate(const Spec& spec, Exprs& ex, Logical& lg, std::string* err)
     case A_RH_RD: gen_rh_rd(P, ex, lg); break;
     case A_RD: gen_rd(P, ex, lg); break;
     case A_BINOMIAL: gen_binomial(P, ex, lg); break;
-    case A_GENERALIZED: gen_generalized(P, spec.knob, false, ex, lg, C_ALLREDUCE, spec.steps); break;
-    case A_GENERALIZED_XOR: gen_generalized(P, spec.knob, true, ex, lg); break;
+    case A_GENERALIZED: gen_generalized(P, spec.knob, radices_of(spec), ex, lg, C_ALLREDUCE, spec.steps); break;
+    case A_GENERALIZED_XOR: gen_generalized(P, spec.knob, radices_of(spec), ex, lg); break;
     case A_AHC: gen_ahc(P, spec.groups, ex, lg); break;
     default: if (err) *err = "unknown algorithm"; return false;
   }
@@ -1276,7 +1316,7 @@ bool select_spec(const Spec& in, const CostModel& m, Spec* out, double* seconds,
     Spec c = in;
     c.algo = a;
     c.knob = r;
-    if (a != A_AHC) c.groups.clear();
+    if (in.algo == kAutoAlgo && a != A_AHC) c.groups.clear();  // AR_AUTO's groups are AHC's
     StepCounts sc;
     if (!step_counts(c, &sc, err)) return false;
     double t = model_seconds(sc, c, m);

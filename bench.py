@@ -39,7 +39,10 @@ WORKLOADS = {
         headline=("rh_rd", 0, "fused"),
         others=[("ring", 0, "fused"), ("direct", 0, "fused"), ("rd", 0, "fused"), ("generalized_xor", 0, "fused"),
                 ("rh_rd", 0, "literal"), ("ring", 0, "literal"),
-                ("rh_rd", 0, "fused", "reduce_scatter"), ("rh_rd", 0, "fused", "all_gather")]),
+                ("rh_rd", 0, "fused", "reduce_scatter"), ("rh_rd", 0, "fused", "all_gather"),
+                ("generalized", 0, "fused", "allreduce", "sum", 0, [2, 4]),
+                ("generalized", 0, "fused", "allreduce", "sum", 0, [4, 2]),
+                ("generalized", 0, "literal", "allreduce", "sum", 0, [4, 2])]),
     "prime_fp32": dict(
         desc="7 ranks x 2^24 fp32 N(0,1e-3), seed 0",
         P=7, n=1 << 24, dtype="fp32", batch=1, groups=None,
@@ -125,14 +128,15 @@ class Runner:
         self.ptrs = [self.work[p].data_ptr() for p in range(wl["P"])]
         self.essential = essential_bytes(wl)
 
-    def call_for(self, algo, knob, ex, start_event=None, stop_event=None, coll="allreduce", op="sum", rsteps=0):
+    def call_for(self, algo, knob, ex, start_event=None, stop_event=None, coll="allreduce", op="sum", rsteps=0,
+                 factors=None):
         wl = self.wl
         return self.A.make_call(wl["P"], wl["n"], wl["dtype"], op, algo, knob, ex, wl["batch"],
-                                wl["groups"] if algo == "ahc" else None,
+                                wl["groups"] if algo == "ahc" else factors,
                                 start_event=start_event, stop_event=stop_event, collective=coll, steps=rsteps)
 
     def time(self, algo, knob, ex, steps, warmup, cold=True, kernel_pass=True, coll="allreduce", op="sum",
-             rsteps=0):
+             rsteps=0, factors=None):
         """Per step: (untimed) restore + flush, then the timed call.
 
         Pass 1 brackets each plain call with two events on the library's stream
@@ -149,7 +153,7 @@ class Runner:
             e.record(st)  # creates the underlying hipEvent_t
             return e
 
-        plain = self.call_for(algo, knob, ex, coll=coll, op=op, rsteps=rsteps)
+        plain = self.call_for(algo, knob, ex, coll=coll, op=op, rsteps=rsteps, factors=factors)
         essential = essential_bytes(self.wl, coll)
 
         def prep():
@@ -177,7 +181,7 @@ class Runner:
                    GBps=essential / (mean * 1e-3) / 1e9)
         if kernel_pass:
             kern_evs = [(ev(), ev()) for _ in range(steps)]
-            calls = [self.call_for(algo, knob, ex, a, b, coll, op, rsteps) for a, b in kern_evs]
+            calls = [self.call_for(algo, knob, ex, a, b, coll, op, rsteps, factors) for a, b in kern_evs]
             torch.cuda.synchronize()
             for k in range(steps):
                 prep()
@@ -444,17 +448,22 @@ def main():
             coll = entry[3] if len(entry) > 3 else "allreduce"
             op = entry[4] if len(entry) > 4 else "sum"
             rsteps = entry[5] if len(entry) > 5 else 0
+            factors = entry[6] if len(entry) > 6 else None
             key = f"{a2}/r{k2}/{e2}" + ("" if coll == "allreduce" else f"/{coll}") + ("" if op == "sum" else f"/{op}")
             key += f"/S{rsteps}" if rsteps else ""
-            schedules[key] = r.time(a2, k2, e2, max(10, args.steps // 2), 2, coll=coll, op=op, rsteps=rsteps)
+            key += "/Z" + "x".join(str(m) for m in factors) if factors else ""
+            schedules[key] = r.time(a2, k2, e2, max(10, args.steps // 2), 2, coll=coll, op=op, rsteps=rsteps,
+                                    factors=factors)
     if args.warm:
         for key in list(schedules):
             a2, k2, e2, *rest = key.split("/")
             coll = next((t for t in rest if t in ("reduce_scatter", "all_gather")), "allreduce")
             op = next((t for t in rest if t in ("max", "avg")), "sum")
             rsteps = next((int(t[1:]) for t in rest if t.startswith("S")), 0)
+            factors = next(([int(v) for v in t[1:].split("x")] for t in rest if t.startswith("Z")), None)
             schedules[key]["warm_GBps"] = r.time(a2, int(k2[1:]), e2, max(10, args.steps // 2), 2, cold=False,
-                                                 kernel_pass=False, coll=coll, op=op, rsteps=rsteps)["GBps"]
+                                                 kernel_pass=False, coll=coll, op=op, rsteps=rsteps,
+                                                 factors=factors)["GBps"]
     for v in schedules.values():
         v["pct_hbm_peak"] = round(100.0 * v["GBps"] / HBM_PEAK_GBPS, 2)
         for k in ("ms", "ms_median", "ms_min", "kernel_ms", "wall_ms_per_step", "GBps", "kernel_GBps"):

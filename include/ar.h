@@ -136,8 +136,16 @@ typedef struct ar_call {
   int64_t n;               /* elements per instance (>= 0) */
   int64_t batch;           /* independent instances per buffer (>= 1); 0 is read as 1 */
   int32_t ngroups;         /* AR_AHC: number of groups G (>= 1); with AR_AUTO, optional (0 leaves
-                              AHC out of the candidates) */
-  const int32_t* groups;   /* AR_AHC: G group sizes summing to P, ranks assigned in order */
+                              AHC out of the candidates); AR_GENERALIZED: optional, the number
+                              of factors t (<= 8) of its group */
+  const int32_t* groups;   /* AR_AHC: G group sizes summing to P, ranks assigned in order.
+                              AR_GENERALIZED: factors m_1..m_t (each >= 2, product P) of the
+                              group T_P = Z_m1 x ... x Z_mt, element k being the mixed-radix number
+                              with digits k mod m_1, (k / m_1) mod m_2, ...; none: Z_P. (P) is the
+                              cyclic group, (2, ..., 2) the self-inverse one of AR_GENERALIZED_XOR.
+                              Other factorizations change which ranks talk in a step; a step can
+                              then have a rank talk to several peers (ar_schedule_info.single_port).
+                              Ignored by the other algorithms. */
   void* workspace;         /* AR_EXEC_LITERAL: device scratch of ar_workspace_bytes() bytes, or
                               NULL to let the library allocate and cache one per device */
   size_t workspace_bytes;

@@ -338,7 +338,40 @@ def _levels(P: int, steps: int | None = None):
     return S, N, h
 
 
-def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: str, phase: str = "all",
+def _product_group(factors, P: int):
+    """The abelian group Z_m1 x ... x Z_mt as a group T_P (generalized paper:
+    any suitable group may replace the cyclic one, Table 1 and the
+    bandwidth-optimal section). Element k is the mixed-radix number with digits
+    (k mod m1, (k // m1) mod m2, ...); the operation adds digits modulo their
+    radix. Returns vectorized (add, sub)."""
+    f = tuple(int(m) for m in factors)
+    if not f or any(m < 2 for m in f) or math.prod(f) != P:
+        raise ValueError("group factors must be >= 2 with product P")
+
+    def digits(x):
+        x = np.asarray(x, dtype=np.int64)
+        out = []
+        for m in f:
+            out.append(x % m)
+            x = x // m
+        return out
+
+    def number(ds):
+        x, w = 0, 1
+        for d, m in zip(ds, f):
+            x = x + (d % m) * w
+            w *= m
+        return x
+
+    def add(a, b):
+        return number([u + v for u, v in zip(digits(a), digits(b))])
+
+    def sub(a, b):
+        return number([u - v for u, v in zip(digits(a), digits(b))])
+    return add, sub
+
+
+def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group, phase: str = "all",
                  steps: int | None = None):
     """Generalized Allreduce (generalized-Allreduce paper: bandwidth-optimal
     section eqs. (17)-(25), intermediate steps eqs. (26)-(36) and Fig. 6,
@@ -392,7 +425,10 @@ def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: 
         owner = lambda p, i: p ^ i  # noqa: E731
         ranks_of = lambda t: t ^ np.arange(P)  # noqa: E731
     else:
-        raise ValueError(group)
+        add, sub = _product_group(group, P)
+        place = add
+        owner = sub
+        ranks_of = lambda t: add(t, np.arange(P))  # noqa: E731
 
     c = -(-n // P) if n else 1
     part_of = (np.asarray(idx, dtype=np.int64) // c) if n else np.zeros(0, dtype=np.int64)
@@ -490,7 +526,7 @@ def _generalized(alg, xacc: np.ndarray, n: int, idx: np.ndarray, r: int, group: 
 # --------------------------------------------------------------------------
 def allreduce(x: np.ndarray, algo: str, dtype: str, op: str = "sum", knob: int = 0,
               groups=None, n: int | None = None, idx=None, symbolic: bool = False,
-              return_stats: bool = False, steps: int | None = None):
+              return_stats: bool = False, steps: int | None = None, factors=None):
     """Replay one Allreduce schedule on the CPU.
 
     x       (P, m) or (P, B, m): each rank's buffer (B independent instances of
@@ -498,7 +534,8 @@ def allreduce(x: np.ndarray, algo: str, dtype: str, op: str = "sum", knob: int =
             n offsets). int32 / fp32 arrays, bf16 as uint16 bit patterns.
     algo    one of ALGOS; ``knob`` is r for the generalized algorithm;
             ``groups`` the AHC group sizes (contiguous ranks); ``steps`` the
-            generalized algorithm's reduction steps (default ceil(log2 P)).
+            generalized algorithm's reduction steps (default ceil(log2 P));
+            ``factors`` (m1, ..., mt) its group Z_m1 x ... x Z_mt (default Z_P).
     symbolic  ignore the values and return, per rank and offset, the id of the
             combination tree (leaves = ranks) in ``stats['algebra']``.
     Returns the per-rank outputs in x's shape (and a stats dict if asked).
@@ -527,8 +564,12 @@ def allreduce(x: np.ndarray, algo: str, dtype: str, op: str = "sum", knob: int =
     elif algo in ("generalized", "generalized_xor"):
         if steps is not None and algo == "generalized_xor" and steps != ceil_log2(P):
             raise ValueError("more steps are defined for the cyclic group only")
-        out, stats = _generalized(alg, xacc, n, idx, knob, "cyclic" if algo == "generalized" else "xor",
-                                  steps=steps)
+        grp = "cyclic" if algo == "generalized" else "xor"
+        if factors:
+            if algo != "generalized":
+                raise ValueError("group factors apply to the generalized algorithm")
+            grp = tuple(factors)
+        out, stats = _generalized(alg, xacc, n, idx, knob, grp, steps=steps)
     else:
         net = Net(alg, xacc.copy(), n, idx)
         if algo == "direct":
@@ -616,7 +657,7 @@ def _half_input(x, alg, symbolic, P):
 
 
 def reduce_scatter(x: np.ndarray, algo: str, dtype: str, op: str = "sum", n: int | None = None, idx=None,
-                   symbolic: bool = False, return_stats: bool = False, steps: int | None = None):
+                   symbolic: bool = False, return_stats: bool = False, steps: int | None = None, factors=None):
     """Replay a reduce-scatter: rank q ends with the reduced part q of the ceil
     split into P parts. x as for ``allreduce``. Returns the result vector
     (element e as rank e // ceil(n / P) holds it), shape (m,) or (B, m).
@@ -635,8 +676,8 @@ def reduce_scatter(x: np.ndarray, algo: str, dtype: str, op: str = "sum", n: int
     if P == 1 or n == 0:
         res, stats = xacc[0].copy(), dict(steps=0)
     elif algo in ("generalized", "generalized_xor"):
-        res, stats = _generalized(alg, xacc, n, idx, 0, "cyclic" if algo == "generalized" else "xor", "reduce",
-                                  steps if algo == "generalized" else None)
+        grp = tuple(factors) if factors and algo == "generalized" else ("cyclic" if algo == "generalized" else "xor")
+        res, stats = _generalized(alg, xacc, n, idx, 0, grp, "reduce", steps if algo == "generalized" else None)
     else:
         net = Net(alg, xacc.copy(), n, idx)
         if algo == "ring":
@@ -661,7 +702,7 @@ def reduce_scatter(x: np.ndarray, algo: str, dtype: str, op: str = "sum", n: int
 
 
 def all_gather(x: np.ndarray, algo: str, dtype: str, n: int | None = None, idx=None, return_stats: bool = False,
-               steps: int | None = None):
+               steps: int | None = None, factors=None):
     """Replay an all-gather: rank q contributes part q of its buffer (the rest
     of its input is ignored); every rank ends with every part. Returns the
     per-rank buffers in x's shape. Pure copies: the bits are the owners'."""
@@ -674,8 +715,8 @@ def all_gather(x: np.ndarray, algo: str, dtype: str, n: int | None = None, idx=N
     if P == 1 or n == 0:
         out, stats = xacc.copy(), dict(steps=0)
     elif algo in ("generalized", "generalized_xor"):
-        out, stats = _generalized(alg, xacc, n, idx, 0, "cyclic" if algo == "generalized" else "xor", "gather",
-                                  steps if algo == "generalized" else None)
+        grp = tuple(factors) if factors and algo == "generalized" else ("cyclic" if algo == "generalized" else "xor")
+        out, stats = _generalized(alg, xacc, n, idx, 0, grp, "gather", steps if algo == "generalized" else None)
     else:
         net = Net(alg, xacc.copy(), n, idx)
         if algo == "ring":

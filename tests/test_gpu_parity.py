@@ -322,3 +322,24 @@ def test_generalized_more_steps_full_size_prime_ranks():
             got = gpu_allreduce(x, "generalized", "fp32", "sum", 0, ex, steps=S)
             assert np.array_equal(bits(got[:, idx]), bits(want)), (S, ex)
         check_tol(got, x, "fp32")
+
+
+# --------------------------------------------------------------------------
+# the generalized algorithm over other groups Z_m1 x ... x Z_mt
+# --------------------------------------------------------------------------
+def test_generalized_product_groups():
+    import allreduce_schedule_algorithms_amd as A
+    for P, fl in ((6, [(2, 3), (3, 2)]), (8, [(2, 4), (4, 2)]), (12, [(2, 6), (3, 4), (2, 2, 3)])):
+        for f in fl:
+            for r in (0, 1):
+                for dtype in ("fp32", "bf16"):
+                    for n in (37, 4099):
+                        x = inputs.make(dtype, P, n, seed=P + r + n)
+                        want = oracle.allreduce(x, "generalized", dtype, "sum", knob=r, factors=f)
+                        info = A.ar_schedule_build(A.make_call(P, n, dtype, "sum", "generalized", r,
+                                                               groups=list(f))).info()
+                        for ex in ("fused", "literal"):
+                            if ex == "fused" and info.max_trees > 8:
+                                continue
+                            got = gpu_allreduce(x, "generalized", dtype, "sum", r, ex, groups=list(f))
+                            assert np.array_equal(bits(got), bits(want)), (P, f, r, dtype, n, ex)
