@@ -54,6 +54,7 @@ class Algo(enum.IntEnum):
     AR_GENERALIZED = 5
     AR_GENERALIZED_XOR = 6
     AR_AHC = 7
+    AR_CHAIN = 8
     AR_AUTO = -1
 
 
@@ -77,7 +78,8 @@ COLLECTIVES = {"allreduce": Collective.AR_ALLREDUCE, "reduce_scatter": Collectiv
                "all_gather": Collective.AR_ALL_GATHER}
 ALGOS = {"direct": Algo.AR_DIRECT, "ring": Algo.AR_RING, "rh_rd": Algo.AR_RH_RD, "rd": Algo.AR_RD,
          "binomial": Algo.AR_BINOMIAL, "generalized": Algo.AR_GENERALIZED,
-         "generalized_xor": Algo.AR_GENERALIZED_XOR, "ahc": Algo.AR_AHC, "auto": Algo.AR_AUTO}
+         "generalized_xor": Algo.AR_GENERALIZED_XOR, "ahc": Algo.AR_AHC, "chain": Algo.AR_CHAIN,
+         "auto": Algo.AR_AUTO}
 ALGO_NAMES = {int(v): k for k, v in ALGOS.items()}
 COST_FORMS = {"busiest": CostForm.AR_COST_BUSIEST_RANK, "all_ranks": CostForm.AR_COST_ALL_RANKS}
 EXECS = {"fused": Exec.AR_EXEC_FUSED, "literal": Exec.AR_EXEC_LITERAL, "replay": Exec.AR_EXEC_REPLAY}

@@ -66,7 +66,7 @@ bool to_spec(const ar_call* c, ar::Spec* s, std::string* err) {
   s->dtype = c->dtype;
   s->op = c->op;
   s->algo = c->algo;
-  s->knob = (c->algo == AR_GENERALIZED || c->algo == AR_GENERALIZED_XOR) ? c->knob : 0;
+  s->knob = (c->algo == AR_GENERALIZED || c->algo == AR_GENERALIZED_XOR || c->algo == AR_CHAIN) ? c->knob : 0;
   s->steps = c->steps;
   s->groups.clear();
   if (c->algo == AR_AHC) {

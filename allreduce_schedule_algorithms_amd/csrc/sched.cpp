@@ -292,6 +292,30 @@ static void gen_binomial(int P, Exprs& ex, Logical& lg) {
   }
 }
 
+// Pipelined chain ("Reduction Operator" page, pipelined algorithm): m pieces;
+// in reduce step t unit i passes piece t - (P - 1 - i) to i - 1, which
+// combines it (P + m - 2 steps, the root holding the last piece at the end);
+// then the broadcast down the chain, unit i passing piece t - i to i + 1.
+static void gen_chain(int P, int m, Exprs& ex, Logical& lg) {
+  BufGen g(P, m, ex, lg);
+  for (int t = 0; t < P + m - 2; ++t) {
+    g.begin();
+    for (int i = 1; i < P; ++i) {
+      int k = t - (P - 1 - i);
+      if (k >= 0 && k < m) g.msg(K_REDUCE, i, i - 1, k, k + 1);
+    }
+    g.end();
+  }
+  for (int t = 0; t < P + m - 2; ++t) {
+    g.begin();
+    for (int i = 0; i + 1 < P; ++i) {
+      int k = t - i;
+      if (k >= 0 && k < m) g.msg(K_COPY, i, i + 1, k, k + 1);
+    }
+    g.end();
+  }
+}
+
 // AHC (HCCL "AHC" page): Lc x G chunks; ring reduce-scatter inside each group,
 // ring Allreduce per piece between its owners, one per group (the page's
 // logical devices that share an ID), over G equal sub-pieces, ring all-gather
@@ -495,6 +519,8 @@ bool validate_spec(const Spec& s, std::string* err) {
     if (s.knob < 0 || s.knob > L) return fail("knob r must be in [0, reduction steps]");
     if (s.algo == A_GENERALIZED_XOR && (s.P & (s.P - 1))) return fail("the XOR group needs P to be a power of two");
   }
+  if (s.algo == A_CHAIN && (s.knob < 1 || s.knob > kMaxChainPieces))
+    return fail("the chain's knob m (pieces) must be in [1, 4096]");
   if (s.coll != C_ALLREDUCE) {
     if (!half_supported(s.algo))
       return fail("reduce-scatter / all-gather support direct, ring, rh_rd, generalized and generalized_xor");
@@ -974,6 +1000,7 @@ static bool generate(const Spec& spec, Exprs& ex, Logical& lg, std::string* err)
     case A_GENERALIZED: gen_generalized(P, spec.knob, radices_of(spec), ex, lg, C_ALLREDUCE, spec.steps); break;
     case A_GENERALIZED_XOR: gen_generalized(P, spec.knob, radices_of(spec), ex, lg); break;
     case A_AHC: gen_ahc(P, spec.groups, ex, lg); break;
+    case A_CHAIN: gen_chain(P, spec.knob, ex, lg); break;
     default: if (err) *err = "unknown algorithm"; return false;
   }
   return true;
@@ -1125,6 +1152,11 @@ static double closed_form(const Schedule& s, double m, double alpha, double beta
       double extra = double((1 << r) - 1);
       return (2 * L - r) * alpha + (2 * (P - 1) + extra * L) * u * beta + ((P - 1) + extra * (2 * L - 2)) * u * gamma;
     }
+    case A_CHAIN: {  // "Reduction Operator" page: (T_start + (n/m) T_byte)(p + m - 2), then the broadcast
+      const int k = s.spec.knob;
+      const double piece = m / k;
+      return (P + k - 2) * (alpha + piece * (beta + gamma)) + (P + k - 2) * (alpha + piece * beta);
+    }
     default:
       return std::numeric_limits<double>::quiet_NaN();  // AHC: the page's formula is truncated
   }
@@ -1208,7 +1240,27 @@ CostOut cost_walk(const Schedule& s, double alpha, double beta, double gamma) {
 // ----------------------------------------------------------------------------
 bool is_auto(const Spec& s) {
   return s.algo == kAutoAlgo ||
-         ((s.algo == A_GENERALIZED || s.algo == A_GENERALIZED_XOR) && s.knob == kAutoKnob);
+         ((s.algo == A_GENERALIZED || s.algo == A_GENERALIZED_XOR || s.algo == A_CHAIN) && s.knob == kAutoKnob);
+}
+
+// Piece counts to try for the pipelined chain: the floor and ceiling of the
+// optimum of (P + m - 2)(2 alpha + (M / m)(2 beta + gamma)), the reduce and the
+// broadcast of the "Reduction Operator" page's pipelined time with T_start =
+// alpha and T_byte = beta + gamma (beta only for the broadcast): m* =
+// sqrt(M (P - 2)(2 beta + gamma) / (2 alpha)), M the bytes of one rank.
+std::vector<int> chain_pieces(const Spec& s, const CostModel& m) {
+  const int cap = int(std::min<int64_t>(kMaxChainPieces, std::max<int64_t>(1, s.n)));
+  const double M = double(s.n) * double(elt_bytes(s.dtype)) * double(s.batch);
+  double x;
+  if (s.P <= 2) x = 0.0;
+  else if (m.alpha > 0) x = std::sqrt(M * double(s.P - 2) * (2 * m.beta + m.gamma) / (2 * m.alpha));
+  else x = double(cap);
+  std::vector<int> out;
+  for (double v : {std::floor(x), std::ceil(x)}) {
+    int k = v < 1 ? 1 : v > cap ? cap : int(v);
+    if (out.empty() || out.back() != k) out.push_back(k);
+  }
+  return out;
 }
 
 bool step_counts(const Spec& spec, StepCounts* out, std::string* err) {
@@ -1304,6 +1356,9 @@ bool select_spec(const Spec& in, const CostModel& m, Spec* out, double* seconds,
     if (pow2)
       for (int r = 0; r <= L; ++r) cand.push_back({A_GENERALIZED_XOR, r});
     if (!in.groups.empty()) cand.push_back({A_AHC, 0});
+    for (int k : chain_pieces(in, m)) cand.push_back({A_CHAIN, k});
+  } else if (in.algo == A_CHAIN) {
+    for (int k : chain_pieces(in, m)) cand.push_back({A_CHAIN, k});
   } else {
     const int S = in.steps > 0 ? in.steps : L;
     for (int r = 0; r <= (in.coll == C_ALLREDUCE ? S : 0); ++r) cand.push_back({in.algo, r});

@@ -24,7 +24,7 @@ namespace ar {
 enum Kind : int32_t { K_REDUCE = 0, K_COPY = 1, K_MOVE = 2 };
 enum Algo : int32_t {
   A_DIRECT = 0, A_RING = 1, A_RH_RD = 2, A_RD = 3, A_BINOMIAL = 4,
-  A_GENERALIZED = 5, A_GENERALIZED_XOR = 6, A_AHC = 7, A_NUM_ALGOS = 8
+  A_GENERALIZED = 5, A_GENERALIZED_XOR = 6, A_AHC = 7, A_CHAIN = 8, A_NUM_ALGOS = 9
 };
 enum Dtype : int32_t { D_INT32 = 0, D_FP32 = 1, D_BF16 = 2 };
 // O_AVG combines as a sum; the complete result is divided by P once.
@@ -35,6 +35,7 @@ enum Op : int32_t { O_SUM = 0, O_MAX = 1, O_AVG = 2 };
 enum Coll : int32_t { C_ALLREDUCE = 0, C_REDUCE_SCATTER = 1, C_ALL_GATHER = 2 };
 
 constexpr int kMaxRanks = 256;
+constexpr int kMaxChainPieces = 4096;
 
 struct Spec {
   int P = 0;
@@ -178,6 +179,7 @@ double model_seconds(const StepCounts& c, const Spec& spec, const CostModel& m);
 // (ties: fewer steps, then the earlier candidate). Other specs pass through.
 bool select_spec(const Spec& in, const CostModel& m, Spec* out, double* seconds, std::string* err);
 bool is_auto(const Spec& s);
+std::vector<int> chain_pieces(const Spec& s, const CostModel& m);
 
 int elt_bytes(int dtype);
 int acc_bytes(int dtype);

@@ -57,7 +57,8 @@ WORKLOADS = {
                 ("generalized", 0, "fused", "allreduce", "sum", 4), ("generalized", 0, "fused", "allreduce", "sum", 6),
                 ("generalized", 0, "literal", "allreduce", "sum", 4),
                 ("generalized", 0, "literal", "allreduce", "sum", 5),
-                ("generalized", 0, "literal", "allreduce", "sum", 6)]),
+                ("generalized", 0, "literal", "allreduce", "sum", 6),
+                ("chain", 1, "fused"), ("chain", 8, "literal"), ("chain", 64, "literal")]),
     "ahc_bf16": dict(
         desc="192 ranks in groups (64, 128) x 2^20 bf16 N(0,1), fp32 accumulation, seed 0",
         P=192, n=1 << 20, dtype="bf16", batch=1, groups=[64, 128],

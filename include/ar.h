@@ -96,7 +96,12 @@ typedef enum { AR_ALLREDUCE = 0, AR_REDUCE_SCATTER = 1, AR_ALL_GATHER = 2 } ar_c
  *                     N_i - 2^(S-i-1)), N_{i+1} = N_i - h_i.
  *  AR_GENERALIZED_XOR the same over the self-inverse group of Table 1.b (P a power of two).
  *  AR_AHC             asymmetric hierarchical Allreduce over contiguous groups (HCCL "AHC"
- *                     page, Description), 2(max g - 1) + 2(G - 1) steps. */
+ *                     page, Description), 2(max g - 1) + 2(G - 1) steps.
+ *  AR_CHAIN           pipelined chain reduce to rank 0 + pipelined chain broadcast ("Reduction
+ *                     Operator" page, pipelined algorithm): knob = m pieces (1..4096, ceil
+ *                     split); in reduce step t rank i passes piece t - (P-1-i) to i - 1, which
+ *                     combines it; 2(P + m - 2) steps. AR_KNOB_AUTO takes the floor or ceiling
+ *                     of the page's optimum m. */
 typedef enum {
   AR_DIRECT = 0,
   AR_RING = 1,
@@ -106,6 +111,7 @@ typedef enum {
   AR_GENERALIZED = 5,
   AR_GENERALIZED_XOR = 6,
   AR_AHC = 7,
+  AR_CHAIN = 8,
   AR_AUTO = -1             /* let the cost model pick (see ar_select) */
 } ar_algo;
 
@@ -130,8 +136,9 @@ typedef struct ar_call {
   int32_t dtype;           /* ar_dtype */
   int32_t op;              /* ar_op */
   int32_t algo;            /* ar_algo; AR_AUTO lets the cost model choose */
-  int32_t knob;            /* AR_GENERALIZED*: r = distribution steps removed, 0..ceil(log2 P),
-                              or AR_KNOB_AUTO; ignored otherwise */
+  int32_t knob;            /* AR_GENERALIZED*: r = distribution steps removed, 0..ceil(log2 P) (or
+                              0..steps), or AR_KNOB_AUTO; AR_CHAIN: pieces m >= 1, or
+                              AR_KNOB_AUTO; ignored otherwise */
   int32_t exec;            /* ar_exec */
   int64_t n;               /* elements per instance (>= 0) */
   int64_t batch;           /* independent instances per buffer (>= 1); 0 is read as 1 */
@@ -280,8 +287,11 @@ ar_status ar_cost_steps(const ar_schedule* s, int64_t* sent, int64_t* recv, int6
  *   AR_COST_ALL_RANKS     every rank's bytes summed: all ranks share one memory, as in this
  *                         library's step-by-step executor (AR_EXEC_LITERAL) on one device.
  * AR_AUTO enumerates AR_DIRECT, AR_RING, AR_RH_RD, AR_RD, AR_BINOMIAL, AR_GENERALIZED r = 0..
- * ceil(log2 P), AR_GENERALIZED_XOR r = 0..ceil(log2 P) when P is a power of two, and AR_AHC when
- * groups are given; AR_KNOB_AUTO enumerates r for the given algorithm. The least model time
+ * ceil(log2 P), AR_GENERALIZED_XOR r = 0..ceil(log2 P) when P is a power of two, AR_AHC when
+ * groups are given, and AR_CHAIN with the floor and the ceiling of the "Reduction Operator"
+ * page's optimal piece count, m* = sqrt(M (P - 2)(2 beta + gamma) / (2 alpha)) for M bytes per
+ * rank (clamped to 1..min(4096, n)); AR_KNOB_AUTO enumerates r (or those m) for the given
+ * algorithm. The least model time
  * wins; ties go to fewer steps, then to the earlier candidate in that order. The choice
  * depends only on (P, n, batch, dtype, groups) and the model, never on timing. The default
  * model is a least-squares fit of AR_EXEC_LITERAL fp32 calls measured on MI355X, form

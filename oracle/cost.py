@@ -107,6 +107,9 @@ def step_counts(P: int, n: int, algo: str, knob: int = 0, groups=None, coll: str
     Nothing moves when n == 0 or P == 1: zero steps. coll selects the
     Allreduce or its reduce-scatter / all-gather half.
     """
+    key = (P, n, algo, knob, tuple(groups) if groups else None, coll, steps)
+    if key in _COUNTS:
+        return _COUNTS[key]
     z = np.zeros((0, P), dtype=np.int64)
     if P == 1 or n == 0:
         return z, z, z
@@ -118,9 +121,16 @@ def step_counts(P: int, n: int, algo: str, knob: int = 0, groups=None, coll: str
     else:
         _, st = schedules.allreduce(x, algo, "int32", "sum", knob=knob, groups=groups, n=n, idx=[0],
                                     return_stats=True, steps=steps)
-    return (np.asarray(st["sent"], dtype=np.int64).reshape(-1, P),
-            np.asarray(st["recv"], dtype=np.int64).reshape(-1, P),
-            np.asarray(st["reduced"], dtype=np.int64).reshape(-1, P))
+    out = tuple(np.asarray(st[k], dtype=np.int64).reshape(-1, P) for k in ("sent", "recv", "reduced"))
+    for a in out:
+        a.setflags(write=False)
+    if len(_COUNTS) > 4096:
+        _COUNTS.clear()
+    _COUNTS[key] = out
+    return out
+
+
+_COUNTS: dict = {}  # replays are deterministic: counts per argument tuple are computed once
 
 
 def model_seconds(counts, elt: int, batch: int, alpha: float, beta: float, gamma: float,
@@ -144,10 +154,36 @@ def model_seconds(counts, elt: int, batch: int, alpha: float, beta: float, gamma
     return alpha * S + beta * (float(xb) * elt * batch) + gamma * (float(xg) * elt * batch)
 
 
-def candidates(P: int, algo: str = "auto", groups=None, coll: str = "allreduce", steps: int | None = None):
-    """(algo, knob) pairs in tie-breaking order (knob up to the reduction steps)."""
+def chain_pieces(P: int, n: int, elt: int, batch: int, alpha: float, beta: float, gamma: float):
+    """Piece counts for the pipelined chain: floor and ceiling of the optimum of
+    the "Reduction Operator" page's time (T_start + (n/m) T_byte)(p + m - 2),
+    taken for the whole Allreduce (the reduce with T_byte = beta + gamma, the
+    broadcast with beta): m* = sqrt(M (P - 2)(2 beta + gamma) / (2 alpha)) for M
+    bytes per rank, clamped to [1, min(4096, n)]."""
+    cap = min(4096, max(1, n))
+    M = float(n) * elt * batch
+    if P <= 2:
+        x = 0.0
+    elif alpha > 0:
+        x = math.sqrt(M * (P - 2) * (2 * beta + gamma) / (2 * alpha))
+    else:
+        x = float(cap)
+    out = []
+    for v in (math.floor(x), math.ceil(x)):
+        k = 1 if v < 1 else cap if v > cap else int(v)
+        if not out or out[-1] != k:
+            out.append(k)
+    return out
+
+
+def candidates(P: int, algo: str = "auto", groups=None, coll: str = "allreduce", steps: int | None = None,
+               chain=()):
+    """(algo, knob) pairs in tie-breaking order (knob up to the reduction steps;
+    ``chain`` the piece counts tried for the pipelined chain)."""
     L = ceil_log2(P) if not steps else steps
     pow2 = P & (P - 1) == 0
+    if algo == "chain":
+        return [("chain", m) for m in chain]
     if coll != "allreduce":
         if algo != "auto":
             return [(algo, 0)]
@@ -161,7 +197,7 @@ def candidates(P: int, algo: str = "auto", groups=None, coll: str = "allreduce",
         out += [("generalized_xor", r) for r in range(L + 1)]
     if groups:
         out.append(("ahc", 0))
-    return out
+    return out + [("chain", m) for m in chain]
 
 
 def select(P: int, n: int, dtype: str, alpha: float, beta: float, gamma: float, form: str = "busiest",
@@ -170,7 +206,8 @@ def select(P: int, n: int, dtype: str, alpha: float, beta: float, gamma: float, 
     ``steps`` (the generalized algorithm's reduction steps) applies to an explicit algorithm only."""
     best = None
     steps = steps if algo != "auto" else None
-    for a, r in candidates(P, algo, groups, coll, steps):
+    chain = chain_pieces(P, n, ELT_BYTES[dtype], batch, alpha, beta, gamma) if coll == "allreduce" else ()
+    for a, r in candidates(P, algo, groups, coll, steps, chain):
         c = step_counts(P, n, a, r, groups if a == "ahc" else None, coll, steps)
         t = model_seconds(c, ELT_BYTES[dtype], batch, alpha, beta, gamma, form)
         key = (t, c[0].shape[0])

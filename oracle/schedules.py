@@ -19,7 +19,7 @@ import numpy as np
 from .net import COPY, REDUCE, Net, partition
 from .numerics import Algebra, Symbolic, ceil_log2
 
-ALGOS = ("direct", "ring", "rh_rd", "rd", "binomial", "generalized", "generalized_xor", "ahc")
+ALGOS = ("direct", "ring", "rh_rd", "rd", "binomial", "generalized", "generalized_xor", "ahc", "chain")
 
 
 def _pow2_floor(P: int) -> int:
@@ -205,6 +205,39 @@ def _binomial(net: Net):
     for k in reversed(range(K)):
         b = 1 << k
         net.step([(i, i + b, 0, n, COPY) for i in range(0, P, 2 * b) if i + b < P])
+
+
+# --------------------------------------------------------------------------
+# pipelined chain reduce + pipelined chain broadcast
+# --------------------------------------------------------------------------
+def _chain(net: Net, m: int):
+    """Pipelined reduction along a chain ("Reduction Operator" page, pipelined
+    algorithm): the vector is cut into m pieces; unit i passes each piece to
+    i - 1 one step after it arrived, combined with its own, so the root 0 holds
+    the first piece after p - 1 steps and the last after p + m - 2. The
+    Allreduce adds a broadcast from the root (same page, where the reduce result
+    is distributed afterwards), pipelined the same way down the chain.
+
+    Reading: in step t unit i sends piece t - (p - 1 - i) to i - 1; the
+    broadcast starts after the reduce (no overlap), unit i forwarding piece
+    t - i to i + 1 in its step t. Pieces follow the ceil split.
+    """
+    P, n = net.P, net.n
+    pieces = partition(n, m)
+    for t in range(P + m - 2):
+        msgs = []
+        for i in range(1, P):
+            k = t - (P - 1 - i)
+            if 0 <= k < m:
+                msgs.append((i, i - 1, *pieces[k], REDUCE))
+        net.step(msgs)
+    for t in range(P + m - 2):
+        msgs = []
+        for i in range(P - 1):
+            k = t - i
+            if 0 <= k < m:
+                msgs.append((i, i + 1, *pieces[k], COPY))
+        net.step(msgs)
 
 
 # --------------------------------------------------------------------------
@@ -584,6 +617,10 @@ def allreduce(x: np.ndarray, algo: str, dtype: str, op: str = "sum", knob: int =
             _binomial(net)
         elif algo == "ahc":
             _ahc(net, list(groups) if groups else [P])
+        elif algo == "chain":
+            if knob < 1:
+                raise ValueError("the chain needs m >= 1 pieces")
+            _chain(net, knob)
         else:
             raise ValueError(f"unknown algorithm {algo!r}")
         out, stats = net.buf, net.stats()

@@ -26,3 +26,13 @@ def golden_rows(name):
 @pytest.fixture
 def golden():
     return golden_rows
+
+
+@pytest.fixture(autouse=True)
+def _fresh_oracle_counts():
+    """The oracle memoizes step counts per argument tuple; a test that plants a
+    mistake in a replay must not see counts cached from the correct one."""
+    from oracle import cost
+    cost._COUNTS.clear()
+    yield
+    cost._COUNTS.clear()

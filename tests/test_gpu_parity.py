@@ -343,3 +343,32 @@ def test_generalized_product_groups():
                                 continue
                             got = gpu_allreduce(x, "generalized", dtype, "sum", r, ex, groups=list(f))
                             assert np.array_equal(bits(got), bits(want)), (P, f, r, dtype, n, ex)
+
+
+# --------------------------------------------------------------------------
+# pipelined chain reduce + broadcast
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["int32", "fp32", "bf16"])
+def test_chain_small(dtype):
+    for P in (2, 3, 5, 8, 12):
+        for m in (1, 3, 16):
+            for n in (37, 4099):
+                x = inputs.make(dtype, P, n, seed=P * m + n)
+                for op in ("sum", "max") + (("avg",) if dtype != "int32" else ()):
+                    want = oracle.allreduce(x, "chain", dtype, op, knob=m)
+                    for ex in ("fused", "literal"):
+                        got = gpu_allreduce(x, "chain", dtype, op, m, ex)
+                        assert np.array_equal(bits(got), bits(want)), (P, m, n, op, ex)
+
+
+def test_chain_full_size_prime_ranks():
+    x = inputs.workload("prime_fp32")
+    P, n = x.shape
+    idx = inputs.sample_indices(n, 64, count=4096)
+    xs = np.ascontiguousarray(x[:, idx])
+    for m in (1, 8, 64):
+        want = oracle.allreduce(xs, "chain", "fp32", "sum", knob=m, n=n, idx=idx)
+        for ex in ("fused", "literal"):
+            got = gpu_allreduce(x, "chain", "fp32", "sum", m, ex)
+            assert np.array_equal(bits(got[:, idx]), bits(want)), (m, ex)
+        check_tol(got, x, "fp32")
