@@ -378,7 +378,24 @@ def model_fit(args):
     print(json.dumps(out))
 
 
-def load_traffic(wl_name, algo, knob, ex):
+def schedule_key(algo, knob, ex, coll="allreduce", op="sum", rsteps=0, factors=None):
+    """Key of a schedule in the bench's table: algo/r<knob>/<exec>[/<collective>][/<op>][/S<steps>][/Z<factors>]."""
+    key = f"{algo}/r{knob}/{ex}" + ("" if coll == "allreduce" else f"/{coll}") + ("" if op == "sum" else f"/{op}")
+    key += f"/S{rsteps}" if rsteps else ""
+    key += "/Z" + "x".join(str(m) for m in factors) if factors else ""
+    return key
+
+
+def parse_key(key):
+    algo, k, ex, *rest = key.split("/")
+    return dict(algo=algo, knob=int(k[1:]), ex=ex,
+                coll=next((t for t in rest if t in ("reduce_scatter", "all_gather")), "allreduce"),
+                op=next((t for t in rest if t in ("max", "avg")), "sum"),
+                rsteps=next((int(t[1:]) for t in rest if t.startswith("S")), 0),
+                factors=next(([int(v) for v in t[1:].split("x")] for t in rest if t.startswith("Z")), None))
+
+
+def load_traffic(wl_name, key):
     """HBM bytes per launch from the committed counter summary (FETCH_SIZE and
     WRITE_SIZE, each scaled by what it reads for a plain copy of known size), or
     None when the summary was taken from a different kernel source."""
@@ -392,7 +409,7 @@ def load_traffic(wl_name, algo, knob, ex):
         return None
     if t.get("kernel_hash") != kernel_source_hash():
         return None
-    rec = t.get("entries", {}).get(f"{wl_name}/{algo}/{knob}/{ex}")
+    rec = t.get("entries", {}).get(f"{wl_name}/{key}")
     return rec.get("bytes_per_launch") if rec else None
 
 
@@ -403,6 +420,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="rh_fp32", choices=sorted(WORKLOADS))
     ap.add_argument("--headline-only", action="store_true", help="time only the headline schedule")
+    ap.add_argument("--schedule", default=None, metavar="KEY",
+                    help="time this schedule as the headline, a key of the schedule table such as "
+                         "ring/r0/fused/reduce_scatter or generalized/r0/literal/S6 (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--warm", action="store_true", help="also report warm-cache (no flush) figures")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -439,32 +459,25 @@ def main():
     wl["name"] = args.workload
     x = make_inputs(wl)
     r = Runner(wl, x)
-    algo, knob, ex = wl["headline"]
+    hkey = args.schedule or schedule_key(*wl["headline"])
+    h = parse_key(hkey)
+    algo, knob, ex = h["algo"], h["knob"], h["ex"]
 
-    head = r.time(algo, knob, ex, args.steps, args.warmup)
-    schedules = {f"{algo}/r{knob}/{ex}": head}
-    if not args.headline_only:
+    def timed(key, steps, warmup, **kw):
+        q = parse_key(key)
+        return r.time(q["algo"], q["knob"], q["ex"], steps, warmup, coll=q["coll"], op=q["op"], rsteps=q["rsteps"],
+                      factors=q["factors"], **kw)
+
+    head = timed(hkey, args.steps, args.warmup)
+    schedules = {hkey: head}
+    if not args.headline_only and not args.schedule:
         for entry in wl["others"]:
-            a2, k2, e2 = entry[:3]
-            coll = entry[3] if len(entry) > 3 else "allreduce"
-            op = entry[4] if len(entry) > 4 else "sum"
-            rsteps = entry[5] if len(entry) > 5 else 0
-            factors = entry[6] if len(entry) > 6 else None
-            key = f"{a2}/r{k2}/{e2}" + ("" if coll == "allreduce" else f"/{coll}") + ("" if op == "sum" else f"/{op}")
-            key += f"/S{rsteps}" if rsteps else ""
-            key += "/Z" + "x".join(str(m) for m in factors) if factors else ""
-            schedules[key] = r.time(a2, k2, e2, max(10, args.steps // 2), 2, coll=coll, op=op, rsteps=rsteps,
-                                    factors=factors)
+            key = schedule_key(*entry)
+            schedules[key] = timed(key, max(10, args.steps // 2), 2)
     if args.warm:
         for key in list(schedules):
-            a2, k2, e2, *rest = key.split("/")
-            coll = next((t for t in rest if t in ("reduce_scatter", "all_gather")), "allreduce")
-            op = next((t for t in rest if t in ("max", "avg")), "sum")
-            rsteps = next((int(t[1:]) for t in rest if t.startswith("S")), 0)
-            factors = next(([int(v) for v in t[1:].split("x")] for t in rest if t.startswith("Z")), None)
-            schedules[key]["warm_GBps"] = r.time(a2, int(k2[1:]), e2, max(10, args.steps // 2), 2, cold=False,
-                                                 kernel_pass=False, coll=coll, op=op, rsteps=rsteps,
-                                                 factors=factors)["GBps"]
+            schedules[key]["warm_GBps"] = timed(key, max(10, args.steps // 2), 2, cold=False,
+                                                kernel_pass=False)["GBps"]
     for v in schedules.values():
         v["pct_hbm_peak"] = round(100.0 * v["GBps"] / HBM_PEAK_GBPS, 2)
         for k in ("ms", "ms_median", "ms_min", "kernel_ms", "wall_ms_per_step", "GBps", "kernel_GBps"):
@@ -474,16 +487,19 @@ def main():
 
     # model bytes from the library's cost walk (fused / literal HBM bytes per call)
     import allreduce_schedule_algorithms_amd as A
-    s = A.ar_schedule_build(r.call_for(algo, knob, ex))
+    s = A.ar_schedule_build(r.call_for(algo, knob, ex, coll=h["coll"], op=h["op"], rsteps=h["rsteps"],
+                                       factors=h["factors"]))
     cst = s.cost()
     value = head["GBps"]
     achieved = head["kernel_GBps"]
-    traffic = load_traffic(args.workload, algo, knob, ex)
+    traffic = load_traffic(args.workload, hkey)
+    kernel = ("k_literal" if ex == "literal" else
+              "k_direct" if (algo == "direct" and ex == "fused" and h["coll"] == "allreduce") else "k_fused")
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "k_fused" if not (algo == "direct" and ex == "fused") else "k_direct",
+                "kernel": kernel,
                 "avg_launch_ms": head["kernel_ms"],
-                "algorithmic_bytes_per_launch": r.essential,
+                "algorithmic_bytes_per_launch": essential_bytes(wl, h["coll"]),
                 "model_bytes_per_launch": cst.fused_hbm_bytes if ex != "literal" else cst.literal_hbm_bytes}
 
     cpu = None if args.no_cpu else cpu_baseline(wl, x)
@@ -501,7 +517,7 @@ def main():
         "dtype": DT_NAME[wl["dtype"]],
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {wl['desc']}", "P": wl["P"], "n": wl["n"], "batch": wl["batch"],
-                   "schedule": algo, "knob": knob, "exec": ex, "cache": "cold (1 GiB flush before each step)"},
+                   "schedule": hkey, "knob": knob, "exec": ex, "cache": "cold (1 GiB flush before each step)"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "runtime_copy_GBps": round(ceiling, 1),  # torch D2D copy of 2 GiB (HIP runtime blit), context only
         "wall_ms_per_step": head["wall_ms_per_step"],
