@@ -372,3 +372,34 @@ def test_chain_full_size_prime_ranks():
             got = gpu_allreduce(x, "chain", "fp32", "sum", m, ex)
             assert np.array_equal(bits(got[:, idx]), bits(want)), (m, ex)
         check_tol(got, x, "fp32")
+
+
+def test_batched_halves_avg_and_chain():
+    from oracle import schedules as sch
+    P, n, B = 6, 106, 64
+    x = inputs.make("fp32", P, n * B, seed=11)
+    xb = x.reshape(P, B, n)
+    own = half_owner(n, P)
+    for ex in ("fused", "literal"):
+        got = gpu_allreduce(x, "ring", "fp32", "sum", 0, ex, batch=B, collective="reduce_scatter").reshape(P, B, n)
+        want = sch.reduce_scatter(xb, "ring", "fp32", "sum")
+        assert np.array_equal(bits(got[own, :, np.arange(n)].T), bits(want)), ex
+        got = gpu_allreduce(x, "generalized", "fp32", "sum", 0, ex, batch=B, collective="all_gather")
+        assert np.array_equal(bits(got.reshape(P, B, n)), bits(sch.all_gather(xb, "generalized", "fp32"))), ex
+        for algo, knob, op in (("rd", 0, "avg"), ("chain", 4, "sum"), ("generalized", 1, "avg")):
+            got = gpu_allreduce(x, algo, "fp32", op, knob, ex, batch=B).reshape(P, B, n)
+            want = oracle.allreduce(xb, algo, "fp32", op, knob=knob, n=n)
+            assert np.array_equal(bits(got), bits(want)), (algo, op, ex)
+
+
+def test_auto_halves_run_the_oracle_choice():
+    import allreduce_schedule_algorithms_amd as A
+    from oracle import cost, schedules as sch
+    m = A.ar_get_cost_model()
+    for P in (5, 8):
+        for n in (64, 1 << 16):
+            x = inputs.make("fp32", P, n, seed=P * n)
+            own = half_owner(n, P)
+            a, r, _ = cost.select(P, n, "fp32", m["alpha"], m["beta"], m["gamma"], m["form"], coll="reduce_scatter")
+            got = gpu_allreduce(x, "auto", "fp32", "sum", 0, "fused", collective="reduce_scatter")
+            assert np.array_equal(bits(got[own, np.arange(n)]), bits(sch.reduce_scatter(x, a, "fp32", "sum"))), (P, n, a)
