@@ -297,12 +297,22 @@ FAKE = [0x1000 * (i + 1) for i in range(256)]
     (dict(algo="generalized", knob=-2), "knob"), (dict(algo="generalized_xor", P=6), "power of two"),
     (dict(algo="ahc", groups=[2, 2]), "sum to P"), (dict(algo="ahc", groups=None), "group"),
     (dict(algo="ahc", groups=[5, 0]), "group sizes"), (dict(exec=9), "exec"),
+    (dict(collective=3), "collective"), (dict(op="avg", dtype="int32"), "avg"),
+    (dict(algo="rd", collective="reduce_scatter"), "reduce-scatter"),
+    (dict(algo="rh_rd", P=6, collective="all_gather"), "power of two"),
+    (dict(algo="generalized", knob=1, collective="reduce_scatter"), "r = 0"),
+    (dict(algo="ring", steps=4), "steps"), (dict(algo="generalized", steps=2), "steps"),
+    (dict(algo="generalized", steps=5), "steps"), (dict(algo="generalized", groups=[2, 2]), "product"),
+    (dict(algo="chain", knob=0), "pieces"), (dict(algo="chain", knob=5000), "pieces"),
 ])
 def test_invalid_arguments_rejected_before_device_work(kw, match):
-    args = dict(P=5, n=100, dtype="fp32", op="sum", algo="ring", knob=0, exec="fused", groups=None)
+    args = dict(P=5, n=100, dtype="fp32", op="sum", algo="ring", knob=0, exec="fused", groups=None,
+                collective="allreduce", steps=0)
     args.update(kw)
     call = A.make_call(args["P"], args["n"], args["dtype"], args["op"], args["algo"], args["knob"],
-                       args["exec"], groups=args["groups"])
+                       args["exec"], groups=args["groups"], steps=args["steps"])
+    call.collective = args["collective"] if isinstance(args["collective"], int) else \
+        int(A.COLLECTIVES[args["collective"]])
     with pytest.raises(A.ArError, match=match) as e:
         A.ar_allreduce_ex(FAKE[: max(args["P"], 1)], call)
     assert e.value.status == A.Status.AR_INVALID_ARGUMENT
@@ -315,6 +325,20 @@ def test_null_and_duplicate_buffers_rejected():
         A.ar_allreduce([FAKE[0], FAKE[1], FAKE[0]], 3, 10, "fp32", "sum", "ring")
     with pytest.raises(A.ArError, match="ar_allreduce_ex"):
         A.ar_allreduce(FAKE[:3], 3, 10, "fp32", "sum", "ahc")
+
+
+def test_half_entry_points_validate_before_device_work():
+    with pytest.raises(A.ArError, match="reduce-scatter"):
+        A.ar_reduce_scatter(FAKE[:5], 5, 100, "fp32", "sum", "binomial")
+    with pytest.raises(A.ArError, match="AHC"):
+        A.ar_all_gather(FAKE[:5], 5, 100, "fp32", "ahc")
+    with pytest.raises(A.ArError, match="share"):
+        A.ar_all_gather([FAKE[0], FAKE[0]], 2, 100, "fp32", "ring")
+    # nothing to move: valid, no device work
+    A.ar_reduce_scatter(FAKE[:1], 1, 100, "bf16", "avg", "ring")
+    A.ar_all_gather(FAKE[:4], 4, 0, "int32", "generalized")
+    with pytest.raises(A.ArError, match="NULL"):
+        A._ar._check(A._ar.lib.ar_table_check_ex(None, None, 0, None))
 
 
 def test_trivial_calls_do_no_device_work():
