@@ -403,3 +403,28 @@ def test_auto_halves_run_the_oracle_choice():
             a, r, _ = cost.select(P, n, "fp32", m["alpha"], m["beta"], m["gamma"], m["form"], coll="reduce_scatter")
             got = gpu_allreduce(x, "auto", "fp32", "sum", 0, "fused", collective="reduce_scatter")
             assert np.array_equal(bits(got[own, np.arange(n)]), bits(sch.reduce_scatter(x, a, "fp32", "sum"))), (P, n, a)
+
+
+# --------------------------------------------------------------------------
+# seeded random sweep over every option (the cases the CPU sweep draws)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(4))
+def test_random_cases_on_gpu(seed):
+    import allreduce_schedule_algorithms_amd as A
+    from test_random_cpu import draw, oracle_result
+    rng = np.random.default_rng(2000 + seed)
+    for _ in range(25):
+        coll, algo, knob, steps, factors, groups, P, n, batch, dtype, op = draw(rng)
+        x = inputs.make(dtype, P, n * batch, seed=int(rng.integers(1 << 30)))
+        want = oracle_result(coll, algo, knob, steps, factors, groups, P, n, batch, dtype, op, x)
+        g = groups if algo == "ahc" else factors
+        info = A.ar_schedule_build(A.make_call(P, n, dtype, op, algo, knob, batch=batch, groups=g,
+                                               collective=coll, steps=steps)).info()
+        case = (coll, algo, knob, steps, factors, groups, P, n, batch, dtype, op)
+        for ex in ("fused", "literal"):
+            if ex == "fused" and info.max_trees > 8:
+                continue
+            got = gpu_allreduce(x, algo, dtype, op, knob, ex, g, batch, collective=coll, steps=steps)
+            if coll == "reduce_scatter":
+                got = got.reshape(P, batch, n)[half_owner(n, P), :, np.arange(n)].T
+            assert np.array_equal(bits(got), bits(want)), case + (ex,)
