@@ -151,6 +151,10 @@ hipError_t upload(DevBuf& b, const std::vector<T>& v) {
 
 int vec_width(int dtype) { return dtype == D_BF16 ? 8 : 4; }
 
+// Fused programs above this size run with one contiguous run of items per XCD
+// (measured: AHC's 300 KB program +3.4%; programs of a few hundred bytes lose 2-6%).
+constexpr size_t kXcdProgramBytes = 64 * 1024;
+
 // Build the fused or literal item tables for one alignment mode.
 RunResult build_items(Plan& pl, bool vec) {
   const Schedule& s = *pl.s;
@@ -400,6 +404,7 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
     if (pl->nitems[mode] == 0) return mark_empty();
     const Item* items = reinterpret_cast<const Item*>(pl->items[mode].p);
     const int32_t* prog = reinterpret_cast<const int32_t*>(pl->prog.p);
+    ptrs.xcd = pl->s->prog.size() * sizeof(int32_t) > kXcdProgramBytes ? 1 : 0;
     AR_DISPATCH(spec.dtype, spec.op,
                 (e = launch_fused_t<DT, OPK>(pl->D, pl->s->max_trees > 1 ? kMaxFusedTrees : 1, spec.P,
                                              pl->s->max_leaves, pl->nitems[mode], ptrs, items, prog, st, ev)));

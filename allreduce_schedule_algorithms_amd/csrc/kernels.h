@@ -15,8 +15,21 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct RankPtrs {
   void* p[kMaxRanks];
-  float div;  // O_AVG: the complete sum is divided by this (P), once, before the store
+  float div;    // O_AVG: the complete sum is divided by this (P), once, before the store
+  int32_t xcd;  // fused replay: give each XCD a contiguous run of work items (item_index)
 };
+
+// MI355X dispatches workgroup b to XCD b % 8, and each XCD has its own L2.
+// With a large fused program (many ranges with long programs, as in AHC), a
+// contiguous run of items per XCD keeps each XCD's share of the program
+// words in its caches; with small programs the plain order streams better.
+constexpr unsigned kXcds = 8;
+__device__ __forceinline__ unsigned item_index(int32_t xcd) {
+  if (!xcd) return blockIdx.x;
+  const unsigned nb = gridDim.x, per = (nb + kXcds - 1) / kXcds, x = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const unsigned full = nb % kXcds == 0 ? kXcds : nb % kXcds;  // XCDs that receive 'per' workgroups
+  return x < full ? x * per + slot : full * per + (x - full) * (per - 1) + slot;
+}
 
 // Work item: `count` > 0 is a run of vectors, < 0 a run of -count single elements;
 // `start` is the element offset of its first element in every rank buffer.
@@ -331,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* _
   constexpr int V = TT<DT>::V;
   constexpr int M = fused_m<DT, D, TM>();
   constexpr bool NT = TM == 1;  // several trees re-read their leaves: keep them cacheable
-  const Item it = items[blockIdx.x];
+  const Item it = items[item_index(ptrs.xcd)];
   const int32_t* w = prog + it.tag;
   if (it.count > 0) {
     for_fragments<M>(it, V, [&](int64_t e, const bool (&ok)[M]) {
@@ -355,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_staged(RankPtrs ptrs, const 
                                                            const int32_t* __restrict__ prog, int P) {
   constexpr int V = TT<DT>::V;
   extern __shared__ u32x4 stage[];
-  const Item it = items[blockIdx.x];
+  const Item it = items[item_index(ptrs.xcd)];
   const int32_t* w = prog + it.tag;
   if (it.count > 0) {
     for_fragments<1>(it, V, [&](int64_t e, const bool (&ok)[1]) {
