@@ -119,10 +119,10 @@ typedef enum {
 #define AR_KNOB_AUTO (-1)
 
 /* Execution of a schedule on the GPU.
- *  AR_EXEC_FUSED    default. AR_DIRECT runs the one-pass direct kernel (read all P, combine
- *                   left to right, write all P); every other schedule runs its fused
- *                   per-element replay: one launch evaluates, per element, exactly the
- *                   combination trees the step list builds, in registers.
+ *  AR_EXEC_FUSED    default. An AR_DIRECT Allreduce runs the one-pass direct kernel (read all
+ *                   P, combine left to right, write all P); every other schedule and collective
+ *                   runs its fused per-element replay: one launch evaluates, per element,
+ *                   exactly the combination trees the step list builds, in registers.
  *  AR_EXEC_LITERAL  one launch per schedule step (chunk REDUCE / COPY kernels), partials
  *                   through HBM workspace slots; a last launch moves results that ended in
  *                   a workspace slot into the caller's buffer.
@@ -265,7 +265,9 @@ typedef struct ar_cost {
   double closed_form_seconds;
   double literal_hbm_bytes;  /* bytes AR_EXEC_LITERAL moves through HBM per call */
   double fused_hbm_bytes;    /* bytes the fused replay requests per call */
-  double essential_bytes;    /* 2 P n batch elt: every input read once, every output written once */
+  double essential_bytes;    /* every input read once, every output written once, per call: 2 P n
+                                batch elt (Allreduce), (P + 1) n batch elt (reduce-scatter),
+                                P n batch elt (all-gather) */
 } ar_cost;
 ar_status ar_cost_report(const ar_schedule* s, double alpha, double beta, double gamma,
                          ar_cost* out);
