@@ -189,6 +189,8 @@ def _check(st: int):
 
 
 def _ptrs(bufs):
+    if isinstance(bufs, C.Array):  # already marshalled (c_void_p * P), e.g. reused across calls
+        return bufs
     ptrs = [b if isinstance(b, int) else b.data_ptr() for b in bufs]
     return (C.c_void_p * max(len(ptrs), 1))(*ptrs)
 

@@ -95,12 +95,12 @@ bool to_spec(const ar_call* c, ar::Spec* s, std::string* err) {
 
 ar_status check_bufs(void* const* bufs, int P) {
   if (!bufs) return fail(AR_INVALID_ARGUMENT, "bufs is NULL");
-  std::vector<uintptr_t> v(P);
+  uintptr_t v[AR_MAX_RANKS];  // P was validated: 1..AR_MAX_RANKS
   for (int p = 0; p < P; ++p) {
     if (!bufs[p]) return fail(AR_INVALID_ARGUMENT, "bufs[" + std::to_string(p) + "] is NULL");
     v[p] = reinterpret_cast<uintptr_t>(bufs[p]);
   }
-  std::sort(v.begin(), v.end());
+  std::sort(v, v + P);
   for (int p = 1; p < P; ++p)
     if (v[p] == v[p - 1]) return fail(AR_INVALID_ARGUMENT, "two ranks share one buffer");
   return AR_OK;

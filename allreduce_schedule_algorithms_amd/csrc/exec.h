@@ -3,6 +3,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <memory>
 #include <string>
 
 #include "sched.h"
@@ -26,6 +27,6 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
 RunResult literal_workspace_bytes(const Spec& spec, size_t* bytes);
 
 // Cached host schedule for a spec (shared with the executor's plan cache).
-const Schedule* cached_schedule(const Spec& spec, std::string* err);
+std::shared_ptr<const Schedule> cached_schedule(const Spec& spec, std::string* err);
 
 }  // namespace ar

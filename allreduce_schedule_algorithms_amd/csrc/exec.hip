@@ -51,22 +51,23 @@ std::string spec_key(const Spec& s) {
   return k.str();
 }
 
-std::map<std::string, std::unique_ptr<Schedule>>& sched_cache() {
-  static std::map<std::string, std::unique_ptr<Schedule>> m;
+// Schedules are shared: a plan keeps its schedule alive even after the
+// schedule cache has been cleared.
+std::map<std::string, std::shared_ptr<const Schedule>>& sched_cache() {
+  static std::map<std::string, std::shared_ptr<const Schedule>> m;
   return m;
 }
 
-const Schedule* schedule_locked(const Spec& spec, std::string* err) {
+std::shared_ptr<const Schedule> schedule_locked(const Spec& spec, std::string* err) {
   auto& m = sched_cache();
   std::string k = spec_key(spec);
   auto it = m.find(k);
-  if (it != m.end()) return it->second.get();
+  if (it != m.end()) return it->second;
   if (m.size() > 512) m.clear();
-  Schedule* s = build_schedule(spec, err);
+  std::shared_ptr<const Schedule> s(build_schedule(spec, err));
   if (!s) return nullptr;
-  auto* raw = s;
-  m.emplace(k, std::unique_ptr<Schedule>(s));
-  return raw;
+  m.emplace(k, s);
+  return s;
 }
 
 int64_t env_int(const char* name, int64_t dflt) {
@@ -104,7 +105,7 @@ struct DevBuf {
 };
 
 struct Plan {
-  const Schedule* s = nullptr;
+  std::shared_ptr<const Schedule> s;
   int exec = E_FUSED;
   int D = 2;
   DevBuf prog;
@@ -253,13 +254,46 @@ RunResult build_items(Plan& pl, bool vec) {
   return RunResult{};
 }
 
+bool same_spec(const Spec& a, const Spec& b) {
+  return a.P == b.P && a.n == b.n && a.batch == b.batch && a.dtype == b.dtype && a.op == b.op && a.algo == b.algo &&
+         a.knob == b.knob && a.coll == b.coll && a.steps == b.steps && a.groups == b.groups;
+}
+
+// Repeated calls with one spec (a training loop's buckets, the unbatched
+// small-message case) skip building the cache key: the last plan found on
+// this thread is reused while the plan cache has not been cleared since.
+uint64_t g_plan_generation = 0;  // bumped whenever the plan cache is cleared (under g_mu)
+struct LastPlan {
+  Spec spec;
+  int exec = -1, device = -1;
+  uint64_t generation = 0;
+  Plan* plan = nullptr;
+};
+thread_local LastPlan t_last;
+
 RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
+  if (t_last.plan && t_last.generation == g_plan_generation && t_last.exec == exec && t_last.device == device &&
+      same_spec(t_last.spec, spec)) {
+    *out = t_last.plan;
+    return RunResult{};
+  }
+  auto remember = [&](Plan* p) {
+    t_last.spec = spec;
+    t_last.exec = exec;
+    t_last.device = device;
+    t_last.generation = g_plan_generation;
+    t_last.plan = p;
+  };
   std::string k = spec_key(spec) + "|" + std::to_string(exec) + "|" + std::to_string(device);
   auto& m = plan_cache();
   auto it = m.find(k);
-  if (it != m.end()) { *out = it->second.get(); return RunResult{}; }
+  if (it != m.end()) {
+    *out = it->second.get();
+    remember(*out);
+    return RunResult{};
+  }
   std::string err;
-  const Schedule* s = schedule_locked(spec, &err);
+  std::shared_ptr<const Schedule> s = schedule_locked(spec, &err);
   if (!s) { RunResult r; r.status = 1; r.message = err; return r; }
   auto pl = std::make_unique<Plan>();
   pl->s = s;
@@ -271,9 +305,11 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
   if (m.size() > 256) {
     (void)hipDeviceSynchronize();
     m.clear();
+    ++g_plan_generation;
   }
   *out = pl.get();
   m.emplace(k, std::move(pl));
+  remember(*out);
   return RunResult{};
 }
 
@@ -292,14 +328,14 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
 
 }  // namespace
 
-const Schedule* cached_schedule(const Spec& spec, std::string* err) {
+std::shared_ptr<const Schedule> cached_schedule(const Spec& spec, std::string* err) {
   std::lock_guard<std::mutex> lk(g_mu);
   return schedule_locked(spec, err);
 }
 
 RunResult literal_workspace_bytes(const Spec& spec, size_t* bytes) {
   std::string err;
-  const Schedule* s = cached_schedule(spec, &err);
+  std::shared_ptr<const Schedule> s = cached_schedule(spec, &err);
   if (!s) { RunResult r; r.status = 1; r.message = err; return r; }
   int64_t slot = (spec.n * spec.batch * int64_t(acc_bytes(spec.dtype)) + 255) / 256 * 256;
   *bytes = size_t(s->nslots - 1) * size_t(spec.P) * size_t(slot);

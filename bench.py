@@ -68,7 +68,8 @@ WORKLOADS = {
         desc="24 ranks x 10^4 instances x 106 fp32 U(-1,1), seed 0",
         P=24, n=106, dtype="fp32", batch=10_000, groups=None,
         headline=("rd", 0, "fused"),
-        others=[("binomial", 0, "fused"), ("direct", 0, "fused"), ("rd", 0, "literal"), ("binomial", 0, "literal")]),
+        others=[("binomial", 0, "fused"), ("direct", 0, "fused"), ("generalized", 5, "fused"),
+                ("rd", 0, "literal"), ("binomial", 0, "literal"), ("generalized", 5, "literal")]),
     "ring_int32": dict(
         desc="5 ranks x 4096 int32 U[-2^20, 2^20], seed 0",
         P=5, n=4096, dtype="int32", batch=1, groups=None,
@@ -192,6 +193,34 @@ class Runner:
             out.update(kernel_ms=kmean, kernel_GBps=essential / (kmean * 1e-3) / 1e9)
         return out
 
+    def unbatched(self, algo, knob, calls):
+        """``calls`` separate one-instance Allreduces (instance b at offset b * n
+        of every rank's buffer), back to back on one stream: the per-call time
+        is the library's per-call alpha on this device (host + launch +
+        kernel)."""
+        import torch
+        wl = self.wl
+        st = self.stream
+        elt = ELT[wl["dtype"]]
+        call = self.A.make_call(wl["P"], wl["n"], wl["dtype"], "sum", algo, knob, "fused", 1, None)
+        calls = min(calls, wl["batch"])
+        ptr_sets = [[p + b * wl["n"] * elt for p in self.ptrs] for b in range(calls)]
+        with torch.cuda.stream(st):
+            self.work.copy_(self.pristine)
+        for b in range(min(calls, 50)):  # warm: plans built, caches filled
+            self.A.ar_allreduce_ex(ptr_sets[b], call, st)
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record(st)
+        for b in range(calls):
+            self.A.ar_allreduce_ex(ptr_sets[b], call, st)
+        z.record(st)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return {"calls": calls, "us_per_call": round(a.elapsed_time(z) * 1e3 / calls, 3),
+                "wall_us_per_call": round(wall * 1e6 / calls, 3), "schedule": f"{algo}/r{knob}/fused"}
+
     def copy_ceiling(self, gib=2):
         import torch
         a = torch.empty(gib << 28, dtype=torch.float32, device="cuda")
@@ -251,7 +280,62 @@ def cpu_baseline(wl, x, budget_s=12.0):
             break
     mean = statistics.fmean(times)
     return {"value": round(ess / mean / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{sample}; {algo} replay, {len(times)} runs, mean {mean:.3f} s (NumPy, one thread)"}
+            "sample": f"{sample}; {algo} replay, {len(times)} runs, mean {mean:.3f} s (NumPy, one thread); "
+                      f"host {host_cpu()}",
+            "brute_force": brute_force_all_cores(xs, wl["dtype"])}
+
+
+def host_cpu():
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {os.cpu_count()} logical CPUs"
+
+
+def brute_force_all_cores(xs, dtype, budget_s=4.0):
+    """The plain elementwise reduction of all ranks (no schedule), in threads
+    over element ranges; NumPy releases the GIL in the adds. Same sample as the
+    oracle leg; bf16 is widened to fp32 first, int32 sums wrap."""
+    import concurrent.futures as cf
+
+    import numpy as np
+    x = np.asarray(xs)
+    P = x.shape[0]
+    flat = x.reshape(P, -1)
+    if dtype == "bf16":
+        flat = (flat.astype(np.uint32) << 16).view(np.float32)
+    elif dtype == "int32":
+        flat = flat.view(np.uint32)
+    m = flat.shape[1]
+    threads = max(1, min(16, os.cpu_count() or 1))
+    cuts = np.linspace(0, m, threads + 1).astype(np.int64)
+
+    def part(i):
+        lo, hi = cuts[i], cuts[i + 1]
+        acc = flat[0, lo:hi].copy()
+        for p in range(1, P):
+            acc += flat[p, lo:hi]
+        return acc
+
+    times = []
+    t_start = time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        while True:
+            t0 = time.perf_counter()
+            list(ex.map(part, range(threads)))
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start > budget_s or len(times) >= 20:
+                break
+    mean = statistics.fmean(times)
+    ess = 2.0 * x.size * x.dtype.itemsize  # read every input, write one result per rank
+    return {"value": round(ess / mean / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "brute-force elementwise reduction (no schedule)"}
 
 
 def model_fit(args):
@@ -484,6 +568,9 @@ def main():
             if k in v:
                 v[k] = round(v[k], 5 if "ms" in k else 2)
     ceiling = r.copy_ceiling()
+    unbatched = None
+    if wl["batch"] > 1 and not args.schedule and not args.headline_only:
+        unbatched = r.unbatched(algo, knob, wl["batch"])
 
     # model bytes from the library's cost walk (fused / literal HBM bytes per call)
     import allreduce_schedule_algorithms_amd as A
@@ -525,6 +612,8 @@ def main():
         "cpu_baseline": cpu,
         "schedules": schedules,
     }
+    if unbatched:
+        line["unbatched"] = unbatched
     print(json.dumps(line))
 
 

@@ -428,3 +428,17 @@ def test_random_cases_on_gpu(seed):
             if coll == "reduce_scatter":
                 got = got.reshape(P, batch, n)[half_owner(n, P), :, np.arange(n)].T
             assert np.array_equal(bits(got), bits(want)), case + (ex,)
+
+
+def test_plans_survive_a_cleared_schedule_cache():
+    # a plan built on the first call must stay valid after other specs have
+    # pushed its schedule out of the schedule cache (more than 512 of them)
+    import allreduce_schedule_algorithms_amd as A
+    x = inputs.make("fp32", 5, 1000, seed=3)
+    want = oracle.allreduce(x, "ring", "fp32", "sum")
+    for ex in ("fused", "literal"):
+        assert np.array_equal(bits(gpu_allreduce(x, "ring", "fp32", "sum", 0, ex)), bits(want))
+    for n in range(1, 530):
+        A.ar_workspace_bytes(A.make_call(3, n, "fp32", "sum", "ring", 0, "literal"))
+    for ex in ("fused", "literal"):
+        assert np.array_equal(bits(gpu_allreduce(x, "ring", "fp32", "sum", 0, ex)), bits(want))
