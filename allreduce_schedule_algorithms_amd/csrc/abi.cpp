@@ -239,8 +239,10 @@ ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes) {
   if (!bytes) return fail(AR_INVALID_ARGUMENT, "bytes is NULL");
   if (!to_spec(call, &spec, &err)) return fail(AR_INVALID_ARGUMENT, err);
   *bytes = 0;
-  if (call->exec != AR_EXEC_LITERAL || spec.P <= 1 || spec.n == 0) return AR_OK;
-  ar::RunResult r = ar::literal_workspace_bytes(spec, bytes);
+  if ((call->exec == AR_EXEC_FUSED && spec.algo == AR_DIRECT && spec.coll == AR_ALLREDUCE) || spec.P <= 1 ||
+      spec.n == 0)
+    return AR_OK;
+  ar::RunResult r = ar::workspace_bytes(spec, call->exec == AR_EXEC_LITERAL ? 1 : 0, bytes);
   if (r.status) return fail(ar_status(r.status), r.message);
   return AR_OK;
 }

@@ -23,8 +23,10 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
                         size_t workspace_bytes, void* stream, void* start_event = nullptr,
                         void* stop_event = nullptr);
 
-// Workspace an AR_EXEC_LITERAL call needs for this spec (builds the schedule).
-RunResult literal_workspace_bytes(const Spec& spec, size_t* bytes);
+// Workspace a call needs (builds the schedule): the literal executor's slots
+// for AR_EXEC_LITERAL, and for fused calls whose replay does not fit (they run
+// the literal steps); 0 otherwise.
+RunResult workspace_bytes(const Spec& spec, int exec, size_t* bytes);
 
 // Cached host schedule for a spec (shared with the executor's plan cache).
 std::shared_ptr<const Schedule> cached_schedule(const Spec& spec, std::string* err);

@@ -333,10 +333,19 @@ std::shared_ptr<const Schedule> cached_schedule(const Spec& spec, std::string* e
   return schedule_locked(spec, err);
 }
 
-RunResult literal_workspace_bytes(const Spec& spec, size_t* bytes) {
+// Whether the fused replay can run a schedule: at most kMaxFusedTrees result
+// trees per range, and several trees only with a stack of depth <= 8.
+static bool fused_runs(const Schedule& s) {
+  const int D = s.max_need <= 2 ? 2 : s.max_need <= 4 ? 4 : s.max_need <= 8 ? 8 : 16;
+  return s.max_trees <= kMaxFusedTrees && !(s.max_trees > 1 && D > 8);
+}
+
+RunResult workspace_bytes(const Spec& spec, int exec, size_t* bytes) {
   std::string err;
   std::shared_ptr<const Schedule> s = cached_schedule(spec, &err);
   if (!s) { RunResult r; r.status = 1; r.message = err; return r; }
+  *bytes = 0;
+  if (exec != E_LITERAL && s->fused_ok && fused_runs(*s)) return RunResult{};  // the replay keeps partials in registers
   int64_t slot = (spec.n * spec.batch * int64_t(acc_bytes(spec.dtype)) + 255) / 256 * 256;
   *bytes = size_t(s->nslots - 1) * size_t(spec.P) * size_t(slot);
   return RunResult{};
@@ -380,20 +389,14 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
     std::lock_guard<std::mutex> lk(g_mu);
     res = get_plan(spec, exec == E_LITERAL ? E_LITERAL : E_FUSED, device, &pl);
     if (res.status) return res;
+    if (pl->exec != E_LITERAL && (!pl->s->fused_ok || !fused_runs(*pl->s))) {
+      // no replay program, or more result trees per range than the replay
+      // keeps in registers: the step-by-step kernels compute the same bits
+      res = get_plan(spec, E_LITERAL, device, &pl);
+      if (res.status) return res;
+    }
     const int mode = vec ? 0 : 1;
     if (!pl->built[mode]) {
-      if (pl->exec != E_LITERAL && !pl->s->fused_ok) {
-        res.status = 5;
-        res.message = "fused replay program unavailable: " + pl->s->fused_error;
-        return res;
-      }
-      if (pl->exec != E_LITERAL && (pl->s->max_trees > kMaxFusedTrees || (pl->s->max_trees > 1 && pl->D > 8))) {
-        res.status = 2;
-        res.message = "fused replay keeps at most " + std::to_string(kMaxFusedTrees) +
-                      " distinct result trees of stack depth <= 8 per range in registers; this schedule has " +
-                      std::to_string(pl->s->max_trees) + " (use AR_EXEC_LITERAL)";
-        return res;
-      }
       res = build_items(*pl, vec);
       if (res.status) return res;
     }

@@ -122,7 +122,11 @@ typedef enum {
  *  AR_EXEC_FUSED    default. An AR_DIRECT Allreduce runs the one-pass direct kernel (read all
  *                   P, combine left to right, write all P); every other schedule and collective
  *                   runs its fused per-element replay: one launch evaluates, per element,
- *                   exactly the combination trees the step list builds, in registers.
+ *                   exactly the combination trees the step list builds, in registers. A
+ *                   schedule the replay cannot hold (ranges with more than 8 result trees,
+ *                   several trees with a stack deeper than 8, or a rounded partial combined
+ *                   again) runs the literal steps instead, with the same bits, and then
+ *                   uses a workspace like AR_EXEC_LITERAL (ar_workspace_bytes says how much).
  *  AR_EXEC_LITERAL  one launch per schedule step (chunk REDUCE / COPY kernels), partials
  *                   through HBM workspace slots; a last launch moves results that ended in
  *                   a workspace slot into the caller's buffer.
@@ -153,7 +157,8 @@ typedef struct ar_call {
                               Other factorizations change which ranks talk in a step; a step can
                               then have a rank talk to several peers (ar_schedule_info.single_port).
                               Ignored by the other algorithms. */
-  void* workspace;         /* AR_EXEC_LITERAL: device scratch of ar_workspace_bytes() bytes, or
+  void* workspace;         /* calls that run the literal steps: device scratch of
+                              ar_workspace_bytes() bytes, or
                               NULL to let the library allocate and cache one per device */
   size_t workspace_bytes;
   void* start_event;       /* optional hipEvent_t (created by the caller): recorded when the
@@ -184,7 +189,9 @@ ar_status ar_all_gather(void* const* bufs, int32_t P, int64_t n, int32_t dtype, 
 /* The collective of call->collective (an Allreduce by default) with every option of ar_call. */
 ar_status ar_allreduce_ex(void* const* bufs, const ar_call* call, void* stream);
 
-/* Workspace bytes an AR_EXEC_LITERAL call needs (0 for fused execution). */
+/* Workspace bytes a call needs: the literal workspace slots for AR_EXEC_LITERAL, and for
+ * AR_EXEC_FUSED calls whose schedule runs the literal steps (see ar_exec); 0 otherwise.
+ * Builds (and caches) the schedule; returns its validation error for invalid calls. */
 ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes);
 
 /* ---- schedules on the host (no GPU needed) ---- */

@@ -12,7 +12,7 @@ import pytest
 import oracle
 from oracle import numerics as nu
 from synth import inputs
-from gpu_util import bits, gpu_allreduce
+from gpu_util import bits, from_device, gpu_allreduce, to_device, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -303,12 +303,38 @@ def test_generalized_more_steps_small():
                     for n in (37, 4099):
                         x = inputs.make(dtype, P, n, seed=S * 13 + r + n)
                         want = oracle.allreduce(x, "generalized", dtype, "sum", knob=r, steps=S)
-                        info = A.ar_schedule_build(A.make_call(P, n, dtype, "sum", "generalized", r, steps=S)).info()
                         for ex in ("fused", "literal"):
-                            if ex == "fused" and info.max_trees > 8:
-                                continue  # more result trees per range than the fused replay keeps
                             got = gpu_allreduce(x, "generalized", dtype, "sum", r, ex, steps=S)
                             assert np.array_equal(bits(got), bits(want)), (P, S, r, dtype, n, ex)
+
+
+def test_fused_falls_back_to_literal_steps():
+    # 13 ranks, 4 steps, r = 4: ranges need more result trees than the fused
+    # replay keeps, so a fused call runs the literal steps (same bits) and takes
+    # the caller's workspace when one is given
+    import allreduce_schedule_algorithms_amd as A
+    torch = torch_mod()
+    P, n = 13, 4099
+    x = inputs.make("fp32", P, n, seed=41)
+    want = oracle.allreduce(x, "generalized", "fp32", "sum", knob=4, steps=4)
+    call = A.make_call(P, n, "fp32", "sum", "generalized", 4, steps=4)
+    assert A.ar_schedule_build(call).info().max_trees > 8
+    assert np.array_equal(bits(gpu_allreduce(x, "generalized", "fp32", "sum", 4, "fused", steps=4)), bits(want))
+    need = A.ar_workspace_bytes(call)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    bufs, keep = to_device(x, "fp32")
+    short = A.make_call(P, n, "fp32", "sum", "generalized", 4, steps=4, workspace=ws.data_ptr(),
+                        workspace_bytes=need - 1)
+    with pytest.raises(A.ArError) as e:
+        A.ar_allreduce_ex([b.data_ptr() for b in bufs], short, torch.cuda.current_stream())
+    assert e.value.status == A.Status.AR_WORKSPACE_TOO_SMALL
+    exact = A.make_call(P, n, "fp32", "sum", "generalized", 4, steps=4, workspace=ws.data_ptr(),
+                        workspace_bytes=need)
+    A.ar_allreduce_ex([b.data_ptr() for b in bufs], exact, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(from_device(bufs, "fp32")), bits(want))
+    del keep
 
 
 def test_generalized_more_steps_full_size_prime_ranks():
@@ -336,11 +362,7 @@ def test_generalized_product_groups():
                     for n in (37, 4099):
                         x = inputs.make(dtype, P, n, seed=P + r + n)
                         want = oracle.allreduce(x, "generalized", dtype, "sum", knob=r, factors=f)
-                        info = A.ar_schedule_build(A.make_call(P, n, dtype, "sum", "generalized", r,
-                                                               groups=list(f))).info()
                         for ex in ("fused", "literal"):
-                            if ex == "fused" and info.max_trees > 8:
-                                continue
                             got = gpu_allreduce(x, "generalized", dtype, "sum", r, ex, groups=list(f))
                             assert np.array_equal(bits(got), bits(want)), (P, f, r, dtype, n, ex)
 
@@ -418,12 +440,8 @@ def test_random_cases_on_gpu(seed):
         x = inputs.make(dtype, P, n * batch, seed=int(rng.integers(1 << 30)))
         want = oracle_result(coll, algo, knob, steps, factors, groups, P, n, batch, dtype, op, x)
         g = groups if algo == "ahc" else factors
-        info = A.ar_schedule_build(A.make_call(P, n, dtype, op, algo, knob, batch=batch, groups=g,
-                                               collective=coll, steps=steps)).info()
         case = (coll, algo, knob, steps, factors, groups, P, n, batch, dtype, op)
         for ex in ("fused", "literal"):
-            if ex == "fused" and info.max_trees > 8:
-                continue
             got = gpu_allreduce(x, algo, dtype, op, knob, ex, g, batch, collective=coll, steps=steps)
             if coll == "reduce_scatter":
                 got = got.reshape(P, batch, n)[half_owner(n, P), :, np.arange(n)].T

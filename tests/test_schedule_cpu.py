@@ -352,6 +352,12 @@ def test_workspace_query():
     assert A.ar_workspace_bytes(lit) == 8 * 1024 * 4  # one fp32 slot per rank
     assert A.ar_workspace_bytes(A.make_call(8, 1024, "bf16", "sum", "ring")) == 0
     assert A.ar_workspace_bytes(A.make_call(8, 1024, "fp32", "sum", "ring", exec="literal")) == 0
+    # a fused call whose ranges need more result trees than the replay keeps
+    # runs the literal steps and needs their workspace
+    big = A.make_call(13, 1000, "fp32", "sum", "generalized", 4, steps=4)
+    assert A.ar_schedule_build(big).info().max_trees > 8
+    lit = A.make_call(13, 1000, "fp32", "sum", "generalized", 4, "literal", steps=4)
+    assert A.ar_workspace_bytes(big) == A.ar_workspace_bytes(lit) > 0
 
 
 def test_status_strings():
