@@ -116,6 +116,50 @@ def essential_bytes(wl, coll="allreduce"):
     return {"allreduce": 2.0 * pn, "reduce_scatter": pn + n1, "all_gather": pn}[coll]
 
 
+class KernelEvents:
+    """Raw HIP timing events created with hipEventDisableSystemFence, for the
+    library's ar_call.start_event / stop_event. torch.cuda.Event has no such
+    flag; its default events add a system-scope release when the stop event is
+    recorded (about 2 us on a 13 us kernel), which a kernel's device time does
+    not include and rocprofv3's kernel trace does not show."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes as C
+
+        import torch  # noqa: F401  (loads the HIP runtime the library shares)
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        self.C = C
+        self.hip = C.CDLL(path or "libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self):
+        e = self.C.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.C.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        f = self.C.c_float()
+        rc = self.hip.hipEventElapsedTime(self.C.byref(f), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return f.value
+
+    def destroy(self, evs):
+        for a, b in evs:
+            self.hip.hipEventDestroy(a)
+            self.hip.hipEventDestroy(b)
+
+
 class Runner:
     def __init__(self, wl, x):
         import torch
@@ -129,6 +173,7 @@ class Runner:
         self.flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
         self.ptrs = [self.work[p].data_ptr() for p in range(wl["P"])]
         self.essential = essential_bytes(wl)
+        self.kernel_events = KernelEvents()
 
     def call_for(self, algo, knob, ex, start_event=None, stop_event=None, coll="allreduce", op="sum", rsteps=0,
                  factors=None):
@@ -145,7 +190,8 @@ class Runner:
         (what a caller waits for, launch latency included): value, ms_per_step.
         Pass 2 repeats the steps with ar_call.start_event / stop_event, which the
         library records at the start and end of its own kernels: the kernels'
-        device time, the figure rocprofv3's kernel trace reports.
+        device time, the figure rocprofv3's kernel trace reports. These events
+        carry no system-scope fence (KernelEvents).
         """
         import torch
         st = self.stream
@@ -182,14 +228,16 @@ class Runner:
         out = dict(ms=mean, ms_median=statistics.median(ms), ms_min=min(ms), wall_ms_per_step=1e3 * wall / steps,
                    GBps=essential / (mean * 1e-3) / 1e9)
         if kernel_pass:
-            kern_evs = [(ev(), ev()) for _ in range(steps)]
+            kev = self.kernel_events
+            kern_evs = [(kev.create(), kev.create()) for _ in range(steps)]
             calls = [self.call_for(algo, knob, ex, a, b, coll, op, rsteps, factors) for a, b in kern_evs]
             torch.cuda.synchronize()
             for k in range(steps):
                 prep()
                 self.A.ar_allreduce_ex(self.ptrs, calls[k], st)
             torch.cuda.synchronize()
-            kmean = statistics.fmean([a.elapsed_time(b) for a, b in kern_evs])
+            kmean = statistics.fmean([kev.elapsed_ms(a, b) for a, b in kern_evs])
+            kev.destroy(kern_evs)
             out.update(kernel_ms=kmean, kernel_GBps=essential / (kmean * 1e-3) / 1e9)
         return out
 
