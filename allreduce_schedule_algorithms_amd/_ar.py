@@ -130,6 +130,7 @@ SIGNATURES = {
                                     C.c_int32, C.c_void_p]),
     "ar_all_gather": (C.c_int, [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_void_p]),
     "ar_workspace_bytes": (C.c_int, [C.POINTER(ar_call), C.POINTER(C.c_size_t)]),
+    "ar_set_launch_blocks": (C.c_int, [C.c_int64, C.POINTER(C.c_int64)]),
     "ar_schedule_build": (C.c_int, [C.POINTER(ar_call), C.POINTER(C.c_void_p)]),
     "ar_schedule_info_get": (C.c_int, [C.c_void_p, C.POINTER(ar_schedule_info)]),
     "ar_schedule_export": (C.c_int, [C.c_void_p, C.POINTER(ar_oprec), C.c_size_t, C.POINTER(C.c_size_t)]),
@@ -258,6 +259,13 @@ def ar_workspace_bytes(call: ar_call) -> int:
     out = C.c_size_t(0)
     _check(lib.ar_workspace_bytes(C.byref(call), C.byref(out)))
     return out.value
+
+
+def ar_set_launch_blocks(max_blocks: int) -> int:
+    """Set the per-launch workgroup limit; returns the previous one."""
+    prev = C.c_int64(0)
+    _check(lib.ar_set_launch_blocks(int(max_blocks), C.byref(prev)))
+    return prev.value
 
 
 def ar_schedule_build(call: ar_call) -> "Schedule":

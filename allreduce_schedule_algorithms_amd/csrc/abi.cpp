@@ -126,6 +126,12 @@ ar_status ar_set_cost_model(const ar_cost_model* m) {
   return AR_OK;
 }
 
+ar_status ar_set_launch_blocks(int64_t max_blocks, int64_t* previous) {
+  if (!ar::set_launch_blocks(max_blocks, previous))
+    return fail(AR_INVALID_ARGUMENT, "max_blocks must be in [1, " + std::to_string(ar::kMaxLaunchBlocks) + "]");
+  return AR_OK;
+}
+
 ar_status ar_get_cost_model(ar_cost_model* m) {
   if (!m) return fail(AR_INVALID_ARGUMENT, "model is NULL");
   std::lock_guard<std::mutex> lk(g_model_mu);

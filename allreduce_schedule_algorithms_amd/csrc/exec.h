@@ -28,6 +28,15 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
 // the literal steps); 0 otherwise.
 RunResult workspace_bytes(const Spec& spec, int exec, size_t* bytes);
 
+// Workgroups one kernel launch may hold: 2^32 work-items at most (32-bit grid
+// size in the dispatch packet), 256 per workgroup.
+constexpr int64_t kMaxLaunchBlocks = (int64_t(1) << 32) / 256 - 1;
+
+// Current per-launch workgroup limit; longer work is split into several launches.
+int64_t launch_blocks();
+// Set the limit (1..kMaxLaunchBlocks; false otherwise); the old value goes to *previous.
+bool set_launch_blocks(int64_t blocks, int64_t* previous);
+
 // Cached host schedule for a spec (shared with the executor's plan cache).
 std::shared_ptr<const Schedule> cached_schedule(const Spec& spec, std::string* err);
 

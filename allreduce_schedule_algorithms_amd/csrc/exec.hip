@@ -22,6 +22,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <limits>
@@ -340,6 +341,21 @@ static bool fused_runs(const Schedule& s) {
   return s.max_trees <= kMaxFusedTrees && !(s.max_trees > 1 && D > 8);
 }
 
+// The dispatch packet counts a grid's work-items in 32 bits, so one launch holds
+// at most kMaxLaunchBlocks workgroups of kThreads; longer work is split into
+// consecutive launches on the same stream. The limit can be lowered.
+static_assert(kThreads == 256, "kMaxLaunchBlocks assumes 256-thread workgroups");
+static std::atomic<int64_t> g_launch_blocks{kMaxLaunchBlocks};
+
+int64_t launch_blocks() { return g_launch_blocks.load(std::memory_order_relaxed); }
+
+bool set_launch_blocks(int64_t blocks, int64_t* previous) {
+  if (blocks < 1 || blocks > kMaxLaunchBlocks) return false;
+  const int64_t old = g_launch_blocks.exchange(blocks);
+  if (previous) *previous = old;
+  return true;
+}
+
 RunResult workspace_bytes(const Spec& spec, int exec, size_t* bytes) {
   std::string err;
   std::shared_ptr<const Schedule> s = cached_schedule(spec, &err);
@@ -376,7 +392,8 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
   const int64_t total = spec.n * spec.batch;
   if (exec == E_FUSED && spec.algo == A_DIRECT && spec.coll == C_ALLREDUCE) {
     hipError_t e = hipSuccess;
-    AR_DISPATCH(spec.dtype, spec.op, (e = launch_direct_t<DT, OPK>(vec, ptrs, spec.P, total, st, ev)));
+    AR_DISPATCH(spec.dtype, spec.op,
+                (e = launch_direct_t<DT, OPK>(vec, ptrs, spec.P, total, launch_blocks(), st, ev)));
     if (e != hipSuccess) return hip_fail(e, "launching the direct kernel");
     return res;
   }
@@ -433,21 +450,32 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
     const LitWork* packed = reinterpret_cast<const LitWork*>(pl->packed[mode].p);
     const auto& lns = pl->launches[mode];
     if (lns.empty()) return mark_empty();
+    const int64_t cap = launch_blocks();
     for (size_t i = 0; i < lns.size(); ++i) {
-      Evs ei{i == 0 ? ev.start : nullptr, i + 1 == lns.size() ? ev.stop : nullptr};
-      AR_DISPATCH(spec.dtype, spec.op,
-                  (e = launch_literal_t<DT, OPK>(lns[i].second, ptrs, wd, work + lns[i].first, packed, st, ei)));
-      if (e != hipSuccess) return hip_fail(e, "launching a literal step");
+      // a step's work records are independent: a long step is cut into launches of <= cap records
+      for (int64_t off = 0; off < lns[i].second; off += cap) {
+        const bool last = i + 1 == lns.size() && off + cap >= lns[i].second;
+        const Evs ei{i == 0 && off == 0 ? ev.start : nullptr, last ? ev.stop : nullptr};
+        const int64_t cnt = std::min(cap, lns[i].second - off);
+        AR_DISPATCH(spec.dtype, spec.op,
+                    (e = launch_literal_t<DT, OPK>(cnt, ptrs, wd, work + lns[i].first + off, packed, st, ei)));
+        if (e != hipSuccess) return hip_fail(e, "launching a literal step");
+      }
     }
   } else {
     if (pl->nitems[mode] == 0) return mark_empty();
     const Item* items = reinterpret_cast<const Item*>(pl->items[mode].p);
     const int32_t* prog = reinterpret_cast<const int32_t*>(pl->prog.p);
     ptrs.xcd = pl->s->prog.size() * sizeof(int32_t) > kXcdProgramBytes ? 1 : 0;
-    AR_DISPATCH(spec.dtype, spec.op,
-                (e = launch_fused_t<DT, OPK>(pl->D, pl->s->max_trees > 1 ? kMaxFusedTrees : 1, spec.P,
-                                             pl->s->max_leaves, pl->nitems[mode], ptrs, items, prog, st, ev)));
-    if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
+    const int64_t nit = pl->nitems[mode], cap = launch_blocks();
+    for (int64_t off = 0; off < nit; off += cap) {  // work items are independent
+      const Evs ei{off == 0 ? ev.start : nullptr, off + cap >= nit ? ev.stop : nullptr};
+      AR_DISPATCH(spec.dtype, spec.op,
+                  (e = launch_fused_t<DT, OPK>(pl->D, pl->s->max_trees > 1 ? kMaxFusedTrees : 1, spec.P,
+                                               pl->s->max_leaves, std::min(cap, nit - off), ptrs, items + off, prog,
+                                               st, ei)));
+      if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
+    }
   }
   (void)V;
   return res;

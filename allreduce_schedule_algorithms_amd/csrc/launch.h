@@ -36,7 +36,8 @@ template <int DT, int OPK>
 hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& ws, const LitWork* work,
                             const LitWork* packed, hipStream_t st, Evs ev);
 template <int DT, int OPK>
-hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total, hipStream_t st, Evs ev);
+hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total, int64_t max_blocks, hipStream_t st,
+                           Evs ev);
 
 #ifdef AR_LAUNCH_DEFINITIONS
 // Launches go through hipExtLaunchKernelGGL so that optional caller events can
@@ -114,33 +115,51 @@ hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& w
   return hipGetLastError();
 }
 
+// One launch per run of at most max_blocks workgroups; each launch gets the
+// rank pointers advanced to its first element. The vector path's element tail
+// (past the last whole vector) goes to block 0 of the last launch.
 template <int DT, int OPK, int B>
-void direct_b(bool vec, const RankPtrs& ptrs, int P, int64_t total, hipStream_t st, Evs ev) {
+hipError_t direct_b(bool vec, const RankPtrs& ptrs, int P, int64_t total, int64_t max_blocks, hipStream_t st,
+                    Evs ev) {
   constexpr int V = TT<DT>::V;
-  if (vec) {
-    int64_t nvec = total / V;
-    int64_t blocks = std::max<int64_t>(1, (nvec + kThreads * kDirectM - 1) / (kThreads * kDirectM));
-    hipExtLaunchKernelGGL((k_direct<DT, OPK, true, B>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, ev.start,
-                          ev.stop, 0, ptrs, P, nvec, total);
-  } else {
-    int64_t blocks = std::max<int64_t>(1, (total + kThreads - 1) / kThreads);
-    hipExtLaunchKernelGGL((k_direct<DT, OPK, false, B>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, ev.start,
-                          ev.stop, 0, ptrs, P, int64_t(0), total);
-  }
+  constexpr int64_t elt = sizeof(typename TT<DT>::S);
+  const int64_t unit = vec ? int64_t(kThreads) * kDirectM * V : int64_t(kThreads);  // elements per workgroup
+  const int64_t whole = vec ? total / V * V : total;  // elements the workgroups cover
+  const int64_t per = max_blocks * unit;
+  RankPtrs pp = ptrs;
+  int64_t done = 0;
+  do {
+    const int64_t len = std::min(per, whole - done);
+    const bool last = done + len >= whole;
+    for (int p = 0; p < P; ++p) pp.p[p] = static_cast<char*>(ptrs.p[p]) + done * elt;
+    const Evs ei{done == 0 ? ev.start : nullptr, last ? ev.stop : nullptr};
+    const int64_t blocks = std::max<int64_t>(1, (len + unit - 1) / unit);
+    if (vec) {
+      hipExtLaunchKernelGGL((k_direct<DT, OPK, true, B>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, ei.start,
+                            ei.stop, 0, pp, P, len / V, last ? total - done : len);
+    } else {
+      hipExtLaunchKernelGGL((k_direct<DT, OPK, false, B>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, ei.start,
+                            ei.stop, 0, pp, P, int64_t(0), len);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    done += len;
+  } while (done < whole);
+  return hipSuccess;
 }
 
 template <int DT, int OPK>
-hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total, hipStream_t st, Evs ev) {
+hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total, int64_t max_blocks, hipStream_t st,
+                           Evs ev) {
   switch (leaf_batch(P)) {
-    case 2: direct_b<DT, OPK, 2>(vec, ptrs, P, total, st, ev); break;
-    case 3: direct_b<DT, OPK, 3>(vec, ptrs, P, total, st, ev); break;
-    case 4: direct_b<DT, OPK, 4>(vec, ptrs, P, total, st, ev); break;
-    case 5: direct_b<DT, OPK, 5>(vec, ptrs, P, total, st, ev); break;
-    case 6: direct_b<DT, OPK, 6>(vec, ptrs, P, total, st, ev); break;
-    case 7: direct_b<DT, OPK, 7>(vec, ptrs, P, total, st, ev); break;
-    default: direct_b<DT, OPK, 8>(vec, ptrs, P, total, st, ev); break;
+    case 2: return direct_b<DT, OPK, 2>(vec, ptrs, P, total, max_blocks, st, ev);
+    case 3: return direct_b<DT, OPK, 3>(vec, ptrs, P, total, max_blocks, st, ev);
+    case 4: return direct_b<DT, OPK, 4>(vec, ptrs, P, total, max_blocks, st, ev);
+    case 5: return direct_b<DT, OPK, 5>(vec, ptrs, P, total, max_blocks, st, ev);
+    case 6: return direct_b<DT, OPK, 6>(vec, ptrs, P, total, max_blocks, st, ev);
+    case 7: return direct_b<DT, OPK, 7>(vec, ptrs, P, total, max_blocks, st, ev);
+    default: return direct_b<DT, OPK, 8>(vec, ptrs, P, total, max_blocks, st, ev);
   }
-  return hipGetLastError();
 }
 
 
@@ -149,7 +168,7 @@ hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total,
                                               const int32_t*, hipStream_t, Evs);                            \
   template hipError_t launch_literal_t<DT, OPK>(int64_t, const RankPtrs&, const WsDesc&, const LitWork*,    \
                                                 const LitWork*, hipStream_t, Evs);                          \
-  template hipError_t launch_direct_t<DT, OPK>(bool, const RankPtrs&, int, int64_t, hipStream_t, Evs);
+  template hipError_t launch_direct_t<DT, OPK>(bool, const RankPtrs&, int, int64_t, int64_t, hipStream_t, Evs);
 #endif  // AR_LAUNCH_DEFINITIONS
 
 }  // namespace ar

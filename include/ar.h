@@ -194,6 +194,15 @@ ar_status ar_allreduce_ex(void* const* bufs, const ar_call* call, void* stream);
  * Builds (and caches) the schedule; returns its validation error for invalid calls. */
 ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes);
 
+/* Largest grid, in 256-thread workgroups, of one kernel launch. A call whose work needs
+ * more (misaligned buffers of 2^32 elements or more, or about 2^35 aligned ones) runs as
+ * several consecutive launches on the caller's stream with the same results; events of
+ * ar_call then mark the first launch's start and the last one's end. The default and
+ * maximum, 2^24 - 1, is what the 32-bit grid size of a dispatch holds. Process-wide; calls
+ * enqueued afterwards use the new value. max_blocks outside [1, 2^24 - 1] returns
+ * AR_INVALID_ARGUMENT and changes nothing. previous (may be NULL) receives the old value. */
+ar_status ar_set_launch_blocks(int64_t max_blocks, int64_t* previous);
+
 /* ---- schedules on the host (no GPU needed) ---- */
 typedef struct ar_schedule ar_schedule;
 

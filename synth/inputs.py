@@ -140,3 +140,32 @@ def sample_indices(n: int, parts: int, count: int = 4096, seed: int = 1) -> np.n
     if not picks:
         return np.zeros(0, dtype=np.int64)
     return np.unique(np.concatenate(picks).astype(np.int64))
+
+
+# ---------------------------------------------------------------------------
+# counter-based values for buffers too large to draw and ship from the host
+# ---------------------------------------------------------------------------
+_M1, _M2 = 65521, 65519  # the two largest primes below 2^16
+
+
+def counter_ints(p: int, e, seed: int = 0):
+    """Value of rank p at element offsets e (int64 array, NumPy or torch):
+    with a = e mod 65521 and b = e mod 65519,
+    (a b + 7 a + 3 b + 11 p + seed) mod 4093 - 2046, an integer in [-2046, 2046].
+
+    A pure function of (seed, p, e), so the GPU can fill a buffer of any size
+    chunk by chunk and the host can compute any sampled offset on its own. The
+    pattern repeats only after 65521 * 65519 (about 2^32) offsets, and small
+    integers keep fp32 sums of a few ranks exact in any order.
+    """
+    a, b = e % _M1, e % _M2
+    return (a * b + 7 * a + 3 * b + 11 * p + seed) % 4093 - 2046
+
+
+def fill_counter_fp32(row, p: int, seed: int = 0, chunk: int = 1 << 27) -> None:
+    """Fill a 1-D float32 torch tensor (any device) with counter_ints(p, 0..len-1)."""
+    import torch
+    n = row.numel()
+    for s in range(0, n, chunk):
+        e = torch.arange(s, min(n, s + chunk), dtype=torch.int64, device=row.device)
+        row[s: s + e.numel()] = counter_ints(p, e, seed).to(torch.float32)

@@ -448,6 +448,81 @@ def test_random_cases_on_gpu(seed):
             assert np.array_equal(bits(got), bits(want)), case + (ex,)
 
 
+def test_long_work_split_over_launches():
+    # with the per-launch workgroup limit lowered to 3, every executor cuts its
+    # work into several launches; the results must not change
+    import allreduce_schedule_algorithms_amd as A
+    torch = torch_mod()
+    cases = [  # (algo, knob, exec, P, n, misalign)
+        ("rh_rd", 0, "fused", 8, 1 << 16, False),
+        ("ring", 0, "fused", 5, 10_003, True),
+        ("generalized", 2, "fused", 7, 50_001, False),   # several trees per range: staged kernel
+        ("ring", 0, "literal", 5, 100_003, False),
+        ("generalized", 3, "literal", 7, 20_000, True),
+        ("direct", 0, "fused", 6, 10_003, False),        # vector path with an element tail
+        ("direct", 0, "fused", 3, 10_000, True),         # element path
+    ]
+    prev = A.ar_set_launch_blocks(3)
+    try:
+        for algo, knob, ex, P, n, mis in cases:
+            for dtype in ("fp32", "bf16"):
+                x = inputs.make(dtype, P, n, seed=P * 31 + n)
+                want = oracle.allreduce(x, algo, dtype, "sum", knob=knob)
+                got = gpu_allreduce(x, algo, dtype, "sum", knob, ex, misalign=mis)
+                assert np.array_equal(bits(got), bits(want)), (algo, knob, ex, P, n, mis, dtype)
+        # the caller's events bracket the first and the last launch
+        x = inputs.make("fp32", 8, 1 << 16, seed=5)
+        bufs, keep = to_device(x, "fp32")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st = torch.cuda.current_stream()
+        a.record(st)
+        b.record(st)
+        call = A.make_call(8, 1 << 16, "fp32", "sum", "rh_rd", start_event=a, stop_event=b)
+        A.ar_allreduce_ex([t.data_ptr() for t in bufs], call, st)
+        torch.cuda.synchronize()
+        assert a.elapsed_time(b) > 0
+        assert np.array_equal(bits(from_device(bufs, "fp32")), bits(oracle.allreduce(x, "rh_rd", "fp32", "sum")))
+        del keep
+    finally:
+        A.ar_set_launch_blocks(prev)
+
+
+def test_buffers_past_2_32_elements():
+    # 2 ranks of 2^32 + 1000 fp32 (16 GiB each), one element off 16-byte
+    # alignment: the element path needs 2^24 + 4 workgroups, one more than a
+    # launch holds, and offsets pass 2^32 elements. Values are small integers
+    # from a counter-based generator, so every sum is exact: sampled offsets are
+    # checked against the oracle, and every offset against x0 + x1 (torch).
+    import allreduce_schedule_algorithms_amd as A
+    torch = torch_mod()
+    P, n = 2, (1 << 32) + 1000
+    cut = ((1 << 32) // 256 - 1) * 256  # first element of the second launch
+    idx = np.unique(np.concatenate([
+        inputs.sample_indices(n, P, count=4096),
+        np.array([0, 1, 255, 256, cut - 1, cut, cut + 1, n // 2 - 1, n // 2, n // 2 + 1,
+                  (1 << 31), (1 << 32) - 1, (1 << 32), n - 1], dtype=np.int64)]))
+    xs = np.stack([inputs.counter_ints(p, idx).astype(np.float32) for p in range(P)])
+    big = torch.empty((P, n + 8), dtype=torch.float32, device="cuda")
+    rows = [big[p, 1: 1 + n] for p in range(P)]
+    tidx = torch.from_numpy(idx).cuda()
+    for algo, ex in (("ring", "fused"), ("direct", "fused"), ("ring", "literal")):
+        for p in range(P):
+            inputs.fill_counter_fp32(rows[p], p)
+        call = A.make_call(P, n, "fp32", "sum", algo, 0, ex)
+        A.ar_allreduce_ex([r.data_ptr() for r in rows], call, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        want = oracle.allreduce(xs, algo, "fp32", "sum", n=n, idx=idx)
+        got = np.stack([r[tidx].cpu().numpy() for r in rows])
+        assert np.array_equal(bits(got), bits(want)), (algo, ex)
+        chunk = 1 << 27
+        for s0 in range(0, n, chunk):
+            e = torch.arange(s0, min(n, s0 + chunk), dtype=torch.int64, device="cuda")
+            ref = (inputs.counter_ints(0, e) + inputs.counter_ints(1, e)).to(torch.float32)
+            for r in rows:
+                assert torch.equal(r[s0: s0 + e.numel()], ref), (algo, ex, s0)
+    del rows, big
+
+
 def test_plans_survive_a_cleared_schedule_cache():
     # a plan built on the first call must stay valid after other specs have
     # pushed its schedule out of the schedule cache (more than 512 of them)

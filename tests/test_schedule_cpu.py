@@ -360,6 +360,21 @@ def test_workspace_query():
     assert A.ar_workspace_bytes(big) == A.ar_workspace_bytes(lit) > 0
 
 
+def test_launch_block_limit_setter():
+    top = (1 << 32) // 256 - 1
+    prev = A.ar_set_launch_blocks(5)
+    try:
+        assert prev == top  # the default is the dispatch limit
+        assert A.ar_set_launch_blocks(7) == 5
+        for bad in (0, -1, top + 1):
+            with pytest.raises(A.ArError) as e:
+                A.ar_set_launch_blocks(bad)
+            assert e.value.status == A.Status.AR_INVALID_ARGUMENT
+        assert A.ar_set_launch_blocks(top) == 7  # a rejected value changes nothing
+    finally:
+        A.ar_set_launch_blocks(prev)
+
+
 def test_status_strings():
     assert A.ar_status_string(0) == "AR_OK"
     assert A.ar_status_string(3) == "AR_WORKSPACE_TOO_SMALL"
