@@ -31,6 +31,12 @@ __device__ __forceinline__ unsigned item_index(int32_t xcd) {
   return x < full ? x * per + slot : full * per + (x - full) * (per - 1) + slot;
 }
 
+// Program words stay unchanged for the whole launch. Reading them through the
+// constant address space lets the compiler use scalar loads for them even after
+// the kernel's own stores, which it cannot otherwise prove leave them alone.
+typedef const __attribute__((address_space(4))) int32_t* ProgPtr;
+__device__ __forceinline__ ProgPtr as_prog(const int32_t* p) { return (ProgPtr)p; }
+
 // Work item: `count` > 0 is a run of vectors, < 0 a run of -count single elements;
 // `start` is the element offset of its first element in every rank buffer.
 struct Item {
@@ -257,13 +263,13 @@ __device__ __forceinline__ void for_fragments(const Item& it, int V, F&& f) {
 // last batch is full where it can (B = 7 for seven leaves); otherwise the
 // missing slots repeat the batch's first leaf.
 template <int DT, int OPK, int D, int M, int B, typename LeafAt>
-__device__ __forceinline__ void eval_one(const int32_t* __restrict__ w, LeafAt&& leaf_at,
+__device__ __forceinline__ void eval_one(ProgPtr w, LeafAt&& leaf_at,
                                          typename TT<DT>::A (&res)[nvals<DT, M>()]) {
   using A = typename TT<DT>::A;
   constexpr int N = nvals<DT, M>();
   const int nl = w[0];
-  const int32_t* __restrict__ leaf = w + 2;
-  const int32_t* __restrict__ nc = leaf + nl;
+  const ProgPtr leaf = w + 2;
+  const ProgPtr nc = leaf + nl;
   A st[D][N];
 #pragma unroll
   for (int d = 0; d < D; ++d)
@@ -299,13 +305,13 @@ __device__ __forceinline__ void eval_one(const int32_t* __restrict__ w, LeafAt&&
 }
 
 template <int DT, int OPK, int D, int TM, int M, int B, typename LeafAt>
-__device__ __forceinline__ void replay(const RankPtrs& ptrs, const int32_t* __restrict__ w, int64_t e,
+__device__ __forceinline__ void replay(const RankPtrs& ptrs, ProgPtr w, int64_t e,
                                        const bool (&ok)[mm<M>()], LeafAt&& leaf_at) {
   using A = typename TT<DT>::A;
   const int ntrees = w[0];
   w += 1;
   A res[TM][nvals<DT, M>()];
-  const int32_t* outs[TM];
+  ProgPtr outs[TM];
   int nouts[TM];
 #pragma unroll
   for (int t = 0; t < TM; ++t) {
@@ -320,7 +326,7 @@ __device__ __forceinline__ void replay(const RankPtrs& ptrs, const int32_t* __re
 #pragma unroll
   for (int t = 0; t < TM; ++t) {
     if (t < ntrees) {
-      const int32_t* ot = outs[t];
+      const ProgPtr ot = outs[t];
       if constexpr (OPK == O_AVG) {
 #pragma unroll
         for (int i = 0; i < nvals<DT, M>(); ++i) res[t][i] = res[t][i] / ptrs.div;
@@ -345,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* _
   constexpr int M = fused_m<DT, D, TM>();
   constexpr bool NT = TM == 1;  // several trees re-read their leaves: keep them cacheable
   const Item it = items[item_index(ptrs.xcd)];
-  const int32_t* w = prog + it.tag;
+  const ProgPtr w = as_prog(prog) + it.tag;
   if (it.count > 0) {
     for_fragments<M>(it, V, [&](int64_t e, const bool (&ok)[M]) {
       replay<DT, OPK, D, TM, M, B>(ptrs, w, e, ok,
@@ -369,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_staged(RankPtrs ptrs, const 
   constexpr int V = TT<DT>::V;
   extern __shared__ u32x4 stage[];
   const Item it = items[item_index(ptrs.xcd)];
-  const int32_t* w = prog + it.tag;
+  const ProgPtr w = as_prog(prog) + it.tag;
   if (it.count > 0) {
     for_fragments<1>(it, V, [&](int64_t e, const bool (&ok)[1]) {
       for (int base = 0; base < P; base += kLeafBatch) {
