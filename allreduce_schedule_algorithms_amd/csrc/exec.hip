@@ -244,7 +244,11 @@ RunResult build_items(Plan& pl, bool vec) {
         for (const FusedRange& r : s.ranges) add_segment(items, b * sp.n + r.start, r.len, r.prog, V, vec);
     }
     if (!pl.prog.p) {
-      hipError_t e = upload(pl.prog, s.prog);
+      // the replay reads each batch's leaf ranks and combination counts as whole
+      // runs of kLeafBatch words, so the last tree's runs may reach past its end
+      std::vector<int32_t> words(s.prog);
+      words.resize(words.size() + 2 * kLeafBatch, 0);
+      hipError_t e = upload(pl.prog, words);
       if (e != hipSuccess) return hip_fail(e, "uploading the fused program");
     }
   }

@@ -276,9 +276,19 @@ __device__ __forceinline__ void eval_one(ProgPtr w, LeafAt&& leaf_at,
 #pragma unroll
     for (int i = 0; i < N; ++i) st[d][i] = A(0);
   for (int base = 0; base < nl; base += B) {
+    // whole runs of B words (scalar loads the compiler can merge; the program
+    // buffer is padded for the last tree), clamped by value past the end
+    int rk[B], cnt[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      rk[k] = leaf[base + k];
+      cnt[k] = nc[base + k];
+    }
+#pragma unroll
+    for (int k = 1; k < B; ++k) rk[k] = base + k < nl ? rk[k] : rk[0];
     u32x4 raw[B][mm<M>()];
 #pragma unroll
-    for (int k = 0; k < B; ++k) leaf_at(leaf[base + k < nl ? base + k : base], raw[k]);
+    for (int k = 0; k < B; ++k) leaf_at(rk[k], raw[k]);
 #pragma unroll
     for (int k = 0; k < B; ++k) {
       if (base + k < nl) {
@@ -289,7 +299,7 @@ __device__ __forceinline__ void eval_one(ProgPtr w, LeafAt&& leaf_at,
           for (int i = 0; i < N; ++i) st[d][i] = st[d - 1][i];
         widen<DT, M>(raw[k], st[0]);
         // each combination folds the top two entries and shifts the rest up
-        for (int c = nc[base + k]; c > 0; --c) {
+        for (int c = cnt[k]; c > 0; --c) {
 #pragma unroll
           for (int i = 0; i < N; ++i) st[0][i] = cmb<OPK>(st[1][i], st[0][i]);
 #pragma unroll
