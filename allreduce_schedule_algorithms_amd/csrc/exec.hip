@@ -108,6 +108,7 @@ struct DevBuf {
 struct Plan {
   std::shared_ptr<const Schedule> s;
   int exec = E_FUSED;
+  int device = 0;  // the device holding the plan's buffers
   int D = 2;
   DevBuf prog;
   DevBuf items[2];  // [vector mode, scalar mode]
@@ -117,6 +118,7 @@ struct Plan {
   // small chunks
   std::vector<std::pair<int64_t, int64_t>> launches[2];
   DevBuf packed[2];
+  bool strided = false;  // fused: items are SItem (batches of short ranges)
   int64_t slot_bytes = 0;
   size_t ws_bytes = 0;
 };
@@ -156,6 +158,11 @@ int vec_width(int dtype) { return dtype == D_BF16 ? 8 : 4; }
 // Fused programs above this size run with one contiguous run of items per XCD
 // (measured: AHC's 300 KB program +3.4%; programs of a few hundred bytes lose 2-6%).
 constexpr size_t kXcdProgramBytes = 64 * 1024;
+
+// Batched calls whose ranges are all shorter than this many elements use
+// strided items (one element per thread across instances) instead of one item
+// per instance and range.
+constexpr int64_t kStridedMaxLen = 64;
 
 // Build the fused or literal item tables for one alignment mode.
 RunResult build_items(Plan& pl, bool vec) {
@@ -236,9 +243,21 @@ RunResult build_items(Plan& pl, bool vec) {
     return RunResult{};
   } else {
     const bool flat = s.ranges.size() == 1 && s.ranges[0].start == 0 && s.ranges[0].len == sp.n;
+    int64_t max_len = 0;
+    for (const FusedRange& r : s.ranges) max_len = std::max(max_len, r.len);
+    std::vector<SItem> sitems;
     if (sp.batch == 1 || flat) {
       const int64_t mult = flat ? sp.batch : 1;
       for (const FusedRange& r : s.ranges) add_segment(items, r.start, r.len * mult, r.prog, V, vec);
+    } else if (max_len < kStridedMaxLen) {
+      // short ranges in many instances: one strided item per range and block
+      // of instances; the items of one block sit next to each other, so the
+      // ranges sharing its cache lines run together
+      const int64_t nb = std::max<int64_t>(1, kThreads / max_len);
+      for (int64_t b0 = 0; b0 < sp.batch; b0 += nb)
+        for (const FusedRange& r : s.ranges)
+          if (r.len > 0)
+            sitems.push_back({b0 * sp.n + r.start, r.prog, int32_t(r.len), int32_t(std::min(nb, sp.batch - b0)), 0});
     } else {
       for (int64_t b = 0; b < sp.batch; ++b)
         for (const FusedRange& r : s.ranges) add_segment(items, b * sp.n + r.start, r.len, r.prog, V, vec);
@@ -250,6 +269,14 @@ RunResult build_items(Plan& pl, bool vec) {
       words.resize(words.size() + 2 * kLeafBatch, 0);
       hipError_t e = upload(pl.prog, words);
       if (e != hipSuccess) return hip_fail(e, "uploading the fused program");
+    }
+    if (!sitems.empty()) {
+      hipError_t e = upload(pl.items[mode], sitems);
+      if (e != hipSuccess) return hip_fail(e, "uploading work items");
+      pl.nitems[mode] = int64_t(sitems.size());
+      pl.strided = true;
+      pl.built[mode] = true;
+      return RunResult{};
     }
   }
   hipError_t e = upload(pl.items[mode], items);
@@ -303,12 +330,20 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
   auto pl = std::make_unique<Plan>();
   pl->s = s;
   pl->exec = exec;
+  pl->device = device;
   pl->D = s->max_need <= 2 ? 2 : s->max_need <= 4 ? 4 : s->max_need <= 8 ? 8 : 16;
   int64_t slot = spec.n * spec.batch * int64_t(acc_bytes(spec.dtype));
   pl->slot_bytes = (slot + 255) / 256 * 256;
   pl->ws_bytes = size_t(s->nslots - 1) * size_t(spec.P) * size_t(pl->slot_bytes);
   if (m.size() > 256) {
-    (void)hipDeviceSynchronize();
+    // every device whose plans are dropped may still run kernels that read them
+    std::vector<int> devs;
+    for (const auto& kv : m)
+      if (std::find(devs.begin(), devs.end(), kv.second->device) == devs.end()) devs.push_back(kv.second->device);
+    for (int d : devs) {
+      if (hipSetDevice(d) == hipSuccess) (void)hipDeviceSynchronize();
+    }
+    (void)hipSetDevice(device);
     m.clear();
     ++g_plan_generation;
   }
@@ -470,14 +505,23 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
     if (pl->nitems[mode] == 0) return mark_empty();
     const Item* items = reinterpret_cast<const Item*>(pl->items[mode].p);
     const int32_t* prog = reinterpret_cast<const int32_t*>(pl->prog.p);
-    ptrs.xcd = pl->s->prog.size() * sizeof(int32_t) > kXcdProgramBytes ? 1 : 0;
+    // strided items of one block of instances share cache lines: keeping
+    // neighbouring items on one XCD keeps those lines in one L2
+    ptrs.xcd = pl->strided || pl->s->prog.size() * sizeof(int32_t) > kXcdProgramBytes ? 1 : 0;
     const int64_t nit = pl->nitems[mode], cap = launch_blocks();
+    const int TM = pl->s->max_trees > 1 ? kMaxFusedTrees : 1;
     for (int64_t off = 0; off < nit; off += cap) {  // work items are independent
       const Evs ei{off == 0 ? ev.start : nullptr, off + cap >= nit ? ev.stop : nullptr};
-      AR_DISPATCH(spec.dtype, spec.op,
-                  (e = launch_fused_t<DT, OPK>(pl->D, pl->s->max_trees > 1 ? kMaxFusedTrees : 1, spec.P,
-                                               pl->s->max_leaves, std::min(cap, nit - off), ptrs, items + off, prog,
-                                               st, ei)));
+      const int64_t cnt = std::min(cap, nit - off);
+      if (pl->strided) {
+        const SItem* sit = reinterpret_cast<const SItem*>(pl->items[mode].p) + off;
+        AR_DISPATCH(spec.dtype, spec.op,
+                    (e = launch_fused_strided_t<DT, OPK>(pl->D, TM, cnt, ptrs, sit, prog, spec.n, st, ei)));
+      } else {
+        AR_DISPATCH(spec.dtype, spec.op,
+                    (e = launch_fused_t<DT, OPK>(pl->D, TM, spec.P, pl->s->max_leaves, cnt, ptrs, items + off, prog,
+                                                 st, ei)));
+      }
       if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
     }
   }

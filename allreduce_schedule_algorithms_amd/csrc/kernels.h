@@ -155,14 +155,22 @@ __device__ __forceinline__ void widen(const u32x4 (&r)[mm<M>()], typename TT<DT>
 }
 
 // Store a fragment in the caller's dtype (bf16: one round to nearest even).
-template <int DT, int M>
+// NT = non-temporal hint; single elements that other workgroups complete into
+// whole lines (strided items) are stored cacheable, so L2 merges the lines.
+template <typename T, bool NT>
+__device__ __forceinline__ void st1(T v, T* p) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+template <int DT, int M, bool NT = true>
 __device__ __forceinline__ void st_user(void* base, int64_t e, const bool (&ok)[mm<M>()],
                                         const typename TT<DT>::A (&v)[nvals<DT, M>()]) {
   using S = typename TT<DT>::S;
   if constexpr (M == 0) {
     if (ok[0]) {
-      if constexpr (DT == D_BF16) __builtin_nontemporal_store(uint16_t(to_bf16(v[0])), reinterpret_cast<uint16_t*>(base) + e);
-      else __builtin_nontemporal_store(as_u(v[0]), reinterpret_cast<uint32_t*>(base) + e);
+      if constexpr (DT == D_BF16) st1<uint16_t, NT>(uint16_t(to_bf16(v[0])), reinterpret_cast<uint16_t*>(base) + e);
+      else st1<uint32_t, NT>(as_u(v[0]), reinterpret_cast<uint32_t*>(base) + e);
     }
   } else {
 #pragma unroll
@@ -185,7 +193,7 @@ __device__ __forceinline__ void st_user(void* base, int64_t e, const bool (&ok)[
 // RUNS: rank_of may be read for whole runs of kLeafBatch indices (it reads
 // padded program words) and is clamped by value past cnt; otherwise only
 // indices below cnt are read.
-template <int DT, int M, bool RUNS = false, typename RankOf>
+template <int DT, int M, bool RUNS = false, bool NT = true, typename RankOf>
 __device__ __forceinline__ void st_user_all(const RankPtrs& ptrs, int cnt, RankOf&& rank_of, int64_t e,
                                             const bool (&ok)[mm<M>()],
                                             const typename TT<DT>::A (&v)[nvals<DT, M>()]) {
@@ -205,7 +213,7 @@ __device__ __forceinline__ void st_user_all(const RankPtrs& ptrs, int cnt, RankO
     }
 #pragma unroll
     for (int k = 0; k < kLeafBatch; ++k)
-      if (b + k < cnt) st_user<DT, M>(pp[k], e, ok, v);
+      if (b + k < cnt) st_user<DT, M, NT>(pp[k], e, ok, v);
   }
 }
 
@@ -342,7 +350,7 @@ __device__ __forceinline__ void eval_one(WP __restrict__ w, LeafAt&& leaf_at,
   for (int i = 0; i < N; ++i) res[i] = st[0][i];
 }
 
-template <int DT, int OPK, int D, int TM, int M, int B, typename WP, typename LeafAt>
+template <int DT, int OPK, int D, int TM, int M, int B, bool NTS = true, typename WP, typename LeafAt>
 __device__ __forceinline__ void replay(const RankPtrs& ptrs, WP __restrict__ w, int64_t e,
                                        const bool (&ok)[mm<M>()], LeafAt&& leaf_at) {
   using A = typename TT<DT>::A;
@@ -369,7 +377,7 @@ __device__ __forceinline__ void replay(const RankPtrs& ptrs, WP __restrict__ w, 
 #pragma unroll
         for (int i = 0; i < nvals<DT, M>(); ++i) res[t][i] = res[t][i] / ptrs.div;
       }
-      st_user_all<DT, M, word_runs<WP>()>(ptrs, nouts[t], [&](int i) { return ot[i]; }, e, ok, res[t]);
+      st_user_all<DT, M, word_runs<WP>(), NTS>(ptrs, nouts[t], [&](int i) { return ot[i]; }, e, ok, res[t]);
     }
   }
 }
@@ -400,6 +408,36 @@ __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* _
       replay<DT, OPK, D, TM, 0, B>(ptrs, w, e, ok,
                                    [&](int rank, u32x4(&r)[1]) { ld_user<DT, 0, NT>(ptrs.p[rank], e, ok, r); });
     });
+  }
+}
+
+// Batches of short instances: a strided item covers one range of `len`
+// elements (the same offsets in every instance) across `nb` consecutive
+// instances `stride` elements apart, one element per thread: instance v / len,
+// offset v % len. Per-instance items would give a workgroup a handful of
+// elements each.
+struct SItem {
+  int64_t start;  // the range's first element in the item's first instance
+  int32_t tag;    // program word offset
+  int32_t len;    // elements of the range in one instance
+  int32_t nb;     // instances
+  int32_t pad;
+};
+
+template <int DT, int OPK, int D, int TM, int B>
+__global__ __launch_bounds__(kThreads) void k_fused_strided(RankPtrs ptrs, const SItem* __restrict__ items,
+                                                            const int32_t* __restrict__ prog, int64_t stride) {
+  const SItem it = items[item_index(ptrs.xcd)];
+  const auto w = prog_words<TM>(prog, it.tag);
+  const int total = it.len * it.nb;
+  for (int v = threadIdx.x; v < total; v += kThreads) {
+    const int b = v / it.len;
+    const int64_t e = it.start + int64_t(b) * stride + (v - b * it.len);
+    const bool ok[1] = {true};
+    // neighbouring ranges of the same instances run in neighbouring items and
+    // share cache lines: cacheable loads and stores
+    replay<DT, OPK, D, TM, 0, B, false>(ptrs, w, e, ok,
+                                        [&](int rank, u32x4(&r)[1]) { ld_user<DT, 0, false>(ptrs.p[rank], e, ok, r); });
   }
 }
 

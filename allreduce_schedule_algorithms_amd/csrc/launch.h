@@ -33,6 +33,9 @@ template <int DT, int OPK>
 hipError_t launch_fused_t(int D, int TM, int P, int leaves, int64_t nitems, const RankPtrs& ptrs, const Item* items,
                           const int32_t* prog, hipStream_t st, Evs ev);
 template <int DT, int OPK>
+hipError_t launch_fused_strided_t(int D, int TM, int64_t nitems, const RankPtrs& ptrs, const SItem* items,
+                                  const int32_t* prog, int64_t stride, hipStream_t st, Evs ev);
+template <int DT, int OPK>
 hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& ws, const LitWork* work,
                             const LitWork* packed, hipStream_t st, Evs ev);
 template <int DT, int OPK>
@@ -108,6 +111,32 @@ hipError_t launch_fused_t(int D, int TM, int P, int leaves, int64_t nitems, cons
 }
 
 template <int DT, int OPK>
+hipError_t launch_fused_strided_t(int D, int TM, int64_t nitems, const RankPtrs& ptrs, const SItem* items,
+                                  const int32_t* prog, int64_t stride, hipStream_t st, Evs ev) {
+  const dim3 g{unsigned(nitems), 1, 1};
+  const dim3 b{unsigned(kThreads), 1, 1};
+#define AR_STRIDED(DD, TT_) \
+  hipExtLaunchKernelGGL((k_fused_strided<DT, OPK, DD, TT_, kLeafBatch>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, \
+                        items, prog, stride)
+  if (TM == 1) {
+    switch (D) {
+      case 2: AR_STRIDED(2, 1); break;
+      case 4: AR_STRIDED(4, 1); break;
+      case 8: AR_STRIDED(8, 1); break;
+      default: AR_STRIDED(16, 1); break;
+    }
+  } else {
+    switch (D) {
+      case 2: AR_STRIDED(2, kMaxFusedTrees); break;
+      case 4: AR_STRIDED(4, kMaxFusedTrees); break;
+      default: AR_STRIDED(8, kMaxFusedTrees); break;
+    }
+  }
+#undef AR_STRIDED
+  return hipGetLastError();
+}
+
+template <int DT, int OPK>
 hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& ws, const LitWork* work,
                             const LitWork* packed, hipStream_t st, Evs ev) {
   hipExtLaunchKernelGGL((k_literal<DT, OPK>), dim3(unsigned(nwork)), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
@@ -166,6 +195,8 @@ hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total,
 #define AR_INSTANTIATE_LAUNCHES(DT, OPK)                                                                    \
   template hipError_t launch_fused_t<DT, OPK>(int, int, int, int, int64_t, const RankPtrs&, const Item*,    \
                                               const int32_t*, hipStream_t, Evs);                            \
+  template hipError_t launch_fused_strided_t<DT, OPK>(int, int, int64_t, const RankPtrs&, const SItem*,     \
+                                                      const int32_t*, int64_t, hipStream_t, Evs);          \
   template hipError_t launch_literal_t<DT, OPK>(int64_t, const RankPtrs&, const WsDesc&, const LitWork*,    \
                                                 const LitWork*, hipStream_t, Evs);                          \
   template hipError_t launch_direct_t<DT, OPK>(bool, const RankPtrs&, int, int64_t, int64_t, hipStream_t, Evs);

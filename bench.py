@@ -66,13 +66,13 @@ WORKLOADS = {
         others=[("direct", 0, "fused"), ("ahc", 0, "literal"), ("ahc", 0, "fused", "allreduce", "avg")]),
     "small_batch": dict(
         desc="24 ranks x 10^4 instances x 106 fp32 U(-1,1), seed 0",
-        P=24, n=106, dtype="fp32", batch=10_000, groups=None,
+        P=24, n=106, dtype="fp32", batch=10_000, groups=None, steps=100,
         headline=("rd", 0, "fused"),
         others=[("binomial", 0, "fused"), ("direct", 0, "fused"), ("generalized", 5, "fused"),
                 ("rd", 0, "literal"), ("binomial", 0, "literal"), ("generalized", 5, "literal")]),
     "ring_int32": dict(
         desc="5 ranks x 4096 int32 U[-2^20, 2^20], seed 0",
-        P=5, n=4096, dtype="int32", batch=1, groups=None,
+        P=5, n=4096, dtype="int32", batch=1, groups=None, steps=100,
         headline=("ring", 0, "fused"),
         others=[("direct", 0, "fused"), ("ring", 0, "literal")]),
 }
@@ -548,7 +548,8 @@ def load_traffic(wl_name, key):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed calls per schedule (default 50; 100 for the latency-bound workloads)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="rh_fp32", choices=sorted(WORKLOADS))
     ap.add_argument("--headline-only", action="store_true", help="time only the headline schedule")
@@ -600,16 +601,20 @@ def main():
         return r.time(q["algo"], q["knob"], q["ex"], steps, warmup, coll=q["coll"], op=q["op"], rsteps=q["rsteps"],
                       factors=q["factors"], **kw)
 
+    if args.steps is None:
+        args.steps = wl.get("steps", 50)
+    # the other schedules: half the headline's calls, at least 20 (all of them
+    # where the workload asks for many calls per schedule)
+    other_steps = args.steps if "steps" in wl else max(20, args.steps // 2)
     head = timed(hkey, args.steps, args.warmup)
     schedules = {hkey: head}
     if not args.headline_only and not args.schedule:
         for entry in wl["others"]:
             key = schedule_key(*entry)
-            schedules[key] = timed(key, max(10, args.steps // 2), 2)
+            schedules[key] = timed(key, other_steps, 2)
     if args.warm:
         for key in list(schedules):
-            schedules[key]["warm_GBps"] = timed(key, max(10, args.steps // 2), 2, cold=False,
-                                                kernel_pass=False)["GBps"]
+            schedules[key]["warm_GBps"] = timed(key, other_steps, 2, cold=False, kernel_pass=False)["GBps"]
     for v in schedules.values():
         v["pct_hbm_peak"] = round(100.0 * v["GBps"] / HBM_PEAK_GBPS, 2)
         for k in ("ms", "ms_median", "ms_min", "kernel_ms", "wall_ms_per_step", "GBps", "kernel_GBps"):

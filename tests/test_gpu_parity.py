@@ -414,6 +414,23 @@ def test_batched_halves_avg_and_chain():
             assert np.array_equal(bits(got), bits(want)), (algo, op, ex)
 
 
+def test_batched_short_ranges():
+    # batches of short instances with chunked schedules: the fused replay runs
+    # one strided item per range and block of instances; instance counts that
+    # are not a multiple of the block, tiny n and misaligned buffers included
+    cases = [(3, 106, "ring", 0, None), (7, 106, "generalized", 3, None), (24, 106, "generalized", 5, None),
+             (24, 106, "generalized", 0, None), (6, 5, "rh_rd", 0, None), (5, 1, "ring", 0, None),
+             (12, 106, "ahc", 0, [5, 7]), (8, 33, "chain", 3, None), (7, 106, "generalized", 1, None)]
+    for i, (P, n, algo, knob, groups) in enumerate(cases):
+        for dtype, op in (("fp32", "sum"), ("bf16", "sum"), ("int32", "max"), ("fp32", "avg")):
+            B = 37 + i
+            x = inputs.make(dtype, P, n * B, seed=100 + i)
+            want = oracle.allreduce(x.reshape(P, B, n), algo, dtype, op, knob=knob, groups=groups, n=n)
+            for ex, mis in (("fused", False), ("fused", True), ("literal", False)):
+                got = gpu_allreduce(x, algo, dtype, op, knob, ex, groups, batch=B, misalign=mis)
+                assert np.array_equal(bits(got.reshape(P, B, n)), bits(want)), (P, n, algo, knob, dtype, op, ex, mis)
+
+
 def test_auto_halves_run_the_oracle_choice():
     import allreduce_schedule_algorithms_amd as A
     from oracle import cost, schedules as sch
@@ -533,5 +550,14 @@ def test_plans_survive_a_cleared_schedule_cache():
         assert np.array_equal(bits(gpu_allreduce(x, "ring", "fp32", "sum", 0, ex)), bits(want))
     for n in range(1, 530):
         A.ar_workspace_bytes(A.make_call(3, n, "fp32", "sum", "ring", 0, "literal"))
+    for ex in ("fused", "literal"):
+        assert np.array_equal(bits(gpu_allreduce(x, "ring", "fp32", "sum", 0, ex)), bits(want))
+    # more than 256 plans (distinct sizes) clear the plan cache: the plans a
+    # later call builds again must give the same bits
+    torch = torch_mod()
+    bufs = [torch.zeros(300, dtype=torch.float32, device="cuda") for _ in range(3)]
+    for n in range(1, 280):
+        A.ar_allreduce([b.data_ptr() for b in bufs], 3, n, "fp32", "sum", "ring")
+    torch.cuda.synchronize()
     for ex in ("fused", "literal"):
         assert np.array_equal(bits(gpu_allreduce(x, "ring", "fp32", "sum", 0, ex)), bits(want))
