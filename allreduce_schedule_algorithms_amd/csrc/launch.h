@@ -147,12 +147,12 @@ hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& w
 // One launch per run of at most max_blocks workgroups; each launch gets the
 // rank pointers advanced to its first element. The vector path's element tail
 // (past the last whole vector) goes to block 0 of the last launch.
-template <int DT, int OPK, int B>
+template <int DT, int OPK, int B, int MD>
 hipError_t direct_b(bool vec, const RankPtrs& ptrs, int P, int64_t total, int64_t max_blocks, hipStream_t st,
                     Evs ev) {
   constexpr int V = TT<DT>::V;
   constexpr int64_t elt = sizeof(typename TT<DT>::S);
-  const int64_t unit = vec ? int64_t(kThreads) * kDirectM * V : int64_t(kThreads);  // elements per workgroup
+  const int64_t unit = vec ? int64_t(kThreads) * MD * V : int64_t(kThreads);  // elements per workgroup
   const int64_t whole = vec ? total / V * V : total;  // elements the workgroups cover
   const int64_t per = max_blocks * unit;
   RankPtrs pp = ptrs;
@@ -164,8 +164,8 @@ hipError_t direct_b(bool vec, const RankPtrs& ptrs, int P, int64_t total, int64_
     const Evs ei{done == 0 ? ev.start : nullptr, last ? ev.stop : nullptr};
     const int64_t blocks = std::max<int64_t>(1, (len + unit - 1) / unit);
     if (vec) {
-      hipExtLaunchKernelGGL((k_direct<DT, OPK, true, B>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, ei.start,
-                            ei.stop, 0, pp, P, len / V, last ? total - done : len);
+      hipExtLaunchKernelGGL((k_direct<DT, OPK, true, B, MD>), dim3(unsigned(blocks)), dim3(kThreads), 0, st,
+                            ei.start, ei.stop, 0, pp, P, len / V, last ? total - done : len);
     } else {
       hipExtLaunchKernelGGL((k_direct<DT, OPK, false, B>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, ei.start,
                             ei.stop, 0, pp, P, int64_t(0), len);
@@ -177,18 +177,28 @@ hipError_t direct_b(bool vec, const RankPtrs& ptrs, int P, int64_t total, int64_
   return hipSuccess;
 }
 
+template <int DT, int OPK, int MD>
+hipError_t direct_m(bool vec, const RankPtrs& ptrs, int P, int64_t total, int64_t max_blocks, hipStream_t st,
+                    Evs ev) {
+  switch (leaf_batch(P)) {
+    case 2: return direct_b<DT, OPK, 2, MD>(vec, ptrs, P, total, max_blocks, st, ev);
+    case 3: return direct_b<DT, OPK, 3, MD>(vec, ptrs, P, total, max_blocks, st, ev);
+    case 4: return direct_b<DT, OPK, 4, MD>(vec, ptrs, P, total, max_blocks, st, ev);
+    case 5: return direct_b<DT, OPK, 5, MD>(vec, ptrs, P, total, max_blocks, st, ev);
+    case 6: return direct_b<DT, OPK, 6, MD>(vec, ptrs, P, total, max_blocks, st, ev);
+    case 7: return direct_b<DT, OPK, 7, MD>(vec, ptrs, P, total, max_blocks, st, ev);
+    default: return direct_b<DT, OPK, 8, MD>(vec, ptrs, P, total, max_blocks, st, ev);
+  }
+}
+
+// Four vectors per thread for launches of at most 2^19 vectors (a few hundred
+// workgroups) with at most 8 ranks; two otherwise.
 template <int DT, int OPK>
 hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total, int64_t max_blocks, hipStream_t st,
                            Evs ev) {
-  switch (leaf_batch(P)) {
-    case 2: return direct_b<DT, OPK, 2>(vec, ptrs, P, total, max_blocks, st, ev);
-    case 3: return direct_b<DT, OPK, 3>(vec, ptrs, P, total, max_blocks, st, ev);
-    case 4: return direct_b<DT, OPK, 4>(vec, ptrs, P, total, max_blocks, st, ev);
-    case 5: return direct_b<DT, OPK, 5>(vec, ptrs, P, total, max_blocks, st, ev);
-    case 6: return direct_b<DT, OPK, 6>(vec, ptrs, P, total, max_blocks, st, ev);
-    case 7: return direct_b<DT, OPK, 7>(vec, ptrs, P, total, max_blocks, st, ev);
-    default: return direct_b<DT, OPK, 8>(vec, ptrs, P, total, max_blocks, st, ev);
-  }
+  if (vec && P <= 8 && total / TT<DT>::V <= (int64_t(1) << 19))
+    return direct_m<DT, OPK, 4>(vec, ptrs, P, total, max_blocks, st, ev);
+  return direct_m<DT, OPK, kDirectM>(vec, ptrs, P, total, max_blocks, st, ev);
 }
 
 

@@ -69,7 +69,9 @@ WORKLOADS = {
         P=24, n=106, dtype="fp32", batch=10_000, groups=None, steps=100,
         headline=("rd", 0, "fused"),
         others=[("binomial", 0, "fused"), ("direct", 0, "fused"), ("generalized", 5, "fused"),
-                ("rd", 0, "literal"), ("binomial", 0, "literal"), ("generalized", 5, "literal")]),
+                ("generalized", 0, "fused"), ("ring", 0, "fused"),
+                ("rd", 0, "literal"), ("binomial", 0, "literal"), ("generalized", 5, "literal"),
+                ("generalized", 0, "literal")]),
     "ring_int32": dict(
         desc="5 ranks x 4096 int32 U[-2^20, 2^20], seed 0",
         P=5, n=4096, dtype="int32", batch=1, groups=None, steps=100,
