@@ -78,8 +78,10 @@ int64_t env_int(const char* name, int64_t dflt) {
   return x > 0 ? x : dflt;
 }
 
-void add_segment(std::vector<Item>& out, int64_t s0, int64_t len, int32_t tag, int V, bool vec) {
-  static const int64_t item_vec = env_int("AR_ITEM_VECTORS", 2 * kThreads);
+void add_segment(std::vector<Item>& out, int64_t s0, int64_t len, int32_t tag, int V, bool vec,
+                 int64_t vectors = 0) {
+  static const int64_t default_vec = env_int("AR_ITEM_VECTORS", 2 * kThreads);
+  const int64_t item_vec = vectors > 0 ? vectors : default_vec;
   const int64_t item_sc = kThreads;
   if (len <= 0) return;
   if (!vec) {
@@ -119,6 +121,8 @@ struct Plan {
   std::vector<std::pair<int64_t, int64_t>> launches[2];
   DevBuf packed[2];
   bool strided = false;  // fused: items are SItem (batches of short ranges)
+  int balanced = 0;       // fused: every tree a perfect binary tree of this many leaves (k_fused_balanced)
+  int md = 2;             // k_fused_balanced: vectors per thread (items of kThreads * md vectors)
   int64_t slot_bytes = 0;
   size_t ws_bytes = 0;
 };
@@ -163,6 +167,25 @@ constexpr size_t kXcdProgramBytes = 64 * 1024;
 // strided items (one element per thread across instances) instead of one item
 // per instance and range.
 constexpr int64_t kStridedMaxLen = 64;
+
+// Whether every tree of a single-tree program is a perfect binary tree of the
+// same 4 or 8 leaves: after leaf k, as many combinations as k + 1 has trailing
+// zero bits. Returns the leaf count, or 0.
+int balanced_leaves(const Schedule& s) {
+  if (s.max_trees != 1 || s.ranges.empty()) return 0;
+  int nl0 = 0;
+  for (const FusedRange& r : s.ranges) {
+    const int32_t* w = s.prog.data() + r.prog;
+    if (w[0] != 1) return 0;
+    const int nl = w[1];
+    if ((nl != 4 && nl != 8) || (nl0 && nl != nl0)) return 0;
+    const int32_t* nc = w + 3 + nl;
+    for (int k = 0; k < nl; ++k)
+      if (nc[k] != __builtin_ctz(unsigned(k + 1))) return 0;
+    nl0 = nl;
+  }
+  return nl0;
+}
 
 // Build the fused or literal item tables for one alignment mode.
 RunResult build_items(Plan& pl, bool vec) {
@@ -246,9 +269,10 @@ RunResult build_items(Plan& pl, bool vec) {
     int64_t max_len = 0;
     for (const FusedRange& r : s.ranges) max_len = std::max(max_len, r.len);
     std::vector<SItem> sitems;
+    const int64_t iv = pl.balanced ? int64_t(kThreads) * pl.md : 0;
     if (sp.batch == 1 || flat) {
       const int64_t mult = flat ? sp.batch : 1;
-      for (const FusedRange& r : s.ranges) add_segment(items, r.start, r.len * mult, r.prog, V, vec);
+      for (const FusedRange& r : s.ranges) add_segment(items, r.start, r.len * mult, r.prog, V, vec, iv);
     } else if (max_len < kStridedMaxLen) {
       // short ranges in many instances: one strided item per range and block
       // of instances; the items of one block sit next to each other, so the
@@ -260,7 +284,7 @@ RunResult build_items(Plan& pl, bool vec) {
             sitems.push_back({b0 * sp.n + r.start, r.prog, int32_t(r.len), int32_t(std::min(nb, sp.batch - b0)), 0});
     } else {
       for (int64_t b = 0; b < sp.batch; ++b)
-        for (const FusedRange& r : s.ranges) add_segment(items, b * sp.n + r.start, r.len, r.prog, V, vec);
+        for (const FusedRange& r : s.ranges) add_segment(items, b * sp.n + r.start, r.len, r.prog, V, vec, iv);
     }
     if (!pl.prog.p) {
       // the replay reads each batch's leaf ranks and combination counts as whole
@@ -331,6 +355,15 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
   pl->s = s;
   pl->exec = exec;
   pl->device = device;
+  static const bool shapes = [] {
+    const char* v = std::getenv("AR_FUSED_SHAPES");  // "0": always the register-stack replay (for comparisons)
+    return !(v && v[0] == '0');
+  }();
+  if (exec != E_LITERAL && s->fused_ok && shapes) {
+    pl->balanced = balanced_leaves(*s);
+    // four vectors per thread for short launches with few ranks, as the direct kernel
+    pl->md = spec.P <= 8 && spec.n * spec.batch / vec_width(spec.dtype) <= (int64_t(1) << 19) ? 4 : 2;
+  }
   pl->D = s->max_need <= 2 ? 2 : s->max_need <= 4 ? 4 : s->max_need <= 8 ? 8 : 16;
   int64_t slot = spec.n * spec.batch * int64_t(acc_bytes(spec.dtype));
   pl->slot_bytes = (slot + 255) / 256 * 256;
@@ -517,6 +550,10 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
         const SItem* sit = reinterpret_cast<const SItem*>(pl->items[mode].p) + off;
         AR_DISPATCH(spec.dtype, spec.op,
                     (e = launch_fused_strided_t<DT, OPK>(pl->D, TM, cnt, ptrs, sit, prog, spec.n, st, ei)));
+      } else if (pl->balanced) {
+        AR_DISPATCH(spec.dtype, spec.op,
+                    (e = launch_fused_balanced_t<DT, OPK>(pl->balanced, pl->md, cnt, ptrs, items + off, prog, st,
+                                                          ei)));
       } else {
         AR_DISPATCH(spec.dtype, spec.op,
                     (e = launch_fused_t<DT, OPK>(pl->D, TM, spec.P, pl->s->max_leaves, cnt, ptrs, items + off, prog,

@@ -411,6 +411,56 @@ __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* _
   }
 }
 
+// Single-tree programs in which every tree is a perfect binary tree of NL = 4
+// or 8 leaves, combined level by level (recursive halving and doubling give
+// these), run without the register stack. The program words still name the
+// leaf ranks (postfix order) and the output ranks; the host checks each tree's
+// combination counts against the shape. cmb(left, right) keeps the operands of
+// the postfix fold. (A chain-shaped variant for the ring measured no faster
+// than the register stack.)
+template <int DT, int OPK, int M, int NL>
+__device__ __forceinline__ void balanced_one(const RankPtrs& ptrs, const int32_t* __restrict__ w, int64_t e,
+                                             const bool (&ok)[mm<M>()]) {
+  using A = typename TT<DT>::A;
+  constexpr int N = nvals<DT, M>();
+  const int nouts = w[1];
+  const int32_t* __restrict__ leaf = w + 2;
+  const int32_t* __restrict__ outs = w + 2 + 2 * NL;
+  u32x4 raw[NL][mm<M>()];
+#pragma unroll
+  for (int k = 0; k < NL; ++k) ld_user<DT, M>(ptrs.p[leaf[k]], e, ok, raw[k]);
+  A v[NL][N];
+#pragma unroll
+  for (int k = 0; k < NL; ++k) widen<DT, M>(raw[k], v[k]);
+  // level by level: v[i] = v[2i] + v[2i+1]; reads never trail the writes
+#pragma unroll
+  for (int h = NL / 2; h >= 1; h /= 2)
+#pragma unroll
+    for (int i = 0; i < h; ++i)
+#pragma unroll
+      for (int j = 0; j < N; ++j) v[i][j] = cmb<OPK>(v[2 * i][j], v[2 * i + 1][j]);
+  if constexpr (OPK == O_AVG) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[0][j] = v[0][j] / ptrs.div;
+  }
+  st_user_all<DT, M>(ptrs, nouts, [&](int i) { return outs[i]; }, e, ok, v[0]);
+}
+
+// NL leaves per tree; M vectors per thread on the vector path (the items hold
+// kThreads * M vectors).
+template <int DT, int OPK, int M, int NL>
+__global__ __launch_bounds__(kThreads) void k_fused_balanced(RankPtrs ptrs, const Item* __restrict__ items,
+                                                             const int32_t* __restrict__ prog) {
+  constexpr int V = TT<DT>::V;
+  const Item it = items[item_index(ptrs.xcd)];
+  const int32_t* __restrict__ w = prog + it.tag + 1;  // the range's only tree
+  if (it.count > 0) {
+    for_fragments<M>(it, V, [&](int64_t e, const bool (&ok)[M]) { balanced_one<DT, OPK, M, NL>(ptrs, w, e, ok); });
+  } else {
+    for_fragments<0>(it, V, [&](int64_t e, const bool (&ok)[1]) { balanced_one<DT, OPK, 0, NL>(ptrs, w, e, ok); });
+  }
+}
+
 // Batches of short instances: a strided item covers one range of `len`
 // elements (the same offsets in every instance) across `nb` consecutive
 // instances `stride` elements apart, one element per thread: instance v / len,

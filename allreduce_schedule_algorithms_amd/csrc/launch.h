@@ -36,6 +36,9 @@ template <int DT, int OPK>
 hipError_t launch_fused_strided_t(int D, int TM, int64_t nitems, const RankPtrs& ptrs, const SItem* items,
                                   const int32_t* prog, int64_t stride, hipStream_t st, Evs ev);
 template <int DT, int OPK>
+hipError_t launch_fused_balanced_t(int nl, int M, int64_t nitems, const RankPtrs& ptrs, const Item* items,
+                                   const int32_t* prog, hipStream_t st, Evs ev);
+template <int DT, int OPK>
 hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& ws, const LitWork* work,
                             const LitWork* packed, hipStream_t st, Evs ev);
 template <int DT, int OPK>
@@ -107,6 +110,23 @@ hipError_t launch_fused_t(int D, int TM, int P, int leaves, int64_t nitems, cons
       default: hipExtLaunchKernelGGL((k_fused<DT, OPK, 8, kMaxFusedTrees, 8>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog); break;
     }
   }
+  return hipGetLastError();
+}
+
+// nl = 4 or 8 leaves per tree; M = 2 or 4 vectors per thread.
+template <int DT, int OPK>
+hipError_t launch_fused_balanced_t(int nl, int M, int64_t nitems, const RankPtrs& ptrs, const Item* items,
+                                   const int32_t* prog, hipStream_t st, Evs ev) {
+  const dim3 g{unsigned(nitems), 1, 1};
+  const dim3 b{unsigned(kThreads), 1, 1};
+#define AR_BAL(M_, NL_) \
+  hipExtLaunchKernelGGL((k_fused_balanced<DT, OPK, M_, NL_>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog)
+  if (M == 4) {
+    if (nl == 4) AR_BAL(4, 4); else AR_BAL(4, 8);
+  } else {
+    if (nl == 4) AR_BAL(2, 4); else AR_BAL(2, 8);
+  }
+#undef AR_BAL
   return hipGetLastError();
 }
 
@@ -205,6 +225,8 @@ hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total,
 #define AR_INSTANTIATE_LAUNCHES(DT, OPK)                                                                    \
   template hipError_t launch_fused_t<DT, OPK>(int, int, int, int, int64_t, const RankPtrs&, const Item*,    \
                                               const int32_t*, hipStream_t, Evs);                            \
+  template hipError_t launch_fused_balanced_t<DT, OPK>(int, int, int64_t, const RankPtrs&, const Item*,     \
+                                                       const int32_t*, hipStream_t, Evs);                   \
   template hipError_t launch_fused_strided_t<DT, OPK>(int, int, int64_t, const RankPtrs&, const SItem*,     \
                                                       const int32_t*, int64_t, hipStream_t, Evs);          \
   template hipError_t launch_literal_t<DT, OPK>(int64_t, const RankPtrs&, const WsDesc&, const LitWork*,    \

@@ -75,6 +75,31 @@ def test_misaligned_buffers_take_element_path(algo):
                 assert np.array_equal(bits(got), bits(want)), (algo, dtype, r, ex)
 
 
+@pytest.mark.parametrize("dtype", ["int32", "fp32", "bf16"])
+def test_perfect_binary_trees(dtype):
+    # schedules whose every tree is a perfect binary tree of 4 or 8 leaves run
+    # the level-by-level kernel (vector and element paths, 2 or 4 vectors per
+    # thread by size); the halves and batches as well
+    import allreduce_schedule_algorithms_amd as A
+    from oracle import schedules as sch
+    ops = ("sum", "max") + (("avg",) if dtype != "int32" else ())
+    for P in (4, 8):
+        for algo, groups in (("rh_rd", None), ("rd", None), ("generalized_xor", None), ("generalized", [2, P // 2])):
+            info = A.ar_schedule_build(A.make_call(P, 4099, dtype, "sum", algo, groups=groups)).info()
+            assert info.max_trees == 1 and info.max_leaves == P
+            for n, mis in ((37, False), (4099, True), (1 << 17, False), (3 << 20, False)):
+                x = inputs.make(dtype, P, n, seed=P + n)
+                for op in ops:
+                    want = oracle.allreduce(x, algo, dtype, op, factors=groups if algo == "generalized" else None)
+                    got = gpu_allreduce(x, algo, dtype, op, 0, "fused", groups, misalign=mis)
+                    assert np.array_equal(bits(got), bits(want)), (P, algo, n, mis, op)
+        x = inputs.make(dtype, P, 4099 * 3, seed=P)
+        want = sch.reduce_scatter(x.reshape(P, 3, 4099), "rh_rd", dtype, "sum")
+        got = gpu_allreduce(x, "rh_rd", dtype, "sum", 0, "fused", batch=3, collective="reduce_scatter")
+        own = half_owner(4099, P)
+        assert np.array_equal(bits(got.reshape(P, 3, 4099)[own, :, np.arange(4099)].T), bits(want)), P
+
+
 @pytest.mark.parametrize("algo", ["ring", "rh_rd", "binomial", "generalized", "ahc"])
 def test_batched_instances(algo):
     P, n, B = 6, 53, 7
