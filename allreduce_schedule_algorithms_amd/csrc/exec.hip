@@ -122,6 +122,7 @@ struct Plan {
   DevBuf packed[2];
   bool strided = false;  // fused: items are SItem (batches of short ranges)
   int balanced = 0;       // fused: every tree a perfect binary tree of this many leaves (k_fused_balanced)
+  RankTab tab;            // k_fused_balanced: leaf and output ranks per range
   int md = 2;             // k_fused_balanced: vectors per thread (items of kThreads * md vectors)
   int64_t slot_bytes = 0;
   size_t ws_bytes = 0;
@@ -168,20 +169,29 @@ constexpr size_t kXcdProgramBytes = 64 * 1024;
 // per instance and range.
 constexpr int64_t kStridedMaxLen = 64;
 
-// Whether every tree of a single-tree program is a perfect binary tree of the
-// same 4 or 8 leaves: after leaf k, as many combinations as k + 1 has trailing
-// zero bits. Returns the leaf count, or 0.
-int balanced_leaves(const Schedule& s) {
-  if (s.max_trees != 1 || s.ranges.empty()) return 0;
+// Whether every tree of a single-tree program of at most kMaxTabRanges ranges
+// is a perfect binary tree of the same 4 or 8 leaves (after leaf k, as many
+// combinations as k + 1 has trailing zero bits) with at most 8 outputs.
+// Returns the leaf count and fills the rank table, or returns 0. Unused table
+// entries stay rank 0, a valid buffer the kernel never touches for them.
+int balanced_leaves(const Schedule& s, RankTab* tab) {
+  if (s.max_trees != 1 || s.ranges.empty() || s.ranges.size() > size_t(kMaxTabRanges)) return 0;
   int nl0 = 0;
-  for (const FusedRange& r : s.ranges) {
-    const int32_t* w = s.prog.data() + r.prog;
+  std::memset(tab, 0, sizeof(*tab));
+  for (size_t i = 0; i < s.ranges.size(); ++i) {
+    const int32_t* w = s.prog.data() + s.ranges[i].prog;
     if (w[0] != 1) return 0;
-    const int nl = w[1];
-    if ((nl != 4 && nl != 8) || (nl0 && nl != nl0)) return 0;
-    const int32_t* nc = w + 3 + nl;
-    for (int k = 0; k < nl; ++k)
+    const int nl = w[1], nouts = w[2];
+    if ((nl != 4 && nl != 8) || (nl0 && nl != nl0) || nouts < 1 || nouts > 8) return 0;
+    const int32_t* leaf = w + 3;
+    const int32_t* nc = leaf + nl;
+    const int32_t* outs = nc + nl;
+    for (int k = 0; k < nl; ++k) {
       if (nc[k] != __builtin_ctz(unsigned(k + 1))) return 0;
+      tab->leaf[i][k] = uint8_t(leaf[k]);
+    }
+    for (int k = 0; k < nouts; ++k) tab->out[i][k] = uint8_t(outs[k]);
+    tab->nouts[i] = uint8_t(nouts);
     nl0 = nl;
   }
   return nl0;
@@ -269,10 +279,13 @@ RunResult build_items(Plan& pl, bool vec) {
     int64_t max_len = 0;
     for (const FusedRange& r : s.ranges) max_len = std::max(max_len, r.len);
     std::vector<SItem> sitems;
+    // the balanced kernel finds a range's ranks by its index in the rank table
     const int64_t iv = pl.balanced ? int64_t(kThreads) * pl.md : 0;
+    auto tag_of = [&](size_t i) { return pl.balanced ? int32_t(i) : s.ranges[i].prog; };
     if (sp.batch == 1 || flat) {
       const int64_t mult = flat ? sp.batch : 1;
-      for (const FusedRange& r : s.ranges) add_segment(items, r.start, r.len * mult, r.prog, V, vec, iv);
+      for (size_t i = 0; i < s.ranges.size(); ++i)
+        add_segment(items, s.ranges[i].start, s.ranges[i].len * mult, tag_of(i), V, vec, iv);
     } else if (max_len < kStridedMaxLen) {
       // short ranges in many instances: one strided item per range and block
       // of instances; the items of one block sit next to each other, so the
@@ -284,7 +297,8 @@ RunResult build_items(Plan& pl, bool vec) {
             sitems.push_back({b0 * sp.n + r.start, r.prog, int32_t(r.len), int32_t(std::min(nb, sp.batch - b0)), 0});
     } else {
       for (int64_t b = 0; b < sp.batch; ++b)
-        for (const FusedRange& r : s.ranges) add_segment(items, b * sp.n + r.start, r.len, r.prog, V, vec, iv);
+        for (size_t i = 0; i < s.ranges.size(); ++i)
+          add_segment(items, b * sp.n + s.ranges[i].start, s.ranges[i].len, tag_of(i), V, vec, iv);
     }
     if (!pl.prog.p) {
       // the replay reads each batch's leaf ranks and combination counts as whole
@@ -360,7 +374,7 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
     return !(v && v[0] == '0');
   }();
   if (exec != E_LITERAL && s->fused_ok && shapes) {
-    pl->balanced = balanced_leaves(*s);
+    pl->balanced = balanced_leaves(*s, &pl->tab);
     // four vectors per thread for short launches with few ranks, as the direct kernel
     pl->md = spec.P <= 8 && spec.n * spec.batch / vec_width(spec.dtype) <= (int64_t(1) << 19) ? 4 : 2;
   }
@@ -552,8 +566,8 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
                     (e = launch_fused_strided_t<DT, OPK>(pl->D, TM, cnt, ptrs, sit, prog, spec.n, st, ei)));
       } else if (pl->balanced) {
         AR_DISPATCH(spec.dtype, spec.op,
-                    (e = launch_fused_balanced_t<DT, OPK>(pl->balanced, pl->md, cnt, ptrs, items + off, prog, st,
-                                                          ei)));
+                    (e = launch_fused_balanced_t<DT, OPK>(pl->balanced, pl->md, cnt, ptrs, items + off, pl->tab,
+                                                          st, ei)));
       } else {
         AR_DISPATCH(spec.dtype, spec.op,
                     (e = launch_fused_t<DT, OPK>(pl->D, TM, spec.P, pl->s->max_leaves, cnt, ptrs, items + off, prog,

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstring>
 
 #include "kernels.h"
 
@@ -37,7 +38,7 @@ hipError_t launch_fused_strided_t(int D, int TM, int64_t nitems, const RankPtrs&
                                   const int32_t* prog, int64_t stride, hipStream_t st, Evs ev);
 template <int DT, int OPK>
 hipError_t launch_fused_balanced_t(int nl, int M, int64_t nitems, const RankPtrs& ptrs, const Item* items,
-                                   const int32_t* prog, hipStream_t st, Evs ev);
+                                   const RankTab& tab, hipStream_t st, Evs ev);
 template <int DT, int OPK>
 hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& ws, const LitWork* work,
                             const LitWork* packed, hipStream_t st, Evs ev);
@@ -116,11 +117,22 @@ hipError_t launch_fused_t(int D, int TM, int P, int leaves, int64_t nitems, cons
 // nl = 4 or 8 leaves per tree; M = 2 or 4 vectors per thread.
 template <int DT, int OPK>
 hipError_t launch_fused_balanced_t(int nl, int M, int64_t nitems, const RankPtrs& ptrs, const Item* items,
-                                   const int32_t* prog, hipStream_t st, Evs ev) {
+                                   const RankTab& tab, hipStream_t st, Evs ev) {
   const dim3 g{unsigned(nitems), 1, 1};
   const dim3 b{unsigned(kThreads), 1, 1};
+  BalPtrs bp;
+  std::memset(&bp, 0, sizeof(bp));
+  for (int r = 0; r < kMaxTabRanges; ++r) {
+    for (int k = 0; k < 8; ++k) {
+      bp.leaf[r][k] = ptrs.p[tab.leaf[r][k]];
+      bp.out[r][k] = ptrs.p[tab.out[r][k]];
+    }
+    bp.nouts[r] = tab.nouts[r];
+  }
+  bp.div = ptrs.div;
+  bp.xcd = ptrs.xcd;
 #define AR_BAL(M_, NL_) \
-  hipExtLaunchKernelGGL((k_fused_balanced<DT, OPK, M_, NL_>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog)
+  hipExtLaunchKernelGGL((k_fused_balanced<DT, OPK, M_, NL_>), g, b, 0, st, ev.start, ev.stop, 0, bp, items)
   if (M == 4) {
     if (nl == 4) AR_BAL(4, 4); else AR_BAL(4, 8);
   } else {
@@ -226,7 +238,7 @@ hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total,
   template hipError_t launch_fused_t<DT, OPK>(int, int, int, int, int64_t, const RankPtrs&, const Item*,    \
                                               const int32_t*, hipStream_t, Evs);                            \
   template hipError_t launch_fused_balanced_t<DT, OPK>(int, int, int64_t, const RankPtrs&, const Item*,     \
-                                                       const int32_t*, hipStream_t, Evs);                   \
+                                                       const RankTab&, hipStream_t, Evs);                   \
   template hipError_t launch_fused_strided_t<DT, OPK>(int, int, int64_t, const RankPtrs&, const SItem*,     \
                                                       const int32_t*, int64_t, hipStream_t, Evs);          \
   template hipError_t launch_literal_t<DT, OPK>(int64_t, const RankPtrs&, const WsDesc&, const LitWork*,    \

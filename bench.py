@@ -530,9 +530,10 @@ def parse_key(key):
 
 
 def load_traffic(wl_name, key):
-    """HBM bytes per launch from the committed counter summary (FETCH_SIZE and
-    WRITE_SIZE, each scaled by what it reads for a plain copy of known size), or
-    None when the summary was taken from a different kernel source."""
+    """The committed counter summary's record for this workload and schedule:
+    HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, each scaled by what it
+    reads for a plain copy of known size) and the kernel the trace names; None
+    when the summary was taken from a different kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -543,8 +544,7 @@ def load_traffic(wl_name, key):
         return None
     if t.get("kernel_hash") != kernel_source_hash():
         return None
-    rec = t.get("entries", {}).get(f"{wl_name}/{key}")
-    return rec.get("bytes_per_launch") if rec else None
+    return t.get("entries", {}).get(f"{wl_name}/{key}")
 
 
 def main():
@@ -634,9 +634,13 @@ def main():
     cst = s.cost()
     value = head["GBps"]
     achieved = head["kernel_GBps"]
-    traffic = load_traffic(args.workload, hkey)
-    kernel = ("k_literal" if ex == "literal" else
-              "k_direct" if (algo == "direct" and ex == "fused" and h["coll"] == "allreduce") else "k_fused")
+    rec = load_traffic(args.workload, hkey)
+    traffic = rec.get("bytes_per_launch") if rec else None
+    if rec and rec.get("kernel"):  # the trace's dominant kernel, e.g. "ar::k_fused_balanced<1, 0, 4, 8>"
+        kernel = rec["kernel"].split("::")[-1].split("<")[0]
+    else:  # the family; the fused executor picks one of its kernels by program shape and size
+        kernel = ("k_literal" if ex == "literal" else
+                  "k_direct" if (algo == "direct" and ex == "fused" and h["coll"] == "allreduce") else "k_fused")
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": kernel,
