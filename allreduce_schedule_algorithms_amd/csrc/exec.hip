@@ -121,9 +121,10 @@ struct Plan {
   std::vector<std::pair<int64_t, int64_t>> launches[2];
   DevBuf packed[2];
   bool strided = false;  // fused: items are SItem (batches of short ranges)
-  int balanced = 0;       // fused: every tree a perfect binary tree of this many leaves (k_fused_balanced)
-  RankTab tab;            // k_fused_balanced: leaf and output ranks per range
-  int md = 2;             // k_fused_balanced: vectors per thread (items of kThreads * md vectors)
+  int shape = SH_NONE;    // fused: every tree of this fixed shape (k_fused_fixed)
+  int shape_nl = 0;       // its leaves per tree
+  RankTab tab;            // k_fused_fixed: leaf and output ranks per range
+  int md = 2;             // k_fused_fixed: vectors per thread (items of kThreads * md vectors)
   int64_t slot_bytes = 0;
   size_t ws_bytes = 0;
 };
@@ -170,31 +171,41 @@ constexpr size_t kXcdProgramBytes = 64 * 1024;
 constexpr int64_t kStridedMaxLen = 64;
 
 // Whether every tree of a single-tree program of at most kMaxTabRanges ranges
-// is a perfect binary tree of the same 4 or 8 leaves (after leaf k, as many
-// combinations as k + 1 has trailing zero bits) with at most 8 outputs.
-// Returns the leaf count and fills the rank table, or returns 0. Unused table
-// entries stay rank 0, a valid buffer the kernel never touches for them.
-int balanced_leaves(const Schedule& s, RankTab* tab) {
-  if (s.max_trees != 1 || s.ranges.empty() || s.ranges.size() > size_t(kMaxTabRanges)) return 0;
-  int nl0 = 0;
+// has the same fixed shape and leaf count, with at most 8 outputs:
+//  - SH_BALANCED: a perfect binary tree of 4 or 8 leaves (after leaf k, as many
+//    combinations as k + 1 has trailing zero bits);
+//  - SH_CHAIN: 2..8 leaves with one combination after every leaf but the first.
+// Returns the shape (leaf count in *nl, ranks in *tab), or SH_NONE. Unused
+// table entries stay rank 0, a valid buffer the kernel never touches for them.
+// Single-leaf trees (the all-gather's copies) keep the register-stack replay,
+// which measured faster for them.
+int fixed_shape(const Schedule& s, RankTab* tab, int* nl_out) {
+  if (s.max_trees != 1 || s.ranges.empty() || s.ranges.size() > size_t(kMaxTabRanges)) return SH_NONE;
+  int shape = SH_NONE, nl0 = 0;
   std::memset(tab, 0, sizeof(*tab));
   for (size_t i = 0; i < s.ranges.size(); ++i) {
     const int32_t* w = s.prog.data() + s.ranges[i].prog;
-    if (w[0] != 1) return 0;
+    if (w[0] != 1) return SH_NONE;
     const int nl = w[1], nouts = w[2];
-    if ((nl != 4 && nl != 8) || (nl0 && nl != nl0) || nouts < 1 || nouts > 8) return 0;
+    if (nl < 2 || nl > 8 || (nl0 && nl != nl0) || nouts < 1 || nouts > 8) return SH_NONE;
     const int32_t* leaf = w + 3;
     const int32_t* nc = leaf + nl;
     const int32_t* outs = nc + nl;
+    bool chain = nc[0] == 0, bal = nl == 4 || nl == 8;
     for (int k = 0; k < nl; ++k) {
-      if (nc[k] != __builtin_ctz(unsigned(k + 1))) return 0;
+      chain = chain && (k == 0 || nc[k] == 1);
+      bal = bal && nc[k] == __builtin_ctz(unsigned(k + 1));
       tab->leaf[i][k] = uint8_t(leaf[k]);
     }
+    const int sh = bal ? SH_BALANCED : chain ? SH_CHAIN : SH_NONE;
+    if (sh == SH_NONE || (shape != SH_NONE && sh != shape)) return SH_NONE;
     for (int k = 0; k < nouts; ++k) tab->out[i][k] = uint8_t(outs[k]);
     tab->nouts[i] = uint8_t(nouts);
+    shape = sh;
     nl0 = nl;
   }
-  return nl0;
+  *nl_out = nl0;
+  return shape;
 }
 
 // Build the fused or literal item tables for one alignment mode.
@@ -279,9 +290,10 @@ RunResult build_items(Plan& pl, bool vec) {
     int64_t max_len = 0;
     for (const FusedRange& r : s.ranges) max_len = std::max(max_len, r.len);
     std::vector<SItem> sitems;
-    // the balanced kernel finds a range's ranks by its index in the rank table
-    const int64_t iv = pl.balanced ? int64_t(kThreads) * pl.md : 0;
-    auto tag_of = [&](size_t i) { return pl.balanced ? int32_t(i) : s.ranges[i].prog; };
+    // the fixed-shape kernel finds a range's buffers by its index in the table
+    const bool fixed = pl.shape != SH_NONE;
+    const int64_t iv = fixed ? int64_t(kThreads) * pl.md : 0;
+    auto tag_of = [&](size_t i) { return fixed ? int32_t(i) : s.ranges[i].prog; };
     if (sp.batch == 1 || flat) {
       const int64_t mult = flat ? sp.batch : 1;
       for (size_t i = 0; i < s.ranges.size(); ++i)
@@ -374,7 +386,7 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
     return !(v && v[0] == '0');
   }();
   if (exec != E_LITERAL && s->fused_ok && shapes) {
-    pl->balanced = balanced_leaves(*s, &pl->tab);
+    pl->shape = fixed_shape(*s, &pl->tab, &pl->shape_nl);
     // four vectors per thread for short launches with few ranks, as the direct kernel
     pl->md = spec.P <= 8 && spec.n * spec.batch / vec_width(spec.dtype) <= (int64_t(1) << 19) ? 4 : 2;
   }
@@ -564,10 +576,10 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
         const SItem* sit = reinterpret_cast<const SItem*>(pl->items[mode].p) + off;
         AR_DISPATCH(spec.dtype, spec.op,
                     (e = launch_fused_strided_t<DT, OPK>(pl->D, TM, cnt, ptrs, sit, prog, spec.n, st, ei)));
-      } else if (pl->balanced) {
+      } else if (pl->shape != SH_NONE) {
         AR_DISPATCH(spec.dtype, spec.op,
-                    (e = launch_fused_balanced_t<DT, OPK>(pl->balanced, pl->md, cnt, ptrs, items + off, pl->tab,
-                                                          st, ei)));
+                    (e = launch_fused_fixed_t<DT, OPK>(pl->shape, pl->shape_nl, pl->md, cnt, ptrs, items + off,
+                                                       pl->tab, st, ei)));
       } else {
         AR_DISPATCH(spec.dtype, spec.op,
                     (e = launch_fused_t<DT, OPK>(pl->D, TM, spec.P, pl->s->max_leaves, cnt, ptrs, items + off, prog,

@@ -411,23 +411,27 @@ __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* _
   }
 }
 
-// Single-tree programs in which every tree is a perfect binary tree of NL = 4
-// or 8 leaves, combined level by level (recursive halving and doubling give
-// these), run without the register stack. The host checks each tree's
-// combination counts against the shape and, for at most kMaxTabRanges ranges,
-// passes the buffer pointers of every range's leaves (postfix order) and
-// outputs as a kernel argument: the data loads then wait on no program read
-// and no rank lookup (measured on 8 x 2^20 fp32: 12.2 us with the ranks read
-// from the program words, 11.9 with a rank table, 11.6 with the pointers).
-// cmb(left, right) keeps the operands of the postfix fold. (A chain-shaped
-// variant for the ring measured no faster than the register stack.)
+// Single-tree programs of at most kMaxTabRanges ranges in which every tree has
+// one fixed shape run without the register stack:
+//  - SH_BALANCED: a perfect binary tree of NL = 4 or 8 leaves, combined level
+//    by level (recursive halving and doubling, the generalized algorithm over
+//    Z_2^k give these);
+//  - SH_CHAIN: ((l0 + l1) + l2) + ... over NL = 2..8 leaves (the ring and the
+//    pipelined chain give these).
+// The host checks each tree's combination counts against the shape and passes,
+// per call, the buffer pointers of every range's leaves (postfix order) and
+// outputs as a kernel argument: the data loads then wait on no program read and
+// no rank lookup (measured on 8 x 2^20 fp32 halving + doubling: 12.2 us with
+// the ranks read from the program words, 11.9 with a rank table, 11.6 with the
+// pointers). cmb(left, right) keeps the operands of the postfix fold.
 constexpr int kMaxTabRanges = 8;
-struct RankTab {  // host side: ranks per range, turned into BalPtrs per call
+enum : int { SH_NONE = 0, SH_BALANCED = 1, SH_CHAIN = 2 };
+struct RankTab {  // host side: ranks per range, turned into FixPtrs per call
   uint8_t leaf[kMaxTabRanges][8];
   uint8_t out[kMaxTabRanges][8];
   uint8_t nouts[kMaxTabRanges];
 };
-struct BalPtrs {
+struct FixPtrs {
   void* leaf[kMaxTabRanges][8];  // range r's leaf buffers, postfix order
   void* out[kMaxTabRanges][8];   // its output buffers
   uint8_t nouts[kMaxTabRanges];
@@ -435,43 +439,50 @@ struct BalPtrs {
   int32_t xcd;                   // as RankPtrs::xcd
 };
 
-template <int DT, int OPK, int M, int NL>
-__device__ __forceinline__ void balanced_one(const BalPtrs& bp, int r, int64_t e, const bool (&ok)[mm<M>()]) {
+template <int DT, int OPK, int SH, int M, int NL>
+__device__ __forceinline__ void fixed_one(const FixPtrs& fp, int r, int64_t e, const bool (&ok)[mm<M>()]) {
   using A = typename TT<DT>::A;
   constexpr int N = nvals<DT, M>();
   u32x4 raw[NL][mm<M>()];
 #pragma unroll
-  for (int k = 0; k < NL; ++k) ld_user<DT, M>(bp.leaf[r][k], e, ok, raw[k]);
+  for (int k = 0; k < NL; ++k) ld_user<DT, M>(fp.leaf[r][k], e, ok, raw[k]);
   A v[NL][N];
 #pragma unroll
   for (int k = 0; k < NL; ++k) widen<DT, M>(raw[k], v[k]);
-  // level by level: v[i] = v[2i] + v[2i+1]; reads never trail the writes
+  if constexpr (SH == SH_BALANCED) {
+    // level by level: v[i] = v[2i] + v[2i+1]; reads never trail the writes
 #pragma unroll
-  for (int h = NL / 2; h >= 1; h /= 2)
+    for (int h = NL / 2; h >= 1; h /= 2)
 #pragma unroll
-    for (int i = 0; i < h; ++i)
+      for (int i = 0; i < h; ++i)
 #pragma unroll
-      for (int j = 0; j < N; ++j) v[i][j] = cmb<OPK>(v[2 * i][j], v[2 * i + 1][j]);
+        for (int j = 0; j < N; ++j) v[i][j] = cmb<OPK>(v[2 * i][j], v[2 * i + 1][j]);
+  } else {
+#pragma unroll
+    for (int k = 1; k < NL; ++k)
+#pragma unroll
+      for (int j = 0; j < N; ++j) v[0][j] = cmb<OPK>(v[0][j], v[k][j]);
+  }
   if constexpr (OPK == O_AVG) {
 #pragma unroll
-    for (int j = 0; j < N; ++j) v[0][j] = v[0][j] / bp.div;
+    for (int j = 0; j < N; ++j) v[0][j] = v[0][j] / fp.div;
   }
-  const int no = bp.nouts[r];
+  const int no = fp.nouts[r];
 #pragma unroll
   for (int k = 0; k < 8; ++k)
-    if (k < no) st_user<DT, M>(bp.out[r][k], e, ok, v[0]);
+    if (k < no) st_user<DT, M>(fp.out[r][k], e, ok, v[0]);
 }
 
 // NL leaves per tree; M vectors per thread on the vector path (the items hold
 // kThreads * M vectors); an item's tag is its range's index.
-template <int DT, int OPK, int M, int NL>
-__global__ __launch_bounds__(kThreads) void k_fused_balanced(BalPtrs bp, const Item* __restrict__ items) {
+template <int DT, int OPK, int SH, int M, int NL>
+__global__ __launch_bounds__(kThreads) void k_fused_fixed(FixPtrs fp, const Item* __restrict__ items) {
   constexpr int V = TT<DT>::V;
-  const Item it = items[item_index(bp.xcd)];
+  const Item it = items[item_index(fp.xcd)];
   if (it.count > 0) {
-    for_fragments<M>(it, V, [&](int64_t e, const bool (&ok)[M]) { balanced_one<DT, OPK, M, NL>(bp, it.tag, e, ok); });
+    for_fragments<M>(it, V, [&](int64_t e, const bool (&ok)[M]) { fixed_one<DT, OPK, SH, M, NL>(fp, it.tag, e, ok); });
   } else {
-    for_fragments<0>(it, V, [&](int64_t e, const bool (&ok)[1]) { balanced_one<DT, OPK, 0, NL>(bp, it.tag, e, ok); });
+    for_fragments<0>(it, V, [&](int64_t e, const bool (&ok)[1]) { fixed_one<DT, OPK, SH, 0, NL>(fp, it.tag, e, ok); });
   }
 }
 

@@ -37,8 +37,8 @@ template <int DT, int OPK>
 hipError_t launch_fused_strided_t(int D, int TM, int64_t nitems, const RankPtrs& ptrs, const SItem* items,
                                   const int32_t* prog, int64_t stride, hipStream_t st, Evs ev);
 template <int DT, int OPK>
-hipError_t launch_fused_balanced_t(int nl, int M, int64_t nitems, const RankPtrs& ptrs, const Item* items,
-                                   const RankTab& tab, hipStream_t st, Evs ev);
+hipError_t launch_fused_fixed_t(int shape, int nl, int M, int64_t nitems, const RankPtrs& ptrs, const Item* items,
+                                const RankTab& tab, hipStream_t st, Evs ev);
 template <int DT, int OPK>
 hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& ws, const LitWork* work,
                             const LitWork* packed, hipStream_t st, Evs ev);
@@ -114,31 +114,47 @@ hipError_t launch_fused_t(int D, int TM, int P, int leaves, int64_t nitems, cons
   return hipGetLastError();
 }
 
-// nl = 4 or 8 leaves per tree; M = 2 or 4 vectors per thread.
+// shape: SH_BALANCED (nl = 4 or 8) or SH_CHAIN (nl = 2..8) leaves per tree;
+// M = 2 or 4 vectors per thread.
 template <int DT, int OPK>
-hipError_t launch_fused_balanced_t(int nl, int M, int64_t nitems, const RankPtrs& ptrs, const Item* items,
-                                   const RankTab& tab, hipStream_t st, Evs ev) {
+hipError_t launch_fused_fixed_t(int shape, int nl, int M, int64_t nitems, const RankPtrs& ptrs, const Item* items,
+                                const RankTab& tab, hipStream_t st, Evs ev) {
   const dim3 g{unsigned(nitems), 1, 1};
   const dim3 b{unsigned(kThreads), 1, 1};
-  BalPtrs bp;
-  std::memset(&bp, 0, sizeof(bp));
+  FixPtrs fp;
+  std::memset(&fp, 0, sizeof(fp));
   for (int r = 0; r < kMaxTabRanges; ++r) {
     for (int k = 0; k < 8; ++k) {
-      bp.leaf[r][k] = ptrs.p[tab.leaf[r][k]];
-      bp.out[r][k] = ptrs.p[tab.out[r][k]];
+      fp.leaf[r][k] = ptrs.p[tab.leaf[r][k]];
+      fp.out[r][k] = ptrs.p[tab.out[r][k]];
     }
-    bp.nouts[r] = tab.nouts[r];
+    fp.nouts[r] = tab.nouts[r];
   }
-  bp.div = ptrs.div;
-  bp.xcd = ptrs.xcd;
-#define AR_BAL(M_, NL_) \
-  hipExtLaunchKernelGGL((k_fused_balanced<DT, OPK, M_, NL_>), g, b, 0, st, ev.start, ev.stop, 0, bp, items)
-  if (M == 4) {
-    if (nl == 4) AR_BAL(4, 4); else AR_BAL(4, 8);
+  fp.div = ptrs.div;
+  fp.xcd = ptrs.xcd;
+#define AR_FIX(SH_, M_, NL_) \
+  hipExtLaunchKernelGGL((k_fused_fixed<DT, OPK, SH_, M_, NL_>), g, b, 0, st, ev.start, ev.stop, 0, fp, items)
+#define AR_CHAIN(M_)                                       \
+  switch (nl) {                                            \
+    case 2: AR_FIX(SH_CHAIN, M_, 2); break;                \
+    case 3: AR_FIX(SH_CHAIN, M_, 3); break;                \
+    case 4: AR_FIX(SH_CHAIN, M_, 4); break;                \
+    case 5: AR_FIX(SH_CHAIN, M_, 5); break;                \
+    case 6: AR_FIX(SH_CHAIN, M_, 6); break;                \
+    case 7: AR_FIX(SH_CHAIN, M_, 7); break;                \
+    default: AR_FIX(SH_CHAIN, M_, 8); break;               \
+  }
+  if (shape == SH_BALANCED) {
+    if (M == 4) {
+      if (nl == 4) AR_FIX(SH_BALANCED, 4, 4); else AR_FIX(SH_BALANCED, 4, 8);
+    } else {
+      if (nl == 4) AR_FIX(SH_BALANCED, 2, 4); else AR_FIX(SH_BALANCED, 2, 8);
+    }
   } else {
-    if (nl == 4) AR_BAL(2, 4); else AR_BAL(2, 8);
+    if (M == 4) { AR_CHAIN(4) } else { AR_CHAIN(2) }
   }
-#undef AR_BAL
+#undef AR_CHAIN
+#undef AR_FIX
   return hipGetLastError();
 }
 
@@ -237,8 +253,8 @@ hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total,
 #define AR_INSTANTIATE_LAUNCHES(DT, OPK)                                                                    \
   template hipError_t launch_fused_t<DT, OPK>(int, int, int, int, int64_t, const RankPtrs&, const Item*,    \
                                               const int32_t*, hipStream_t, Evs);                            \
-  template hipError_t launch_fused_balanced_t<DT, OPK>(int, int, int64_t, const RankPtrs&, const Item*,     \
-                                                       const RankTab&, hipStream_t, Evs);                   \
+  template hipError_t launch_fused_fixed_t<DT, OPK>(int, int, int, int64_t, const RankPtrs&, const Item*,   \
+                                                    const RankTab&, hipStream_t, Evs);                      \
   template hipError_t launch_fused_strided_t<DT, OPK>(int, int, int64_t, const RankPtrs&, const SItem*,     \
                                                       const int32_t*, int64_t, hipStream_t, Evs);          \
   template hipError_t launch_literal_t<DT, OPK>(int64_t, const RankPtrs&, const WsDesc&, const LitWork*,    \

@@ -100,6 +100,27 @@ def test_perfect_binary_trees(dtype):
         assert np.array_equal(bits(got.reshape(P, 3, 4099)[own, :, np.arange(4099)].T), bits(want)), P
 
 
+@pytest.mark.parametrize("dtype", ["int32", "fp32", "bf16"])
+def test_chain_trees(dtype):
+    # schedules whose every tree is a chain of 2..8 leaves (ring, pipelined
+    # chain) run the fixed-shape kernel; the reduce-scatter half as well
+    from oracle import schedules as sch
+    ops = ("sum", "max") + (("avg",) if dtype != "int32" else ())
+    for P in (2, 3, 5, 7, 8):
+        for algo, knob in (("ring", 0), ("chain", 1), ("chain", 3)):
+            for n, mis in ((37, False), (4099, True), (1 << 17, False), (3 << 20, False)):
+                x = inputs.make(dtype, P, n, seed=P * 3 + n)
+                for op in ops:
+                    want = oracle.allreduce(x, algo, dtype, op, knob=knob)
+                    got = gpu_allreduce(x, algo, dtype, op, knob, "fused", misalign=mis)
+                    assert np.array_equal(bits(got), bits(want)), (P, algo, knob, n, mis, op)
+        x = inputs.make(dtype, P, 4099 * 3, seed=P)
+        want = sch.reduce_scatter(x.reshape(P, 3, 4099), "ring", dtype, "sum")
+        got = gpu_allreduce(x, "ring", dtype, "sum", 0, "fused", batch=3, collective="reduce_scatter")
+        own = half_owner(4099, P)
+        assert np.array_equal(bits(got.reshape(P, 3, 4099)[own, :, np.arange(4099)].T), bits(want)), P
+
+
 @pytest.mark.parametrize("algo", ["ring", "rh_rd", "binomial", "generalized", "ahc"])
 def test_batched_instances(algo):
     P, n, B = 6, 53, 7
