@@ -121,6 +121,32 @@ def test_chain_trees(dtype):
         assert np.array_equal(bits(got.reshape(P, 3, 4099)[own, :, np.arange(4099)].T), bits(want)), P
 
 
+@pytest.mark.parametrize("dtype", ["int32", "fp32", "bf16"])
+def test_one_shape_per_program(dtype):
+    # single-tree programs of at most 8 ranges whose trees all share one shape
+    # that is neither a chain nor a perfect binary tree (the generalized
+    # algorithm over Z_P, recursive doubling and halving with fold-in, the
+    # binomial tree, AHC with small groups): the register-stack replay, beside
+    # the fixed-shape kernel's Z_4 x Z_2 case
+    from oracle import schedules as sch
+    ops = ("sum", "max") + (("avg",) if dtype != "int32" else ())
+    cases = [(7, "generalized", None), (5, "generalized", None), (6, "generalized", None), (6, "rd", None),
+             (7, "binomial", None), (5, "rh_rd", None), (6, "ahc", [2, 4]), (8, "generalized", [4, 2])]
+    for P, algo, groups in cases:
+        for n, mis in ((37, False), (4099, True), (1 << 17, False), (3 << 20, False)):
+            x = inputs.make(dtype, P, n, seed=P * 5 + n)
+            for op in ops:
+                want = oracle.allreduce(x, algo, dtype, op, groups=groups if algo == "ahc" else None,
+                                        factors=groups if algo == "generalized" else None)
+                got = gpu_allreduce(x, algo, dtype, op, 0, "fused", groups, misalign=mis)
+                assert np.array_equal(bits(got), bits(want)), (P, algo, groups, n, mis, op)
+    x = inputs.make(dtype, 7, 4099 * 3, seed=7)
+    want = sch.reduce_scatter(x.reshape(7, 3, 4099), "generalized", dtype, "sum")
+    got = gpu_allreduce(x, "generalized", dtype, "sum", 0, "fused", batch=3, collective="reduce_scatter")
+    own = half_owner(4099, 7)
+    assert np.array_equal(bits(got.reshape(7, 3, 4099)[own, :, np.arange(4099)].T), bits(want))
+
+
 @pytest.mark.parametrize("algo", ["ring", "rh_rd", "binomial", "generalized", "ahc"])
 def test_batched_instances(algo):
     P, n, B = 6, 53, 7
