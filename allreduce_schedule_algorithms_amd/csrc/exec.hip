@@ -174,11 +174,10 @@ constexpr int64_t kStridedMaxLen = 64;
 // has the same fixed shape and leaf count, with at most 8 outputs:
 //  - SH_BALANCED: a perfect binary tree of 4 or 8 leaves (after leaf k, as many
 //    combinations as k + 1 has trailing zero bits);
-//  - SH_CHAIN: 2..8 leaves with one combination after every leaf but the first.
+//  - SH_CHAIN: 1..8 leaves with one combination after every leaf but the first
+//    (one leaf: the all-gather's copies).
 // Returns the shape (leaf count in *nl, ranks in *tab), or SH_NONE. Unused
 // table entries stay rank 0, a valid buffer the kernel never touches for them.
-// Single-leaf trees (the all-gather's copies) keep the register-stack replay,
-// which measured faster for them.
 int fixed_shape(const Schedule& s, RankTab* tab, int* nl_out) {
   if (s.max_trees != 1 || s.ranges.empty() || s.ranges.size() > size_t(kMaxTabRanges)) return SH_NONE;
   int shape = SH_NONE, nl0 = 0;
@@ -187,7 +186,7 @@ int fixed_shape(const Schedule& s, RankTab* tab, int* nl_out) {
     const int32_t* w = s.prog.data() + s.ranges[i].prog;
     if (w[0] != 1) return SH_NONE;
     const int nl = w[1], nouts = w[2];
-    if (nl < 2 || nl > 8 || (nl0 && nl != nl0) || nouts < 1 || nouts > 8) return SH_NONE;
+    if (nl < 1 || nl > 8 || (nl0 && nl != nl0) || nouts < 1 || nouts > 8) return SH_NONE;
     const int32_t* leaf = w + 3;
     const int32_t* nc = leaf + nl;
     const int32_t* outs = nc + nl;

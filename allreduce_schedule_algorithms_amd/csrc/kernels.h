@@ -416,8 +416,8 @@ __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* _
 //  - SH_BALANCED: a perfect binary tree of NL = 4 or 8 leaves, combined level
 //    by level (recursive halving and doubling, the generalized algorithm over
 //    Z_2^k give these);
-//  - SH_CHAIN: ((l0 + l1) + l2) + ... over NL = 2..8 leaves (the ring and the
-//    pipelined chain give these).
+//  - SH_CHAIN: ((l0 + l1) + l2) + ... over NL = 1..8 leaves (the ring and the
+//    pipelined chain give these; one leaf is the all-gather's copy).
 // The host checks each tree's combination counts against the shape and passes,
 // per call, the buffer pointers of every range's leaves (postfix order) and
 // outputs as a kernel argument: the data loads then wait on no program read and

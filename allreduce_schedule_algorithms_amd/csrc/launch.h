@@ -114,7 +114,7 @@ hipError_t launch_fused_t(int D, int TM, int P, int leaves, int64_t nitems, cons
   return hipGetLastError();
 }
 
-// shape: SH_BALANCED (nl = 4 or 8) or SH_CHAIN (nl = 2..8) leaves per tree;
+// shape: SH_BALANCED (nl = 4 or 8) or SH_CHAIN (nl = 1..8) leaves per tree;
 // M = 2 or 4 vectors per thread.
 template <int DT, int OPK>
 hipError_t launch_fused_fixed_t(int shape, int nl, int M, int64_t nitems, const RankPtrs& ptrs, const Item* items,
@@ -136,6 +136,7 @@ hipError_t launch_fused_fixed_t(int shape, int nl, int M, int64_t nitems, const 
   hipExtLaunchKernelGGL((k_fused_fixed<DT, OPK, SH_, M_, NL_>), g, b, 0, st, ev.start, ev.stop, 0, fp, items)
 #define AR_CHAIN(M_)                                       \
   switch (nl) {                                            \
+    case 1: AR_FIX(SH_CHAIN, M_, 1); break;                \
     case 2: AR_FIX(SH_CHAIN, M_, 2); break;                \
     case 3: AR_FIX(SH_CHAIN, M_, 3); break;                \
     case 4: AR_FIX(SH_CHAIN, M_, 4); break;                \

@@ -119,6 +119,11 @@ def test_chain_trees(dtype):
         got = gpu_allreduce(x, "ring", dtype, "sum", 0, "fused", batch=3, collective="reduce_scatter")
         own = half_owner(4099, P)
         assert np.array_equal(bits(got.reshape(P, 3, 4099)[own, :, np.arange(4099)].T), bits(want)), P
+        for n, mis in ((4099, True), (1 << 17, False)):  # the all-gather's single-leaf copies
+            x = inputs.make(dtype, P, n, seed=P + 2 * n)
+            want = sch.all_gather(x, "ring", dtype)
+            got = gpu_allreduce(x, "ring", dtype, "sum", 0, "fused", misalign=mis, collective="all_gather")
+            assert np.array_equal(bits(got), bits(want)), (P, n, mis)
 
 
 @pytest.mark.parametrize("dtype", ["int32", "fp32", "bf16"])
