@@ -170,41 +170,51 @@ constexpr size_t kXcdProgramBytes = 64 * 1024;
 // per instance and range.
 constexpr int64_t kStridedMaxLen = 64;
 
-// Whether every tree of a single-tree program of at most kMaxTabRanges ranges
-// has the same fixed shape and leaf count, with at most 8 outputs:
+// Whether every range of a single-tree program of at most kMaxTabRanges ranges
+// has a tree of the same shape, 1..8 leaves and at most 8 outputs, and which:
 //  - SH_BALANCED: a perfect binary tree of 4 or 8 leaves (after leaf k, as many
 //    combinations as k + 1 has trailing zero bits);
-//  - SH_CHAIN: 1..8 leaves with one combination after every leaf but the first
-//    (one leaf: the all-gather's copies).
-// Returns the shape (leaf count in *nl, ranks in *tab), or SH_NONE. Unused
-// table entries stay rank 0, a valid buffer the kernel never touches for them.
+//  - SH_CHAIN: one combination after every leaf but the first (one leaf: the
+//    all-gather's copies);
+//  - SH_STACK: any other shape of 3..8 leaves whose stack stays within 4.
+// Returns the shape (leaf count in *nl, ranks and counts in *tab), or SH_NONE.
+// Unused table entries stay rank 0, a valid buffer the kernel never touches
+// for them.
 int fixed_shape(const Schedule& s, RankTab* tab, int* nl_out) {
   if (s.max_trees != 1 || s.ranges.empty() || s.ranges.size() > size_t(kMaxTabRanges)) return SH_NONE;
-  int shape = SH_NONE, nl0 = 0;
   std::memset(tab, 0, sizeof(*tab));
+  const int32_t* nc0 = nullptr;
+  int nl0 = 0;
   for (size_t i = 0; i < s.ranges.size(); ++i) {
     const int32_t* w = s.prog.data() + s.ranges[i].prog;
     if (w[0] != 1) return SH_NONE;
     const int nl = w[1], nouts = w[2];
-    if (nl < 1 || nl > 8 || (nl0 && nl != nl0) || nouts < 1 || nouts > 8) return SH_NONE;
+    if (nl < 1 || nl > 8 || nouts < 1 || nouts > 8 || (i > 0 && nl != nl0)) return SH_NONE;
     const int32_t* leaf = w + 3;
     const int32_t* nc = leaf + nl;
     const int32_t* outs = nc + nl;
-    bool chain = nc[0] == 0, bal = nl == 4 || nl == 8;
+    if (i == 0) { nc0 = nc; nl0 = nl; }
     for (int k = 0; k < nl; ++k) {
-      chain = chain && (k == 0 || nc[k] == 1);
-      bal = bal && nc[k] == __builtin_ctz(unsigned(k + 1));
+      if (nc[k] != nc0[k]) return SH_NONE;
       tab->leaf[i][k] = uint8_t(leaf[k]);
     }
-    const int sh = bal ? SH_BALANCED : chain ? SH_CHAIN : SH_NONE;
-    if (sh == SH_NONE || (shape != SH_NONE && sh != shape)) return SH_NONE;
     for (int k = 0; k < nouts; ++k) tab->out[i][k] = uint8_t(outs[k]);
     tab->nouts[i] = uint8_t(nouts);
-    shape = sh;
-    nl0 = nl;
+  }
+  bool chain = nc0[0] == 0, bal = nl0 == 4 || nl0 == 8;
+  int depth = 0, most = 0;
+  for (int k = 0; k < nl0; ++k) {
+    chain = chain && (k == 0 || nc0[k] == 1);
+    bal = bal && nc0[k] == __builtin_ctz(unsigned(k + 1));
+    depth += 1;
+    most = std::max(most, depth);
+    depth -= nc0[k];
+    tab->nc[k] = uint8_t(nc0[k]);
   }
   *nl_out = nl0;
-  return shape;
+  if (bal) return SH_BALANCED;
+  if (chain) return SH_CHAIN;
+  return nl0 >= 3 && most <= 4 && depth == 1 ? SH_STACK : SH_NONE;
 }
 
 // Build the fused or literal item tables for one alignment mode.

@@ -417,7 +417,12 @@ __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* _
 //    by level (recursive halving and doubling, the generalized algorithm over
 //    Z_2^k give these);
 //  - SH_CHAIN: ((l0 + l1) + l2) + ... over NL = 1..8 leaves (the ring and the
-//    pipelined chain give these; one leaf is the all-gather's copy).
+//    pipelined chain give these; one leaf is the all-gather's copy);
+//  - SH_STACK: any other tree of NL = 3..8 leaves, the same shape in every
+//    range (the generalized algorithm over Z_P, halving and doubling with
+//    fold-in, the binomial tree): the register stack (depth 4 holds every such
+//    tree in the program's Sethi-Ullman order) driven by the combination
+//    counts in the kernel argument.
 // The host checks each tree's combination counts against the shape and passes,
 // per call, the buffer pointers of every range's leaves (postfix order) and
 // outputs as a kernel argument: the data loads then wait on no program read and
@@ -425,16 +430,18 @@ __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* _
 // the ranks read from the program words, 11.9 with a rank table, 11.6 with the
 // pointers). cmb(left, right) keeps the operands of the postfix fold.
 constexpr int kMaxTabRanges = 8;
-enum : int { SH_NONE = 0, SH_BALANCED = 1, SH_CHAIN = 2 };
+enum : int { SH_NONE = 0, SH_BALANCED = 1, SH_CHAIN = 2, SH_STACK = 3 };
 struct RankTab {  // host side: ranks per range, turned into FixPtrs per call
   uint8_t leaf[kMaxTabRanges][8];
   uint8_t out[kMaxTabRanges][8];
   uint8_t nouts[kMaxTabRanges];
+  uint8_t nc[8];  // SH_STACK: combinations after each leaf (every range alike)
 };
 struct FixPtrs {
   void* leaf[kMaxTabRanges][8];  // range r's leaf buffers, postfix order
   void* out[kMaxTabRanges][8];   // its output buffers
   uint8_t nouts[kMaxTabRanges];
+  uint8_t nc[8];                 // SH_STACK
   float div;                     // O_AVG: divide the complete sum by this (P)
   int32_t xcd;                   // as RankPtrs::xcd
 };
@@ -449,7 +456,40 @@ __device__ __forceinline__ void fixed_one(const FixPtrs& fp, int r, int64_t e, c
   A v[NL][N];
 #pragma unroll
   for (int k = 0; k < NL; ++k) widen<DT, M>(raw[k], v[k]);
-  if constexpr (SH == SH_BALANCED) {
+  if constexpr (SH == SH_STACK) {
+    // as eval_one with the leaves already loaded: a push shifts the stack down
+    // (static moves); each combination folds the top two entries, cmb(deeper,
+    // top), and shifts the rest up
+    constexpr int D = 4;
+    A st[D][N];
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+#pragma unroll
+      for (int j = 0; j < N; ++j) st[d][j] = A(0);
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+#pragma unroll
+      for (int d = D - 1; d > 0; --d)
+#pragma unroll
+        for (int j = 0; j < N; ++j) st[d][j] = st[d - 1][j];
+#pragma unroll
+      for (int j = 0; j < N; ++j) st[0][j] = v[k][j];
+      const int c = fp.nc[k];
+#pragma unroll
+      for (int q = 0; q < D - 1; ++q) {
+        if (q < c) {
+#pragma unroll
+          for (int j = 0; j < N; ++j) st[0][j] = cmb<OPK>(st[1][j], st[0][j]);
+#pragma unroll
+          for (int d = 1; d < D - 1; ++d)
+#pragma unroll
+            for (int j = 0; j < N; ++j) st[d][j] = st[d + 1][j];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[0][j] = st[0][j];
+  } else if constexpr (SH == SH_BALANCED) {
     // level by level: v[i] = v[2i] + v[2i+1]; reads never trail the writes
 #pragma unroll
     for (int h = NL / 2; h >= 1; h /= 2)

@@ -114,8 +114,8 @@ hipError_t launch_fused_t(int D, int TM, int P, int leaves, int64_t nitems, cons
   return hipGetLastError();
 }
 
-// shape: SH_BALANCED (nl = 4 or 8) or SH_CHAIN (nl = 1..8) leaves per tree;
-// M = 2 or 4 vectors per thread.
+// shape: SH_BALANCED (nl = 4 or 8), SH_CHAIN (nl = 1..8) or SH_STACK (nl =
+// 3..8) leaves per tree; M = 2 or 4 vectors per thread.
 template <int DT, int OPK>
 hipError_t launch_fused_fixed_t(int shape, int nl, int M, int64_t nitems, const RankPtrs& ptrs, const Item* items,
                                 const RankTab& tab, hipStream_t st, Evs ev) {
@@ -130,6 +130,7 @@ hipError_t launch_fused_fixed_t(int shape, int nl, int M, int64_t nitems, const 
     }
     fp.nouts[r] = tab.nouts[r];
   }
+  for (int k = 0; k < 8; ++k) fp.nc[k] = tab.nc[k];
   fp.div = ptrs.div;
   fp.xcd = ptrs.xcd;
 #define AR_FIX(SH_, M_, NL_) \
@@ -145,7 +146,18 @@ hipError_t launch_fused_fixed_t(int shape, int nl, int M, int64_t nitems, const 
     case 7: AR_FIX(SH_CHAIN, M_, 7); break;                \
     default: AR_FIX(SH_CHAIN, M_, 8); break;               \
   }
-  if (shape == SH_BALANCED) {
+#define AR_STK(M_)                                         \
+  switch (nl) {                                            \
+    case 3: AR_FIX(SH_STACK, M_, 3); break;                \
+    case 4: AR_FIX(SH_STACK, M_, 4); break;                \
+    case 5: AR_FIX(SH_STACK, M_, 5); break;                \
+    case 6: AR_FIX(SH_STACK, M_, 6); break;                \
+    case 7: AR_FIX(SH_STACK, M_, 7); break;                \
+    default: AR_FIX(SH_STACK, M_, 8); break;               \
+  }
+  if (shape == SH_STACK) {
+    if (M == 4) { AR_STK(4) } else { AR_STK(2) }
+  } else if (shape == SH_BALANCED) {
     if (M == 4) {
       if (nl == 4) AR_FIX(SH_BALANCED, 4, 4); else AR_FIX(SH_BALANCED, 4, 8);
     } else {
@@ -154,6 +166,7 @@ hipError_t launch_fused_fixed_t(int shape, int nl, int M, int64_t nitems, const 
   } else {
     if (M == 4) { AR_CHAIN(4) } else { AR_CHAIN(2) }
   }
+#undef AR_STK
 #undef AR_CHAIN
 #undef AR_FIX
   return hipGetLastError();
