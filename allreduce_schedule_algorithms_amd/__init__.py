@@ -9,7 +9,8 @@ from __future__ import annotations
 from . import _ar
 from ._ar import (  # noqa: F401
     ALGO_NAMES, ALGOS, AR_KNOB_AUTO, COLLECTIVES, COST_FORMS, DTYPES, EXECS, OPS, Algo, ArError, Collective,
-    CostForm, Dtype, Exec, Op, Schedule, Status, ar_all_gather, ar_allreduce, ar_allreduce_ex, ar_get_cost_model,
+    CostForm, Dtype, Exec, Kernel, Op, Schedule, Status, ar_all_gather, ar_allreduce, ar_allreduce_ex,
+    ar_get_cost_model, ar_kernel_of,
     ar_last_error_message, ar_last_hip_error, ar_reduce_scatter, ar_schedule_build, ar_select, ar_set_cost_model,
     ar_set_launch_blocks, ar_status_string, ar_table_check, ar_table_check_ex, ar_version, ar_workspace_bytes,
     make_call,

@@ -66,6 +66,18 @@ class CostForm(enum.IntEnum):
     AR_COST_ALL_RANKS = 1
 
 
+class Kernel(enum.IntEnum):
+    AR_KERNEL_NONE = 0
+    AR_KERNEL_DIRECT = 1
+    AR_KERNEL_LITERAL = 2
+    AR_KERNEL_REPLAY = 3
+    AR_KERNEL_STAGED = 4
+    AR_KERNEL_STRIDED = 5
+    AR_KERNEL_FIXED_CHAIN = 6
+    AR_KERNEL_FIXED_BALANCED = 7
+    AR_KERNEL_FIXED_STACK = 8
+
+
 class Exec(enum.IntEnum):
     AR_EXEC_FUSED = 0
     AR_EXEC_LITERAL = 1
@@ -131,6 +143,7 @@ SIGNATURES = {
     "ar_all_gather": (C.c_int, [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_void_p]),
     "ar_workspace_bytes": (C.c_int, [C.POINTER(ar_call), C.POINTER(C.c_size_t)]),
     "ar_set_launch_blocks": (C.c_int, [C.c_int64, C.POINTER(C.c_int64)]),
+    "ar_kernel_of": (C.c_int, [C.POINTER(ar_call), C.POINTER(C.c_int32)]),
     "ar_schedule_build": (C.c_int, [C.POINTER(ar_call), C.POINTER(C.c_void_p)]),
     "ar_schedule_info_get": (C.c_int, [C.c_void_p, C.POINTER(ar_schedule_info)]),
     "ar_schedule_export": (C.c_int, [C.c_void_p, C.POINTER(ar_oprec), C.c_size_t, C.POINTER(C.c_size_t)]),
@@ -259,6 +272,13 @@ def ar_workspace_bytes(call: ar_call) -> int:
     out = C.c_size_t(0)
     _check(lib.ar_workspace_bytes(C.byref(call), C.byref(out)))
     return out.value
+
+
+def ar_kernel_of(call: ar_call) -> Kernel:
+    """The kernel family the call runs (host only)."""
+    out = C.c_int32(0)
+    _check(lib.ar_kernel_of(C.byref(call), C.byref(out)))
+    return Kernel(out.value)
 
 
 def ar_set_launch_blocks(max_blocks: int) -> int:

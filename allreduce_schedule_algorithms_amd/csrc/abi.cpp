@@ -253,6 +253,18 @@ ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes) {
   return AR_OK;
 }
 
+ar_status ar_kernel_of(const ar_call* call, int32_t* kernel) {
+  std::string err;
+  ar::Spec spec;
+  if (!kernel) return fail(AR_INVALID_ARGUMENT, "kernel is NULL");
+  if (!to_spec(call, &spec, &err)) return fail(AR_INVALID_ARGUMENT, err);
+  int k = 0;
+  ar::RunResult r = ar::kernel_of(spec, call->exec, &k);
+  if (r.status) return fail(ar_status(r.status), r.message);
+  *kernel = k;
+  return AR_OK;
+}
+
 ar_status ar_schedule_build(const ar_call* call, ar_schedule** out) {
   std::string err;
   ar::Spec spec;

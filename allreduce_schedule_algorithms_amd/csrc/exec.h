@@ -37,6 +37,14 @@ int64_t launch_blocks();
 // Set the limit (1..kMaxLaunchBlocks; false otherwise); the old value goes to *previous.
 bool set_launch_blocks(int64_t blocks, int64_t* previous);
 
+// Which kernel family a call runs (host only; builds the schedule). Values as
+// ar_kernel in include/ar.h.
+enum Kernel : int32_t {
+  K_NONE = 0, K_DIRECT = 1, K_LITERAL = 2, K_REPLAY = 3, K_STAGED = 4, K_STRIDED = 5,
+  K_FIXED_CHAIN = 6, K_FIXED_BALANCED = 7, K_FIXED_STACK = 8
+};
+RunResult kernel_of(const Spec& spec, int exec, int* kernel);
+
 // Cached host schedule for a spec (shared with the executor's plan cache).
 std::shared_ptr<const Schedule> cached_schedule(const Spec& spec, std::string* err);
 

@@ -217,6 +217,25 @@ int fixed_shape(const Schedule& s, RankTab* tab, int* nl_out) {
   return nl0 >= 3 && most <= 4 && depth == 1 ? SH_STACK : SH_NONE;
 }
 
+// Whether a batched call's fused replay uses strided items: several ranges,
+// all shorter than kStridedMaxLen elements.
+bool strided_items(const Schedule& s) {
+  const Spec& sp = s.spec;
+  const bool flat = s.ranges.size() == 1 && s.ranges[0].start == 0 && s.ranges[0].len == sp.n;
+  if (sp.batch <= 1 || flat) return false;
+  int64_t max_len = 0;
+  for (const FusedRange& r : s.ranges) max_len = std::max(max_len, r.len);
+  return max_len < kStridedMaxLen;
+}
+
+bool fixed_shapes_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("AR_FUSED_SHAPES");  // "0": never the fixed-shape kernel (for comparisons)
+    return !(v && v[0] == '0');
+  }();
+  return on;
+}
+
 // Build the fused or literal item tables for one alignment mode.
 RunResult build_items(Plan& pl, bool vec) {
   const Schedule& s = *pl.s;
@@ -299,6 +318,7 @@ RunResult build_items(Plan& pl, bool vec) {
     int64_t max_len = 0;
     for (const FusedRange& r : s.ranges) max_len = std::max(max_len, r.len);
     std::vector<SItem> sitems;
+    const bool strided = strided_items(s);
     // the fixed-shape kernel finds a range's buffers by its index in the table
     const bool fixed = pl.shape != SH_NONE;
     const int64_t iv = fixed ? int64_t(kThreads) * pl.md : 0;
@@ -307,7 +327,7 @@ RunResult build_items(Plan& pl, bool vec) {
       const int64_t mult = flat ? sp.batch : 1;
       for (size_t i = 0; i < s.ranges.size(); ++i)
         add_segment(items, s.ranges[i].start, s.ranges[i].len * mult, tag_of(i), V, vec, iv);
-    } else if (max_len < kStridedMaxLen) {
+    } else if (strided) {
       // short ranges in many instances: one strided item per range and block
       // of instances; the items of one block sit next to each other, so the
       // ranges sharing its cache lines run together
@@ -390,11 +410,7 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
   pl->s = s;
   pl->exec = exec;
   pl->device = device;
-  static const bool shapes = [] {
-    const char* v = std::getenv("AR_FUSED_SHAPES");  // "0": always the register-stack replay (for comparisons)
-    return !(v && v[0] == '0');
-  }();
-  if (exec != E_LITERAL && s->fused_ok && shapes) {
+  if (exec != E_LITERAL && s->fused_ok && fixed_shapes_enabled()) {
     pl->shape = fixed_shape(*s, &pl->tab, &pl->shape_nl);
     // four vectors per thread for short launches with few ranks, as the direct kernel
     pl->md = spec.P <= 8 && spec.n * spec.batch / vec_width(spec.dtype) <= (int64_t(1) << 19) ? 4 : 2;
@@ -471,6 +487,28 @@ RunResult workspace_bytes(const Spec& spec, int exec, size_t* bytes) {
   if (exec != E_LITERAL && s->fused_ok && fused_runs(*s)) return RunResult{};  // the replay keeps partials in registers
   int64_t slot = (spec.n * spec.batch * int64_t(acc_bytes(spec.dtype)) + 255) / 256 * 256;
   *bytes = size_t(s->nslots - 1) * size_t(spec.P) * size_t(slot);
+  return RunResult{};
+}
+
+RunResult kernel_of(const Spec& spec, int exec, int* kernel) {
+  *kernel = K_NONE;
+  if (spec.P <= 1 || spec.n == 0) return RunResult{};
+  if (exec == E_LITERAL) { *kernel = K_LITERAL; return RunResult{}; }
+  if (exec == E_FUSED && spec.algo == A_DIRECT && spec.coll == C_ALLREDUCE) { *kernel = K_DIRECT; return RunResult{}; }
+  std::string err;
+  std::shared_ptr<const Schedule> s = cached_schedule(spec, &err);
+  if (!s) { RunResult r; r.status = 1; r.message = err; return r; }
+  if (!s->fused_ok || !fused_runs(*s)) { *kernel = K_LITERAL; return RunResult{}; }
+  int nl = 0;
+  RankTab tab;
+  const int shape = fixed_shapes_enabled() ? fixed_shape(*s, &tab, &nl) : SH_NONE;
+  // the same order of choices as run_allreduce's launch
+  if (strided_items(*s)) *kernel = K_STRIDED;
+  else if (shape == SH_CHAIN) *kernel = K_FIXED_CHAIN;
+  else if (shape == SH_BALANCED) *kernel = K_FIXED_BALANCED;
+  else if (shape == SH_STACK) *kernel = K_FIXED_STACK;
+  else if (s->max_trees > 1 && spec.P <= kMaxStagedRanks) *kernel = K_STAGED;
+  else *kernel = K_REPLAY;
   return RunResult{};
 }
 

@@ -529,6 +529,15 @@ def parse_key(key):
                 factors=next(([int(v) for v in t[1:].split("x")] for t in rest if t.startswith("Z")), None))
 
 
+# ar_kernel_of's answer -> the kernel function it launches
+KERNEL_NAMES = {
+    "AR_KERNEL_NONE": None, "AR_KERNEL_DIRECT": "k_direct", "AR_KERNEL_LITERAL": "k_literal",
+    "AR_KERNEL_REPLAY": "k_fused", "AR_KERNEL_STAGED": "k_fused_staged", "AR_KERNEL_STRIDED": "k_fused_strided",
+    "AR_KERNEL_FIXED_CHAIN": "k_fused_fixed", "AR_KERNEL_FIXED_BALANCED": "k_fused_fixed",
+    "AR_KERNEL_FIXED_STACK": "k_fused_fixed",
+}
+
+
 def load_traffic(wl_name, key):
     """The committed counter summary's record for this workload and schedule:
     HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, each scaled by what it
@@ -636,11 +645,10 @@ def main():
     achieved = head["kernel_GBps"]
     rec = load_traffic(args.workload, hkey)
     traffic = rec.get("bytes_per_launch") if rec else None
-    if rec and rec.get("kernel"):  # the trace's dominant kernel, e.g. "ar::k_fused_balanced<1, 0, 4, 8>"
-        kernel = rec["kernel"].split("::")[-1].split("<")[0]
-    else:  # the family; the fused executor picks one of its kernels by program shape and size
-        kernel = ("k_literal" if ex == "literal" else
-                  "k_direct" if (algo == "direct" and ex == "fused" and h["coll"] == "allreduce") else "k_fused")
+    # the kernel the library picks for this call (its own answer, host side)
+    kind = A.ar_kernel_of(r.call_for(algo, knob, ex, coll=h["coll"], op=h["op"], rsteps=h["rsteps"],
+                                     factors=h["factors"]))
+    kernel = KERNEL_NAMES[kind.name]
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": kernel,

@@ -194,6 +194,37 @@ ar_status ar_allreduce_ex(void* const* bufs, const ar_call* call, void* stream);
  * Builds (and caches) the schedule; returns its validation error for invalid calls. */
 ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes);
 
+/* The kernel family a call runs on the GPU (host only: builds and caches the schedule, like
+ * ar_workspace_bytes). Fused execution picks one replay kernel per schedule and size; all
+ * compute the same combination trees:
+ *  AR_KERNEL_NONE            no launch (P = 1 or n = 0)
+ *  AR_KERNEL_DIRECT          the one-pass direct kernel (AR_DIRECT Allreduce, AR_EXEC_FUSED)
+ *  AR_KERNEL_LITERAL         one launch per schedule step (AR_EXEC_LITERAL, and fused calls the
+ *                            replay cannot hold; see ar_exec)
+ *  AR_KERNEL_REPLAY          the register-stack replay of the fused program
+ *  AR_KERNEL_STAGED          the same with several result trees per range and P <= 16: every
+ *                            rank's fragment is loaded once into LDS
+ *  AR_KERNEL_STRIDED         batches whose ranges are all shorter than 64 elements: one element
+ *                            per thread across a block of instances
+ *  AR_KERNEL_FIXED_CHAIN     single-tree programs of at most 8 ranges whose trees are all chains
+ *                            of 1..8 leaves ((x + y) + z ..., the ring, the pipelined chain)
+ *  AR_KERNEL_FIXED_BALANCED  ... all perfect binary trees of 4 or 8 leaves (halving + doubling)
+ *  AR_KERNEL_FIXED_STACK     ... all one other shape of 3..8 leaves (the generalized algorithm
+ *                            over Z_P for small P); the fixed kinds take the ranges' buffer
+ *                            pointers as a kernel argument. */
+typedef enum {
+  AR_KERNEL_NONE = 0,
+  AR_KERNEL_DIRECT = 1,
+  AR_KERNEL_LITERAL = 2,
+  AR_KERNEL_REPLAY = 3,
+  AR_KERNEL_STAGED = 4,
+  AR_KERNEL_STRIDED = 5,
+  AR_KERNEL_FIXED_CHAIN = 6,
+  AR_KERNEL_FIXED_BALANCED = 7,
+  AR_KERNEL_FIXED_STACK = 8
+} ar_kernel;
+ar_status ar_kernel_of(const ar_call* call, int32_t* kernel);
+
 /* Largest grid, in 256-thread workgroups, of one kernel launch. A call whose work needs
  * more (misaligned buffers of 2^32 elements or more, or about 2^35 aligned ones) runs as
  * several consecutive launches on the caller's stream with the same results; events of

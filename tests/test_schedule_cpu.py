@@ -360,6 +360,42 @@ def test_workspace_query():
     assert A.ar_workspace_bytes(big) == A.ar_workspace_bytes(lit) > 0
 
 
+def test_kernel_choice():
+    # which kernel family a call runs: the host's choice, by schedule shape and size
+    K = A.Kernel
+    cases = [
+        (dict(P=8, n=1 << 20, algo="rh_rd"), K.AR_KERNEL_FIXED_BALANCED),
+        (dict(P=4, n=4099, algo="rd"), K.AR_KERNEL_FIXED_BALANCED),
+        (dict(P=8, n=1 << 20, algo="ring"), K.AR_KERNEL_FIXED_CHAIN),
+        (dict(P=5, n=77, algo="chain", knob=3), K.AR_KERNEL_FIXED_CHAIN),
+        (dict(P=7, n=1 << 24, algo="ring", collective="all_gather"), K.AR_KERNEL_FIXED_CHAIN),
+        (dict(P=7, n=1 << 24, algo="generalized"), K.AR_KERNEL_FIXED_STACK),
+        (dict(P=6, n=1000, algo="binomial"), K.AR_KERNEL_FIXED_STACK),
+        (dict(P=7, n=1 << 24, algo="generalized", knob=3), K.AR_KERNEL_STAGED),
+        (dict(P=12, n=4099, algo="generalized", knob=2), K.AR_KERNEL_STAGED),
+        (dict(P=24, n=106, algo="generalized", knob=5, batch=10_000), K.AR_KERNEL_REPLAY),
+        (dict(P=192, n=1 << 20, dtype="bf16", algo="ahc", groups=[64, 128]), K.AR_KERNEL_REPLAY),
+        (dict(P=24, n=106, algo="rd", batch=10_000), K.AR_KERNEL_REPLAY),
+        (dict(P=24, n=106, algo="generalized", batch=10_000), K.AR_KERNEL_STRIDED),
+        (dict(P=8, n=1 << 20, algo="direct"), K.AR_KERNEL_DIRECT),
+        (dict(P=8, n=1 << 20, algo="direct", exec="replay"), K.AR_KERNEL_FIXED_CHAIN),
+        (dict(P=8, n=1 << 20, algo="direct", collective="reduce_scatter"), K.AR_KERNEL_FIXED_CHAIN),
+        (dict(P=8, n=1 << 20, algo="ring", exec="literal"), K.AR_KERNEL_LITERAL),
+        (dict(P=13, n=1000, algo="generalized", knob=4, steps=4), K.AR_KERNEL_LITERAL),  # more than 8 trees
+        (dict(P=1, n=10, algo="ring"), K.AR_KERNEL_NONE),
+        (dict(P=5, n=0, algo="ring"), K.AR_KERNEL_NONE),
+    ]
+    for kw, want in cases:
+        kw = dict(kw)
+        P, n = kw.pop("P"), kw.pop("n")
+        dtype, algo, knob = kw.pop("dtype", "fp32"), kw.pop("algo"), kw.pop("knob", 0)
+        ex = kw.pop("exec", "fused")
+        got = A.ar_kernel_of(A.make_call(P, n, dtype, "sum", algo, knob, ex, **kw))
+        assert got == want, (P, n, algo, knob, ex, kw, got)
+    with pytest.raises(A.ArError):
+        A.ar_kernel_of(A.make_call(6, 100, "fp32", "sum", "generalized_xor"))  # Z_2^k needs a power of two
+
+
 def test_launch_block_limit_setter():
     top = (1 << 32) // 256 - 1
     prev = A.ar_set_launch_blocks(5)
