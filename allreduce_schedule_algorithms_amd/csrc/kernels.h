@@ -752,9 +752,13 @@ __global__ __launch_bounds__(kThreads) void k_direct(RankPtrs ptrs, int P, int64
 #pragma unroll
     for (int j = 0; j < MD; ++j) ok[j] = vb + j * kThreads < nvec;
     if (ok[0]) direct_one<DT, OPK, MD, B>(ptrs, P, vb * V, ok);
-    if (blockIdx.x == 0) {
+    // the elements past the last whole vector: the last block's highest
+    // threads, which a short launch leaves without vectors, so the tail does
+    // not add a round of loads after the vectors
+    if (blockIdx.x == gridDim.x - 1) {
       const bool one[1] = {true};
-      for (int64_t e = nvec * V + threadIdx.x; e < total; e += kThreads) direct_one<DT, OPK, 0, B>(ptrs, P, e, one);
+      for (int64_t e = nvec * V + (kThreads - 1 - int(threadIdx.x)); e < total; e += kThreads)
+        direct_one<DT, OPK, 0, B>(ptrs, P, e, one);
     }
   } else {
     const int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x;

@@ -254,10 +254,16 @@ hipError_t direct_m(bool vec, const RankPtrs& ptrs, int P, int64_t total, int64_
 }
 
 // Four vectors per thread for launches of at most 2^19 vectors (a few hundred
-// workgroups) with at most 8 ranks; two otherwise.
+// workgroups) with at most 8 ranks; two otherwise. Latency-bound launches
+// (at most 2^14 elements) with 9..32 ranks fetch every rank in one batch
+// instead of rounds of 8, each of which waits on memory.
 template <int DT, int OPK>
 hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total, int64_t max_blocks, hipStream_t st,
                            Evs ev) {
+  if (P > 8 && P <= 32 && total <= (int64_t(1) << 14)) {
+    if (P <= 16) return direct_b<DT, OPK, 16, 1>(vec, ptrs, P, total, max_blocks, st, ev);
+    return direct_b<DT, OPK, 32, 1>(vec, ptrs, P, total, max_blocks, st, ev);
+  }
   if (vec && P <= 8 && total / TT<DT>::V <= (int64_t(1) << 19))
     return direct_m<DT, OPK, 4>(vec, ptrs, P, total, max_blocks, st, ev);
   return direct_m<DT, OPK, kDirectM>(vec, ptrs, P, total, max_blocks, st, ev);

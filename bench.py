@@ -268,8 +268,23 @@ class Runner:
         z.record(st)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        return {"calls": calls, "us_per_call": round(a.elapsed_time(z) * 1e3 / calls, 3),
-                "wall_us_per_call": round(wall * 1e6 / calls, 3), "schedule": f"{algo}/r{knob}/fused"}
+        out = {"calls": calls, "us_per_call": round(a.elapsed_time(z) * 1e3 / calls, 3),
+               "wall_us_per_call": round(wall * 1e6 / calls, 3), "schedule": f"{algo}/r{knob}/fused"}
+        # the same calls captured once in a HIP graph and replayed: the device's
+        # per-call time without the host's enqueue cost (plans are built above)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            for b in range(calls):
+                self.A.ar_allreduce_ex(ptr_sets[b], call, st)
+        g.replay()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            a.record(st)
+            g.replay()
+            z.record(st)
+        torch.cuda.synchronize()
+        out["graph_us_per_call"] = round(a.elapsed_time(z) * 1e3 / calls, 3)
+        return out
 
     def copy_ceiling(self, gib=2):
         import torch
@@ -386,6 +401,52 @@ def brute_force_all_cores(xs, dtype, budget_s=4.0):
     ess = 2.0 * x.size * x.dtype.itemsize  # read every input, write one result per rank
     return {"value": round(ess / mean / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "brute-force elementwise reduction (no schedule)"}
+
+
+LATENCY_CASES = [  # (P, n, algo, knob): one 106-fp32 instance (about 425 bytes) per rank, and neighbours
+    (2, 106, "direct", 0), (8, 106, "direct", 0), (24, 106, "direct", 0), (24, 1, "direct", 0),
+    (3, 106, "rd", 0), (6, 106, "rd", 0), (12, 106, "rd", 0), (24, 106, "rd", 0), (24, 106, "binomial", 0),
+    (24, 106, "generalized", 5), (8, 106, "rh_rd", 0), (8, 106, "ring", 0),
+]
+
+
+def latency(calls=2000):
+    """Per-call device time of single small Allreduces: `calls` calls on
+    consecutive instances, captured once in a HIP graph and replayed, timed
+    with events around the replay. Without the host's enqueue cost this is the
+    library's alpha on this device (launch, one kernel, completion)."""
+    import numpy as np
+    import torch
+
+    import allreduce_schedule_algorithms_amd as A
+    from synth import inputs
+    rows = []
+    for P, n, algo, knob in LATENCY_CASES:
+        x = inputs.make("fp32", P, n * calls, seed=1)
+        bufs = [torch.from_numpy(np.ascontiguousarray(x[p])).cuda() for p in range(P)]
+        call = A.make_call(P, n, "fp32", "sum", algo, knob)
+        st = torch.cuda.Stream()
+        ptrs = [[b.data_ptr() + i * n * 4 for b in bufs] for i in range(calls)]
+        with torch.cuda.stream(st):
+            for i in range(20):  # plans built outside the capture
+                A.ar_allreduce_ex(ptrs[i], call, st)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            for i in range(calls):
+                A.ar_allreduce_ex(ptrs[i], call, st)
+        g.replay()
+        torch.cuda.synchronize()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(st):
+            a.record(st)
+            g.replay()
+            z.record(st)
+        torch.cuda.synchronize()
+        rows.append({"P": P, "n": n, "schedule": f"{algo}/r{knob}/fused", "kernel": KERNEL_NAMES[A.ar_kernel_of(call).name],
+                     "us_per_call": round(a.elapsed_time(z) * 1e3 / calls, 3)})
+        del g, bufs
+    print(json.dumps({"latency_fp32_graph_replay": rows, "calls": calls}))
 
 
 def model_fit(args):
@@ -571,6 +632,8 @@ def main():
     ap.add_argument("--warm", action="store_true", help="also report warm-cache (no flush) figures")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run one plain device copy of MIB MiB (for counter scaling) and exit")
+    ap.add_argument("--latency", action="store_true",
+                    help="per-call device time of single small Allreduces (graph replay) and exit")
     ap.add_argument("--model", action="store_true",
                     help="fit alpha/beta/gamma to literal-mode (one launch per step) timings and check "
                          "the model's choice of schedule and knob against measurement")
@@ -593,6 +656,10 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": nbytes}))
+        return
+
+    if args.latency:
+        latency()
         return
 
     if args.model:

@@ -617,6 +617,40 @@ def test_buffers_past_2_32_elements():
     del rows, big
 
 
+def test_calls_captured_in_a_hip_graph():
+    # one-instance calls captured in a graph and replayed: every replay gives
+    # the eager bits, with eager work (restoring the inputs) between replays
+    import allreduce_schedule_algorithms_amd as A
+    torch = torch_mod()
+    P, n, B = 6, 106, 40
+    for algo, knob in (("rd", 0), ("ring", 0), ("generalized", 1)):
+        x = inputs.make("fp32", P, n * B, seed=B + knob)
+        want = oracle.allreduce(x.reshape(P, B, n), algo, "fp32", "sum", knob=knob, n=n).reshape(P, B * n)
+        bufs, keep = to_device(x, "fp32")
+        pristine = [b.clone() for b in bufs]
+        call = A.make_call(P, n, "fp32", "sum", algo, knob)
+        st = torch.cuda.Stream()
+        ptr_sets = [[b.data_ptr() + i * n * 4 for b in bufs] for i in range(B)]
+        with torch.cuda.stream(st):
+            for i in range(B):  # eager: builds the plan (no allocation may happen inside the capture)
+                A.ar_allreduce_ex(ptr_sets[i], call, st)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(from_device(bufs, "fp32")), bits(want)), (algo, "eager")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            for i in range(B):
+                A.ar_allreduce_ex(ptr_sets[i], call, st)
+        for rep in range(3):
+            with torch.cuda.stream(st):
+                for b, p0 in zip(bufs, pristine):
+                    b.copy_(p0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(from_device(bufs, "fp32")), bits(want)), (algo, rep)
+        del g, keep
+
+
 def test_plans_survive_a_cleared_schedule_cache():
     # a plan built on the first call must stay valid after other specs have
     # pushed its schedule out of the schedule cache (more than 512 of them)
