@@ -412,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* _
 }
 
 // Single-tree programs of at most kMaxTabRanges ranges in which every tree has
-// one fixed shape run without the register stack:
+// one fixed shape of at most 8 leaves run with their leaves loaded at once:
 //  - SH_BALANCED: a perfect binary tree of NL = 4 or 8 leaves, combined level
 //    by level (recursive halving and doubling, the generalized algorithm over
 //    Z_2^k give these);
