@@ -76,6 +76,7 @@ class Kernel(enum.IntEnum):
     AR_KERNEL_FIXED_CHAIN = 6
     AR_KERNEL_FIXED_BALANCED = 7
     AR_KERNEL_FIXED_STACK = 8
+    AR_KERNEL_MULTI = 9
 
 
 class Exec(enum.IntEnum):

@@ -124,6 +124,9 @@ struct Plan {
   int shape = SH_NONE;    // fused: every tree of this fixed shape (k_fused_fixed)
   int shape_nl = 0;       // its leaves per tree
   RankTab tab;            // k_fused_fixed: leaf and output ranks per range
+  int multi = 0;          // fused: k_fused_multi with this many leaves per tree
+  MultiTab mt;            // its ranks
+  DevBuf mtab;            // the same as device words
   int md = 2;             // k_fused_fixed: vectors per thread (items of kThreads * md vectors)
   int64_t slot_bytes = 0;
   size_t ws_bytes = 0;
@@ -219,6 +222,46 @@ int fixed_shape(const Schedule& s, RankTab* tab, int* nl_out) {
   if (bal) return SH_BALANCED;
   if (chain) return SH_CHAIN;
   return nl0 >= 3 && most <= 4 && depth == 1 ? SH_STACK : SH_NONE;
+}
+
+// Whether a program of several trees per range fits k_fused_multi: at most 8
+// ranges of at most 8 trees, every tree with the same combination counts over
+// all P = 3..8 leaves and at most 8 outputs. Fills the ranks of *mt.
+int multi_shape(const Schedule& s, MultiTab* mt) {
+  const int P = s.spec.P;
+  if (s.max_trees <= 1 || P < 3 || P > 8 || s.ranges.empty() || s.ranges.size() > 8) return 0;
+  std::memset(mt, 0, sizeof(*mt));
+  const int32_t* nc0 = nullptr;
+  for (size_t i = 0; i < s.ranges.size(); ++i) {
+    const int32_t* w = s.prog.data() + s.ranges[i].prog;
+    const int nt = w[0];
+    if (nt < 1 || nt > 8) return 0;
+    mt->ntrees[i] = uint8_t(nt);
+    w += 1;
+    for (int t = 0; t < nt; ++t) {
+      const int nl = w[0], nouts = w[1];
+      if (nl != P || nouts < 1 || nouts > 8) return 0;
+      const int32_t* leaf = w + 2;
+      const int32_t* nc = leaf + nl;
+      const int32_t* outs = nc + nl;
+      if (!nc0) nc0 = nc;
+      for (int k = 0; k < nl; ++k) {
+        if (nc[k] != nc0[k]) return 0;
+        mt->leaf[i][t][k] = uint8_t(leaf[k]);
+      }
+      for (int j = 0; j < nouts; ++j) mt->out[i][t][j] = uint8_t(outs[j]);
+      mt->nouts[i][t] = uint8_t(nouts);
+      w = outs + nouts;
+    }
+  }
+  int depth = 0, most = 0;
+  for (int k = 0; k < P; ++k) {
+    depth += 1;
+    most = std::max(most, depth);
+    depth -= nc0[k];
+    mt->nc[k] = uint8_t(nc0[k]);
+  }
+  return most <= 4 && depth == 1 ? P : 0;
 }
 
 // Whether a batched call's fused replay uses strided items: several ranges,
@@ -324,8 +367,8 @@ RunResult build_items(Plan& pl, bool vec) {
     std::vector<SItem> sitems;
     const bool strided = strided_items(s);
     // the fixed-shape kernel finds a range's buffers by its index in the table
-    const bool fixed = pl.shape != SH_NONE;
-    const int64_t iv = fixed ? int64_t(kThreads) * pl.md : 0;
+    const bool fixed = pl.shape != SH_NONE || pl.multi;
+    const int64_t iv = pl.multi ? 2 * int64_t(kThreads) : fixed ? int64_t(kThreads) * pl.md : 0;
     auto tag_of = [&](size_t i) { return fixed ? int32_t(i) : s.ranges[i].prog; };
     if (sp.batch == 1 || flat) {
       const int64_t mult = flat ? sp.batch : 1;
@@ -344,6 +387,22 @@ RunResult build_items(Plan& pl, bool vec) {
       for (int64_t b = 0; b < sp.batch; ++b)
         for (size_t i = 0; i < s.ranges.size(); ++i)
           add_segment(items, b * sp.n + s.ranges[i].start, s.ranges[i].len, tag_of(i), V, vec, iv);
+    }
+    if (pl.multi && !pl.mtab.p) {
+      std::vector<int32_t> t(8 + 8 * kMultiRangeWords + 16, 0);
+      for (int k = 0; k < 8; ++k) t[k] = pl.mt.nc[k];
+      for (int r = 0; r < 8; ++r) {
+        int32_t* rw = t.data() + 8 + r * kMultiRangeWords;
+        rw[0] = pl.mt.ntrees[r];
+        for (int q = 0; q < 8; ++q) {
+          int32_t* tw = rw + 1 + q * 17;
+          for (int k = 0; k < 8; ++k) tw[k] = pl.mt.leaf[r][q][k];
+          tw[8] = pl.mt.nouts[r][q];
+          for (int k = 0; k < 8; ++k) tw[9 + k] = pl.mt.out[r][q][k];
+        }
+      }
+      hipError_t e = upload(pl.mtab, t);
+      if (e != hipSuccess) return hip_fail(e, "uploading the multi-tree table");
     }
     if (!pl.prog.p) {
       // the replay reads each batch's leaf ranks and combination counts as whole
@@ -416,6 +475,7 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
   pl->device = device;
   if (exec != E_LITERAL && s->fused_ok && fixed_shapes_enabled()) {
     pl->shape = fixed_shape(*s, &pl->tab, &pl->shape_nl);
+    if (pl->shape == SH_NONE) pl->multi = multi_shape(*s, &pl->mt);
     // four vectors per thread for short launches with few ranks, as the direct kernel
     pl->md = spec.P <= 8 && spec.n * spec.batch / vec_width(spec.dtype) <= (int64_t(1) << 19) ? 4 : 2;
   }
@@ -507,10 +567,12 @@ RunResult kernel_of(const Spec& spec, int exec, int* kernel) {
   RankTab tab;
   const int shape = fixed_shapes_enabled() ? fixed_shape(*s, &tab, &nl) : SH_NONE;
   // the same order of choices as run_allreduce's launch
+  MultiTab mt;
   if (strided_items(*s)) *kernel = K_STRIDED;
   else if (shape == SH_CHAIN) *kernel = K_FIXED_CHAIN;
   else if (shape == SH_BALANCED) *kernel = K_FIXED_BALANCED;
   else if (shape == SH_STACK) *kernel = K_FIXED_STACK;
+  else if (fixed_shapes_enabled() && multi_shape(*s, &mt)) *kernel = K_MULTI;
   else if (s->max_trees > 1 && spec.P <= kMaxStagedRanks) *kernel = K_STAGED;
   else *kernel = K_REPLAY;
   return RunResult{};
@@ -632,6 +694,15 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
         const SItem* sit = reinterpret_cast<const SItem*>(pl->items[mode].p) + off;
         AR_DISPATCH(spec.dtype, spec.op,
                     (e = launch_fused_strided_t<DT, OPK>(pl->D, TM, cnt, ptrs, sit, prog, spec.n, st, ei)));
+      } else if (pl->multi) {
+        MultiPtrs mp;
+        std::memset(&mp, 0, sizeof(mp));
+        for (int q = 0; q < spec.P; ++q) mp.p[q] = ptrs.p[q];
+        mp.div = ptrs.div;
+        mp.xcd = ptrs.xcd;
+        AR_DISPATCH(spec.dtype, spec.op,
+                    (e = launch_fused_multi_t<DT, OPK>(pl->multi, cnt, mp, items + off,
+                                                       reinterpret_cast<const int32_t*>(pl->mtab.p), st, ei)));
       } else if (pl->shape != SH_NONE) {
         AR_DISPATCH(spec.dtype, spec.op,
                     (e = launch_fused_fixed_t<DT, OPK>(pl->shape, pl->shape_nl, pl->md, cnt, ptrs, items + off,

@@ -37,6 +37,9 @@ template <int DT, int OPK>
 hipError_t launch_fused_strided_t(int D, int TM, int64_t nitems, const RankPtrs& ptrs, const SItem* items,
                                   const int32_t* prog, int64_t stride, hipStream_t st, Evs ev);
 template <int DT, int OPK>
+hipError_t launch_fused_multi_t(int nl, int64_t nitems, const MultiPtrs& mp, const Item* items, const int32_t* tab,
+                                hipStream_t st, Evs ev);
+template <int DT, int OPK>
 hipError_t launch_fused_fixed_t(int shape, int nl, int M, int64_t nitems, const RankPtrs& ptrs, const Item* items,
                                 const RankTab& tab, hipStream_t st, Evs ev);
 template <int DT, int OPK>
@@ -173,6 +176,25 @@ hipError_t launch_fused_fixed_t(int shape, int nl, int M, int64_t nitems, const 
 }
 
 template <int DT, int OPK>
+hipError_t launch_fused_multi_t(int nl, int64_t nitems, const MultiPtrs& mp, const Item* items, const int32_t* tab,
+                                hipStream_t st, Evs ev) {
+  const dim3 g{unsigned(nitems), 1, 1};
+  const dim3 b{unsigned(kThreads), 1, 1};
+  const uint32_t lds = uint32_t(nl) * kThreads * sizeof(u32x4);
+#define AR_MT(NL_) hipExtLaunchKernelGGL((k_fused_multi<DT, OPK, NL_>), g, b, lds, st, ev.start, ev.stop, 0, mp, items, tab)
+  switch (nl) {
+    case 3: AR_MT(3); break;
+    case 4: AR_MT(4); break;
+    case 5: AR_MT(5); break;
+    case 6: AR_MT(6); break;
+    case 7: AR_MT(7); break;
+    default: AR_MT(8); break;
+  }
+#undef AR_MT
+  return hipGetLastError();
+}
+
+template <int DT, int OPK>
 hipError_t launch_fused_strided_t(int D, int TM, int64_t nitems, const RankPtrs& ptrs, const SItem* items,
                                   const int32_t* prog, int64_t stride, hipStream_t st, Evs ev) {
   const dim3 g{unsigned(nitems), 1, 1};
@@ -275,6 +297,8 @@ hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total,
                                               const int32_t*, hipStream_t, Evs);                            \
   template hipError_t launch_fused_fixed_t<DT, OPK>(int, int, int, int64_t, const RankPtrs&, const Item*,   \
                                                     const RankTab&, hipStream_t, Evs);                      \
+  template hipError_t launch_fused_multi_t<DT, OPK>(int, int64_t, const MultiPtrs&, const Item*,          \
+                                                    const int32_t*, hipStream_t, Evs);                      \
   template hipError_t launch_fused_strided_t<DT, OPK>(int, int, int64_t, const RankPtrs&, const SItem*,     \
                                                       const int32_t*, int64_t, hipStream_t, Evs);          \
   template hipError_t launch_literal_t<DT, OPK>(int64_t, const RankPtrs&, const WsDesc&, const LitWork*,    \

@@ -211,7 +211,11 @@ ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes);
  *  AR_KERNEL_FIXED_BALANCED  ... all perfect binary trees of 4 or 8 leaves (halving + doubling)
  *  AR_KERNEL_FIXED_STACK     ... all one other shape of 3..8 leaves (the generalized algorithm
  *                            over Z_P for small P); the fixed kinds take the ranges' buffer
- *                            pointers as a kernel argument. */
+ *                            pointers as a kernel argument
+ *  AR_KERNEL_MULTI           several trees per range, all of one shape over P = 3..8 leaves, at
+ *                            most 8 ranges of 8 trees (the generalized algorithm with r > 0 on
+ *                            up to 8 ranks): ranks staged in LDS once, the trees' ranks read
+ *                            from a fixed-stride table. */
 typedef enum {
   AR_KERNEL_NONE = 0,
   AR_KERNEL_DIRECT = 1,
@@ -221,7 +225,8 @@ typedef enum {
   AR_KERNEL_STRIDED = 5,
   AR_KERNEL_FIXED_CHAIN = 6,
   AR_KERNEL_FIXED_BALANCED = 7,
-  AR_KERNEL_FIXED_STACK = 8
+  AR_KERNEL_FIXED_STACK = 8,
+  AR_KERNEL_MULTI = 9
 } ar_kernel;
 ar_status ar_kernel_of(const ar_call* call, int32_t* kernel);
 
