@@ -77,6 +77,7 @@ class Kernel(enum.IntEnum):
     AR_KERNEL_FIXED_BALANCED = 7
     AR_KERNEL_FIXED_STACK = 8
     AR_KERNEL_MULTI = 9
+    AR_KERNEL_ROWS = 10
 
 
 class Exec(enum.IntEnum):

@@ -121,6 +121,10 @@ struct Plan {
   std::vector<std::pair<int64_t, int64_t>> launches[2];
   DevBuf packed[2];
   bool strided = false;  // fused: items are SItem (batches of short ranges)
+  bool rows = false;      // fused: k_fused_rows (strided batches of one program shape)
+  int rows_ref = 0;       // its reference range
+  std::vector<uint8_t> rows_tab;  // its range and rank tables
+  DevBuf rtab;            // the same on the device
   int shape = SH_NONE;    // fused: every tree of this fixed shape (k_fused_fixed)
   int shape_nl = 0;       // its leaves per tree
   RankTab tab;            // k_fused_fixed: leaf and output ranks per range
@@ -275,6 +279,66 @@ bool strided_items(const Schedule& s) {
   return max_len < kStridedMaxLen;
 }
 
+// Whether a batched call with strided items can run k_fused_rows instead:
+// every range's program is the reference range's (the first non-empty one)
+// with its leaf ranks renamed, one renaming per range for all its trees, with
+// the same combination counts and the same output ranks per tree. Fills *t
+// with the range of each offset of an instance (n bytes, padded to 8), then per
+// range a row of P bytes mapping a leaf rank of the reference range to the
+// range's own, and *ref with the reference range's index.
+constexpr int64_t kRowsMaxTable = 4096;  // limit on R x (P | 1) and on n (LDS)
+bool rows_table(const Schedule& s, std::vector<uint8_t>* t, int* ref) {
+  const Spec& sp = s.spec;
+  const int64_t R = int64_t(s.ranges.size()), P = sp.P;
+  if (!strided_items(s) || R > 255 || R * (P | 1) > kRowsMaxTable || sp.n > kRowsMaxTable) return false;
+  const int64_t moff = (sp.n + 7) / 8 * 8;
+  t->assign(size_t(moff + R * P), 0);
+  std::vector<int> cover(size_t(sp.n), -1);
+  *ref = -1;
+  for (int64_t r = 0; r < R; ++r) {
+    const FusedRange& fr = s.ranges[size_t(r)];
+    if (fr.len > 0 && *ref < 0) *ref = int(r);
+    for (int64_t o = fr.start; o < fr.start + fr.len; ++o) {
+      if (o < 0 || o >= sp.n || cover[size_t(o)] >= 0) return false;
+      cover[size_t(o)] = int(r);
+    }
+  }
+  for (int64_t o = 0; o < sp.n; ++o) {
+    if (cover[size_t(o)] < 0) return false;
+    (*t)[size_t(o)] = uint8_t(cover[size_t(o)]);
+  }
+  const int32_t* w0 = s.prog.data() + s.ranges[size_t(*ref)].prog;
+  for (int64_t r = 0; r < R; ++r) {
+    if (s.ranges[size_t(r)].len == 0) continue;
+    std::vector<int> map(size_t(P), -1);
+    const int32_t* a = w0;
+    const int32_t* b = s.prog.data() + s.ranges[size_t(r)].prog;
+    if (a[0] != b[0]) return false;
+    const int nt = a[0];
+    ++a;
+    ++b;
+    for (int q = 0; q < nt; ++q) {
+      const int nl = a[0], no = a[1];
+      if (b[0] != nl || b[1] != no) return false;
+      for (int k = 0; k < nl; ++k) {
+        if (a[2 + nl + k] != b[2 + nl + k]) return false;  // combination counts
+        int& m = map[size_t(a[2 + k])];
+        if (m < 0) m = b[2 + k];
+        else if (m != b[2 + k]) return false;
+      }
+      std::vector<int32_t> oa(a + 2 + 2 * nl, a + 2 + 2 * nl + no), ob(b + 2 + 2 * nl, b + 2 + 2 * nl + no);
+      std::sort(oa.begin(), oa.end());
+      std::sort(ob.begin(), ob.end());
+      if (oa != ob) return false;
+      a += 2 + 2 * nl + no;
+      b += 2 + 2 * nl + no;
+    }
+    uint8_t* row = t->data() + moff + r * P;
+    for (int64_t x = 0; x < P; ++x) row[x] = uint8_t(map[size_t(x)] < 0 ? 0 : map[size_t(x)]);
+  }
+  return true;
+}
+
 bool fixed_shapes_enabled() {
   static const bool on = [] {
     const char* v = std::getenv("AR_FUSED_SHAPES");  // "0": never the fixed-shape kernel (for comparisons)
@@ -388,6 +452,13 @@ RunResult build_items(Plan& pl, bool vec) {
         for (size_t i = 0; i < s.ranges.size(); ++i)
           add_segment(items, b * sp.n + s.ranges[i].start, s.ranges[i].len, tag_of(i), V, vec, iv);
     }
+    if (pl.rows) {
+      if (!pl.rtab.p) {
+        hipError_t e = upload(pl.rtab, pl.rows_tab);
+        if (e != hipSuccess) return hip_fail(e, "uploading the range table");
+      }
+      sitems.clear();
+    }
     if (pl.multi && !pl.mtab.p) {
       std::vector<int32_t> t(8 + 8 * kMultiRangeWords + 16, 0);
       for (int k = 0; k < 8; ++k) t[k] = pl.mt.nc[k];
@@ -411,6 +482,11 @@ RunResult build_items(Plan& pl, bool vec) {
       words.resize(words.size() + 2 * kLeafBatch, 0);
       hipError_t e = upload(pl.prog, words);
       if (e != hipSuccess) return hip_fail(e, "uploading the fused program");
+    }
+    if (pl.rows) {
+      pl.nitems[mode] = 1;  // launched by element count (run_allreduce)
+      pl.built[mode] = true;
+      return RunResult{};
     }
     if (!sitems.empty()) {
       hipError_t e = upload(pl.items[mode], sitems);
@@ -476,6 +552,7 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
   if (exec != E_LITERAL && s->fused_ok && fixed_shapes_enabled()) {
     pl->shape = fixed_shape(*s, &pl->tab, &pl->shape_nl);
     if (pl->shape == SH_NONE) pl->multi = multi_shape(*s, &pl->mt);
+    pl->rows = rows_table(*s, &pl->rows_tab, &pl->rows_ref);
     // four vectors per thread for short launches with few ranks, as the direct kernel
     pl->md = spec.P <= 8 && spec.n * spec.batch / vec_width(spec.dtype) <= (int64_t(1) << 19) ? 4 : 2;
   }
@@ -568,7 +645,10 @@ RunResult kernel_of(const Spec& spec, int exec, int* kernel) {
   const int shape = fixed_shapes_enabled() ? fixed_shape(*s, &tab, &nl) : SH_NONE;
   // the same order of choices as run_allreduce's launch
   MultiTab mt;
-  if (strided_items(*s)) *kernel = K_STRIDED;
+  std::vector<uint8_t> rt;
+  int ref = 0;
+  if (fixed_shapes_enabled() && rows_table(*s, &rt, &ref)) *kernel = K_ROWS;
+  else if (strided_items(*s)) *kernel = K_STRIDED;
   else if (shape == SH_CHAIN) *kernel = K_FIXED_CHAIN;
   else if (shape == SH_BALANCED) *kernel = K_FIXED_BALANCED;
   else if (shape == SH_STACK) *kernel = K_FIXED_STACK;
@@ -690,7 +770,18 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
     for (int64_t off = 0; off < nit; off += cap) {  // work items are independent
       const Evs ei{off == 0 ? ev.start : nullptr, off + cap >= nit ? ev.stop : nullptr};
       const int64_t cnt = std::min(cap, nit - off);
-      if (pl->strided) {
+      if (pl->rows) {
+        // one launch (split by the launcher) over the whole batch
+        const int64_t total = spec.n * spec.batch;
+        const int iters = int(std::clamp<int64_t>(total / (int64_t(kThreads) * 16384), 1, 8));
+        const int32_t* ref = prog + pl->s->ranges[size_t(pl->rows_ref)].prog;
+        AR_DISPATCH(spec.dtype, spec.op,
+                    (e = launch_fused_rows_t<DT, OPK>(pl->D, TM, ptrs, ref, reinterpret_cast<const uint8_t*>(pl->rtab.p),
+                                                      total, int(spec.n), int(pl->s->ranges.size()), spec.P, iters,
+                                                      cap, st, ev)));
+        if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
+        break;
+      } else if (pl->strided) {
         const SItem* sit = reinterpret_cast<const SItem*>(pl->items[mode].p) + off;
         AR_DISPATCH(spec.dtype, spec.op,
                     (e = launch_fused_strided_t<DT, OPK>(pl->D, TM, cnt, ptrs, sit, prog, spec.n, st, ei)));

@@ -667,6 +667,54 @@ __global__ __launch_bounds__(kThreads) void k_fused_strided(RankPtrs ptrs, const
   }
 }
 
+// Batches of short instances whose ranges all run one program up to a renaming
+// of leaf ranks (the pieces of a vector of ~100 elements split over many ranks
+// by reduce-scatter/all-gather style schedules). A workgroup takes `iters` x
+// kThreads consecutive elements of the whole batch, one per thread per step, so
+// every cache line is fetched once, by one workgroup. Each thread looks up its
+// element's range in LDS and evaluates the reference range's program, reading
+// leaf `rank` from the buffer that the range's row names. `tab` holds the range
+// of each of the n offsets of an instance (padded to 8 bytes), then one row of
+// P ranks per range. The evaluation order is the reference program's, so the
+// bits equal those of the replay over per-range items.
+template <int DT, int OPK, int D, int TM, int B>
+__global__ __launch_bounds__(kThreads) void k_fused_rows(RankPtrs ptrs, const int32_t* __restrict__ prog,
+                                                         const uint8_t* __restrict__ tab, int64_t first,
+                                                         int64_t total, int32_t n, int32_t R, int32_t P,
+                                                         int32_t iters) {
+  extern __shared__ uint64_t rows_lds[];
+  // rows of Q = P | 1 pointers: an odd stride of 8-byte entries puts the rows
+  // that one load's lanes read in distinct LDS banks
+  const int Q = P | 1;
+  void** row_ptr = reinterpret_cast<void**>(rows_lds);         // R x Q buffers
+  void** base = row_ptr + R * Q;                               // P buffers
+  uint8_t* range_of = reinterpret_cast<uint8_t*>(base + P);    // n ranges
+  if (threadIdx.x == 0)
+    for (int x = 0; x < P; ++x) base[x] = ptrs.p[x];
+  for (int o = threadIdx.x; o < n; o += kThreads) range_of[o] = tab[o];
+  __syncthreads();
+  const int moff = (n + 7) / 8 * 8;
+  for (int i = threadIdx.x; i < R * P; i += kThreads) row_ptr[i / P * Q + i % P] = base[tab[moff + i]];
+  __syncthreads();
+  const auto w = prog_words<TM>(prog, 0);
+  const int64_t v0 = first + int64_t(blockIdx.x) * iters * kThreads;  // the workgroup's first element
+  int64_t v = v0 + threadIdx.x;
+  int o = int(v0 % n) + int(threadIdx.x);  // one wide division per workgroup, a narrow one per thread
+  o = o % n;
+  const int step = kThreads % n;
+  for (int i = 0; i < iters; ++i) {
+    const bool ok[1] = {v < total};
+    void* const* row = row_ptr + range_of[o] * Q;
+    // a line of one rank is read by the several loads whose ranges it spans:
+    // cacheable loads
+    replay<DT, OPK, D, TM, 0, B>(ptrs, w, v, ok,
+                                 [&](int rank, u32x4(&r)[1]) { ld_user<DT, 0, false>(row[rank], v, ok, r); });
+    v += kThreads;
+    o += step;
+    if (o >= n) o -= n;
+  }
+}
+
 // Several result trees per range and few ranks: each thread loads its fragment of
 // every rank once (non-temporal) into its own LDS slots, then evaluates every tree
 // from LDS. Dynamic LDS holds P x kThreads 16-byte entries; each thread touches

@@ -215,7 +215,12 @@ ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes);
  *  AR_KERNEL_MULTI           several trees per range, all of one shape over P = 3..8 leaves, at
  *                            most 8 ranges of 8 trees (the generalized algorithm with r > 0 on
  *                            up to 8 ranks): ranks staged in LDS once, the trees' ranks read
- *                            from a fixed-stride table. */
+ *                            from a fixed-stride table.
+ *  AR_KERNEL_ROWS            batches whose ranges are all shorter than 64 elements and all run one
+ *                            program up to a renaming of leaf ranks (the ring and the generalized
+ *                            algorithm's pieces of a short vector): one element per thread over
+ *                            consecutive elements of the batch, each thread's range and its
+ *                            buffers looked up in LDS. */
 typedef enum {
   AR_KERNEL_NONE = 0,
   AR_KERNEL_DIRECT = 1,
@@ -226,7 +231,8 @@ typedef enum {
   AR_KERNEL_FIXED_CHAIN = 6,
   AR_KERNEL_FIXED_BALANCED = 7,
   AR_KERNEL_FIXED_STACK = 8,
-  AR_KERNEL_MULTI = 9
+  AR_KERNEL_MULTI = 9,
+  AR_KERNEL_ROWS = 10
 } ar_kernel;
 ar_status ar_kernel_of(const ar_call* call, int32_t* kernel);
 

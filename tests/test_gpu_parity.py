@@ -508,6 +508,37 @@ def test_batched_short_ranges():
                 assert np.array_equal(bits(got.reshape(P, B, n)), bits(want)), (P, n, algo, knob, dtype, op, ex, mis)
 
 
+def test_rows_kernel_batches():
+    # batches of short instances whose ranges all run one program up to a
+    # renaming of leaf ranks take k_fused_rows (one element per thread over the
+    # whole batch, range and buffers looked up in LDS); other shapes keep the
+    # strided items. The 24-rank 10^4-instance batch runs two steps per
+    # workgroup; a tiny launch limit splits one call into many launches.
+    import allreduce_schedule_algorithms_amd as A
+    K = A.Kernel
+    cases = [(24, 106, "generalized", 0, 10_000, K.AR_KERNEL_ROWS, (("fp32", "sum"),)),
+             (24, 106, "ring", 0, 777, K.AR_KERNEL_ROWS, (("bf16", "sum"), ("int32", "max"), ("fp32", "avg"))),
+             (12, 50, "generalized", 0, 301, K.AR_KERNEL_ROWS, (("fp32", "sum"), ("bf16", "avg"))),
+             (6, 106, "ring", 0, 45, K.AR_KERNEL_ROWS, (("fp32", "sum"),)),
+             (24, 106, "generalized", 1, 200, K.AR_KERNEL_STRIDED, (("fp32", "sum"),))]
+    for i, (P, n, algo, knob, B, kern, types) in enumerate(cases):
+        assert A.ar_kernel_of(A.make_call(P, n, "fp32", "sum", algo, knob, batch=B)) == kern, (P, n, algo, knob)
+        for dtype, op in types:
+            x = inputs.make(dtype, P, n * B, seed=300 + i)
+            want = oracle.allreduce(x.reshape(P, B, n), algo, dtype, op, knob=knob, n=n)
+            for mis in (False, True):
+                got = gpu_allreduce(x, algo, dtype, op, knob, "fused", batch=B, misalign=mis)
+                assert np.array_equal(bits(got.reshape(P, B, n)), bits(want)), (P, n, algo, knob, B, dtype, op, mis)
+    x = inputs.make("fp32", 24, 106 * 100, seed=7)
+    want = oracle.allreduce(x.reshape(24, 100, 106), "ring", "fp32", "sum", n=106)
+    prev = A.ar_set_launch_blocks(3)
+    try:
+        got = gpu_allreduce(x, "ring", "fp32", "sum", 0, "fused", batch=100)
+    finally:
+        A.ar_set_launch_blocks(prev)
+    assert np.array_equal(bits(got.reshape(24, 100, 106)), bits(want))
+
+
 def test_auto_halves_run_the_oracle_choice():
     import allreduce_schedule_algorithms_amd as A
     from oracle import cost, schedules as sch
