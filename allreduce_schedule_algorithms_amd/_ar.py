@@ -78,6 +78,7 @@ class Kernel(enum.IntEnum):
     AR_KERNEL_FIXED_STACK = 8
     AR_KERNEL_MULTI = 9
     AR_KERNEL_ROWS = 10
+    AR_KERNEL_ROWS_VEC = 11
 
 
 class Exec(enum.IntEnum):

@@ -336,7 +336,17 @@ bool rows_table(const Schedule& s, std::vector<uint8_t>* t, int* ref) {
     uint8_t* row = t->data() + moff + r * P;
     for (int64_t x = 0; x < P; ++x) row[x] = uint8_t(map[size_t(x)] < 0 ? 0 : map[size_t(x)]);
   }
+  t->resize((t->size() + 7) / 8 * 8, 0);  // k_fused_rows_vec copies it in 8-byte runs
   return true;
+}
+
+// Whether a k_fused_rows call runs k_fused_rows_vec for its whole vectors:
+// 4-byte elements, one tree per range, at most 32 ranks, aligned buffers and
+// more than kTinyElements elements.
+constexpr int kRowsVecMaxRanks = 32;
+bool rows_vec(const Schedule& s) {
+  const Spec& sp = s.spec;
+  return vec_width(sp.dtype) == 4 && s.max_trees == 1 && sp.P <= kRowsVecMaxRanks && sp.n * sp.batch > kTinyElements;
 }
 
 bool fixed_shapes_enabled() {
@@ -647,7 +657,7 @@ RunResult kernel_of(const Spec& spec, int exec, int* kernel) {
   MultiTab mt;
   std::vector<uint8_t> rt;
   int ref = 0;
-  if (fixed_shapes_enabled() && rows_table(*s, &rt, &ref)) *kernel = K_ROWS;
+  if (fixed_shapes_enabled() && rows_table(*s, &rt, &ref)) *kernel = rows_vec(*s) ? K_ROWS_VEC : K_ROWS;
   else if (strided_items(*s)) *kernel = K_STRIDED;
   else if (shape == SH_CHAIN) *kernel = K_FIXED_CHAIN;
   else if (shape == SH_BALANCED) *kernel = K_FIXED_BALANCED;
@@ -771,15 +781,28 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
       const Evs ei{off == 0 ? ev.start : nullptr, off + cap >= nit ? ev.stop : nullptr};
       const int64_t cnt = std::min(cap, nit - off);
       if (pl->rows) {
-        // one launch (split by the launcher) over the whole batch
+        // whole vectors in k_fused_rows_vec where it applies, the rest (or all)
+        // in k_fused_rows; each launcher splits its launch by the block limit
         const int64_t total = spec.n * spec.batch;
-        const int iters = int(std::clamp<int64_t>(total / (int64_t(kThreads) * 16384), 1, 8));
         const int32_t* ref = prog + pl->s->ranges[size_t(pl->rows_ref)].prog;
-        AR_DISPATCH(spec.dtype, spec.op,
-                    (e = launch_fused_rows_t<DT, OPK>(pl->D, TM, ptrs, ref, reinterpret_cast<const uint8_t*>(pl->rtab.p),
-                                                      total, int(spec.n), int(pl->s->ranges.size()), spec.P, iters,
-                                                      cap, st, ev)));
-        if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
+        const uint8_t* rt = reinterpret_cast<const uint8_t*>(pl->rtab.p);
+        const int R = int(pl->s->ranges.size());
+        const int64_t nvec = vec && rows_vec(*pl->s) ? total / 4 : 0;
+        if (nvec > 0) {
+          const Evs ev1{ev.start, nvec * 4 == total ? ev.stop : nullptr};
+          AR_DISPATCH(spec.dtype, spec.op,
+                      (e = launch_fused_rows_vec_t<DT, OPK>(pl->D, ptrs, ref, rt, nvec, int(spec.n), R, spec.P, cap,
+                                                            st, ev1)));
+          if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
+        }
+        if (nvec * 4 < total) {
+          const int iters = int(std::clamp<int64_t>(total / (int64_t(kThreads) * 16384), 1, 8));
+          const Evs ev2{nvec > 0 ? nullptr : ev.start, ev.stop};
+          AR_DISPATCH(spec.dtype, spec.op,
+                      (e = launch_fused_rows_t<DT, OPK>(pl->D, TM, ptrs, ref, rt, nvec * 4, total, int(spec.n), R,
+                                                        spec.P, iters, cap, st, ev2)));
+          if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
+        }
         break;
       } else if (pl->strided) {
         const SItem* sit = reinterpret_cast<const SItem*>(pl->items[mode].p) + off;

@@ -715,6 +715,59 @@ __global__ __launch_bounds__(kThreads) void k_fused_rows(RankPtrs ptrs, const in
   }
 }
 
+// The same batches with 4-byte elements, 16-byte aligned buffers, one tree per
+// range and at most PB ranks. A one-wave workgroup loads every rank's 16-byte
+// vector at each lane's four elements, one coalesced load per rank (each line
+// once, by one instruction), and stages them in LDS, each lane in its own
+// column of [rank][element][lane] words, so no barrier is needed. It then
+// evaluates the reference range's program, reading leaf `rank` of element j
+// from the slot of the rank that element j's range renames it to; the results
+// are stored as whole vectors. `tab` is the table of k_fused_rows, padded to a
+// multiple of 8 bytes.
+constexpr int kRowsVecThreads = 64;
+template <int DT, int OPK, int D, int B, int PB>
+__global__ __launch_bounds__(kRowsVecThreads) void k_fused_rows_vec(RankPtrs ptrs, const int32_t* __restrict__ prog,
+                                                                    const uint8_t* __restrict__ tab, int64_t first,
+                                                                    int64_t nvec, int32_t n, int32_t R, int32_t P) {
+  static_assert(TT<DT>::V == 4, "four 4-byte elements per vector");
+  constexpr int T = kRowsVecThreads;
+  extern __shared__ uint32_t rows_vec_lds[];
+  uint32_t* stage = rows_vec_lds;                                // P x 4 x T words
+  uint32_t* tabw = stage + P * 4 * T;                            // the table
+  const int moff = (n + 7) / 8 * 8;
+  const int words = (moff + R * P + 7) / 8 * 2;
+  for (int i = threadIdx.x; i < words; i += T) tabw[i] = reinterpret_cast<const uint32_t*>(tab)[i];
+  __syncthreads();
+  const uint8_t* range_of = reinterpret_cast<const uint8_t*>(tabw);
+  const uint8_t* map = range_of + moff;
+  const int64_t g = first + int64_t(blockIdx.x) * T + threadIdx.x;  // vector index
+  const bool ok[1] = {g < nvec};
+  const int64_t e = g * 4;
+  int rb[4];  // each element's row of the renaming table
+  int o = int(e % n);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    rb[j] = range_of[o] * P;
+    o = o + 1 == n ? 0 : o + 1;
+  }
+  u32x4 v[PB][1];
+#pragma unroll
+  for (int y = 0; y < PB; ++y) {
+    v[y][0] = u32x4{0, 0, 0, 0};
+    if (y < P) ld_user<DT, 1, true>(ptrs.p[y], e, ok, v[y]);
+  }
+#pragma unroll
+  for (int y = 0; y < PB; ++y)
+    if (y < P)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) stage[(y * 4 + j) * T + threadIdx.x] = v[y][0][j];
+  const auto w = prog_words<1>(prog, 0);
+  replay<DT, OPK, D, 1, 1, B>(ptrs, w, e, ok, [&](int rank, u32x4(&r)[1]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[0][j] = stage[(map[rb[j] + rank] * 4 + j) * T + threadIdx.x];
+  });
+}
+
 // Several result trees per range and few ranks: each thread loads its fragment of
 // every rank once (non-temporal) into its own LDS slots, then evaluates every tree
 // from LDS. Dynamic LDS holds P x kThreads 16-byte entries; each thread touches

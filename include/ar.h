@@ -220,7 +220,12 @@ ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes);
  *                            program up to a renaming of leaf ranks (the ring and the generalized
  *                            algorithm's pieces of a short vector): one element per thread over
  *                            consecutive elements of the batch, each thread's range and its
- *                            buffers looked up in LDS. */
+ *                            buffers looked up in LDS.
+ *  AR_KERNEL_ROWS_VEC        the same batches with 4-byte elements, one tree per range, at most 32
+ *                            ranks and more than 4096 elements (16-byte aligned buffers; otherwise
+ *                            AR_KERNEL_ROWS runs): every rank's vector at four elements per thread
+ *                            loaded once and staged in LDS, the leaves read from there in each
+ *                            range's order. */
 typedef enum {
   AR_KERNEL_NONE = 0,
   AR_KERNEL_DIRECT = 1,
@@ -232,7 +237,8 @@ typedef enum {
   AR_KERNEL_FIXED_BALANCED = 7,
   AR_KERNEL_FIXED_STACK = 8,
   AR_KERNEL_MULTI = 9,
-  AR_KERNEL_ROWS = 10
+  AR_KERNEL_ROWS = 10,
+  AR_KERNEL_ROWS_VEC = 11
 } ar_kernel;
 ar_status ar_kernel_of(const ar_call* call, int32_t* kernel);
 

@@ -516,10 +516,16 @@ def test_rows_kernel_batches():
     # workgroup; a tiny launch limit splits one call into many launches.
     import allreduce_schedule_algorithms_amd as A
     K = A.Kernel
-    cases = [(24, 106, "generalized", 0, 10_000, K.AR_KERNEL_ROWS, (("fp32", "sum"),)),
-             (24, 106, "ring", 0, 777, K.AR_KERNEL_ROWS, (("bf16", "sum"), ("int32", "max"), ("fp32", "avg"))),
-             (12, 50, "generalized", 0, 301, K.AR_KERNEL_ROWS, (("fp32", "sum"), ("bf16", "avg"))),
-             (6, 106, "ring", 0, 45, K.AR_KERNEL_ROWS, (("fp32", "sum"),)),
+    # fp32 calls of more than 4096 elements on aligned buffers run the vector
+    # form (k_fused_rows_vec) for their whole vectors and k_fused_rows for a
+    # ragged tail; bf16, misaligned buffers and tiny calls run k_fused_rows alone
+    cases = [(24, 106, "generalized", 0, 10_000, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"),)),
+             (24, 106, "ring", 0, 777, K.AR_KERNEL_ROWS_VEC, (("bf16", "sum"), ("int32", "max"), ("fp32", "avg"))),
+             (12, 50, "generalized", 0, 301, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"), ("bf16", "avg"))),
+             (6, 106, "ring", 0, 45, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"), ("int32", "sum"))),
+             (24, 106, "ring", 0, 30, K.AR_KERNEL_ROWS, (("fp32", "sum"),)),
+             (32, 70, "ring", 0, 99, K.AR_KERNEL_ROWS_VEC, (("fp32", "max"),)),
+             (31, 200, "ring", 0, 41, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"),)),
              (24, 106, "generalized", 1, 200, K.AR_KERNEL_STRIDED, (("fp32", "sum"),))]
     for i, (P, n, algo, knob, B, kern, types) in enumerate(cases):
         assert A.ar_kernel_of(A.make_call(P, n, "fp32", "sum", algo, knob, batch=B)) == kern, (P, n, algo, knob)

@@ -377,8 +377,10 @@ def test_kernel_choice():
         (dict(P=24, n=106, algo="generalized", knob=5, batch=10_000), K.AR_KERNEL_REPLAY),
         (dict(P=192, n=1 << 20, dtype="bf16", algo="ahc", groups=[64, 128]), K.AR_KERNEL_REPLAY),
         (dict(P=24, n=106, algo="rd", batch=10_000), K.AR_KERNEL_REPLAY),
-        (dict(P=24, n=106, algo="generalized", batch=10_000), K.AR_KERNEL_ROWS),
-        (dict(P=24, n=106, algo="ring", batch=10_000), K.AR_KERNEL_ROWS),
+        (dict(P=24, n=106, algo="generalized", batch=10_000), K.AR_KERNEL_ROWS_VEC),
+        (dict(P=24, n=106, algo="ring", batch=10_000), K.AR_KERNEL_ROWS_VEC),
+        (dict(P=24, n=106, algo="ring", batch=10_000, dtype="bf16"), K.AR_KERNEL_ROWS),
+        (dict(P=24, n=106, algo="ring", batch=30), K.AR_KERNEL_ROWS),
         (dict(P=24, n=106, algo="generalized", knob=1, batch=10_000), K.AR_KERNEL_STRIDED),
         (dict(P=8, n=1 << 20, algo="direct"), K.AR_KERNEL_DIRECT),
         (dict(P=8, n=1 << 20, algo="direct", exec="replay"), K.AR_KERNEL_FIXED_CHAIN),
