@@ -123,6 +123,7 @@ struct Plan {
   bool strided = false;  // fused: items are SItem (batches of short ranges)
   bool rows = false;      // fused: k_fused_rows (strided batches of one program shape)
   int rows_ref = 0;       // its reference range
+  int64_t rows_n = 0;     // the instance length its table describes (1: one range, identity renaming)
   std::vector<uint8_t> rows_tab;  // its range and rank tables
   DevBuf rtab;            // the same on the device
   int shape = SH_NONE;    // fused: every tree of this fixed shape (k_fused_fixed)
@@ -341,12 +342,27 @@ bool rows_table(const Schedule& s, std::vector<uint8_t>* t, int* ref) {
 }
 
 // Whether a k_fused_rows call runs k_fused_rows_vec for its whole vectors:
-// 4-byte elements, one tree per range, at most 32 ranks, aligned buffers and
-// more than kTinyElements elements.
+// 4-byte elements, at most 32 ranks, aligned buffers and more than
+// kTinyElements elements.
 constexpr int kRowsVecMaxRanks = 32;
 bool rows_vec(const Schedule& s) {
   const Spec& sp = s.spec;
-  return vec_width(sp.dtype) == 4 && s.max_trees == 1 && sp.P <= kRowsVecMaxRanks && sp.n * sp.batch > kTinyElements;
+  return vec_width(sp.dtype) == 4 && sp.P <= kRowsVecMaxRanks && sp.n * sp.batch > kTinyElements;
+}
+
+// Whether a single-range program of several trees over more ranks than the
+// LDS staging of k_fused_staged holds (17..32) runs the rows kernels as one
+// range of instance length 1 (4-byte elements, more than kTinyElements
+// elements): every rank is then loaded once per element, not once per tree.
+// Fills *t with that table (range 0, identity renaming).
+bool rows_flat(const Schedule& s, std::vector<uint8_t>* t) {
+  const Spec& sp = s.spec;
+  const bool flat = s.ranges.size() == 1 && s.ranges[0].start == 0 && s.ranges[0].len == sp.n;
+  if (!flat || s.max_trees <= 1 || sp.P <= kMaxStagedRanks || !rows_vec(s)) return false;
+  t->assign(size_t(8 + sp.P), 0);
+  for (int x = 0; x < sp.P; ++x) (*t)[size_t(8 + x)] = uint8_t(x);
+  t->resize((t->size() + 7) / 8 * 8, 0);
+  return true;
 }
 
 bool fixed_shapes_enabled() {
@@ -563,6 +579,12 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
     pl->shape = fixed_shape(*s, &pl->tab, &pl->shape_nl);
     if (pl->shape == SH_NONE) pl->multi = multi_shape(*s, &pl->mt);
     pl->rows = rows_table(*s, &pl->rows_tab, &pl->rows_ref);
+    pl->rows_n = spec.n;
+    if (!pl->rows && rows_flat(*s, &pl->rows_tab)) {
+      pl->rows = true;
+      pl->rows_ref = 0;
+      pl->rows_n = 1;
+    }
     // four vectors per thread for short launches with few ranks, as the direct kernel
     pl->md = spec.P <= 8 && spec.n * spec.batch / vec_width(spec.dtype) <= (int64_t(1) << 19) ? 4 : 2;
   }
@@ -657,7 +679,8 @@ RunResult kernel_of(const Spec& spec, int exec, int* kernel) {
   MultiTab mt;
   std::vector<uint8_t> rt;
   int ref = 0;
-  if (fixed_shapes_enabled() && rows_table(*s, &rt, &ref)) *kernel = rows_vec(*s) ? K_ROWS_VEC : K_ROWS;
+  if (fixed_shapes_enabled() && (rows_table(*s, &rt, &ref) || rows_flat(*s, &rt)))
+    *kernel = rows_vec(*s) ? K_ROWS_VEC : K_ROWS;
   else if (strided_items(*s)) *kernel = K_STRIDED;
   else if (shape == SH_CHAIN) *kernel = K_FIXED_CHAIN;
   else if (shape == SH_BALANCED) *kernel = K_FIXED_BALANCED;
@@ -791,16 +814,16 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
         if (nvec > 0) {
           const Evs ev1{ev.start, nvec * 4 == total ? ev.stop : nullptr};
           AR_DISPATCH(spec.dtype, spec.op,
-                      (e = launch_fused_rows_vec_t<DT, OPK>(pl->D, ptrs, ref, rt, nvec, int(spec.n), R, spec.P, cap,
-                                                            st, ev1)));
+                      (e = launch_fused_rows_vec_t<DT, OPK>(pl->D, TM, pl->rows_n == 1, ptrs, ref, rt, nvec,
+                                                            int(pl->rows_n), R, spec.P, cap, st, ev1)));
           if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
         }
         if (nvec * 4 < total) {
           const int iters = int(std::clamp<int64_t>(total / (int64_t(kThreads) * 16384), 1, 8));
           const Evs ev2{nvec > 0 ? nullptr : ev.start, ev.stop};
           AR_DISPATCH(spec.dtype, spec.op,
-                      (e = launch_fused_rows_t<DT, OPK>(pl->D, TM, ptrs, ref, rt, nvec * 4, total, int(spec.n), R,
-                                                        spec.P, iters, cap, st, ev2)));
+                      (e = launch_fused_rows_t<DT, OPK>(pl->D, TM, ptrs, ref, rt, nvec * 4, total, int(pl->rows_n),
+                                                        R, spec.P, iters, cap, st, ev2)));
           if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
         }
         break;

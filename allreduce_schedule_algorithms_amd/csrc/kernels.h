@@ -715,8 +715,9 @@ __global__ __launch_bounds__(kThreads) void k_fused_rows(RankPtrs ptrs, const in
   }
 }
 
-// The same batches with 4-byte elements, 16-byte aligned buffers, one tree per
-// range and at most PB ranks. A one-wave workgroup loads every rank's 16-byte
+// The same batches with 4-byte elements, 16-byte aligned buffers and at most
+// PB ranks (and single-range programs of several trees over 17..32 ranks, as
+// one range of instance length 1). A one-wave workgroup loads every rank's 16-byte
 // vector at each lane's four elements, one coalesced load per rank (each line
 // once, by one instruction), and stages them in LDS, each lane in its own
 // column of [rank][element][lane] words, so no barrier is needed. It then
@@ -725,7 +726,9 @@ __global__ __launch_bounds__(kThreads) void k_fused_rows(RankPtrs ptrs, const in
 // are stored as whole vectors. `tab` is the table of k_fused_rows, padded to a
 // multiple of 8 bytes.
 constexpr int kRowsVecThreads = 64;
-template <int DT, int OPK, int D, int B, int PB>
+// With ID (one range, identity renaming) no table is read and each lane's
+// vectors are staged whole, [rank][lane] (one 16-byte LDS access per leaf).
+template <int DT, int OPK, int D, int TM, int B, int PB, bool ID>
 __global__ __launch_bounds__(kRowsVecThreads) void k_fused_rows_vec(RankPtrs ptrs, const int32_t* __restrict__ prog,
                                                                     const uint8_t* __restrict__ tab, int64_t first,
                                                                     int64_t nvec, int32_t n, int32_t R, int32_t P) {
@@ -733,6 +736,24 @@ __global__ __launch_bounds__(kRowsVecThreads) void k_fused_rows_vec(RankPtrs ptr
   constexpr int T = kRowsVecThreads;
   extern __shared__ uint32_t rows_vec_lds[];
   uint32_t* stage = rows_vec_lds;                                // P x 4 x T words
+  if constexpr (ID) {
+    u32x4* st4 = reinterpret_cast<u32x4*>(stage);
+    const int64_t g = first + int64_t(blockIdx.x) * T + threadIdx.x;
+    const bool ok[1] = {g < nvec};
+    const int64_t e = g * 4;
+    u32x4 v[PB][1];
+#pragma unroll
+    for (int y = 0; y < PB; ++y) {
+      v[y][0] = u32x4{0, 0, 0, 0};
+      if (y < P) ld_user<DT, 1, true>(ptrs.p[y], e, ok, v[y]);
+    }
+#pragma unroll
+    for (int y = 0; y < PB; ++y)
+      if (y < P) st4[y * T + threadIdx.x] = v[y][0];
+    const auto w = prog_words<TM>(prog, 0);
+    replay<DT, OPK, D, TM, 1, B>(ptrs, w, e, ok, [&](int rank, u32x4(&r)[1]) { r[0] = st4[rank * T + threadIdx.x]; });
+    return;
+  }
   uint32_t* tabw = stage + P * 4 * T;                            // the table
   const int moff = (n + 7) / 8 * 8;
   const int words = (moff + R * P + 7) / 8 * 2;
@@ -761,8 +782,8 @@ __global__ __launch_bounds__(kRowsVecThreads) void k_fused_rows_vec(RankPtrs ptr
     if (y < P)
 #pragma unroll
       for (int j = 0; j < 4; ++j) stage[(y * 4 + j) * T + threadIdx.x] = v[y][0][j];
-  const auto w = prog_words<1>(prog, 0);
-  replay<DT, OPK, D, 1, 1, B>(ptrs, w, e, ok, [&](int rank, u32x4(&r)[1]) {
+  const auto w = prog_words<TM>(prog, 0);
+  replay<DT, OPK, D, TM, 1, B>(ptrs, w, e, ok, [&](int rank, u32x4(&r)[1]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) r[0][j] = stage[(map[rb[j] + rank] * 4 + j) * T + threadIdx.x];
   });

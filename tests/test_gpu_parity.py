@@ -512,8 +512,9 @@ def test_rows_kernel_batches():
     # batches of short instances whose ranges all run one program up to a
     # renaming of leaf ranks take k_fused_rows (one element per thread over the
     # whole batch, range and buffers looked up in LDS); other shapes keep the
-    # strided items. The 24-rank 10^4-instance batch runs two steps per
-    # workgroup; a tiny launch limit splits one call into many launches.
+    # strided items; single-range programs of several trees over 17..32 ranks
+    # run as one range of instance length 1. A tiny launch limit splits one
+    # call into many launches.
     import allreduce_schedule_algorithms_amd as A
     K = A.Kernel
     # fp32 calls of more than 4096 elements on aligned buffers run the vector
@@ -526,6 +527,8 @@ def test_rows_kernel_batches():
              (24, 106, "ring", 0, 30, K.AR_KERNEL_ROWS, (("fp32", "sum"),)),
              (32, 70, "ring", 0, 99, K.AR_KERNEL_ROWS_VEC, (("fp32", "max"),)),
              (31, 200, "ring", 0, 41, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"),)),
+             (24, 106, "generalized", 5, 500, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"), ("int32", "max"), ("fp32", "avg"))),
+             (24, 20_001, "generalized", 4, 1, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"),)),
              (24, 106, "generalized", 1, 200, K.AR_KERNEL_STRIDED, (("fp32", "sum"),))]
     for i, (P, n, algo, knob, B, kern, types) in enumerate(cases):
         assert A.ar_kernel_of(A.make_call(P, n, "fp32", "sum", algo, knob, batch=B)) == kern, (P, n, algo, knob)

@@ -374,7 +374,9 @@ def test_kernel_choice():
         (dict(P=7, n=1 << 24, algo="generalized", knob=3), K.AR_KERNEL_MULTI),
         (dict(P=7, n=1 << 24, algo="generalized", knob=1), K.AR_KERNEL_MULTI),
         (dict(P=12, n=4099, algo="generalized", knob=2), K.AR_KERNEL_STAGED),
-        (dict(P=24, n=106, algo="generalized", knob=5, batch=10_000), K.AR_KERNEL_REPLAY),
+        (dict(P=24, n=106, algo="generalized", knob=5, batch=10_000), K.AR_KERNEL_ROWS_VEC),
+        (dict(P=24, n=106, algo="generalized", knob=5, batch=10_000, dtype="bf16"), K.AR_KERNEL_REPLAY),
+        (dict(P=24, n=106, algo="generalized", knob=5, batch=30), K.AR_KERNEL_REPLAY),
         (dict(P=192, n=1 << 20, dtype="bf16", algo="ahc", groups=[64, 128]), K.AR_KERNEL_REPLAY),
         (dict(P=24, n=106, algo="rd", batch=10_000), K.AR_KERNEL_REPLAY),
         (dict(P=24, n=106, algo="generalized", batch=10_000), K.AR_KERNEL_ROWS_VEC),
