@@ -281,9 +281,9 @@ bool strided_items(const Schedule& s) {
 }
 
 // Whether a batched call with strided items can run k_fused_rows instead:
-// every range's program is the reference range's (the first non-empty one)
-// with its leaf ranks renamed, one renaming per range for all its trees, with
-// the same combination counts and the same output ranks per tree. Fills *t
+// one tree per range, and every range's program is the reference range's (the
+// first non-empty one) with its leaf ranks renamed, with the same combination
+// counts and the same output ranks. Fills *t
 // with the range of each offset of an instance (n bytes, padded to 8), then per
 // range a row of P bytes mapping a leaf rank of the reference range to the
 // range's own, and *ref with the reference range's index.
@@ -291,7 +291,8 @@ constexpr int64_t kRowsMaxTable = 4096;  // limit on R x (P | 1) and on n (LDS)
 bool rows_table(const Schedule& s, std::vector<uint8_t>* t, int* ref) {
   const Spec& sp = s.spec;
   const int64_t R = int64_t(s.ranges.size()), P = sp.P;
-  if (!strided_items(s) || R > 255 || R * (P | 1) > kRowsMaxTable || sp.n > kRowsMaxTable) return false;
+  if (!strided_items(s) || s.max_trees != 1 || R > 255 || R * (P | 1) > kRowsMaxTable || sp.n > kRowsMaxTable)
+    return false;
   const int64_t moff = (sp.n + 7) / 8 * 8;
   t->assign(size_t(moff + R * P), 0);
   std::vector<int> cover(size_t(sp.n), -1);

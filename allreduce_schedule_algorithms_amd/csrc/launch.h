@@ -249,10 +249,9 @@ hipError_t launch_fused_rows_vec_t(int D, int TM, bool ident, const RankPtrs& pt
   if (P <= 8) return rows_vec_d<DT, OPK, DD, 1, 8>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);       \
   if (P <= 16) return rows_vec_d<DT, OPK, DD, 1, 16>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);     \
   return rows_vec_d<DT, OPK, DD, 1, 32>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev)
-#define AR_ROWS_VEC_TREES(DD)                                                                                    \
-  if (ident) return rows_vec_d<DT, OPK, DD, kMaxFusedTrees, 32, true>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev); \
-  return rows_vec_d<DT, OPK, DD, kMaxFusedTrees, 32>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev)
-    if (P > 32) return hipErrorInvalidValue;
+#define AR_ROWS_VEC_TREES(DD) \
+  return rows_vec_d<DT, OPK, DD, kMaxFusedTrees, 32, true>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev)
+    if (P > 32 || (TM > 1 && !ident)) return hipErrorInvalidValue;  // several trees: one range, identity renaming
     if (TM > 1) {
       switch (D) {
         case 2: AR_ROWS_VEC_TREES(2);
