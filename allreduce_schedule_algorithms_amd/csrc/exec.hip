@@ -801,34 +801,35 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
     ptrs.xcd = pl->strided || pl->s->prog.size() * sizeof(int32_t) > kXcdProgramBytes ? 1 : 0;
     const int64_t nit = pl->nitems[mode], cap = launch_blocks();
     const int TM = pl->s->max_trees > 1 ? kMaxFusedTrees : 1;
+    if (pl->rows) {
+      // whole vectors in k_fused_rows_vec where it applies, the rest (or all)
+      // in k_fused_rows; each launcher splits its launch by the block limit
+      const int64_t total = spec.n * spec.batch;
+      const int32_t* ref = prog + pl->s->ranges[size_t(pl->rows_ref)].prog;
+      const uint8_t* rt = reinterpret_cast<const uint8_t*>(pl->rtab.p);
+      const int R = int(pl->s->ranges.size());
+      const int64_t nvec = vec && rows_vec(*pl->s) ? total / 4 : 0;
+      if (nvec > 0) {
+        const Evs ev1{ev.start, nvec * 4 == total ? ev.stop : nullptr};
+        AR_DISPATCH(spec.dtype, spec.op,
+                    (e = launch_fused_rows_vec_t<DT, OPK>(pl->D, TM, pl->rows_n == 1, ptrs, ref, rt, nvec,
+                                                          int(pl->rows_n), R, spec.P, cap, st, ev1)));
+        if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
+      }
+      if (nvec * 4 < total) {
+        const int iters = int(std::clamp<int64_t>(total / (int64_t(kThreads) * 16384), 1, 8));
+        const Evs ev2{nvec > 0 ? nullptr : ev.start, ev.stop};
+        AR_DISPATCH(spec.dtype, spec.op,
+                    (e = launch_fused_rows_t<DT, OPK>(pl->D, TM, ptrs, ref, rt, nvec * 4, total, int(pl->rows_n), R,
+                                                      spec.P, iters, cap, st, ev2)));
+        if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
+      }
+      return res;
+    }
     for (int64_t off = 0; off < nit; off += cap) {  // work items are independent
       const Evs ei{off == 0 ? ev.start : nullptr, off + cap >= nit ? ev.stop : nullptr};
       const int64_t cnt = std::min(cap, nit - off);
-      if (pl->rows) {
-        // whole vectors in k_fused_rows_vec where it applies, the rest (or all)
-        // in k_fused_rows; each launcher splits its launch by the block limit
-        const int64_t total = spec.n * spec.batch;
-        const int32_t* ref = prog + pl->s->ranges[size_t(pl->rows_ref)].prog;
-        const uint8_t* rt = reinterpret_cast<const uint8_t*>(pl->rtab.p);
-        const int R = int(pl->s->ranges.size());
-        const int64_t nvec = vec && rows_vec(*pl->s) ? total / 4 : 0;
-        if (nvec > 0) {
-          const Evs ev1{ev.start, nvec * 4 == total ? ev.stop : nullptr};
-          AR_DISPATCH(spec.dtype, spec.op,
-                      (e = launch_fused_rows_vec_t<DT, OPK>(pl->D, TM, pl->rows_n == 1, ptrs, ref, rt, nvec,
-                                                            int(pl->rows_n), R, spec.P, cap, st, ev1)));
-          if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
-        }
-        if (nvec * 4 < total) {
-          const int iters = int(std::clamp<int64_t>(total / (int64_t(kThreads) * 16384), 1, 8));
-          const Evs ev2{nvec > 0 ? nullptr : ev.start, ev.stop};
-          AR_DISPATCH(spec.dtype, spec.op,
-                      (e = launch_fused_rows_t<DT, OPK>(pl->D, TM, ptrs, ref, rt, nvec * 4, total, int(pl->rows_n),
-                                                        R, spec.P, iters, cap, st, ev2)));
-          if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
-        }
-        break;
-      } else if (pl->strided) {
+      if (pl->strided) {
         const SItem* sit = reinterpret_cast<const SItem*>(pl->items[mode].p) + off;
         AR_DISPATCH(spec.dtype, spec.op,
                     (e = launch_fused_strided_t<DT, OPK>(pl->D, TM, cnt, ptrs, sit, prog, spec.n, st, ei)));
