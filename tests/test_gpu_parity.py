@@ -527,6 +527,10 @@ def test_rows_kernel_batches():
              (24, 106, "ring", 0, 30, K.AR_KERNEL_ROWS, (("fp32", "sum"),)),
              (32, 70, "ring", 0, 99, K.AR_KERNEL_ROWS_VEC, (("fp32", "max"),)),
              (31, 200, "ring", 0, 41, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"),)),
+             # fewer elements than ranks: one-element ranges, vectors spanning instances
+             (24, 20, "ring", 0, 500, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"), ("int32", "sum"))),
+             (24, 7, "ring", 0, 1001, K.AR_KERNEL_ROWS_VEC, (("fp32", "max"),)),
+             (17, 16, "generalized", 0, 300, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"),)),
              (24, 106, "generalized", 5, 500, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"), ("int32", "max"), ("fp32", "avg"))),
              (24, 20_001, "generalized", 4, 1, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"),)),
              (24, 106, "generalized", 1, 200, K.AR_KERNEL_STRIDED, (("fp32", "sum"),))]
