@@ -368,7 +368,7 @@ bool rows_flat(const Schedule& s, std::vector<uint8_t>* t) {
 
 bool fixed_shapes_enabled() {
   static const bool on = [] {
-    const char* v = std::getenv("AR_FUSED_SHAPES");  // "0": never the fixed-shape kernel (for comparisons)
+    const char* v = std::getenv("AR_FUSED_SHAPES");  // "0": no shape-specialised kernel (for comparisons)
     return !(v && v[0] == '0');
   }();
   return on;
