@@ -256,12 +256,14 @@ hipError_t launch_fused_rows_vec_t(int D, int TM, bool ident, const RankPtrs& pt
       switch (D) {
         case 2: AR_ROWS_VEC_TREES(2);
         case 4: AR_ROWS_VEC_TREES(4);
+        case 6: AR_ROWS_VEC_TREES(6);
         default: AR_ROWS_VEC_TREES(8);
       }
     }
     switch (D) {
       case 2: AR_ROWS_VEC(2);
       case 4: AR_ROWS_VEC(4);
+      case 6: AR_ROWS_VEC(6);
       case 8: AR_ROWS_VEC(8);
       default: AR_ROWS_VEC(16);
     }
