@@ -550,6 +550,21 @@ def test_rows_kernel_batches():
     finally:
         A.ar_set_launch_blocks(prev)
     assert np.array_equal(bits(got.reshape(24, 100, 106)), bits(want))
+    # the caller's events bracket the vector launch and the ragged tail's launch
+    torch = torch_mod()
+    x = inputs.make("fp32", 24, 106 * 39, seed=9)  # 4134 elements: 1033 vectors and 2 more
+    bufs, keep = to_device(x, "fp32")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st = torch.cuda.current_stream()
+    a.record(st)
+    b.record(st)
+    call = A.make_call(24, 106, "fp32", "sum", "ring", batch=39, start_event=a, stop_event=b)
+    A.ar_allreduce_ex([t.data_ptr() for t in bufs], call, st)
+    torch.cuda.synchronize()
+    assert a.elapsed_time(b) > 0
+    want = oracle.allreduce(x.reshape(24, 39, 106), "ring", "fp32", "sum", n=106).reshape(24, 39 * 106)
+    assert np.array_equal(bits(from_device(bufs, "fp32")), bits(want))
+    del keep
 
 
 def test_auto_halves_run_the_oracle_choice():
