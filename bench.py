@@ -640,7 +640,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build runs every rank of an Allreduce as a buffer "
+        print(f"bench.py measures one GPU: the library runs every rank of an Allreduce as a buffer "
               f"in one GPU's HBM and has no multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 
