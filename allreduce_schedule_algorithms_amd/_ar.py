@@ -79,6 +79,7 @@ class Kernel(enum.IntEnum):
     AR_KERNEL_MULTI = 9
     AR_KERNEL_ROWS = 10
     AR_KERNEL_ROWS_VEC = 11
+    AR_KERNEL_DAG = 12
 
 
 class Exec(enum.IntEnum):
@@ -131,6 +132,12 @@ class ar_cost(C.Structure):
                 ("essential_bytes", C.c_double)]
 
 
+class ar_cache_stats(C.Structure):
+    _fields_ = [("live_plans", C.c_int64), ("retired_plans", C.c_int64), ("workspaces", C.c_int64),
+                ("retired_workspaces", C.c_int64), ("plan_device_bytes", C.c_int64),
+                ("workspace_device_bytes", C.c_int64)]
+
+
 class ar_cost_model(C.Structure):
     _fields_ = [("alpha", C.c_double), ("beta", C.c_double), ("gamma", C.c_double), ("form", C.c_int32),
                 ("reserved", C.c_int32)]
@@ -146,6 +153,8 @@ SIGNATURES = {
     "ar_all_gather": (C.c_int, [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_void_p]),
     "ar_workspace_bytes": (C.c_int, [C.POINTER(ar_call), C.POINTER(C.c_size_t)]),
     "ar_set_launch_blocks": (C.c_int, [C.c_int64, C.POINTER(C.c_int64)]),
+    "ar_cache_stats_get": (C.c_int, [C.POINTER(ar_cache_stats)]),
+    "ar_release_cached": (C.c_int, []),
     "ar_kernel_of": (C.c_int, [C.POINTER(ar_call), C.POINTER(C.c_int32)]),
     "ar_schedule_build": (C.c_int, [C.POINTER(ar_call), C.POINTER(C.c_void_p)]),
     "ar_schedule_info_get": (C.c_int, [C.c_void_p, C.POINTER(ar_schedule_info)]),
@@ -210,6 +219,12 @@ def _ptrs(bufs):
         return bufs
     ptrs = [b if isinstance(b, int) else b.data_ptr() for b in bufs]
     return (C.c_void_p * max(len(ptrs), 1))(*ptrs)
+
+
+def marshal_ptrs(bufs):
+    """The host array of P device pointers an entry point takes, built once: a
+    caller that repeats calls on the same buffers passes it instead of a list."""
+    return _ptrs(bufs)
 
 
 def _stream(stream):
@@ -282,6 +297,18 @@ def ar_kernel_of(call: ar_call) -> Kernel:
     out = C.c_int32(0)
     _check(lib.ar_kernel_of(C.byref(call), C.byref(out)))
     return Kernel(out.value)
+
+
+def ar_cache_stats_get() -> dict:
+    """Plans and workspaces the library holds (live and retired) and their device bytes."""
+    out = ar_cache_stats()
+    _check(lib.ar_cache_stats_get(C.byref(out)))
+    return {name: getattr(out, name) for name, _ in ar_cache_stats._fields_}
+
+
+def ar_release_cached() -> None:
+    """Free every plan, workspace and cached schedule (see include/ar.h for the conditions)."""
+    _check(lib.ar_release_cached())
 
 
 def ar_set_launch_blocks(max_blocks: int) -> int:

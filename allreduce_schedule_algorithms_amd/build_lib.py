@@ -1,4 +1,5 @@
-"""Build libar_mi355x.so in-tree with hipcc for gfx950.
+"""Build libar_mi355x.so (the Allreduce library) and libar_probe.so (memory-traffic
+ceiling kernels for measurement) in-tree with hipcc for gfx950.
 
 Usage: python allreduce_schedule_algorithms_amd/build_lib.py   (or __graft_entry__.build())
 Run it as a file, not as a package module: importing the package loads the library.
@@ -14,6 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libar_mi355x.so")
+PROBE_LIB = os.path.join(HERE, "libar_probe.so")
 ROOT = os.path.dirname(HERE)
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -43,18 +45,24 @@ def _compile(src: str, device: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4, 16)) as ex:
-        objs = list(ex.map(lambda s: _compile(*s), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + [("probe.hip", True)]
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4, 16)) as ex:
+        objs = list(ex.map(lambda s: _compile(*s), srcs))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

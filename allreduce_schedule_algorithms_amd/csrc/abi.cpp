@@ -265,6 +265,27 @@ ar_status ar_kernel_of(const ar_call* call, int32_t* kernel) {
   return AR_OK;
 }
 
+ar_status ar_cache_stats_get(ar_cache_stats* out) {
+  if (!out) return fail(AR_INVALID_ARGUMENT, "out is NULL");
+  const ar::CacheStats c = ar::cache_stats();
+  out->live_plans = c.live_plans;
+  out->retired_plans = c.retired_plans;
+  out->workspaces = c.workspaces;
+  out->retired_workspaces = c.retired_workspaces;
+  out->plan_device_bytes = c.plan_device_bytes;
+  out->workspace_device_bytes = c.workspace_device_bytes;
+  return AR_OK;
+}
+
+ar_status ar_release_cached(void) {
+  ar::RunResult r = ar::release_cached();
+  if (r.status) {
+    t_hip = r.hip_error;
+    return fail(ar_status(r.status), r.message);
+  }
+  return AR_OK;
+}
+
 ar_status ar_schedule_build(const ar_call* call, ar_schedule** out) {
   std::string err;
   ar::Spec spec;

@@ -41,9 +41,21 @@ bool set_launch_blocks(int64_t blocks, int64_t* previous);
 // ar_kernel in include/ar.h.
 enum Kernel : int32_t {
   K_NONE = 0, K_DIRECT = 1, K_LITERAL = 2, K_REPLAY = 3, K_STAGED = 4, K_STRIDED = 5,
-  K_FIXED_CHAIN = 6, K_FIXED_BALANCED = 7, K_FIXED_STACK = 8, K_MULTI = 9, K_ROWS = 10, K_ROWS_VEC = 11
+  K_FIXED_CHAIN = 6, K_FIXED_BALANCED = 7, K_FIXED_STACK = 8, K_MULTI = 9, K_ROWS = 10, K_ROWS_VEC = 11,
+  K_DAG = 12
 };
 RunResult kernel_of(const Spec& spec, int exec, int* kernel);
+
+// Plans (device tables per schedule and size) and literal workspaces held by
+// the library; retired ones stay allocated until release_cached().
+struct CacheStats {
+  int64_t live_plans = 0, retired_plans = 0, workspaces = 0, retired_workspaces = 0;
+  int64_t plan_device_bytes = 0, workspace_device_bytes = 0;
+};
+CacheStats cache_stats();
+// Synchronize every device the caches touch, then free every plan, workspace
+// and cached schedule.
+RunResult release_cached();
 
 // Cached host schedule for a spec (shared with the executor's plan cache).
 std::shared_ptr<const Schedule> cached_schedule(const Spec& spec, std::string* err);

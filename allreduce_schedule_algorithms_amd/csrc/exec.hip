@@ -23,6 +23,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <limits>
@@ -142,20 +143,40 @@ struct Plan {
   int md = 2;             // k_fused_fixed: vectors per thread (items of kThreads * md vectors)
   int64_t slot_bytes = 0;
   size_t ws_bytes = 0;
+  int kernel = K_NONE;     // the kernel family the plan launches (ar_kernel)
+  std::string fallback;   // why a fused call runs the literal steps (empty otherwise)
+  size_t device_bytes = 0;  // device memory the plan's tables hold
 };
 
+// Plans hold device tables that enqueued launches and captured HIP graphs keep
+// as kernel arguments, so none is freed while the process may still use it:
+// when the cache is full its plans move to the retired list, which keeps them
+// (and their device buffers) until ar_release_cached().
 std::map<std::string, std::unique_ptr<Plan>>& plan_cache() {
   static std::map<std::string, std::unique_ptr<Plan>> m;
   return m;
 }
+std::vector<std::unique_ptr<Plan>>& retired_plans() {
+  static std::vector<std::unique_ptr<Plan>> v;
+  return v;
+}
+constexpr size_t kMaxLivePlans = 256;
 
+// Literal workspace for calls that bring none: one per (device, stream), so
+// calls on different streams never share partials. A workspace that has to
+// grow is retired (kept, like a plan) rather than freed, because launches
+// still in flight or captured earlier may use it.
 struct Workspace {
   void* p = nullptr;
   size_t bytes = 0;
 };
-std::map<int, Workspace>& ws_cache() {
-  static std::map<int, Workspace> m;
+std::map<std::pair<int, uintptr_t>, Workspace>& ws_cache() {
+  static std::map<std::pair<int, uintptr_t>, Workspace> m;
   return m;
+}
+std::vector<Workspace>& retired_ws() {
+  static std::vector<Workspace> v;
+  return v;
 }
 
 RunResult hip_fail(hipError_t e, const char* what) {
@@ -166,11 +187,16 @@ RunResult hip_fail(hipError_t e, const char* what) {
   return r;
 }
 
+// Device copy of a host table. The copy is synchronous, so a plan is complete
+// before its first launch is enqueued; run_allreduce refuses to build one while
+// the caller's stream is capturing.
+size_t* g_upload_bytes = nullptr;  // the plan being built counts its bytes here (under g_mu)
 template <typename T>
 hipError_t upload(DevBuf& b, const std::vector<T>& v) {
   if (v.empty()) return hipSuccess;
   hipError_t e = hipMalloc(&b.p, v.size() * sizeof(T));
   if (e != hipSuccess) { b.p = nullptr; return e; }
+  if (g_upload_bytes) *g_upload_bytes += v.size() * sizeof(T);
   return hipMemcpy(b.p, v.data(), v.size() * sizeof(T), hipMemcpyHostToDevice);
 }
 
@@ -544,18 +570,93 @@ bool same_spec(const Spec& a, const Spec& b) {
          a.knob == b.knob && a.coll == b.coll && a.steps == b.steps && a.groups == b.groups;
 }
 
+// Whether the fused replay can run a schedule: at most kMaxFusedTrees result
+// trees per range, and several trees only with a stack of depth <= 8.
+bool fused_runs(const Schedule& s) {
+  const int D = s.max_need <= 2 ? 2 : s.max_need <= 4 ? 4 : s.max_need <= 8 ? 8 : 16;
+  return s.max_trees <= kMaxFusedTrees && !(s.max_trees > 1 && D > 8);
+}
+
+const char* kernel_name(int k) {
+  static const char* names[] = {"none", "k_direct", "k_literal", "k_fused", "k_fused_staged", "k_fused_strided",
+                                "k_fused_fixed (chain)", "k_fused_fixed (balanced)", "k_fused_fixed (stack)",
+                                "k_fused_multi", "k_fused_rows", "k_fused_rows_vec", "k_fused_dag"};
+  return k >= 0 && k < int(sizeof(names) / sizeof(names[0])) ? names[k] : "?";
+}
+
+// The kernel family a fused plan launches, in the order run_allreduce tries
+// them; K_LITERAL (with the reason in pl.fallback) when no replay holds the
+// program.
+void choose_kernel(Plan& pl) {
+  const Schedule& s = *pl.s;
+  if (pl.exec == E_LITERAL) { pl.kernel = K_LITERAL; return; }
+  if (!s.fused_ok) {
+    pl.kernel = K_LITERAL;
+    pl.fallback = "no replay program (" + s.fused_error + ")";
+    return;
+  }
+  if (!fused_runs(s)) {
+    pl.kernel = K_LITERAL;
+    pl.fallback = std::to_string(s.max_trees) + " result trees per range with a stack of " +
+                  std::to_string(s.max_need) + " (the replay keeps at most " + std::to_string(kMaxFusedTrees) +
+                  " trees, with a stack of at most 8)";
+    return;
+  }
+  if (pl.rows) pl.kernel = rows_vec(s) ? K_ROWS_VEC : K_ROWS;
+  else if (strided_items(s)) pl.kernel = K_STRIDED;
+  else if (pl.shape == SH_CHAIN) pl.kernel = K_FIXED_CHAIN;
+  else if (pl.shape == SH_BALANCED) pl.kernel = K_FIXED_BALANCED;
+  else if (pl.shape == SH_STACK) pl.kernel = K_FIXED_STACK;
+  else if (pl.multi) pl.kernel = K_MULTI;
+  else if (s.max_trees > 1 && s.spec.P <= kMaxStagedRanks) pl.kernel = K_STAGED;
+  else pl.kernel = K_REPLAY;
+}
+
+bool trace_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("AR_TRACE");  // "1": one line per plan on stderr
+    return v && v[0] && v[0] != '0';
+  }();
+  return on;
+}
+
+void trace_plan(const Plan& pl) {
+  static const char* dt[] = {"int32", "fp32", "bf16"};
+  static const char* op[] = {"sum", "max", "avg"};
+  static const char* coll[] = {"allreduce", "reduce_scatter", "all_gather"};
+  static const char* algo[] = {"direct", "ring", "rh_rd", "rd", "binomial", "generalized", "generalized_xor", "ahc",
+                               "chain"};
+  const Schedule& s = *pl.s;
+  const Spec& sp = s.spec;
+  std::ostringstream o;
+  o << "ar: plan P=" << sp.P << " n=" << sp.n << " batch=" << sp.batch << ' ' << dt[sp.dtype] << ' ' << op[sp.op]
+    << ' ' << algo[sp.algo] << " knob=" << sp.knob << " steps=" << sp.steps << ' ' << coll[sp.coll];
+  if (!sp.groups.empty()) {
+    o << " groups=";
+    for (size_t i = 0; i < sp.groups.size(); ++i) o << (i ? "," : "") << sp.groups[i];
+  }
+  o << " exec=" << (pl.exec == E_LITERAL ? "literal" : "fused") << " device=" << pl.device << ": kernel "
+    << kernel_name(pl.kernel) << " (method steps " << s.nsteps << ", slots " << s.nslots << ", ranges "
+    << s.ranges.size() << ", most trees " << s.max_trees << ", stack " << s.max_need << ", most leaves "
+    << s.max_leaves << ", program words " << s.prog.size() << ")";
+  if (pl.kernel == K_LITERAL) o << "; " << s.nsteps << " step launches" << (s.finalize_ops ? " + 1 finalize" : "");
+  if (!pl.fallback.empty()) o << "; literal fallback: " << pl.fallback;
+  std::fprintf(stderr, "%s\n", o.str().c_str());
+}
+
 // Repeated calls with one spec (a training loop's buckets, the unbatched
 // small-message case) skip building the cache key: the last plan found on
-// this thread is reused while the plan cache has not been cleared since.
-uint64_t g_plan_generation = 0;  // bumped whenever the plan cache is cleared (under g_mu)
+// this thread is reused while the plan cache has not been emptied since.
+uint64_t g_plan_generation = 0;  // bumped whenever the plan cache is emptied (under g_mu)
 struct LastPlan {
   Spec spec;
-  int exec = -1, device = -1;
+  int exec = -1, device = -2;
   uint64_t generation = 0;
   Plan* plan = nullptr;
 };
 thread_local LastPlan t_last;
 
+// Device -1 builds a host-only plan (kernel choice, sizes; no device tables).
 RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
   if (t_last.plan && t_last.generation == g_plan_generation && t_last.exec == exec && t_last.device == device &&
       same_spec(t_last.spec, spec)) {
@@ -601,15 +702,11 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
   int64_t slot = spec.n * spec.batch * int64_t(acc_bytes(spec.dtype));
   pl->slot_bytes = (slot + 255) / 256 * 256;
   pl->ws_bytes = size_t(s->nslots - 1) * size_t(spec.P) * size_t(pl->slot_bytes);
-  if (m.size() > 256) {
-    // every device whose plans are dropped may still run kernels that read them
-    std::vector<int> devs;
-    for (const auto& kv : m)
-      if (std::find(devs.begin(), devs.end(), kv.second->device) == devs.end()) devs.push_back(kv.second->device);
-    for (int d : devs) {
-      if (hipSetDevice(d) == hipSuccess) (void)hipDeviceSynchronize();
-    }
-    (void)hipSetDevice(device);
+  choose_kernel(*pl);
+  if (trace_enabled()) trace_plan(*pl);
+  if (m.size() >= kMaxLivePlans) {
+    // retire, never free: launches in flight and captured graphs keep their tables
+    for (auto& kv : m) retired_plans().push_back(std::move(kv.second));
     m.clear();
     ++g_plan_generation;
   }
@@ -639,13 +736,6 @@ std::shared_ptr<const Schedule> cached_schedule(const Spec& spec, std::string* e
   return schedule_locked(spec, err);
 }
 
-// Whether the fused replay can run a schedule: at most kMaxFusedTrees result
-// trees per range, and several trees only with a stack of depth <= 8.
-static bool fused_runs(const Schedule& s) {
-  const int D = s.max_need <= 2 ? 2 : s.max_need <= 4 ? 4 : s.max_need <= 8 ? 8 : 16;
-  return s.max_trees <= kMaxFusedTrees && !(s.max_trees > 1 && D > 8);
-}
-
 // The dispatch packet counts a grid's work-items in 32 bits, so one launch holds
 // at most kMaxLaunchBlocks workgroups of kThreads; longer work is split into
 // consecutive launches on the same stream. The limit can be lowered.
@@ -662,13 +752,12 @@ bool set_launch_blocks(int64_t blocks, int64_t* previous) {
 }
 
 RunResult workspace_bytes(const Spec& spec, int exec, size_t* bytes) {
-  std::string err;
-  std::shared_ptr<const Schedule> s = cached_schedule(spec, &err);
-  if (!s) { RunResult r; r.status = 1; r.message = err; return r; }
-  *bytes = 0;
-  if (exec != E_LITERAL && s->fused_ok && fused_runs(*s)) return RunResult{};  // the replay keeps partials in registers
-  int64_t slot = (spec.n * spec.batch * int64_t(acc_bytes(spec.dtype)) + 255) / 256 * 256;
-  *bytes = size_t(s->nslots - 1) * size_t(spec.P) * size_t(slot);
+  std::lock_guard<std::mutex> lk(g_mu);
+  Plan* pl = nullptr;
+  RunResult r = get_plan(spec, exec == E_LITERAL ? E_LITERAL : E_FUSED, -1, &pl);
+  if (r.status) return r;
+  // the replay keeps partials in registers; the literal steps need the slots
+  *bytes = pl->kernel == K_LITERAL ? pl->ws_bytes : 0;
   return RunResult{};
 }
 
@@ -677,27 +766,70 @@ RunResult kernel_of(const Spec& spec, int exec, int* kernel) {
   if (spec.P <= 1 || spec.n == 0) return RunResult{};
   if (exec == E_LITERAL) { *kernel = K_LITERAL; return RunResult{}; }
   if (exec == E_FUSED && spec.algo == A_DIRECT && spec.coll == C_ALLREDUCE) { *kernel = K_DIRECT; return RunResult{}; }
-  std::string err;
-  std::shared_ptr<const Schedule> s = cached_schedule(spec, &err);
-  if (!s) { RunResult r; r.status = 1; r.message = err; return r; }
-  if (!s->fused_ok || !fused_runs(*s)) { *kernel = K_LITERAL; return RunResult{}; }
-  int nl = 0;
-  RankTab tab;
-  const int shape = fixed_shapes_enabled() ? fixed_shape(*s, &tab, &nl) : SH_NONE;
-  // the same order of choices as run_allreduce's launch
-  MultiTab mt;
-  std::vector<uint8_t> rt;
-  int ref = 0;
-  if (fixed_shapes_enabled() && (rows_table(*s, &rt, &ref) || rows_flat(*s, &rt)))
-    *kernel = rows_vec(*s) ? K_ROWS_VEC : K_ROWS;
-  else if (strided_items(*s)) *kernel = K_STRIDED;
-  else if (shape == SH_CHAIN) *kernel = K_FIXED_CHAIN;
-  else if (shape == SH_BALANCED) *kernel = K_FIXED_BALANCED;
-  else if (shape == SH_STACK) *kernel = K_FIXED_STACK;
-  else if (fixed_shapes_enabled() && multi_shape(*s, &mt)) *kernel = K_MULTI;
-  else if (s->max_trees > 1 && spec.P <= kMaxStagedRanks) *kernel = K_STAGED;
-  else *kernel = K_REPLAY;
+  std::lock_guard<std::mutex> lk(g_mu);
+  Plan* pl = nullptr;
+  RunResult r = get_plan(spec, E_FUSED, -1, &pl);  // the launch's own choice, on a host-only plan
+  if (r.status) return r;
+  *kernel = pl->kernel;
   return RunResult{};
+}
+
+CacheStats cache_stats() {
+  std::lock_guard<std::mutex> lk(g_mu);
+  CacheStats c;
+  for (const auto& kv : plan_cache()) {
+    ++c.live_plans;
+    c.plan_device_bytes += int64_t(kv.second->device_bytes);
+  }
+  for (const auto& p : retired_plans()) {
+    ++c.retired_plans;
+    c.plan_device_bytes += int64_t(p->device_bytes);
+  }
+  for (const auto& kv : ws_cache()) {
+    ++c.workspaces;
+    c.workspace_device_bytes += int64_t(kv.second.bytes);
+  }
+  for (const auto& w : retired_ws()) {
+    ++c.retired_workspaces;
+    c.workspace_device_bytes += int64_t(w.bytes);
+  }
+  return c;
+}
+
+RunResult release_cached() {
+  std::lock_guard<std::mutex> lk(g_mu);
+  int cur = -1;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  std::vector<int> devs;
+  auto note = [&](int d) {
+    if (d >= 0 && std::find(devs.begin(), devs.end(), d) == devs.end()) devs.push_back(d);
+  };
+  for (const auto& kv : plan_cache()) note(kv.second->device);
+  for (const auto& p : retired_plans()) note(p->device);
+  for (const auto& kv : ws_cache()) note(kv.first.first);
+  RunResult res;
+  // every launch that may read a table or workspace ends before it is freed
+  for (int d : devs) {
+    hipError_t e = hipSetDevice(d);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess && !res.status) res = hip_fail(e, "synchronizing before the release");
+  }
+  if (res.status) {
+    if (have_cur) (void)hipSetDevice(cur);
+    return res;
+  }
+  plan_cache().clear();
+  retired_plans().clear();
+  for (auto& kv : ws_cache())
+    if (kv.second.p) (void)hipFree(kv.second.p);
+  for (auto& w : retired_ws())
+    if (w.p) (void)hipFree(w.p);
+  ws_cache().clear();
+  retired_ws().clear();
+  sched_cache().clear();
+  ++g_plan_generation;
+  if (have_cur) (void)hipSetDevice(cur);
+  return res;
 }
 
 RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* workspace, size_t workspace_bytes,
@@ -739,20 +871,35 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
   int device = 0;
   hipError_t e = hipGetDevice(&device);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  // building device tables (first call of a schedule, size and alignment) or a
+  // workspace allocates and copies synchronously, which a stream capture cannot hold
+  auto capturing = [&]() {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
+  };
+  auto refuse_capture = [&](const char* what) {
+    RunResult r;
+    r.status = 2;  // AR_UNSUPPORTED
+    r.message = std::string(what) + " cannot be built while the stream is capturing: make one call with this "
+                "schedule, size and buffer alignment before the capture";
+    return r;
+  };
   void* ws = nullptr;
   {
     std::lock_guard<std::mutex> lk(g_mu);
     res = get_plan(spec, exec == E_LITERAL ? E_LITERAL : E_FUSED, device, &pl);
     if (res.status) return res;
-    if (pl->exec != E_LITERAL && (!pl->s->fused_ok || !fused_runs(*pl->s))) {
-      // no replay program, or more result trees per range than the replay
-      // keeps in registers: the step-by-step kernels compute the same bits
+    if (pl->kernel == K_LITERAL && pl->exec != E_LITERAL) {
+      // no replay holds the program: the step-by-step kernels compute the same bits
       res = get_plan(spec, E_LITERAL, device, &pl);
       if (res.status) return res;
     }
     const int mode = vec ? 0 : 1;
     if (!pl->built[mode]) {
+      if (capturing()) return refuse_capture("the call's device tables");
+      g_upload_bytes = &pl->device_bytes;
       res = build_items(*pl, vec);
+      g_upload_bytes = nullptr;
       if (res.status) return res;
     }
     if (pl->exec == E_LITERAL && pl->ws_bytes) {
@@ -764,17 +911,14 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
         }
         ws = workspace;
       } else {
-        Workspace& w = ws_cache()[device];
+        Workspace& w = ws_cache()[{device, reinterpret_cast<uintptr_t>(st)}];
         if (w.bytes < pl->ws_bytes) {
-          if (w.p) {
-            e = hipDeviceSynchronize();
-            if (e != hipSuccess) return hip_fail(e, "synchronizing before growing the workspace");
-            (void)hipFree(w.p);
-            w.p = nullptr;
-            w.bytes = 0;
-          }
-          e = hipMalloc(&w.p, pl->ws_bytes);
-          if (e != hipSuccess) { w.p = nullptr; return hip_fail(e, "allocating the literal workspace"); }
+          if (capturing()) return refuse_capture("the literal workspace");
+          void* p = nullptr;
+          e = hipMalloc(&p, pl->ws_bytes);
+          if (e != hipSuccess) return hip_fail(e, "allocating the literal workspace");
+          if (w.p) retired_ws().push_back(w);  // earlier launches on this stream may still use it
+          w.p = p;
           w.bytes = pl->ws_bytes;
         }
         ws = w.p;

@@ -32,7 +32,19 @@
  *    and reproducibility"). max uses the total order with -0 < +0; inputs must
  *    be NaN-free.
  *  - Threading: calls are thread-safe; calls on one stream run in order.
- *    Calls that overlap on different streams must not share buffers.
+ *    Calls that overlap on different streams must not share buffers. A call
+ *    that brings no workspace and runs the literal steps uses a workspace the
+ *    library keeps per (device, stream), so such calls on different streams
+ *    never share partial results.
+ *  - Device tables and HIP graphs: the first call of a given schedule, size
+ *    and buffer alignment on a device builds device tables (a synchronous
+ *    allocation and copy); literal calls without a workspace may also allocate
+ *    one. Neither can happen while the stream is being captured: such a call
+ *    returns AR_UNSUPPORTED and enqueues nothing, so make one call outside the
+ *    capture first. The library never frees a table or workspace that an
+ *    enqueued or captured call may use: tables and workspaces it replaces are
+ *    retired and kept until ar_release_cached(), so a captured graph stays
+ *    valid however many other calls follow.
  *  - Limits: 1 <= P <= 256 (AR_MAX_RANKS).
  */
 #ifndef AR_MI355X_H
@@ -238,9 +250,30 @@ typedef enum {
   AR_KERNEL_FIXED_STACK = 8,
   AR_KERNEL_MULTI = 9,
   AR_KERNEL_ROWS = 10,
-  AR_KERNEL_ROWS_VEC = 11
+  AR_KERNEL_ROWS_VEC = 11,
+  AR_KERNEL_DAG = 12
 } ar_kernel;
 ar_status ar_kernel_of(const ar_call* call, int32_t* kernel);
+
+/* Device memory the library holds between calls: plans (the device tables of one
+ * schedule, size and alignment per device) and literal workspaces (one per device and
+ * stream, for calls that bring none). Live ones serve new calls; retired ones were
+ * replaced (the plan cache holds at most 256 plans; a workspace that had to grow) and
+ * are kept because enqueued or captured calls may still use them. */
+typedef struct ar_cache_stats {
+  int64_t live_plans, retired_plans;
+  int64_t workspaces, retired_workspaces;
+  int64_t plan_device_bytes;       /* tables of live and retired plans */
+  int64_t workspace_device_bytes;  /* live and retired workspaces */
+} ar_cache_stats;
+ar_status ar_cache_stats_get(ar_cache_stats* out);
+/* Free every plan, workspace and cached schedule the library holds (live and retired).
+ * It first synchronizes every device they belong to, so launches already enqueued end
+ * before their memory is freed. The caller must ensure that no call runs concurrently
+ * on another thread and that no HIP graph captured before this call, containing calls
+ * of this library, is launched afterwards: its kernels would read freed tables.
+ * Returns AR_HIP_ERROR (nothing freed) if a synchronization fails. */
+ar_status ar_release_cached(void);
 
 /* Largest grid, in 256-thread workgroups, of one kernel launch. A call whose work needs
  * more (misaligned buffers of 2^32 elements or more, or about 2^35 aligned ones) runs as

@@ -1,0 +1,95 @@
+"""Host side of the executor, without a GPU: the kernel each call's plan picks
+(AR_TRACE names it, and any fall back to the literal steps), and the plan cache's
+retirement, which keeps every plan a launch or a captured graph may still use."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import allreduce_schedule_algorithms_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def run_py(code: str, env_extra=None):
+    env = dict(os.environ)
+    env.update(env_extra or {})
+    env["PYTHONPATH"] = ROOT + os.pathsep + env.get("PYTHONPATH", "")
+    return subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=300)
+
+
+TRACE_CASES = [  # (P, n, dtype, algo, knob, exec)
+    (8, 1 << 20, "fp32", "rh_rd", 0, "fused"),
+    (7, 1 << 24, "fp32", "generalized", 3, "fused"),
+    (24, 106, "fp32", "generalized", 5, "fused"),
+    (127, 106, "fp32", "generalized", 4, "fused"),
+    (127, 4099, "bf16", "generalized", 7, "fused"),
+    (5, 4096, "int32", "ring", 0, "literal"),
+]
+
+
+def test_trace_names_each_plans_kernel():
+    code = (
+        "import json, allreduce_schedule_algorithms_amd as A\n"
+        f"cases = {TRACE_CASES!r}\n"
+        "out = []\n"
+        "for P, n, dt, algo, knob, ex in cases:\n"
+        "    out.append(A.ar_kernel_of(A.make_call(P, n, dt, 'sum', algo, knob, ex)).name)\n"
+        "print(json.dumps(out))\n")
+    r = run_py(code, {"AR_TRACE": "1"})
+    assert r.returncode == 0, r.stderr
+    kinds = json.loads(r.stdout.strip().splitlines()[-1])
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("ar: plan ")]
+    fused = [c for c in TRACE_CASES if c[5] != "literal"]
+    assert len(lines) == len(fused)  # one line per new plan; literal calls need no plan to answer
+    names = {"AR_KERNEL_FIXED_BALANCED": "k_fused_fixed (balanced)", "AR_KERNEL_MULTI": "k_fused_multi",
+             "AR_KERNEL_ROWS_VEC": "k_fused_rows_vec", "AR_KERNEL_ROWS": "k_fused_rows",
+             "AR_KERNEL_DAG": "k_fused_dag", "AR_KERNEL_LITERAL": "k_literal", "AR_KERNEL_REPLAY": "k_fused",
+             "AR_KERNEL_STAGED": "k_fused_staged", "AR_KERNEL_STRIDED": "k_fused_strided"}
+    for (P, n, dt, algo, knob, ex), kind, ln in zip(fused, kinds, lines):
+        assert f"P={P} n={n} " in ln and f" {algo} knob={knob} " in ln, ln
+        assert f"kernel {names[kind]} " in ln, (kind, ln)
+        # a fused call that runs the literal steps says so, and why
+        assert ("literal fallback:" in ln) == (kind == "AR_KERNEL_LITERAL"), ln
+    assert kinds[-1] == "AR_KERNEL_LITERAL"
+
+
+def test_no_trace_without_the_variable():
+    r = run_py("import allreduce_schedule_algorithms_amd as A\n"
+               "A.ar_kernel_of(A.make_call(8, 4096, 'fp32', 'sum', 'ring'))\n", {"AR_TRACE": ""})
+    assert r.returncode == 0, r.stderr
+    assert "ar: plan" not in r.stderr
+
+
+def test_plans_are_retired_not_freed():
+    # 300 distinct plans: the cache keeps at most 256 live, and the ones it
+    # replaces stay held (retired) until ar_release_cached
+    code = (
+        "import json, allreduce_schedule_algorithms_amd as A\n"
+        "for i in range(300):\n"
+        "    A.ar_kernel_of(A.make_call(7, 1000 + i, 'fp32', 'sum', 'generalized', 1))\n"
+        "a = A.ar_cache_stats_get()\n"
+        "A.ar_release_cached()\n"
+        "b = A.ar_cache_stats_get()\n"
+        "print(json.dumps([a, b]))\n")
+    r = run_py(code)
+    assert r.returncode == 0, r.stderr
+    a, b = json.loads(r.stdout.strip().splitlines()[-1])
+    assert a["live_plans"] + a["retired_plans"] == 300
+    assert 0 < a["live_plans"] <= 256 and a["retired_plans"] >= 44
+    assert all(v == 0 for v in b.values()), b
+
+
+def test_kernel_of_and_workspace_agree_with_the_plan():
+    # a call whose plan runs a replay kernel needs no workspace; literal calls need the slots
+    for P, algo, knob in ((7, "generalized", 2), (8, "rh_rd", 0), (12, "binomial", 0)):
+        fused = A.make_call(P, 4099, "fp32", "sum", algo, knob, "fused")
+        lit = A.make_call(P, 4099, "fp32", "sum", algo, knob, "literal")
+        k = A.ar_kernel_of(fused)
+        assert k != A.Kernel.AR_KERNEL_LITERAL
+        assert A.ar_workspace_bytes(fused) == 0
+        sched = A.ar_schedule_build(lit).info()
+        slot = -(-4099 * 4 // 256) * 256
+        assert A.ar_workspace_bytes(lit) == (sched.slots - 1) * P * slot

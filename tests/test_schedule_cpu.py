@@ -421,3 +421,16 @@ def test_launch_block_limit_setter():
 def test_status_strings():
     assert A.ar_status_string(0) == "AR_OK"
     assert A.ar_status_string(3) == "AR_WORKSPACE_TOO_SMALL"
+
+
+def test_probe_library_exports_every_declared_symbol():
+    # the measurement library (memory-traffic ceilings) that bench.py loads
+    from allreduce_schedule_algorithms_amd import probe
+    with open(os.path.join(ROOT, "include", "ar_probe.h")) as f:
+        names = sorted(set(re.findall(r"^\s*[a-z_0-9]+\s+(ar_[a-z_]+)\s*\(", f.read(), re.M)))
+    assert names == ["ar_probe_last_hip_error", "ar_probe_stream"]
+    out = subprocess.run(["nm", "-D", "--defined-only", probe.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (ar_[a-z_]+)\b", out))
+    for nm in names:
+        assert nm in exported, nm
+        assert nm in probe.SIGNATURES
