@@ -162,6 +162,9 @@ SIGNATURES = {
     "ar_schedule_fused_export": (C.c_int, [C.c_void_p, C.POINTER(C.c_int64), C.POINTER(C.c_int64),
                                            C.POINTER(C.c_int32), C.c_size_t, C.POINTER(C.c_int32), C.c_size_t,
                                            C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
+    "ar_schedule_dag_export": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.c_size_t,
+                                         C.POINTER(C.c_uint8), C.c_size_t, C.POINTER(C.c_int32), C.c_size_t,
+                                         C.POINTER(C.c_size_t), C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
     "ar_schedule_free": (None, [C.c_void_p]),
     "ar_table_check": (C.c_int, [C.c_int32, C.c_int64, C.c_int32, C.POINTER(ar_oprec), C.c_size_t,
                                  C.POINTER(C.c_int32)]),
@@ -412,6 +415,21 @@ class Schedule:
         _check(lib.ar_schedule_fused_export(self._h, starts, lens, offs, nr.value, words, nw.value,
                                             C.byref(nr), C.byref(nw)))
         return list(starts[: nr.value]), list(lens[: nr.value]), list(offs[: nr.value]), list(words[: nw.value])
+
+    def dag_export(self):
+        """(shared, offsets per range, maps as a (ranges, P) array or None, program words)."""
+        import numpy as np
+        sh = C.c_int32(0)
+        nr, nm, nw = C.c_size_t(0), C.c_size_t(0), C.c_size_t(0)
+        _check(lib.ar_schedule_dag_export(self._h, C.byref(sh), None, 0, None, 0, None, 0, C.byref(nr),
+                                          C.byref(nm), C.byref(nw)))
+        offs = (C.c_int32 * max(nr.value, 1))()
+        maps = (C.c_uint8 * max(nm.value, 1))()
+        words = (C.c_int32 * max(nw.value, 1))()
+        _check(lib.ar_schedule_dag_export(self._h, C.byref(sh), offs, nr.value, maps, nm.value, words, nw.value,
+                                          C.byref(nr), C.byref(nm), C.byref(nw)))
+        m = np.frombuffer(bytes(maps[: nm.value]), dtype=np.uint8).reshape(nr.value, -1) if nm.value else None
+        return bool(sh.value), list(offs[: nr.value]), m, list(words[: nw.value])
 
     def cost(self, alpha=0.0, beta=0.0, gamma=0.0) -> ar_cost:
         out = ar_cost()

@@ -298,6 +298,25 @@ ar_status ar_schedule_build(const ar_call* call, ar_schedule** out) {
   return AR_OK;
 }
 
+ar_status ar_schedule_dag_export(const ar_schedule* sh, int32_t* shared, int32_t* offsets, size_t range_cap,
+                                 uint8_t* maps, size_t map_cap, int32_t* words, size_t word_cap, size_t* nranges,
+                                 size_t* nmaps, size_t* nwords) {
+  if (!sh) return fail(AR_INVALID_ARGUMENT, "NULL schedule");
+  const ar::Schedule& s = *reinterpret_cast<const ar::Schedule*>(sh);
+  if (!s.fused_ok) return fail(AR_UNSUPPORTED, "no fused program: " + s.fused_error);
+  ar::DagPlan d;
+  std::string err;
+  if (!ar::dag_plan(s, &d, &err)) return fail(AR_UNSUPPORTED, err);
+  if (shared) *shared = d.shared ? 1 : 0;
+  if (nranges) *nranges = d.offsets.size();
+  if (nmaps) *nmaps = d.maps.size();
+  if (nwords) *nwords = d.words.size();
+  if (offsets) std::memcpy(offsets, d.offsets.data(), std::min(range_cap, d.offsets.size()) * sizeof(int32_t));
+  if (maps && !d.maps.empty()) std::memcpy(maps, d.maps.data(), std::min(map_cap, d.maps.size()));
+  if (words) std::memcpy(words, d.words.data(), std::min(word_cap, d.words.size()) * sizeof(int32_t));
+  return AR_OK;
+}
+
 void ar_schedule_free(ar_schedule* s) { delete reinterpret_cast<ar::Schedule*>(s); }
 
 ar_status ar_schedule_info_get(const ar_schedule* sh, ar_schedule_info* info) {

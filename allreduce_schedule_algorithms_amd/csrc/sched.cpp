@@ -962,6 +962,216 @@ static bool plan_fused(Schedule& s, std::string* err) {
 }
 
 // ----------------------------------------------------------------------------
+// DAG form of a range's program
+// ----------------------------------------------------------------------------
+std::vector<int32_t> DagProgram::words() const {
+  std::vector<int32_t> w = {S, int32_t(leaves.size()), int32_t(level_start.size()) - 1, int32_t(instr.size()),
+                            int32_t(outs.size())};
+  w.insert(w.end(), leaves.begin(), leaves.end());
+  w.insert(w.end(), level_start.begin(), level_start.end());
+  for (uint32_t i : instr) w.push_back(int32_t(i));
+  w.insert(w.end(), outs.begin(), outs.end());
+  return w;
+}
+
+bool compile_dag(const int32_t* w, int P, DagProgram* out, std::string* err) {
+  // nodes: leaves first (by first appearance), then combinations in creation order
+  struct Node { int a, b, level; };
+  std::vector<Node> nodes;
+  std::vector<int> leaf_node(size_t(P), -1);
+  std::unordered_map<uint64_t, int> ids;
+  std::vector<std::pair<int, int>> roots;  // (node, output rank)
+  out->leaves.clear();
+  const int ntrees = w[0];
+  const int32_t* t = w + 1;
+  // leaf nodes get their ids in a first pass, so leaf k is node k and slot k
+  for (int q = 0, off = 0; q < ntrees; ++q) {
+    const int nl = t[off], no = t[off + 1];
+    for (int k = 0; k < nl; ++k) {
+      const int r = t[off + 2 + k];
+      if (r < 0 || r >= P) { *err = "leaf rank out of range"; return false; }
+      if (leaf_node[size_t(r)] < 0) {
+        leaf_node[size_t(r)] = int(nodes.size());
+        nodes.push_back({-1, -1, 0});
+        out->leaves.push_back(r);
+      }
+    }
+    off += 2 + 2 * nl + no;
+  }
+  const int nleaf = int(nodes.size());
+  for (int q = 0; q < ntrees; ++q) {
+    const int nl = t[0], no = t[1];
+    const int32_t* leaf = t + 2;
+    const int32_t* nc = leaf + nl;
+    const int32_t* os = nc + nl;
+    std::vector<int> st;
+    for (int k = 0; k < nl; ++k) {
+      st.push_back(leaf_node[size_t(leaf[k])]);
+      for (int c = 0; c < nc[k]; ++c) {
+        if (st.size() < 2) { *err = "malformed postfix program"; return false; }
+        const int b = st.back();
+        st.pop_back();
+        const int a = st.back();
+        st.pop_back();
+        const uint64_t key = (uint64_t(uint32_t(std::min(a, b))) << 32) | uint32_t(std::max(a, b));
+        auto it = ids.find(key);
+        int id;
+        if (it != ids.end()) {
+          id = it->second;
+        } else {
+          id = int(nodes.size());
+          nodes.push_back({a, b, 1 + std::max(nodes[size_t(a)].level, nodes[size_t(b)].level)});
+          ids.emplace(key, id);
+        }
+        st.push_back(id);
+      }
+    }
+    if (st.size() != 1) { *err = "malformed postfix program"; return false; }
+    for (int j = 0; j < no; ++j) roots.push_back({st[0], os[j]});
+    t = os + no;
+  }
+  // last level in which each node is read; outputs are read after every level
+  int nlev = 0;
+  for (const Node& nd : nodes) nlev = std::max(nlev, nd.level);
+  std::vector<int> last(nodes.size(), 0);
+  for (size_t i = size_t(nleaf); i < nodes.size(); ++i) {
+    last[size_t(nodes[i].a)] = std::max(last[size_t(nodes[i].a)], nodes[i].level);
+    last[size_t(nodes[i].b)] = std::max(last[size_t(nodes[i].b)], nodes[i].level);
+  }
+  for (auto& rt : roots) last[size_t(rt.first)] = nlev + 1;
+  // by level, creation order within a level
+  std::vector<std::vector<int>> by_level(size_t(nlev) + 1);
+  for (size_t i = size_t(nleaf); i < nodes.size(); ++i) by_level[size_t(nodes[i].level)].push_back(int(i));
+  // values whose last read is in level l (their slot is free from level l + 1),
+  // and how many combinations of a level read each value
+  std::vector<std::vector<int>> by_last(size_t(nlev) + 2);
+  for (size_t i = 0; i < nodes.size(); ++i)
+    if (last[i] <= nlev) by_last[size_t(last[i])].push_back(int(i));
+  std::vector<int> readers(nodes.size(), 0);
+  std::vector<char> taken(nodes.size(), 0);  // slot handed on to the combination that read it last
+  std::vector<int> slot(nodes.size(), -1);
+  std::set<int> pool;
+  int S = nleaf;
+  for (int i = 0; i < nleaf; ++i) slot[size_t(i)] = i;
+  out->level_start.assign(1, 0);
+  out->instr.clear();
+  for (int l = 1; l <= nlev; ++l) {
+    for (int id : by_last[size_t(l - 1)])
+      if (!taken[size_t(id)]) pool.insert(slot[size_t(id)]);
+    for (int id : by_level[size_t(l)]) {
+      ++readers[size_t(nodes[size_t(id)].a)];
+      ++readers[size_t(nodes[size_t(id)].b)];
+    }
+    for (int id : by_level[size_t(l)]) {
+      const Node& nd = nodes[size_t(id)];
+      int sl = -1;
+      // an operand read for the last time, by this combination alone, passes its
+      // slot on: the same lane reads both operands before it writes
+      for (int op : {nd.a, nd.b}) {
+        if (sl < 0 && last[size_t(op)] == l && readers[size_t(op)] == 1 && !taken[size_t(op)]) {
+          taken[size_t(op)] = 1;
+          sl = slot[size_t(op)];
+        }
+      }
+      if (sl < 0) {
+        if (!pool.empty()) {
+          sl = *pool.begin();
+          pool.erase(pool.begin());
+        } else {
+          sl = S++;
+        }
+      }
+      slot[size_t(id)] = sl;
+      out->instr.push_back(uint32_t(sl) | (uint32_t(slot[size_t(nd.a)]) << 10) | (uint32_t(slot[size_t(nd.b)]) << 20));
+    }
+    for (int id : by_level[size_t(l)]) {
+      readers[size_t(nodes[size_t(id)].a)] = 0;
+      readers[size_t(nodes[size_t(id)].b)] = 0;
+    }
+    out->level_start.push_back(int32_t(out->instr.size()));
+  }
+  if (S > kDagMaxSlots) { *err = "more than 1024 live values"; return false; }
+  out->S = S;
+  out->outs.clear();
+  for (auto& rt : roots) out->outs.push_back(int32_t((slot[size_t(rt.first)] << 16) | rt.second));
+  return true;
+}
+
+bool dag_renaming(const DagProgram& a, const DagProgram& b, int P, std::vector<int>* map) {
+  if (a.S != b.S || a.leaves.size() != b.leaves.size() || a.level_start != b.level_start || a.instr != b.instr ||
+      a.outs.size() != b.outs.size())
+    return false;
+  map->assign(size_t(P), -1);
+  std::vector<int> inv(size_t(P), -1);
+  auto bind = [&](int x, int y) {
+    int& m = (*map)[size_t(x)];
+    if (m < 0 && inv[size_t(y)] < 0) {
+      m = y;
+      inv[size_t(y)] = x;
+      return true;
+    }
+    return m == y;
+  };
+  for (size_t k = 0; k < a.leaves.size(); ++k)
+    if (!bind(a.leaves[k], b.leaves[k])) return false;
+  for (size_t k = 0; k < a.outs.size(); ++k) {
+    if ((a.outs[k] >> 16) != (b.outs[k] >> 16)) return false;
+    if (!bind(a.outs[k] & 0xffff, b.outs[k] & 0xffff)) return false;
+  }
+  // complete the permutation with the ranks neither program names
+  int free_y = 0;
+  for (int x = 0; x < P; ++x) {
+    if ((*map)[size_t(x)] >= 0) continue;
+    if (inv[size_t(x)] < 0) {
+      (*map)[size_t(x)] = x;
+      inv[size_t(x)] = x;
+      continue;
+    }
+    while (inv[size_t(free_y)] >= 0) ++free_y;
+    (*map)[size_t(x)] = free_y;
+    inv[size_t(free_y)] = x;
+  }
+  return true;
+}
+
+bool dag_plan(const Schedule& s, DagPlan* out, std::string* err) {
+  const int P = s.spec.P;
+  const size_t R = s.ranges.size();
+  std::vector<DagProgram> progs(R);
+  *out = DagPlan{};
+  for (size_t r = 0; r < R; ++r) {
+    if (!compile_dag(s.prog.data() + s.ranges[r].prog, P, &progs[r], err)) return false;
+    out->S = std::max(out->S, progs[r].S);
+    out->levels = std::max(out->levels, int(progs[r].level_start.size()) - 1);
+    out->instr = std::max<int64_t>(out->instr, int64_t(progs[r].instr.size()));
+  }
+  out->offsets.assign(R, 0);
+  if (R == 0) return true;
+  // one program for every range when they differ only by a renaming of ranks
+  out->shared = true;
+  out->maps.assign(R * size_t(P), 0);
+  std::vector<int> map;
+  for (size_t r = 0; r < R && out->shared; ++r) {
+    if (!dag_renaming(progs[0], progs[r], P, &map)) {
+      out->shared = false;
+      break;
+    }
+    for (int x = 0; x < P; ++x) out->maps[r * size_t(P) + size_t(x)] = uint8_t(map[size_t(x)]);
+  }
+  if (out->shared) {
+    out->words = progs[0].words();
+    return true;
+  }
+  out->maps.clear();
+  for (size_t r = 0; r < R; ++r) {
+    out->offsets[r] = int32_t(out->words.size());
+    const std::vector<int32_t> w = progs[r].words();
+    out->words.insert(out->words.end(), w.begin(), w.end());
+  }
+  return true;
+}
+
+// ----------------------------------------------------------------------------
 // build
 // ----------------------------------------------------------------------------
 // Radices of the generalized algorithm's group: the caller's factors, else

@@ -115,6 +115,50 @@ struct Schedule {
   int max_need = 0, max_trees = 0, max_leaves = 0;
 };
 
+// DAG form of one range's fused program (its words in Schedule::prog). The
+// range's result trees share sub-trees (the generalized algorithm's shifted
+// schedules combine the same partial sums), so every distinct combination --
+// a node identified by its unordered pair of operands, itself hash-consed --
+// is evaluated once. Nodes are grouped in levels (a node's level is one more
+// than its deeper operand's); the combinations of one level are independent.
+// Values live in numbered slots: leaf k (k-th distinct leaf rank in postfix
+// order) in slot k, and each node in a slot freed by a value whose last use
+// lies in an earlier level, so no slot is read and written within one level.
+// A combination keeps the operand order in which the postfix program first
+// builds it. Outputs are read after the last level. Programs of ranges whose
+// trees are equal up to a renaming of ranks differ only in leaf and output ranks.
+struct DagProgram {
+  int32_t S = 0;                     // slots
+  std::vector<int32_t> leaves;       // rank of the leaf in slot k
+  std::vector<int32_t> level_start;  // levels + 1 offsets into instr
+  std::vector<uint32_t> instr;       // dst | a << 10 | b << 20: slot dst = slot a (+) slot b
+  std::vector<int32_t> outs;         // slot << 16 | rank: rank's result is slot's value
+  // serialized: S, leaves, levels, instructions, outputs, then the arrays
+  std::vector<int32_t> words() const;
+};
+constexpr int kDagMaxSlots = 1024;
+bool compile_dag(const int32_t* range_words, int P, DagProgram* out, std::string* err);
+// Whether b equals a with every leaf and output rank renamed: fills map with
+// a's rank -> b's rank (ranks a does not use map to themselves if free, else
+// to an unused rank) so that map is a permutation.
+bool dag_renaming(const DagProgram& a, const DagProgram& b, int P, std::vector<int>* map);
+
+// DAG programs of a whole fused program. Shared: every range's program is the
+// reference range's with ranks renamed, so one program serves all ranges and
+// maps holds, per range, P bytes (reference rank -> the range's rank); otherwise
+// one program per range, at offsets into words.
+struct DagPlan {
+  bool shared = false;
+  int ref = 0;                   // shared: the reference range
+  std::vector<int32_t> words;    // serialized programs (DagProgram::words)
+  std::vector<int32_t> offsets;  // per range: its program's offset in words (shared: 0)
+  std::vector<uint8_t> maps;     // shared: ranges x P renaming rows
+  int S = 0;                     // most slots of any program
+  int levels = 0;                // most levels
+  int64_t instr = 0;             // combinations per element, most of any range
+};
+bool dag_plan(const Schedule& s, DagPlan* out, std::string* err);
+
 // Generate + realize + plan. Returns nullptr and sets *err on invalid input.
 Schedule* build_schedule(const Spec& spec, std::string* err);
 

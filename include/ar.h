@@ -331,6 +331,21 @@ ar_status ar_schedule_export(const ar_schedule* s, ar_oprec* ops, size_t cap, si
 ar_status ar_schedule_fused_export(const ar_schedule* s, int64_t* starts, int64_t* lens,
                                    int32_t* offsets, size_t range_cap, int32_t* words,
                                    size_t word_cap, size_t* nranges, size_t* nwords);
+/* DAG form of the fused program, the one AR_KERNEL_DAG runs. Every distinct combination of a
+ * range's result trees (a node identified by its unordered operands) is evaluated once, grouped
+ * in levels of independent combinations, with values in numbered slots; a slot is reused only in
+ * a level after its value's last read. Words of one program:
+ *   S, nleaf, nlevel, ninstr, nout, then nleaf leaf ranks (leaf k in slot k), nlevel + 1
+ *   instruction offsets (level l runs instructions [lv[l], lv[l + 1])), ninstr instructions
+ *   (dst | a << 10 | b << 20: slot dst = slot a (+) slot b), nout outputs (slot << 16 | rank:
+ *   the rank's result is the slot's value after the last level).
+ * *shared = 1: one program serves every range; maps holds P bytes per range mapping the
+ * program's ranks to the range's (offsets are all 0). *shared = 0: range r's program starts at
+ * words[offsets[r]]. Ranges are those of ar_schedule_fused_export. Any pointer may be NULL to
+ * query sizes (*nmaps = bytes of maps). */
+ar_status ar_schedule_dag_export(const ar_schedule* s, int32_t* shared, int32_t* offsets, size_t range_cap,
+                                 uint8_t* maps, size_t map_cap, int32_t* words, size_t word_cap, size_t* nranges,
+                                 size_t* nmaps, size_t* nwords);
 void ar_schedule_free(ar_schedule* s);
 
 /* Validate any table (for example a modified export): snapshot hazards inside a step,

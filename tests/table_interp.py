@@ -134,3 +134,61 @@ def run_fused(x, starts, lens, offs, words, dtype, op, n, batch=1):
                     out[r][sl] = _from_acc(res, dtype)
                 w += 2 + 2 * nl + no
     return out
+
+
+def dag_parse(words, off=0):
+    """One serialized DAG program at words[off:]: (S, leaves, level starts,
+    instructions as (dst, a, b), outputs as (slot, rank))."""
+    S, nleaf, nlev, ninstr, nout = words[off: off + 5]
+    p = off + 5
+    leaves = list(words[p: p + nleaf])
+    p += nleaf
+    lv = list(words[p: p + nlev + 1])
+    p += nlev + 1
+    ins = [(w & 1023, (w >> 10) & 1023, (w >> 20) & 1023) for w in words[p: p + ninstr]]
+    p += ninstr
+    outs = [(w >> 16, w & 0xFFFF) for w in words[p: p + nout]]
+    return S, leaves, lv, ins, outs
+
+
+def dag_hazards(prog):
+    """Every level's combinations must be independent when lanes of different
+    threads run them in any order: distinct destination slots, and no slot one
+    combination writes is read by another combination of the same level."""
+    S, leaves, lv, ins, outs = prog
+    for l in range(len(lv) - 1):
+        level = ins[lv[l]: lv[l + 1]]
+        dsts = [d for d, _, _ in level]
+        assert len(set(dsts)) == len(dsts), ("duplicate destination", l)
+        for i, (d, _, _) in enumerate(level):
+            for j, (_, a, b) in enumerate(level):
+                assert j == i or d not in (a, b), ("read and written in one level", l, d)
+        assert all(max(d, a, b) < S for d, a, b in level)
+    assert all(s < S for s, _ in outs)
+
+
+def run_dag(x, starts, lens, shared, offs, maps, words, dtype, op, n, batch=1):
+    """Evaluate exported DAG programs on host arrays: per range its own program,
+    or (shared) the one program with leaf and output ranks renamed by the
+    range's row of maps. Levels run their combinations in reverse order, so a
+    hazard that dag_hazards misses would show as wrong values."""
+    P = x.shape[0]
+    out = np.array(x)
+    acc = [_to_acc(x[p], dtype) for p in range(P)]
+    for r, (st, ln) in enumerate(zip(starts, lens)):
+        prog = dag_parse(words, 0 if shared else offs[r])
+        dag_hazards(prog)
+        S, leaves, lv, ins, outs = prog
+        ren = (lambda q: int(maps[r][q])) if shared else (lambda q: q)
+        for b in range(batch):
+            sl = slice(b * n + st, b * n + st + ln)
+            vals = [None] * S
+            for k, q in enumerate(leaves):
+                vals[k] = acc[ren(q)][sl].copy()
+            for l in range(len(lv) - 1):
+                for d, a, bb in reversed(ins[lv[l]: lv[l + 1]]):
+                    vals[d] = _combine(vals[a], vals[bb], dtype, op)
+            for s, q in outs:
+                res = vals[s] / np.float32(P) if op == "avg" else vals[s]
+                out[ren(q)][sl] = _from_acc(res, dtype)
+    return out
