@@ -86,6 +86,7 @@ class Exec(enum.IntEnum):
     AR_EXEC_FUSED = 0
     AR_EXEC_LITERAL = 1
     AR_EXEC_REPLAY = 2
+    AR_EXEC_DAG = 3
 
 
 DTYPES = {"int32": Dtype.AR_INT32, "fp32": Dtype.AR_FP32, "bf16": Dtype.AR_BF16}
@@ -98,7 +99,8 @@ ALGOS = {"direct": Algo.AR_DIRECT, "ring": Algo.AR_RING, "rh_rd": Algo.AR_RH_RD,
          "auto": Algo.AR_AUTO}
 ALGO_NAMES = {int(v): k for k, v in ALGOS.items()}
 COST_FORMS = {"busiest": CostForm.AR_COST_BUSIEST_RANK, "all_ranks": CostForm.AR_COST_ALL_RANKS}
-EXECS = {"fused": Exec.AR_EXEC_FUSED, "literal": Exec.AR_EXEC_LITERAL, "replay": Exec.AR_EXEC_REPLAY}
+EXECS = {"fused": Exec.AR_EXEC_FUSED, "literal": Exec.AR_EXEC_LITERAL, "replay": Exec.AR_EXEC_REPLAY,
+         "dag": Exec.AR_EXEC_DAG}
 
 
 class ar_call(C.Structure):

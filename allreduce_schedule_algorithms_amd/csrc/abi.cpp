@@ -85,7 +85,7 @@ bool to_spec(const ar_call* c, ar::Spec* s, std::string* err) {
     probe.algo = ar::A_AHC;
     if (!ar::validate_spec(probe, err)) return false;
   }
-  if (c->exec < AR_EXEC_FUSED || c->exec > AR_EXEC_REPLAY) { *err = "unknown exec mode"; return false; }
+  if (c->exec < AR_EXEC_FUSED || c->exec > AR_EXEC_DAG) { *err = "unknown exec mode"; return false; }
   if (c->collective < AR_ALLREDUCE || c->collective > AR_ALL_GATHER) { *err = "unknown collective"; return false; }
   s->coll = c->collective;
   if (s->coll == AR_ALL_GATHER) s->op = ar::O_SUM;  // copies only: the op plays no part
@@ -248,7 +248,7 @@ ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes) {
   if ((call->exec == AR_EXEC_FUSED && spec.algo == AR_DIRECT && spec.coll == AR_ALLREDUCE) || spec.P <= 1 ||
       spec.n == 0)
     return AR_OK;
-  ar::RunResult r = ar::workspace_bytes(spec, call->exec == AR_EXEC_LITERAL ? 1 : 0, bytes);
+  ar::RunResult r = ar::workspace_bytes(spec, call->exec, bytes);
   if (r.status) return fail(ar_status(r.status), r.message);
   return AR_OK;
 }

@@ -10,7 +10,7 @@
 
 namespace ar {
 
-enum Exec : int32_t { E_FUSED = 0, E_LITERAL = 1, E_REPLAY = 2 };
+enum Exec : int32_t { E_FUSED = 0, E_LITERAL = 1, E_REPLAY = 2, E_DAG = 3 };
 
 struct RunResult {
   int status = 0;     // ar_status value

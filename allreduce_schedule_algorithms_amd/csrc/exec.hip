@@ -143,6 +143,13 @@ struct Plan {
   int md = 2;             // k_fused_fixed: vectors per thread (items of kThreads * md vectors)
   int64_t slot_bytes = 0;
   size_t ws_bytes = 0;
+  bool dag = false;         // fused: k_fused_dag
+  bool dag_shared = false;  // one program for every range, ranks renamed per lane
+  DagPlan dp;               // its programs
+  std::vector<uint8_t> dag_tab;  // shared: range of each offset, then the renaming rows
+  DevBuf dtab;
+  size_t dag_lds[2] = {0, 0};    // per alignment mode: dynamic LDS bytes
+  size_t lds_limit = 0;
   int kernel = K_NONE;     // the kernel family the plan launches (ar_kernel)
   std::string fallback;   // why a fused call runs the literal steps (empty otherwise)
   size_t device_bytes = 0;  // device memory the plan's tables hold
@@ -399,6 +406,71 @@ bool rows_flat(const Schedule& s, std::vector<uint8_t>* t) {
   return true;
 }
 
+// LDS one workgroup may allocate on a device (gfx950: 160 KB); host-only plans
+// assume the gfx950 figure.
+size_t lds_limit(int device) {
+  static std::map<int, size_t> m;
+  auto it = m.find(device);
+  if (it != m.end()) return it->second;
+  int v = 0;
+  size_t lim = 160 * 1024;
+  if (device >= 0 && hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, device) == hipSuccess && v > 0)
+    lim = size_t(v);
+  m[device] = lim;
+  return lim;
+}
+
+bool dag_forced() {
+  static const bool on = [] {
+    const char* v = std::getenv("AR_DAG");  // "1": the DAG replay for every program with several trees per range
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+// Renaming table of a shared DAG program (the layout of rows_table): the range
+// of each offset of an instance, padded to 8 bytes, then per range the P bytes
+// of its renaming. False when the ranges do not cover every offset once.
+bool dag_table(const Schedule& s, const DagPlan& d, std::vector<uint8_t>* t) {
+  const Spec& sp = s.spec;
+  const int64_t R = int64_t(s.ranges.size());
+  if (R > 256 || !d.shared) return false;
+  const int64_t moff = (sp.n + 7) / 8 * 8;
+  t->assign(size_t(moff + R * sp.P), 0);
+  std::vector<char> seen(size_t(sp.n), 0);
+  for (int64_t r = 0; r < R; ++r) {
+    const FusedRange& fr = s.ranges[size_t(r)];
+    for (int64_t o = fr.start; o < fr.start + fr.len; ++o) {
+      if (o < 0 || o >= sp.n || seen[size_t(o)]) return false;
+      seen[size_t(o)] = 1;
+      (*t)[size_t(o)] = uint8_t(r);
+    }
+  }
+  for (int64_t o = 0; o < sp.n; ++o)
+    if (!seen[size_t(o)]) return false;
+  std::memcpy(t->data() + moff, d.maps.data(), size_t(R * sp.P));
+  return true;
+}
+
+// Work items of the DAG replay: at most kDagLanes positions each, all in one
+// range; vec4: runs of 4-element vectors starting on 64-element boundaries,
+// the ragged head and tail as single elements.
+void dag_segment(std::vector<Item>& out, int64_t s0, int64_t len, int32_t tag, bool vec4) {
+  if (len <= 0) return;
+  if (!vec4) {
+    for (int64_t off = 0; off < len; off += kDagLanes)
+      out.push_back({s0 + off, -int32_t(std::min<int64_t>(kDagLanes, len - off)), tag});
+    return;
+  }
+  const int64_t head = std::min<int64_t>((kDagLanes - s0 % kDagLanes) % kDagLanes, len);
+  if (head) out.push_back({s0, -int32_t(head), tag});
+  const int64_t b0 = s0 + head, nv = (len - head) / 4;
+  for (int64_t off = 0; off < nv; off += kDagLanes)
+    out.push_back({b0 + off * 4, int32_t(std::min<int64_t>(kDagLanes, nv - off)), tag});
+  const int64_t t0 = b0 + nv * 4;
+  if (s0 + len > t0) out.push_back({t0, -int32_t(s0 + len - t0), tag});
+}
+
 bool fixed_shapes_enabled() {
   static const bool on = [] {
     const char* v = std::getenv("AR_FUSED_SHAPES");  // "0": no shape-specialised kernel (for comparisons)
@@ -484,6 +556,35 @@ RunResult build_items(Plan& pl, bool vec) {
     pl.nitems[mode] = int64_t(work.size());
     pl.built[mode] = true;
     return RunResult{};
+  } else if (pl.dag) {
+    if (!pl.prog.p) {
+      hipError_t e = upload(pl.prog, pl.dp.words);
+      if (e != hipSuccess) return hip_fail(e, "uploading the DAG program");
+    }
+    const size_t vals1 = size_t(pl.dp.S) * kDagLanes * 4;
+    if (pl.dag_shared) {
+      if (!pl.dtab.p) {
+        hipError_t e = upload(pl.dtab, pl.dag_tab);
+        if (e != hipSuccess) return hip_fail(e, "uploading the renaming table");
+      }
+      pl.dag_lds[mode] = vals1 + size_t(sp.P) * sizeof(void*);
+      pl.nitems[mode] = 1;  // launched by element count
+      pl.built[mode] = true;
+      return RunResult{};
+    }
+    // vectors of 4 elements where the buffers are aligned and four times the values fit the LDS
+    const bool vec4 = vec && 4 * vals1 <= pl.lds_limit;
+    const bool flat = s.ranges.size() == 1 && s.ranges[0].start == 0 && s.ranges[0].len == sp.n;
+    if (sp.batch == 1 || flat) {
+      const int64_t mult = flat ? sp.batch : 1;
+      for (size_t i = 0; i < s.ranges.size(); ++i)
+        dag_segment(items, s.ranges[i].start, s.ranges[i].len * mult, pl.dp.offsets[i], vec4);
+    } else {
+      for (int64_t b = 0; b < sp.batch; ++b)
+        for (size_t i = 0; i < s.ranges.size(); ++i)
+          dag_segment(items, b * sp.n + s.ranges[i].start, s.ranges[i].len, pl.dp.offsets[i], vec4);
+    }
+    pl.dag_lds[mode] = vec4 ? 4 * vals1 : vals1;
   } else {
     const bool flat = s.ranges.size() == 1 && s.ranges[0].start == 0 && s.ranges[0].len == sp.n;
     int64_t max_len = 0;
@@ -595,6 +696,28 @@ void choose_kernel(Plan& pl) {
     pl.fallback = "no replay program (" + s.fused_error + ")";
     return;
   }
+  if (pl.exec == E_DAG || (s.max_trees > 1 && (!fused_runs(s) || dag_forced()))) {
+    // several trees per range beyond what the register replays hold: the DAG replay
+    std::string err;
+    if (!dag_plan(s, &pl.dp, &err)) {
+      pl.kernel = K_LITERAL;
+      pl.fallback = "no DAG program (" + err + ")";
+      return;
+    }
+    int64_t max_len = 0;
+    for (const FusedRange& r : s.ranges) max_len = std::max(max_len, r.len);
+    pl.dag_shared = pl.dp.shared && s.ranges.size() > 1 && max_len < 4 * kDagLanes && dag_table(s, pl.dp, &pl.dag_tab);
+    const size_t need = size_t(pl.dp.S) * kDagLanes * 4 + (pl.dag_shared ? size_t(s.spec.P) * sizeof(void*) : 0);
+    if (need > pl.lds_limit) {
+      pl.kernel = K_LITERAL;
+      pl.fallback = "the DAG replay needs " + std::to_string(need) + " bytes of LDS per workgroup (" +
+                    std::to_string(pl.dp.S) + " values per element); the device allows " + std::to_string(pl.lds_limit);
+      return;
+    }
+    pl.dag = true;
+    pl.kernel = K_DAG;
+    return;
+  }
   if (!fused_runs(s)) {
     pl.kernel = K_LITERAL;
     pl.fallback = std::to_string(s.max_trees) + " result trees per range with a stack of " +
@@ -635,14 +758,22 @@ void trace_plan(const Plan& pl) {
     o << " groups=";
     for (size_t i = 0; i < sp.groups.size(); ++i) o << (i ? "," : "") << sp.groups[i];
   }
-  o << " exec=" << (pl.exec == E_LITERAL ? "literal" : "fused") << " device=" << pl.device << ": kernel "
+  static const char* ex[] = {"fused", "literal", "replay", "dag"};
+  o << " exec=" << ex[pl.exec] << " device=" << pl.device << ": kernel "
     << kernel_name(pl.kernel) << " (method steps " << s.nsteps << ", slots " << s.nslots << ", ranges "
     << s.ranges.size() << ", most trees " << s.max_trees << ", stack " << s.max_need << ", most leaves "
     << s.max_leaves << ", program words " << s.prog.size() << ")";
+  if (pl.kernel == K_DAG)
+    o << "; DAG " << (pl.dag_shared ? "shared by every range" : pl.dp.shared ? "one program" : "per range")
+      << ": " << pl.dp.instr << " combinations per element in " << pl.dp.levels << " levels, " << pl.dp.S << " slots";
   if (pl.kernel == K_LITERAL) o << "; " << s.nsteps << " step launches" << (s.finalize_ops ? " + 1 finalize" : "");
   if (!pl.fallback.empty()) o << "; literal fallback: " << pl.fallback;
   std::fprintf(stderr, "%s\n", o.str().c_str());
 }
+
+// The plan kind of an execution mode: AR_EXEC_REPLAY shares the fused plans
+// (it only differs for AR_DIRECT, which then replays instead of the direct kernel).
+int plan_exec(int exec) { return exec == E_REPLAY ? E_FUSED : exec; }
 
 // Repeated calls with one spec (a training loop's buckets, the unbatched
 // small-message case) skip building the cache key: the last plan found on
@@ -685,7 +816,7 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
   pl->s = s;
   pl->exec = exec;
   pl->device = device;
-  if (exec != E_LITERAL && s->fused_ok && fixed_shapes_enabled()) {
+  if (exec == E_FUSED && s->fused_ok && fixed_shapes_enabled()) {
     pl->shape = fixed_shape(*s, &pl->tab, &pl->shape_nl);
     if (pl->shape == SH_NONE) pl->multi = multi_shape(*s, &pl->mt);
     pl->rows = rows_table(*s, &pl->rows_tab, &pl->rows_ref);
@@ -702,6 +833,7 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
   int64_t slot = spec.n * spec.batch * int64_t(acc_bytes(spec.dtype));
   pl->slot_bytes = (slot + 255) / 256 * 256;
   pl->ws_bytes = size_t(s->nslots - 1) * size_t(spec.P) * size_t(pl->slot_bytes);
+  pl->lds_limit = lds_limit(device);
   choose_kernel(*pl);
   if (trace_enabled()) trace_plan(*pl);
   if (m.size() >= kMaxLivePlans) {
@@ -754,9 +886,9 @@ bool set_launch_blocks(int64_t blocks, int64_t* previous) {
 RunResult workspace_bytes(const Spec& spec, int exec, size_t* bytes) {
   std::lock_guard<std::mutex> lk(g_mu);
   Plan* pl = nullptr;
-  RunResult r = get_plan(spec, exec == E_LITERAL ? E_LITERAL : E_FUSED, -1, &pl);
+  RunResult r = get_plan(spec, plan_exec(exec), -1, &pl);
   if (r.status) return r;
-  // the replay keeps partials in registers; the literal steps need the slots
+  // the replays keep partials in registers or LDS; the literal steps need the slots
   *bytes = pl->kernel == K_LITERAL ? pl->ws_bytes : 0;
   return RunResult{};
 }
@@ -768,7 +900,7 @@ RunResult kernel_of(const Spec& spec, int exec, int* kernel) {
   if (exec == E_FUSED && spec.algo == A_DIRECT && spec.coll == C_ALLREDUCE) { *kernel = K_DIRECT; return RunResult{}; }
   std::lock_guard<std::mutex> lk(g_mu);
   Plan* pl = nullptr;
-  RunResult r = get_plan(spec, E_FUSED, -1, &pl);  // the launch's own choice, on a host-only plan
+  RunResult r = get_plan(spec, plan_exec(exec), -1, &pl);  // the launch's own choice, on a host-only plan
   if (r.status) return r;
   *kernel = pl->kernel;
   return RunResult{};
@@ -887,7 +1019,7 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
   void* ws = nullptr;
   {
     std::lock_guard<std::mutex> lk(g_mu);
-    res = get_plan(spec, exec == E_LITERAL ? E_LITERAL : E_FUSED, device, &pl);
+    res = get_plan(spec, plan_exec(exec), device, &pl);
     if (res.status) return res;
     if (pl->kernel == K_LITERAL && pl->exec != E_LITERAL) {
       // no replay holds the program: the step-by-step kernels compute the same bits
@@ -953,6 +1085,19 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
     ptrs.xcd = pl->strided || pl->s->prog.size() * sizeof(int32_t) > kXcdProgramBytes ? 1 : 0;
     const int64_t nit = pl->nitems[mode], cap = launch_blocks();
     const int TM = pl->s->max_trees > 1 ? kMaxFusedTrees : 1;
+    if (pl->dag) {
+      // few workgroups (a latency-bound call): 16 waves each share the levels' combinations
+      const int64_t total = spec.n * spec.batch;
+      const int64_t blocks = pl->dag_shared ? (total + kDagLanes - 1) / kDagLanes : nit;
+      const int threads = blocks <= 512 ? 1024 : 256;
+      const Item* ditems = pl->dag_shared ? nullptr : items;
+      AR_DISPATCH(spec.dtype, spec.op,
+                  (e = launch_fused_dag_t<DT, OPK>(pl->dag_shared, threads, pl->dag_lds[mode], nit, ptrs, ditems, prog,
+                                                   reinterpret_cast<const uint8_t*>(pl->dtab.p), total, int(spec.n),
+                                                   spec.P, pl->dp.S, cap, st, ev)));
+      if (e != hipSuccess) return hip_fail(e, "launching the DAG replay");
+      return res;
+    }
     if (pl->rows) {
       // whole vectors in k_fused_rows_vec where it applies, the rest (or all)
       // in k_fused_rows; each launcher splits its launch by the block limit

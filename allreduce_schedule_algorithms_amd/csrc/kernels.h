@@ -830,6 +830,201 @@ __global__ __launch_bounds__(kThreads) void k_fused_staged(RankPtrs ptrs, const 
 }
 
 // ----------------------------------------------------------------------------
+// DAG replay: every distinct combination of a range's result trees once
+// ----------------------------------------------------------------------------
+// A program (words as DagProgram::words on the host: S, nleaf, nlevel, ninstr,
+// nout, leaf ranks, level starts, instructions, outputs) evaluates the result
+// trees of a range as a DAG in which each distinct combination appears once,
+// grouped in levels of independent combinations. A workgroup takes up to
+// kDagLanes positions, one per lane (a position is one element, or VW = 4
+// consecutive elements), and keeps every value in LDS, [slot][lane] of VW
+// words. Its waves share the work of each phase: a wave loads the leaves k =
+// wave, wave + waves, ... (four loads in flight), runs the combinations of a
+// level the same way (instruction words are wave-uniform: scalar loads; four
+// independent combinations per round), and after the last level stores the
+// outputs. Barriers separate the phases and the levels; a slot is reused only
+// in a later level than its value's last read, or by the one combination that
+// reads it last, which reads both operands before it writes. Every store
+// follows every load of the workgroup's positions, and no other workgroup
+// touches them, so in-place buffers are safe.
+constexpr int kDagLanes = 64;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// VW elements at element e of a rank buffer, as accumulation-type bits
+template <int DT, int VW>
+__device__ __forceinline__ void dag_ld(const void* base, int64_t e, uint32_t (&v)[VW]) {
+  if constexpr (VW == 4) {
+    if constexpr (DT == D_BF16) {
+      const u32x2 r = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + e));
+      v[0] = r[0] << 16;
+      v[1] = r[0] & 0xffff0000u;
+      v[2] = r[1] << 16;
+      v[3] = r[1] & 0xffff0000u;
+    } else {
+      const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint32_t*>(base) + e));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = r[j];
+    }
+  } else {
+    if constexpr (DT == D_BF16) v[0] = uint32_t(__builtin_nontemporal_load(static_cast<const uint16_t*>(base) + e)) << 16;
+    else v[0] = __builtin_nontemporal_load(static_cast<const uint32_t*>(base) + e);
+  }
+}
+
+template <int DT, int OPK>
+__device__ __forceinline__ uint32_t dag_cmb(uint32_t a, uint32_t b) {
+  if constexpr (DT == D_INT32) return cmb<OPK>(a, b);
+  else return as_u(cmb<OPK>(as_f(a), as_f(b)));
+}
+
+// a complete result: O_AVG divides by P, bf16 rounds once to nearest even
+template <int DT, int OPK, int VW>
+__device__ __forceinline__ void dag_st(void* base, int64_t e, const uint32_t (&v)[VW], float div) {
+  uint32_t r[VW];
+#pragma unroll
+  for (int j = 0; j < VW; ++j) r[j] = OPK == O_AVG ? as_u(as_f(v[j]) / div) : v[j];
+  if constexpr (VW == 4) {
+    if constexpr (DT == D_BF16) {
+      const u32x2 q = {to_bf16(as_f(r[0])) | (to_bf16(as_f(r[1])) << 16),
+                       to_bf16(as_f(r[2])) | (to_bf16(as_f(r[3])) << 16)};
+      __builtin_nontemporal_store(q, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + e));
+    } else {
+      const u32x4 q = {r[0], r[1], r[2], r[3]};
+      __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(static_cast<uint32_t*>(base) + e));
+    }
+  } else {
+    if constexpr (DT == D_BF16) __builtin_nontemporal_store(uint16_t(to_bf16(as_f(r[0]))), static_cast<uint16_t*>(base) + e);
+    else __builtin_nontemporal_store(r[0], static_cast<uint32_t*>(base) + e);
+  }
+}
+
+template <int VW>
+__device__ __forceinline__ void dag_get(const uint32_t* vals, int slot, int lane, uint32_t (&v)[VW]) {
+  if constexpr (VW == 4) {
+    const u32x4 q = reinterpret_cast<const u32x4*>(vals)[slot * kDagLanes + lane];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = q[j];
+  } else {
+    v[0] = vals[slot * kDagLanes + lane];
+  }
+}
+template <int VW>
+__device__ __forceinline__ void dag_put(uint32_t* vals, int slot, int lane, const uint32_t (&v)[VW]) {
+  if constexpr (VW == 4) reinterpret_cast<u32x4*>(vals)[slot * kDagLanes + lane] = u32x4{v[0], v[1], v[2], v[3]};
+  else vals[slot * kDagLanes + lane] = v[0];
+}
+
+// One workgroup's positions [start, start + cnt * VW). SHARED: the program's
+// ranks are renamed per lane through `row` (the lane's range's row of the
+// renaming table) and the buffers come from the LDS pointer table `lptr`.
+template <int DT, int OPK, int VW, bool SHARED>
+__device__ __forceinline__ void dag_body(const RankPtrs& ptrs, ProgPtr w, int64_t start, int cnt, void* const* lptr,
+                                         const uint8_t* row, uint32_t* vals) {
+  const int lane = int(threadIdx.x) & (kDagLanes - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kDagLanes);
+  const int NW = int(blockDim.x) / kDagLanes;
+  const bool act = lane < cnt;
+  const int64_t e = start + int64_t(lane) * VW;
+  const int nleaf = w[1], nlev = w[2], ninstr = w[3], nout = w[4];
+  const ProgPtr leaves = w + 5;
+  const ProgPtr lv = leaves + nleaf;
+  const ProgPtr ins = lv + nlev + 1;
+  const ProgPtr outs = ins + ninstr;
+  auto buf = [&](int rank) -> void* {
+    if constexpr (SHARED) return lptr[row[rank]];
+    else return ptrs.p[rank];
+  };
+  for (int k0 = wave; k0 < nleaf; k0 += 4 * NW) {
+    uint32_t v[4][VW];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + u * NW;
+      if (k < nleaf && act) dag_ld<DT, VW>(buf(leaves[k]), e, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + u * NW;
+      if (k < nleaf && act) dag_put<VW>(vals, k, lane, v[u]);
+    }
+  }
+  __syncthreads();
+  for (int l = 0; l < nlev; ++l) {
+    const int i0 = lv[l], i1 = lv[l + 1];
+    for (int ib = i0 + wave; ib < i1; ib += 4 * NW) {
+      uint32_t iw[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) iw[u] = ib + u * NW < i1 ? uint32_t(ins[ib + u * NW]) : 0u;
+      uint32_t a[4][VW], b[4][VW];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (ib + u * NW < i1 && act) {
+          dag_get<VW>(vals, int((iw[u] >> 10) & 1023u), lane, a[u]);
+          dag_get<VW>(vals, int(iw[u] >> 20), lane, b[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (ib + u * NW < i1 && act) {
+#pragma unroll
+          for (int j = 0; j < VW; ++j) a[u][j] = dag_cmb<DT, OPK>(a[u][j], b[u][j]);
+          dag_put<VW>(vals, int(iw[u] & 1023u), lane, a[u]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  for (int o0 = wave; o0 < nout; o0 += 4 * NW) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int o = o0 + u * NW;
+      if (o < nout && act) {
+        const int ow = outs[o];
+        uint32_t v[VW];
+        dag_get<VW>(vals, ow >> 16, lane, v);
+        dag_st<DT, OPK, VW>(buf(ow & 0xffff), e, v, ptrs.div);
+      }
+    }
+  }
+}
+
+// Per-range programs (SHARED false): one work item per workgroup, `count` > 0
+// positions of 4 elements (16-byte aligned vectors; 8-byte for bf16), < 0 single
+// elements, at most kDagLanes, all in one range; the item's tag is its program's
+// offset. One program for every range (SHARED): workgroup b takes elements
+// first + b * kDagLanes onward, one per lane; `tab` holds the range of each of
+// the n offsets of an instance (padded to 8 bytes), then per range a row of P
+// bytes renaming the program's ranks to the range's. LDS: S x kDagLanes values
+// (of 4 words if any item has vectors), then (SHARED) the P buffer pointers.
+template <int DT, int OPK, bool SHARED>
+__global__ __launch_bounds__(1024) void k_fused_dag(RankPtrs ptrs, const Item* __restrict__ items,
+                                                    const int32_t* __restrict__ prog, const uint8_t* __restrict__ tab,
+                                                    int64_t first, int64_t total, int32_t n, int32_t P, int32_t S) {
+  extern __shared__ u32x4 dag_lds[];
+  uint32_t* vals = reinterpret_cast<uint32_t*>(dag_lds);
+  if constexpr (SHARED) {
+    void** lptr = reinterpret_cast<void**>(vals + S * kDagLanes);
+    if (threadIdx.x == 0)
+      for (int x = 0; x < P; ++x) lptr[x] = ptrs.p[x];
+    __syncthreads();
+    const int64_t pos0 = first + int64_t(blockIdx.x) * kDagLanes;
+    const int64_t left = total - pos0;
+    const int cnt = int(left < kDagLanes ? left : kDagLanes);
+    const int lane = int(threadIdx.x) & (kDagLanes - 1);
+    const uint8_t* row = tab;
+    if (lane < cnt) {
+      const int o = int((pos0 + lane) % n);
+      row = tab + (n + 7) / 8 * 8 + int(tab[o]) * P;
+    }
+    dag_body<DT, OPK, 1, true>(ptrs, as_prog(prog), pos0, cnt, lptr, row, vals);
+  } else {
+    const Item it = items[item_index(ptrs.xcd)];
+    const ProgPtr w = as_prog(prog) + it.tag;
+    if (it.count > 0) dag_body<DT, OPK, 4, false>(ptrs, w, it.start, it.count, nullptr, nullptr, vals);
+    else dag_body<DT, OPK, 1, false>(ptrs, w, it.start, -it.count, nullptr, nullptr, vals);
+  }
+}
+
+// ----------------------------------------------------------------------------
 // literal step execution
 // ----------------------------------------------------------------------------
 struct WsDesc {

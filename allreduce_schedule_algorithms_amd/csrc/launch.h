@@ -53,6 +53,12 @@ hipError_t launch_fused_fixed_t(int shape, int nl, int M, int64_t nitems, const 
 template <int DT, int OPK>
 hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& ws, const LitWork* work,
                             const LitWork* packed, hipStream_t st, Evs ev);
+// shared: one program for every range (blocks of kDagLanes elements over [0, total));
+// otherwise nitems work items. threads: 256 or 1024; lds: dynamic LDS bytes.
+template <int DT, int OPK>
+hipError_t launch_fused_dag_t(bool shared, int threads, size_t lds, int64_t nitems, const RankPtrs& ptrs,
+                              const Item* items, const int32_t* prog, const uint8_t* tab, int64_t total, int n,
+                              int P, int S, int64_t max_blocks, hipStream_t st, Evs ev);
 template <int DT, int OPK>
 hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total, int64_t max_blocks, hipStream_t st,
                            Evs ev);
@@ -328,6 +334,38 @@ hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& w
   return hipGetLastError();
 }
 
+template <int DT, int OPK, bool SH>
+hipError_t dag_d(int threads, size_t lds, int64_t nitems, const RankPtrs& ptrs, const Item* items,
+                 const int32_t* prog, const uint8_t* tab, int64_t total, int n, int P, int S, int64_t max_blocks,
+                 hipStream_t st, Evs ev) {
+  static bool raised = false;  // LDS beyond 64 KB per workgroup needs the kernel's attribute raised once
+  if (lds > 65536 && !raised) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fused_dag<DT, OPK, SH>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+    raised = true;
+  }
+  const int64_t blocks = SH ? (total + kDagLanes - 1) / kDagLanes : nitems;
+  for (int64_t b0 = 0; b0 < blocks; b0 += max_blocks) {  // workgroups are independent
+    const int64_t cnt = std::min(max_blocks, blocks - b0);
+    const Evs ei{b0 == 0 ? ev.start : nullptr, b0 + cnt >= blocks ? ev.stop : nullptr};
+    hipExtLaunchKernelGGL((k_fused_dag<DT, OPK, SH>), dim3(unsigned(cnt)), dim3(unsigned(threads)), uint32_t(lds), st,
+                          ei.start, ei.stop, 0, ptrs, SH ? items : items + b0, prog, tab, b0 * kDagLanes, total,
+                          int32_t(n), int32_t(P), int32_t(S));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int DT, int OPK>
+hipError_t launch_fused_dag_t(bool shared, int threads, size_t lds, int64_t nitems, const RankPtrs& ptrs,
+                              const Item* items, const int32_t* prog, const uint8_t* tab, int64_t total, int n,
+                              int P, int S, int64_t max_blocks, hipStream_t st, Evs ev) {
+  if (shared) return dag_d<DT, OPK, true>(threads, lds, nitems, ptrs, items, prog, tab, total, n, P, S, max_blocks, st, ev);
+  return dag_d<DT, OPK, false>(threads, lds, nitems, ptrs, items, prog, tab, total, n, P, S, max_blocks, st, ev);
+}
+
 // One launch per run of at most max_blocks workgroups; each launch gets the
 // rank pointers advanced to its first element. The vector path's element tail
 // (past the last whole vector) goes to block 0 of the last launch.
@@ -412,6 +450,9 @@ hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total,
                                                       const int32_t*, int64_t, hipStream_t, Evs);          \
   template hipError_t launch_literal_t<DT, OPK>(int64_t, const RankPtrs&, const WsDesc&, const LitWork*,    \
                                                 const LitWork*, hipStream_t, Evs);                          \
+  template hipError_t launch_fused_dag_t<DT, OPK>(bool, int, size_t, int64_t, const RankPtrs&, const Item*,  \
+                                                  const int32_t*, const uint8_t*, int64_t, int, int, int,     \
+                                                  int64_t, hipStream_t, Evs);                                 \
   template hipError_t launch_direct_t<DT, OPK>(bool, const RankPtrs&, int, int64_t, int64_t, hipStream_t, Evs);
 #endif  // AR_LAUNCH_DEFINITIONS
 

@@ -50,6 +50,7 @@ WORKLOADS = {
         headline=("generalized", 0, "fused"),
         others=[("direct", 0, "fused"), ("ring", 0, "fused"), ("rh_rd", 0, "fused"),
                 ("generalized", 1, "fused"), ("generalized", 2, "fused"), ("generalized", 3, "fused"),
+                ("generalized", 1, "dag"), ("generalized", 2, "dag"), ("generalized", 3, "dag"),
                 ("generalized", 0, "fused", "allreduce", "sum", 4), ("generalized", 0, "fused", "allreduce", "sum", 5),
                 ("generalized", 0, "fused", "allreduce", "sum", 6),
                 ("rd", 0, "fused"), ("binomial", 0, "fused"), ("chain", 1, "fused"),
@@ -71,7 +72,7 @@ WORKLOADS = {
         P=24, n=106, dtype="fp32", batch=10_000, groups=None, steps=50,
         headline=("rd", 0, "fused"),
         others=[("binomial", 0, "fused"), ("direct", 0, "fused"), ("generalized", "L", "fused"),
-                ("generalized", 0, "fused"), ("ring", 0, "fused"),
+                ("generalized", "L", "dag"), ("generalized", 0, "fused"), ("ring", 0, "fused"),
                 ("rd", 0, "literal"), ("binomial", 0, "literal"), ("generalized", "L", "literal")]),
     "rh_fp32": dict(
         desc="8 ranks x 2^20 fp32 N(0,1), seed 0",

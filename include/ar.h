@@ -134,17 +134,24 @@ typedef enum {
  *  AR_EXEC_FUSED    default. An AR_DIRECT Allreduce runs the one-pass direct kernel (read all
  *                   P, combine left to right, write all P); every other schedule and collective
  *                   runs its fused per-element replay: one launch evaluates, per element,
- *                   exactly the combination trees the step list builds, in registers. A
- *                   schedule the replay cannot hold (ranges with more than 8 result trees,
- *                   several trees with a stack deeper than 8, or a rounded partial combined
- *                   again) runs the literal steps instead, with the same bits, and then
- *                   uses a workspace like AR_EXEC_LITERAL (ar_workspace_bytes says how much).
+ *                   exactly the combination trees the step list builds, in registers, or for
+ *                   ranges with more than 8 result trees (or several trees with a stack deeper
+ *                   than 8) in the DAG replay, with the values in LDS. A schedule neither can
+ *                   hold (a rounded partial combined again, or a DAG whose values exceed the
+ *                   workgroup's LDS) runs the literal steps instead, with the same bits, and
+ *                   then uses a workspace like AR_EXEC_LITERAL (ar_workspace_bytes says how
+ *                   much).
  *  AR_EXEC_LITERAL  one launch per schedule step (chunk REDUCE / COPY kernels), partials
  *                   through HBM workspace slots; a last launch moves results that ended in
  *                   a workspace slot into the caller's buffer.
  *  AR_EXEC_REPLAY   the fused replay kernel for every schedule, AR_DIRECT included.
+ *  AR_EXEC_DAG      the DAG replay (AR_KERNEL_DAG) for every schedule, AR_DIRECT included:
+ *                   each distinct combination of a range's result trees is evaluated once, in
+ *                   levels, with the values in LDS (see ar_schedule_dag_export). AR_EXEC_FUSED
+ *                   runs it for programs with more result trees per range than the register
+ *                   replays hold.
  * All three give bit-identical results for the same schedule. */
-typedef enum { AR_EXEC_FUSED = 0, AR_EXEC_LITERAL = 1, AR_EXEC_REPLAY = 2 } ar_exec;
+typedef enum { AR_EXEC_FUSED = 0, AR_EXEC_LITERAL = 1, AR_EXEC_REPLAY = 2, AR_EXEC_DAG = 3 } ar_exec;
 
 /* Full description of one call. */
 typedef struct ar_call {
@@ -237,7 +244,10 @@ ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes);
  *                            ranks and more than 4096 elements (16-byte aligned buffers; otherwise
  *                            AR_KERNEL_ROWS runs): every rank's vector at four elements per thread
  *                            loaded once and staged in LDS, the leaves read from there in each
- *                            range's order. */
+ *                            range's order.
+ *  AR_KERNEL_DAG             the DAG replay: more than 8 result trees per range (the generalized
+ *                            algorithm with large r at large P), and every call under
+ *                            AR_EXEC_DAG; each distinct combination once, values in LDS. */
 typedef enum {
   AR_KERNEL_NONE = 0,
   AR_KERNEL_DIRECT = 1,

@@ -386,28 +386,26 @@ def test_generalized_more_steps_small():
 
 
 def test_fused_falls_back_to_literal_steps():
-    # 13 ranks, 4 steps, r = 4: ranges need more result trees than the fused
-    # replay keeps, so a fused call runs the literal steps (same bits) and takes
-    # the caller's workspace when one is given
+    # 255 ranks, r = 8: the DAG of a range holds more values than a workgroup's
+    # LDS, so a fused call runs the literal steps (same bits) and takes the
+    # caller's workspace when one is given
     import allreduce_schedule_algorithms_amd as A
     torch = torch_mod()
-    P, n = 13, 4099
+    P, n = 255, 600
     x = inputs.make("fp32", P, n, seed=41)
-    want = oracle.allreduce(x, "generalized", "fp32", "sum", knob=4, steps=4)
-    call = A.make_call(P, n, "fp32", "sum", "generalized", 4, steps=4)
-    assert A.ar_schedule_build(call).info().max_trees > 8
-    assert np.array_equal(bits(gpu_allreduce(x, "generalized", "fp32", "sum", 4, "fused", steps=4)), bits(want))
+    want = oracle.allreduce(x, "generalized", "fp32", "sum", knob=8)
+    call = A.make_call(P, n, "fp32", "sum", "generalized", 8)
+    assert A.ar_kernel_of(call) == A.Kernel.AR_KERNEL_LITERAL
+    assert np.array_equal(bits(gpu_allreduce(x, "generalized", "fp32", "sum", 8, "fused")), bits(want))
     need = A.ar_workspace_bytes(call)
     assert need > 0
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     bufs, keep = to_device(x, "fp32")
-    short = A.make_call(P, n, "fp32", "sum", "generalized", 4, steps=4, workspace=ws.data_ptr(),
-                        workspace_bytes=need - 1)
+    short = A.make_call(P, n, "fp32", "sum", "generalized", 8, workspace=ws.data_ptr(), workspace_bytes=need - 1)
     with pytest.raises(A.ArError) as e:
         A.ar_allreduce_ex([b.data_ptr() for b in bufs], short, torch.cuda.current_stream())
     assert e.value.status == A.Status.AR_WORKSPACE_TOO_SMALL
-    exact = A.make_call(P, n, "fp32", "sum", "generalized", 4, steps=4, workspace=ws.data_ptr(),
-                        workspace_bytes=need)
+    exact = A.make_call(P, n, "fp32", "sum", "generalized", 8, workspace=ws.data_ptr(), workspace_bytes=need)
     A.ar_allreduce_ex([b.data_ptr() for b in bufs], exact, torch.cuda.current_stream())
     torch.cuda.synchronize()
     assert np.array_equal(bits(from_device(bufs, "fp32")), bits(want))

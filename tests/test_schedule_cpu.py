@@ -352,12 +352,20 @@ def test_workspace_query():
     assert A.ar_workspace_bytes(lit) == 8 * 1024 * 4  # one fp32 slot per rank
     assert A.ar_workspace_bytes(A.make_call(8, 1024, "bf16", "sum", "ring")) == 0
     assert A.ar_workspace_bytes(A.make_call(8, 1024, "fp32", "sum", "ring", exec="literal")) == 0
-    # a fused call whose ranges need more result trees than the replay keeps
-    # runs the literal steps and needs their workspace
+    # ranges with more result trees than the register replays keep run the DAG
+    # replay, values in LDS: no workspace
     big = A.make_call(13, 1000, "fp32", "sum", "generalized", 4, steps=4)
     assert A.ar_schedule_build(big).info().max_trees > 8
+    assert A.ar_kernel_of(big) == A.Kernel.AR_KERNEL_DAG
+    assert A.ar_workspace_bytes(big) == 0
     lit = A.make_call(13, 1000, "fp32", "sum", "generalized", 4, "literal", steps=4)
-    assert A.ar_workspace_bytes(big) == A.ar_workspace_bytes(lit) > 0
+    assert A.ar_workspace_bytes(lit) > 0
+    # a DAG whose values exceed a workgroup's LDS (255 ranks, r = 8) runs the
+    # literal steps and needs their workspace
+    huge = A.make_call(255, 600, "fp32", "sum", "generalized", 8)
+    assert A.ar_kernel_of(huge) == A.Kernel.AR_KERNEL_LITERAL
+    lit = A.make_call(255, 600, "fp32", "sum", "generalized", 8, "literal")
+    assert A.ar_workspace_bytes(huge) == A.ar_workspace_bytes(lit) > 0
 
 
 def test_kernel_choice():
@@ -388,7 +396,14 @@ def test_kernel_choice():
         (dict(P=8, n=1 << 20, algo="direct", exec="replay"), K.AR_KERNEL_FIXED_CHAIN),
         (dict(P=8, n=1 << 20, algo="direct", collective="reduce_scatter"), K.AR_KERNEL_FIXED_CHAIN),
         (dict(P=8, n=1 << 20, algo="ring", exec="literal"), K.AR_KERNEL_LITERAL),
-        (dict(P=13, n=1000, algo="generalized", knob=4, steps=4), K.AR_KERNEL_LITERAL),  # more than 8 trees
+        (dict(P=13, n=1000, algo="generalized", knob=4, steps=4), K.AR_KERNEL_DAG),  # more than 8 trees
+        (dict(P=127, n=106, algo="generalized", knob=7), K.AR_KERNEL_DAG),
+        (dict(P=127, n=1 << 16, algo="generalized", knob=4), K.AR_KERNEL_DAG),
+        (dict(P=63, n=106, algo="generalized", knob=6), K.AR_KERNEL_DAG),
+        (dict(P=100, n=106, algo="generalized", knob=7), K.AR_KERNEL_DAG),
+        (dict(P=255, n=600, algo="generalized", knob=8), K.AR_KERNEL_LITERAL),  # its DAG exceeds the LDS
+        (dict(P=8, n=1 << 20, algo="rh_rd", exec="dag"), K.AR_KERNEL_DAG),
+        (dict(P=8, n=1 << 20, algo="direct", exec="dag"), K.AR_KERNEL_DAG),
         (dict(P=1, n=10, algo="ring"), K.AR_KERNEL_NONE),
         (dict(P=5, n=0, algo="ring"), K.AR_KERNEL_NONE),
     ]
