@@ -149,6 +149,8 @@ struct Plan {
   std::vector<uint8_t> dag_tab;  // shared: range of each offset, then the renaming rows
   DevBuf dtab;
   size_t dag_lds[2] = {0, 0};    // per alignment mode: dynamic LDS bytes
+  int dag_vals[2] = {0, 0};      // per alignment mode: LDS words of the values
+  int dag_words = 0;             // longest program, in words
   size_t lds_limit = 0;
   int kernel = K_NONE;     // the kernel family the plan launches (ar_kernel)
   std::string fallback;   // why a fused call runs the literal steps (empty otherwise)
@@ -391,21 +393,6 @@ bool rows_vec(const Schedule& s) {
   return vec_width(sp.dtype) == 4 && sp.P <= kRowsVecMaxRanks && sp.n * sp.batch > kTinyElements;
 }
 
-// Whether a single-range program of several trees over more ranks than the
-// LDS staging of k_fused_staged holds (17..32) runs the rows kernels as one
-// range of instance length 1 (4-byte elements, more than kTinyElements
-// elements): every rank is then loaded once per element, not once per tree.
-// Fills *t with that table (range 0, identity renaming).
-bool rows_flat(const Schedule& s, std::vector<uint8_t>* t) {
-  const Spec& sp = s.spec;
-  const bool flat = s.ranges.size() == 1 && s.ranges[0].start == 0 && s.ranges[0].len == sp.n;
-  if (!flat || s.max_trees <= 1 || sp.P <= kMaxStagedRanks || !rows_vec(s)) return false;
-  t->assign(size_t(8 + sp.P), 0);
-  for (int x = 0; x < sp.P; ++x) (*t)[size_t(8 + x)] = uint8_t(x);
-  t->resize((t->size() + 7) / 8 * 8, 0);
-  return true;
-}
-
 // LDS one workgroup may allocate on a device (gfx950: 160 KB); host-only plans
 // assume the gfx950 figure.
 size_t lds_limit(int device) {
@@ -562,18 +549,20 @@ RunResult build_items(Plan& pl, bool vec) {
       if (e != hipSuccess) return hip_fail(e, "uploading the DAG program");
     }
     const size_t vals1 = size_t(pl.dp.S) * kDagLanes * 4;
+    const size_t progb = 0;  // the program is read from global memory (scalar loads)
     if (pl.dag_shared) {
       if (!pl.dtab.p) {
         hipError_t e = upload(pl.dtab, pl.dag_tab);
         if (e != hipSuccess) return hip_fail(e, "uploading the renaming table");
       }
-      pl.dag_lds[mode] = vals1 + size_t(sp.P) * sizeof(void*);
+      pl.dag_vals[mode] = int(vals1 / 4);
+      pl.dag_lds[mode] = vals1 + progb + size_t(sp.P) * sizeof(void*);
       pl.nitems[mode] = 1;  // launched by element count
       pl.built[mode] = true;
       return RunResult{};
     }
     // vectors of 4 elements where the buffers are aligned and four times the values fit the LDS
-    const bool vec4 = vec && 4 * vals1 <= pl.lds_limit;
+    const bool vec4 = vec && 4 * vals1 + progb <= pl.lds_limit;
     const bool flat = s.ranges.size() == 1 && s.ranges[0].start == 0 && s.ranges[0].len == sp.n;
     if (sp.batch == 1 || flat) {
       const int64_t mult = flat ? sp.batch : 1;
@@ -584,7 +573,8 @@ RunResult build_items(Plan& pl, bool vec) {
         for (size_t i = 0; i < s.ranges.size(); ++i)
           dag_segment(items, b * sp.n + s.ranges[i].start, s.ranges[i].len, pl.dp.offsets[i], vec4);
     }
-    pl.dag_lds[mode] = vec4 ? 4 * vals1 : vals1;
+    pl.dag_vals[mode] = int((vec4 ? 4 * vals1 : vals1) / 4);
+    pl.dag_lds[mode] = (vec4 ? 4 * vals1 : vals1) + progb;
   } else {
     const bool flat = s.ranges.size() == 1 && s.ranges[0].start == 0 && s.ranges[0].len == sp.n;
     int64_t max_len = 0;
@@ -696,28 +686,55 @@ void choose_kernel(Plan& pl) {
     pl.fallback = "no replay program (" + s.fused_error + ")";
     return;
   }
-  if (pl.exec == E_DAG || (s.max_trees > 1 && (!fused_runs(s) || dag_forced()))) {
-    // several trees per range beyond what the register replays hold: the DAG replay
+  // The DAG replay (each distinct combination once, values in LDS) takes:
+  // programs with more result trees than the register replays hold; other
+  // programs of several trees per range except those k_fused_multi holds and
+  // batches of short ranges of several shapes (strided items); and
+  // latency-bound calls over many ranks whose trees are shallow (one element
+  // per lane, every rank loaded at once instead of in rounds of eight).
+  const bool tiny = s.spec.n * s.spec.batch <= kTinyElements;
+  const bool many = s.max_trees > 1 && !pl.multi && !strided_items(s);
+  const bool wide = s.max_trees == 1 && tiny && s.spec.P >= 16;
+  if (pl.exec == E_DAG || (s.max_trees > 1 && (!fused_runs(s) || dag_forced())) ||
+      (pl.exec == E_FUSED && fixed_shapes_enabled() && (many || wide))) {
     std::string err;
     if (!dag_plan(s, &pl.dp, &err)) {
       pl.kernel = K_LITERAL;
       pl.fallback = "no DAG program (" + err + ")";
       return;
     }
+    if (pl.exec == E_FUSED && fused_runs(s) && !dag_forced() && wide && !many &&
+        pl.dp.levels > 2 * ceil_log2(s.spec.P)) {
+      pl.dp = DagPlan{};  // a deep tree (a chain): one barrier per level would not pay
+      goto registers;
+    }
     int64_t max_len = 0;
     for (const FusedRange& r : s.ranges) max_len = std::max(max_len, r.len);
     pl.dag_shared = pl.dp.shared && s.ranges.size() > 1 && max_len < 4 * kDagLanes && dag_table(s, pl.dp, &pl.dag_tab);
+    if (pl.dp.shared && s.ranges.size() > 1 && !pl.dag_shared && !dag_plan(s, &pl.dp, &err, false)) {
+      // long ranges run per-range work items, each with its own range's program
+      pl.kernel = K_LITERAL;
+      pl.fallback = "no DAG program (" + err + ")";
+      return;
+    }
+    pl.dag_words = 0;
+    for (size_t r = 0; r < pl.dp.offsets.size(); ++r) {
+      const int32_t* w = pl.dp.words.data() + pl.dp.offsets[r];
+      pl.dag_words = std::max(pl.dag_words, 5 + w[1] + w[2] + 1 + w[3] + w[4]);
+    }
     const size_t need = size_t(pl.dp.S) * kDagLanes * 4 + (pl.dag_shared ? size_t(s.spec.P) * sizeof(void*) : 0);
     if (need > pl.lds_limit) {
       pl.kernel = K_LITERAL;
       pl.fallback = "the DAG replay needs " + std::to_string(need) + " bytes of LDS per workgroup (" +
-                    std::to_string(pl.dp.S) + " values per element); the device allows " + std::to_string(pl.lds_limit);
+                    std::to_string(pl.dp.S) + " values per element, a program of " + std::to_string(pl.dag_words) +
+                    " words); the device allows " + std::to_string(pl.lds_limit);
       return;
     }
     pl.dag = true;
     pl.kernel = K_DAG;
     return;
   }
+registers:
   if (!fused_runs(s)) {
     pl.kernel = K_LITERAL;
     pl.fallback = std::to_string(s.max_trees) + " result trees per range with a stack of " +
@@ -821,11 +838,6 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
     if (pl->shape == SH_NONE) pl->multi = multi_shape(*s, &pl->mt);
     pl->rows = rows_table(*s, &pl->rows_tab, &pl->rows_ref);
     pl->rows_n = spec.n;
-    if (!pl->rows && rows_flat(*s, &pl->rows_tab)) {
-      pl->rows = true;
-      pl->rows_ref = 0;
-      pl->rows_n = 1;
-    }
     // four vectors per thread for short launches with few ranks, as the direct kernel
     pl->md = spec.P <= 8 && spec.n * spec.batch / vec_width(spec.dtype) <= (int64_t(1) << 19) ? 4 : 2;
   }
@@ -1094,7 +1106,7 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
       AR_DISPATCH(spec.dtype, spec.op,
                   (e = launch_fused_dag_t<DT, OPK>(pl->dag_shared, threads, pl->dag_lds[mode], nit, ptrs, ditems, prog,
                                                    reinterpret_cast<const uint8_t*>(pl->dtab.p), total, int(spec.n),
-                                                   spec.P, pl->dp.S, cap, st, ev)));
+                                                   spec.P, pl->dag_vals[mode], cap, st, ev)));
       if (e != hipSuccess) return hip_fail(e, "launching the DAG replay");
       return res;
     }
@@ -1112,8 +1124,8 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
         // stack; measured 5% faster than 8 on 24-rank trees of three results)
         const int dv = pl->D == 8 && pl->s->max_need <= 6 ? 6 : pl->D;
         AR_DISPATCH(spec.dtype, spec.op,
-                    (e = launch_fused_rows_vec_t<DT, OPK>(dv, TM, pl->rows_n == 1, ptrs, ref, rt, nvec,
-                                                          int(pl->rows_n), R, spec.P, cap, st, ev1)));
+                    (e = launch_fused_rows_vec_t<DT, OPK>(dv, ptrs, ref, rt, nvec, int(pl->rows_n), R, spec.P, cap, st,
+                                                          ev1)));
         if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
       }
       if (nvec * 4 < total) {

@@ -716,8 +716,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_rows(RankPtrs ptrs, const in
 }
 
 // The same batches with 4-byte elements, 16-byte aligned buffers and at most
-// PB ranks (and single-range programs of several trees over 17..32 ranks, as
-// one range of instance length 1). A workgroup loads every rank's 16-byte
+// PB ranks. A workgroup loads every rank's 16-byte
 // vector at each lane's four elements, one coalesced load per rank (each line
 // once, by one instruction), and stages them in LDS, each lane in its own
 // column of [rank][element][lane] words, so no barrier is needed. It then
@@ -726,9 +725,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_rows(RankPtrs ptrs, const in
 // are stored as whole vectors. `tab` is the table of k_fused_rows, padded to a
 // multiple of 8 bytes.
 constexpr int kRowsVecThreads = 128;  // two waves: one table copy per two (measured 5% faster than one)
-// With ID (one range, identity renaming) no table is read and each lane's
-// vectors are staged whole, [rank][lane] (one 16-byte LDS access per leaf).
-template <int DT, int OPK, int D, int TM, int B, int PB, bool ID>
+template <int DT, int OPK, int D, int TM, int B, int PB>
 __global__ __launch_bounds__(kRowsVecThreads) void k_fused_rows_vec(RankPtrs ptrs, const int32_t* __restrict__ prog,
                                                                     const uint8_t* __restrict__ tab, int64_t first,
                                                                     int64_t nvec, int32_t n, int32_t R, int32_t P) {
@@ -736,24 +733,6 @@ __global__ __launch_bounds__(kRowsVecThreads) void k_fused_rows_vec(RankPtrs ptr
   constexpr int T = kRowsVecThreads;
   extern __shared__ uint32_t rows_vec_lds[];
   uint32_t* stage = rows_vec_lds;                                // P x 4 x T words
-  if constexpr (ID) {
-    u32x4* st4 = reinterpret_cast<u32x4*>(stage);
-    const int64_t g = first + int64_t(blockIdx.x) * T + threadIdx.x;
-    const bool ok[1] = {g < nvec};
-    const int64_t e = g * 4;
-    u32x4 v[PB][1];
-#pragma unroll
-    for (int y = 0; y < PB; ++y) {
-      v[y][0] = u32x4{0, 0, 0, 0};
-      if (y < P) ld_user<DT, 1, true>(ptrs.p[y], e, ok, v[y]);
-    }
-#pragma unroll
-    for (int y = 0; y < PB; ++y)
-      if (y < P) st4[y * T + threadIdx.x] = v[y][0];
-    const auto w = prog_words<TM>(prog, 0);
-    replay<DT, OPK, D, TM, 1, B>(ptrs, w, e, ok, [&](int rank, u32x4(&r)[1]) { r[0] = st4[rank * T + threadIdx.x]; });
-    return;
-  }
   uint32_t* tabw = stage + P * 4 * T;                            // the table
   const int moff = (n + 7) / 8 * 8;
   const int words = (moff + R * P + 7) / 8 * 2;
@@ -914,9 +893,19 @@ __device__ __forceinline__ void dag_put(uint32_t* vals, int slot, int lane, cons
   else vals[slot * kDagLanes + lane] = v[0];
 }
 
-// One workgroup's positions [start, start + cnt * VW). SHARED: the program's
-// ranks are renamed per lane through `row` (the lane's range's row of the
-// renaming table) and the buffers come from the LDS pointer table `lptr`.
+// The contiguous block [*b0, *b1) of n units that wave `wave` of NW takes (the
+// units of a phase split evenly: consecutive program words per wave).
+__device__ __forceinline__ void wave_block(int n, int wave, int NW, int* b0, int* b1) {
+  const int per = (n + NW - 1) / NW;
+  *b0 = min(n, wave * per);
+  *b1 = min(n, *b0 + per);
+}
+
+// One workgroup's positions [start, start + cnt * VW). `w` is the program (its
+// words are read as scalars; each wave reads a contiguous block of each phase,
+// so its words share scalar cache lines). SHARED: the program's ranks are
+// renamed per lane through `row` (the lane's range's row of the renaming table)
+// and the buffers come from the LDS pointer table `lptr`.
 template <int DT, int OPK, int VW, bool SHARED>
 __device__ __forceinline__ void dag_body(const RankPtrs& ptrs, ProgPtr w, int64_t start, int cnt, void* const* lptr,
                                          const uint8_t* row, uint32_t* vals) {
@@ -934,55 +923,72 @@ __device__ __forceinline__ void dag_body(const RankPtrs& ptrs, ProgPtr w, int64_
     if constexpr (SHARED) return lptr[row[rank]];
     else return ptrs.p[rank];
   };
-  for (int k0 = wave; k0 < nleaf; k0 += 4 * NW) {
-    uint32_t v[4][VW];
+  // The combinations below are branch-free over the unrolled units, so their
+  // LDS accesses overlap. Lanes past `cnt` compute on their own LDS column and
+  // skip only the global accesses. Global loads and stores past a block are
+  // skipped by wave-uniform (scalar) branches: a repeated non-temporal access
+  // would move its line through HBM again.
+  int b0, b1;
+  wave_block(nleaf, wave, NW, &b0, &b1);
+  for (int k0 = b0; k0 < b1; k0 += 8) {  // up to eight loads in flight per lane
+    uint32_t v[8][VW];
+    if (act) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = k0 + u * NW;
-      if (k < nleaf && act) dag_ld<DT, VW>(buf(leaves[k]), e, v[u]);
+      for (int u = 0; u < 8; ++u)
+        if (k0 + u < b1) dag_ld<DT, VW>(buf(leaves[k0 + u]), e, v[u]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = k0 + u * NW;
-      if (k < nleaf && act) dag_put<VW>(vals, k, lane, v[u]);
-    }
+    for (int u = 0; u < 8; ++u)
+      if (k0 + u < b1) dag_put<VW>(vals, k0 + u, lane, v[u]);
   }
   __syncthreads();
   for (int l = 0; l < nlev; ++l) {
-    const int i0 = lv[l], i1 = lv[l + 1];
-    for (int ib = i0 + wave; ib < i1; ib += 4 * NW) {
-      uint32_t iw[4];
+    wave_block(lv[l + 1] - lv[l], wave, NW, &b0, &b1);
+    b0 += lv[l];
+    b1 += lv[l];
+    // whole groups of four (their eight operand reads in flight together), then
+    // the block's remainder one combination at a time
+    int i = b0;
+    for (; i + 4 <= b1; i += 4) {
+      uint32_t iw[4], a[4][VW], b[4][VW];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) iw[u] = ib + u * NW < i1 ? uint32_t(ins[ib + u * NW]) : 0u;
-      uint32_t a[4][VW], b[4][VW];
+      for (int u = 0; u < 4; ++u) iw[u] = uint32_t(ins[i + u]);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (ib + u * NW < i1 && act) {
-          dag_get<VW>(vals, int((iw[u] >> 10) & 1023u), lane, a[u]);
-          dag_get<VW>(vals, int(iw[u] >> 20), lane, b[u]);
-        }
+        dag_get<VW>(vals, int((iw[u] >> 10) & 1023u), lane, a[u]);
+        dag_get<VW>(vals, int(iw[u] >> 20), lane, b[u]);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (ib + u * NW < i1 && act) {
 #pragma unroll
-          for (int j = 0; j < VW; ++j) a[u][j] = dag_cmb<DT, OPK>(a[u][j], b[u][j]);
-          dag_put<VW>(vals, int(iw[u] & 1023u), lane, a[u]);
-        }
+        for (int j = 0; j < VW; ++j) a[u][j] = dag_cmb<DT, OPK>(a[u][j], b[u][j]);
+        dag_put<VW>(vals, int(iw[u] & 1023u), lane, a[u]);
       }
+    }
+    for (; i < b1; ++i) {
+      const uint32_t iw = uint32_t(ins[i]);
+      uint32_t a[VW], b[VW];
+      dag_get<VW>(vals, int((iw >> 10) & 1023u), lane, a);
+      dag_get<VW>(vals, int(iw >> 20), lane, b);
+#pragma unroll
+      for (int j = 0; j < VW; ++j) a[j] = dag_cmb<DT, OPK>(a[j], b[j]);
+      dag_put<VW>(vals, int(iw & 1023u), lane, a);
     }
     __syncthreads();
   }
-  for (int o0 = wave; o0 < nout; o0 += 4 * NW) {
+  wave_block(nout, wave, NW, &b0, &b1);
+  for (int o0 = b0; o0 < b1; o0 += 8) {
+    int ow[8];
+    uint32_t v[8][VW];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int o = o0 + u * NW;
-      if (o < nout && act) {
-        const int ow = outs[o];
-        uint32_t v[VW];
-        dag_get<VW>(vals, ow >> 16, lane, v);
-        dag_st<DT, OPK, VW>(buf(ow & 0xffff), e, v, ptrs.div);
-      }
+    for (int u = 0; u < 8; ++u) {
+      ow[u] = outs[min(o0 + u, b1 - 1)];
+      dag_get<VW>(vals, ow[u] >> 16, lane, v[u]);
+    }
+    if (act) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (o0 + u < b1) dag_st<DT, OPK, VW>(buf(ow[u] & 0xffff), e, v[u], ptrs.div);
     }
   }
 }
@@ -993,16 +999,18 @@ __device__ __forceinline__ void dag_body(const RankPtrs& ptrs, ProgPtr w, int64_
 // offset. One program for every range (SHARED): workgroup b takes elements
 // first + b * kDagLanes onward, one per lane; `tab` holds the range of each of
 // the n offsets of an instance (padded to 8 bytes), then per range a row of P
-// bytes renaming the program's ranks to the range's. LDS: S x kDagLanes values
-// (of 4 words if any item has vectors), then (SHARED) the P buffer pointers.
+// bytes renaming the program's ranks to the range's. LDS: S slots of kDagLanes
+// values (of 4 words if any item has vectors; `vals_words` words in all), then
+// (SHARED) the P buffer pointers.
 template <int DT, int OPK, bool SHARED>
 __global__ __launch_bounds__(1024) void k_fused_dag(RankPtrs ptrs, const Item* __restrict__ items,
                                                     const int32_t* __restrict__ prog, const uint8_t* __restrict__ tab,
-                                                    int64_t first, int64_t total, int32_t n, int32_t P, int32_t S) {
+                                                    int64_t first, int64_t total, int32_t n, int32_t P,
+                                                    int32_t vals_words) {
   extern __shared__ u32x4 dag_lds[];
   uint32_t* vals = reinterpret_cast<uint32_t*>(dag_lds);
   if constexpr (SHARED) {
-    void** lptr = reinterpret_cast<void**>(vals + S * kDagLanes);
+    void** lptr = reinterpret_cast<void**>(vals + vals_words);
     if (threadIdx.x == 0)
       for (int x = 0; x < P; ++x) lptr[x] = ptrs.p[x];
     __syncthreads();

@@ -41,9 +41,8 @@ hipError_t launch_fused_rows_t(int D, int TM, const RankPtrs& ptrs, const int32_
                                int64_t first, int64_t total, int n, int R, int P, int iters, int64_t max_blocks,
                                hipStream_t st, Evs ev);
 template <int DT, int OPK>
-hipError_t launch_fused_rows_vec_t(int D, int TM, bool ident, const RankPtrs& ptrs, const int32_t* prog,
-                                   const uint8_t* tab, int64_t nvec, int n, int R, int P, int64_t max_blocks,
-                                   hipStream_t st, Evs ev);
+hipError_t launch_fused_rows_vec_t(int D, const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab, int64_t nvec,
+                                   int n, int R, int P, int64_t max_blocks, hipStream_t st, Evs ev);
 template <int DT, int OPK>
 hipError_t launch_fused_multi_t(int nl, int64_t nitems, const MultiPtrs& mp, const Item* items, const int32_t* tab,
                                 hipStream_t st, Evs ev);
@@ -58,7 +57,7 @@ hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& w
 template <int DT, int OPK>
 hipError_t launch_fused_dag_t(bool shared, int threads, size_t lds, int64_t nitems, const RankPtrs& ptrs,
                               const Item* items, const int32_t* prog, const uint8_t* tab, int64_t total, int n,
-                              int P, int S, int64_t max_blocks, hipStream_t st, Evs ev);
+                              int P, int vals_words, int64_t max_blocks, hipStream_t st, Evs ev);
 template <int DT, int OPK>
 hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total, int64_t max_blocks, hipStream_t st,
                            Evs ev);
@@ -226,16 +225,15 @@ hipError_t rows_d(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab,
   return hipSuccess;
 }
 
-template <int DT, int OPK, int D, int TM, int PB, bool ID = false>
+template <int DT, int OPK, int D, int TM, int PB>
 hipError_t rows_vec_d(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab, int64_t nvec, int n, int R, int P,
                       int64_t max_blocks, hipStream_t st, Evs ev) {
   const int64_t blocks = (nvec + kRowsVecThreads - 1) / kRowsVecThreads;
-  const size_t lds = size_t(P) * 4 * kRowsVecThreads * sizeof(uint32_t) +
-                    (ID ? 0 : size_t((n + 7) / 8 * 8 + R * P + 7) / 8 * 8);
+  const size_t lds = size_t(P) * 4 * kRowsVecThreads * sizeof(uint32_t) + size_t((n + 7) / 8 * 8 + R * P + 7) / 8 * 8;
   for (int64_t b0 = 0; b0 < blocks; b0 += max_blocks) {  // workgroups are independent
     const int64_t cnt = std::min(max_blocks, blocks - b0);
     const Evs ei{b0 == 0 ? ev.start : nullptr, b0 + cnt >= blocks ? ev.stop : nullptr};
-    hipExtLaunchKernelGGL((k_fused_rows_vec<DT, OPK, D, TM, kLeafBatch, PB, ID>), dim3(unsigned(cnt)), dim3(kRowsVecThreads),
+    hipExtLaunchKernelGGL((k_fused_rows_vec<DT, OPK, D, TM, kLeafBatch, PB>), dim3(unsigned(cnt)), dim3(kRowsVecThreads),
                           lds, st, ei.start, ei.stop, 0, ptrs, prog, tab, b0 * kRowsVecThreads, nvec, int32_t(n),
                           int32_t(R), int32_t(P));
     const hipError_t e = hipGetLastError();
@@ -245,9 +243,8 @@ hipError_t rows_vec_d(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* 
 }
 
 template <int DT, int OPK>
-hipError_t launch_fused_rows_vec_t(int D, int TM, bool ident, const RankPtrs& ptrs, const int32_t* prog,
-                                   const uint8_t* tab, int64_t nvec, int n, int R, int P, int64_t max_blocks,
-                                   hipStream_t st, Evs ev) {
+hipError_t launch_fused_rows_vec_t(int D, const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab, int64_t nvec,
+                                   int n, int R, int P, int64_t max_blocks, hipStream_t st, Evs ev) {
   if constexpr (TT<DT>::V != 4) {
     return hipErrorInvalidValue;  // 4-byte elements only
   } else {
@@ -255,17 +252,7 @@ hipError_t launch_fused_rows_vec_t(int D, int TM, bool ident, const RankPtrs& pt
   if (P <= 8) return rows_vec_d<DT, OPK, DD, 1, 8>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);       \
   if (P <= 16) return rows_vec_d<DT, OPK, DD, 1, 16>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);     \
   return rows_vec_d<DT, OPK, DD, 1, 32>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev)
-#define AR_ROWS_VEC_TREES(DD) \
-  return rows_vec_d<DT, OPK, DD, kMaxFusedTrees, 32, true>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev)
-    if (P > 32 || (TM > 1 && !ident)) return hipErrorInvalidValue;  // several trees: one range, identity renaming
-    if (TM > 1) {
-      switch (D) {
-        case 2: AR_ROWS_VEC_TREES(2);
-        case 4: AR_ROWS_VEC_TREES(4);
-        case 6: AR_ROWS_VEC_TREES(6);
-        default: AR_ROWS_VEC_TREES(8);
-      }
-    }
+    if (P > 32) return hipErrorInvalidValue;
     switch (D) {
       case 2: AR_ROWS_VEC(2);
       case 4: AR_ROWS_VEC(4);
@@ -273,7 +260,6 @@ hipError_t launch_fused_rows_vec_t(int D, int TM, bool ident, const RankPtrs& pt
       case 8: AR_ROWS_VEC(8);
       default: AR_ROWS_VEC(16);
     }
-#undef AR_ROWS_VEC_TREES
 #undef AR_ROWS_VEC
   }
 }
@@ -336,8 +322,8 @@ hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& w
 
 template <int DT, int OPK, bool SH>
 hipError_t dag_d(int threads, size_t lds, int64_t nitems, const RankPtrs& ptrs, const Item* items,
-                 const int32_t* prog, const uint8_t* tab, int64_t total, int n, int P, int S, int64_t max_blocks,
-                 hipStream_t st, Evs ev) {
+                 const int32_t* prog, const uint8_t* tab, int64_t total, int n, int P, int vals_words,
+                 int64_t max_blocks, hipStream_t st, Evs ev) {
   static bool raised = false;  // LDS beyond 64 KB per workgroup needs the kernel's attribute raised once
   if (lds > 65536 && !raised) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fused_dag<DT, OPK, SH>),
@@ -351,7 +337,7 @@ hipError_t dag_d(int threads, size_t lds, int64_t nitems, const RankPtrs& ptrs, 
     const Evs ei{b0 == 0 ? ev.start : nullptr, b0 + cnt >= blocks ? ev.stop : nullptr};
     hipExtLaunchKernelGGL((k_fused_dag<DT, OPK, SH>), dim3(unsigned(cnt)), dim3(unsigned(threads)), uint32_t(lds), st,
                           ei.start, ei.stop, 0, ptrs, SH ? items : items + b0, prog, tab, b0 * kDagLanes, total,
-                          int32_t(n), int32_t(P), int32_t(S));
+                          int32_t(n), int32_t(P), int32_t(vals_words));
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -361,9 +347,12 @@ hipError_t dag_d(int threads, size_t lds, int64_t nitems, const RankPtrs& ptrs, 
 template <int DT, int OPK>
 hipError_t launch_fused_dag_t(bool shared, int threads, size_t lds, int64_t nitems, const RankPtrs& ptrs,
                               const Item* items, const int32_t* prog, const uint8_t* tab, int64_t total, int n,
-                              int P, int S, int64_t max_blocks, hipStream_t st, Evs ev) {
-  if (shared) return dag_d<DT, OPK, true>(threads, lds, nitems, ptrs, items, prog, tab, total, n, P, S, max_blocks, st, ev);
-  return dag_d<DT, OPK, false>(threads, lds, nitems, ptrs, items, prog, tab, total, n, P, S, max_blocks, st, ev);
+                              int P, int vals_words, int64_t max_blocks, hipStream_t st, Evs ev) {
+  if (shared)
+    return dag_d<DT, OPK, true>(threads, lds, nitems, ptrs, items, prog, tab, total, n, P, vals_words, max_blocks, st,
+                                ev);
+  return dag_d<DT, OPK, false>(threads, lds, nitems, ptrs, items, prog, tab, total, n, P, vals_words, max_blocks, st,
+                               ev);
 }
 
 // One launch per run of at most max_blocks workgroups; each launch gets the
@@ -443,9 +432,8 @@ hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total,
   template hipError_t launch_fused_rows_t<DT, OPK>(int, int, const RankPtrs&, const int32_t*, const uint8_t*, \
                                                    int64_t, int64_t, int, int, int, int, int64_t, hipStream_t,  \
                                                    Evs);                                                        \
-  template hipError_t launch_fused_rows_vec_t<DT, OPK>(int, int, bool, const RankPtrs&, const int32_t*,      \
-                                                       const uint8_t*, int64_t, int, int, int, int64_t,         \
-                                                       hipStream_t, Evs);                                       \
+  template hipError_t launch_fused_rows_vec_t<DT, OPK>(int, const RankPtrs&, const int32_t*, const uint8_t*,  \
+                                                       int64_t, int, int, int, int64_t, hipStream_t, Evs);      \
   template hipError_t launch_fused_strided_t<DT, OPK>(int, int, int64_t, const RankPtrs&, const SItem*,     \
                                                       const int32_t*, int64_t, hipStream_t, Evs);          \
   template hipError_t launch_literal_t<DT, OPK>(int64_t, const RankPtrs&, const WsDesc&, const LitWork*,    \

@@ -1134,7 +1134,7 @@ bool dag_renaming(const DagProgram& a, const DagProgram& b, int P, std::vector<i
   return true;
 }
 
-bool dag_plan(const Schedule& s, DagPlan* out, std::string* err) {
+bool dag_plan(const Schedule& s, DagPlan* out, std::string* err, bool allow_shared) {
   const int P = s.spec.P;
   const size_t R = s.ranges.size();
   std::vector<DagProgram> progs(R);
@@ -1148,7 +1148,7 @@ bool dag_plan(const Schedule& s, DagPlan* out, std::string* err) {
   out->offsets.assign(R, 0);
   if (R == 0) return true;
   // one program for every range when they differ only by a renaming of ranks
-  out->shared = true;
+  out->shared = allow_shared;
   out->maps.assign(R * size_t(P), 0);
   std::vector<int> map;
   for (size_t r = 0; r < R && out->shared; ++r) {

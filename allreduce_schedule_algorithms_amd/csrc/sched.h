@@ -157,7 +157,8 @@ struct DagPlan {
   int levels = 0;                // most levels
   int64_t instr = 0;             // combinations per element, most of any range
 };
-bool dag_plan(const Schedule& s, DagPlan* out, std::string* err);
+// allow_shared false: one program per range even where they differ only by a renaming.
+bool dag_plan(const Schedule& s, DagPlan* out, std::string* err, bool allow_shared = true);
 
 // Generate + realize + plan. Returns nullptr and sets *err on invalid input.
 Schedule* build_schedule(const Spec& spec, std::string* err);

@@ -474,7 +474,8 @@ def latency(calls=2000):
     consecutive instances, captured once in a HIP graph and replayed, timed
     with events around the replay. Without the host's enqueue cost this is the
     library's alpha on this device (launch, one kernel, completion). Literal
-    execution of the same call (one launch per step) is timed the same way."""
+    execution of the same call (one launch per step) and the DAG replay
+    (AR_EXEC_DAG) are timed the same way."""
     import numpy as np
     import torch
 
@@ -488,7 +489,7 @@ def latency(calls=2000):
         st = torch.cuda.Stream()
         ptrs = [A.marshal_ptrs([b.data_ptr() + i * n * 4 for b in bufs]) for i in range(reps)]
         row = {"P": P, "n": n, "schedule": f"{algo}/r{knob}"}
-        for ex in ("fused", "literal"):
+        for ex in ("fused", "dag", "literal"):
             call = A.make_call(P, n, "fp32", "sum", algo, knob, ex)
             with torch.cuda.stream(st):
                 for i in range(20):  # plans and workspace built outside the capture

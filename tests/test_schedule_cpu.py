@@ -381,10 +381,15 @@ def test_kernel_choice():
         (dict(P=6, n=1000, algo="binomial"), K.AR_KERNEL_FIXED_STACK),
         (dict(P=7, n=1 << 24, algo="generalized", knob=3), K.AR_KERNEL_MULTI),
         (dict(P=7, n=1 << 24, algo="generalized", knob=1), K.AR_KERNEL_MULTI),
-        (dict(P=12, n=4099, algo="generalized", knob=2), K.AR_KERNEL_STAGED),
-        (dict(P=24, n=106, algo="generalized", knob=5, batch=10_000), K.AR_KERNEL_ROWS_VEC),
-        (dict(P=24, n=106, algo="generalized", knob=5, batch=10_000, dtype="bf16"), K.AR_KERNEL_REPLAY),
-        (dict(P=24, n=106, algo="generalized", knob=5, batch=30), K.AR_KERNEL_REPLAY),
+        (dict(P=12, n=4099, algo="generalized", knob=2), K.AR_KERNEL_DAG),
+        (dict(P=24, n=106, algo="generalized", knob=5, batch=10_000), K.AR_KERNEL_DAG),
+        (dict(P=24, n=106, algo="generalized", knob=5, batch=10_000, dtype="bf16"), K.AR_KERNEL_DAG),
+        (dict(P=24, n=106, algo="generalized", knob=5, batch=30), K.AR_KERNEL_DAG),
+        (dict(P=24, n=106, algo="rd"), K.AR_KERNEL_DAG),  # latency-bound, many ranks, shallow tree
+        (dict(P=24, n=106, algo="binomial"), K.AR_KERNEL_DAG),
+        (dict(P=127, n=106, algo="generalized"), K.AR_KERNEL_DAG),
+        (dict(P=24, n=106, algo="ring"), K.AR_KERNEL_REPLAY),  # a chain: one level per rank
+        (dict(P=12, n=106, algo="rd"), K.AR_KERNEL_REPLAY),
         (dict(P=192, n=1 << 20, dtype="bf16", algo="ahc", groups=[64, 128]), K.AR_KERNEL_REPLAY),
         (dict(P=24, n=106, algo="rd", batch=10_000), K.AR_KERNEL_REPLAY),
         (dict(P=24, n=106, algo="generalized", batch=10_000), K.AR_KERNEL_ROWS_VEC),
