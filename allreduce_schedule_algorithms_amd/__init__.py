@@ -13,7 +13,7 @@ from ._ar import (  # noqa: F401
     ar_get_cost_model, ar_kernel_of,
     ar_last_error_message, ar_last_hip_error, ar_reduce_scatter, ar_schedule_build, ar_select, ar_set_cost_model,
     ar_set_launch_blocks, ar_status_string, ar_table_check, ar_table_check_ex, ar_version, ar_workspace_bytes,
-    make_call, marshal_ptrs, ar_cache_stats_get, ar_release_cached,
+    make_call, marshal_ptrs, ar_cache_stats_get, ar_release_cached, ar_allreduce_noalloc, AR_NOALLOC_SCRATCH_BYTES,
 )
 
 _TORCH_DTYPE = {"int32": "int32", "fp32": "float32", "bf16": "bfloat16"}

@@ -150,6 +150,7 @@ SIGNATURES = {
     "ar_allreduce": (C.c_int, [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_int32,
                                C.c_int32, C.c_void_p]),
     "ar_allreduce_ex": (C.c_int, [C.POINTER(C.c_void_p), C.POINTER(ar_call), C.c_void_p]),
+    "ar_allreduce_noalloc": (C.c_int, [C.POINTER(C.c_void_p), C.POINTER(ar_call), C.c_void_p]),
     "ar_reduce_scatter": (C.c_int, [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int32, C.c_int32,
                                     C.c_int32, C.c_void_p]),
     "ar_all_gather": (C.c_int, [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_void_p]),
@@ -289,6 +290,14 @@ def ar_all_gather(bufs, P, n, dtype, algo, stream=None):
 
 def ar_allreduce_ex(bufs, call: ar_call, stream=None):
     _check(lib.ar_allreduce_ex(_ptrs(bufs), C.byref(call), _stream(stream)))
+
+
+AR_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def ar_allreduce_noalloc(bufs, call: ar_call, stream=None):
+    """Allocation-free variant of ar_allreduce_ex (literal execution, scratch in a static device array)."""
+    _check(lib.ar_allreduce_noalloc(_ptrs(bufs), C.byref(call), _stream(stream)))
 
 
 def ar_workspace_bytes(call: ar_call) -> int:

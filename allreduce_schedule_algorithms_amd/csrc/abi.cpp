@@ -208,6 +208,24 @@ ar_status ar_allreduce(void* const* bufs, int32_t P, int64_t n, int32_t dtype, i
   return ar_allreduce_ex(bufs, &c, stream);
 }
 
+static_assert(AR_NOALLOC_SCRATCH_BYTES == ar::kScratchBytes, "scratch size");
+
+ar_status ar_allreduce_noalloc(void* const* bufs, const ar_call* call, void* stream) {
+  std::string err;
+  ar::Spec spec;
+  if (!to_spec(call, &spec, &err)) return fail(AR_INVALID_ARGUMENT, err);
+  if (call->exec != AR_EXEC_LITERAL)
+    return fail(AR_INVALID_ARGUMENT, "the allocation-free entry point runs the literal steps: exec must be AR_EXEC_LITERAL");
+  if (call->workspace) return fail(AR_INVALID_ARGUMENT, "the allocation-free entry point takes no workspace");
+  ar_status st = check_bufs(bufs, spec.P);
+  if (st != AR_OK) return st;
+  ar::RunResult r = ar::run_noalloc(bufs, spec, stream, call->start_event, call->stop_event);
+  t_hip = r.hip_error;
+  if (r.status) return fail(ar_status(r.status), r.message);
+  t_msg.clear();
+  return AR_OK;
+}
+
 ar_status ar_reduce_scatter(void* const* bufs, int32_t P, int64_t n, int32_t dtype, int32_t op, int32_t algo,
                             void* stream) {
   if (algo == AR_AHC) return fail(AR_INVALID_ARGUMENT, "AR_AHC has no reduce-scatter half here");

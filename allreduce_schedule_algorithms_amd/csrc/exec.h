@@ -23,6 +23,14 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
                         size_t workspace_bytes, void* stream, void* start_event = nullptr,
                         void* stop_event = nullptr);
 
+// The allocation-free variant of run_allreduce's literal execution: the
+// call's work records and workspace slots live in a static device array of
+// kScratchBytes per device (no allocation, no device tables). Calls on one
+// device share the array: overlapping calls race.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+RunResult run_noalloc(void* const* bufs, const Spec& spec, void* stream, void* start_event = nullptr,
+                      void* stop_event = nullptr);
+
 // Workspace a call needs (builds the schedule): the literal executor's slots
 // for AR_EXEC_LITERAL, and for fused calls whose replay does not fit (they run
 // the literal steps); 0 otherwise.

@@ -128,6 +128,8 @@ struct Plan {
   // small chunks
   std::vector<std::pair<int64_t, int64_t>> launches[2];
   DevBuf packed[2];
+  std::vector<LitWork> lit_work[2], lit_packed[2];  // literal: the records on the host
+  bool host_built[2] = {false, false};
   bool strided = false;  // fused: items are SItem (batches of short ranges)
   bool rows = false;      // fused: k_fused_rows (strided batches of one program shape)
   int rows_ref = 0;       // its reference range
@@ -466,14 +468,13 @@ bool fixed_shapes_enabled() {
   return on;
 }
 
-// Build the fused or literal item tables for one alignment mode.
-RunResult build_items(Plan& pl, bool vec) {
+// The literal executor's work records for one alignment mode, on the host.
+RunResult literal_tables(Plan& pl, bool vec) {
   const Schedule& s = *pl.s;
   const Spec& sp = s.spec;
   const int V = vec_width(sp.dtype);
   const int mode = vec ? 0 : 1;
-  std::vector<Item> items;
-  if (pl.exec == E_LITERAL) {
+  {
     // per launch (schedule step, then the finalize moves): the step's chunks,
     // each joint op with its op code inline
     if (s.nslots > 255) return RunResult{2, 0, "literal execution supports at most 255 slots"};
@@ -536,10 +537,31 @@ RunResult build_items(Plan& pl, bool vec) {
       }
       launches.push_back({w0, int64_t(work.size()) - w0});
     }
+    pl.lit_work[mode] = std::move(work);
+    pl.lit_packed[mode] = std::move(packed);
+    pl.launches[mode] = std::move(launches);
+    pl.host_built[mode] = true;
+  }
+  return RunResult{};
+}
+
+// Build the fused or literal item tables for one alignment mode.
+RunResult build_items(Plan& pl, bool vec) {
+  const Schedule& s = *pl.s;
+  const Spec& sp = s.spec;
+  const int V = vec_width(sp.dtype);
+  const int mode = vec ? 0 : 1;
+  std::vector<Item> items;
+  if (pl.exec == E_LITERAL) {
+    if (!pl.host_built[mode]) {
+      RunResult r = literal_tables(pl, vec);
+      if (r.status) return r;
+    }
+    const std::vector<LitWork>& work = pl.lit_work[mode];
+    const std::vector<LitWork>& packed = pl.lit_packed[mode];
     hipError_t e = upload(pl.items[mode], work);
     if (e == hipSuccess) e = upload(pl.packed[mode], packed);
     if (e != hipSuccess) return hip_fail(e, "uploading literal work");
-    pl.launches[mode] = launches;
     pl.nitems[mode] = int64_t(work.size());
     pl.built[mode] = true;
     return RunResult{};
@@ -976,6 +998,27 @@ RunResult release_cached() {
   return res;
 }
 
+// One launch per literal step (a long step is cut into launches of at most
+// launch_blocks() records: a step's records are independent).
+static RunResult literal_launches(const Plan& pl, int mode, const RankPtrs& ptrs, const WsDesc& wd,
+                                  const LitWork* work, const LitWork* packed, hipStream_t st, const Evs& ev) {
+  const Spec& spec = pl.s->spec;
+  const auto& lns = pl.launches[mode];
+  const int64_t cap = launch_blocks();
+  hipError_t e = hipSuccess;
+  for (size_t i = 0; i < lns.size(); ++i) {
+    for (int64_t off = 0; off < lns[i].second; off += cap) {
+      const bool last = i + 1 == lns.size() && off + cap >= lns[i].second;
+      const Evs ei{i == 0 && off == 0 ? ev.start : nullptr, last ? ev.stop : nullptr};
+      const int64_t cnt = std::min(cap, lns[i].second - off);
+      AR_DISPATCH(spec.dtype, spec.op,
+                  (e = launch_literal_t<DT, OPK>(cnt, ptrs, wd, work + lns[i].first + off, packed, st, ei)));
+      if (e != hipSuccess) return hip_fail(e, "launching a literal step");
+    }
+  }
+  return RunResult{};
+}
+
 RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* workspace, size_t workspace_bytes,
                         void* stream, void* start_event, void* stop_event) {
   RunResult res;
@@ -1074,20 +1117,8 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
     WsDesc wd{reinterpret_cast<char*>(ws), pl->slot_bytes, spec.P};
     const LitWork* work = reinterpret_cast<const LitWork*>(pl->items[mode].p);
     const LitWork* packed = reinterpret_cast<const LitWork*>(pl->packed[mode].p);
-    const auto& lns = pl->launches[mode];
-    if (lns.empty()) return mark_empty();
-    const int64_t cap = launch_blocks();
-    for (size_t i = 0; i < lns.size(); ++i) {
-      // a step's work records are independent: a long step is cut into launches of <= cap records
-      for (int64_t off = 0; off < lns[i].second; off += cap) {
-        const bool last = i + 1 == lns.size() && off + cap >= lns[i].second;
-        const Evs ei{i == 0 && off == 0 ? ev.start : nullptr, last ? ev.stop : nullptr};
-        const int64_t cnt = std::min(cap, lns[i].second - off);
-        AR_DISPATCH(spec.dtype, spec.op,
-                    (e = launch_literal_t<DT, OPK>(cnt, ptrs, wd, work + lns[i].first + off, packed, st, ei)));
-        if (e != hipSuccess) return hip_fail(e, "launching a literal step");
-      }
-    }
+    if (pl->launches[mode].empty()) return mark_empty();
+    return literal_launches(*pl, mode, ptrs, wd, work, packed, st, ev);
   } else {
     if (pl->nitems[mode] == 0) return mark_empty();
     const Item* items = reinterpret_cast<const Item*>(pl->items[mode].p);
@@ -1168,6 +1199,94 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
   }
   (void)V;
   return res;
+}
+
+// ----------------------------------------------------------------------------
+// allocation-free literal execution
+// ----------------------------------------------------------------------------
+// Device memory the allocation-free entry point uses in place of allocations:
+// one call's literal work records and its workspace slots. Every device holds
+// its own copy of the array from the library's load until the process ends;
+// host code reaches it only through the address hipGetSymbolAddress returns on
+// that device (the array's name is not a device address in host code).
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::map<int, char*>& scratch_ptrs() {
+  static std::map<int, char*> m;
+  return m;
+}
+}  // namespace
+
+RunResult run_noalloc(void* const* bufs, const Spec& spec, void* stream, void* start_event, void* stop_event) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const Evs ev{reinterpret_cast<hipEvent_t>(start_event), reinterpret_cast<hipEvent_t>(stop_event)};
+  auto mark_empty = [&]() -> RunResult {
+    hipError_t e = hipSuccess;
+    if (ev.start) e = hipEventRecord(ev.start, st);
+    if (e == hipSuccess && ev.stop) e = hipEventRecord(ev.stop, st);
+    return e == hipSuccess ? RunResult{} : hip_fail(e, "recording events");
+  };
+  if (spec.P <= 1 || spec.n == 0) return mark_empty();
+  RankPtrs ptrs;
+  std::memset(&ptrs, 0, sizeof(ptrs));
+  bool vec = true;
+  for (int p = 0; p < spec.P; ++p) {
+    ptrs.p[p] = bufs[p];
+    if (reinterpret_cast<uintptr_t>(bufs[p]) % 16) vec = false;
+  }
+  ptrs.div = float(spec.P);
+  const int mode = vec ? 0 : 1;
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  Plan* pl = nullptr;
+  char* base = nullptr;
+  size_t off_packed = 0, off_ws = 0;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    // the device's copy of the array: its address, taken once with the device current
+    auto it = scratch_ptrs().find(device);
+    if (it == scratch_ptrs().end()) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress");
+      it = scratch_ptrs().emplace(device, static_cast<char*>(p)).first;
+    }
+    base = it->second;
+    // a plan's host tables only: no device tables, no workspace allocation
+    RunResult res = get_plan(spec, E_LITERAL, device, &pl);
+    if (res.status) return res;
+    if (!pl->host_built[mode]) {
+      res = literal_tables(*pl, vec);
+      if (res.status) return res;
+    }
+    const size_t wb = pl->lit_work[mode].size() * sizeof(LitWork);
+    const size_t pb = pl->lit_packed[mode].size() * sizeof(LitWork);
+    off_packed = (wb + 255) / 256 * 256;
+    off_ws = off_packed + (pb + 255) / 256 * 256;
+    const size_t need = off_ws + pl->ws_bytes;
+    if (need > kScratchBytes) {
+      RunResult r;
+      r.status = 2;  // AR_UNSUPPORTED
+      r.message = "the call needs " + std::to_string(need) + " bytes of device scratch (work records and workspace "
+                  "slots); the allocation-free entry point holds at most " + std::to_string(kScratchBytes);
+      return r;
+    }
+  }
+  if (pl->launches[mode].empty()) return mark_empty();
+  // this call's records, ordered on the stream before its launches (the array
+  // keeps whatever the previous call on this device left; every workspace slot
+  // element is written by a step before any step reads it)
+  const auto& work = pl->lit_work[mode];
+  const auto& packed = pl->lit_packed[mode];
+  e = hipMemcpyAsync(base, work.data(), work.size() * sizeof(LitWork), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess && !packed.empty())
+    e = hipMemcpyAsync(base + off_packed, packed.data(), packed.size() * sizeof(LitWork), hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "copying the work records to the scratch array");
+  WsDesc wd{base + off_ws, pl->slot_bytes, spec.P};
+  return literal_launches(*pl, mode, ptrs, wd, reinterpret_cast<const LitWork*>(base),
+                          reinterpret_cast<const LitWork*>(base + off_packed), st, ev);
 }
 
 }  // namespace ar

@@ -208,6 +208,24 @@ ar_status ar_all_gather(void* const* bufs, int32_t P, int64_t n, int32_t dtype, 
 /* The collective of call->collective (an Allreduce by default) with every option of ar_call. */
 ar_status ar_allreduce_ex(void* const* bufs, const ar_call* call, void* stream);
 
+/* Allocation-free variant of ar_allreduce_ex, for callers that cannot allocate device memory
+ * (tight serving loops, harnesses that forbid allocation). The call runs its schedule step by
+ * step as AR_EXEC_LITERAL does, with the same kernels and bits, but its work records and
+ * workspace slots live in a device array the library declares statically: 64 MiB
+ * (AR_NOALLOC_SCRATCH_BYTES) per device, held from the library's load until the process ends.
+ * The call allocates nothing and builds no device tables: it copies the call's work records
+ * (host tables built on its first use) into the array with hipMemcpyAsync on `stream`, then
+ * enqueues the step launches. No element of the array needs clearing: each step writes a slot
+ * before any step reads it.
+ * Requirements: call->exec must be AR_EXEC_LITERAL and call->workspace NULL; the records and
+ * slots must fit the array (ar_workspace_bytes gives the slots' share), else AR_UNSUPPORTED and
+ * nothing is enqueued. Every call on one device shares that device's array, which keeps the last
+ * call's contents: calls that overlap on one device (different streams, or threads) race and
+ * corrupt each other's results; serialize them. Not meant for stream capture (the copies read
+ * host memory). Other arguments, events and errors as ar_allreduce_ex. */
+#define AR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ar_status ar_allreduce_noalloc(void* const* bufs, const ar_call* call, void* stream);
+
 /* Workspace bytes a call needs: the literal workspace slots for AR_EXEC_LITERAL, and for
  * AR_EXEC_FUSED calls whose schedule runs the literal steps (see ar_exec); 0 otherwise.
  * Builds (and caches) the schedule; returns its validation error for invalid calls. */
