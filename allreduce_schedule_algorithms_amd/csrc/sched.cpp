@@ -124,25 +124,25 @@ static void gen_direct(int P, Exprs& ex, Logical& lg) {
 }
 
 // Ring reduce-scatter + all-gather (all-reduce blog page, "The ring
-// algorithm"; generalized-Allreduce paper eqs. (14)-(16)).
+// algorithm"; generalized-Allreduce paper eqs. (14)-(16)). P parts, each
+// making two laps of the ring, one hop r -> r + 1 per step for all parts at
+// once: on the combining lap part k starts at rank k and every rank it reaches
+// adds its own copy, so after P - 1 hops rank k - 1 holds the complete part;
+// on the copying lap it leaves that rank and overwrites each copy it reaches.
+static void ring_lap(BufGen& g, int P, int first_offset, int kind) {
+  for (int t = 0; t < P - 1; ++t) {
+    g.begin();
+    for (int k = 0; k < P; ++k) {
+      const int at = ((k + first_offset + t) % P + P) % P;  // part k's position before this hop
+      g.msg(kind, at, (at + 1) % P, k, k + 1);
+    }
+    g.end();
+  }
+}
 static void gen_ring(int P, Exprs& ex, Logical& lg) {
   BufGen g(P, P, ex, lg);
-  for (int t = 0; t < P - 1; ++t) {
-    g.begin();
-    for (int r = 0; r < P; ++r) {
-      int k = ((r - t) % P + P) % P;
-      g.msg(K_REDUCE, r, (r + 1) % P, k, k + 1);
-    }
-    g.end();
-  }
-  for (int t = 0; t < P - 1; ++t) {
-    g.begin();
-    for (int r = 0; r < P; ++r) {
-      int k = ((r + 1 - t) % P + P) % P;
-      g.msg(K_COPY, r, (r + 1) % P, k, k + 1);
-    }
-    g.end();
-  }
+  ring_lap(g, P, 0, K_REDUCE);   // part k starts at rank k
+  ring_lap(g, P, -1, K_COPY);    // and leaves its owner, rank k - 1
 }
 
 // Non-power-of-two preparation / finalization (generalized-Allreduce paper,
@@ -204,29 +204,16 @@ static void gen_rh_rd(int P, Exprs& ex, Logical& lg) {
 }
 
 // Reduce-scatter and all-gather halves (part q belongs to rank q; P parts).
-// Ring: the ring's phases with part labels rotated by one, so that part q
-// travels q+1, q+2, ..., q and completes on arrival at rank q.
+// Ring: the two laps with part q's start moved by one, so that the combining
+// lap of part q starts at rank q + 1 and ends at its owner q, and the copying
+// lap starts from q.
 static void gen_ring_rs(int P, Exprs& ex, Logical& lg) {
   BufGen g(P, P, ex, lg);
-  for (int t = 0; t < P - 1; ++t) {
-    g.begin();
-    for (int r = 0; r < P; ++r) {
-      int k = ((r - t - 1) % P + P) % P;
-      g.msg(K_REDUCE, r, (r + 1) % P, k, k + 1);
-    }
-    g.end();
-  }
+  ring_lap(g, P, 1, K_REDUCE);
 }
 static void gen_ring_ag(int P, Exprs& ex, Logical& lg) {
   BufGen g(P, P, ex, lg);
-  for (int t = 0; t < P - 1; ++t) {
-    g.begin();
-    for (int r = 0; r < P; ++r) {
-      int k = ((r - t) % P + P) % P;
-      g.msg(K_COPY, r, (r + 1) % P, k, k + 1);
-    }
-    g.end();
-  }
+  ring_lap(g, P, 0, K_COPY);
 }
 // Direct: the one-root fold (rank order), then rank 0 hands part q to rank q;
 // all-gather: every rank sends its part to every other rank in one step.

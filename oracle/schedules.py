@@ -53,18 +53,27 @@ def _ring(net: Net):
     case of the straightforward algorithm, generalized-Allreduce paper,
     eqs. (14)-(16) and Fig. 5).
 
-    P parts by the ceil split. Reduce-scatter: in step t = 0..P-2 every rank
-    r passes part (r - t) mod P to its right neighbour r + 1, which adds it
-    into its own copy. Afterwards rank r owns the full sum of part (r + 1)
-    mod P. All-gather: in step t rank r passes part (r + 1 - t) mod P to
-    r + 1, which overwrites its copy.
+    The data is cut into P parts (ceil split) and every part makes two laps of
+    the ring, one hop r -> r + 1 per step for all parts at once. Reduce lap:
+    part k sets out from rank k; each rank it reaches adds its own copy of the
+    part, so after P - 1 hops it rests at rank k - 1 holding every rank's
+    contribution (that rank owns part k). Gather lap: the finished part k
+    leaves its owner and hops on, each rank it reaches overwriting its copy,
+    until after P - 1 more hops every rank has it.
     """
     P, n = net.P, net.n
     parts = partition(n, P)
-    for t in range(P - 1):
-        net.step([(r, (r + 1) % P, *parts[(r - t) % P], REDUCE) for r in range(P)])
-    for t in range(P - 1):
-        net.step([(r, (r + 1) % P, *parts[(r + 1 - t) % P], COPY) for r in range(P)])
+
+    def lap(first_holder, kind):
+        for t in range(P - 1):
+            msgs = []
+            for k in range(P):
+                at = (first_holder(k) + t) % P  # where part k is before this hop
+                msgs.append((at, (at + 1) % P, *parts[k], kind))
+            net.step(msgs)
+
+    lap(lambda k: k, REDUCE)            # part k starts at its first contributor, rank k
+    lap(lambda k: (k - 1) % P, COPY)    # and leaves its owner, rank k - 1
 
 
 # --------------------------------------------------------------------------

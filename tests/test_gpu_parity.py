@@ -275,6 +275,25 @@ def test_ahc_bf16_192_ranks_sampled():
     assert np.array_equal(bits(got[:, idx]), bits(want))
 
 
+def test_ring_halving_generalized_on_192_bf16_ranks_sampled():
+    # the ring, recursive halving + doubling (128 ranks after folding in the 64
+    # excess ones) and the generalized algorithm over Z_192 (r = 0, and r = 2)
+    # on the 192-rank 2^20 bf16 workload: sampled offsets (every part boundary)
+    # against the oracle, every element against the fp64 tolerance
+    x = inputs.workload("ahc_bf16")
+    P, n = x.shape
+    idx = inputs.sample_indices(n, P, count=2048)
+    xs = np.ascontiguousarray(x[:, idx])
+    for algo, r, ex in (("ring", 0, "fused"), ("rh_rd", 0, "fused"), ("generalized", 0, "fused"),
+                        ("generalized", 2, "fused"), ("ring", 0, "literal"), ("rh_rd", 0, "literal")):
+        got = gpu_allreduce(x, algo, "bf16", "sum", r, ex)
+        want = oracle.allreduce(xs, algo, "bf16", "sum", knob=r, n=n, idx=idx)
+        assert np.array_equal(bits(got[:, idx]), bits(want)), (algo, r, ex)
+        check_tol(got, x, "bf16")
+        if r == 0:
+            assert (got == got[:1]).all(), (algo, ex)  # one tree per part
+
+
 # --------------------------------------------------------------------------
 # model-driven choice: the call runs the schedule the oracle's model picks
 # --------------------------------------------------------------------------

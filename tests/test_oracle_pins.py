@@ -471,12 +471,14 @@ def test_planted_ring_direction_is_caught(monkeypatch):
     orig = sch._ring
 
     def bad_ring(net):
+        # the reduce lap runs against the ring direction (part k hops k -> k - 1)
+        # while the gather lap still starts from rank k - 1 and runs with it
         P, n = net.P, net.n
         parts = partition(n, P)
         for t in range(P - 1):
-            net.step([(r, (r + 1) % P, *parts[(r + t) % P], oracle.net.REDUCE) for r in range(P)])
+            net.step([((k - t) % P, (k - t - 1) % P, *parts[k], oracle.net.REDUCE) for k in range(P)])
         for t in range(P - 1):
-            net.step([(r, (r + 1) % P, *parts[(r + 1 - t) % P], oracle.net.COPY) for r in range(P)])
+            net.step([((k - 1 + t) % P, (k + t) % P, *parts[k], oracle.net.COPY) for k in range(P)])
     monkeypatch.setattr(sch, "_ring", bad_ring)
     x = inputs.make("int32", 5, 20, seed=1)
     y = run(x, "ring", "int32", "sum")
