@@ -25,14 +25,32 @@ thread_local int32_t t_hip = 0;
 
 // M 16-byte vectors per thread and rank at vector offsets v, v + kThreads, ...
 // inside the block's run of kThreads * M vectors (every wave-level access is
-// 1 KB contiguous). Ranks go kBatch at a time: all loads of a batch are issued
-// before its stores, so 2 * kBatch * M accesses per thread are in flight.
-template <int M>
-__global__ __launch_bounds__(kThreads) void k_probe_streams(Bufs b, int P, int64_t nvec) {
+// 1 KB contiguous). NP > 0: compiled for exactly NP ranks, every rank loaded
+// before any store (the direct kernel's order); NP == 0: any P, ranks kBatch
+// at a time, the loads of a batch issued before its stores.
+// `key` is 0 at run time; the stores write the loaded data XOR key, so the
+// compiler cannot drop them as stores of the value just loaded from the same
+// address.
+template <int M, int NP>
+__global__ __launch_bounds__(kThreads) void k_probe_streams(Bufs b, int P, int64_t nvec, uint32_t key) {
   const int64_t v0 = int64_t(blockIdx.x) * kThreads * M + threadIdx.x;
   bool ok[M];
 #pragma unroll
   for (int j = 0; j < M; ++j) ok[j] = v0 + int64_t(j) * kThreads < nvec;
+  if constexpr (NP > 0) {
+    u32x4 r[NP][M];
+#pragma unroll
+    for (int k = 0; k < NP; ++k)
+#pragma unroll
+      for (int j = 0; j < M; ++j)
+        if (ok[j]) r[k][j] = __builtin_nontemporal_load(b.p[k] + v0 + int64_t(j) * kThreads);
+#pragma unroll
+    for (int k = 0; k < NP; ++k)
+#pragma unroll
+      for (int j = 0; j < M; ++j)
+        if (ok[j]) __builtin_nontemporal_store(r[k][j] ^ key, b.p[k] + v0 + int64_t(j) * kThreads);
+    return;
+  }
   for (int base = 0; base < P; base += kBatch) {
     u32x4 r[kBatch][M];
 #pragma unroll
@@ -44,13 +62,14 @@ __global__ __launch_bounds__(kThreads) void k_probe_streams(Bufs b, int P, int64
     for (int k = 0; k < kBatch; ++k)
 #pragma unroll
       for (int j = 0; j < M; ++j)
-        if (base + k < P && ok[j]) __builtin_nontemporal_store(r[k][j], b.p[base + k] + v0 + int64_t(j) * kThreads);
+        if (base + k < P && ok[j])
+          __builtin_nontemporal_store(r[k][j] ^ key, b.p[base + k] + v0 + int64_t(j) * kThreads);
   }
 }
 
 template <int M>
 __global__ __launch_bounds__(kThreads) void k_probe_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                         int64_t nvec) {
+                                                         int64_t nvec, uint32_t key) {
   const int64_t v0 = int64_t(blockIdx.x) * kThreads * M + threadIdx.x;
   u32x4 r[M];
 #pragma unroll
@@ -58,18 +77,28 @@ __global__ __launch_bounds__(kThreads) void k_probe_copy(const u32x4* __restrict
     if (v0 + int64_t(j) * kThreads < nvec) r[j] = __builtin_nontemporal_load(src + v0 + int64_t(j) * kThreads);
 #pragma unroll
   for (int j = 0; j < M; ++j)
-    if (v0 + int64_t(j) * kThreads < nvec) __builtin_nontemporal_store(r[j], dst + v0 + int64_t(j) * kThreads);
+    if (v0 + int64_t(j) * kThreads < nvec) __builtin_nontemporal_store(r[j] ^ key, dst + v0 + int64_t(j) * kThreads);
+}
+
+template <int M, int NP>
+void streams(const Bufs& b, int P, int64_t nvec, int64_t blocks, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  hipExtLaunchKernelGGL((k_probe_streams<M, NP>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, e0, e1, 0, b, P, nvec,
+                        0u);
 }
 
 template <int M>
 hipError_t launch(const Bufs& b, int P, int64_t nvec, int kind, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const int64_t blocks = (nvec + int64_t(kThreads) * M - 1) / (int64_t(kThreads) * M);
   if (blocks > (int64_t(1) << 24) - 1) return hipErrorInvalidValue;
-  if (kind == AR_PROBE_STREAMS)
-    hipExtLaunchKernelGGL((k_probe_streams<M>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, e0, e1, 0, b, P, nvec);
-  else
+  if (kind == AR_PROBE_STREAMS) {
+    switch (P) {  // the rank counts of the large workloads, compiled exactly
+      case 7: streams<M, 7>(b, P, nvec, blocks, st, e0, e1); break;
+      case 8: streams<M, 8>(b, P, nvec, blocks, st, e0, e1); break;
+      default: streams<M, 0>(b, P, nvec, blocks, st, e0, e1); break;
+    }
+  } else
     hipExtLaunchKernelGGL((k_probe_copy<M>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, e0, e1, 0, b.p[0], b.p[1],
-                          nvec);
+                          nvec, 0u);
   return hipGetLastError();
 }
 

@@ -13,8 +13,10 @@
  *                    (in place, 2P streams of `bytes` each way per rank). Element
  *                    offsets are laid out like the direct kernel's: a thread takes
  *                    `vectors_per_thread` 16-byte vectors per rank, block-
- *                    interleaved so every wave-level access covers 1 KB; ranks
- *                    go 8 at a time (load 8, store 8). Bytes moved: 2 P bytes.
+ *                    interleaved so every wave-level access covers 1 KB. For 7 and
+ *                    8 ranks the kernel is compiled for P and loads every rank
+ *                    before any store; other P go 8 ranks at a time (load 8,
+ *                    store 8). Bytes moved: 2 P bytes.
  *  AR_PROBE_COPY     bufs[1] = bufs[0] over `bytes` (P must be 2): one read and
  *                    one write stream. Bytes moved: 2 bytes.
  *
