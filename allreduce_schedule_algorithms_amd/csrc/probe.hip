@@ -67,6 +67,36 @@ __global__ __launch_bounds__(kThreads) void k_probe_streams(Bufs b, int P, int64
   }
 }
 
+// The smallest one-pass Allreduce kernel: fp32 sum of NP ranks (compiled for
+// 7 or 8), written back to every rank; M vectors per thread and rank laid out
+// as above, all loads before any store, no work items, no rank table.
+template <int M, int NP>
+__global__ __launch_bounds__(kThreads) void k_probe_fold(Bufs b, int64_t nvec) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int64_t v0 = int64_t(blockIdx.x) * kThreads * M + threadIdx.x;
+  bool ok[M];
+#pragma unroll
+  for (int j = 0; j < M; ++j) ok[j] = v0 + int64_t(j) * kThreads < nvec;
+  f32x4 x[NP][M];
+#pragma unroll
+  for (int k = 0; k < NP; ++k)
+#pragma unroll
+    for (int j = 0; j < M; ++j)
+      if (ok[j]) x[k][j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(b.p[k] + v0 + int64_t(j) * kThreads));
+  f32x4 acc[M];
+#pragma unroll
+  for (int j = 0; j < M; ++j) acc[j] = x[0][j];
+#pragma unroll
+  for (int k = 1; k < NP; ++k)
+#pragma unroll
+    for (int j = 0; j < M; ++j) acc[j] = acc[j] + x[k][j];
+#pragma unroll
+  for (int k = 0; k < NP; ++k)
+#pragma unroll
+    for (int j = 0; j < M; ++j)
+      if (ok[j]) __builtin_nontemporal_store(acc[j], reinterpret_cast<f32x4*>(b.p[k] + v0 + int64_t(j) * kThreads));
+}
+
 template <int M>
 __global__ __launch_bounds__(kThreads) void k_probe_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                          int64_t nvec, uint32_t key) {
@@ -96,6 +126,11 @@ hipError_t launch(const Bufs& b, int P, int64_t nvec, int kind, hipStream_t st, 
       case 8: streams<M, 8>(b, P, nvec, blocks, st, e0, e1); break;
       default: streams<M, 0>(b, P, nvec, blocks, st, e0, e1); break;
     }
+  } else if (kind == AR_PROBE_FOLD) {
+    if (P == 7)
+      hipExtLaunchKernelGGL((k_probe_fold<M, 7>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, e0, e1, 0, b, nvec);
+    else
+      hipExtLaunchKernelGGL((k_probe_fold<M, 8>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, e0, e1, 0, b, nvec);
   } else
     hipExtLaunchKernelGGL((k_probe_copy<M>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, e0, e1, 0, b.p[0], b.p[1],
                           nvec, 0u);
@@ -109,8 +144,9 @@ extern "C" {
 int32_t ar_probe_stream(void* const* bufs, int32_t P, int64_t bytes, int32_t kind, int32_t vectors_per_thread,
                         void* stream, void* start_event, void* stop_event) {
   if (!bufs || P < 1 || P > kMaxRanks || bytes <= 0 || bytes % 16) return 1;
-  if (kind != AR_PROBE_STREAMS && kind != AR_PROBE_COPY) return 1;
+  if (kind != AR_PROBE_STREAMS && kind != AR_PROBE_COPY && kind != AR_PROBE_FOLD) return 1;
   if (kind == AR_PROBE_COPY && P != 2) return 1;
+  if (kind == AR_PROBE_FOLD && P != 7 && P != 8) return 1;
   Bufs b;
   std::memset(&b, 0, sizeof(b));
   for (int p = 0; p < P; ++p) {

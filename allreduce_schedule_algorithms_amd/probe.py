@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(_HERE, "libar_probe.so")
 
 AR_PROBE_STREAMS = 0
 AR_PROBE_COPY = 1
+AR_PROBE_FOLD = 2
 
 SIGNATURES = {
     "ar_probe_stream": (C.c_int32, [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int32, C.c_int32,

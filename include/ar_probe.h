@@ -19,6 +19,12 @@
  *                    store 8). Bytes moved: 2 P bytes.
  *  AR_PROBE_COPY     bufs[1] = bufs[0] over `bytes` (P must be 2): one read and
  *                    one write stream. Bytes moved: 2 bytes.
+ *  AR_PROBE_FOLD     the smallest one-pass Allreduce kernel: the fp32 sum of the
+ *                    P ranks (P = 7 or 8, compiled for P) written back to every
+ *                    rank, every load before any store, with no work items and
+ *                    no rank table: the 2P streams of the direct kernel without
+ *                    the library's generality. Bytes moved: 2 P bytes. Its
+ *                    results are sums, not the ranks' data.
  *
  * Arguments: bufs is a host array of P device pointers, each 16-byte aligned and
  * holding at least `bytes` bytes; `bytes` must be a positive multiple of 16.
@@ -37,7 +43,7 @@
 extern "C" {
 #endif
 
-typedef enum { AR_PROBE_STREAMS = 0, AR_PROBE_COPY = 1 } ar_probe_kind;
+typedef enum { AR_PROBE_STREAMS = 0, AR_PROBE_COPY = 1, AR_PROBE_FOLD = 2 } ar_probe_kind;
 
 int32_t ar_probe_stream(void* const* bufs, int32_t P, int64_t bytes, int32_t kind, int32_t vectors_per_thread,
                         void* stream, void* start_event, void* stop_event);
