@@ -438,6 +438,7 @@ bool dag_table(const Schedule& s, const DagPlan& d, std::vector<uint8_t>* t) {
   for (int64_t o = 0; o < sp.n; ++o)
     if (!seen[size_t(o)]) return false;
   std::memcpy(t->data() + moff, d.maps.data(), size_t(R * sp.P));
+  t->resize((t->size() + 3) / 4 * 4, 0);  // the kernel copies it to LDS in 4-byte words
   return true;
 }
 
@@ -578,7 +579,7 @@ RunResult build_items(Plan& pl, bool vec) {
         if (e != hipSuccess) return hip_fail(e, "uploading the renaming table");
       }
       pl.dag_vals[mode] = int(vals1 / 4);
-      pl.dag_lds[mode] = vals1 + progb + size_t(sp.P) * sizeof(void*);
+      pl.dag_lds[mode] = vals1 + progb + size_t(sp.P) * sizeof(void*) + pl.dag_tab.size();
       pl.nitems[mode] = 1;  // launched by element count
       pl.built[mode] = true;
       return RunResult{};
@@ -732,7 +733,9 @@ void choose_kernel(Plan& pl) {
     }
     int64_t max_len = 0;
     for (const FusedRange& r : s.ranges) max_len = std::max(max_len, r.len);
-    pl.dag_shared = pl.dp.shared && s.ranges.size() > 1 && max_len < 4 * kDagLanes && dag_table(s, pl.dp, &pl.dag_tab);
+    // the renaming table goes to LDS: only short instances (n <= 4096) share one program
+    pl.dag_shared = pl.dp.shared && s.ranges.size() > 1 && max_len < 4 * kDagLanes && s.spec.n <= 4096 &&
+                    dag_table(s, pl.dp, &pl.dag_tab);
     if (pl.dp.shared && s.ranges.size() > 1 && !pl.dag_shared && !dag_plan(s, &pl.dp, &err, false)) {
       // long ranges run per-range work items, each with its own range's program
       pl.kernel = K_LITERAL;
@@ -744,7 +747,8 @@ void choose_kernel(Plan& pl) {
       const int32_t* w = pl.dp.words.data() + pl.dp.offsets[r];
       pl.dag_words = std::max(pl.dag_words, 5 + w[1] + w[2] + 1 + w[3] + w[4]);
     }
-    const size_t need = size_t(pl.dp.S) * kDagLanes * 4 + (pl.dag_shared ? size_t(s.spec.P) * sizeof(void*) : 0);
+    const size_t need = size_t(pl.dp.S) * kDagLanes * 4 +
+                        (pl.dag_shared ? size_t(s.spec.P) * sizeof(void*) + pl.dag_tab.size() : 0);
     if (need > pl.lds_limit) {
       pl.kernel = K_LITERAL;
       pl.fallback = "the DAG replay needs " + std::to_string(need) + " bytes of LDS per workgroup (" +
@@ -1137,7 +1141,8 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
       AR_DISPATCH(spec.dtype, spec.op,
                   (e = launch_fused_dag_t<DT, OPK>(pl->dag_shared, threads, pl->dag_lds[mode], nit, ptrs, ditems, prog,
                                                    reinterpret_cast<const uint8_t*>(pl->dtab.p), total, int(spec.n),
-                                                   spec.P, pl->dag_vals[mode], cap, st, ev)));
+                                                   spec.P, pl->dag_vals[mode], int(pl->s->ranges.size()), cap, st,
+                                                   ev)));
       if (e != hipSuccess) return hip_fail(e, "launching the DAG replay");
       return res;
     }

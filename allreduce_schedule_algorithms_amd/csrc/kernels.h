@@ -999,29 +999,36 @@ __device__ __forceinline__ void dag_body(const RankPtrs& ptrs, ProgPtr w, int64_
 // offset. One program for every range (SHARED): workgroup b takes elements
 // first + b * kDagLanes onward, one per lane; `tab` holds the range of each of
 // the n offsets of an instance (padded to 8 bytes), then per range a row of P
-// bytes renaming the program's ranks to the range's. LDS: S slots of kDagLanes
-// values (of 4 words if any item has vectors; `vals_words` words in all), then
-// (SHARED) the P buffer pointers.
+// bytes renaming the program's ranks to the range's (tab_rows rows; the table is
+// padded to a multiple of 4 bytes). LDS: S slots of kDagLanes values (of 4
+// words if any item has vectors; `vals_words` words in all), then (SHARED) the
+// P buffer pointers and the table.
 template <int DT, int OPK, bool SHARED>
 __global__ __launch_bounds__(1024) void k_fused_dag(RankPtrs ptrs, const Item* __restrict__ items,
                                                     const int32_t* __restrict__ prog, const uint8_t* __restrict__ tab,
                                                     int64_t first, int64_t total, int32_t n, int32_t P,
-                                                    int32_t vals_words) {
+                                                    int32_t vals_words, int32_t tab_rows) {
   extern __shared__ u32x4 dag_lds[];
   uint32_t* vals = reinterpret_cast<uint32_t*>(dag_lds);
   if constexpr (SHARED) {
+    // the buffer pointers and the renaming table (range of each offset, then
+    // the rows) copied to LDS once: a lane's rank lookups are LDS reads
     void** lptr = reinterpret_cast<void**>(vals + vals_words);
+    uint8_t* ltab = reinterpret_cast<uint8_t*>(lptr + P);
+    const int tab_words = ((n + 7) / 8 * 8 + tab_rows * P + 3) / 4;
     if (threadIdx.x == 0)
       for (int x = 0; x < P; ++x) lptr[x] = ptrs.p[x];
+    for (int i = int(threadIdx.x); i < tab_words; i += int(blockDim.x))
+      reinterpret_cast<uint32_t*>(ltab)[i] = reinterpret_cast<const uint32_t*>(tab)[i];
     __syncthreads();
     const int64_t pos0 = first + int64_t(blockIdx.x) * kDagLanes;
     const int64_t left = total - pos0;
     const int cnt = int(left < kDagLanes ? left : kDagLanes);
     const int lane = int(threadIdx.x) & (kDagLanes - 1);
-    const uint8_t* row = tab;
+    const uint8_t* row = ltab;
     if (lane < cnt) {
       const int o = int((pos0 + lane) % n);
-      row = tab + (n + 7) / 8 * 8 + int(tab[o]) * P;
+      row = ltab + (n + 7) / 8 * 8 + int(ltab[o]) * P;
     }
     dag_body<DT, OPK, 1, true>(ptrs, as_prog(prog), pos0, cnt, lptr, row, vals);
   } else {

@@ -57,7 +57,7 @@ hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& w
 template <int DT, int OPK>
 hipError_t launch_fused_dag_t(bool shared, int threads, size_t lds, int64_t nitems, const RankPtrs& ptrs,
                               const Item* items, const int32_t* prog, const uint8_t* tab, int64_t total, int n,
-                              int P, int vals_words, int64_t max_blocks, hipStream_t st, Evs ev);
+                              int P, int vals_words, int tab_rows, int64_t max_blocks, hipStream_t st, Evs ev);
 template <int DT, int OPK>
 hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total, int64_t max_blocks, hipStream_t st,
                            Evs ev);
@@ -323,7 +323,7 @@ hipError_t launch_literal_t(int64_t nwork, const RankPtrs& ptrs, const WsDesc& w
 template <int DT, int OPK, bool SH>
 hipError_t dag_d(int threads, size_t lds, int64_t nitems, const RankPtrs& ptrs, const Item* items,
                  const int32_t* prog, const uint8_t* tab, int64_t total, int n, int P, int vals_words,
-                 int64_t max_blocks, hipStream_t st, Evs ev) {
+                 int tab_rows, int64_t max_blocks, hipStream_t st, Evs ev) {
   static bool raised = false;  // LDS beyond 64 KB per workgroup needs the kernel's attribute raised once
   if (lds > 65536 && !raised) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fused_dag<DT, OPK, SH>),
@@ -337,7 +337,7 @@ hipError_t dag_d(int threads, size_t lds, int64_t nitems, const RankPtrs& ptrs, 
     const Evs ei{b0 == 0 ? ev.start : nullptr, b0 + cnt >= blocks ? ev.stop : nullptr};
     hipExtLaunchKernelGGL((k_fused_dag<DT, OPK, SH>), dim3(unsigned(cnt)), dim3(unsigned(threads)), uint32_t(lds), st,
                           ei.start, ei.stop, 0, ptrs, SH ? items : items + b0, prog, tab, b0 * kDagLanes, total,
-                          int32_t(n), int32_t(P), int32_t(vals_words));
+                          int32_t(n), int32_t(P), int32_t(vals_words), int32_t(tab_rows));
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -347,12 +347,12 @@ hipError_t dag_d(int threads, size_t lds, int64_t nitems, const RankPtrs& ptrs, 
 template <int DT, int OPK>
 hipError_t launch_fused_dag_t(bool shared, int threads, size_t lds, int64_t nitems, const RankPtrs& ptrs,
                               const Item* items, const int32_t* prog, const uint8_t* tab, int64_t total, int n,
-                              int P, int vals_words, int64_t max_blocks, hipStream_t st, Evs ev) {
+                              int P, int vals_words, int tab_rows, int64_t max_blocks, hipStream_t st, Evs ev) {
   if (shared)
-    return dag_d<DT, OPK, true>(threads, lds, nitems, ptrs, items, prog, tab, total, n, P, vals_words, max_blocks, st,
-                                ev);
-  return dag_d<DT, OPK, false>(threads, lds, nitems, ptrs, items, prog, tab, total, n, P, vals_words, max_blocks, st,
-                               ev);
+    return dag_d<DT, OPK, true>(threads, lds, nitems, ptrs, items, prog, tab, total, n, P, vals_words, tab_rows,
+                                max_blocks, st, ev);
+  return dag_d<DT, OPK, false>(threads, lds, nitems, ptrs, items, prog, tab, total, n, P, vals_words, tab_rows,
+                               max_blocks, st, ev);
 }
 
 // One launch per run of at most max_blocks workgroups; each launch gets the
@@ -439,7 +439,7 @@ hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total,
   template hipError_t launch_literal_t<DT, OPK>(int64_t, const RankPtrs&, const WsDesc&, const LitWork*,    \
                                                 const LitWork*, hipStream_t, Evs);                          \
   template hipError_t launch_fused_dag_t<DT, OPK>(bool, int, size_t, int64_t, const RankPtrs&, const Item*,  \
-                                                  const int32_t*, const uint8_t*, int64_t, int, int, int,     \
+                                                  const int32_t*, const uint8_t*, int64_t, int, int, int, int,\
                                                   int64_t, hipStream_t, Evs);                                 \
   template hipError_t launch_direct_t<DT, OPK>(bool, const RankPtrs&, int, int64_t, int64_t, hipStream_t, Evs);
 #endif  // AR_LAUNCH_DEFINITIONS

@@ -1101,10 +1101,22 @@ bool dag_renaming(const DagProgram& a, const DagProgram& b, int P, std::vector<i
   };
   for (size_t k = 0; k < a.leaves.size(); ++k)
     if (!bind(a.leaves[k], b.leaves[k])) return false;
+  // outputs are a set of (slot, rank): a's, renamed, must be b's in any order
+  std::vector<std::pair<int, int>> oa, ob;
   for (size_t k = 0; k < a.outs.size(); ++k) {
-    if ((a.outs[k] >> 16) != (b.outs[k] >> 16)) return false;
-    if (!bind(a.outs[k] & 0xffff, b.outs[k] & 0xffff)) return false;
+    const int ra = a.outs[k] & 0xffff;
+    if ((*map)[size_t(ra)] < 0) {  // a rank that is no leaf: pair it with b's output of the same slot
+      int y = -1;
+      for (size_t j = 0; j < b.outs.size() && y < 0; ++j)
+        if ((b.outs[j] >> 16) == (a.outs[k] >> 16) && inv[size_t(b.outs[j] & 0xffff)] < 0) y = b.outs[j] & 0xffff;
+      if (y < 0 || !bind(ra, y)) return false;
+    }
+    oa.push_back({a.outs[k] >> 16, (*map)[size_t(ra)]});
+    ob.push_back({b.outs[k] >> 16, b.outs[k] & 0xffff});
   }
+  std::sort(oa.begin(), oa.end());
+  std::sort(ob.begin(), ob.end());
+  if (oa != ob) return false;
   // complete the permutation with the ranks neither program names
   int free_y = 0;
   for (int x = 0; x < P; ++x) {

@@ -138,9 +138,10 @@ struct DagProgram {
 };
 constexpr int kDagMaxSlots = 1024;
 bool compile_dag(const int32_t* range_words, int P, DagProgram* out, std::string* err);
-// Whether b equals a with every leaf and output rank renamed: fills map with
-// a's rank -> b's rank (ranks a does not use map to themselves if free, else
-// to an unused rank) so that map is a permutation.
+// Whether b equals a with every leaf and output rank renamed (leaves in order;
+// outputs as a set of (slot, rank)): fills map with a's rank -> b's rank (ranks
+// a does not use map to themselves if free, else to an unused rank) so that map
+// is a permutation.
 bool dag_renaming(const DagProgram& a, const DagProgram& b, int P, std::vector<int>* map);
 
 // DAG programs of a whole fused program. Shared: every range's program is the
