@@ -328,9 +328,10 @@ bool strided_items(const Schedule& s) {
 // one tree per range, and every range's program is the reference range's (the
 // first non-empty one) with its leaf ranks renamed, with the same combination
 // counts and the same output ranks. Fills *t
-// with the range of each offset of an instance (n bytes, padded to 8), then per
-// range a row of P bytes mapping a leaf rank of the reference range to the
-// range's own, and *ref with the reference range's index.
+// with the range of each offset of an instance (n bytes, padded to 8), then the
+// renaming map[rank][range] (R bytes per leaf rank of the reference range: the
+// rank it stands for in each range; the lanes of one lookup read neighbouring
+// bytes), and *ref with the reference range's index.
 constexpr int64_t kRowsMaxTable = 4096;  // limit on R x (P | 1) and on n (LDS)
 bool rows_table(const Schedule& s, std::vector<uint8_t>* t, int* ref) {
   const Spec& sp = s.spec;
@@ -379,20 +380,22 @@ bool rows_table(const Schedule& s, std::vector<uint8_t>* t, int* ref) {
       a += 2 + 2 * nl + no;
       b += 2 + 2 * nl + no;
     }
-    uint8_t* row = t->data() + moff + r * P;
-    for (int64_t x = 0; x < P; ++x) row[x] = uint8_t(map[size_t(x)] < 0 ? 0 : map[size_t(x)]);
+    for (int64_t x = 0; x < P; ++x) (*t)[size_t(moff + x * R + r)] = uint8_t(map[size_t(x)] < 0 ? 0 : map[size_t(x)]);
   }
   t->resize((t->size() + 7) / 8 * 8, 0);  // k_fused_rows_vec copies it in 8-byte runs
   return true;
 }
 
 // Whether a k_fused_rows call runs k_fused_rows_vec for its whole vectors:
-// 4-byte elements, at most 32 ranks, aligned buffers and more than
-// kTinyElements elements.
+// 4-byte elements, at most 32 ranks, aligned buffers, more than
+// kTinyElements elements, and a reference tree whose result goes to all P ranks
+// (an Allreduce's).
 constexpr int kRowsVecMaxRanks = 32;
-bool rows_vec(const Schedule& s) {
+bool rows_vec(const Schedule& s, int ref) {
   const Spec& sp = s.spec;
-  return vec_width(sp.dtype) == 4 && sp.P <= kRowsVecMaxRanks && sp.n * sp.batch > kTinyElements;
+  if (vec_width(sp.dtype) != 4 || sp.P > kRowsVecMaxRanks || sp.n * sp.batch <= kTinyElements || ref < 0) return false;
+  const int32_t* w = s.prog.data() + s.ranges[size_t(ref)].prog;
+  return w[0] == 1 && w[2] == sp.P;
 }
 
 // LDS one workgroup may allocate on a device (gfx950: 160 KB); host-only plans
@@ -768,7 +771,7 @@ registers:
                   " trees, with a stack of at most 8)";
     return;
   }
-  if (pl.rows) pl.kernel = rows_vec(s) ? K_ROWS_VEC : K_ROWS;
+  if (pl.rows) pl.kernel = rows_vec(s, pl.rows_ref) ? K_ROWS_VEC : K_ROWS;
   else if (strided_items(s)) pl.kernel = K_STRIDED;
   else if (pl.shape == SH_CHAIN) pl.kernel = K_FIXED_CHAIN;
   else if (pl.shape == SH_BALANCED) pl.kernel = K_FIXED_BALANCED;
@@ -1153,7 +1156,7 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
       const int32_t* ref = prog + pl->s->ranges[size_t(pl->rows_ref)].prog;
       const uint8_t* rt = reinterpret_cast<const uint8_t*>(pl->rtab.p);
       const int R = int(pl->s->ranges.size());
-      const int64_t nvec = vec && rows_vec(*pl->s) ? total / 4 : 0;
+      const int64_t nvec = vec && rows_vec(*pl->s, pl->rows_ref) ? total / 4 : 0;
       if (nvec > 0) {
         const Evs ev1{ev.start, nvec * 4 == total ? ev.stop : nullptr};
         // a stack of 6 for trees that need 5 or 6 (each push shifts the whole

@@ -674,8 +674,8 @@ __global__ __launch_bounds__(kThreads) void k_fused_strided(RankPtrs ptrs, const
 // every cache line is fetched once, by one workgroup. Each thread looks up its
 // element's range in LDS and evaluates the reference range's program, reading
 // leaf `rank` from the buffer that the range's row names. `tab` holds the range
-// of each of the n offsets of an instance (padded to 8 bytes), then one row of
-// P ranks per range. The evaluation order is the reference program's, so the
+// of each of the n offsets of an instance (padded to 8 bytes), then the renaming
+// as map[rank][range]: R bytes per leaf rank of the reference range. The evaluation order is the reference program's, so the
 // bits equal those of the replay over per-range items.
 template <int DT, int OPK, int D, int TM, int B>
 __global__ __launch_bounds__(kThreads) void k_fused_rows(RankPtrs ptrs, const int32_t* __restrict__ prog,
@@ -694,7 +694,8 @@ __global__ __launch_bounds__(kThreads) void k_fused_rows(RankPtrs ptrs, const in
   for (int o = threadIdx.x; o < n; o += kThreads) range_of[o] = tab[o];
   __syncthreads();
   const int moff = (n + 7) / 8 * 8;
-  for (int i = threadIdx.x; i < R * P; i += kThreads) row_ptr[i / P * Q + i % P] = base[tab[moff + i]];
+  // the table holds map[rank][range]
+  for (int i = threadIdx.x; i < R * P; i += kThreads) row_ptr[(i % R) * Q + i / R] = base[tab[moff + i]];
   __syncthreads();
   const auto w = prog_words<TM>(prog, 0);
   const int64_t v0 = first + int64_t(blockIdx.x) * iters * kThreads;  // the workgroup's first element
@@ -716,56 +717,139 @@ __global__ __launch_bounds__(kThreads) void k_fused_rows(RankPtrs ptrs, const in
 }
 
 // The same batches with 4-byte elements, 16-byte aligned buffers and at most
-// PB ranks. A workgroup loads every rank's 16-byte
-// vector at each lane's four elements, one coalesced load per rank (each line
-// once, by one instruction), and stages them in LDS, each lane in its own
-// column of [rank][element][lane] words, so no barrier is needed. It then
-// evaluates the reference range's program, reading leaf `rank` of element j
-// from the slot of the rank that element j's range renames it to; the results
-// are stored as whole vectors. `tab` is the table of k_fused_rows, padded to a
-// multiple of 8 bytes.
-constexpr int kRowsVecThreads = 128;  // two waves: one table copy per two (measured 5% faster than one)
-template <int DT, int OPK, int D, int TM, int B, int PB>
+// 32 ranks, whose reference tree stores to all P ranks. Each wave works on
+// positions of 64 K consecutive elements (16 K vectors), K elements per lane,
+// and walks the positions of the launch with a stride of all its waves; the
+// grid holds what the device keeps resident. Per position:
+//  - the loads: with K = 1 (9..32 ranks) the P x 16 vectors are spread over
+//    the lanes, lane L loading vector L % 16 of ranks L / 16, L / 16 + 4, ...
+//    (G = ceil(P / 4) loads per lane; one instruction covers four 256-byte runs,
+//    which measured as fast as 1 KB runs of one rank); with K = 4 (at most 8
+//    ranks) lane L loads vector L of every rank (G = P loads of 1 KB runs).
+//    16-byte non-temporal loads, each line once, written to the wave's own LDS
+//    stage, [rank][element];
+//  - lane L evaluates the reference range's program for elements L, L + 64, ...
+//    reading leaf `rank` from the stage row of the rank its element's range
+//    renames it to (map[rank][range]: the lanes of one read hit consecutive
+//    bytes; stage reads hit consecutive words);
+//  - the results go through LDS once more, so that each lane stores whole
+//    vectors to the program's output ranks.
+// The loads of the next position are issued before the current one is
+// evaluated, so every wave keeps a position in flight while it works. Only the
+// wave reads what it wrote to its stage; wave-scope fences order the LDS
+// accesses. The waves of a workgroup share one copy of `tab` (the table of
+// k_fused_rows, padded to a multiple of 8 bytes) and of the buffer table.
+constexpr int kRowsVecThreads = 256;  // at most; the host picks 1 or 4 waves per workgroup
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+template <int DT, int OPK, int D, int B, int K, int G>
 __global__ __launch_bounds__(kRowsVecThreads) void k_fused_rows_vec(RankPtrs ptrs, const int32_t* __restrict__ prog,
-                                                                    const uint8_t* __restrict__ tab, int64_t first,
-                                                                    int64_t nvec, int32_t n, int32_t R, int32_t P) {
+                                                                    const uint8_t* __restrict__ tab, int64_t nvec,
+                                                                    int32_t n, int32_t R, int32_t P) {
   static_assert(TT<DT>::V == 4, "four 4-byte elements per vector");
-  constexpr int T = kRowsVecThreads;
+  static_assert(K == 1 || K == 4, "one or four elements per lane");
+  using A = typename TT<DT>::A;
+  constexpr int E = 64 * K, NV = 16 * K;  // elements and vectors of a position
   extern __shared__ uint32_t rows_vec_lds[];
-  uint32_t* stage = rows_vec_lds;                                // P x 4 x T words
-  uint32_t* tabw = stage + P * 4 * T;                            // the table
+  const int lane = int(threadIdx.x) & 63, wave = int(threadIdx.x) >> 6, waves = int(blockDim.x) >> 6;
+  uint32_t* stage = rows_vec_lds + wave * (P + 1) * E;  // P rows of E words, then the E results
+  uint32_t* outw = stage + P * E;
+  // K = 1, buffer table: entry 4 i + y is the rank that lane group y loads in
+  // its i-th load, entry 4 (G + i) + y the output it stores to in its i-th
+  // store (past the last rank a group repeats it: the same vector from the same
+  // lane slot within one instruction, one request and one line, written back
+  // to the same stage word or output with the same value)
+  u32x4** ptab = reinterpret_cast<u32x4**>(rows_vec_lds + waves * (P + 1) * E);
+  uint32_t* tabw = reinterpret_cast<uint32_t*>(ptab + (K == 1 ? 8 * G : 0));
+  const ProgPtr tree = as_prog(prog) + 1;  // the reference range's single tree, P outputs
+  const ProgPtr outs = tree + 2 + 2 * tree[0];
+  auto cl = [P](int k) { return k < P ? k : P - 1; };
+  if constexpr (K == 1) {
+    if (threadIdx.x < 8 * G) {
+      const int e = int(threadIdx.x);
+      ptab[e] = static_cast<u32x4*>(e < 4 * G ? ptrs.p[cl(e)] : ptrs.p[outs[cl(e - 4 * G)]]);
+    }
+  }
   const int moff = (n + 7) / 8 * 8;
   const int words = (moff + R * P + 7) / 8 * 2;
-  for (int i = threadIdx.x; i < words; i += T) tabw[i] = reinterpret_cast<const uint32_t*>(tab)[i];
+  for (int i = threadIdx.x; i < words; i += blockDim.x) tabw[i] = reinterpret_cast<const uint32_t*>(tab)[i];
   __syncthreads();
   const uint8_t* range_of = reinterpret_cast<const uint8_t*>(tabw);
-  const uint8_t* map = range_of + moff;
-  const int64_t g = first + int64_t(blockIdx.x) * T + threadIdx.x;  // vector index
-  const bool ok[1] = {g < nvec};
-  const int64_t e = g * 4;
-  int rb[4];  // each element's row of the renaming table
-  int o = int(e % n);
+  const uint8_t* map = range_of + moff;  // [rank][range]
+  const int64_t npos = (nvec + NV - 1) / NV;
+  const int64_t stride = int64_t(gridDim.x) * waves;
+  int64_t pos = int64_t(blockIdx.x) * waves + wave;
+  if (pos >= npos) return;
+  const int q = K == 1 ? lane & 15 : lane, y0 = K == 1 ? lane >> 4 : 0;  // vector in the position, lane group
+  const int ostep = int((stride * E) % n);
+  int o[K];  // offsets of the lane's elements in their instances
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    rb[j] = range_of[o] * P;
-    o = o + 1 == n ? 0 : o + 1;
+  for (int j = 0; j < K; ++j) o[j] = int((pos * E + 64 * j + lane) % n);
+  u32x4 cur[G];
+  // the last position may be partial: its lanes past the end repeat the last
+  // vector (within the instruction) and store nothing
+  auto load = [&](int64_t ps) {
+    const int64_t g = ps * NV + q < nvec ? ps * NV + q : nvec - 1;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const u32x4* b = K == 1 ? ptab[4 * i + y0] : static_cast<const u32x4*>(ptrs.p[i]);
+      cur[i] = __builtin_nontemporal_load(b + g);
+    }
+  };
+  // stage the loaded position, evaluate, store; `next` issues the following
+  // position's loads between the stage writes and the evaluation. Only a
+  // wave's last position can be partial.
+  auto step = [&](auto next, bool last) {
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      *reinterpret_cast<u32x4*>(stage + (K == 1 ? cl(4 * i + y0) : i) * E + q * 4) = cur[i];
+    next();
+    wave_lds_sync();
+    int rr[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) rr[j] = range_of[o[j]];
+    constexpr int M = K == 1 ? 0 : 1;
+    A res[nvals<DT, M>()];
+    eval_one<DT, OPK, D, M, B>(tree, [&](int rank, u32x4(&v)[1]) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) v[0][j] = stage[map[rank * R + rr[j]] * E + 64 * j + lane];
+    }, res);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if constexpr (OPK == O_AVG) res[j] = res[j] / ptrs.div;
+      outw[64 * j + lane] = as_u(res[j]);
+    }
+    wave_lds_sync();
+    const u32x4 rv = *reinterpret_cast<const u32x4*>(outw + q * 4);
+    if (!last || pos * NV + q < nvec)
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        u32x4* d = K == 1 ? ptab[4 * (G + i) + y0] : static_cast<u32x4*>(ptrs.p[outs[i]]);
+        __builtin_nontemporal_store(rv, d + pos * NV + q);
+      }
+    wave_lds_sync();  // the next position's stage writes follow this one's reads
+  };
+  auto advance = [&] {
+    pos += stride;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      o[j] += ostep;
+      if (o[j] >= n) o[j] -= n;
+    }
+  };
+  load(pos);
+  if (pos + stride < npos) {
+    // the first position apart, so that the loop is entered, like its back
+    // edge, with a position's loads and stores in flight (the compiler then
+    // waits for the loads alone)
+    step([&] { load(pos + stride); }, false);  // in flight while this position is evaluated
+    advance();
+    for (; pos + stride < npos; advance()) step([&] { load(pos + stride); }, false);
   }
-  u32x4 v[PB][1];
-#pragma unroll
-  for (int y = 0; y < PB; ++y) {
-    v[y][0] = u32x4{0, 0, 0, 0};
-    if (y < P) ld_user<DT, 1, true>(ptrs.p[y], e, ok, v[y]);
-  }
-#pragma unroll
-  for (int y = 0; y < PB; ++y)
-    if (y < P)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) stage[(y * 4 + j) * T + threadIdx.x] = v[y][0][j];
-  const auto w = prog_words<TM>(prog, 0);
-  replay<DT, OPK, D, TM, 1, B>(ptrs, w, e, ok, [&](int rank, u32x4(&r)[1]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r[0][j] = stage[(map[rb[j] + rank] * 4 + j) * T + threadIdx.x];
-  });
+  step([] {}, true);
 }
 
 // Several result trees per range and few ranks: each thread loads its fragment of

@@ -7,6 +7,9 @@
 
 #include <algorithm>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "kernels.h"
 
@@ -225,21 +228,81 @@ hipError_t rows_d(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab,
   return hipSuccess;
 }
 
-template <int DT, int OPK, int D, int TM, int PB>
+// Workgroups of `fn` (with `lds` bytes of dynamic LDS) that the current device
+// holds at once: compute units x resident workgroups per unit, cached per
+// kernel, LDS size and device. 0 when HIP cannot tell.
+inline int64_t resident_blocks(const void* fn, int threads, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<const void*, int, size_t, int>, int64_t> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lk(mu);
+  const auto key = std::make_tuple(fn, threads, lds, dev);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per = 0;
+  int64_t v = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, threads, lds) == hipSuccess)
+    v = int64_t(cus) * per;
+  cache[key] = v;
+  return v;
+}
+
+template <int DT, int OPK, int D, int K, int G>
 hipError_t rows_vec_d(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab, int64_t nvec, int n, int R, int P,
                       int64_t max_blocks, hipStream_t st, Evs ev) {
-  const int64_t blocks = (nvec + kRowsVecThreads - 1) / kRowsVecThreads;
-  const size_t lds = size_t(P) * 4 * kRowsVecThreads * sizeof(uint32_t) + size_t((n + 7) / 8 * 8 + R * P + 7) / 8 * 8;
-  for (int64_t b0 = 0; b0 < blocks; b0 += max_blocks) {  // workgroups are independent
-    const int64_t cnt = std::min(max_blocks, blocks - b0);
-    const Evs ei{b0 == 0 ? ev.start : nullptr, b0 + cnt >= blocks ? ev.stop : nullptr};
-    hipExtLaunchKernelGGL((k_fused_rows_vec<DT, OPK, D, TM, kLeafBatch, PB>), dim3(unsigned(cnt)), dim3(kRowsVecThreads),
-                          lds, st, ei.start, ei.stop, 0, ptrs, prog, tab, b0 * kRowsVecThreads, nvec, int32_t(n),
-                          int32_t(R), int32_t(P));
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  const int64_t npos = (nvec + 16 * K - 1) / (16 * K);
+  // one launch: each wave walks its positions (16 K vectors) with the stride of
+  // every wave of the grid, which holds at most what the device keeps resident.
+  // Four waves per workgroup share the tables; when the device holds more than
+  // half the positions at once, single-wave workgroups spread them evenly.
+  const void* fn = reinterpret_cast<const void*>(&k_fused_rows_vec<DT, OPK, D, kLeafBatch, K, G>);
+  auto lds_of = [&](int waves) {
+    return size_t(waves) * (P + 1) * 64 * K * sizeof(uint32_t) + size_t(K == 1 ? 8 * G : 0) * sizeof(void*) +
+           size_t((n + 7) / 8 * 8 + R * P + 7) / 8 * 8;
+  };
+  int waves = 4;
+  int64_t res = resident_blocks(fn, 64 * waves, lds_of(waves));
+  if (res > 0 && npos < 2 * res * waves) {
+    waves = 1;
+    res = resident_blocks(fn, 64, lds_of(1));
   }
-  return hipSuccess;
+  int64_t blocks = (npos + waves - 1) / waves;
+  if (res > 0) blocks = std::min(blocks, res);
+  blocks = std::max<int64_t>(1, std::min(blocks, max_blocks));
+  hipExtLaunchKernelGGL((k_fused_rows_vec<DT, OPK, D, kLeafBatch, K, G>), dim3(unsigned(blocks)), dim3(64 * waves),
+                        lds_of(waves), st, ev.start, ev.stop, 0, ptrs, prog, tab, nvec, int32_t(n), int32_t(R),
+                        int32_t(P));
+  return hipGetLastError();
+}
+
+// At most 8 ranks: four elements per lane, one load per rank (G = P); 9..32
+// ranks: one element per lane, G = ceil(P / 4) loads of four ranks each.
+template <int DT, int OPK, int D>
+hipError_t rows_vec_g(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab, int64_t nvec, int n, int R, int P,
+                      int64_t max_blocks, hipStream_t st, Evs ev) {
+#define AR_RV(K_, G_) return rows_vec_d<DT, OPK, D, K_, G_>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev)
+  switch (P) {
+    case 1: AR_RV(4, 1);
+    case 2: AR_RV(4, 2);
+    case 3: AR_RV(4, 3);
+    case 4: AR_RV(4, 4);
+    case 5: AR_RV(4, 5);
+    case 6: AR_RV(4, 6);
+    case 7: AR_RV(4, 7);
+    case 8: AR_RV(4, 8);
+    default: break;
+  }
+  switch ((P + 3) / 4) {
+    case 3: AR_RV(1, 3);
+    case 4: AR_RV(1, 4);
+    case 5: AR_RV(1, 5);
+    case 6: AR_RV(1, 6);
+    case 7: AR_RV(1, 7);
+    default: AR_RV(1, 8);
+  }
+#undef AR_RV
 }
 
 template <int DT, int OPK>
@@ -248,19 +311,14 @@ hipError_t launch_fused_rows_vec_t(int D, const RankPtrs& ptrs, const int32_t* p
   if constexpr (TT<DT>::V != 4) {
     return hipErrorInvalidValue;  // 4-byte elements only
   } else {
-#define AR_ROWS_VEC(DD)                                                                                        \
-  if (P <= 8) return rows_vec_d<DT, OPK, DD, 1, 8>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);       \
-  if (P <= 16) return rows_vec_d<DT, OPK, DD, 1, 16>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);     \
-  return rows_vec_d<DT, OPK, DD, 1, 32>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev)
-    if (P > 32) return hipErrorInvalidValue;
+    if (P < 1 || P > 32) return hipErrorInvalidValue;
     switch (D) {
-      case 2: AR_ROWS_VEC(2);
-      case 4: AR_ROWS_VEC(4);
-      case 6: AR_ROWS_VEC(6);
-      case 8: AR_ROWS_VEC(8);
-      default: AR_ROWS_VEC(16);
+      case 2: return rows_vec_g<DT, OPK, 2>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
+      case 4: return rows_vec_g<DT, OPK, 4>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
+      case 6: return rows_vec_g<DT, OPK, 6>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
+      case 8: return rows_vec_g<DT, OPK, 8>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
+      default: return rows_vec_g<DT, OPK, 16>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
     }
-#undef AR_ROWS_VEC
   }
 }
 

@@ -528,10 +528,10 @@ def test_batched_short_ranges():
 def test_rows_kernel_batches():
     # batches of short instances whose ranges all run one program up to a
     # renaming of leaf ranks take k_fused_rows (one element per thread over the
-    # whole batch, range and buffers looked up in LDS); other shapes keep the
-    # strided items; single-range programs of several trees over 17..32 ranks
-    # run as one range of instance length 1. A tiny launch limit splits one
-    # call into many launches.
+    # whole batch, range and buffers looked up in LDS); several trees per range
+    # take the DAG replay, other shapes keep the strided items. A tiny launch
+    # limit splits one call into many launches, or leaves the vector form's
+    # waves many positions each.
     import allreduce_schedule_algorithms_amd as A
     K = A.Kernel
     # fp32 calls of more than 4096 elements on aligned buffers run the vector
@@ -548,6 +548,12 @@ def test_rows_kernel_batches():
              (24, 20, "ring", 0, 500, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"), ("int32", "sum"))),
              (24, 7, "ring", 0, 1001, K.AR_KERNEL_ROWS_VEC, (("fp32", "max"),)),
              (17, 16, "generalized", 0, 300, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"),)),
+             # four elements per lane and one load per rank (up to 8 ranks), or
+             # one element per lane and up to eight loads of four ranks each
+             (4, 106, "ring", 0, 100, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"), ("int32", "max"))),
+             (3, 106, "generalized", 0, 57, K.AR_KERNEL_ROWS_VEC, (("fp32", "avg"),)),
+             (8, 64, "ring", 0, 129, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"), ("int32", "sum"))),
+             (27, 90, "ring", 0, 213, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"),)),
              (24, 106, "generalized", 5, 500, K.AR_KERNEL_DAG, (("fp32", "sum"), ("int32", "max"), ("fp32", "avg"))),
              (24, 20_001, "generalized", 4, 1, K.AR_KERNEL_DAG, (("fp32", "sum"),)),
              (24, 106, "generalized", 1, 200, K.AR_KERNEL_STRIDED, (("fp32", "sum"),))]
@@ -567,6 +573,15 @@ def test_rows_kernel_batches():
     finally:
         A.ar_set_launch_blocks(prev)
     assert np.array_equal(bits(got.reshape(24, 100, 106)), bits(want))
+    # a grid smaller than the positions: every wave walks many of them
+    x = inputs.make("fp32", 12, 50 * 3001, seed=8)
+    want = oracle.allreduce(x.reshape(12, 3001, 50), "generalized", "fp32", "sum", n=50)
+    prev = A.ar_set_launch_blocks(5)
+    try:
+        got = gpu_allreduce(x, "generalized", "fp32", "sum", 0, "fused", batch=3001)
+    finally:
+        A.ar_set_launch_blocks(prev)
+    assert np.array_equal(bits(got.reshape(12, 3001, 50)), bits(want))
     # the caller's events bracket the vector launch and the ragged tail's launch
     torch = torch_mod()
     x = inputs.make("fp32", 24, 106 * 39, seed=9)  # 4134 elements: 1033 vectors and 2 more
