@@ -87,14 +87,37 @@ int64_t replay_item_vectors() {
   return v;
 }
 
+// With `edges` (the program-driven replay, k_fused), the partial vectors at a
+// range's ends run in its vector items instead of in element items: the run
+// starts at the 256-byte boundary at or before s0 and ends on the vector that
+// holds the range's last element, and each item carries in its count the
+// elements to skip before s0 (first item) and past the end (last item). Only
+// where that last vector would reach past the buffer (`limit` elements) does
+// a tail element item remain.
 void add_segment(std::vector<Item>& out, int64_t s0, int64_t len, int32_t tag, int V, bool vec,
-                 int64_t vectors = 0) {
+                 int64_t vectors = 0, int64_t limit = -1) {
   const int64_t item_vec = vectors > 0 ? vectors : 2 * kThreads;
   const int64_t item_sc = kThreads;
   if (len <= 0) return;
   if (!vec) {
     for (int64_t off = 0; off < len; off += item_sc) out.push_back({s0 + off, -int32_t(std::min(item_sc, len - off)), tag});
     return;
+  }
+  if (limit >= 0) {
+    const int64_t A = int64_t(V) * 16, a0 = s0 / A * A, end = s0 + len;
+    int64_t t1 = (end + V - 1) / V * V;
+    if (t1 > limit) t1 = end / V * V;
+    if (t1 > s0) {  // at least one whole vector in the buffer holds range elements
+      const int64_t nv = (t1 - a0) / V;
+      for (int64_t off = 0; off < nv; off += item_vec) {
+        const int64_t cnt = std::min(item_vec, nv - off);
+        const int64_t b = a0 + off * V, skip = std::max<int64_t>(0, s0 - b), trim = std::max<int64_t>(0, b + cnt * V - end);
+        if (skip >= cnt * V) continue;  // no range element in this item (a head run longer than an item)
+        out.push_back({b, item_count(cnt, skip, trim), tag});
+      }
+      if (end > t1) out.push_back({t1, -int32_t(end - t1), tag});
+      return;
+    }
   }
   // Vector runs start on a 256-byte boundary (16 vectors of V elements): a wave's
   // 1 KB access then covers whole 128-byte lines instead of splitting one line
@@ -612,10 +635,13 @@ RunResult build_items(Plan& pl, bool vec) {
     // k_fused_multi: one vector per thread per item (2-5% faster than two on 7 ranks, r = 1..3)
     const int64_t iv = pl.multi ? int64_t(kThreads) : fixed ? int64_t(kThreads) * pl.md : replay_item_vectors();
     auto tag_of = [&](size_t i) { return fixed ? int32_t(i) : s.ranges[i].prog; };
+    // the program-driven replay of single-tree programs takes the partial
+    // vectors at range ends in its vector items
+    const int64_t limit = pl.kernel == K_REPLAY && s.max_trees == 1 ? sp.n * sp.batch : -1;
     if (sp.batch == 1 || flat) {
       const int64_t mult = flat ? sp.batch : 1;
       for (size_t i = 0; i < s.ranges.size(); ++i)
-        add_segment(items, s.ranges[i].start, s.ranges[i].len * mult, tag_of(i), V, vec, iv);
+        add_segment(items, s.ranges[i].start, s.ranges[i].len * mult, tag_of(i), V, vec, iv, limit);
     } else if (strided) {
       // short ranges in many instances: one strided item per range and block
       // of instances; the items of one block sit next to each other, so the
@@ -628,7 +654,7 @@ RunResult build_items(Plan& pl, bool vec) {
     } else {
       for (int64_t b = 0; b < sp.batch; ++b)
         for (size_t i = 0; i < s.ranges.size(); ++i)
-          add_segment(items, b * sp.n + s.ranges[i].start, s.ranges[i].len, tag_of(i), V, vec, iv);
+          add_segment(items, b * sp.n + s.ranges[i].start, s.ranges[i].len, tag_of(i), V, vec, iv, limit);
     }
     if (pl.rows) {
       if (!pl.rtab.p) {

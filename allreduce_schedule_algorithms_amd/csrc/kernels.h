@@ -56,6 +56,15 @@ struct Item {
   int32_t tag;  // program word offset (fused) or op index (literal)
 };
 
+// A vector item of the program-driven replay may cover partial vectors at a
+// range's ends: its count then holds the vectors in bits 0..15, the elements
+// before the range in bits 16..23 and those past it in bits 24..27 (neither is
+// loaded for the range's sake nor stored).
+__host__ __device__ constexpr int32_t item_count(int64_t vectors, int64_t skip, int64_t trim) {
+  return int32_t(vectors | (skip << 16) | (trim << 24));
+}
+constexpr int32_t kItemVectorsMask = 0xffff;
+
 constexpr int kThreads = 256;
 constexpr int kLeafBatch = 8;
 constexpr int kMaxFusedTrees = 8;  // distinct result trees per range the fused replay keeps in registers
@@ -188,15 +197,47 @@ __device__ __forceinline__ void st_user(void* base, int64_t e, const bool (&ok)[
   }
 }
 
+// st_user for a fragment of vectors of which those not wholly inside [lo, hi)
+// (the partial vectors at a range's ends) store only their elements inside it.
+template <int DT, int M, bool NT = true>
+__device__ __forceinline__ void st_user_edge(void* base, int64_t e, const bool (&ok)[mm<M>()],
+                                             const typename TT<DT>::A (&v)[nvals<DT, M>()], int64_t lo, int64_t hi) {
+  static_assert(M > 0, "vector fragments");
+  using S = typename TT<DT>::S;
+  constexpr int V = TT<DT>::V;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    if (!ok[j]) continue;
+    const int64_t ej = e + int64_t(j) * kThreads * V;
+    if (ej >= lo && ej + V <= hi) {
+      u32x4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (DT == D_BF16) r[i] = to_bf16(v[8 * j + 2 * i]) | (to_bf16(v[8 * j + 2 * i + 1]) << 16);
+        else r[i] = as_u(v[4 * j + i]);
+      }
+      st1<u32x4, NT>(r, reinterpret_cast<u32x4*>(reinterpret_cast<S*>(base) + ej));
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+        if (ej + i >= lo && ej + i < hi) {
+          if constexpr (DT == D_BF16) *(reinterpret_cast<uint16_t*>(base) + ej + i) = uint16_t(to_bf16(v[V * j + i]));
+          else *(reinterpret_cast<uint32_t*>(base) + ej + i) = as_u(v[V * j + i]);
+        }
+    }
+  }
+}
+
 // Store one fragment to `cnt` ranks: rank_of(i) gives the i-th destination.
 // Destinations go 8 at a time so their pointer lookups (scalar loads) overlap.
 // RUNS: rank_of may be read for whole runs of kLeafBatch indices (it reads
 // padded program words) and is clamped by value past cnt; otherwise only
 // indices below cnt are read.
-template <int DT, int M, bool RUNS = false, bool NT = true, typename RankOf>
+template <int DT, int M, bool RUNS = false, bool NT = true, bool EDGE = false, typename RankOf>
 __device__ __forceinline__ void st_user_all(const RankPtrs& ptrs, int cnt, RankOf&& rank_of, int64_t e,
                                             const bool (&ok)[mm<M>()],
-                                            const typename TT<DT>::A (&v)[nvals<DT, M>()]) {
+                                            const typename TT<DT>::A (&v)[nvals<DT, M>()], int64_t lo = 0,
+                                            int64_t hi = 0) {
   for (int b = 0; b < cnt; b += kLeafBatch) {
     void* pp[kLeafBatch];
     if constexpr (RUNS) {
@@ -213,7 +254,10 @@ __device__ __forceinline__ void st_user_all(const RankPtrs& ptrs, int cnt, RankO
     }
 #pragma unroll
     for (int k = 0; k < kLeafBatch; ++k)
-      if (b + k < cnt) st_user<DT, M, NT>(pp[k], e, ok, v);
+      if (b + k < cnt) {
+        if constexpr (EDGE) st_user_edge<DT, M, NT>(pp[k], e, ok, v, lo, hi);
+        else st_user<DT, M, NT>(pp[k], e, ok, v);
+      }
   }
 }
 
@@ -350,9 +394,10 @@ __device__ __forceinline__ void eval_one(WP __restrict__ w, LeafAt&& leaf_at,
   for (int i = 0; i < N; ++i) res[i] = st[0][i];
 }
 
-template <int DT, int OPK, int D, int TM, int M, int B, bool NTS = true, typename WP, typename LeafAt>
+template <int DT, int OPK, int D, int TM, int M, int B, bool NTS = true, bool EDGE = false, typename WP,
+          typename LeafAt>
 __device__ __forceinline__ void replay(const RankPtrs& ptrs, WP __restrict__ w, int64_t e,
-                                       const bool (&ok)[mm<M>()], LeafAt&& leaf_at) {
+                                       const bool (&ok)[mm<M>()], LeafAt&& leaf_at, int64_t lo = 0, int64_t hi = 0) {
   using A = typename TT<DT>::A;
   const int ntrees = w[0];
   w += 1;
@@ -377,17 +422,20 @@ __device__ __forceinline__ void replay(const RankPtrs& ptrs, WP __restrict__ w, 
 #pragma unroll
         for (int i = 0; i < nvals<DT, M>(); ++i) res[t][i] = res[t][i] / ptrs.div;
       }
-      st_user_all<DT, M, word_runs<WP>(), NTS>(ptrs, nouts[t], [&](int i) { return ot[i]; }, e, ok, res[t]);
+      st_user_all<DT, M, word_runs<WP>(), NTS, EDGE>(ptrs, nouts[t], [&](int i) { return ot[i]; }, e, ok, res[t], lo,
+                                                     hi);
     }
   }
 }
 
-// Vectors per thread of the fused replay: two for single-tree programs whose
-// register stack fits (depth <= 8 for 4-byte types, <= 4 for bf16, which widens
-// to twice the values per vector), one where the stack or several results
-// need the room.
+// Register fragments per thread of the program-driven replay. Its work items
+// hold one vector per thread, so the second fragment of a two-fragment form
+// stays idle; yet for single-tree programs with a stack of 4 to 8 (bf16: 4)
+// that form measured faster (interleaved runs: AHC 5.96 vs 5.87 TB/s, 24-rank
+// binomial 5.18 vs 5.00 TB/s). Chains (a stack of 2) take one fragment: the
+// idle one's arithmetic cost the 192-rank bf16 ring 8% (4.42 vs 4.79 TB/s).
 template <int DT, int D, int TM> constexpr int fused_m() {
-  return (TM == 1 && D <= (DT == D_BF16 ? 4 : 8)) ? 2 : 1;
+  return (TM == 1 && D > 2 && D <= (DT == D_BF16 ? 4 : 8)) ? 2 : 1;
 }
 
 template <int DT, int OPK, int D, int TM, int B>
@@ -398,7 +446,22 @@ __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* _
   constexpr bool NT = TM == 1;  // several trees re-read their leaves: keep them cacheable
   const Item it = items[item_index(ptrs.xcd)];
   const auto w = prog_words<TM>(prog, it.tag);
-  if (it.count > 0) {
+  if (TM == 1 && it.count > kItemVectorsMask) {
+    // partial vectors at the range's ends (single-tree programs): load them
+    // whole (in the buffer), store only the range's elements; vectors wholly
+    // before the range stay idle
+    Item jt = it;
+    jt.count = it.count & kItemVectorsMask;
+    const int64_t lo = it.start + ((it.count >> 16) & 0xff);
+    const int64_t hi = it.start + int64_t(jt.count) * V - ((it.count >> 24) & 0xf);
+    for_fragments<M>(jt, V, [&](int64_t e, const bool (&ok0)[M]) {
+      bool ok[M];
+#pragma unroll
+      for (int j = 0; j < M; ++j) ok[j] = ok0[j] && e + int64_t(j) * kThreads * V + V > lo;
+      replay<DT, OPK, D, TM, M, B, true, true>(
+          ptrs, w, e, ok, [&](int rank, u32x4(&r)[M]) { ld_user<DT, M, NT>(ptrs.p[rank], e, ok, r); }, lo, hi);
+    });
+  } else if (it.count > 0) {
     for_fragments<M>(it, V, [&](int64_t e, const bool (&ok)[M]) {
       replay<DT, OPK, D, TM, M, B>(ptrs, w, e, ok,
                                    [&](int rank, u32x4(&r)[M]) { ld_user<DT, M, NT>(ptrs.p[rank], e, ok, r); });
