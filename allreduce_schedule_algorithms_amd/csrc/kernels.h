@@ -94,10 +94,9 @@ template <int OPK> __device__ __forceinline__ float cmb(float a, float b) {
   if constexpr (OPK == O_SUM || OPK == O_AVG) {
     return a + b;
   } else {
-    // total order on non-NaN floats with -0 < +0: flip the magnitude bits of negatives
-    int ia = __float_as_int(a), ib = __float_as_int(b);
-    int ka = ia ^ ((ia >> 31) & 0x7fffffff), kb = ib ^ ((ib >> 31) & 0x7fffffff);
-    return kb > ka ? b : a;
+    // total order on non-NaN floats with -0 < +0: IEEE 754-2019 maximum, one
+    // v_maximum3_f32 on gfx950 (denormals are kept, so they compare exactly)
+    return __builtin_elementwise_maximum(a, b);
   }
 }
 template <int OPK> __device__ __forceinline__ uint32_t cmb(uint32_t a, uint32_t b) {
@@ -454,12 +453,15 @@ __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* _
     jt.count = it.count & kItemVectorsMask;
     const int64_t lo = it.start + ((it.count >> 16) & 0xff);
     const int64_t hi = it.start + int64_t(jt.count) * V - ((it.count >> 24) & 0xf);
+    // program words through the constant address space: the element stores
+    // would otherwise make the compiler fetch every later word with a vector load
+    const ProgPtr wc = as_prog(prog) + it.tag;
     for_fragments<M>(jt, V, [&](int64_t e, const bool (&ok0)[M]) {
       bool ok[M];
 #pragma unroll
       for (int j = 0; j < M; ++j) ok[j] = ok0[j] && e + int64_t(j) * kThreads * V + V > lo;
       replay<DT, OPK, D, TM, M, B, true, true>(
-          ptrs, w, e, ok, [&](int rank, u32x4(&r)[M]) { ld_user<DT, M, NT>(ptrs.p[rank], e, ok, r); }, lo, hi);
+          ptrs, wc, e, ok, [&](int rank, u32x4(&r)[M]) { ld_user<DT, M, NT>(ptrs.p[rank], e, ok, r); }, lo, hi);
     });
   } else if (it.count > 0) {
     for_fragments<M>(it, V, [&](int64_t e, const bool (&ok)[M]) {

@@ -190,6 +190,27 @@ def test_many_tiny_chunks_pack_into_shared_workgroups():
             assert np.array_equal(bits(got), bits(want)), (n, algo, r)
 
 
+def test_max_signed_zeros_subnormals_infinities():
+    # max is the total order with -0 < +0 on non-NaN values: ties between zeros
+    # of both signs, subnormals next to zeros, infinities and repeated values,
+    # in every kernel family that combines (fixed shapes, program-driven replay,
+    # DAG, rows, direct, literal), fp32 and bf16
+    pool = {"fp32": np.array([0.0, -0.0, 2.0**-149, -(2.0**-149), 2.0**-130, -(2.0**-130), 1.0, -1.0, np.inf,
+                              -np.inf, 3.5, -3.5, 2.0**-149 * 7], dtype=np.float32),
+            "bf16": np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x0080, 0x8080, 0x3F80, 0xBF80, 0x7F80, 0xFF80,
+                              0x4060, 0xC060, 0x0007], dtype=np.uint16)}
+    rng = np.random.default_rng(11)
+    cases = [(8, 4096, "rh_rd", 0, "fused", 1), (12, 3000, "ring", 0, "fused", 1), (24, 106, "generalized", 5, "fused", 40),
+             (24, 106, "ring", 0, "fused", 60), (7, 5000, "generalized", 2, "fused", 1), (7, 999, "direct", 0, "fused", 1),
+             (9, 777, "generalized", 3, "literal", 1), (63, 300, "generalized", 6, "fused", 1)]
+    for P, n, algo, knob, ex, B in cases:
+        for dtype in ("fp32", "bf16"):
+            x = pool[dtype][rng.integers(0, len(pool[dtype]), size=(P, n * B))]
+            want = oracle.allreduce(x.reshape(P, B, n) if B > 1 else x, algo, dtype, "max", knob=knob, n=n)
+            got = gpu_allreduce(x, algo, dtype, "max", knob, ex, batch=B)
+            assert np.array_equal(bits(got.reshape(np.shape(want))), bits(want)), (P, n, algo, knob, ex, dtype)
+
+
 def test_side_stream_and_signed_zero():
     import torch
     s = torch.cuda.Stream()
