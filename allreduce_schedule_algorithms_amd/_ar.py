@@ -80,6 +80,7 @@ class Kernel(enum.IntEnum):
     AR_KERNEL_ROWS = 10
     AR_KERNEL_ROWS_VEC = 11
     AR_KERNEL_DAG = 12
+    AR_KERNEL_JIT = 13
 
 
 class Exec(enum.IntEnum):

@@ -30,6 +30,7 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 SOURCES = [
     ("sched.cpp", False),
     ("abi.cpp", False),
+    ("jit.cpp", False),
     ("exec.hip", True),
 ] + [(f"launch_{d}_{o}.hip", True) for d in ("i32", "f32", "bf16") for o in ("sum", "max")] + \
     [(f"launch_{d}_avg.hip", True) for d in ("f32", "bf16")]

@@ -50,7 +50,7 @@ bool set_launch_blocks(int64_t blocks, int64_t* previous);
 enum Kernel : int32_t {
   K_NONE = 0, K_DIRECT = 1, K_LITERAL = 2, K_REPLAY = 3, K_STAGED = 4, K_STRIDED = 5,
   K_FIXED_CHAIN = 6, K_FIXED_BALANCED = 7, K_FIXED_STACK = 8, K_MULTI = 9, K_ROWS = 10, K_ROWS_VEC = 11,
-  K_DAG = 12
+  K_DAG = 12, K_JIT = 13
 };
 RunResult kernel_of(const Spec& spec, int exec, int* kernel);
 

@@ -34,6 +34,7 @@
 #include <vector>
 
 #include "exec.h"
+#include "jit.h"
 #include "launch.h"
 
 namespace ar {
@@ -180,6 +181,15 @@ struct Plan {
   int kernel = K_NONE;     // the kernel family the plan launches (ar_kernel)
   std::string fallback;   // why a fused call runs the literal steps (empty otherwise)
   size_t device_bytes = 0;  // device memory the plan's tables hold
+  // K_JIT: the register DAG kernel compiled for this schedule; loaded on the
+  // plan's device at its first launch, unloaded with the plan
+  std::vector<char> jit_code;
+  int jit_vectors = 2;     // 16-byte vectors per thread (items of kThreads * jit_vectors vectors)
+  std::string jit_note;    // why a multi-tree program does not run compiled (empty otherwise)
+  struct JitModule {
+    JitKernel k;
+    ~JitModule() { jit_unload(&k); }
+  } jit;
 };
 
 // Plans hold device tables that enqueued launches and captured HIP graphs keep
@@ -630,10 +640,12 @@ RunResult build_items(Plan& pl, bool vec) {
     for (const FusedRange& r : s.ranges) max_len = std::max(max_len, r.len);
     std::vector<SItem> sitems;
     const bool strided = strided_items(s);
-    // the fixed-shape kernel finds a range's buffers by its index in the table
-    const bool fixed = pl.shape != SH_NONE || pl.multi;
+    // the fixed-shape and compiled kernels find a range by its index
+    const bool jit = pl.kernel == K_JIT;
+    const bool fixed = jit || pl.shape != SH_NONE || pl.multi;
     // k_fused_multi: one vector per thread per item (2-5% faster than two on 7 ranks, r = 1..3)
-    const int64_t iv = pl.multi ? int64_t(kThreads) : fixed ? int64_t(kThreads) * pl.md : replay_item_vectors();
+    const int64_t iv = jit ? int64_t(kThreads) * pl.jit_vectors
+                           : pl.multi ? int64_t(kThreads) : fixed ? int64_t(kThreads) * pl.md : replay_item_vectors();
     auto tag_of = [&](size_t i) { return fixed ? int32_t(i) : s.ranges[i].prog; };
     // the program-driven replay of single-tree programs takes the partial
     // vectors at range ends in its vector items
@@ -723,13 +735,43 @@ bool fused_runs(const Schedule& s) {
 const char* kernel_name(int k) {
   static const char* names[] = {"none", "k_direct", "k_literal", "k_fused", "k_fused_staged", "k_fused_strided",
                                 "k_fused_fixed (chain)", "k_fused_fixed (balanced)", "k_fused_fixed (stack)",
-                                "k_fused_multi", "k_fused_rows", "k_fused_rows_vec", "k_fused_dag"};
+                                "k_fused_multi", "k_fused_rows", "k_fused_rows_vec", "k_fused_dag", "ar_jit"};
   return k >= 0 && k < int(sizeof(names) / sizeof(names[0])) ? names[k] : "?";
 }
 
 // The kernel family a fused plan launches, in the order run_allreduce tries
 // them; K_LITERAL (with the reason in pl.fallback) when no replay holds the
 // program.
+bool jit_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("AR_JIT");  // "0": no run-time compiled kernels (for comparisons)
+    return !(v && v[0] == '0');
+  }();
+  return on;
+}
+
+// The compiled register DAG kernel of s: generated, then compiled once per
+// distinct source (schedules of one shape at other sizes share it). False and
+// *why when it is not available.
+bool jit_code_for(const Schedule& s, std::vector<char>* code, int* vectors, std::string* why) {
+  static std::mutex mu;
+  static std::map<std::string, std::pair<std::vector<char>, int>> cache;
+  if (!jit_available(why)) return false;
+  std::string src;
+  int v = 0;
+  if (!jit_source(s, s.spec.dtype, s.spec.op, &src, &v, why)) return false;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(src);
+  if (it == cache.end()) {
+    std::vector<char> c;
+    if (!jit_compile(src, &c, why)) return false;
+    it = cache.emplace(src, std::make_pair(std::move(c), v)).first;
+  }
+  *code = it->second.first;
+  *vectors = it->second.second;
+  return true;
+}
+
 void choose_kernel(Plan& pl) {
   const Schedule& s = *pl.s;
   if (pl.exec == E_LITERAL) { pl.kernel = K_LITERAL; return; }
@@ -737,6 +779,16 @@ void choose_kernel(Plan& pl) {
     pl.kernel = K_LITERAL;
     pl.fallback = "no replay program (" + s.fused_error + ")";
     return;
+  }
+  // Several result trees per range over few ranks and ranges: the range's DAG
+  // as straight-line register code, compiled for the schedule (jit.h), where
+  // hipRTC is there to compile it; otherwise the kernels below.
+  if (pl.exec == E_FUSED && fixed_shapes_enabled() && jit_enabled() && s.max_trees > 1 && !strided_items(s) &&
+      s.spec.P <= kJitMaxRanks && int(s.ranges.size()) <= kJitMaxRanges) {
+    if (jit_code_for(s, &pl.jit_code, &pl.jit_vectors, &pl.jit_note)) {
+      pl.kernel = K_JIT;
+      return;
+    }
   }
   // The DAG replay (each distinct combination once, values in LDS) takes:
   // programs with more result trees than the register replays hold; other
@@ -839,6 +891,10 @@ void trace_plan(const Plan& pl) {
     o << "; DAG " << (pl.dag_shared ? "shared by every range" : pl.dp.shared ? "one program" : "per range")
       << ": " << pl.dp.instr << " combinations per element in " << pl.dp.levels << " levels, " << pl.dp.S << " slots";
   if (pl.kernel == K_LITERAL) o << "; " << s.nsteps << " step launches" << (s.finalize_ops ? " + 1 finalize" : "");
+  if (pl.kernel == K_JIT)
+    o << "; compiled register DAG, " << pl.jit_vectors << " vectors per thread, code object " << pl.jit_code.size()
+      << " bytes";
+  if (!pl.jit_note.empty()) o << "; not compiled: " << pl.jit_note;
   if (!pl.fallback.empty()) o << "; literal fallback: " << pl.fallback;
   std::fprintf(stderr, "%s\n", o.str().c_str());
 }
@@ -1203,10 +1259,28 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
       }
       return res;
     }
+    if (pl->kernel == K_JIT && !pl->jit.k.fn) {
+      std::string err;
+      if (!jit_load(pl->jit_code, &pl->jit.k, &err)) {
+        RunResult r;
+        r.status = 4;  // AR_HIP_ERROR
+        r.message = "loading the compiled replay: " + err;
+        return r;
+      }
+    }
     for (int64_t off = 0; off < nit; off += cap) {  // work items are independent
       const Evs ei{off == 0 ? ev.start : nullptr, off + cap >= nit ? ev.stop : nullptr};
       const int64_t cnt = std::min(cap, nit - off);
-      if (pl->strided) {
+      if (pl->kernel == K_JIT) {
+        JitArgs ja;
+        std::memset(&ja, 0, sizeof(ja));
+        for (int q = 0; q < spec.P; ++q) ja.p[q] = ptrs.p[q];
+        ja.items = items + off;
+        ja.div = ptrs.div;
+        void* params[] = {&ja};
+        e = hipExtModuleLaunchKernel(static_cast<hipFunction_t>(pl->jit.k.fn), uint32_t(cnt * kThreads), 1, 1,
+                                     kThreads, 1, 1, 0, st, params, nullptr, ei.start, ei.stop, 0);
+      } else if (pl->strided) {
         const SItem* sit = reinterpret_cast<const SItem*>(pl->items[mode].p) + off;
         AR_DISPATCH(spec.dtype, spec.op,
                     (e = launch_fused_strided_t<DT, OPK>(pl->D, TM, cnt, ptrs, sit, prog, spec.n, st, ei)));

@@ -668,7 +668,7 @@ KERNEL_NAMES = {
     "AR_KERNEL_REPLAY": "k_fused", "AR_KERNEL_STAGED": "k_fused_staged", "AR_KERNEL_STRIDED": "k_fused_strided",
     "AR_KERNEL_FIXED_CHAIN": "k_fused_fixed", "AR_KERNEL_FIXED_BALANCED": "k_fused_fixed",
     "AR_KERNEL_FIXED_STACK": "k_fused_fixed", "AR_KERNEL_MULTI": "k_fused_multi", "AR_KERNEL_ROWS": "k_fused_rows",
-    "AR_KERNEL_ROWS_VEC": "k_fused_rows_vec", "AR_KERNEL_DAG": "k_fused_dag",
+    "AR_KERNEL_ROWS_VEC": "k_fused_rows_vec", "AR_KERNEL_DAG": "k_fused_dag", "AR_KERNEL_JIT": "ar_jit",
 }
 
 

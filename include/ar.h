@@ -265,7 +265,16 @@ ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes);
  *                            range's order.
  *  AR_KERNEL_DAG             the DAG replay: more than 8 result trees per range (the generalized
  *                            algorithm with large r at large P), and every call under
- *                            AR_EXEC_DAG; each distinct combination once, values in LDS. */
+ *                            AR_EXEC_DAG; each distinct combination once, values in LDS.
+ *  AR_KERNEL_JIT             several result trees per range over at most 16 ranks and 16 ranges
+ *                            (the generalized algorithm with r > 0 on few ranks), not short
+ *                            ranges of a batch: each range's DAG written out as straight-line
+ *                            register code and compiled for the schedule with hipRTC on the
+ *                            plan's first call (one compile per distinct program, kept for the
+ *                            process), loaded on the device at its first launch. Where hipRTC
+ *                            is missing or the program exceeds the register budget, the
+ *                            kernels above run instead (AR_TRACE=1 says why); AR_JIT=0 turns it
+ *                            off. */
 typedef enum {
   AR_KERNEL_NONE = 0,
   AR_KERNEL_DIRECT = 1,
@@ -279,7 +288,8 @@ typedef enum {
   AR_KERNEL_MULTI = 9,
   AR_KERNEL_ROWS = 10,
   AR_KERNEL_ROWS_VEC = 11,
-  AR_KERNEL_DAG = 12
+  AR_KERNEL_DAG = 12,
+  AR_KERNEL_JIT = 13
 } ar_kernel;
 ar_status ar_kernel_of(const ar_call* call, int32_t* kernel);
 

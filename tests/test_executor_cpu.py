@@ -47,7 +47,7 @@ def test_trace_names_each_plans_kernel():
     names = {"AR_KERNEL_FIXED_BALANCED": "k_fused_fixed (balanced)", "AR_KERNEL_MULTI": "k_fused_multi",
              "AR_KERNEL_ROWS_VEC": "k_fused_rows_vec", "AR_KERNEL_ROWS": "k_fused_rows",
              "AR_KERNEL_DAG": "k_fused_dag", "AR_KERNEL_LITERAL": "k_literal", "AR_KERNEL_REPLAY": "k_fused",
-             "AR_KERNEL_STAGED": "k_fused_staged", "AR_KERNEL_STRIDED": "k_fused_strided"}
+             "AR_KERNEL_STAGED": "k_fused_staged", "AR_KERNEL_STRIDED": "k_fused_strided", "AR_KERNEL_JIT": "ar_jit"}
     for (P, n, dt, algo, knob, ex), kind, ln in zip(fused, kinds, lines):
         assert f"P={P} n={n} " in ln and f" {algo} knob={knob} " in ln, ln
         assert f"kernel {names[kind]} " in ln, (kind, ln)

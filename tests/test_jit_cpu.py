@@ -1,0 +1,42 @@
+"""The compiled register DAG on the host: which calls take it, what AR_TRACE
+says about it, and the kernels that run instead with AR_JIT=0 (no GPU needed:
+hipRTC compiles for gfx950 without one)."""
+import os
+import subprocess
+import sys
+
+import allreduce_schedule_algorithms_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _choices(env_extra):
+    code = ("import allreduce_schedule_algorithms_amd as A\n"
+            "for P, n, r in ((7, 1 << 24, 3), (7, 1 << 24, 1), (12, 4099, 2), (13, 1000, 4)):\n"
+            "    st = 4 if P == 13 else 0\n"
+            "    print(int(A.ar_kernel_of(A.make_call(P, n, 'fp32', 'sum', 'generalized', r, steps=st))))\n")
+    env = dict(os.environ, **env_extra)
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    return [int(x) for x in r.stdout.split()], r.stderr
+
+
+def test_jit_choice_trace_and_off_switch():
+    K = A.Kernel
+    on, err = _choices({"AR_TRACE": "1"})
+    assert on == [K.AR_KERNEL_JIT] * 4
+    lines = [ln for ln in err.splitlines() if ln.startswith("ar: plan ")]
+    assert len(lines) == 4 and all("kernel ar_jit" in ln and "compiled register DAG" in ln for ln in lines), err
+    off, _ = _choices({"AR_JIT": "0"})
+    assert off == [K.AR_KERNEL_MULTI, K.AR_KERNEL_MULTI, K.AR_KERNEL_DAG, K.AR_KERNEL_DAG]
+
+
+def test_jit_takes_no_workspace_and_keeps_batches_of_short_ranges_elsewhere():
+    K = A.Kernel
+    call = A.make_call(7, 1 << 24, "bf16", "max", "generalized", 2)
+    assert A.ar_kernel_of(call) == K.AR_KERNEL_JIT
+    assert A.ar_workspace_bytes(call) == 0
+    # short ranges of a batch: strided work, not the compiled kernel
+    assert A.ar_kernel_of(A.make_call(24, 106, "fp32", "sum", "generalized", 1, batch=10_000)) == K.AR_KERNEL_STRIDED
+    # more than 16 ranks: the DAG replay
+    assert A.ar_kernel_of(A.make_call(17, 5000, "fp32", "sum", "generalized", 2)) == K.AR_KERNEL_DAG

@@ -352,12 +352,15 @@ def test_workspace_query():
     assert A.ar_workspace_bytes(lit) == 8 * 1024 * 4  # one fp32 slot per rank
     assert A.ar_workspace_bytes(A.make_call(8, 1024, "bf16", "sum", "ring")) == 0
     assert A.ar_workspace_bytes(A.make_call(8, 1024, "fp32", "sum", "ring", exec="literal")) == 0
-    # ranges with more result trees than the register replays keep run the DAG
-    # replay, values in LDS: no workspace
+    # ranges with more result trees than the register replays keep run the
+    # compiled register DAG (or, over more ranks, the DAG replay): no workspace
     big = A.make_call(13, 1000, "fp32", "sum", "generalized", 4, steps=4)
     assert A.ar_schedule_build(big).info().max_trees > 8
-    assert A.ar_kernel_of(big) == A.Kernel.AR_KERNEL_DAG
+    assert A.ar_kernel_of(big) == A.Kernel.AR_KERNEL_JIT
     assert A.ar_workspace_bytes(big) == 0
+    bigger = A.make_call(63, 1000, "fp32", "sum", "generalized", 6)
+    assert A.ar_kernel_of(bigger) == A.Kernel.AR_KERNEL_DAG
+    assert A.ar_workspace_bytes(bigger) == 0
     lit = A.make_call(13, 1000, "fp32", "sum", "generalized", 4, "literal", steps=4)
     assert A.ar_workspace_bytes(lit) > 0
     # a DAG whose values exceed a workgroup's LDS (255 ranks, r = 8) runs the
@@ -379,9 +382,10 @@ def test_kernel_choice():
         (dict(P=7, n=1 << 24, algo="ring", collective="all_gather"), K.AR_KERNEL_FIXED_CHAIN),
         (dict(P=7, n=1 << 24, algo="generalized"), K.AR_KERNEL_FIXED_STACK),
         (dict(P=6, n=1000, algo="binomial"), K.AR_KERNEL_FIXED_STACK),
-        (dict(P=7, n=1 << 24, algo="generalized", knob=3), K.AR_KERNEL_MULTI),
-        (dict(P=7, n=1 << 24, algo="generalized", knob=1), K.AR_KERNEL_MULTI),
-        (dict(P=12, n=4099, algo="generalized", knob=2), K.AR_KERNEL_DAG),
+        (dict(P=7, n=1 << 24, algo="generalized", knob=3), K.AR_KERNEL_JIT),
+        (dict(P=7, n=1 << 24, algo="generalized", knob=1), K.AR_KERNEL_JIT),
+        (dict(P=7, n=1 << 20, algo="generalized", knob=2, dtype="bf16"), K.AR_KERNEL_JIT),
+        (dict(P=12, n=4099, algo="generalized", knob=2), K.AR_KERNEL_JIT),
         (dict(P=24, n=106, algo="generalized", knob=5, batch=10_000), K.AR_KERNEL_DAG),
         (dict(P=24, n=106, algo="generalized", knob=5, batch=10_000, dtype="bf16"), K.AR_KERNEL_DAG),
         (dict(P=24, n=106, algo="generalized", knob=5, batch=30), K.AR_KERNEL_DAG),
@@ -401,7 +405,8 @@ def test_kernel_choice():
         (dict(P=8, n=1 << 20, algo="direct", exec="replay"), K.AR_KERNEL_FIXED_CHAIN),
         (dict(P=8, n=1 << 20, algo="direct", collective="reduce_scatter"), K.AR_KERNEL_FIXED_CHAIN),
         (dict(P=8, n=1 << 20, algo="ring", exec="literal"), K.AR_KERNEL_LITERAL),
-        (dict(P=13, n=1000, algo="generalized", knob=4, steps=4), K.AR_KERNEL_DAG),  # more than 8 trees
+        (dict(P=13, n=1000, algo="generalized", knob=4, steps=4), K.AR_KERNEL_JIT),  # more than 8 trees
+        (dict(P=17, n=1000, algo="generalized", knob=4), K.AR_KERNEL_DAG),  # more ranks than the compiled form
         (dict(P=127, n=106, algo="generalized", knob=7), K.AR_KERNEL_DAG),
         (dict(P=127, n=1 << 16, algo="generalized", knob=4), K.AR_KERNEL_DAG),
         (dict(P=63, n=106, algo="generalized", knob=6), K.AR_KERNEL_DAG),
