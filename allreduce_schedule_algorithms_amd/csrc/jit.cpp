@@ -272,7 +272,8 @@ bool jit_available(std::string* why) {
   return r->h != nullptr;
 }
 
-bool jit_source(const Schedule& s, int dtype, int op, std::string* src, int* vectors, std::string* why) {
+bool jit_source(const Schedule& s, int dtype, int op, int max_vectors, std::string* src, int* vectors,
+                std::string* why) {
   const Spec& sp = s.spec;
   if (sp.P > kJitMaxRanks) {
     *why = "more than " + std::to_string(kJitMaxRanks) + " ranks";
@@ -295,7 +296,9 @@ bool jit_source(const Schedule& s, int dtype, int op, std::string* src, int* vec
   // two vectors per thread where the live values fit the register budget
   // (measured 23% faster than one on 7 x 2^24 fp32), else one
   const int per_vector = dtype == D_BF16 ? 8 : 4;
-  *vectors = live * 2 * per_vector <= kJitRegisterBudget ? 2 : live * per_vector <= kJitRegisterBudget ? 1 : 0;
+  *vectors = max_vectors >= 2 && live * 2 * per_vector <= kJitRegisterBudget ? 2
+             : live * per_vector <= kJitRegisterBudget                       ? 1
+                                                                             : 0;
   if (!*vectors) {
     *why = std::to_string(live) + " values live at once exceed the register budget";
     return false;

@@ -46,9 +46,11 @@ struct JitArgs {
 
 // Source of the kernel `ar_jit` for schedule s with the given element type and
 // operation (Dtype, Op of sched.h); *vectors is the 16-byte vectors a thread
-// takes per item (1 or 2; work items then hold 256 x *vectors vectors). False
-// (and *why) when a range's program exceeds the limits above.
-bool jit_source(const Schedule& s, int dtype, int op, std::string* src, int* vectors, std::string* why);
+// takes per item (at most max_vectors, 1 or 2; work items then hold 256 x
+// *vectors vectors). False (and *why) when a range's program exceeds the
+// limits above.
+bool jit_source(const Schedule& s, int dtype, int op, int max_vectors, std::string* src, int* vectors,
+                std::string* why);
 
 // Compile src for gfx950 (no packed fp32, no contraction, IEEE denormals).
 bool jit_compile(const std::string& src, std::vector<char>* code, std::string* err);

@@ -63,3 +63,18 @@ def test_jit_batches_and_more_steps():
         for mis in (False, True):
             got = gpu_allreduce(x, algo, dtype, op, r, "fused", batch=B, misalign=mis, steps=steps)
             assert np.array_equal(bits(got.reshape(P, B, n)), bits(want)), (P, n, r, B, dtype, op, mis)
+
+
+def test_jit_two_vectors_per_thread_sampled():
+    # calls of at least 2^20 vectors take two vectors per thread where the live
+    # values fit; sampled offsets against the oracle (every part of the buffer)
+    import allreduce_schedule_algorithms_amd as A
+    for P, r, dtype, op in ((7, 2, "int32", "max"), (5, 1, "fp32", "avg"), (6, 2, "fp32", "sum")):
+        n = (1 << 22) + 40
+        assert _kernel(P, n, dtype, "generalized", r) == A.Kernel.AR_KERNEL_JIT
+        x = inputs.make(dtype, P, n, seed=P + r)
+        idx = inputs.sample_indices(n, P, count=4096)
+        want = oracle.allreduce(np.ascontiguousarray(x[:, idx]), "generalized", dtype, op, knob=r, n=n, idx=idx)
+        got = gpu_allreduce(x, "generalized", dtype, op, r, "fused")
+        assert np.array_equal(bits(got[:, idx]), bits(want)), (P, r, dtype, op)
+
