@@ -785,11 +785,13 @@ void choose_kernel(Plan& pl) {
     pl.fallback = "no replay program (" + s.fused_error + ")";
     return;
   }
-  // Several result trees per range over few ranks and ranges: the range's DAG
-  // as straight-line register code, compiled for the schedule (jit.h), where
-  // hipRTC is there to compile it; otherwise the kernels below.
-  if (pl.exec == E_FUSED && fixed_shapes_enabled() && jit_enabled() && s.max_trees > 1 && !strided_items(s) &&
-      s.spec.P <= kJitMaxRanks && int(s.ranges.size()) <= kJitMaxRanges) {
+  // Several result trees per range, or a latency-bound call over more than 8
+  // ranks, with few ranks and ranges: the range's DAG as straight-line register
+  // code, compiled for the schedule (jit.h), where hipRTC is there to compile
+  // it; otherwise the kernels below.
+  const bool jit_tiny = s.spec.n * s.spec.batch <= kTinyElements && s.spec.P > 8;
+  if (pl.exec == E_FUSED && fixed_shapes_enabled() && jit_enabled() && (s.max_trees > 1 || jit_tiny) &&
+      !strided_items(s) && s.spec.P <= kJitMaxRanks && int(s.ranges.size()) <= kJitMaxRanges) {
     if (jit_code_for(s, &pl.jit_code, &pl.jit_vectors, &pl.jit_note)) {
       pl.kernel = K_JIT;
       return;

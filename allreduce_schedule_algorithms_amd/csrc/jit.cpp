@@ -21,7 +21,7 @@ namespace {
 const char* kPrelude = R"(
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 struct Item { long long start; int count; int tag; };
-struct Args { void* p[16]; const Item* items; float div; int pad; };
+struct Args { void* p[32]; const Item* items; float div; int pad; };
 #if AR_DT == 0
 typedef unsigned A;
 #define AR_V 4

@@ -28,9 +28,9 @@ struct JitKernel {
 
 // Limits of the register form: ranks (buffer pointers in the kernel argument),
 // ranges (one function each), distinct combinations per range.
-constexpr int kJitMaxRanks = 16;
+constexpr int kJitMaxRanks = 32;
 constexpr int kJitMaxRanges = 16;
-constexpr int kJitMaxNodes = 128;
+constexpr int kJitMaxNodes = 256;
 // 32-bit registers per thread for values live at once (fragments of one or two
 // 16-byte vectors per value, widened to fp32 for bf16)
 constexpr int kJitRegisterBudget = 192;

@@ -575,8 +575,8 @@ def test_rows_kernel_batches():
              (3, 106, "generalized", 0, 57, K.AR_KERNEL_ROWS_VEC, (("fp32", "avg"),)),
              (8, 64, "ring", 0, 129, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"), ("int32", "sum"))),
              (27, 90, "ring", 0, 213, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"),)),
-             (24, 106, "generalized", 5, 500, K.AR_KERNEL_DAG, (("fp32", "sum"), ("int32", "max"), ("fp32", "avg"))),
-             (24, 20_001, "generalized", 4, 1, K.AR_KERNEL_DAG, (("fp32", "sum"),)),
+             (24, 106, "generalized", 5, 500, K.AR_KERNEL_JIT, (("fp32", "sum"), ("int32", "max"), ("fp32", "avg"))),
+             (24, 20_001, "generalized", 4, 1, K.AR_KERNEL_JIT, (("fp32", "sum"),)),
              (24, 106, "generalized", 1, 200, K.AR_KERNEL_STRIDED, (("fp32", "sum"),))]
     for i, (P, n, algo, knob, B, kern, types) in enumerate(cases):
         assert A.ar_kernel_of(A.make_call(P, n, "fp32", "sum", algo, knob, batch=B)) == kern, (P, n, algo, knob)

@@ -386,14 +386,17 @@ def test_kernel_choice():
         (dict(P=7, n=1 << 24, algo="generalized", knob=1), K.AR_KERNEL_JIT),
         (dict(P=7, n=1 << 20, algo="generalized", knob=2, dtype="bf16"), K.AR_KERNEL_JIT),
         (dict(P=12, n=4099, algo="generalized", knob=2), K.AR_KERNEL_JIT),
-        (dict(P=24, n=106, algo="generalized", knob=5, batch=10_000), K.AR_KERNEL_DAG),
+        (dict(P=24, n=106, algo="generalized", knob=5, batch=10_000), K.AR_KERNEL_JIT),
+        # bf16 values take two registers each: 24 live leaves exceed the budget
         (dict(P=24, n=106, algo="generalized", knob=5, batch=10_000, dtype="bf16"), K.AR_KERNEL_DAG),
-        (dict(P=24, n=106, algo="generalized", knob=5, batch=30), K.AR_KERNEL_DAG),
-        (dict(P=24, n=106, algo="rd"), K.AR_KERNEL_DAG),  # latency-bound, many ranks, shallow tree
-        (dict(P=24, n=106, algo="binomial"), K.AR_KERNEL_DAG),
+        (dict(P=24, n=106, algo="generalized", knob=5, batch=30), K.AR_KERNEL_JIT),
+        (dict(P=24, n=106, algo="rd"), K.AR_KERNEL_JIT),  # latency-bound over more than 8 ranks
+        (dict(P=24, n=106, algo="binomial"), K.AR_KERNEL_JIT),
+        (dict(P=24, n=106, algo="generalized"), K.AR_KERNEL_DAG),  # 24 ranges: more than the compiled form takes
         (dict(P=127, n=106, algo="generalized"), K.AR_KERNEL_DAG),
         (dict(P=24, n=106, algo="ring"), K.AR_KERNEL_REPLAY),  # a chain: one level per rank
-        (dict(P=12, n=106, algo="rd"), K.AR_KERNEL_REPLAY),
+        (dict(P=12, n=106, algo="rd"), K.AR_KERNEL_JIT),
+        (dict(P=12, n=5000, algo="rd"), K.AR_KERNEL_REPLAY),
         (dict(P=192, n=1 << 20, dtype="bf16", algo="ahc", groups=[64, 128]), K.AR_KERNEL_REPLAY),
         (dict(P=24, n=106, algo="rd", batch=10_000), K.AR_KERNEL_REPLAY),
         (dict(P=24, n=106, algo="generalized", batch=10_000), K.AR_KERNEL_ROWS_VEC),
