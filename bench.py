@@ -101,7 +101,7 @@ def ceil_log2(P: int) -> int:
 def kernel_source_hash() -> str:
     """Hash of the device code and of the executor that lays out its work items."""
     h = hashlib.sha256()
-    for name in ("kernels.h", "launch.h", "exec.hip"):
+    for name in ("kernels.h", "launch.h", "exec.hip", "jit.cpp"):
         with open(os.path.join(ROOT, "allreduce_schedule_algorithms_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -764,10 +764,17 @@ PROFILE_COMMANDS = """command (kernel trace):
 commands (counters, one pass each):
   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof/{case}/fetch -o c --output-format csv -- python3 bench.py --workload {wl} --schedule {key} --steps 3 --warmup 1 --no-cpu --no-extras
   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof/{case}/write -o c --output-format csv -- python3 bench.py --workload {wl} --schedule {key} --steps 3 --warmup 1 --no-cpu --no-extras
+  rocprofv3 --pmc {sq} -d gpurun_out/prof/{case}/sq -o c --output-format csv -- python3 bench.py --workload {wl} --schedule {key} --steps 3 --warmup 1 --no-cpu --no-extras
   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof/calib/fetch -o c --output-format csv -- python3 bench.py --calibrate-copy 512
   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof/calib/write -o c --output-format csv -- python3 bench.py --calibrate-copy 512
 summary:
   python3 bench.py --summarize-profiles gpurun_out/prof"""
+
+
+# the shader-sequencer counters of the profile's third pass (at most 8 SQ
+# counters fit one pass)
+SQ_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT",
+               "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_LDS")
 
 
 def _csv_rows(pattern):
@@ -797,6 +804,19 @@ def _counter_kib(dirpath, counter):
         acc.setdefault(name, {}).setdefault(disp, 0.0)
         acc[name][disp] += float(_col(row, "Counter_Value"))
     return {k: (statistics.fmean(v.values()), len(v)) for k, v in acc.items()}
+
+
+def _counters(dirpath, kernel):
+    """Mean value per dispatch of every counter recorded for `kernel`."""
+    acc = {}
+    for row in _csv_rows(os.path.join(dirpath, "**", "*counter_collection.csv")):
+        if _col(row, "Kernel_Name") != kernel:
+            continue
+        name = _col(row, "Counter_Name")
+        disp = _col(row, "Dispatch_Id", "Correlation_Id")
+        acc.setdefault(name, {}).setdefault(disp, 0.0)
+        acc[name][disp] += float(_col(row, "Counter_Value"))
+    return {k: statistics.fmean(v.values()) for k, v in acc.items()}
 
 
 def _kernel_stats(dirpath):
@@ -856,7 +876,7 @@ def summarize_profiles(root):
         launches = line["roofline"].get("launches_per_call", 1)
         lines = [f"# {dom_name} on {line['config']['workload']}; schedule {key}",
                  f"# kernel source hash {traffic['kernel_hash']}", "",
-                 PROFILE_COMMANDS.format(case=case, wl=wl, key=key), "",
+                 PROFILE_COMMANDS.format(case=case, wl=wl, key=key, sq=" ".join(SQ_COUNTERS)), "",
                  "kernel stats (rocprofv3 --stats, all kernels of the run):",
                  f"  {'name':70s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
         for s in stats[:6]:
@@ -882,6 +902,18 @@ def summarize_profiles(root):
                       f"  traffic / algorithmic = {tb / (alg / launches):.4f}",
                       f"  scale factors from a plain 512 MiB device copy: FETCH_SIZE reads {cal_f:.0f} KiB, "
                       f"WRITE_SIZE {cal_w:.0f} KiB for 524288 KiB moved each way"]
+        sq = _counters(os.path.join(cdir, "sq"), dom["name"])
+        if sq.get("SQ_WAVES"):
+            waves = sq["SQ_WAVES"]
+            lines += ["", "shader sequencer (per dispatch; per wave where it is a count of instructions):"]
+            for c in SQ_COUNTERS:
+                if c in sq:
+                    per = f"  ({sq[c] / waves:.1f} per wave)" if c.startswith("SQ_INSTS") else ""
+                    lines.append(f"  {c:22s} {sq[c]:14.0f}{per}")
+            if "SQ_INSTS_LDS" in sq and "SQ_LDS_BANK_CONFLICT" in sq:
+                lines.append(f"  LDS bank-conflict cycles per LDS instruction: "
+                             f"{sq['SQ_LDS_BANK_CONFLICT'] / max(sq['SQ_INSTS_LDS'], 1):.2f}")
+            entry["sq"] = {c: round(sq[c]) for c in SQ_COUNTERS if c in sq}
         traffic["entries"][f"{wl}/{key}"] = entry
         safe = key.replace("/", "_")
         path = os.path.join(ROOT, "profiles", f"{dom_name}_{wl}_{safe}.txt")
