@@ -401,7 +401,9 @@ class Schedule:
         self._h = handle
 
     def __del__(self):
-        if getattr(self, "_h", None):
+        # at interpreter exit the module's globals may already be gone; the
+        # process then releases the schedule with everything else
+        if getattr(self, "_h", None) and lib is not None:
             lib.ar_schedule_free(self._h)
             self._h = None
 
