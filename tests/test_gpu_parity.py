@@ -734,9 +734,13 @@ def test_calls_captured_in_a_hip_graph():
     # the eager bits, with eager work (restoring the inputs) between replays
     import allreduce_schedule_algorithms_amd as A
     torch = torch_mod()
-    P, n, B = 6, 106, 40
-    for algo, knob in (("rd", 0), ("ring", 0), ("generalized", 1)):
-        x = inputs.make("fp32", P, n * B, seed=B + knob)
+    n, B = 106, 40
+    # fixed-shape kernels, and the compiled register DAG (several trees; a
+    # latency-bound call over 12 ranks), launched as module kernels
+    for P, algo, knob in ((6, "rd", 0), (6, "ring", 0), (6, "generalized", 1), (12, "rd", 0), (12, "generalized", 2)):
+        if P == 12:
+            assert A.ar_kernel_of(A.make_call(P, n, "fp32", "sum", algo, knob)) == A.Kernel.AR_KERNEL_JIT
+        x = inputs.make("fp32", P, n * B, seed=B + knob + P)
         want = oracle.allreduce(x.reshape(P, B, n), algo, "fp32", "sum", knob=knob, n=n).reshape(P, B * n)
         bufs, keep = to_device(x, "fp32")
         pristine = [b.clone() for b in bufs]
