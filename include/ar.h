@@ -266,8 +266,9 @@ ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes);
  *  AR_KERNEL_DAG             the DAG replay: more than 8 result trees per range (the generalized
  *                            algorithm with large r at large P), and every call under
  *                            AR_EXEC_DAG; each distinct combination once, values in LDS.
- *  AR_KERNEL_JIT             several result trees per range over at most 16 ranks and 16 ranges
- *                            (the generalized algorithm with r > 0 on few ranks), not short
+ *  AR_KERNEL_JIT             several result trees per range, or a call of at most 4096 elements
+ *                            over more than 8 ranks, with at most 32 ranks and 16 ranges (the
+ *                            generalized algorithm with r > 0; latency-bound calls), not short
  *                            ranges of a batch: each range's DAG written out as straight-line
  *                            register code and compiled for the schedule with hipRTC on the
  *                            plan's first call (one compile per distinct program, kept for the

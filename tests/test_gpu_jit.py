@@ -1,5 +1,5 @@
 """GPU parity of the compiled register DAG (AR_KERNEL_JIT): several result trees
-per range over at most 16 ranks, each range's DAG written out as straight-line
+per range (or a latency-bound call) over at most 32 ranks, each range's DAG written out as straight-line
 register code and compiled for the schedule at run time. Bit-exact against the
 CPU oracle, every dtype and operation, aligned and unaligned buffers (vector
 and element paths), one and two vectors per thread, batches of long ranges."""

@@ -38,5 +38,5 @@ def test_jit_takes_no_workspace_and_keeps_batches_of_short_ranges_elsewhere():
     assert A.ar_workspace_bytes(call) == 0
     # short ranges of a batch: strided work, not the compiled kernel
     assert A.ar_kernel_of(A.make_call(24, 106, "fp32", "sum", "generalized", 1, batch=10_000)) == K.AR_KERNEL_STRIDED
-    # more than 16 ranks: the DAG replay
+    # 17 ranges (one per rank), more than the compiled form's 16: the DAG replay
     assert A.ar_kernel_of(A.make_call(17, 5000, "fp32", "sum", "generalized", 2)) == K.AR_KERNEL_DAG
