@@ -186,6 +186,10 @@ struct Plan {
   std::vector<char> jit_code;
   int jit_vectors = 2;     // 16-byte vectors per thread (items of kThreads * jit_vectors vectors)
   std::string jit_note;    // why a multi-tree program does not run compiled (empty otherwise)
+  bool jit_table = false;  // the table form: one tree shape for every range, ranks from jtab
+  std::vector<int32_t> jit_tab;
+  int jit_w = 0;           // words per range in jit_tab
+  DevBuf jtab;
   struct JitModule {
     JitKernel k;
     ~JitModule() { jit_unload(&k); }
@@ -644,12 +648,12 @@ RunResult build_items(Plan& pl, bool vec) {
     const bool jit = pl.kernel == K_JIT;
     const bool fixed = jit || pl.shape != SH_NONE || pl.multi;
     // k_fused_multi: one vector per thread per item (2-5% faster than two on 7 ranks, r = 1..3)
-    const int64_t iv = jit ? int64_t(kThreads) * pl.jit_vectors
+    const int64_t iv = jit ? int64_t(pl.jit_table ? 64 : kThreads) * pl.jit_vectors
                            : pl.multi ? int64_t(kThreads) : fixed ? int64_t(kThreads) * pl.md : replay_item_vectors();
     auto tag_of = [&](size_t i) { return fixed ? int32_t(i) : s.ranges[i].prog; };
     // the program-driven replay of single-tree programs takes the partial
     // vectors at range ends in its vector items
-    const int64_t limit = pl.kernel == K_REPLAY && s.max_trees == 1 ? sp.n * sp.batch : -1;
+    const int64_t limit = (pl.kernel == K_REPLAY && s.max_trees == 1) || pl.jit_table ? sp.n * sp.batch : -1;
     if (sp.batch == 1 || flat) {
       const int64_t mult = flat ? sp.batch : 1;
       for (size_t i = 0; i < s.ranges.size(); ++i)
@@ -674,6 +678,10 @@ RunResult build_items(Plan& pl, bool vec) {
         if (e != hipSuccess) return hip_fail(e, "uploading the range table");
       }
       sitems.clear();
+    }
+    if (pl.jit_table && !pl.jtab.p) {
+      hipError_t e = upload(pl.jtab, pl.jit_tab);
+      if (e != hipSuccess) return hip_fail(e, "uploading the rank table");
     }
     if (pl.multi && !pl.mtab.p) {
       std::vector<int32_t> t(8 + 8 * kMultiRangeWords + 16, 0);
@@ -712,6 +720,18 @@ RunResult build_items(Plan& pl, bool vec) {
       pl.built[mode] = true;
       return RunResult{};
     }
+  }
+  if (pl.jit_table) {
+    // element items of at most one element per lane (64), then four wave
+    // items per workgroup: pad with empty ones
+    std::vector<Item> w;
+    w.reserve(items.size() + 8);
+    for (const Item& x : items) {
+      if (x.count >= 0) { w.push_back(x); continue; }
+      for (int32_t k = 0; k < -x.count; k += 64) w.push_back(Item{x.start + k, -std::min(64, -x.count - k), x.tag});
+    }
+    while (w.size() % 4) w.push_back(Item{0, 0, 0});
+    items.swap(w);
   }
   hipError_t e = upload(pl.items[mode], items);
   if (e != hipSuccess) return hip_fail(e, "uploading work items");
@@ -777,6 +797,27 @@ bool jit_code_for(const Schedule& s, std::vector<char>* code, int* vectors, std:
   return true;
 }
 
+// The table-form kernel of s (jit.h), compiled once per distinct source.
+bool jit_table_code_for(const Schedule& s, Plan& pl, std::string* why) {
+  static std::mutex mu;
+  static std::map<std::string, std::pair<std::vector<char>, int>> cache;
+  if (!jit_available(why)) return false;
+  std::string src;
+  int vectors = 0;
+  if (!jit_table_source(s, s.spec.dtype, s.spec.op, 2, &src, &pl.jit_tab, &pl.jit_w, &vectors, why)) return false;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(src);
+  if (it == cache.end()) {
+    std::vector<char> c;
+    if (!jit_compile(src, &c, why)) return false;
+    it = cache.emplace(src, std::make_pair(std::move(c), vectors)).first;
+  }
+  pl.jit_code = it->second.first;
+  pl.jit_vectors = it->second.second;
+  pl.jit_table = true;
+  return true;
+}
+
 void choose_kernel(Plan& pl) {
   const Schedule& s = *pl.s;
   if (pl.exec == E_LITERAL) { pl.kernel = K_LITERAL; return; }
@@ -790,6 +831,16 @@ void choose_kernel(Plan& pl) {
   // code, compiled for the schedule (jit.h), where hipRTC is there to compile
   // it; otherwise the kernels below.
   const bool jit_tiny = s.spec.n * s.spec.batch <= kTinyElements && s.spec.P > 8;
+  // One range of single-tree programs over more than 32 ranks (halving and
+  // doubling, recursive doubling, the binomial tree, the pipelined chain): the
+  // tree shape compiled with a rank table, in wave-sized work items.
+  if (pl.exec == E_FUSED && fixed_shapes_enabled() && jit_enabled() && s.max_trees == 1 && s.ranges.size() == 1 &&
+      s.spec.P > kJitMaxRanks && !jit_tiny && !strided_items(s) && !pl.rows && pl.shape == SH_NONE) {
+    if (jit_table_code_for(s, pl, &pl.jit_note)) {
+      pl.kernel = K_JIT;
+      return;
+    }
+  }
   if (pl.exec == E_FUSED && fixed_shapes_enabled() && jit_enabled() && (s.max_trees > 1 || jit_tiny) &&
       !strided_items(s) && s.spec.P <= kJitMaxRanks && int(s.ranges.size()) <= kJitMaxRanges) {
     if (jit_code_for(s, &pl.jit_code, &pl.jit_vectors, &pl.jit_note)) {
@@ -899,7 +950,8 @@ void trace_plan(const Plan& pl) {
       << ": " << pl.dp.instr << " combinations per element in " << pl.dp.levels << " levels, " << pl.dp.S << " slots";
   if (pl.kernel == K_LITERAL) o << "; " << s.nsteps << " step launches" << (s.finalize_ops ? " + 1 finalize" : "");
   if (pl.kernel == K_JIT)
-    o << "; compiled register DAG, " << pl.jit_vectors << " vectors per thread, code object " << pl.jit_code.size()
+    o << "; compiled " << (pl.jit_table ? "tree shape with a rank table, wave items" : "register DAG")
+      << ", " << pl.jit_vectors << " vectors per thread, code object " << pl.jit_code.size()
       << " bytes";
   if (!pl.jit_note.empty()) o << "; not compiled: " << pl.jit_note;
   if (!pl.fallback.empty()) o << "; literal fallback: " << pl.fallback;
@@ -1275,10 +1327,22 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
         return r;
       }
     }
-    for (int64_t off = 0; off < nit; off += cap) {  // work items are independent
-      const Evs ei{off == 0 ? ev.start : nullptr, off + cap >= nit ? ev.stop : nullptr};
-      const int64_t cnt = std::min(cap, nit - off);
-      if (pl->kernel == K_JIT) {
+    const int64_t per = pl->jit_table ? 4 : 1;  // work items per workgroup
+    for (int64_t off = 0; off < nit; off += cap * per) {  // work items are independent
+      const Evs ei{off == 0 ? ev.start : nullptr, off + cap * per >= nit ? ev.stop : nullptr};
+      const int64_t cnt = std::min(cap * per, nit - off) / per;
+      if (pl->kernel == K_JIT && pl->jit_table) {
+        JitTabArgs ja;
+        std::memset(&ja, 0, sizeof(ja));
+        for (int q = 0; q < spec.P; ++q) ja.p[q] = ptrs.p[q];
+        ja.items = items + off;
+        ja.tab = pl->jtab.p;
+        ja.div = ptrs.div;
+        ja.w = pl->jit_w;
+        void* params[] = {&ja};
+        e = hipExtModuleLaunchKernel(static_cast<hipFunction_t>(pl->jit.k.fn), uint32_t(cnt * kThreads), 1, 1,
+                                     kThreads, 1, 1, 0, st, params, nullptr, ei.start, ei.stop, 0);
+      } else if (pl->kernel == K_JIT) {
         JitArgs ja;
         std::memset(&ja, 0, sizeof(ja));
         for (int q = 0; q < spec.P; ++q) ja.p[q] = ptrs.p[q];

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <sstream>
@@ -21,7 +23,6 @@ namespace {
 const char* kPrelude = R"(
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 struct Item { long long start; int count; int tag; };
-struct Args { void* p[32]; const Item* items; float div; int pad; };
 #if AR_DT == 0
 typedef unsigned A;
 #define AR_V 4
@@ -110,6 +111,7 @@ __device__ __forceinline__ void st1(void* base, long long e, A x, float div) {
 // The kernel body: one work item per workgroup of 256 threads; the range's
 // function is picked by the item's tag (uniform).
 const char* kKernelHead = R"(
+struct Args { void* p[32]; const Item* items; float div; int pad; };
 extern "C" __global__ __launch_bounds__(256) void ar_jit(Args a) {
   const Item it = a.items[blockIdx.x];
   if (it.count > 0) {
@@ -144,6 +146,146 @@ const char* kKernelMid = R"(
 const char* kKernelTail = R"(
       }
     }
+  }
+}
+)";
+
+// Device code of the table form: raw 16-byte vectors (or single elements) as
+// loaded, widened where a leaf is pushed; T points at the item's range row of
+// the rank table (leaves, then outputs), read through the constant address
+// space so that its words are scalar loads even after the kernel's stores.
+const char* kTabPrelude = R"(
+struct TArgs { void* p[256]; const Item* items; const int* tab; float div; int w; };
+typedef const __attribute__((address_space(4))) int* CI;
+template <int F> struct Raw { u32x4 q[F / AR_V]; };
+template <> struct Raw<1> { unsigned u; };
+template <int F> __device__ __forceinline__ Fr<F> wid(const Raw<F>& r) {
+  Fr<F> f;
+#pragma unroll
+  for (int j = 0; j < F / AR_V; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#if AR_DT == 2
+      f.v[j * 8 + 2 * i] = val(r.q[j][i] << 16);
+      f.v[j * 8 + 2 * i + 1] = val(r.q[j][i] & 0xffff0000u);
+#else
+      f.v[j * 4 + i] = val(r.q[j][i]);
+#endif
+    }
+  return f;
+}
+__device__ __forceinline__ Fr<1> wid(const Raw<1>& r) {
+  Fr<1> f;
+#if AR_DT == 2
+  f.v[0] = val(r.u << 16);
+#else
+  f.v[0] = val(r.u);
+#endif
+  return f;
+}
+// Loads and stores at a byte offset (32 bits) from a base the work item has
+// advanced to its first element (a scalar): the instructions then take the base
+// in scalar registers and one offset register for every leaf.
+#if AR_DT == 2
+typedef unsigned short S;
+#else
+typedef unsigned S;
+#endif
+__device__ __forceinline__ u32x4 ldq(const char* base, unsigned off) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
+}
+__device__ __forceinline__ unsigned ldu(const char* base, unsigned off) {
+  return __builtin_nontemporal_load(reinterpret_cast<const S*>(base + off));
+}
+template <int F> __device__ __forceinline__ void stq(char* base, unsigned off, const Fr<F>& f, int o, float div) {
+  u32x4 r;
+#if AR_DT == 2
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = to_bf16(fin(f.v[o + 2 * i], div)) | (to_bf16(fin(f.v[o + 2 * i + 1], div)) << 16);
+#else
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = bits(fin(f.v[o + i], div));
+#endif
+  __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(base + off));
+}
+__device__ __forceinline__ void stu(char* base, unsigned off, A x, float div) {
+#if AR_DT == 2
+  __builtin_nontemporal_store((S)to_bf16(fin(x, div)), reinterpret_cast<S*>(base + off));
+#else
+  __builtin_nontemporal_store(bits(fin(x, div)), reinterpret_cast<S*>(base + off));
+#endif
+}
+// a vector partly inside the range (its element indices [lo, hi) relative to
+// the item's first element): its elements inside, one at a time
+template <int F>
+__device__ __forceinline__ void stq_part(char* base, int e, const Fr<F>& f, int o, float div, int lo, int hi) {
+#pragma unroll
+  for (int i = 0; i < AR_V; ++i)
+    if (e + i >= lo && e + i < hi) stu(base, unsigned(e + i) * sizeof(S), f.v[o + i], div);
+}
+#define SB __builtin_amdgcn_sched_barrier(0)
+)";
+
+// The table-form kernel: one work item per workgroup; a vector item's count
+// holds its vectors in bits 0..15 and, at a range's ends, the elements before
+// the range (bits 16..23) and past it (bits 24..27), which are loaded with
+// their vector but not stored; element items take one element per thread.
+const char* kTabKernel = R"(
+extern "C" __global__ __launch_bounds__(256) void ar_jit(TArgs a) {
+  // TArgs is the only argument: its rank pointers are read in place, from the
+  // kernel argument segment, so that indexing them by a table value needs no
+  // private copy of the argument
+  typedef char* Ptr;
+  typedef const __attribute__((address_space(4))) Ptr* CP;
+  typedef const __attribute__((address_space(4))) Item* CIt;
+  const CP P = (CP)__builtin_amdgcn_kernarg_segment_ptr();
+  // one work item per wave, four per workgroup (the wave index made scalar:
+  // items and table rows are then scalar loads)
+  const int lane = threadIdx.x & 63;
+  const Item it = ((CIt)a.items)[blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
+  const float div = a.div;
+  const long long base = it.start * (long long)sizeof(S);  // the item's first element, in bytes
+  if (it.count > 0) {
+    const CI T = (CI)a.tab + (long long)it.tag * a.w;
+    const int nv = it.count & 0xffff;
+    if (lane >= nv) return;
+    const bool two = AR_M == 2 && lane + 64 < nv;
+    const unsigned o0 = unsigned(lane) * 16u, o1 = two ? o0 + 1024u : o0;
+    auto ld = [&](int k) {
+      const char* b = P[T[k]] + base;
+      Raw<AR_M * AR_V> r;
+      r.q[0] = ldq(b, o0);
+      if (AR_M == 2) r.q[AR_M - 1] = ldq(b, o1);
+      return r;
+    };
+    const Fr<AR_M * AR_V> x = shape<AR_M * AR_V>(ld);
+    // whole vectors inside the range are stored whole; a vector across one of
+    // its ends, element by element (only the items at a range's ends hold one)
+    const int lo = (it.count >> 16) & 0xff, hi = nv * AR_V - ((it.count >> 24) & 0xf);
+    const int e0 = lane * AR_V, e1 = e0 + 64 * AR_V;
+    const bool w0 = e0 >= lo && e0 + AR_V <= hi, w1 = e1 >= lo && e1 + AR_V <= hi;
+    const bool p0 = !w0 && e0 < hi && e0 + AR_V > lo, p1 = two && !w1 && e1 < hi && e1 + AR_V > lo;
+#pragma unroll 8
+    for (int j = 0; j < AR_NO; ++j) {
+      char* b = P[T[AR_NL + j]] + base;
+      if (w0) stq(b, o0, x, 0, div);
+      else if (p0) stq_part(b, e0, x, 0, div, lo, hi);
+      if (two) {
+        if (w1) stq(b, o1, x, AR_V, div);
+        else if (p1) stq_part(b, e1, x, AR_V, div, lo, hi);
+      }
+    }
+  } else if (lane < -it.count) {
+    // element items (at most 64 elements): one element per lane. Their table
+    // row is read through an offset the compiler cannot equate with the vector
+    // path's, so that it does not merge the two paths' table reads and hoist
+    // all of them above the branch.
+    const CI Te = (CI)a.tab + __builtin_amdgcn_readfirstlane(it.tag * a.w);
+    const unsigned o = unsigned(lane) * sizeof(S);
+    auto ld = [&](int k) { Raw<1> r; r.u = ldu(P[Te[k]] + base, o); return r; };
+    const Fr<1> x = shape<1>(ld);
+#pragma unroll 8
+    for (int j = 0; j < AR_NO; ++j) stu(P[Te[AR_NL + j]] + base, o, x.v[0], div);
   }
 }
 )";
@@ -317,11 +459,110 @@ bool jit_source(const Schedule& s, int dtype, int op, int max_vectors, std::stri
   return true;
 }
 
+bool jit_table_source(const Schedule& s, int dtype, int op, int max_vectors, std::string* src, std::vector<int32_t>* tab,
+                      int* w, int* vectors, std::string* why) {
+  const Spec& sp = s.spec;
+  if (sp.P > kJitTabRanks) {
+    *why = "more than " + std::to_string(kJitTabRanks) + " ranks";
+    return false;
+  }
+  if (s.max_trees != 1 || s.ranges.empty()) {
+    *why = "not one result tree per range";
+    return false;
+  }
+  // the shape of the first range; every other range must repeat it
+  const int32_t* w0 = s.prog.data() + s.ranges[0].prog;
+  const int nl = w0[1], no = w0[2];
+  if (w0[0] != 1 || nl < 1 || no < 1 || nl > 1024) {
+    *why = "a tree of " + std::to_string(nl) + " leaves";
+    return false;
+  }
+  const int32_t* nc0 = w0 + 3 + nl;
+  *w = nl + no;
+  tab->assign(s.ranges.size() * size_t(*w), 0);
+  for (size_t r = 0; r < s.ranges.size(); ++r) {
+    const int32_t* x = s.prog.data() + s.ranges[r].prog;
+    if (x[0] != 1 || x[1] != nl || x[2] != no || !std::equal(nc0, nc0 + nl, x + 3 + nl)) {
+      *why = "range " + std::to_string(r) + " has another tree shape than range 0";
+      return false;
+    }
+    int32_t* row = tab->data() + r * size_t(*w);
+    std::copy(x + 3, x + 3 + nl, row);                   // leaf ranks, postfix order
+    std::copy(x + 3 + 2 * nl, x + 3 + 2 * nl + no, row + nl);  // output ranks
+  }
+  // the postfix program on a stack of value names: every combination pops two
+  std::ostringstream body;
+  std::vector<std::string> stk;
+  int most = 0, ci = 0;
+  const int batch = kJitTableBatch, ahead = 1;
+  const int nb = (nl + batch - 1) / batch;
+  auto loads = [&](int b) {
+    for (int k = b * batch; k < std::min(nl, (b + 1) * batch); ++k)
+      body << "  const Raw<F> r" << k << " = ld(" << k << ");\n";
+  };
+  for (int b = 0; b <= ahead && b < nb; ++b) loads(b);
+  for (int b = 0; b < nb; ++b) {
+    body << "  SB;\n";
+    for (int k = b * batch; k < std::min(nl, (b + 1) * batch); ++k) {
+      body << "  const Fr<F> w" << k << " = wid(r" << k << ");\n";
+      stk.push_back("w" + std::to_string(k));
+      most = std::max(most, int(stk.size()));
+      for (int c = 0; c < nc0[k]; ++c) {
+        if (stk.size() < 2) {
+          *why = "a combination with fewer than two values on the stack";
+          return false;
+        }
+        const std::string right = stk.back();
+        stk.pop_back();
+        const std::string left = stk.back();
+        stk.pop_back();
+        body << "  const Fr<F> c" << ci << " = add(" << left << ", " << right << ");\n";
+        stk.push_back("c" + std::to_string(ci++));
+      }
+    }
+    if (b + ahead + 1 < nb) {
+      body << "  SB;\n";
+      loads(b + ahead + 1);
+    }
+  }
+  if (stk.size() != 1) {
+    *why = "the tree leaves " + std::to_string(stk.size()) + " values";
+    return false;
+  }
+  body << "  SB;\n  return " << stk.back() << ";\n";
+  // registers per thread: raw vectors in flight, values on the stack; two
+  // vectors per lane where they fit
+  const int per_vector = dtype == D_BF16 ? 8 : 4;
+  auto regs = [&](int v) { return (ahead + 1) * batch * v * 4 + most * v * per_vector; };
+  *vectors = max_vectors >= 2 && regs(2) <= kJitTableRegisters ? 2 : regs(1) <= kJitTableRegisters ? 1 : 0;
+  if (!*vectors) {
+    *why = std::to_string(regs(1)) + " registers per thread for loads in flight and stack values";
+    return false;
+  }
+  std::ostringstream o;
+  o << "#define AR_DT " << dtype << "\n#define AR_OP " << op << "\n#define AR_M " << *vectors << "\n#define AR_NL "
+    << nl << "\n#define AR_NO " << no << "\n"
+    << kPrelude << kTabPrelude
+    << "template <int F, typename LD> __device__ __forceinline__ Fr<F> shape(LD& ld) {\n"
+    << body.str() << "}\n"
+    << kTabKernel;
+  *src = o.str();
+  return true;
+}
+
 bool jit_compile(const std::string& src, std::vector<char>* code, std::string* err) {
   Rtc* r = rtc();
   if (!r->h) {
     *err = r->why;
     return false;
+  }
+  if (const char* dir = std::getenv("AR_JIT_SOURCE")) {  // a directory: keep each compiled source there
+    static int seq = 0;
+    const std::string path = std::string(dir) + "/ar_jit_" + std::to_string(seq++) + ".hip";
+    if (FILE* f = std::fopen(path.c_str(), "w")) {
+      std::fwrite(src.data(), 1, src.size(), f);
+      std::fclose(f);
+    }
   }
   void* prog = nullptr;
   if (r->create(&prog, src.c_str(), "ar_jit.hip", 0, nullptr, nullptr) != 0) {

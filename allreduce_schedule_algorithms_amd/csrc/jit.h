@@ -52,6 +52,30 @@ struct JitArgs {
 bool jit_source(const Schedule& s, int dtype, int op, int max_vectors, std::string* src, int* vectors,
                 std::string* why);
 
+// Table form, for programs of one result tree per range in which every
+// range's tree has one shape (leaf count, combinations after each leaf, output
+// count) and only the ranks differ: the shape is compiled once as straight-line
+// code, and each work item reads its range's leaf and output ranks from a
+// table (kJitTabRanks buffer pointers in the kernel argument). A work item is
+// one wave's (64 lanes x *vectors 16-byte vectors, or up to 64 single
+// elements), four per workgroup. Leaves are loaded in batches of
+// kJitTableBatch, the next batch in flight while one is combined.
+constexpr int kJitTabRanks = 256;
+constexpr int kJitTableBatch = 8;
+constexpr int kJitTableRegisters = 256;  // loads in flight and stack values, 32-bit registers per lane
+struct JitTabArgs {
+  void* p[kJitTabRanks];
+  const void* items;
+  const void* tab;  // int32 ranks: per range, its leaves (postfix order), then its outputs
+  float div;
+  int32_t w;        // words per range in tab
+};
+// *tab, *w: the rank table; *vectors: 16-byte vectors per lane (at most
+// max_vectors). False (and *why) when the ranges differ in shape or the
+// program exceeds the limits.
+bool jit_table_source(const Schedule& s, int dtype, int op, int max_vectors, std::string* src, std::vector<int32_t>* tab,
+                      int* w, int* vectors, std::string* why);
+
 // Compile src for gfx950 (no packed fp32, no contraction, IEEE denormals).
 bool jit_compile(const std::string& src, std::vector<char>* code, std::string* err);
 
