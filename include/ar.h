@@ -275,7 +275,11 @@ ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes);
  *                            process), loaded on the device at its first launch. Where hipRTC
  *                            is missing or the program exceeds the register budget, the
  *                            kernels above run instead (AR_TRACE=1 says why); AR_JIT=0 turns it
- *                            off. */
+ *                            off. It also runs one range of one result tree over more than 32
+ *                            ranks (halving and doubling, recursive doubling, the binomial tree,
+ *                            the pipelined chain at large P): the tree's shape compiled once,
+ *                            the leaf and output ranks read from a table, one work item per
+ *                            wave. */
 typedef enum {
   AR_KERNEL_NONE = 0,
   AR_KERNEL_DIRECT = 1,
