@@ -648,12 +648,22 @@ RunResult build_items(Plan& pl, bool vec) {
     const bool jit = pl.kernel == K_JIT;
     const bool fixed = jit || pl.shape != SH_NONE || pl.multi;
     // k_fused_multi: one vector per thread per item (2-5% faster than two on 7 ranks, r = 1..3)
-    const int64_t iv = jit ? int64_t(pl.jit_table ? 64 : kThreads) * pl.jit_vectors
+    int64_t iv = jit ? int64_t(pl.jit_table ? 64 : kThreads) * pl.jit_vectors
                            : pl.multi ? int64_t(kThreads) : fixed ? int64_t(kThreads) * pl.md : replay_item_vectors();
     auto tag_of = [&](size_t i) { return fixed ? int32_t(i) : s.ranges[i].prog; };
     // the program-driven replay of single-tree programs takes the partial
     // vectors at range ends in its vector items
     const int64_t limit = (pl.kernel == K_REPLAY && s.max_trees == 1) || pl.jit_table ? sp.n * sp.batch : -1;
+    if (pl.shape != SH_NONE && pl.md == 4 && vec && (sp.batch == 1 || flat)) {
+      // four vectors per thread only where their items fill whole rounds of the compute units
+      std::vector<Item> probe;
+      for (size_t i = 0; i < s.ranges.size(); ++i)
+        add_segment(probe, s.ranges[i].start, s.ranges[i].len * (flat ? sp.batch : 1), tag_of(i), V, vec, iv, limit);
+      if (!probe.empty() && !four_vectors_fit(int64_t(probe.size()), device_cus())) {
+        pl.md = 2;
+        iv = int64_t(kThreads) * pl.md;
+      }
+    }
     if (sp.batch == 1 || flat) {
       const int64_t mult = flat ? sp.batch : 1;
       for (size_t i = 0; i < s.ranges.size(); ++i)

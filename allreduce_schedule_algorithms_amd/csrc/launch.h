@@ -65,6 +65,31 @@ template <int DT, int OPK>
 hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total, int64_t max_blocks, hipStream_t st,
                            Evs ev);
 
+// Compute units of the current device (cached per device; 256 when HIP cannot tell).
+inline int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  cache[dev] = cus;
+  return cus;
+}
+
+// Whether `blocks` workgroups of four vectors per thread fill whole rounds of
+// the compute units well enough: launches of a few hundred workgroups run as
+// long as their busiest compute unit, so a last round of a few workgroups
+// (259 for 256 units: 6 ranks x 10^4 x 106 fp32) costs nearly a whole one;
+// twice the workgroups of two vectors then spread evenly (12.2 -> 10.1 us).
+inline bool four_vectors_fit(int64_t blocks, int cus) {
+  const int64_t rest = blocks % cus;
+  return blocks <= cus || rest == 0 || rest >= cus / 2;
+}
+
 #ifdef AR_LAUNCH_DEFINITIONS
 // Launches go through hipExtLaunchKernelGGL so that optional caller events can
 // be recorded at the kernel's own start and end.
@@ -471,7 +496,8 @@ hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total,
     if (P <= 16) return direct_b<DT, OPK, 16, 1>(vec, ptrs, P, total, max_blocks, st, ev);
     return direct_b<DT, OPK, 32, 1>(vec, ptrs, P, total, max_blocks, st, ev);
   }
-  if (vec && P <= 8 && total / TT<DT>::V <= (int64_t(1) << 19))
+  if (vec && P <= 8 && total / TT<DT>::V <= (int64_t(1) << 19) &&
+      four_vectors_fit((total / TT<DT>::V + 4 * kThreads - 1) / (4 * kThreads), device_cus()))
     return direct_m<DT, OPK, 4>(vec, ptrs, P, total, max_blocks, st, ev);
   // 9..32 ranks: one vector per thread, twice the workgroups (24 ranks x 1.06M
   // fp32: 41.3 -> 39.1 us); many more ranks keep two (192 ranks: 137 vs 147 us)
