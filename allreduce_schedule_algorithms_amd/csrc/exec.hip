@@ -587,7 +587,10 @@ RunResult literal_tables(Plan& pl, bool vec) {
 }
 
 // Build the fused or literal item tables for one alignment mode.
+bool trace_enabled();
+
 RunResult build_items(Plan& pl, bool vec) {
+  int64_t item_vectors_traced = 0;
   const Schedule& s = *pl.s;
   const Spec& sp = s.spec;
   const int V = vec_width(sp.dtype);
@@ -654,6 +657,28 @@ RunResult build_items(Plan& pl, bool vec) {
     // the program-driven replay of single-tree programs takes the partial
     // vectors at range ends in its vector items
     const int64_t limit = (pl.kernel == K_REPLAY && s.max_trees == 1) || pl.jit_table ? sp.n * sp.batch : -1;
+    if (vec && (sp.batch == 1 || flat) && !strided &&
+        (pl.kernel == K_REPLAY || (pl.kernel == K_JIT && !pl.jit_table && pl.jit_vectors == 1))) {
+      // items of one vector per thread: the fewest rounds of workgroups over
+      // the compute units that items of kThreads vectors need, shared out
+      // evenly (the smallest items that still need no more rounds), in whole
+      // 256-byte runs so that no two items split a cache line
+      auto count = [&](int64_t S) {
+        std::vector<Item> probe;
+        for (size_t i = 0; i < s.ranges.size(); ++i)
+          add_segment(probe, s.ranges[i].start, s.ranges[i].len * (flat ? sp.batch : 1), tag_of(i), V, vec, S, limit);
+        return int64_t(probe.size());
+      };
+      const int64_t cus = device_cus(), most = count(iv);
+      const int64_t cap = (most + cus - 1) / cus * cus;
+      int64_t lo = kThreads / 64, hi = iv / 16;  // in runs of 16 vectors; count(16 hi) <= cap
+      while (lo < hi) {
+        const int64_t mid = (lo + hi) / 2;
+        if (count(16 * mid) <= cap) hi = mid;
+        else lo = mid + 1;
+      }
+      iv = 16 * hi;
+    }
     if (pl.shape != SH_NONE && pl.md == 4 && vec && (sp.batch == 1 || flat)) {
       // four vectors per thread only where their items fill whole rounds of the compute units
       std::vector<Item> probe;
@@ -664,6 +689,7 @@ RunResult build_items(Plan& pl, bool vec) {
         iv = int64_t(kThreads) * pl.md;
       }
     }
+    item_vectors_traced = iv;
     if (sp.batch == 1 || flat) {
       const int64_t mult = flat ? sp.batch : 1;
       for (size_t i = 0; i < s.ranges.size(); ++i)
@@ -743,6 +769,9 @@ RunResult build_items(Plan& pl, bool vec) {
     while (w.size() % 4) w.push_back(Item{0, 0, 0});
     items.swap(w);
   }
+  if (trace_enabled())
+    std::fprintf(stderr, "ar: plan P=%d n=%lld: %zu work items (%s buffers, vector items of at most %lld vectors)\n",
+                 sp.P, (long long)sp.n, items.size(), vec ? "aligned" : "unaligned", (long long)item_vectors_traced);
   hipError_t e = upload(pl.items[mode], items);
   if (e != hipSuccess) return hip_fail(e, "uploading work items");
   pl.nitems[mode] = int64_t(items.size());
