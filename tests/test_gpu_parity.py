@@ -788,3 +788,21 @@ def test_plans_survive_a_cleared_schedule_cache():
     torch.cuda.synchronize()
     for ex in ("fused", "literal"):
         assert np.array_equal(bits(gpu_allreduce(x, "ring", "fp32", "sum", 0, ex)), bits(want))
+
+
+def test_many_ranks_ragged_ranges_in_sized_items():
+    # programs of many ranges over many ranks on ragged sizes: the program-driven
+    # replay sizes its items to whole rounds of workgroups over the compute
+    # units (items of 16-vector multiples below 256, partial vectors at every
+    # range end); every element against the oracle
+    import allreduce_schedule_algorithms_amd as A
+    cases = [(40, 30011, "bf16", "sum", "ring", 0), (70, 50001, "fp32", "max", "generalized", 0),
+             (100, 123457, "bf16", "avg", "ahc", 0), (150, 400003, "bf16", "sum", "ring", 0),
+             (63, 200001, "int32", "sum", "generalized", 0), (129, 99991, "fp32", "sum", "ring", 0)]
+    for i, (P, n, dtype, op, algo, r) in enumerate(cases):
+        g = groups_for(algo, P)
+        assert A.ar_kernel_of(A.make_call(P, n, dtype, op, algo, r, groups=g)) == A.Kernel.AR_KERNEL_REPLAY, (P, algo)
+        x = inputs.make(dtype, P, n, seed=900 + i)
+        want = oracle.allreduce(x, algo, dtype, op, knob=r, groups=g)
+        got = gpu_allreduce(x, algo, dtype, op, r, "fused", g)
+        assert np.array_equal(bits(got), bits(want)), (P, n, dtype, op, algo)
