@@ -226,10 +226,11 @@ __device__ __forceinline__ void stq_part(char* base, int e, const Fr<F>& f, int 
 #define SB __builtin_amdgcn_sched_barrier(0)
 )";
 
-// The table-form kernel: one work item per workgroup; a vector item's count
-// holds its vectors in bits 0..15 and, at a range's ends, the elements before
-// the range (bits 16..23) and past it (bits 24..27), which are loaded with
-// their vector but not stored; element items take one element per thread.
+// The table-form kernel: one work item per wave, four per workgroup; a vector
+// item's count holds its vectors in bits 0..15 and, at a range's ends, the
+// elements before the range (bits 16..23) and past it (bits 24..27), which are
+// loaded with their vector but not stored; element items take one element per
+// lane.
 const char* kTabKernel = R"(
 extern "C" __global__ __launch_bounds__(256) void ar_jit(TArgs a) {
   // TArgs is the only argument: its rank pointers are read in place, from the
