@@ -657,12 +657,21 @@ RunResult build_items(Plan& pl, bool vec) {
     // the program-driven replay of single-tree programs takes the partial
     // vectors at range ends in its vector items
     const int64_t limit = (pl.kernel == K_REPLAY && s.max_trees == 1) || pl.jit_table ? sp.n * sp.batch : -1;
+    if (pl.shape != SH_NONE && pl.md == 4 && vec && (sp.batch == 1 || flat)) {
+      // four vectors per thread only where their items fill whole rounds of the compute units
+      std::vector<Item> probe;
+      for (size_t i = 0; i < s.ranges.size(); ++i)
+        add_segment(probe, s.ranges[i].start, s.ranges[i].len * (flat ? sp.batch : 1), tag_of(i), V, vec, iv, limit);
+      if (!probe.empty() && !four_vectors_fit(int64_t(probe.size()), device_cus())) {
+        pl.md = 2;
+        iv = int64_t(kThreads) * pl.md;
+      }
+    }
     if (vec && (sp.batch == 1 || flat) && !strided &&
-        (pl.kernel == K_REPLAY || (pl.kernel == K_JIT && !pl.jit_table && pl.jit_vectors == 1))) {
-      // items of one vector per thread: the fewest rounds of workgroups over
-      // the compute units that items of kThreads vectors need, shared out
-      // evenly (the smallest items that still need no more rounds), in whole
-      // 256-byte runs so that no two items split a cache line
+        (pl.kernel == K_REPLAY || pl.shape != SH_NONE || (pl.kernel == K_JIT && !pl.jit_table && pl.jit_vectors == 1))) {
+      // the fewest rounds of workgroups over the compute units that full items
+      // need, shared out evenly (the smallest items that still need no more
+      // rounds), in whole 256-byte runs so that no two items split a cache line
       auto count = [&](int64_t S) {
         std::vector<Item> probe;
         for (size_t i = 0; i < s.ranges.size(); ++i)
@@ -678,16 +687,6 @@ RunResult build_items(Plan& pl, bool vec) {
         else lo = mid + 1;
       }
       iv = 16 * hi;
-    }
-    if (pl.shape != SH_NONE && pl.md == 4 && vec && (sp.batch == 1 || flat)) {
-      // four vectors per thread only where their items fill whole rounds of the compute units
-      std::vector<Item> probe;
-      for (size_t i = 0; i < s.ranges.size(); ++i)
-        add_segment(probe, s.ranges[i].start, s.ranges[i].len * (flat ? sp.batch : 1), tag_of(i), V, vec, iv, limit);
-      if (!probe.empty() && !four_vectors_fit(int64_t(probe.size()), device_cus())) {
-        pl.md = 2;
-        iv = int64_t(kThreads) * pl.md;
-      }
     }
     item_vectors_traced = iv;
     if (sp.batch == 1 || flat) {
