@@ -1335,14 +1335,16 @@ __device__ __forceinline__ void direct_one(const RankPtrs& ptrs, int P, int64_t 
 // 2 stays faster at 7 x 2^24 fp32 and at 192 ranks).
 constexpr int kDirectM = 2;
 
+// A workgroup takes `per` vectors (at most kThreads x MD): thread t the
+// vectors t, t + kThreads, ... below per.
 template <int DT, int OPK, bool VEC, int B, int MD = kDirectM>
-__global__ __launch_bounds__(kThreads) void k_direct(RankPtrs ptrs, int P, int64_t nvec, int64_t total) {
+__global__ __launch_bounds__(kThreads) void k_direct(RankPtrs ptrs, int P, int64_t nvec, int64_t total, int per) {
   constexpr int V = TT<DT>::V;
   if constexpr (VEC) {
-    const int64_t vb = int64_t(blockIdx.x) * kThreads * MD + threadIdx.x;
+    const int64_t vb = int64_t(blockIdx.x) * per + threadIdx.x;
     bool ok[MD];
 #pragma unroll
-    for (int j = 0; j < MD; ++j) ok[j] = vb + j * kThreads < nvec;
+    for (int j = 0; j < MD; ++j) ok[j] = int(threadIdx.x) + j * kThreads < per && vb + j * kThreads < nvec;
     if (ok[0]) direct_one<DT, OPK, MD, B>(ptrs, P, vb * V, ok);
     // the elements past the last whole vector: the last block's highest
     // threads, which a short launch leaves without vectors, so the tail does

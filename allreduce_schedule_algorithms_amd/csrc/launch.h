@@ -446,8 +446,20 @@ hipError_t direct_b(bool vec, const RankPtrs& ptrs, int P, int64_t total, int64_
                     Evs ev) {
   constexpr int V = TT<DT>::V;
   constexpr int64_t elt = sizeof(typename TT<DT>::S);
-  const int64_t unit = vec ? int64_t(kThreads) * MD * V : int64_t(kThreads);  // elements per workgroup
   const int64_t whole = vec ? total / V * V : total;  // elements the workgroups cover
+  // vectors per workgroup: kThreads x MD, or, for a launch of a few rounds of
+  // workgroups over the compute units, the smallest multiple of 16 that needs
+  // no more rounds, so that every unit gets the same count (fixed-shape replay:
+  // 6 ranks x 10^4 x 106 fp32 4.8 -> 5.4 TB/s)
+  int64_t per_block = int64_t(kThreads) * MD;
+  if (vec) {
+    const int64_t nvec = whole / V, full = (nvec + per_block - 1) / per_block;
+    if (full > 0 && full <= max_blocks) {
+      const int64_t cus = device_cus(), cap = (full + cus - 1) / cus * cus;
+      per_block = std::min(per_block, std::max<int64_t>(64, ((nvec + cap - 1) / cap + 15) / 16 * 16));
+    }
+  }
+  const int64_t unit = vec ? per_block * V : int64_t(kThreads);  // elements per workgroup
   const int64_t per = max_blocks * unit;
   RankPtrs pp = ptrs;
   int64_t done = 0;
@@ -459,10 +471,10 @@ hipError_t direct_b(bool vec, const RankPtrs& ptrs, int P, int64_t total, int64_
     const int64_t blocks = std::max<int64_t>(1, (len + unit - 1) / unit);
     if (vec) {
       hipExtLaunchKernelGGL((k_direct<DT, OPK, true, B, MD>), dim3(unsigned(blocks)), dim3(kThreads), 0, st,
-                            ei.start, ei.stop, 0, pp, P, len / V, last ? total - done : len);
+                            ei.start, ei.stop, 0, pp, P, len / V, last ? total - done : len, int(per_block));
     } else {
       hipExtLaunchKernelGGL((k_direct<DT, OPK, false, B>), dim3(unsigned(blocks)), dim3(kThreads), 0, st, ei.start,
-                            ei.stop, 0, pp, P, int64_t(0), len);
+                            ei.stop, 0, pp, P, int64_t(0), len, kThreads);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
