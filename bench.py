@@ -761,15 +761,15 @@ def extra_workload(name, flush, P=None, unbatched=False):
 # rocprofv3 output -> profiles/ summaries
 # --------------------------------------------------------------------------
 PROFILE_COMMANDS = """command (kernel trace):
-  rocprofv3 --kernel-trace --stats -d gpurun_out/prof/{case}/trace -o t --output-format csv -- python3 bench.py --workload {wl} --schedule {key} --steps 30 --warmup 5 --no-cpu --no-extras > gpurun_out/prof/{case}/bench.json
+  rocprofv3 --kernel-trace --stats -d {root}/{case}/trace -o t --output-format csv -- python3 bench.py --workload {wl} --schedule {key} --steps 30 --warmup 5 --no-cpu --no-extras > {root}/{case}/bench.json
 commands (counters, one pass each):
-  rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof/{case}/fetch -o c --output-format csv -- python3 bench.py --workload {wl} --schedule {key} --steps 3 --warmup 1 --no-cpu --no-extras
-  rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof/{case}/write -o c --output-format csv -- python3 bench.py --workload {wl} --schedule {key} --steps 3 --warmup 1 --no-cpu --no-extras
-  rocprofv3 --pmc {sq} -d gpurun_out/prof/{case}/sq -o c --output-format csv -- python3 bench.py --workload {wl} --schedule {key} --steps 3 --warmup 1 --no-cpu --no-extras
-  rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof/calib/fetch -o c --output-format csv -- python3 bench.py --calibrate-copy 512
-  rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof/calib/write -o c --output-format csv -- python3 bench.py --calibrate-copy 512
+  rocprofv3 --pmc FETCH_SIZE -d {root}/{case}/fetch -o c --output-format csv -- python3 bench.py --workload {wl} --schedule {key} --steps 3 --warmup 1 --no-cpu --no-extras
+  rocprofv3 --pmc WRITE_SIZE -d {root}/{case}/write -o c --output-format csv -- python3 bench.py --workload {wl} --schedule {key} --steps 3 --warmup 1 --no-cpu --no-extras
+  rocprofv3 --pmc {sq} -d {root}/{case}/sq -o c --output-format csv -- python3 bench.py --workload {wl} --schedule {key} --steps 3 --warmup 1 --no-cpu --no-extras
+  rocprofv3 --pmc FETCH_SIZE -d {root}/calib/fetch -o c --output-format csv -- python3 bench.py --calibrate-copy 512
+  rocprofv3 --pmc WRITE_SIZE -d {root}/calib/write -o c --output-format csv -- python3 bench.py --calibrate-copy 512
 summary:
-  python3 bench.py --summarize-profiles gpurun_out/prof"""
+  python3 bench.py --summarize-profiles {root}"""
 
 
 # the shader-sequencer counters of the profile's third pass (at most 8 SQ
@@ -877,7 +877,7 @@ def summarize_profiles(root):
         launches = line["roofline"].get("launches_per_call", 1)
         lines = [f"# {dom_name} on {line['config']['workload']}; schedule {key}",
                  f"# kernel source hash {traffic['kernel_hash']}", "",
-                 PROFILE_COMMANDS.format(case=case, wl=wl, key=key, sq=" ".join(SQ_COUNTERS)), "",
+                 PROFILE_COMMANDS.format(root=root.rstrip("/"), case=case, wl=wl, key=key, sq=" ".join(SQ_COUNTERS)), "",
                  "kernel stats (rocprofv3 --stats, all kernels of the run):",
                  f"  {'name':70s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
         for s in stats[:6]:
