@@ -806,3 +806,31 @@ def test_many_ranks_ragged_ranges_in_sized_items():
         want = oracle.allreduce(x, algo, dtype, op, knob=r, groups=g)
         got = gpu_allreduce(x, algo, dtype, op, r, "fused", g)
         assert np.array_equal(bits(got), bits(want)), (P, n, dtype, op, algo)
+
+
+def test_random_large_cases_on_gpu():
+    # larger random cases than the 2-16 rank draws above: 9-192 ranks, up to
+    # 3 x 10^5 elements, one- and many-range schedules, aligned and unaligned
+    # buffers, so that the round-sized items, the masked range ends, the
+    # compiled kernels and their element paths all run; every element against
+    # the oracle
+    import allreduce_schedule_algorithms_amd as A
+    rng = np.random.default_rng(4242)
+    kernels = set()
+    for _ in range(30):
+        P = int(rng.choice([9, 12, 17, 24, 33, 40, 63, 100, 127, 192]))
+        algo = str(rng.choice(["ring", "rh_rd", "rd", "binomial", "generalized", "ahc", "direct", "chain"]))
+        knob = int(rng.integers(1, 9)) if algo == "chain" else 0
+        if algo == "generalized" and P <= 24:
+            knob = int(rng.integers(0, nu.ceil_log2(P) + 1))
+        n = int(rng.integers(1000, 300_000 if P <= 64 else 100_000))
+        dtype = str(rng.choice(["int32", "fp32", "bf16"]))
+        op = str(rng.choice(["sum", "max"] + (["avg"] if dtype != "int32" else [])))
+        mis = bool(rng.random() < 0.25)
+        g = groups_for(algo, P)
+        kernels.add(A.ar_kernel_of(A.make_call(P, n, dtype, op, algo, knob, groups=g)).name)
+        x = inputs.make(dtype, P, n, seed=int(rng.integers(1 << 30)))
+        want = oracle.allreduce(x, algo, dtype, op, knob=knob, groups=g)
+        got = gpu_allreduce(x, algo, dtype, op, knob, "fused", g, misalign=mis)
+        assert np.array_equal(bits(got), bits(want)), (P, n, algo, knob, dtype, op, mis)
+    assert len(kernels) >= 4, kernels
