@@ -80,6 +80,13 @@ int64_t env_int(const char* name, int64_t dflt) {
   return x > 0 ? x : dflt;
 }
 
+// Buffers in leaf order for one-tree replay over at most 32 ranks (AR_ORDERED=0
+// keeps the rank lookups from the program, for comparisons).
+bool ordered_enabled() {
+  static const bool on = env_int("AR_ORDERED", 1) != 0;
+  return on;
+}
+
 // Vectors per work item of the program-driven replay (k_fused, k_fused_staged):
 // one per thread (measured 2-3% faster than two on the 24-rank batch and on
 // AHC's 192 ranks; the literal steps keep two).
@@ -155,6 +162,10 @@ struct Plan {
   std::vector<LitWork> lit_work[2], lit_packed[2];  // literal: the records on the host
   bool host_built[2] = {false, false};
   bool strided = false;  // fused: items are SItem (batches of short ranges)
+  // k_fused on one range of one tree over at most 32 ranks: the buffers go to
+  // the kernel in leaf order, then output order (these ranks)
+  bool ordered = false;
+  std::vector<int32_t> ordered_ranks;
   bool rows = false;      // fused: k_fused_rows (strided batches of one program shape)
   int rows_ref = 0;       // its reference range
   int64_t rows_n = 0;     // the instance length its table describes (1: one range, identity renaming)
@@ -953,6 +964,16 @@ registers:
   else if (pl.multi) pl.kernel = K_MULTI;
   else if (s.max_trees > 1 && s.spec.P <= kMaxStagedRanks) pl.kernel = K_STAGED;
   else pl.kernel = K_REPLAY;
+  if (pl.kernel == K_REPLAY && s.max_trees == 1 && s.ranges.size() == 1 && s.spec.P <= 32 && pl.D <= 8 &&
+      ordered_enabled()) {
+    const int32_t* w = s.prog.data() + s.ranges[0].prog;  // ntrees, leaves, outputs, ranks, counts, outputs
+    const int nl = w[1], no = w[2];
+    if (nl + no <= kMaxRanks) {
+      pl.ordered_ranks.assign(w + 3, w + 3 + nl);
+      pl.ordered_ranks.insert(pl.ordered_ranks.end(), w + 3 + 2 * nl, w + 3 + 2 * nl + no);
+      pl.ordered = true;
+    }
+  }
 }
 
 bool trace_enabled() {
@@ -1406,6 +1427,12 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
         AR_DISPATCH(spec.dtype, spec.op,
                     (e = launch_fused_fixed_t<DT, OPK>(pl->shape, pl->shape_nl, pl->md, cnt, ptrs, items + off,
                                                        pl->tab, st, ei)));
+      } else if (pl->ordered) {
+        RankPtrs op = ptrs;  // leaf buffers in postfix order, then the output buffers
+        for (size_t q = 0; q < pl->ordered_ranks.size(); ++q) op.p[q] = ptrs.p[pl->ordered_ranks[q]];
+        AR_DISPATCH(spec.dtype, spec.op,
+                    (e = launch_fused_t<DT, OPK>(pl->D, TM, spec.P, pl->s->max_leaves, cnt, op, items + off, prog,
+                                                 st, ei, true)));
       } else {
         AR_DISPATCH(spec.dtype, spec.op,
                     (e = launch_fused_t<DT, OPK>(pl->D, TM, spec.P, pl->s->max_leaves, cnt, ptrs, items + off, prog,

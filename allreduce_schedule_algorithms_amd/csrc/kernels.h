@@ -337,7 +337,9 @@ __device__ __forceinline__ void for_fragments(const Item& it, int V, F&& f) {
 // clause of loads in flight. The host picks B from the leaf count so that the
 // last batch is full where it can (B = 7 for seven leaves); otherwise the
 // missing slots repeat the batch's first leaf.
-template <int DT, int OPK, int D, int M, int B, typename WP, typename LeafAt>
+// IDL: the leaves are ranks 0, 1, ... in postfix order (the caller passes
+// the buffers in that order), so their ranks need no program read.
+template <int DT, int OPK, int D, int M, int B, bool IDL = false, typename WP, typename LeafAt>
 __device__ __forceinline__ void eval_one(WP __restrict__ w, LeafAt&& leaf_at,
                                          typename TT<DT>::A (&res)[nvals<DT, M>()]) {
   using A = typename TT<DT>::A;
@@ -353,7 +355,13 @@ __device__ __forceinline__ void eval_one(WP __restrict__ w, LeafAt&& leaf_at,
   for (int base = 0; base < nl; base += B) {
     u32x4 raw[B][mm<M>()];
     int cnt[B];
-    if constexpr (word_runs<WP>()) {  // whole runs of B words, clamped by value past the end
+    if constexpr (IDL) {
+#pragma unroll
+      for (int k = 0; k < B; ++k) {
+        leaf_at(base + k < nl ? base + k : base, raw[k]);
+        if constexpr (word_runs<WP>()) cnt[k] = nc[base + k];
+      }
+    } else if constexpr (word_runs<WP>()) {  // whole runs of B words, clamped by value past the end
       int rk[B];
 #pragma unroll
       for (int k = 0; k < B; ++k) {
@@ -393,23 +401,27 @@ __device__ __forceinline__ void eval_one(WP __restrict__ w, LeafAt&& leaf_at,
   for (int i = 0; i < N; ++i) res[i] = st[0][i];
 }
 
-template <int DT, int OPK, int D, int TM, int M, int B, bool NTS = true, bool EDGE = false, typename WP,
-          typename LeafAt>
+// IDL (one tree): leaves are ranks 0 .. nl - 1 and outputs nl, nl + 1, ... of
+// ptrs, which the caller orders so.
+template <int DT, int OPK, int D, int TM, int M, int B, bool NTS = true, bool EDGE = false, bool IDL = false,
+          typename WP, typename LeafAt>
 __device__ __forceinline__ void replay(const RankPtrs& ptrs, WP __restrict__ w, int64_t e,
                                        const bool (&ok)[mm<M>()], LeafAt&& leaf_at, int64_t lo = 0, int64_t hi = 0) {
+  static_assert(!IDL || TM == 1, "ordered buffers for one tree");
   using A = typename TT<DT>::A;
   const int ntrees = w[0];
   w += 1;
   A res[TM][nvals<DT, M>()];
   WP outs[TM];
-  int nouts[TM];
+  int nouts[TM], nls[TM];
 #pragma unroll
   for (int t = 0; t < TM; ++t) {
     if (t < ntrees) {
       const int nl = w[0];
+      nls[t] = nl;
       nouts[t] = w[1];
       outs[t] = w + 2 + 2 * nl;
-      eval_one<DT, OPK, D, M, B>(w, leaf_at, res[t]);
+      eval_one<DT, OPK, D, M, B, IDL>(w, leaf_at, res[t]);
       w = outs[t] + nouts[t];
     }
   }
@@ -421,8 +433,13 @@ __device__ __forceinline__ void replay(const RankPtrs& ptrs, WP __restrict__ w, 
 #pragma unroll
         for (int i = 0; i < nvals<DT, M>(); ++i) res[t][i] = res[t][i] / ptrs.div;
       }
-      st_user_all<DT, M, word_runs<WP>(), NTS, EDGE>(ptrs, nouts[t], [&](int i) { return ot[i]; }, e, ok, res[t], lo,
-                                                     hi);
+      if constexpr (IDL) {
+        const int first = nls[t];
+        st_user_all<DT, M, false, NTS, EDGE>(ptrs, nouts[t], [&](int i) { return first + i; }, e, ok, res[t], lo, hi);
+      } else {
+        st_user_all<DT, M, word_runs<WP>(), NTS, EDGE>(ptrs, nouts[t], [&](int i) { return ot[i]; }, e, ok, res[t],
+                                                       lo, hi);
+      }
     }
   }
 }
@@ -437,7 +454,7 @@ template <int DT, int D, int TM> constexpr int fused_m() {
   return (TM == 1 && D > 2 && D <= (DT == D_BF16 ? 4 : 8)) ? 2 : 1;
 }
 
-template <int DT, int OPK, int D, int TM, int B>
+template <int DT, int OPK, int D, int TM, int B, bool IDL = false>
 __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* __restrict__ items,
                                                     const int32_t* __restrict__ prog) {
   constexpr int V = TT<DT>::V;
@@ -460,18 +477,18 @@ __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* _
       bool ok[M];
 #pragma unroll
       for (int j = 0; j < M; ++j) ok[j] = ok0[j] && e + int64_t(j) * kThreads * V + V > lo;
-      replay<DT, OPK, D, TM, M, B, true, true>(
+      replay<DT, OPK, D, TM, M, B, true, true, IDL>(
           ptrs, wc, e, ok, [&](int rank, u32x4(&r)[M]) { ld_user<DT, M, NT>(ptrs.p[rank], e, ok, r); }, lo, hi);
     });
   } else if (it.count > 0) {
     for_fragments<M>(it, V, [&](int64_t e, const bool (&ok)[M]) {
-      replay<DT, OPK, D, TM, M, B>(ptrs, w, e, ok,
-                                   [&](int rank, u32x4(&r)[M]) { ld_user<DT, M, NT>(ptrs.p[rank], e, ok, r); });
+      replay<DT, OPK, D, TM, M, B, true, false, IDL>(
+          ptrs, w, e, ok, [&](int rank, u32x4(&r)[M]) { ld_user<DT, M, NT>(ptrs.p[rank], e, ok, r); });
     });
   } else {
     for_fragments<0>(it, V, [&](int64_t e, const bool (&ok)[1]) {
-      replay<DT, OPK, D, TM, 0, B>(ptrs, w, e, ok,
-                                   [&](int rank, u32x4(&r)[1]) { ld_user<DT, 0, NT>(ptrs.p[rank], e, ok, r); });
+      replay<DT, OPK, D, TM, 0, B, true, false, IDL>(
+          ptrs, w, e, ok, [&](int rank, u32x4(&r)[1]) { ld_user<DT, 0, NT>(ptrs.p[rank], e, ok, r); });
     });
   }
 }

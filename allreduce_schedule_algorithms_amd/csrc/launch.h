@@ -35,7 +35,7 @@ inline int leaf_batch(int P) {
 // P: ranks (LDS staging); leaves: the most leaves of one tree (leaf batch).
 template <int DT, int OPK>
 hipError_t launch_fused_t(int D, int TM, int P, int leaves, int64_t nitems, const RankPtrs& ptrs, const Item* items,
-                          const int32_t* prog, hipStream_t st, Evs ev);
+                          const int32_t* prog, hipStream_t st, Evs ev, bool ordered = false);
 template <int DT, int OPK>
 hipError_t launch_fused_strided_t(int D, int TM, int64_t nitems, const RankPtrs& ptrs, const SItem* items,
                                   const int32_t* prog, int64_t stride, hipStream_t st, Evs ev);
@@ -98,17 +98,56 @@ inline bool four_vectors_fit(int64_t blocks, int cus) {
 // empty slots in the last batch (larger on ties); 1 for single-leaf trees. Single-tree programs are
 // compiled for the (stack depth, batch) pairs that occur; others use 8.
 
-template <int DT, int OPK, int D, int B>
+template <int DT, int OPK, int D, int B, bool IDL = false>
 void fused1(const dim3& g, const dim3& b, hipStream_t st, Evs ev, const RankPtrs& ptrs, const Item* items,
             const int32_t* prog) {
-  hipExtLaunchKernelGGL((k_fused<DT, OPK, D, 1, B>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog);
+  hipExtLaunchKernelGGL((k_fused<DT, OPK, D, 1, B, IDL>), g, b, 0, st, ev.start, ev.stop, 0, ptrs, items, prog);
+}
+
+// One tree over at most 32 ranks with the buffers passed in leaf order, then
+// output order (`ordered`): the leaves' ranks need no program read.
+template <int DT, int OPK>
+void fused_ordered(int D, int B, const dim3& g, const dim3& b, hipStream_t st, Evs ev, const RankPtrs& ptrs,
+                   const Item* items, const int32_t* prog) {
+  if (D == 2) {
+    switch (B) {
+      case 1: fused1<DT, OPK, 2, 1, true>(g, b, st, ev, ptrs, items, prog); break;
+      case 2: fused1<DT, OPK, 2, 2, true>(g, b, st, ev, ptrs, items, prog); break;
+      case 3: fused1<DT, OPK, 2, 3, true>(g, b, st, ev, ptrs, items, prog); break;
+      case 4: fused1<DT, OPK, 2, 4, true>(g, b, st, ev, ptrs, items, prog); break;
+      case 5: fused1<DT, OPK, 2, 5, true>(g, b, st, ev, ptrs, items, prog); break;
+      case 6: fused1<DT, OPK, 2, 6, true>(g, b, st, ev, ptrs, items, prog); break;
+      case 7: fused1<DT, OPK, 2, 7, true>(g, b, st, ev, ptrs, items, prog); break;
+      default: fused1<DT, OPK, 2, 8, true>(g, b, st, ev, ptrs, items, prog); break;
+    }
+  } else if (D == 4) {
+    switch (B) {
+      case 3: fused1<DT, OPK, 4, 3, true>(g, b, st, ev, ptrs, items, prog); break;
+      case 4: fused1<DT, OPK, 4, 4, true>(g, b, st, ev, ptrs, items, prog); break;
+      case 5: fused1<DT, OPK, 4, 5, true>(g, b, st, ev, ptrs, items, prog); break;
+      case 6: fused1<DT, OPK, 4, 6, true>(g, b, st, ev, ptrs, items, prog); break;
+      case 7: fused1<DT, OPK, 4, 7, true>(g, b, st, ev, ptrs, items, prog); break;
+      default: fused1<DT, OPK, 4, 8, true>(g, b, st, ev, ptrs, items, prog); break;
+    }
+  } else {
+    switch (B) {
+      case 5: fused1<DT, OPK, 8, 5, true>(g, b, st, ev, ptrs, items, prog); break;
+      case 6: fused1<DT, OPK, 8, 6, true>(g, b, st, ev, ptrs, items, prog); break;
+      case 7: fused1<DT, OPK, 8, 7, true>(g, b, st, ev, ptrs, items, prog); break;
+      default: fused1<DT, OPK, 8, 8, true>(g, b, st, ev, ptrs, items, prog); break;
+    }
+  }
 }
 
 template <int DT, int OPK>
 hipError_t launch_fused_t(int D, int TM, int P, int leaves, int64_t nitems, const RankPtrs& ptrs, const Item* items,
-                          const int32_t* prog, hipStream_t st, Evs ev) {
+                          const int32_t* prog, hipStream_t st, Evs ev, bool ordered) {
   const dim3 g{unsigned(nitems), 1, 1};
   const dim3 b{unsigned(kThreads), 1, 1};
+  if (TM == 1 && ordered && D <= 8) {
+    fused_ordered<DT, OPK>(D, leaf_batch(std::min(P, leaves)), g, b, st, ev, ptrs, items, prog);
+    return hipGetLastError();
+  }
   if (TM == 1) {
     const int B = leaf_batch(std::min(P, leaves));
     if (D == 2) {
@@ -520,7 +559,7 @@ hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total,
 
 #define AR_INSTANTIATE_LAUNCHES(DT, OPK)                                                                    \
   template hipError_t launch_fused_t<DT, OPK>(int, int, int, int, int64_t, const RankPtrs&, const Item*,    \
-                                              const int32_t*, hipStream_t, Evs);                            \
+                                              const int32_t*, hipStream_t, Evs, bool);                      \
   template hipError_t launch_fused_fixed_t<DT, OPK>(int, int, int, int64_t, const RankPtrs&, const Item*,   \
                                                     const RankTab&, hipStream_t, Evs);                      \
   template hipError_t launch_fused_multi_t<DT, OPK>(int, int64_t, const MultiPtrs&, const Item*,          \
