@@ -431,6 +431,17 @@ bool rows_table(const Schedule& s, std::vector<uint8_t>* t, int* ref) {
     for (int64_t x = 0; x < P; ++x) (*t)[size_t(moff + x * R + r)] = uint8_t(map[size_t(x)] < 0 ? 0 : map[size_t(x)]);
   }
   t->resize((t->size() + 7) / 8 * 8, 0);  // k_fused_rows_vec copies it in 8-byte runs
+  if (P <= kRowsRegMaxRanks) {
+    // k_fused_rows_vec in registers: per offset o, one word whose bits
+    // 4 x .. 4 x + 3 hold the rank that reference leaf rank x reads at o
+    const size_t loff = t->size();
+    t->resize(loff + 4 * size_t(sp.n), 0);
+    for (int64_t o = 0; o < sp.n; ++o) {
+      uint32_t w = 0;
+      for (int64_t x = 0; x < P; ++x) w |= uint32_t((*t)[size_t(moff + x * R + cover[size_t(o)])]) << (4 * x);
+      std::memcpy(t->data() + loff + 4 * size_t(o), &w, sizeof w);
+    }
+  }
   return true;
 }
 

@@ -800,138 +800,239 @@ __global__ __launch_bounds__(kThreads) void k_fused_rows(RankPtrs ptrs, const in
 
 // The same batches with 4-byte elements, 16-byte aligned buffers and at most
 // 32 ranks, whose reference tree stores to all P ranks. Each wave works on
-// positions of 64 K consecutive elements (16 K vectors), K elements per lane,
-// and walks the positions of the launch with a stride of all its waves; the
-// grid holds what the device keeps resident. Per position:
-//  - the loads: with K = 1 (9..32 ranks) the P x 16 vectors are spread over
-//    the lanes, lane L loading vector L % 16 of ranks L / 16, L / 16 + 4, ...
-//    (G = ceil(P / 4) loads per lane; one instruction covers four 256-byte runs,
-//    which measured as fast as 1 KB runs of one rank); with K = 4 (at most 8
-//    ranks) lane L loads vector L of every rank (G = P loads of 1 KB runs).
-//    16-byte non-temporal loads, each line once, written to the wave's own LDS
-//    stage, [rank][element];
-//  - lane L evaluates the reference range's program for elements L, L + 64, ...
-//    reading leaf `rank` from the stage row of the rank its element's range
-//    renames it to (map[rank][range]: the lanes of one read hit consecutive
-//    bytes; stage reads hit consecutive words);
-//  - the results go through LDS once more, so that each lane stores whole
-//    vectors to the program's output ranks.
-// The loads of the next position are issued before the current one is
-// evaluated, so every wave keeps a position in flight while it works. Only the
-// wave reads what it wrote to its stage; wave-scope fences order the LDS
-// accesses. The waves of a workgroup share one copy of `tab` (the table of
-// k_fused_rows, padded to a multiple of 8 bytes) and of the buffer table.
+// positions of 64 K consecutive elements (16 K vectors) and walks the
+// positions of the launch with a stride of all its waves; the grid holds what
+// the device keeps resident. The loads of a wave's next position are issued
+// before the current one is evaluated, and its first position is loaded before
+// the tables are copied, so that memory round trip overlaps theirs (with one
+// position per wave, as on 3 or 6 ranks x 10^4 x 106 elements, it is the
+// wave's whole life). Three forms:
+//  - at most kRowsRegMaxRanks ranks (REG, K = 4): lane L loads vector L of
+//    every rank (G = P non-temporal 16-byte loads, 1 KB runs) and evaluates
+//    the reference range's program for its own four elements in registers.
+//    Leaf `rank` of an element is the loaded value of the rank that the
+//    element's range renames it to, picked by selects among the G loads; one
+//    LDS word per offset of an instance holds those ranks for every leaf
+//    (4 bits each). The results go straight from registers to the outputs.
+//    The selects grow as P^2 per element; past a few ranks the staged form
+//    below is faster.
+//  - staged, K = 4 (up to 8 ranks): lane L loads vector L of every rank
+//    (G = P loads) into the wave's own LDS stage, [rank][element];
+//  - staged, K = 1 (9..32 ranks): the P x 16 vectors are spread over the
+//    lanes, lane L loading vector L % 16 of ranks L / 16, L / 16 + 4, ...
+//    (G = ceil(P / 4) loads per lane; one instruction covers four 256-byte
+//    runs, which measured as fast as 1 KB runs of one rank), each line once.
+//  In the staged forms lane L evaluates the reference range's program for
+//  elements L, L + 64, ..., reading leaf `rank` from the stage row of the rank
+//  its element's range renames it to (map[rank][range]: the lanes of one read
+//  hit consecutive bytes; stage reads hit consecutive words); the results go
+//  through LDS once more, so that each lane stores whole vectors to the
+//  program's output ranks. Only the wave reads what it wrote to its stage;
+//  wave-scope fences order those LDS accesses.
+// The waves of a workgroup share one copy of the tables (those of k_fused_rows,
+// then the packed leaf ranks for at most kRowsRegMaxRanks ranks, each padded
+// to a multiple of 8 bytes) and, staged, of the output buffer table.
 constexpr int kRowsVecThreads = 256;  // at most; the host picks 1 or 4 waves per workgroup
+constexpr int kRowsRegMaxRanks = 3;   // ranks up to which the register form runs (even at 4, slower from 5)
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
-template <int DT, int OPK, int D, int B, int K, int G>
+template <int DT, int OPK, int D, int B, int K, int G, bool REG>
 __global__ __launch_bounds__(kRowsVecThreads) void k_fused_rows_vec(RankPtrs ptrs, const int32_t* __restrict__ prog,
                                                                     const uint8_t* __restrict__ tab, int64_t nvec,
                                                                     int32_t n, int32_t R, int32_t P) {
   static_assert(TT<DT>::V == 4, "four 4-byte elements per vector");
   static_assert(K == 1 || K == 4, "one or four elements per lane");
+  static_assert(!REG || (K == 4 && G <= kRowsRegMaxRanks), "the register form: one vector per lane and rank");
   using A = typename TT<DT>::A;
   constexpr int E = 64 * K, NV = 16 * K;  // elements and vectors of a position
   extern __shared__ uint32_t rows_vec_lds[];
-  const int lane = int(threadIdx.x) & 63, wave = int(threadIdx.x) >> 6, waves = int(blockDim.x) >> 6;
-  uint32_t* stage = rows_vec_lds + wave * (P + 1) * E;  // P rows of E words, then the E results
-  uint32_t* outw = stage + P * E;
-  // K = 1, buffer table: entry 4 i + y is the rank that lane group y loads in
-  // its i-th load, entry 4 (G + i) + y the output it stores to in its i-th
-  // store (past the last rank a group repeats it: the same vector from the same
-  // lane slot within one instruction, one request and one line, written back
-  // to the same stage word or output with the same value)
-  u32x4** ptab = reinterpret_cast<u32x4**>(rows_vec_lds + waves * (P + 1) * E);
-  uint32_t* tabw = reinterpret_cast<uint32_t*>(ptab + (K == 1 ? 8 * G : 0));
-  const ProgPtr tree = as_prog(prog) + 1;  // the reference range's single tree, P outputs
-  const ProgPtr outs = tree + 2 + 2 * tree[0];
-  auto cl = [P](int k) { return k < P ? k : P - 1; };
-  if constexpr (K == 1) {
-    if (threadIdx.x < 8 * G) {
-      const int e = int(threadIdx.x);
-      ptab[e] = static_cast<u32x4*>(e < 4 * G ? ptrs.p[cl(e)] : ptrs.p[outs[cl(e - 4 * G)]]);
-    }
-  }
-  const int moff = (n + 7) / 8 * 8;
-  const int words = (moff + R * P + 7) / 8 * 2;
-  for (int i = threadIdx.x; i < words; i += blockDim.x) tabw[i] = reinterpret_cast<const uint32_t*>(tab)[i];
-  __syncthreads();
-  const uint8_t* range_of = reinterpret_cast<const uint8_t*>(tabw);
-  const uint8_t* map = range_of + moff;  // [rank][range]
+  const int lane = int(threadIdx.x) & 63, waves = int(blockDim.x) >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
   const int64_t npos = (nvec + NV - 1) / NV;
   const int64_t stride = int64_t(gridDim.x) * waves;
   int64_t pos = int64_t(blockIdx.x) * waves + wave;
-  if (pos >= npos) return;
-  const int q = K == 1 ? lane & 15 : lane, y0 = K == 1 ? lane >> 4 : 0;  // vector in the position, lane group
+  const ProgPtr tree = as_prog(prog) + 1;  // the reference range's single tree, P outputs
+  const ProgPtr outs = tree + 2 + 2 * tree[0];
+  const int moff = (n + 7) / 8 * 8;
   const int ostep = int((stride * E) % n);
-  int o[K];  // offsets of the lane's elements in their instances
+  const int b0 = int(pos * E % n);  // the offset of the position's first element in its instance
+  if constexpr (REG) {
+    const u32x4* src[G];
+    u32x4* dst[G];
 #pragma unroll
-  for (int j = 0; j < K; ++j) o[j] = int((pos * E + 64 * j + lane) % n);
-  u32x4 cur[G];
-  // the last position may be partial: its lanes past the end repeat the last
-  // vector (within the instruction) and store nothing
-  auto load = [&](int64_t ps) {
-    const int64_t g = ps * NV + q < nvec ? ps * NV + q : nvec - 1;
+    for (int i = 0; i < G; ++i) src[i] = static_cast<const u32x4*>(ptrs.p[i]);
+    // the last position may be partial: its lanes past the end repeat the
+    // last vector and store nothing
+    auto load = [&](int64_t ps, u32x4(&r)[G]) {
+      const int64_t g = ps * NV + lane < nvec ? ps * NV + lane : nvec - 1;
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const u32x4* b = K == 1 ? ptab[4 * i + y0] : static_cast<const u32x4*>(ptrs.p[i]);
-      cur[i] = __builtin_nontemporal_load(b + g);
+      for (int i = 0; i < G; ++i) r[i] = __builtin_nontemporal_load(src[i] + g);
+    };
+    u32x4 ra[G], rb[G];
+    if (pos < npos) load(pos, ra);
+    uint32_t* lrank = rows_vec_lds;  // per offset: the rank each leaf reads, 4 bits per leaf rank
+    const uint32_t* lsrc = reinterpret_cast<const uint32_t*>(tab) + (moff + R * P + 7) / 8 * 2;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) lrank[i] = lsrc[i];
+#pragma unroll
+    for (int i = 0; i < G; ++i) dst[i] = static_cast<u32x4*>(ptrs.p[outs[i]]);
+    int o[4];  // offsets of the lane's elements in their instances
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = int(unsigned(b0 + 4 * lane + c) % unsigned(n));
+    __syncthreads();
+    if (pos >= npos) return;
+    // evaluate the position in `cur` (loads of the next one into `nxt` first)
+    auto step = [&](u32x4(&cur)[G], u32x4(&nxt)[G], bool more) {
+      if (more) load(pos + stride, nxt);
+      uint32_t pk[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) pk[c] = lrank[o[c]];
+      A res[nvals<DT, 1>()];
+      eval_one<DT, OPK, D, 1, B>(tree, [&](int rank, u32x4(&x)[1]) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t row = (pk[c] >> (4 * rank)) & 15u;
+          uint32_t y = cur[0][c];
+#pragma unroll
+          for (int i = 1; i < G; ++i) y = row == uint32_t(i) ? cur[i][c] : y;
+          x[0][c] = y;
+        }
+      }, res);
+      u32x4 rv;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (OPK == O_AVG) res[c] = res[c] / ptrs.div;
+        rv[c] = as_u(res[c]);
+      }
+      const int64_t g = pos * NV + lane;
+      if (g < nvec)
+#pragma unroll
+        for (int i = 0; i < G; ++i) __builtin_nontemporal_store(rv, dst[i] + g);
+    };
+    auto advance = [&] {
+      pos += stride;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        o[c] += ostep;
+        if (o[c] >= n) o[c] -= n;
+      }
+    };
+    // two register sets in turn, so that no loaded value is moved while its
+    // load may be in flight
+    for (;;) {
+      bool more = pos + stride < npos;
+      step(ra, rb, more);
+      if (!more) break;
+      advance();
+      more = pos + stride < npos;
+      step(rb, ra, more);
+      if (!more) break;
+      advance();
     }
-  };
-  // stage the loaded position, evaluate, store; `next` issues the following
-  // position's loads between the stage writes and the evaluation. Only a
-  // wave's last position can be partial.
-  auto step = [&](auto next, bool last) {
+  } else {
+    uint32_t* stage = rows_vec_lds + wave * (P + 1) * E;  // P rows of E words, then the E results
+    uint32_t* outw = stage + P * E;
+    const int q = K == 1 ? lane & 15 : lane, y0 = K == 1 ? lane >> 4 : 0;  // vector in the position, lane group
+    // the buffer of each load: K = 4, rank i; K = 1, rank 4 i + y0, and past
+    // the last rank the last rank again (the same vector from the same lane
+    // slot within one instruction: one request and one line, written to the
+    // same stage word with the same value). Chosen from the kernel argument by
+    // uniform selects at constant indices, once.
+    const u32x4* src[G];
+    if constexpr (K == 4) {
 #pragma unroll
-    for (int i = 0; i < G; ++i)
-      *reinterpret_cast<u32x4*>(stage + (K == 1 ? cl(4 * i + y0) : i) * E + q * 4) = cur[i];
-    next();
-    wave_lds_sync();
-    int rr[K];
-#pragma unroll
-    for (int j = 0; j < K; ++j) rr[j] = range_of[o[j]];
-    constexpr int M = K == 1 ? 0 : 1;
-    A res[nvals<DT, M>()];
-    eval_one<DT, OPK, D, M, B>(tree, [&](int rank, u32x4(&v)[1]) {
-#pragma unroll
-      for (int j = 0; j < K; ++j) v[0][j] = stage[map[rank * R + rr[j]] * E + 64 * j + lane];
-    }, res);
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      if constexpr (OPK == O_AVG) res[j] = res[j] / ptrs.div;
-      outw[64 * j + lane] = as_u(res[j]);
-    }
-    wave_lds_sync();
-    const u32x4 rv = *reinterpret_cast<const u32x4*>(outw + q * 4);
-    if (!last || pos * NV + q < nvec)
+      for (int i = 0; i < G; ++i) src[i] = static_cast<const u32x4*>(ptrs.p[i]);
+    } else {
+      const int lk = P - 1 - 4 * (G - 1);  // the last rank's place in the last group of four
+      void* const last = lk == 0 ? ptrs.p[4 * G - 4] : lk == 1 ? ptrs.p[4 * G - 3] : lk == 2 ? ptrs.p[4 * G - 2]
+                                                                                              : ptrs.p[4 * G - 1];
 #pragma unroll
       for (int i = 0; i < G; ++i) {
-        u32x4* d = K == 1 ? ptab[4 * (G + i) + y0] : static_cast<u32x4*>(ptrs.p[outs[i]]);
-        __builtin_nontemporal_store(rv, d + pos * NV + q);
-      }
-    wave_lds_sync();  // the next position's stage writes follow this one's reads
-  };
-  auto advance = [&] {
-    pos += stride;
+        void* c[4];
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      o[j] += ostep;
-      if (o[j] >= n) o[j] -= n;
+        for (int y = 0; y < 4; ++y) c[y] = 4 * i + y < P ? ptrs.p[4 * i + y] : last;
+        src[i] = static_cast<const u32x4*>(y0 == 0 ? c[0] : y0 == 1 ? c[1] : y0 == 2 ? c[2] : c[3]);
+      }
     }
-  };
-  load(pos);
-  if (pos + stride < npos) {
-    // the first position apart, so that the loop is entered, like its back
-    // edge, with a position's loads and stores in flight (the compiler then
-    // waits for the loads alone)
-    step([&] { load(pos + stride); }, false);  // in flight while this position is evaluated
-    advance();
-    for (; pos + stride < npos; advance()) step([&] { load(pos + stride); }, false);
+    u32x4 cur[G];
+    // the last position may be partial: its lanes past the end repeat the last
+    // vector (within the instruction) and store nothing
+    auto load = [&](int64_t ps) {
+      const int64_t g = ps * NV + q < nvec ? ps * NV + q : nvec - 1;
+#pragma unroll
+      for (int i = 0; i < G; ++i) cur[i] = __builtin_nontemporal_load(src[i] + g);
+    };
+    if (pos < npos) load(pos);
+    // K = 1: the output table, entry 4 i + y the output lane group y stores to
+    // in its i-th store (past the last output the last one again)
+    u32x4** ptab = reinterpret_cast<u32x4**>(rows_vec_lds + waves * (P + 1) * E);
+    uint32_t* tabw = reinterpret_cast<uint32_t*>(ptab + (K == 1 ? 4 * G : 0));
+    auto cl = [P](int k) { return k < P ? k : P - 1; };
+    if constexpr (K == 1) {
+      if (threadIdx.x < 4 * G) ptab[threadIdx.x] = static_cast<u32x4*>(ptrs.p[outs[cl(int(threadIdx.x))]]);
+    }
+    const int words = (moff + R * P + 7) / 8 * 2;
+    for (int i = threadIdx.x; i < words; i += blockDim.x) tabw[i] = reinterpret_cast<const uint32_t*>(tab)[i];
+    int o[K];  // offsets of the lane's elements in their instances
+#pragma unroll
+    for (int j = 0; j < K; ++j) o[j] = int(unsigned(b0 + 64 * j + lane) % unsigned(n));
+    __syncthreads();
+    if (pos >= npos) return;
+    const uint8_t* range_of = reinterpret_cast<const uint8_t*>(tabw);
+    const uint8_t* map = range_of + moff;  // [rank][range]
+    // stage the loaded position, evaluate, store; `next` issues the following
+    // position's loads between the stage writes and the evaluation. Only a
+    // wave's last position can be partial.
+    auto step = [&](auto next, bool last) {
+#pragma unroll
+      for (int i = 0; i < G; ++i)
+        *reinterpret_cast<u32x4*>(stage + (K == 1 ? cl(4 * i + y0) : i) * E + q * 4) = cur[i];
+      next();
+      wave_lds_sync();
+      int rr[K];
+#pragma unroll
+      for (int j = 0; j < K; ++j) rr[j] = range_of[o[j]];
+      constexpr int M = K == 1 ? 0 : 1;
+      A res[nvals<DT, M>()];
+      eval_one<DT, OPK, D, M, B>(tree, [&](int rank, u32x4(&v)[1]) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) v[0][j] = stage[map[rank * R + rr[j]] * E + 64 * j + lane];
+      }, res);
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        if constexpr (OPK == O_AVG) res[j] = res[j] / ptrs.div;
+        outw[64 * j + lane] = as_u(res[j]);
+      }
+      wave_lds_sync();
+      const u32x4 rv = *reinterpret_cast<const u32x4*>(outw + q * 4);
+      if (!last || pos * NV + q < nvec)
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          u32x4* d = K == 1 ? ptab[4 * i + y0] : static_cast<u32x4*>(ptrs.p[outs[i]]);
+          __builtin_nontemporal_store(rv, d + pos * NV + q);
+        }
+      wave_lds_sync();  // the next position's stage writes follow this one's reads
+    };
+    auto advance = [&] {
+      pos += stride;
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        o[j] += ostep;
+        if (o[j] >= n) o[j] -= n;
+      }
+    };
+    if (pos + stride < npos) {
+      // the first position apart, so that the loop is entered, like its back
+      // edge, with a position's loads and stores in flight (the compiler then
+      // waits for the loads alone)
+      step([&] { load(pos + stride); }, false);  // in flight while this position is evaluated
+      advance();
+      for (; pos + stride < npos; advance()) step([&] { load(pos + stride); }, false);
+    }
+    step([] {}, true);
   }
-  step([] {}, true);
 }
 
 // Several result trees per range and few ranks: each thread loads its fragment of

@@ -313,7 +313,7 @@ inline int64_t resident_blocks(const void* fn, int threads, size_t lds) {
   return v;
 }
 
-template <int DT, int OPK, int D, int K, int G>
+template <int DT, int OPK, int D, int K, int G, bool REG>
 hipError_t rows_vec_d(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab, int64_t nvec, int n, int R, int P,
                       int64_t max_blocks, hipStream_t st, Evs ev) {
   const int64_t npos = (nvec + 16 * K - 1) / (16 * K);
@@ -321,9 +321,10 @@ hipError_t rows_vec_d(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* 
   // every wave of the grid, which holds at most what the device keeps resident.
   // Four waves per workgroup share the tables; when the device holds more than
   // half the positions at once, single-wave workgroups spread them evenly.
-  const void* fn = reinterpret_cast<const void*>(&k_fused_rows_vec<DT, OPK, D, kLeafBatch, K, G>);
+  const void* fn = reinterpret_cast<const void*>(&k_fused_rows_vec<DT, OPK, D, kLeafBatch, K, G, REG>);
   auto lds_of = [&](int waves) {
-    return size_t(waves) * (P + 1) * 64 * K * sizeof(uint32_t) + size_t(K == 1 ? 8 * G : 0) * sizeof(void*) +
+    if (REG) return size_t(n + 1) / 2 * 8;  // the packed leaf ranks of each offset
+    return size_t(waves) * (P + 1) * 64 * K * sizeof(uint32_t) + size_t(K == 1 ? 4 * G : 0) * sizeof(void*) +
            size_t((n + 7) / 8 * 8 + R * P + 7) / 8 * 8;
   };
   int waves = 4;
@@ -335,37 +336,45 @@ hipError_t rows_vec_d(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* 
   int64_t blocks = (npos + waves - 1) / waves;
   if (res > 0) blocks = std::min(blocks, res);
   blocks = std::max<int64_t>(1, std::min(blocks, max_blocks));
-  hipExtLaunchKernelGGL((k_fused_rows_vec<DT, OPK, D, kLeafBatch, K, G>), dim3(unsigned(blocks)), dim3(64 * waves),
+  hipExtLaunchKernelGGL((k_fused_rows_vec<DT, OPK, D, kLeafBatch, K, G, REG>), dim3(unsigned(blocks)), dim3(64 * waves),
                         lds_of(waves), st, ev.start, ev.stop, 0, ptrs, prog, tab, nvec, int32_t(n), int32_t(R),
                         int32_t(P));
   return hipGetLastError();
 }
 
-// At most 8 ranks: four elements per lane, one load per rank (G = P); 9..32
-// ranks: one element per lane, G = ceil(P / 4) loads of four ranks each.
+// At most 8 ranks: four elements per lane, one load per rank (G = P), in
+// registers up to kRowsRegMaxRanks ranks, else staged; 9..32 ranks: one element
+// per lane, G = ceil(P / 4) loads of four ranks each.
+template <int DT, int OPK, int D, int G>
+hipError_t rows_vec_few(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab, int64_t nvec, int n, int R, int P,
+                        int64_t max_blocks, hipStream_t st, Evs ev) {
+  return rows_vec_d<DT, OPK, D, 4, G, (G <= kRowsRegMaxRanks)>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
+}
 template <int DT, int OPK, int D>
 hipError_t rows_vec_g(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab, int64_t nvec, int n, int R, int P,
                       int64_t max_blocks, hipStream_t st, Evs ev) {
-#define AR_RV(K_, G_) return rows_vec_d<DT, OPK, D, K_, G_>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev)
+#define AR_RF(G_) return rows_vec_few<DT, OPK, D, G_>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev)
+#define AR_RV(G_) return rows_vec_d<DT, OPK, D, 1, G_, false>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev)
   switch (P) {
-    case 1: AR_RV(4, 1);
-    case 2: AR_RV(4, 2);
-    case 3: AR_RV(4, 3);
-    case 4: AR_RV(4, 4);
-    case 5: AR_RV(4, 5);
-    case 6: AR_RV(4, 6);
-    case 7: AR_RV(4, 7);
-    case 8: AR_RV(4, 8);
+    case 1: AR_RF(1);
+    case 2: AR_RF(2);
+    case 3: AR_RF(3);
+    case 4: AR_RF(4);
+    case 5: AR_RF(5);
+    case 6: AR_RF(6);
+    case 7: AR_RF(7);
+    case 8: AR_RF(8);
     default: break;
   }
   switch ((P + 3) / 4) {
-    case 3: AR_RV(1, 3);
-    case 4: AR_RV(1, 4);
-    case 5: AR_RV(1, 5);
-    case 6: AR_RV(1, 6);
-    case 7: AR_RV(1, 7);
-    default: AR_RV(1, 8);
+    case 3: AR_RV(3);
+    case 4: AR_RV(4);
+    case 5: AR_RV(5);
+    case 6: AR_RV(6);
+    case 7: AR_RV(7);
+    default: AR_RV(8);
   }
+#undef AR_RF
 #undef AR_RV
 }
 

@@ -603,6 +603,19 @@ def test_rows_kernel_batches():
     finally:
         A.ar_set_launch_blocks(prev)
     assert np.array_equal(bits(got.reshape(12, 3001, 50)), bits(want))
+    # the same with at most 8 ranks (each lane evaluates its own vectors in
+    # registers, the positions' loads alternating between two register sets)
+    for P, n, B, algo, dtype, op, blocks in ((6, 106, 3001, "ring", "fp32", "sum", 5),
+                                             (3, 106, 2999, "generalized", "int32", "max", 7),
+                                             (5, 33, 4001, "ring", "fp32", "avg", 2)):
+        x = inputs.make(dtype, P, n * B, seed=P + B)
+        want = oracle.allreduce(x.reshape(P, B, n), algo, dtype, op, n=n)
+        prev = A.ar_set_launch_blocks(blocks)
+        try:
+            got = gpu_allreduce(x, algo, dtype, op, 0, "fused", batch=B)
+        finally:
+            A.ar_set_launch_blocks(prev)
+        assert np.array_equal(bits(got.reshape(P, B, n)), bits(want)), (P, n, B, algo, dtype, op)
     # the caller's events bracket the vector launch and the ragged tail's launch
     torch = torch_mod()
     x = inputs.make("fp32", 24, 106 * 39, seed=9)  # 4134 elements: 1033 vectors and 2 more
