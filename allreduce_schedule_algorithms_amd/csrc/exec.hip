@@ -168,6 +168,7 @@ struct Plan {
   std::vector<int32_t> ordered_ranks;
   bool rows = false;      // fused: k_fused_rows (strided batches of one program shape)
   int rows_ref = 0;       // its reference range
+  bool rows_chain = false;  // whose tree is a chain (each leaf after the first followed by one combination)
   int64_t rows_n = 0;     // the instance length its table describes (1: one range, identity renaming)
   std::vector<uint8_t> rows_tab;  // its range and rank tables
   DevBuf rtab;            // the same on the device
@@ -442,6 +443,19 @@ bool rows_table(const Schedule& s, std::vector<uint8_t>* t, int* ref) {
       std::memcpy(t->data() + loff + 4 * size_t(o), &w, sizeof w);
     }
   }
+  return true;
+}
+
+// Whether range `ref`'s program is one tree that is a chain: at least two
+// leaves, each after the first followed by exactly one combination.
+bool chain_tree(const Schedule& s, int ref) {
+  if (ref < 0) return false;
+  const int32_t* w = s.prog.data() + s.ranges[size_t(ref)].prog;
+  if (w[0] != 1 || w[1] < 2) return false;
+  const int nl = w[1];
+  const int32_t* nc = w + 3 + nl;
+  for (int k = 0; k < nl; ++k)
+    if (nc[k] != (k == 0 ? 0 : 1)) return false;
   return true;
 }
 
@@ -1077,6 +1091,7 @@ RunResult get_plan(const Spec& spec, int exec, int device, Plan** out) {
     pl->shape = fixed_shape(*s, &pl->tab, &pl->shape_nl);
     if (pl->shape == SH_NONE) pl->multi = multi_shape(*s, &pl->mt);
     pl->rows = rows_table(*s, &pl->rows_tab, &pl->rows_ref);
+    if (pl->rows) pl->rows_chain = chain_tree(*s, pl->rows_ref);
     pl->rows_n = spec.n;
     // four vectors per thread for short launches with few ranks, as the direct kernel
     pl->md = spec.P <= 8 && spec.n * spec.batch / vec_width(spec.dtype) <= (int64_t(1) << 19) ? 4 : 2;
@@ -1374,8 +1389,8 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
         // stack; measured 5% faster than 8 on 24-rank trees of three results)
         const int dv = pl->D == 8 && pl->s->max_need <= 6 ? 6 : pl->D;
         AR_DISPATCH(spec.dtype, spec.op,
-                    (e = launch_fused_rows_vec_t<DT, OPK>(dv, ptrs, ref, rt, nvec, int(pl->rows_n), R, spec.P, cap, st,
-                                                          ev1)));
+                    (e = launch_fused_rows_vec_t<DT, OPK>(dv, pl->rows_chain, ptrs, ref, rt, nvec, int(pl->rows_n), R,
+                                                          spec.P, cap, st, ev1)));
         if (e != hipSuccess) return hip_fail(e, "launching the fused replay");
       }
       if (nvec * 4 < total) {

@@ -401,6 +401,38 @@ __device__ __forceinline__ void eval_one(WP __restrict__ w, LeafAt&& leaf_at,
   for (int i = 0; i < N; ++i) res[i] = st[0][i];
 }
 
+// A chain (every leaf after the first followed by one combination) needs no
+// stack: res = combine(res, leaf) in leaf order, the operations the register
+// stack performs on it, with the same operands in the same order. Leaf ranks
+// are read in runs of B words like eval_one's (the host pads the program).
+template <int DT, int OPK, int M, int B, typename WP, typename LeafAt>
+__device__ __forceinline__ void eval_chain(WP __restrict__ w, LeafAt&& leaf_at,
+                                           typename TT<DT>::A (&res)[nvals<DT, M>()]) {
+  using A = typename TT<DT>::A;
+  constexpr int N = nvals<DT, M>();
+  const int nl = w[0];
+  const WP __restrict__ leaf = w + 2;
+  for (int base = 0; base < nl; base += B) {
+    int rk[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k) rk[k] = leaf[base + k];
+#pragma unroll
+    for (int k = 1; k < B; ++k) rk[k] = base + k < nl ? rk[k] : rk[0];
+    u32x4 raw[B][mm<M>()];
+#pragma unroll
+    for (int k = 0; k < B; ++k) leaf_at(rk[k], raw[k]);
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      if (base + k < nl) {
+        A x[N];
+        widen<DT, M>(raw[k], x);
+#pragma unroll
+        for (int i = 0; i < N; ++i) res[i] = base + k == 0 ? x[i] : cmb<OPK>(res[i], x[i]);
+      }
+    }
+  }
+}
+
 // IDL (one tree): leaves are ranks 0 .. nl - 1 and outputs nl, nl + 1, ... of
 // ptrs, which the caller orders so.
 template <int DT, int OPK, int D, int TM, int M, int B, bool NTS = true, bool EDGE = false, bool IDL = false,
@@ -825,10 +857,11 @@ __global__ __launch_bounds__(kThreads) void k_fused_rows(RankPtrs ptrs, const in
 //  In the staged forms lane L evaluates the reference range's program for
 //  elements L, L + 64, ..., reading leaf `rank` from the stage row of the rank
 //  its element's range renames it to (map[rank][range]: the lanes of one read
-//  hit consecutive bytes; stage reads hit consecutive words); the results go
-//  through LDS once more, so that each lane stores whole vectors to the
-//  program's output ranks. Only the wave reads what it wrote to its stage;
-//  wave-scope fences order those LDS accesses.
+//  hit consecutive bytes; stage reads hit consecutive words). A chain (the
+//  ring's trees; CHAIN) is folded leaf by leaf without the register stack.
+//  The results go through LDS once more, so that each lane stores whole
+//  vectors to the program's output ranks. Only the wave reads what it wrote
+//  to its stage; wave-scope fences order those LDS accesses.
 // The waves of a workgroup share one copy of the tables (those of k_fused_rows,
 // then the packed leaf ranks for at most kRowsRegMaxRanks ranks, each padded
 // to a multiple of 8 bytes) and, staged, of the output buffer table.
@@ -839,13 +872,14 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
-template <int DT, int OPK, int D, int B, int K, int G, bool REG>
+template <int DT, int OPK, int D, int B, int K, int G, bool REG, bool CHAIN>
 __global__ __launch_bounds__(kRowsVecThreads) void k_fused_rows_vec(RankPtrs ptrs, const int32_t* __restrict__ prog,
                                                                     const uint8_t* __restrict__ tab, int64_t nvec,
                                                                     int32_t n, int32_t R, int32_t P) {
   static_assert(TT<DT>::V == 4, "four 4-byte elements per vector");
   static_assert(K == 1 || K == 4, "one or four elements per lane");
   static_assert(!REG || (K == 4 && G <= kRowsRegMaxRanks), "the register form: one vector per lane and rank");
+  static_assert(!(REG && CHAIN), "chains are evaluated apart in the staged forms");
   using A = typename TT<DT>::A;
   constexpr int E = 64 * K, NV = 16 * K;  // elements and vectors of a position
   extern __shared__ uint32_t rows_vec_lds[];
@@ -996,10 +1030,12 @@ __global__ __launch_bounds__(kRowsVecThreads) void k_fused_rows_vec(RankPtrs ptr
       for (int j = 0; j < K; ++j) rr[j] = range_of[o[j]];
       constexpr int M = K == 1 ? 0 : 1;
       A res[nvals<DT, M>()];
-      eval_one<DT, OPK, D, M, B>(tree, [&](int rank, u32x4(&v)[1]) {
+      auto leaf = [&](int rank, u32x4(&v)[1]) {
 #pragma unroll
         for (int j = 0; j < K; ++j) v[0][j] = stage[map[rank * R + rr[j]] * E + 64 * j + lane];
-      }, res);
+      };
+      if constexpr (CHAIN) eval_chain<DT, OPK, M, B>(tree, leaf, res);
+      else eval_one<DT, OPK, D, M, B>(tree, leaf, res);
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         if constexpr (OPK == O_AVG) res[j] = res[j] / ptrs.div;

@@ -43,9 +43,10 @@ template <int DT, int OPK>
 hipError_t launch_fused_rows_t(int D, int TM, const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab,
                                int64_t first, int64_t total, int n, int R, int P, int iters, int64_t max_blocks,
                                hipStream_t st, Evs ev);
+// chain: the reference tree is a chain of combinations (D is then ignored).
 template <int DT, int OPK>
-hipError_t launch_fused_rows_vec_t(int D, const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab, int64_t nvec,
-                                   int n, int R, int P, int64_t max_blocks, hipStream_t st, Evs ev);
+hipError_t launch_fused_rows_vec_t(int D, bool chain, const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab,
+                                   int64_t nvec, int n, int R, int P, int64_t max_blocks, hipStream_t st, Evs ev);
 template <int DT, int OPK>
 hipError_t launch_fused_multi_t(int nl, int64_t nitems, const MultiPtrs& mp, const Item* items, const int32_t* tab,
                                 hipStream_t st, Evs ev);
@@ -313,7 +314,7 @@ inline int64_t resident_blocks(const void* fn, int threads, size_t lds) {
   return v;
 }
 
-template <int DT, int OPK, int D, int K, int G, bool REG>
+template <int DT, int OPK, int D, int K, int G, bool REG, bool CHAIN>
 hipError_t rows_vec_d(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab, int64_t nvec, int n, int R, int P,
                       int64_t max_blocks, hipStream_t st, Evs ev) {
   const int64_t npos = (nvec + 16 * K - 1) / (16 * K);
@@ -321,7 +322,7 @@ hipError_t rows_vec_d(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* 
   // every wave of the grid, which holds at most what the device keeps resident.
   // Four waves per workgroup share the tables; when the device holds more than
   // half the positions at once, single-wave workgroups spread them evenly.
-  const void* fn = reinterpret_cast<const void*>(&k_fused_rows_vec<DT, OPK, D, kLeafBatch, K, G, REG>);
+  const void* fn = reinterpret_cast<const void*>(&k_fused_rows_vec<DT, OPK, D, kLeafBatch, K, G, REG, CHAIN>);
   auto lds_of = [&](int waves) {
     if (REG) return size_t(n + 1) / 2 * 8;  // the packed leaf ranks of each offset
     return size_t(waves) * (P + 1) * 64 * K * sizeof(uint32_t) + size_t(K == 1 ? 4 * G : 0) * sizeof(void*) +
@@ -336,7 +337,7 @@ hipError_t rows_vec_d(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* 
   int64_t blocks = (npos + waves - 1) / waves;
   if (res > 0) blocks = std::min(blocks, res);
   blocks = std::max<int64_t>(1, std::min(blocks, max_blocks));
-  hipExtLaunchKernelGGL((k_fused_rows_vec<DT, OPK, D, kLeafBatch, K, G, REG>), dim3(unsigned(blocks)), dim3(64 * waves),
+  hipExtLaunchKernelGGL((k_fused_rows_vec<DT, OPK, D, kLeafBatch, K, G, REG, CHAIN>), dim3(unsigned(blocks)), dim3(64 * waves),
                         lds_of(waves), st, ev.start, ev.stop, 0, ptrs, prog, tab, nvec, int32_t(n), int32_t(R),
                         int32_t(P));
   return hipGetLastError();
@@ -345,16 +346,19 @@ hipError_t rows_vec_d(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* 
 // At most 8 ranks: four elements per lane, one load per rank (G = P), in
 // registers up to kRowsRegMaxRanks ranks, else staged; 9..32 ranks: one element
 // per lane, G = ceil(P / 4) loads of four ranks each.
-template <int DT, int OPK, int D, int G>
+template <int DT, int OPK, int D, int G, bool CHAIN>
 hipError_t rows_vec_few(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab, int64_t nvec, int n, int R, int P,
                         int64_t max_blocks, hipStream_t st, Evs ev) {
-  return rows_vec_d<DT, OPK, D, 4, G, (G <= kRowsRegMaxRanks)>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
+  constexpr bool reg = G <= kRowsRegMaxRanks;
+  return rows_vec_d<DT, OPK, D, 4, G, reg, CHAIN && !reg>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
 }
-template <int DT, int OPK, int D>
+// CHAIN: the reference tree is a chain (evaluated without the register stack
+// in the staged forms; D is then 2)
+template <int DT, int OPK, int D, bool CHAIN>
 hipError_t rows_vec_g(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab, int64_t nvec, int n, int R, int P,
                       int64_t max_blocks, hipStream_t st, Evs ev) {
-#define AR_RF(G_) return rows_vec_few<DT, OPK, D, G_>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev)
-#define AR_RV(G_) return rows_vec_d<DT, OPK, D, 1, G_, false>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev)
+#define AR_RF(G_) return rows_vec_few<DT, OPK, D, G_, CHAIN>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev)
+#define AR_RV(G_) return rows_vec_d<DT, OPK, D, 1, G_, false, CHAIN>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev)
   switch (P) {
     case 1: AR_RF(1);
     case 2: AR_RF(2);
@@ -379,18 +383,19 @@ hipError_t rows_vec_g(const RankPtrs& ptrs, const int32_t* prog, const uint8_t* 
 }
 
 template <int DT, int OPK>
-hipError_t launch_fused_rows_vec_t(int D, const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab, int64_t nvec,
-                                   int n, int R, int P, int64_t max_blocks, hipStream_t st, Evs ev) {
+hipError_t launch_fused_rows_vec_t(int D, bool chain, const RankPtrs& ptrs, const int32_t* prog, const uint8_t* tab,
+                                   int64_t nvec, int n, int R, int P, int64_t max_blocks, hipStream_t st, Evs ev) {
   if constexpr (TT<DT>::V != 4) {
     return hipErrorInvalidValue;  // 4-byte elements only
   } else {
     if (P < 1 || P > 32) return hipErrorInvalidValue;
+    if (chain) return rows_vec_g<DT, OPK, 2, true>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
     switch (D) {
-      case 2: return rows_vec_g<DT, OPK, 2>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
-      case 4: return rows_vec_g<DT, OPK, 4>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
-      case 6: return rows_vec_g<DT, OPK, 6>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
-      case 8: return rows_vec_g<DT, OPK, 8>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
-      default: return rows_vec_g<DT, OPK, 16>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
+      case 2: return rows_vec_g<DT, OPK, 2, false>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
+      case 4: return rows_vec_g<DT, OPK, 4, false>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
+      case 6: return rows_vec_g<DT, OPK, 6, false>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
+      case 8: return rows_vec_g<DT, OPK, 8, false>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
+      default: return rows_vec_g<DT, OPK, 16, false>(ptrs, prog, tab, nvec, n, R, P, max_blocks, st, ev);
     }
   }
 }
@@ -576,8 +581,9 @@ hipError_t launch_direct_t(bool vec, const RankPtrs& ptrs, int P, int64_t total,
   template hipError_t launch_fused_rows_t<DT, OPK>(int, int, const RankPtrs&, const int32_t*, const uint8_t*, \
                                                    int64_t, int64_t, int, int, int, int, int64_t, hipStream_t,  \
                                                    Evs);                                                        \
-  template hipError_t launch_fused_rows_vec_t<DT, OPK>(int, const RankPtrs&, const int32_t*, const uint8_t*,  \
-                                                       int64_t, int, int, int, int64_t, hipStream_t, Evs);      \
+  template hipError_t launch_fused_rows_vec_t<DT, OPK>(int, bool, const RankPtrs&, const int32_t*,           \
+                                                       const uint8_t*, int64_t, int, int, int, int64_t,        \
+                                                       hipStream_t, Evs);                                       \
   template hipError_t launch_fused_strided_t<DT, OPK>(int, int, int64_t, const RankPtrs&, const SItem*,     \
                                                       const int32_t*, int64_t, hipStream_t, Evs);          \
   template hipError_t launch_literal_t<DT, OPK>(int64_t, const RankPtrs&, const WsDesc&, const LitWork*,    \
