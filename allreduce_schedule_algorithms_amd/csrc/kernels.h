@@ -867,6 +867,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_rows(RankPtrs ptrs, const in
 // to a multiple of 8 bytes) and, staged, of the output buffer table.
 constexpr int kRowsVecThreads = 256;  // at most; the host picks 1 or 4 waves per workgroup
 constexpr int kRowsRegMaxRanks = 3;   // ranks up to which the register form runs (even at 4, slower from 5)
+constexpr int kRowsTableRegs = 4;     // register form: table words per thread loaded ahead of the data
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -905,11 +906,31 @@ __global__ __launch_bounds__(kRowsVecThreads) void k_fused_rows_vec(RankPtrs ptr
 #pragma unroll
       for (int i = 0; i < G; ++i) r[i] = __builtin_nontemporal_load(src[i] + g);
     };
-    u32x4 ra[G], rb[G];
-    if (pos < npos) load(pos, ra);
-    uint32_t* lrank = rows_vec_lds;  // per offset: the rank each leaf reads, 4 bits per leaf rank
+    // the table's first words are loaded ahead of the data, so that the wait
+    // before their LDS copy covers them alone (loads retire in order) and the
+    // lookups of the first position run while its data is in flight. The data
+    // loads read memory nothing has stored to yet, which the compiler may
+    // place anywhere: scheduling barriers keep them after the table loads and
+    // ahead of the table's copy and the workgroup barrier. Unconditional,
+    // clamped loads leave no branch between a load and its wait.
     const uint32_t* lsrc = reinterpret_cast<const uint32_t*>(tab) + (moff + R * P + 7) / 8 * 2;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) lrank[i] = lsrc[i];
+    uint32_t tw[kRowsTableRegs];
+#pragma unroll
+    for (int r = 0; r < kRowsTableRegs; ++r) {
+      const int i = int(threadIdx.x) + r * int(blockDim.x);
+      tw[r] = lsrc[i < n ? i : n - 1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 ra[G], rb[G];
+    load(pos, ra);  // past the end (an idle wave) the last vector, unused
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t* lrank = rows_vec_lds;  // per offset: the rank each leaf reads, 4 bits per leaf rank
+#pragma unroll
+    for (int r = 0; r < kRowsTableRegs; ++r) {
+      const int i = int(threadIdx.x) + r * int(blockDim.x);
+      if (i < n) lrank[i] = tw[r];
+    }
+    for (int i = int(threadIdx.x) + kRowsTableRegs * int(blockDim.x); i < n; i += int(blockDim.x)) lrank[i] = lsrc[i];
 #pragma unroll
     for (int i = 0; i < G; ++i) dst[i] = static_cast<u32x4*>(ptrs.p[outs[i]]);
     int o[4];  // offsets of the lane's elements in their instances
