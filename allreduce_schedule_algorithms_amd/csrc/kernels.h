@@ -864,7 +864,8 @@ __global__ __launch_bounds__(kThreads) void k_fused_rows(RankPtrs ptrs, const in
 //  to its stage; wave-scope fences order those LDS accesses.
 // The waves of a workgroup share one copy of the tables (those of k_fused_rows,
 // then the packed leaf ranks for at most kRowsRegMaxRanks ranks, each padded
-// to a multiple of 8 bytes) and, staged, of the output buffer table.
+// to a multiple of 8 bytes) and, with one element per lane, of the output
+// buffer table.
 constexpr int kRowsVecThreads = 256;  // at most; the host picks 1 or 4 waves per workgroup
 constexpr int kRowsRegMaxRanks = 3;   // ranks up to which the register form runs (even at 4, slower from 5)
 constexpr int kRowsTableRegs = 4;     // register form: table words per thread loaded ahead of the data
@@ -1019,17 +1020,41 @@ __global__ __launch_bounds__(kRowsVecThreads) void k_fused_rows_vec(RankPtrs ptr
 #pragma unroll
       for (int i = 0; i < G; ++i) cur[i] = __builtin_nontemporal_load(src[i] + g);
     };
-    if (pos < npos) load(pos);
+    // TF (9..12 ranks): like the register form, a word of the table per
+    // thread is loaded ahead of the data, the output table is written from
+    // scalar reads, and each position's range lookup precedes its stage
+    // writes, so the first position's lookups run while its data is in flight
+    // (measured +3-4.5% at 12 ranks; at 24 ranks, with more positions per
+    // wave, 1% slower)
+    constexpr bool TF = K == 1 && G <= 3;
+    const uint32_t* tsrc = reinterpret_cast<const uint32_t*>(tab);
+    const int words = (moff + R * P + 7) / 8 * 2;
+    uint32_t tw0 = 0;
+    if constexpr (TF) {
+      tw0 = tsrc[int(threadIdx.x) < words ? int(threadIdx.x) : words - 1];
+      __builtin_amdgcn_sched_barrier(0);
+      load(pos);  // past the end (an idle wave) the last vector, unused
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      if (pos < npos) load(pos);
+    }
     // K = 1: the output table, entry 4 i + y the output lane group y stores to
     // in its i-th store (past the last output the last one again)
     u32x4** ptab = reinterpret_cast<u32x4**>(rows_vec_lds + waves * (P + 1) * E);
     uint32_t* tabw = reinterpret_cast<uint32_t*>(ptab + (K == 1 ? 4 * G : 0));
     auto cl = [P](int k) { return k < P ? k : P - 1; };
-    if constexpr (K == 1) {
-      if (threadIdx.x < 4 * G) ptab[threadIdx.x] = static_cast<u32x4*>(ptrs.p[outs[cl(int(threadIdx.x))]]);
+    if constexpr (TF) {
+      if (threadIdx.x == 0)
+#pragma unroll
+        for (int e = 0; e < 4 * G; ++e) ptab[e] = static_cast<u32x4*>(ptrs.p[outs[cl(e)]]);
+      if (int(threadIdx.x) < words) tabw[threadIdx.x] = tw0;
+      for (int i = int(threadIdx.x + blockDim.x); i < words; i += int(blockDim.x)) tabw[i] = tsrc[i];
+    } else {
+      if constexpr (K == 1) {
+        if (threadIdx.x < 4 * G) ptab[threadIdx.x] = static_cast<u32x4*>(ptrs.p[outs[cl(int(threadIdx.x))]]);
+      }
+      for (int i = threadIdx.x; i < words; i += blockDim.x) tabw[i] = tsrc[i];
     }
-    const int words = (moff + R * P + 7) / 8 * 2;
-    for (int i = threadIdx.x; i < words; i += blockDim.x) tabw[i] = reinterpret_cast<const uint32_t*>(tab)[i];
     int o[K];  // offsets of the lane's elements in their instances
 #pragma unroll
     for (int j = 0; j < K; ++j) o[j] = int(unsigned(b0 + 64 * j + lane) % unsigned(n));
@@ -1041,14 +1066,16 @@ __global__ __launch_bounds__(kRowsVecThreads) void k_fused_rows_vec(RankPtrs ptr
     // position's loads between the stage writes and the evaluation. Only a
     // wave's last position can be partial.
     auto step = [&](auto next, bool last) {
+      int rr[K];
+      if constexpr (TF) rr[0] = range_of[o[0]];  // before the stage writes, which wait for the loads
 #pragma unroll
       for (int i = 0; i < G; ++i)
         *reinterpret_cast<u32x4*>(stage + (K == 1 ? cl(4 * i + y0) : i) * E + q * 4) = cur[i];
       next();
       wave_lds_sync();
-      int rr[K];
+      if constexpr (!TF)
 #pragma unroll
-      for (int j = 0; j < K; ++j) rr[j] = range_of[o[j]];
+        for (int j = 0; j < K; ++j) rr[j] = range_of[o[j]];
       constexpr int M = K == 1 ? 0 : 1;
       A res[nvals<DT, M>()];
       auto leaf = [&](int rank, u32x4(&v)[1]) {
