@@ -575,6 +575,11 @@ def test_rows_kernel_batches():
              (3, 106, "generalized", 0, 57, K.AR_KERNEL_ROWS_VEC, (("fp32", "avg"),)),
              (8, 64, "ring", 0, 129, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"), ("int32", "sum"))),
              (27, 90, "ring", 0, 213, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"),)),
+             # 9-12 ranks with instances long enough that the range and map
+             # table has more words than a single-wave workgroup has lanes
+             (12, 500, "ring", 0, 60, K.AR_KERNEL_ROWS_VEC, (("fp32", "sum"), ("int32", "max"))),
+             (10, 600, "generalized", 0, 45, K.AR_KERNEL_ROWS_VEC, (("fp32", "avg"),)),
+             (11, 690, "ring", 0, 40, K.AR_KERNEL_ROWS_VEC, (("fp32", "max"),)),
              (24, 106, "generalized", 5, 500, K.AR_KERNEL_JIT, (("fp32", "sum"), ("int32", "max"), ("fp32", "avg"))),
              (24, 20_001, "generalized", 4, 1, K.AR_KERNEL_JIT, (("fp32", "sum"),)),
              (24, 106, "generalized", 1, 200, K.AR_KERNEL_STRIDED, (("fp32", "sum"),))]
