@@ -1456,9 +1456,10 @@ RunResult run_allreduce(void* const* bufs, const Spec& spec, int exec, void* wor
       } else if (pl->ordered) {
         RankPtrs op = ptrs;  // leaf buffers in postfix order, then the output buffers
         for (size_t q = 0; q < pl->ordered_ranks.size(); ++q) op.p[q] = ptrs.p[pl->ordered_ranks[q]];
+        const int dv = pl->D == 8 && pl->s->max_need <= 6 ? 6 : pl->D;  // a stack of 6 where it suffices
         AR_DISPATCH(spec.dtype, spec.op,
-                    (e = launch_fused_t<DT, OPK>(pl->D, TM, spec.P, pl->s->max_leaves, cnt, op, items + off, prog,
-                                                 st, ei, true)));
+                    (e = launch_fused_t<DT, OPK>(dv, TM, spec.P, pl->s->max_leaves, cnt, op, items + off, prog, st,
+                                                 ei, true)));
       } else {
         AR_DISPATCH(spec.dtype, spec.op,
                     (e = launch_fused_t<DT, OPK>(pl->D, TM, spec.P, pl->s->max_leaves, cnt, ptrs, items + off, prog,

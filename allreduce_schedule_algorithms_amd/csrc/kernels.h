@@ -479,18 +479,26 @@ __device__ __forceinline__ void replay(const RankPtrs& ptrs, WP __restrict__ w, 
 // Register fragments per thread of the program-driven replay. Its work items
 // hold one vector per thread, so the second fragment of a two-fragment form
 // stays idle; yet for single-tree programs with a stack of 4 to 8 (bf16: 4)
-// that form measured faster (interleaved runs: AHC 5.96 vs 5.87 TB/s, 24-rank
-// binomial 5.18 vs 5.00 TB/s). Chains (a stack of 2) take one fragment: the
-// idle one's arithmetic cost the 192-rank bf16 ring 8% (4.42 vs 4.79 TB/s).
+// that read their leaf ranks from the program, that form measured faster
+// (interleaved runs: AHC 5.96 vs 5.87 TB/s; 24-rank binomial 5.18 vs 5.00 TB/s
+// before single-range programs took the ordered form below, which keeps one).
+// Chains (a stack of 2) take one fragment: the idle one's arithmetic cost the
+// 192-rank bf16 ring 8% (4.42 vs 4.79 TB/s).
 template <int DT, int D, int TM> constexpr int fused_m() {
   return (TM == 1 && D > 2 && D <= (DT == D_BF16 ? 4 : 8)) ? 2 : 1;
 }
 
+// With the buffers in leaf order (IDL) the replay takes one fragment at every
+// stack depth: the loads no longer wait on rank reads from the program, and
+// the smaller register footprint (fp32: 96 VGPRs at a stack of 6, 112 at 8,
+// against 114-162 with two fragments) keeps more waves resident (interleaved
+// runs, 10^4 x 106 fp32: 24-rank recursive doubling and binomial +3%, 12-rank
+// +1-2%).
 template <int DT, int OPK, int D, int TM, int B, bool IDL = false>
 __global__ __launch_bounds__(kThreads) void k_fused(RankPtrs ptrs, const Item* __restrict__ items,
                                                     const int32_t* __restrict__ prog) {
   constexpr int V = TT<DT>::V;
-  constexpr int M = fused_m<DT, D, TM>();
+  constexpr int M = IDL ? 1 : fused_m<DT, D, TM>();
   constexpr bool NT = TM == 1;  // several trees re-read their leaves: keep them cacheable
   const Item it = items[item_index(ptrs.xcd)];
   const auto w = prog_words<TM>(prog, it.tag);

@@ -130,6 +130,13 @@ void fused_ordered(int D, int B, const dim3& g, const dim3& b, hipStream_t st, E
       case 7: fused1<DT, OPK, 4, 7, true>(g, b, st, ev, ptrs, items, prog); break;
       default: fused1<DT, OPK, 4, 8, true>(g, b, st, ev, ptrs, items, prog); break;
     }
+  } else if (D == 6) {
+    switch (B) {
+      case 5: fused1<DT, OPK, 6, 5, true>(g, b, st, ev, ptrs, items, prog); break;
+      case 6: fused1<DT, OPK, 6, 6, true>(g, b, st, ev, ptrs, items, prog); break;
+      case 7: fused1<DT, OPK, 6, 7, true>(g, b, st, ev, ptrs, items, prog); break;
+      default: fused1<DT, OPK, 6, 8, true>(g, b, st, ev, ptrs, items, prog); break;
+    }
   } else {
     switch (B) {
       case 5: fused1<DT, OPK, 8, 5, true>(g, b, st, ev, ptrs, items, prog); break;

@@ -260,9 +260,9 @@ ar_status ar_workspace_bytes(const ar_call* call, size_t* bytes);
  *                            buffers looked up in LDS.
  *  AR_KERNEL_ROWS_VEC        the same batches with 4-byte elements, one tree per range, at most 32
  *                            ranks and more than 4096 elements (16-byte aligned buffers; otherwise
- *                            AR_KERNEL_ROWS runs): every rank's vector at four elements per thread
- *                            loaded once and staged in LDS, the leaves read from there in each
- *                            range's order.
+ *                            AR_KERNEL_ROWS runs): every rank's vectors loaded once, and the leaves
+ *                            read in each range's order from registers (at most 3 ranks) or from
+ *                            an LDS stage.
  *  AR_KERNEL_DAG             the DAG replay: more than 8 result trees per range (the generalized
  *                            algorithm with large r at large P), and every call under
  *                            AR_EXEC_DAG; each distinct combination once, values in LDS.
