@@ -672,6 +672,12 @@ KERNEL_NAMES = {
 }
 
 
+def profile_name(wl_name, P):
+    """A workload's name in profile summaries and traffic records: the name, and
+    the rank count where it is not the workload's default (small_batch_P3)."""
+    return wl_name if P is None or P == WORKLOADS[wl_name]["P"] else f"{wl_name}_P{P}"
+
+
 def load_traffic(wl_name, key):
     """The committed counter summary's record for this workload and schedule:
     HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, each scaled by what it
@@ -761,11 +767,11 @@ def extra_workload(name, flush, P=None, unbatched=False):
 # rocprofv3 output -> profiles/ summaries
 # --------------------------------------------------------------------------
 PROFILE_COMMANDS = """command (kernel trace):
-  rocprofv3 --kernel-trace --stats -d {root}/{case}/trace -o t --output-format csv -- python3 bench.py --workload {wl} --schedule {key} --steps 30 --warmup 5 --no-cpu --no-extras > {root}/{case}/bench.json
+  rocprofv3 --kernel-trace --stats -d {root}/{case}/trace -o t --output-format csv -- python3 bench.py --workload {wl}{popt} --schedule {key} --steps 30 --warmup 5 --no-cpu --no-extras > {root}/{case}/bench.json
 commands (counters, one pass each):
-  rocprofv3 --pmc FETCH_SIZE -d {root}/{case}/fetch -o c --output-format csv -- python3 bench.py --workload {wl} --schedule {key} --steps 3 --warmup 1 --no-cpu --no-extras
-  rocprofv3 --pmc WRITE_SIZE -d {root}/{case}/write -o c --output-format csv -- python3 bench.py --workload {wl} --schedule {key} --steps 3 --warmup 1 --no-cpu --no-extras
-  rocprofv3 --pmc {sq} -d {root}/{case}/sq -o c --output-format csv -- python3 bench.py --workload {wl} --schedule {key} --steps 3 --warmup 1 --no-cpu --no-extras
+  rocprofv3 --pmc FETCH_SIZE -d {root}/{case}/fetch -o c --output-format csv -- python3 bench.py --workload {wl}{popt} --schedule {key} --steps 3 --warmup 1 --no-cpu --no-extras
+  rocprofv3 --pmc WRITE_SIZE -d {root}/{case}/write -o c --output-format csv -- python3 bench.py --workload {wl}{popt} --schedule {key} --steps 3 --warmup 1 --no-cpu --no-extras
+  rocprofv3 --pmc {sq} -d {root}/{case}/sq -o c --output-format csv -- python3 bench.py --workload {wl}{popt} --schedule {key} --steps 3 --warmup 1 --no-cpu --no-extras
   rocprofv3 --pmc FETCH_SIZE -d {root}/calib/fetch -o c --output-format csv -- python3 bench.py --calibrate-copy 512
   rocprofv3 --pmc WRITE_SIZE -d {root}/calib/write -o c --output-format csv -- python3 bench.py --calibrate-copy 512
 summary:
@@ -863,7 +869,10 @@ def summarize_profiles(root):
             continue
         with open(bj) as f:
             line = json.loads([ln for ln in f if ln.startswith("{")][-1])
-        wl = line["config"]["workload"].split(":")[0]
+        wl0 = line["config"]["workload"].split(":")[0]
+        P = line["config"].get("P")
+        wl = profile_name(wl0, P)
+        popt = "" if wl == wl0 else f" --P {P}"
         key = line["config"]["schedule"]
         alg = line["roofline"]["algorithmic_bytes_per_launch"]
         stats = _kernel_stats(os.path.join(cdir, "trace"))
@@ -877,7 +886,8 @@ def summarize_profiles(root):
         launches = line["roofline"].get("launches_per_call", 1)
         lines = [f"# {dom_name} on {line['config']['workload']}; schedule {key}",
                  f"# kernel source hash {traffic['kernel_hash']}", "",
-                 PROFILE_COMMANDS.format(root=root.rstrip("/"), case=case, wl=wl, key=key, sq=" ".join(SQ_COUNTERS)), "",
+                 PROFILE_COMMANDS.format(root=root.rstrip("/"), case=case, wl=wl0, popt=popt, key=key,
+                                         sq=" ".join(SQ_COUNTERS)), "",
                  "kernel stats (rocprofv3 --stats, all kernels of the run):",
                  f"  {'name':70s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
         for s in stats[:6]:
@@ -1010,7 +1020,7 @@ def main():
     cst = A.ar_schedule_build(call).cost()
     value = head["GBps"]
     achieved = head["kernel_GBps"]
-    rec = load_traffic(wl["name"], hkey)
+    rec = load_traffic(profile_name(wl["name"], wl["P"]), hkey)
     traffic = rec.get("bytes_per_launch") if rec else None
     alg = essential_bytes(wl, h["coll"])
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
